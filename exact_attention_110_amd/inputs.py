@@ -1,0 +1,150 @@
+"""Seeded synthetic inputs for the attention workloads (no attention arithmetic here).
+
+This module only draws random numbers, rounds them to the storage dtype and
+builds block masks. Both the HIP path (tests, bench) and the float64 oracle
+consume what it returns; it holds none of the method's arithmetic.
+
+The workloads stand in for the ones the pages measure on (GPT-2 and
+long-range-arena training in the nadeemcite summary, "Summary"); those need
+models and datasets, so the inputs here are i.i.d. normal draws with the
+pages' shapes instead:
+
+* ``single_head_fp32`` is the lesson's worked example ("FlashAttention" lesson,
+  Developer tier, flash_numpy.py): one head, N=512, d=32, float32 draws from
+  ``numpy.random.default_rng(0)`` in the order Q, K, V.
+* the others draw Q, K, V (and the upstream gradient dO when a backward pass
+  is timed) in that order, each with C-order shape [B, H or Hkv, N, d], as
+  float32 normals from ``default_rng(seed)``, then round to the storage dtype
+  with round-to-nearest-even.
+"""
+
+from dataclasses import dataclass, field
+import math
+
+import numpy as np
+
+MASK_BLOCK = 128
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    Hkv: int
+    N: int
+    d: int
+    dtype: str            # "fp32", "bf16" or "fp16"
+    causal: bool
+    seed: int
+    backward: bool
+    sigma: float = 1.0
+    sparse: bool = False  # band of 4 diagonal blocks plus 5% random off-band blocks
+    check_heads: int = 0  # 0 = every (b, h); k > 0 = k seeded heads of batch 0
+    note: str = field(default="", compare=False)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def G(self) -> int:
+        return self.H // self.Hkv
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("single_head_fp32", 1, 1, 1, 512, 32, "fp32", False, 0, False,
+                 note="the lesson's worked example, forward only"),
+        Workload("gpt2_small_bf16", 8, 12, 12, 1024, 64, "bf16", True, 2, True,
+                 note="GPT-2-small attention shape, causal"),
+        Workload("long_seq_bf16", 1, 16, 16, 16384, 128, "bf16", True, 3, True, check_heads=2,
+                 note="long-sequence causal attention, the throughput workload"),
+        Workload("gqa_bf16", 4, 32, 8, 8192, 128, "bf16", True, 4, False,
+                 note="grouped-query attention, group of 4, forward only"),
+        Workload("block_sparse_fp16", 1, 8, 8, 65536, 64, "fp16", False, 5, True, sigma=0.5,
+                 sparse=True, check_heads=1,
+                 note="128x128 block mask: band of 4 diagonal blocks + 5% random off-band"),
+    ]
+}
+
+
+def _torch_dtype(name):
+    import torch
+    return {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[name]
+
+
+def draw(shape, rng, sigma=1.0):
+    """float32 normal draws N(0, sigma) of the given C-order shape."""
+    return rng.normal(0.0, sigma, size=shape).astype(np.float32)
+
+
+def round_to(x, dtype):
+    """Round a float32 numpy array to the storage dtype (RNE), as a CPU torch tensor."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to(_torch_dtype(dtype))
+
+
+def band_plus_random_mask(n, seed, band=4, frac=0.05, block=MASK_BLOCK):
+    """uint8 [nb, nb] block mask: blocks (I, J) with I-band < J <= I, plus
+    round(frac * #off-band) off-band blocks drawn uniformly without replacement
+    from ``default_rng(seed)``."""
+    nb = -(-n // block)
+    m = np.zeros((nb, nb), dtype=np.uint8)
+    ii, jj = np.meshgrid(np.arange(nb), np.arange(nb), indexing="ij")
+    in_band = (jj <= ii) & (jj > ii - band)
+    m[in_band] = 1
+    off = np.flatnonzero(~in_band.ravel())
+    k = int(round(frac * off.size))
+    pick = np.random.default_rng(seed).choice(off.size, size=k, replace=False)
+    m.ravel()[off[pick]] = 1
+    return m
+
+
+def check_heads(w: Workload):
+    """The (b, h) pairs the oracle checks fully for a workload."""
+    if w.check_heads == 0:
+        return [(b, h) for b in range(w.B) for h in range(w.H)]
+    hs = np.random.default_rng(w.seed + 100).choice(w.H, size=w.check_heads, replace=False)
+    return [(0, int(h)) for h in sorted(hs)]
+
+
+def make(w: Workload, with_grad=None):
+    """Inputs of a workload as CPU torch tensors in the storage dtype.
+
+    Returns a dict with q, k, v, (do), mask (uint8 numpy array or None).
+    """
+    rng = np.random.default_rng(w.seed)
+    out = {}
+    qs = (w.B, w.H, w.N, w.d)
+    ks = (w.B, w.Hkv, w.N, w.d)
+    out["q"] = round_to(draw(qs, rng, w.sigma), w.dtype)
+    out["k"] = round_to(draw(ks, rng, w.sigma), w.dtype)
+    out["v"] = round_to(draw(ks, rng, w.sigma), w.dtype)
+    if w.backward if with_grad is None else with_grad:
+        out["do"] = round_to(draw(qs, rng, w.sigma), w.dtype)
+    out["mask"] = band_plus_random_mask(w.N, w.seed + 200) if w.sparse else None
+    return out
+
+
+def make_small(B, H, Hkv, N, d, dtype, seed, sigma=1.0, with_grad=True):
+    """Small seeded inputs of any shape (same recipe), as CPU torch tensors."""
+    rng = np.random.default_rng(seed)
+    out = {
+        "q": round_to(draw((B, H, N, d), rng, sigma), dtype),
+        "k": round_to(draw((B, Hkv, N, d), rng, sigma), dtype),
+        "v": round_to(draw((B, Hkv, N, d), rng, sigma), dtype),
+    }
+    if with_grad:
+        out["do"] = round_to(draw((B, H, N, d), rng, sigma), dtype)
+    return out
+
+
+def random_block_mask(n, density, seed, block=MASK_BLOCK, keep_diagonal=False):
+    """uint8 [nb, nb] mask with i.i.d. Bernoulli(density) blocks (for small tests)."""
+    nb = -(-n // block)
+    m = (np.random.default_rng(seed).random((nb, nb)) < density).astype(np.uint8)
+    if keep_diagonal:
+        np.fill_diagonal(m, 1)
+    return m

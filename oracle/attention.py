@@ -1,0 +1,227 @@
+"""Float64 reference for exact attention: forward and analytic backward.
+
+Test infrastructure only (see the package docstring). Nothing here is tiled,
+fused or reordered beyond what the definition states: each query row's full
+score vector over its visible keys is materialised, normalised and applied.
+Rows are processed a chunk at a time only so that numpy can vectorise; the
+chunking does not change the arithmetic of any row.
+
+Sources (cited by page title and section):
+* "FlashAttention" lesson (learn.pranaymahendrakar.com), Researcher tier,
+  "The problem being solved": O = softmax(Q K^T / sqrt(d)) V, with S and P
+  the N x N score and probability matrices.
+* Same lesson, Developer tier, flash_numpy.py ``naive_attention``: the scale
+  multiplies Q K^T before the row maximum is subtracted and exp is taken.
+* Same lesson, Researcher tier, "IO complexity", and the nadeemcite.github.io
+  summary "FlashAttention: Fast and Memory-Efficient Exact Attention with
+  IO-Awareness", Core Idea item 3: the backward pass rebuilds P from saved
+  softmax statistics. The statistic kept here is L = m + ln(l), the natural-log
+  log-sum-exp of a row's scaled scores, so that P = exp(S - L).
+* Causal masking: the lesson's Beginner tier ("What was broken before") says a
+  word attends to earlier words; read here as key j visible to query i iff
+  j <= i (self included).
+* Block-sparse masking: the nadeemcite summary, Key Method Details,
+  "Block-sparse extension": a mask over blocks. Read here as a uint8 matrix of
+  128 x 128 blocks, nonzero = keep, shared by every batch and head, combined
+  with causal masking by intersection.
+* Grouped-query attention: the lesson's related-term card "Grouped-query
+  attention": a group of query heads shares one key/value head. Read here as
+  contiguous groups, kv head = h // (H // Hkv).
+
+The gradient formulas are not on the pages; they are the chain rule through
+the row softmax (its Jacobian is diag(p) - p p^T), pinned by finite
+differences in the tests.
+"""
+
+import numpy as np
+
+MASK_BLOCK = 128  # block-mask granularity in rows and columns
+
+
+def visible(rows, keys, causal, block_mask, block=MASK_BLOCK):
+    """Boolean matrix a[r, c]: is key ``keys[c]`` visible to query ``rows[r]``.
+
+    Causal: j <= i. Block mask: mask[i // block][j // block] != 0. Both, when
+    given, must hold.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+    a = np.ones((rows.size, keys.size), dtype=bool)
+    if causal:
+        a &= keys[None, :] <= rows[:, None]
+    if block_mask is not None:
+        bm = np.asarray(block_mask) != 0
+        a &= bm[(rows // block)[:, None], (keys // block)[None, :]]
+    return a
+
+
+def candidate_keys(rows, n_keys, causal, block_mask, block=MASK_BLOCK):
+    """Keys that at least one of ``rows`` may see (a superset used to gather K, V).
+
+    Keys outside this set are invisible to every row of the chunk, so leaving
+    them out drops only terms whose probability is exactly zero.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.arange(n_keys, dtype=np.int64)
+    if rows.size == 0:
+        return keys[:0]
+    if causal:
+        keys = keys[keys <= rows.max()]
+    if block_mask is not None:
+        bm = np.asarray(block_mask) != 0
+        any_row = bm[np.unique(rows // block)].any(axis=0)
+        keys = keys[any_row[keys // block]]
+    return keys
+
+
+def _chunks(rows, size):
+    for i in range(0, rows.size, size):
+        yield rows[i:i + size]
+
+
+def _row_softmax(q_rows, k_keys, scale, vis):
+    """Scores, probabilities and log-sum-exp of one chunk of rows.
+
+    s = scale * q k^T over the gathered keys, -inf where a key is invisible.
+    L = m + ln(sum exp(s - m)) with m the row maximum (the safe-softmax shift of
+    ``naive_attention``); p = exp(s - L). A row with no visible key has
+    L = -inf and p = 0 (nothing to attend to, so it contributes nothing).
+    """
+    s = scale * (q_rows @ k_keys.T)
+    s = np.where(vis, s, -np.inf)
+    m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
+    has = np.isfinite(m)
+    m0 = np.where(has, m, 0.0)
+    e = np.exp(s - m0[:, None])
+    ssum = e.sum(axis=1)
+    with np.errstate(divide="ignore"):
+        lse = np.where(has, m0 + np.log(np.where(has, ssum, 1.0)), -np.inf)
+    p = np.where(has[:, None], e / np.where(has, ssum, 1.0)[:, None], 0.0)
+    return s, p, lse
+
+
+def head_probabilities(q, k, scale, causal=False, block_mask=None, rows=None):
+    """Full probability rows P[rows, :] (N keys wide) of one query head.
+
+    q: [N, d] float64 query rows of the head, k: [N, d] keys of its kv head.
+    """
+    n = k.shape[0]
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    keys = np.arange(n)
+    vis = visible(rows, keys, causal, block_mask)
+    _, p, lse = _row_softmax(q[rows], k, scale, vis)
+    return p, lse
+
+
+def head_forward(q, k, v, scale, causal=False, block_mask=None, rows=None, chunk=256):
+    """O and L for the given query rows of one head (q: [N, d], k, v: [N, d])."""
+    n = k.shape[0]
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.zeros((rows.size, v.shape[1]))
+    lse = np.full(rows.size, -np.inf)
+    pos = 0
+    for ch in _chunks(rows, chunk):
+        keys = candidate_keys(ch, n, causal, block_mask)
+        if keys.size:
+            vis = visible(ch, keys, causal, block_mask)
+            _, p, l_ = _row_softmax(q[ch], k[keys], scale, vis)
+            o[pos:pos + ch.size] = p @ v[keys]
+            lse[pos:pos + ch.size] = l_
+        pos += ch.size
+    return o, lse
+
+
+def head_backward(q, k, v, do, scale, causal=False, block_mask=None, chunk=256):
+    """Gradients of sum(O * dO) for one query head.
+
+    With p the probability rows and g = dO:
+      dV_j += sum_i p_ij g_i
+      dP_ij = g_i . v_j
+      D_i   = sum_j p_ij dP_ij            (equals g_i . o_i)
+      dS_ij = p_ij (dP_ij - D_i)          (softmax Jacobian)
+      dQ_i  = scale * sum_j dS_ij k_j
+      dK_j += scale * sum_i dS_ij q_i
+    Returns dq [N, d] and this head's contributions dk, dv [N, d] to its kv
+    head (callers sum them over a grouped-query group).
+    """
+    n = k.shape[0]
+    rows = np.arange(q.shape[0], dtype=np.int64)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for ch in _chunks(rows, chunk):
+        keys = candidate_keys(ch, n, causal, block_mask)
+        if keys.size == 0:
+            continue
+        vis = visible(ch, keys, causal, block_mask)
+        _, p, _ = _row_softmax(q[ch], k[keys], scale, vis)
+        g = do[ch]
+        dv[keys] += p.T @ g
+        dp = g @ v[keys].T
+        dd = (p * dp).sum(axis=1)
+        ds = p * (dp - dd[:, None])
+        dq[ch] = scale * (ds @ k[keys])
+        dk[keys] += scale * (ds.T @ q[ch])
+    return dq, dk, dv
+
+
+def _heads(B, H, heads):
+    if heads is None:
+        return [(b, h) for b in range(B) for h in range(H)]
+    return [(int(b), int(h)) for b, h in heads]
+
+
+def forward(q, k, v, scale, causal=False, block_mask=None, heads=None, rows=None):
+    """Attention forward over [B, H, N, d] queries and [B, Hkv, N, d] keys/values.
+
+    Query head h reads kv head h // (H // Hkv). With ``heads=None`` returns full
+    o [B, H, R, d] and lse [B, H, R] (R = len(rows) or N); otherwise arrays
+    stacked in the order of ``heads`` (a list of (b, h)): o [nh, R, d], lse [nh, R].
+    """
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if H % Hkv:
+        raise ValueError("H must be a multiple of Hkv")
+    G = H // Hkv
+    hl = _heads(B, H, heads)
+    outs, lses = [], []
+    for b, h in hl:
+        o, l_ = head_forward(q[b, h], k[b, h // G], v[b, h // G], scale, causal, block_mask, rows)
+        outs.append(o)
+        lses.append(l_)
+    o = np.stack(outs)
+    lse = np.stack(lses)
+    if heads is None:
+        R = o.shape[1]
+        return o.reshape(B, H, R, d), lse.reshape(B, H, R)
+    return o, lse
+
+
+def backward(q, k, v, do, scale, causal=False, block_mask=None, heads=None):
+    """Gradients of sum(O * dO) with respect to q, k, v.
+
+    With ``heads=None`` returns full dq [B, H, N, d], dk, dv [B, Hkv, N, d]
+    (dk, dv summed over each kv head's group of query heads). With a list of
+    (b, h) returns per-head arrays [nh, N, d]: dq and that query head's
+    contributions to dk and dv.
+    """
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if H % Hkv:
+        raise ValueError("H must be a multiple of Hkv")
+    G = H // Hkv
+    if heads is None:
+        dq = np.zeros_like(q)
+        dk = np.zeros_like(k)
+        dv = np.zeros_like(v)
+        for b in range(B):
+            for h in range(H):
+                a, bk, bv = head_backward(q[b, h], k[b, h // G], v[b, h // G], do[b, h],
+                                          scale, causal, block_mask)
+                dq[b, h] = a
+                dk[b, h // G] += bk
+                dv[b, h // G] += bv
+        return dq, dk, dv
+    res = [head_backward(q[b, h], k[b, h // G], v[b, h // G], do[b, h], scale, causal, block_mask)
+           for b, h in _heads(B, H, heads)]
+    return tuple(np.stack(x) for x in zip(*res))

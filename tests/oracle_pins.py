@@ -1,0 +1,443 @@
+"""Checks that pin the float64 oracle to facts that do not come from the oracle.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+what the pages or the mathematics fix. ``test_oracle.py`` runs them on the
+oracle as written; ``test_oracle_mutants.py`` plants plausible mistakes in the
+oracle (on the CPU) and checks that at least one pin fails for each.
+
+Sources, by page and section:
+* worked example: "FlashAttention" lesson (learn.pranaymahendrakar.com),
+  Developer tier, flash_numpy.py and its printed Output;
+* the online-softmax recurrence: same lesson, Researcher tier, "Online softmax"
+  (the equations for m, l and O and the final O / l);
+* O = softmax(Q K^T / sqrt(d)) V: same lesson, Researcher tier, "The problem
+  being solved";
+* causal = earlier words only: same lesson, Beginner tier, "What was broken
+  before"; block-sparse: nadeemcite summary, Key Method Details;
+* grouped-query attention: the lesson's related-term card "Grouped-query
+  attention".
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle.attention as A
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).normal(size=shape)
+
+
+# ----------------------------------------------------------------------------------------------
+# P-1: the lesson's worked example (this is the single-head fp32 workload)
+# ----------------------------------------------------------------------------------------------
+def page_inputs():
+    g = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    rng = np.random.default_rng(g["inputs"]["seed"])
+    n, d = g["N"], g["d"]
+    q = rng.normal(size=(n, d)).astype(np.float32)
+    k = rng.normal(size=(n, d)).astype(np.float32)
+    v = rng.normal(size=(n, d)).astype(np.float32)
+    return g, q, k, v
+
+
+def fp32_tiled_recurrence(q, k, v, scale, tile):
+    """The lesson's streaming update evaluated in float32, one key tile at a time.
+
+    Running max m, running sum of exponentials l and running unnormalised
+    output O; each tile rescales l and O by exp(m_old - m_new) before adding
+    its own terms; the result is O / l.
+    """
+    n = q.shape[0]
+    o = np.zeros_like(q)
+    m = np.full(n, -np.inf, dtype=np.float32)
+    l = np.zeros(n, dtype=np.float32)
+    for j in range(0, k.shape[0], tile):
+        s = (q @ k[j:j + tile].T) * scale
+        m_new = np.maximum(m, s.max(axis=1))
+        c = np.exp(m - m_new)
+        p = np.exp(s - m_new[:, None])
+        l = c * l + p.sum(axis=1)
+        o = c[:, None] * o + p @ v[j:j + tile]
+        m = m_new
+    return o / l[:, None]
+
+
+def pin_worked_example():
+    g, q, k, v = page_inputs()
+    pr = g["printed"]
+    n, d, tile = g["N"], g["d"], g["key_tile"]
+    # the shapes the page printed its buffer sizes for
+    assert n * n * 4 == pr["naive_score_bytes"]
+    assert n * tile * 4 == pr["tile_score_bytes"]
+    assert pr["naive_score_bytes"] // pr["tile_score_bytes"] == pr["ratio"]
+    for s, gb in pr["bf16_full_score_GB"].items():
+        assert round(int(s) ** 2 * 2 / 1e9, 2) == gb
+    scale = np.float32(1.0 / np.sqrt(d))      # float32 scale, as under NumPy 1.x
+    o64, lse = A.forward(q[None, None].astype(np.float64), k[None, None].astype(np.float64),
+                         v[None, None].astype(np.float64), float(scale))
+    o32 = fp32_tiled_recurrence(q, k, v, scale, tile)
+    diff = float(np.abs(o32 - o64[0, 0]).max())
+    # the page: allclose at 1e-5, largest difference of order 2.4e-7 (float32 rounding)
+    assert diff <= pr["outputs_match_allclose_atol"], diff
+    assert diff <= 10 * pr["largest_absolute_difference"], diff
+    assert np.all(np.isfinite(lse))
+
+
+# ----------------------------------------------------------------------------------------------
+# P-2: the streaming recurrence in float64 equals the definition for every key-tile width
+# ----------------------------------------------------------------------------------------------
+def recurrence64(q, k, v, scale, tile, causal=False, block_mask=None, block=128):
+    """The lesson's online-softmax equations in float64, with -inf for invisible keys.
+
+    A tile that leaves a row's running max at -inf contributes nothing; the
+    guard keeps exp(-inf - (-inf)) out of the arithmetic. Returns O / l and
+    the log-sum-exp m + ln l.
+    """
+    n = q.shape[0]
+    ii = np.arange(n)[:, None]
+    o = np.zeros_like(q)
+    m = np.full(n, -np.inf)
+    l = np.zeros(n)
+    for j in range(0, k.shape[0], tile):
+        jj = np.arange(j, min(j + tile, k.shape[0]))[None, :]
+        s = (q @ k[j:j + tile].T) * scale
+        ok = np.ones(s.shape, dtype=bool)
+        if causal:
+            ok &= jj <= ii
+        if block_mask is not None:
+            ok &= np.asarray(block_mask)[ii // block, jj // block] != 0
+        s = np.where(ok, s, -np.inf)
+        m_new = np.maximum(m, s.max(axis=1))
+        live = np.isfinite(m_new)
+        ref = np.where(live, m_new, 0.0)
+        c = np.where(live, np.exp(m - ref), 1.0)
+        p = np.exp(s - ref[:, None])
+        l = c * l + p.sum(axis=1)
+        o = c[:, None] * o + p @ v[j:j + tile]
+        m = m_new
+    with np.errstate(divide="ignore", invalid="ignore"):
+        out = np.where(l[:, None] > 0, o / np.where(l > 0, l, 1)[:, None], 0.0)
+        lse = np.where(l > 0, m + np.log(np.where(l > 0, l, 1)), -np.inf)
+    return out, lse
+
+
+def pin_recurrence():
+    n, d = 300, 8
+    q, k, v = _rand((n, d), 1), _rand((n, d), 2), _rand((n, d), 3)
+    mask = np.array([[1, 0, 1], [1, 1, 0], [0, 1, 1]], dtype=np.uint8)
+    for causal, bm in [(False, None), (True, None), (False, mask), (True, mask)]:
+        o_ref, l_ref = A.forward(q[None, None], k[None, None], v[None, None], 0.3, causal, bm)
+        for tile in (1, 16, 128, 512):
+            o, l_ = recurrence64(q, k, v, 0.3, tile, causal, bm)
+            assert np.abs(o - o_ref[0, 0]).max() <= 1e-12, (causal, tile)
+            assert np.abs(l_ - l_ref[0, 0]).max() <= 1e-12, (causal, tile)
+
+
+# ----------------------------------------------------------------------------------------------
+# P-3: brute force with scalar loops on tiny inputs, and the two-key closed form
+# ----------------------------------------------------------------------------------------------
+def brute_force(q, k, v, scale, causal):
+    n, d = len(q), len(q[0])
+    dv = len(v[0])
+    outs, lses = [], []
+    for i in range(n):
+        keys = [j for j in range(len(k)) if (not causal or j <= i)]
+        sc = [scale * sum(q[i][t] * k[j][t] for t in range(d)) for j in keys]
+        mx = max(sc)
+        w = [math.exp(s - mx) for s in sc]
+        z = sum(w)
+        outs.append([sum(w[a] * v[j][t] for a, j in enumerate(keys)) / z for t in range(dv)])
+        lses.append(mx + math.log(z))
+    return np.array(outs), np.array(lses)
+
+
+def pin_brute_force():
+    seed = 10
+    for n in (1, 2, 3, 4):
+        for d in (1, 2, 3):
+            for causal in (False, True):
+                seed += 1
+                q, k, v = _rand((n, d), seed), _rand((n, d), seed + 100), _rand((n, d), seed + 200)
+                o, l_ = A.forward(q[None, None], k[None, None], v[None, None], 0.7, causal)
+                ob, lb = brute_force(q.tolist(), k.tolist(), v.tolist(), 0.7, causal)
+                assert np.abs(o[0, 0] - ob).max() <= 1e-12, (n, d, causal)
+                assert np.abs(l_[0, 0] - lb).max() <= 1e-12, (n, d, causal)
+    # two keys: o_0 = sigma(s00 - s01) v_0 + (1 - sigma) v_1, L = log(e^s00 + e^s01)
+    q, k, v = _rand((2, 3), 77), _rand((2, 3), 78), _rand((2, 3), 79)
+    o, l_ = A.forward(q[None, None], k[None, None], v[None, None], 0.5)
+    s00, s01 = 0.5 * q[0] @ k[0], 0.5 * q[0] @ k[1]
+    sig = 1.0 / (1.0 + math.exp(-(s00 - s01)))
+    assert np.abs(o[0, 0, 0] - (sig * v[0] + (1 - sig) * v[1])).max() <= 1e-14
+    assert abs(l_[0, 0, 0] - math.log(math.exp(s00) + math.exp(s01))) <= 1e-14
+
+
+# ----------------------------------------------------------------------------------------------
+# P-4: probability rows sum to one; invisible keys carry exactly zero
+# ----------------------------------------------------------------------------------------------
+def pin_rows_sum_to_one():
+    n, d = 260, 8
+    q, k = _rand((n, d), 5), _rand((n, d), 6)
+    mask = np.array([[1, 0, 0], [1, 1, 0], [1, 0, 1]], dtype=np.uint8)
+    for causal, bm in [(False, None), (True, None), (False, mask), (True, mask)]:
+        p, _ = A.head_probabilities(q, k, 0.4, causal, bm)
+        assert np.abs(p.sum(axis=1) - 1).max() <= 1e-14
+        vis = A.visible(np.arange(n), np.arange(n), causal, bm)
+        assert np.all(p[~vis] == 0)
+        assert np.all(p[vis] > 0)
+
+
+# ----------------------------------------------------------------------------------------------
+# P-5: Q = 0 gives the mean of the visible values and L = ln(#visible)
+# ----------------------------------------------------------------------------------------------
+def pin_zero_query():
+    n, d = 300, 4
+    q = np.zeros((n, d))
+    k, v = _rand((n, d), 8), _rand((n, d), 9)
+    mask = np.array([[1, 0, 1], [0, 1, 0], [1, 1, 1]], dtype=np.uint8)
+    for causal, bm in [(False, None), (True, None), (False, mask), (True, mask)]:
+        o, l_ = A.forward(q[None, None], k[None, None], v[None, None], 0.5, causal, bm)
+        for i in range(n):
+            keys = [j for j in range(n) if (not causal or j <= i)
+                    and (bm is None or bm[i // 128][j // 128])]
+            assert np.abs(o[0, 0, i] - v[keys].mean(axis=0)).max() <= 1e-13
+            assert abs(l_[0, 0, i] - math.log(len(keys))) <= 1e-13
+    # causal, dense: row i is the prefix mean
+    o, _ = A.forward(q[None, None], k[None, None], v[None, None], 0.5, True)
+    pref = np.cumsum(v, axis=0) / np.arange(1, n + 1)[:, None]
+    assert np.abs(o[0, 0] - pref).max() <= 1e-13
+
+
+# ----------------------------------------------------------------------------------------------
+# P-6: one dominant score drags the output row onto that key's value row
+# ----------------------------------------------------------------------------------------------
+def pin_dominant_score():
+    n, d = 64, 16
+    q, k, v = _rand((n, d), 11), _rand((n, d), 12), _rand((n, d), 13)
+    scale = 0.25
+    for i, jstar, c in [(5, 40, 3.0), (20, 3, 6.0), (63, 0, 10.0)]:
+        kk = k.copy()
+        kk[jstar] = c * q[i]
+        s = scale * (q[i] @ kk.T)
+        gap = s[jstar] - np.max(np.delete(s, jstar))
+        assert gap > 2
+        o, _ = A.forward(q[None, None], kk[None, None], v[None, None], scale)
+        bound = 2 * (n - 1) * math.exp(-gap) * np.abs(v).max()
+        assert np.abs(o[0, 0, i] - v[jstar]).max() <= bound
+
+
+# ----------------------------------------------------------------------------------------------
+# P-7: permutation equivariance (non-causal, dense)
+# ----------------------------------------------------------------------------------------------
+def pin_permutation():
+    n, d = 200, 8
+    q, k, v, g = (_rand((1, 1, n, d), s) for s in (21, 22, 23, 24))
+    perm = np.random.default_rng(25).permutation(n)
+    o, l_ = A.forward(q, k, v, 0.3)
+    dq, dk, dv = A.backward(q, k, v, g, 0.3)
+    o2, l2 = A.forward(q, k[:, :, perm], v[:, :, perm], 0.3)
+    assert np.abs(o2 - o).max() <= 1e-13 and np.abs(l2 - l_).max() <= 1e-13
+    dq2, dk2, dv2 = A.backward(q, k[:, :, perm], v[:, :, perm], g, 0.3)
+    assert np.abs(dq2 - dq).max() <= 1e-13
+    assert np.abs(dk2 - dk[:, :, perm]).max() <= 1e-13
+    assert np.abs(dv2 - dv[:, :, perm]).max() <= 1e-13
+    o3, l3 = A.forward(q[:, :, perm], k, v, 0.3)
+    assert np.abs(o3 - o[:, :, perm]).max() <= 1e-13 and np.abs(l3 - l_[:, :, perm]).max() <= 1e-13
+    dq3, dk3, dv3 = A.backward(q[:, :, perm], k, v, g[:, :, perm], 0.3)
+    assert np.abs(dq3 - dq[:, :, perm]).max() <= 1e-13
+    assert np.abs(dk3 - dk).max() <= 1e-13 and np.abs(dv3 - dv).max() <= 1e-13
+
+
+# ----------------------------------------------------------------------------------------------
+# P-8: causal rows depend only on earlier keys; row 0 sees only key 0
+# ----------------------------------------------------------------------------------------------
+def pin_causal_locality():
+    n, d = 300, 8
+    q, k, v = (_rand((1, 1, n, d), s) for s in (31, 32, 33))
+    o, l_ = A.forward(q, k, v, 0.5, True)
+    for i0 in (0, 17, 127, 128, 250):
+        k2, v2 = k.copy(), v.copy()
+        k2[0, 0, i0 + 1:] += _rand((n - i0 - 1, d), i0)
+        v2[0, 0, i0 + 1:] -= 3.0
+        o2, l2 = A.forward(q, k2, v2, 0.5, True)
+        assert np.array_equal(o2[0, 0, :i0 + 1], o[0, 0, :i0 + 1])
+        assert np.array_equal(l2[0, 0, :i0 + 1], l_[0, 0, :i0 + 1])
+    assert np.abs(o[0, 0, 0] - v[0, 0, 0]).max() <= 1e-15
+    assert abs(l_[0, 0, 0] - 0.5 * q[0, 0, 0] @ k[0, 0, 0]) <= 1e-14
+
+
+# ----------------------------------------------------------------------------------------------
+# P-9: analytic gradients against central finite differences of f = sum(O * dO)
+# ----------------------------------------------------------------------------------------------
+def _fd_case(B, H, Hkv, n, d, causal, bm, seed, ncoord=24, h=1e-6):
+    q = _rand((B, H, n, d), seed)
+    k = _rand((B, Hkv, n, d), seed + 1)
+    v = _rand((B, Hkv, n, d), seed + 2)
+    g = _rand((B, H, n, d), seed + 3)
+    scale = 0.6
+
+    def f(q_, k_, v_):
+        o, _ = A.forward(q_, k_, v_, scale, causal, bm)
+        return float((o * g).sum())
+
+    grads = A.backward(q, k, v, g, scale, causal, bm)
+    rng = np.random.default_rng(seed + 4)
+    for which, x in enumerate((q, k, v)):
+        num, ana = [], []
+        for flat in rng.choice(x.size, size=min(ncoord, x.size), replace=False):
+            idx = np.unravel_index(flat, x.shape)
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[which], args_m[which] = xp, xm
+            num.append((f(*args_p) - f(*args_m)) / (2 * h))
+            ana.append(grads[which][idx])
+        num, ana = np.array(num), np.array(ana)
+        err = np.abs(num - ana).max() / max(np.abs(ana).max(), 1e-3)
+        assert err <= 1e-6, ("qkv"[which], err)
+
+
+def pin_finite_differences():
+    _fd_case(1, 1, 1, 12, 4, False, None, 40)
+    _fd_case(1, 2, 2, 12, 4, True, None, 50)
+    _fd_case(2, 4, 2, 10, 3, True, None, 60)                       # grouped-query
+    mask = np.array([[1, 0], [1, 1]], dtype=np.uint8)
+    _fd_case(1, 2, 1, 140, 2, False, mask, 70, ncoord=16)          # block mask, 2 blocks
+
+
+# ----------------------------------------------------------------------------------------------
+# P-10: grouped-query attention equals attention with K, V repeated per query head
+# ----------------------------------------------------------------------------------------------
+def pin_gqa_repeat():
+    B, H, Hkv, n, d = 2, 6, 2, 50, 4
+    q = _rand((B, H, n, d), 91)
+    k, v = _rand((B, Hkv, n, d), 92), _rand((B, Hkv, n, d), 93)
+    g = _rand((B, H, n, d), 94)
+    G = H // Hkv
+    kr, vr = np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)
+    for causal in (False, True):
+        o, l_ = A.forward(q, k, v, 0.5, causal)
+        o2, l2 = A.forward(q, kr, vr, 0.5, causal)
+        assert np.abs(o - o2).max() <= 1e-14 and np.abs(l_ - l2).max() <= 1e-14
+        dq, dk, dv = A.backward(q, k, v, g, 0.5, causal)
+        dq2, dk2, dv2 = A.backward(q, kr, vr, g, 0.5, causal)
+        assert np.abs(dq - dq2).max() <= 1e-13
+        assert np.abs(dk - dk2.reshape(B, Hkv, G, n, d).sum(2)).max() <= 1e-13
+        assert np.abs(dv - dv2.reshape(B, Hkv, G, n, d).sum(2)).max() <= 1e-13
+    # subset API: per-head contributions add up to the full kv-head gradient
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    dqs, dks, dvs = A.backward(q, k, v, g, 0.5, True, None, heads)
+    dq, dk, dv = A.backward(q, k, v, g, 0.5, True)
+    for t, (b, h) in enumerate(heads):
+        assert np.abs(dqs[t] - dq[b, h]).max() <= 1e-13
+    assert np.abs(dks.reshape(B, Hkv, G, n, d).sum(2) - dk).max() <= 1e-13
+    assert np.abs(dvs.reshape(B, Hkv, G, n, d).sum(2) - dv).max() <= 1e-13
+
+
+# ----------------------------------------------------------------------------------------------
+# P-11: block-mask semantics
+# ----------------------------------------------------------------------------------------------
+def pin_mask_semantics():
+    n, d = 300, 4
+    q, k, v = (_rand((1, 1, n, d), s) for s in (101, 102, 103))
+    g = _rand((1, 1, n, d), 104)
+    nb = 3
+    ones = np.ones((nb, nb), dtype=np.uint8)
+    o, l_ = A.forward(q, k, v, 0.5, False)
+    o1, l1 = A.forward(q, k, v, 0.5, False, ones)
+    assert np.array_equal(o, o1) and np.array_equal(l_, l1)
+    tril = np.tril(ones)
+    oc, lc = A.forward(q, k, v, 0.5, True)
+    oc2, lc2 = A.forward(q, k, v, 0.5, True, tril)
+    assert np.array_equal(oc, oc2) and np.array_equal(lc, lc2)
+    # against an explicit N x N additive mask built element by element
+    from scipy.special import logsumexp, softmax
+    bm = np.array([[1, 0, 1], [0, 0, 1], [1, 1, 0]], dtype=np.uint8)
+    full = np.zeros((n, n))
+    for i in range(n):
+        for j in range(n):
+            if not bm[i // 128][j // 128]:
+                full[i, j] = -np.inf
+    s = 0.5 * q[0, 0] @ k[0, 0].T + full
+    om, lm = A.forward(q, k, v, 0.5, False, bm)
+    assert np.abs(om[0, 0] - softmax(s, axis=1) @ v[0, 0]).max() <= 1e-13
+    assert np.abs(lm[0, 0] - logsumexp(s, axis=1)).max() <= 1e-13
+    # gradients against the same explicit mask through torch autograd
+    import torch
+    tq, tk, tv = (torch.tensor(x[0, 0], requires_grad=True) for x in (q, k, v))
+    ts = 0.5 * tq @ tk.T + torch.tensor(full)
+    to = torch.softmax(ts, dim=1) @ tv
+    to.backward(torch.tensor(g[0, 0]))
+    dq, dk, dv = A.backward(q, k, v, g, 0.5, False, bm)
+    for a, b in ((dq, tq), (dk, tk), (dv, tv)):
+        assert np.abs(a[0, 0] - b.grad.numpy()).max() <= 1e-12
+
+
+def pin_empty_rows():
+    """A row that sees no key: O = 0, L = -inf, zero gradients, no contribution."""
+    n, d = 300, 4
+    q, k, v, g = (_rand((1, 1, n, d), s) for s in (111, 112, 113, 114))
+    bm = np.array([[1, 0, 0], [0, 0, 0], [1, 1, 1]], dtype=np.uint8)   # block row 1 empty
+    o, l_ = A.forward(q, k, v, 0.5, False, bm)
+    assert np.all(o[0, 0, 128:256] == 0) and np.all(np.isneginf(l_[0, 0, 128:256]))
+    assert np.all(np.isfinite(l_[0, 0, :128])) and np.all(np.isfinite(l_[0, 0, 256:]))
+    dq, dk, dv = A.backward(q, k, v, g, 0.5, False, bm)
+    assert np.all(dq[0, 0, 128:256] == 0)
+    g2 = g.copy()
+    g2[0, 0, 128:256] = 1e3             # upstream gradient on empty rows must not leak
+    dq2, dk2, dv2 = A.backward(q, k, v, g2, 0.5, False, bm)
+    assert np.array_equal(dk, dk2) and np.array_equal(dv, dv2)
+
+
+# ----------------------------------------------------------------------------------------------
+# P-12: scale 0 gives uniform weights
+# ----------------------------------------------------------------------------------------------
+def pin_scale_zero():
+    n, d = 100, 5
+    q, k, v = (_rand((1, 1, n, d), s) for s in (121, 122, 123))
+    for causal in (False, True):
+        o, l_ = A.forward(q, k, v, 0.0, causal)
+        cnt = np.arange(1, n + 1) if causal else np.full(n, n)
+        ref = np.cumsum(v[0, 0], axis=0) / cnt[:, None] if causal else np.tile(v[0, 0].mean(0), (n, 1))
+        assert np.abs(o[0, 0] - ref).max() <= 1e-13
+        assert np.abs(l_[0, 0] - np.log(cnt)).max() <= 1e-13
+
+
+# ----------------------------------------------------------------------------------------------
+# Library cross-check: PyTorch's float64 CPU attention (math path) and autograd
+# ----------------------------------------------------------------------------------------------
+def pin_torch_sdpa():
+    import torch
+    import torch.nn.functional as F
+    for (B, H, Hkv, n, d, causal, seed) in [(2, 4, 4, 130, 16, False, 131), (2, 4, 4, 130, 16, True, 132),
+                                            (1, 8, 2, 70, 8, True, 133), (1, 3, 1, 33, 32, False, 134)]:
+        q, k, v = _rand((B, H, n, d), seed), _rand((B, Hkv, n, d), seed + 1), _rand((B, Hkv, n, d), seed + 2)
+        g = _rand((B, H, n, d), seed + 3)
+        scale = 1.0 / math.sqrt(d)
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        to = F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale, enable_gqa=Hkv != H)
+        to.backward(torch.tensor(g))
+        o, l_ = A.forward(q, k, v, scale, causal)
+        dq, dk, dv = A.backward(q, k, v, g, scale, causal)
+        assert np.abs(o - to.detach().numpy()).max() <= 1e-12
+        assert np.abs(dq - tq.grad.numpy()).max() <= 1e-12
+        assert np.abs(dk - tk.grad.numpy()).max() <= 1e-12
+        assert np.abs(dv - tv.grad.numpy()).max() <= 1e-12
+        # log-sum-exp against torch.logsumexp of the masked scaled scores
+        G = H // Hkv
+        s = torch.tensor(q) @ torch.tensor(np.repeat(k, G, axis=1)).transpose(-1, -2) * scale
+        if causal:
+            s = s.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), float("-inf"))
+        assert np.abs(l_ - torch.logsumexp(s, dim=-1).numpy()).max() <= 1e-12
+
+
+ALL_PINS = [pin_worked_example, pin_recurrence, pin_brute_force, pin_rows_sum_to_one, pin_zero_query,
+            pin_dominant_score, pin_permutation, pin_causal_locality, pin_finite_differences,
+            pin_gqa_repeat, pin_mask_semantics, pin_empty_rows, pin_scale_zero, pin_torch_sdpa]

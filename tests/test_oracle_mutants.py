@@ -1,0 +1,60 @@
+"""Plant plausible mistakes in a copy of the oracle and check that a pin catches each.
+
+Each mutant is the oracle's source with one textual edit, loaded as a separate
+module on the CPU; the pins in ``oracle_pins`` are then run against it. A
+mutant that every pin accepts would mean the pins leave that part of the
+oracle unchecked.
+"""
+
+import importlib.util
+import os
+import types
+
+import pytest
+
+import oracle_pins as P
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "attention.py")
+
+MUTANTS = {
+    "causal_strict": ("a &= keys[None, :] <= rows[:, None]", "a &= keys[None, :] < rows[:, None]"),
+    "causal_reversed": ("a &= keys[None, :] <= rows[:, None]", "a &= keys[None, :] >= rows[:, None]"),
+    "mask_transposed": ("bm[(rows // block)[:, None], (keys // block)[None, :]]",
+                        "bm[(keys // block)[None, :], (rows // block)[:, None]]"),
+    "scale_dropped": ("s = scale * (q_rows @ k_keys.T)", "s = q_rows @ k_keys.T"),
+    "lse_without_max": ("m0 + np.log(np.where(has, ssum, 1.0))", "np.log(np.where(has, ssum, 1.0))"),
+    "output_uses_keys": ("o[pos:pos + ch.size] = p @ v[keys]", "o[pos:pos + ch.size] = p @ k[keys]"),
+    "dv_wrong_operand": ("dv[keys] += p.T @ g", "dv[keys] += p.T @ q[ch]"),
+    "ds_sign": ("ds = p * (dp - dd[:, None])", "ds = p * (dp + dd[:, None])"),
+    "ds_drops_p": ("ds = p * (dp - dd[:, None])", "ds = (dp - dd[:, None])"),
+    "dd_drops_p": ("dd = (p * dp).sum(axis=1)", "dd = dp.sum(axis=1)"),
+    "dk_missing_scale": ("dk[keys] += scale * (ds.T @ q[ch])", "dk[keys] += ds.T @ q[ch]"),
+    "dq_transposed_keys": ("dq[ch] = scale * (ds @ k[keys])", "dq[ch] = scale * (ds @ v[keys])"),
+    "gqa_modulo": ("o, l_ = head_forward(q[b, h], k[b, h // G], v[b, h // G]",
+                   "o, l_ = head_forward(q[b, h], k[b, h % Hkv], v[b, h % Hkv]"),
+    "gqa_backward_modulo": ("dk[b, h // G] += bk", "dk[b, h % Hkv] += bk"),
+    "candidate_keys_short": ("keys = keys[keys <= rows.max()]", "keys = keys[keys < rows.max()]"),
+}
+
+
+def _load_mutant(old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, old
+    src = src.replace(old, new)
+    mod = types.ModuleType("oracle_mutant")
+    mod.__file__ = SRC
+    exec(compile(src, SRC + " (mutant)", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    mod = _load_mutant(*MUTANTS[name])
+    monkeypatch.setattr(P, "A", mod)
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            pin()
+        except Exception:          # an assertion or a crash both expose the mistake
+            caught.append(pin.__name__)
+    assert caught, f"no pin detects mutant {name}"
