@@ -1,0 +1,153 @@
+"""Thin Python binding of the C-ABI attention library ``libfa.so``.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind ``fa_forward`` / ``fa_backward``. PyTorch supplies device memory
+(outputs and workspace are allocated with torch on the inputs' device) and the
+current stream. There is no fallback: if the library is missing or a call
+fails, an exception is raised.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfa.so")
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+MASK_BLOCK = 128
+_DTYPES = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    """A nonzero status returned by the library."""
+
+    def __init__(self, status, where):
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def load():
+    """Load libfa.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m exact_attention_110_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_forward.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, I, P]
+    lib.fa_forward.restype = I
+    lib.fa_backward_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.fa_backward_workspace_size.restype = S
+    bw = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, P, I, P, S, P]
+    lib.fa_backward.argtypes = bw
+    lib.fa_backward.restype = I
+    lib.fa_backward_stage.argtypes = [I] + bw
+    lib.fa_backward_stage.restype = I
+    lib.fa_status_string.argtypes = [I]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = I
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load().fa_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _shape(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d] / [B, Hkv, N, d]")
+    B, H, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be a contiguous device tensor of dtype {q.dtype}")
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    return B, H, k.shape[1], N, d
+
+
+def _mask(block_mask, N, device):
+    if block_mask is None:
+        return None
+    nb = -(-N // MASK_BLOCK)
+    if not isinstance(block_mask, torch.Tensor):
+        block_mask = torch.as_tensor(block_mask)
+    if tuple(block_mask.shape) != (nb, nb) or block_mask.dtype != torch.uint8:
+        raise ValueError(f"block_mask must be uint8 [{nb}, {nb}]")
+    return block_mask.to(device).contiguous()
+
+
+def forward(q, k, v, scale=None, causal=False, block_mask=None, out=None, lse=None):
+    """O, LSE = attention(q, k, v); q [B,H,N,d], k, v [B,Hkv,N,d] on the GPU."""
+    B, H, Hkv, N, d = _shape(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    m = _mask(block_mask, N, q.device)
+    st = load().fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, Hkv, N, d, scale,
+                           int(bool(causal)), _ptr(m), _DTYPES[q.dtype], _stream(q.device))
+    if st != 0:
+        raise FAError(st, "fa_forward")
+    return o, lse_t
+
+
+def workspace_size(B, H, Hkv, N, d, dtype):
+    return int(load().fa_backward_workspace_size(B, H, Hkv, N, d, _DTYPES[dtype]))
+
+
+def workspace(q, k):
+    B, H, N, d = q.shape
+    n = workspace_size(B, H, k.shape[1], N, d, q.dtype)
+    if n == 0:
+        raise ValueError("no backward for these arguments")
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
+def _bwd_args(q, k, v, o, lse, do, dq, dk, dv, scale, causal, m, ws):
+    B, H, Hkv, N, d = _shape(q, k, v)
+    return [_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+            B, H, Hkv, N, d, scale, int(bool(causal)), _ptr(m), _DTYPES[q.dtype], _ptr(ws),
+            ws.numel(), _stream(q.device)]
+
+
+def backward(q, k, v, o, lse, do, scale=None, causal=False, block_mask=None, ws=None, grads=None):
+    """dq, dk, dv of sum(O * do), recomputing P from q, k and lse."""
+    B, H, Hkv, N, d = _shape(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    for name, t in (("o", o), ("do", do)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must match q")
+    m = _mask(block_mask, N, q.device)
+    ws = workspace(q, k) if ws is None else ws
+    dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    st = load().fa_backward(*_bwd_args(q, k, v, o, lse, do, dq, dk, dv, scale, causal, m, ws))
+    if st != 0:
+        raise FAError(st, "fa_backward")
+    return dq, dk, dv
+
+
+def backward_stage(stage, q, k, v, o, lse, do, dq, dk, dv, ws, scale=None, causal=False, block_mask=None):
+    """Run one stage (0, 1 or 2) of the backward pass; see fa_backward_stage."""
+    d = q.shape[3]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    m = _mask(block_mask, q.shape[2], q.device)
+    st = load().fa_backward_stage(int(stage), *_bwd_args(q, k, v, o, lse, do, dq, dk, dv, scale, causal, m, ws))
+    if st != 0:
+        raise FAError(st, f"fa_backward_stage({stage})")

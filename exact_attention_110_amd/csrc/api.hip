@@ -1,0 +1,153 @@
+// C-ABI entry points of the attention library (declared in include/fa.h).
+// Every argument is validated before the HIP runtime is touched; on success
+// the kernels are enqueued on the caller's stream and the call returns.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "params.hpp"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape checks shared by every entry point. Sizes must keep per-head offsets
+// and row counts inside 32-bit signed range and fit the launch grid.
+int check_shape(int B, int H, int Hkv, int N, int d, float scale, int dtype) {
+  if (B < 1 || H < 1 || Hkv < 1 || N < 1) return FA_ERR_INVALID_ARG;
+  if (H % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (d != 32 && d != 64 && d != 128) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
+  const long long rows = (long long)B * H * N;
+  if (rows > INT32_MAX || (long long)N * d > INT32_MAX) return FA_ERR_INVALID_ARG;
+  if (B > 65535 || (N + 127) / 128 > 65535) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+fa::AttnShape make_shape(int B, int H, int Hkv, int N, int d, float scale, int causal,
+                         const uint8_t* mask) {
+  fa::AttnShape s;
+  s.B = B;
+  s.H = H;
+  s.Hkv = Hkv;
+  s.N = N;
+  s.d = d;
+  s.G = H / Hkv;
+  s.scale = scale;
+  s.causal = causal != 0;
+  s.mask = mask;
+  s.nb = (N + 127) / 128;
+  return s;
+}
+
+// Block masks are compacted per row / column in LDS lists of 2048 entries.
+constexpr int kMaxMaskBlocks = 2048;
+
+size_t dvec_bytes(int B, int H, int N) { return round_up((size_t)B * H * N * sizeof(float)); }
+size_t dqacc_bytes(int B, int H, int N, int d) {
+  return round_up((size_t)B * H * N * d * sizeof(float));
+}
+
+int check_backward(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N,
+                   int d, float scale, const uint8_t* block_mask, int dtype, void* workspace,
+                   size_t workspace_bytes) {
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3u))
+    return FA_ERR_INVALID_ARG;
+  int st = check_shape(B, H, Hkv, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (block_mask && (N + 127) / 128 > kMaxMaskBlocks) return FA_ERR_UNSUPPORTED;
+  if (!workspace || ((uintptr_t)workspace % kAlign) != 0) return FA_ERR_WORKSPACE;
+  if (workspace_bytes < dvec_bytes(B, H, N) + dqacc_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int Hkv, int N, int d, float scale, int causal, const uint8_t* block_mask,
+               int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u))
+    return FA_ERR_INVALID_ARG;
+  int st = check_shape(B, H, Hkv, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (block_mask && (N + 127) / 128 > kMaxMaskBlocks) return FA_ERR_UNSUPPORTED;
+  fa::FwdArgs a;
+  a.s = make_shape(B, H, Hkv, N, d, scale, causal, block_mask);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  (void)hipGetLastError();  // clear a stale error so the check below sees only this launch
+  return fa::launch_forward(a, dtype, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_backward_workspace_size(int B, int H, int Hkv, int N, int d, int dtype) {
+  if (check_shape(B, H, Hkv, N, d, 1.0f, dtype) != FA_OK || dtype == FA_F32) return 0;
+  return dvec_bytes(B, H, N) + dqacc_bytes(B, H, N, d);
+}
+
+int fa_backward_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H,
+                      int Hkv, int N, int d, float scale, int causal, const uint8_t* block_mask,
+                      int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (stage < 0 || stage > 2) return FA_ERR_INVALID_ARG;
+  int st = check_backward(q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, N, d, scale, block_mask,
+                          dtype, workspace, workspace_bytes);
+  if (st != FA_OK) return st;
+  fa::BwdArgs a;
+  a.s = make_shape(B, H, Hkv, N, d, scale, causal, block_mask);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dO = dO;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dvec = (float*)workspace;
+  a.dqacc = (float*)((char*)workspace + dvec_bytes(B, H, N));
+  (void)hipGetLastError();
+  return fa::launch_backward_stage(stage, a, dtype, (hipStream_t)stream) == hipSuccess ? FA_OK
+                                                                                        : FA_ERR_HIP;
+}
+
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
+                float scale, int causal, const uint8_t* block_mask, int dtype, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  for (int stage = 0; stage < 3; ++stage) {
+    int st = fa_backward_stage(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, N, d, scale,
+                               causal, block_mask, dtype, workspace, workspace_bytes, stream);
+    if (st != FA_OK) return st;
+  }
+  return FA_OK;
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case FA_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int fa_version(void) { return 100; }
+
+}  // extern "C"

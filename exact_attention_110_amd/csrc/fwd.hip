@@ -1,0 +1,374 @@
+// Forward pass of IO-aware exact attention on gfx950.
+//
+// One workgroup owns a block of 128 query rows of one (batch, head) and
+// streams the visible key/value tiles of its kv head through LDS, keeping the
+// running row maximum m, the running sum l of exponentials and the unnormalised
+// output in registers; whenever m grows the earlier partial sums are rescaled
+// by exp(m_old - m_new). This is the online-softmax recurrence of the
+// pranaymahendrakar.com lesson "FlashAttention" (Researcher tier, "Online
+// softmax"); the output is O / l and the saved statistic is m + ln(l).
+//
+// gfx950 mapping (16-bit inputs):
+//  * 4 waves x 32 query rows. Each wave computes S^T = K Q^T for a 64-key tile
+//    with v_mfma_f32_32x32x16 (Q^T is the B operand and stays in registers).
+//    In the 32x32 result layout a lane owns one query column, so the row
+//    maximum needs one cross-half exchange (permlane32 swap) and the row sum
+//    none until the end.
+//  * The probabilities, converted to 16 bits, are already laid out as the B
+//    operand of O^T = V^T P^T. The matching V^T operand comes from LDS with the
+//    gfx950 transposing read ds_read_b64_tr_b16, so V needs no transpose pass.
+//  * K and V tiles are double-buffered in LDS with a register-staged prefetch
+//    of the next tile; row pitches are padded so that the 16-byte row reads
+//    of K and the transposing reads of V are free of bank conflicts.
+//  * Causal: a workgroup stops at its diagonal tile, waves skip tiles that lie
+//    wholly after their rows, and only diagonal and tail tiles are masked
+//    element by element. Heaviest query blocks are launched first.
+//  * Block-sparse: the nonzero 128-key blocks of the workgroup's mask row are
+//    compacted into an LDS list first; zero blocks are never loaded.
+//  * Grouped-query: query head h reads kv head h / (H / Hkv).
+//
+// float32 inputs take a separate VALU kernel (fp32 FMA throughout) that runs
+// the same recurrence one query row per lane.
+#include "common.hpp"
+#include "params.hpp"
+
+namespace fa {
+
+constexpr int FWD_NW = 4;             // waves per workgroup
+constexpr int FWD_BM = 32 * FWD_NW;   // query rows per workgroup (= mask block)
+constexpr int FWD_BN = 64;            // keys per tile
+constexpr int FWD_LIST = 2048;        // capacity of the compacted mask-block list
+static_assert(FWD_BM == 128, "a forward workgroup must cover exactly one mask block row");
+
+template <class T, int D, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
+  constexpr int KP = D * 2 + 16;  // K row pitch in LDS, bytes (16 mod 128: conflict-free 16-byte reads)
+  constexpr int VP = D * 2 + 32;  // V row pitch in LDS, bytes (32 mod 128: conflict-free transposing reads)
+  constexpr int KBUF = FWD_BN * KP;
+  constexpr int VBUF = FWD_BN * VP;
+  constexpr int CH = D / 8;                            // 16-byte chunks per row
+  constexpr int PER = FWD_BN * CH / (FWD_NW * 64);     // chunks per thread per tensor per tile
+  static_assert(PER >= 1 && (FWD_BN * CH) % (FWD_NW * 64) == 0, "tile loader shape");
+  constexpr int NS = D / 16;  // k-steps of Q K^T
+  constexpr int ND = D / 32;  // 32-wide d tiles of the output
+
+  __shared__ __attribute__((aligned(16))) char smem_raw[2 * KBUF + 2 * VBUF + (MASK ? 2 * FWD_LIST + 16 : 16)];
+  lds_t* smem = (lds_t*)smem_raw;
+  lds_t* kbuf = smem;
+  lds_t* vbuf = smem + 2 * KBUF;
+  __attribute__((address_space(3))) short* blist =
+      (__attribute__((address_space(3))) short*)(smem + 2 * KBUF + 2 * VBUF);
+  __attribute__((address_space(3))) int* bcount =
+      (__attribute__((address_space(3))) int*)(smem + 2 * KBUF + 2 * VBUF + (MASK ? 2 * FWD_LIST : 0));
+
+  const AttnShape& s = a.s;
+  const int N = s.N;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  // grid = (H, query blocks, B): consecutive workgroups take different heads, so
+  // the round-robin spread over the 8 XCDs keeps each head on one XCD's L2;
+  // under causal masking the longest query blocks are dispatched first
+  const int qb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+  const int h = blockIdx.x, b = blockIdx.z;
+  const int hk = h / s.G;
+  const size_t qrow0 = (size_t)(b * s.H + h) * N;
+  const size_t krow0 = (size_t)(b * s.Hkv + hk) * N;
+  const unsigned short* Q = (const unsigned short*)a.q + qrow0 * D;
+  const unsigned short* K = (const unsigned short*)a.k + krow0 * D;
+  const unsigned short* V = (const unsigned short*)a.v + krow0 * D;
+  const int q0 = qb * FWD_BM;
+  const int qw = q0 + 32 * w;   // first query row of this wave
+  const int qi = qw + l32;      // query row of this lane's column
+  // exponent scale: S * c is the score in log2 units; a zero scale is kept just
+  // above zero so that masked entries stay -inf (-inf * 0 would be NaN)
+  const float c = fmaxf(s.scale * kLog2e, 1e-30f);
+
+  const int kend = CAUSAL ? min(N, q0 + FWD_BM) : N;
+  const int ntile_all = (kend + FWD_BN - 1) / FWD_BN;
+  int ntiles = ntile_all;
+  if constexpr (MASK) {
+    const int nbk = (kend + 127) / 128;
+    if (w == 0) {
+      int cnt = 0;
+      for (int j0 = 0; j0 < nbk; j0 += 64) {
+        const int j = j0 + lane;
+        const bool keep = j < nbk && s.mask[(size_t)qb * s.nb + j] != 0;
+        const unsigned long long bal = __ballot(keep);
+        if (keep) blist[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (short)j;
+        cnt += __popcll(bal);
+      }
+      if (lane == 0) *bcount = cnt;
+    }
+    __syncthreads();
+    const int cnt = *bcount;
+    ntiles = 2 * cnt;
+    if (cnt > 0 && 2 * blist[cnt - 1] + 1 >= ntile_all) ntiles -= 1;  // half block past kend
+  }
+  auto tile_at = [&](int e) -> int {
+    if constexpr (MASK) return 2 * blist[e >> 1] + (e & 1);
+    else return e;
+  };
+
+  // Q^T operand: lane holds query qi, d = 16 * ss + 8 * hh + 0..7
+  s16x8 qf[NS];
+#pragma unroll
+  for (int ss = 0; ss < NS; ++ss) {
+    if (qi < N) qf[ss] = gload16(Q + (size_t)qi * D + 16 * ss + 8 * hh);
+    else qf[ss] = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
+  }
+
+  f32x16 acc[ND];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+  float m = -INFINITY;  // running maximum of S * c over the keys seen
+  float l = 0.f;        // this lane's share of the running sum (its half of the keys)
+
+  // lane offsets for the transposing V reads (row = key, column = d)
+  const int g16 = lane >> 4;
+  const int roff = 4 * (g16 >> 1) + ((lane & 15) >> 2);
+  const int coff = 16 * (g16 & 1) + 4 * (lane & 3);
+
+  s16x8 kreg[PER], vreg[PER];
+  auto gload_tile = [&](int t) {
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int ci = tid + r * (FWD_NW * 64);
+      const int row = ci / CH, col = (ci % CH) * 8;
+      const int key = t * FWD_BN + row;
+      if (key < N) {
+        kreg[r] = gload16(K + (size_t)key * D + col);
+        vreg[r] = gload16(V + (size_t)key * D + col);
+      } else {
+        kreg[r] = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
+        vreg[r] = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+  };
+  auto lstore_tile = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int ci = tid + r * (FWD_NW * 64);
+      const int row = ci / CH, col = (ci % CH) * 8;
+      lds_write16(kbuf + buf * KBUF + row * KP + col * 2, kreg[r]);
+      lds_write16(vbuf + buf * VBUF + row * VP + col * 2, vreg[r]);
+    }
+  };
+
+  if (ntiles > 0) {
+    gload_tile(tile_at(0));
+    lstore_tile(0);
+  }
+  __syncthreads();
+
+  for (int e = 0; e < ntiles; ++e) {
+    const int buf = e & 1;
+    const int ks = tile_at(e) * FWD_BN;
+    if (e + 1 < ntiles) gload_tile(tile_at(e + 1));
+
+    const bool active = !(CAUSAL && ks > qw + 31);  // wave-uniform
+    if (active) {
+      const lds_t* kb = kbuf + buf * KBUF;
+      const lds_t* vb = vbuf + buf * VBUF;
+      f32x16 sc[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sc[0][i] = 0.f;
+        sc[1][i] = 0.f;
+      }
+#pragma unroll
+      for (int ss = 0; ss < NS; ++ss) {
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const s16x8 ka = lds_read16(kb + (32 * t2 + l32) * KP + (16 * ss + 8 * hh) * 2);
+          sc[t2] = mfma32<T>(ka, qf[ss], sc[t2]);
+        }
+      }
+      // sc[t2][i] is S for query qi and key ks + 32 t2 + 8 (i / 4) + 4 hh + i % 4
+      const bool need_mask = (CAUSAL && ks + FWD_BN - 1 > qw) || (ks + FWD_BN > N);
+      if (need_mask) {
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = ks + 32 * t2 + 8 * (i >> 2) + 4 * hh + (i & 3);
+            if ((CAUSAL && key > qi) || key >= N) sc[t2][i] = -INFINITY;
+          }
+      }
+      float mx = sc[0][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[0][i]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[1][i]);
+      mx = fmaxf(mx, swap_halves(mx));
+      const float m_new = fmaxf(m, mx * c);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float corr = fast_exp2(m - m_use);
+      m = m_new;
+      l *= corr;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[dt][i] *= corr;
+
+      unsigned int pk[2][8];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p0 = fast_exp2(fmaf(sc[t2][2 * j], c, -m_use));
+          const float p1 = fast_exp2(fmaf(sc[t2][2 * j + 1], c, -m_use));
+          l += p0 + p1;
+          pk[t2][j] = pack2<T>(p0, p1);
+        }
+      // O^T(d x q) += V^T(d x key) P^T(key x q); B operand k-slot j of step (t2, u)
+      // is key 32 t2 + 16 u + 8 (j / 4) + 4 hh + j % 4, matched by the V^T reads
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const lds_t* vp = vb + (32 * t2 + 16 * u + roff) * VP + (32 * dt + coff) * 2;
+            const s16x8 va = concat(lds_read_tr(vp), lds_read_tr(vp + 8 * VP));
+            const s16x8 pb = as_operand(pk[t2][4 * u], pk[t2][4 * u + 1], pk[t2][4 * u + 2],
+                                        pk[t2][4 * u + 3]);
+            acc[dt] = mfma32<T>(va, pb, acc[dt]);
+          }
+    }
+    if (e + 1 < ntiles) lstore_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float lt = l + swap_halves(l);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
+  if (qi < N) {
+    unsigned short* Op = (unsigned short*)a.o + (qrow0 + qi) * D;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2 v2 = {pack2<T>(acc[dt][4 * j] * inv, acc[dt][4 * j + 1] * inv),
+                    pack2<T>(acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv)};
+        *reinterpret_cast<u32x2*>(Op + 32 * dt + 8 * j + 4 * hh) = v2;
+      }
+    if (hh == 0) a.lse[qrow0 + qi] = lse;
+  }
+}
+
+// float32: one query row per lane, fp32 FMA for every product, keys in LDS tiles.
+constexpr int F32_ROWS = 64;
+constexpr int F32_BN = 32;
+
+template <int D>
+__global__ __launch_bounds__(F32_ROWS) void fwd_f32_kernel(FwdArgs a) {
+  __shared__ float Ks[F32_BN][D];
+  __shared__ float Vs[F32_BN][D];
+  const AttnShape& s = a.s;
+  const int N = s.N;
+  const int tid = threadIdx.x;
+  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int hk = h / s.G;
+  const size_t qrow0 = (size_t)(b * s.H + h) * N;
+  const size_t krow0 = (size_t)(b * s.Hkv + hk) * N;
+  const float* Q = (const float*)a.q + qrow0 * D;
+  const float* K = (const float*)a.k + krow0 * D;
+  const float* V = (const float*)a.v + krow0 * D;
+  const int q0 = qb * F32_ROWS;
+  const int qi = q0 + tid;
+  const float c = fmaxf(s.scale * kLog2e, 1e-30f);
+  const int mrow = q0 / 128;  // the 64 rows of a workgroup lie in one mask block row
+
+  float q[D], o[D];
+#pragma unroll
+  for (int dd = 0; dd < D; ++dd) {
+    q[dd] = qi < N ? Q[(size_t)qi * D + dd] : 0.f;
+    o[dd] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  const int kend = s.causal ? min(N, q0 + F32_ROWS) : N;
+  for (int ks = 0; ks < kend; ks += F32_BN) {
+    if (s.mask && s.mask[(size_t)mrow * s.nb + ks / 128] == 0) continue;  // uniform
+    __syncthreads();
+    for (int i = tid; i < F32_BN * D; i += F32_ROWS) {
+      const int r = i / D, cc = i % D;
+      const int key = ks + r;
+      Ks[r][cc] = key < N ? K[(size_t)key * D + cc] : 0.f;
+      Vs[r][cc] = key < N ? V[(size_t)key * D + cc] : 0.f;
+    }
+    __syncthreads();
+    float x[F32_BN];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < F32_BN; ++j) {
+      float dot = 0.f;
+#pragma unroll
+      for (int dd = 0; dd < D; ++dd) dot = fmaf(q[dd], Ks[j][dd], dot);
+      const int key = ks + j;
+      const bool vis = key < N && (!s.causal || key <= qi);
+      x[j] = vis ? dot * c : -INFINITY;
+      mx = fmaxf(mx, x[j]);
+    }
+    const float m_new = fmaxf(m, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float corr = fast_exp2(m - m_use);
+    m = m_new;
+    l *= corr;
+#pragma unroll
+    for (int dd = 0; dd < D; ++dd) o[dd] *= corr;
+#pragma unroll
+    for (int j = 0; j < F32_BN; ++j) {
+      const float p = fast_exp2(x[j] - m_use);
+      l += p;
+#pragma unroll
+      for (int dd = 0; dd < D; ++dd) o[dd] = fmaf(p, Vs[j][dd], o[dd]);
+    }
+  }
+  if (qi < N) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float* Op = (float*)a.o + (qrow0 + qi) * D;
+#pragma unroll
+    for (int dd = 0; dd < D; ++dd) Op[dd] = o[dd] * inv;
+    a.lse[qrow0 + qi] = l > 0.f ? (m + fast_log2(l)) * kLn2 : -INFINITY;
+  }
+}
+
+template <class T, int D>
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
+  const dim3 grid(a.s.H, (a.s.N + FWD_BM - 1) / FWD_BM, a.s.B);
+  const dim3 block(FWD_NW * 64);
+  const bool causal = a.s.causal != 0, mask = a.s.mask != nullptr;
+  if (causal && mask) hipLaunchKernelGGL((fwd_kernel<T, D, true, true>), grid, block, 0, st, a);
+  else if (causal) hipLaunchKernelGGL((fwd_kernel<T, D, true, false>), grid, block, 0, st, a);
+  else if (mask) hipLaunchKernelGGL((fwd_kernel<T, D, false, true>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((fwd_kernel<T, D, false, false>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st) {
+  const dim3 grid((a.s.N + F32_ROWS - 1) / F32_ROWS, a.s.H, a.s.B);
+  hipLaunchKernelGGL((fwd_f32_kernel<D>), grid, dim3(F32_ROWS), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_forward(const FwdArgs& a, int dtype, hipStream_t st) {
+  const int d = a.s.d;
+  if (dtype == 0) {
+    if (d == 32) return launch_fwd_f32<32>(a, st);
+    if (d == 64) return launch_fwd_f32<64>(a, st);
+    return launch_fwd_f32<128>(a, st);
+  }
+  if (dtype == 2) {
+    if (d == 32) return launch_fwd_t<BF16, 32>(a, st);
+    if (d == 64) return launch_fwd_t<BF16, 64>(a, st);
+    return launch_fwd_t<BF16, 128>(a, st);
+  }
+  if (d == 32) return launch_fwd_t<F16, 32>(a, st);
+  if (d == 64) return launch_fwd_t<F16, 64>(a, st);
+  return launch_fwd_t<F16, 128>(a, st);
+}
+
+}  // namespace fa

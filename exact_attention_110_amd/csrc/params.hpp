@@ -1,0 +1,48 @@
+// Kernel argument blocks and the internal launch interface shared by the
+// forward, backward and C-ABI translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct AttnShape {
+  int B, H, Hkv, N, d;
+  int G;          // H / Hkv, query heads per kv head
+  float scale;    // multiplies Q K^T
+  int causal;     // key j visible to query i only if j <= i
+  const uint8_t* mask;  // NULL or uint8 [nb][nb], nb = ceil(N / 128)
+  int nb;         // ceil(N / 128)
+};
+
+struct FwdArgs {
+  AttnShape s;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+};
+
+struct BwdArgs {
+  AttnShape s;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dO;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dvec;    // workspace: D = rowsum(dO * O), [B][H][N]
+  float* dqacc;   // workspace: float32 dq accumulator, [B][H][N][d]
+};
+
+// Internal launchers (return a hipError_t from the launch).
+hipError_t launch_forward(const FwdArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_backward_stage(int stage, const BwdArgs& a, int dtype, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,142 @@
+/*
+ * fa.h - IO-aware exact attention for AMD MI355X (gfx950): forward and backward.
+ *
+ * What is computed. For every batch b and query head h, with kv head
+ * g = h / (H / Hkv) (grouped-query attention: contiguous groups of query heads
+ * share one key/value head, as on the "Grouped-query attention" card of the
+ * pranaymahendrakar.com lesson "FlashAttention"):
+ *
+ *     S = scale * Q K^T,  P = softmax(S) row by row,  O = P V
+ *
+ * (that lesson, Researcher tier, "The problem being solved"), computed tile by
+ * tile with a running row maximum m and running sum l of exponentials, the
+ * partial output rescaled by exp(m_old - m_new) whenever the maximum grows
+ * (same lesson, "Online softmax"), so that S and P are never written to memory
+ * (nadeemcite.github.io summary "FlashAttention: Fast and Memory-Efficient
+ * Exact Attention with IO-Awareness", Core Idea items 1, 2 and 4). The forward
+ * pass saves one statistic per row, LSE = m + ln(l), the natural-log
+ * log-sum-exp of the row's scaled scores; the backward pass recomputes P tile
+ * by tile as exp(S - LSE) instead of reading it back (Core Idea item 3).
+ *
+ * Masks. causal != 0 keeps key j visible to query i only when j <= i (the
+ * lesson's Beginner tier: a word looks at earlier words). block_mask, when not
+ * NULL, is a device array of uint8 [ceil(N/128)][ceil(N/128)], row-major; block
+ * (I, J) nonzero keeps keys 128J..128J+127 visible to queries 128I..128I+127
+ * (the summary's "Block-sparse extension", Key Method Details). The same mask
+ * serves every batch and head; with causal it is intersected. Zero blocks are
+ * skipped without being read. A query that sees no key at all gets O = 0,
+ * LSE = -inf and zero gradients.
+ *
+ * Layouts. All tensors are dense, row-major, device-resident:
+ *   q, o, dO, dq : [B][H][N][d]        k, v, dk, dv : [B][Hkv][N][d]
+ *   lse          : [B][H][N] float32
+ * q, k, v, o, dO, dq, dk, dv share one element type, FA_BF16, FA_F16 or FA_F32
+ * (FA_F32: forward only). Every pointer must be 16-byte aligned. d is 32, 64
+ * or 128; N >= 1 is any length (no multiple-of-tile restriction); H must be a
+ * multiple of Hkv; scale must be finite and >= 0 (1/sqrt(d) is the usual one).
+ *
+ * Ownership. The caller owns every buffer. The library allocates no device or
+ * host memory and keeps no state between calls; outputs are overwritten, never
+ * accumulated into, and must not alias inputs. Calls are thread-safe.
+ *
+ * Streams and errors. `stream` is a hipStream_t (NULL = the default stream).
+ * Every entry point checks all of its arguments before it touches the HIP
+ * runtime; on a bad argument it returns a negative status and enqueues
+ * nothing. Otherwise it enqueues its kernels on `stream` and returns at once
+ * (no host synchronisation); a launch failure reported by the runtime returns
+ * FA_ERR_HIP. Non-finite inputs propagate into the outputs; they are not
+ * checked.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define FA_OK 0
+#define FA_ERR_INVALID_ARG (-1) /* NULL pointer, bad size, bad dtype, bad scale, misaligned */
+#define FA_ERR_UNSUPPORTED (-2) /* well-formed but not implemented (e.g. FA_F32 backward)  */
+#define FA_ERR_WORKSPACE (-3)   /* workspace NULL or smaller than fa_backward_workspace_size */
+#define FA_ERR_HIP (-4)         /* the HIP runtime reported an error at launch              */
+
+/* Element types of q, k, v, o, dO, dq, dk, dv. */
+#define FA_F32 0
+#define FA_F16 1
+#define FA_BF16 2
+
+/* Block-mask granularity, in rows and in columns. */
+#define FA_MASK_BLOCK 128
+
+/*
+ * fa_forward: O and LSE from Q, K, V.
+ *   q [B][H][N][d], k, v [B][Hkv][N][d]    inputs (device)
+ *   o [B][H][N][d]                          output (device), same dtype as q
+ *   lse [B][H][N] float32                   output (device): m + ln(l) per row,
+ *                                           -inf for a row that sees no key
+ *   block_mask                              NULL (dense) or device uint8 mask
+ *   dtype                                   FA_BF16, FA_F16 or FA_F32
+ * Returns FA_OK or a negative status.
+ */
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int Hkv, int N, int d, float scale, int causal,
+               const uint8_t* block_mask, int dtype, void* stream);
+
+/*
+ * fa_backward_workspace_size: bytes of device scratch fa_backward needs for
+ * these sizes: one float32 per query row (D = rowsum(dO * O)) plus a float32
+ * [B][H][N][d] accumulator for dq, each rounded up to 256 bytes. Linear in N.
+ * Returns 0 for arguments fa_backward would reject.
+ */
+size_t fa_backward_workspace_size(int B, int H, int Hkv, int N, int d, int dtype);
+
+/*
+ * fa_backward: dq, dk, dv of sum(O * dO) from the forward pass's inputs and
+ * its saved o and lse. The probabilities are recomputed tile by tile from q,
+ * k and lse. For grouped-query attention dk and dv of a kv head are summed
+ * over its group of query heads. dtype is FA_BF16 or FA_F16 (FA_F32 returns
+ * FA_ERR_UNSUPPORTED). causal, block_mask and scale must be those of the
+ * forward call that produced o and lse.
+ *   workspace        device buffer of at least fa_backward_workspace_size()
+ *                    bytes, 256-byte aligned; its contents on entry do not
+ *                    matter and on return are unspecified. Owned by the caller;
+ *                    two calls in flight at once need two workspaces.
+ * Returns FA_OK or a negative status.
+ */
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dO, void* dq, void* dk, void* dv,
+                int B, int H, int Hkv, int N, int d, float scale, int causal,
+                const uint8_t* block_mask, int dtype,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_backward_stage: one of the three stages fa_backward runs, in this order,
+ * with the same arguments and the same workspace:
+ *   stage 0  D = rowsum(dO * O) per query row; clears the dq accumulator
+ *   stage 1  per key block: recompute P, then dv, dk and the dq contributions
+ *   stage 2  dq = accumulator, rounded to dtype
+ * Running stages 0, 1, 2 in order equals one fa_backward call. It exists so
+ * that each stage can be timed on its own. Returns FA_OK or a negative status
+ * (FA_ERR_INVALID_ARG for a stage outside 0..2).
+ */
+int fa_backward_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                      int B, int H, int Hkv, int N, int d, float scale, int causal,
+                      const uint8_t* block_mask, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* fa_status_string: a static, human-readable description of a status code. */
+const char* fa_status_string(int status);
+
+/* fa_version: the library version as 10000*major + 100*minor + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,95 @@
+"""Helpers that run the HIP path and the float64 oracle on the same seeded inputs
+and compare them (used by the GPU parity tests and the smoke check).
+
+Bars (the stated tolerances of the attention workloads):
+* float32 outputs (O of a float32 run, and LSE always): max abs error <= 1e-5;
+* bf16 / fp16 outputs: max abs error <= 2e-2;
+* gradients: per-tensor relative Frobenius error <= 5e-2.
+A row that sees no key must come back as O = 0 and LSE = -inf exactly.
+"""
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from exact_attention_110_amd import binding
+from exact_attention_110_amd import inputs as I
+
+TOL_F32 = 1e-5
+TOL_16 = 2e-2
+TOL_LSE = 1e-5
+TOL_GRAD = 5e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def np64(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def max_abs(a, b):
+    return float(np.abs(a - b).max()) if a.size else 0.0
+
+
+def check_lse(lse, ref, where):
+    assert lse.shape == ref.shape, where
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(ref)), f"{where}: -inf rows differ"
+    assert np.all(np.isfinite(lse[fin])), f"{where}: non-finite LSE"
+    err = max_abs(lse[fin], ref[fin])
+    assert err <= TOL_LSE, f"{where}: LSE max abs err {err:.3g} > {TOL_LSE}"
+    return err
+
+
+def check_out(o, ref, dtype, where):
+    assert np.all(np.isfinite(o)), f"{where}: non-finite O"
+    tol = TOL_F32 if dtype == "fp32" else TOL_16
+    err = max_abs(o, ref)
+    assert err <= tol, f"{where}: O max abs err {err:.3g} > {tol}"
+    return err
+
+
+def rel_frob(x, ref):
+    den = float(np.linalg.norm(ref))
+    num = float(np.linalg.norm(x - ref))
+    if den == 0.0:
+        return num
+    return num / den
+
+
+def check_grad(g, ref, where):
+    assert np.all(np.isfinite(g)), f"{where}: non-finite gradient"
+    err = rel_frob(g, ref)
+    assert err <= TOL_GRAD, f"{where}: relative Frobenius err {err:.3g} > {TOL_GRAD}"
+    return err
+
+
+def run_small(B, H, Hkv, N, d, dtype, causal, mask=None, seed=0, sigma=1.0, backward=True, scale=None):
+    """Full comparison (every output element) for a small seeded case."""
+    where = f"B{B} H{H} Hkv{Hkv} N{N} d{d} {dtype} causal={causal} mask={mask is not None} seed={seed}"
+    say("case", where)
+    x = I.make_small(B, H, Hkv, N, d, dtype, seed, sigma, with_grad=backward)
+    dev = torch.device("cuda", 0)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    mt = None if mask is None else torch.from_numpy(mask).to(dev)
+    o, lse = binding.forward(q, k, v, scale, causal, mt)
+    torch.cuda.synchronize()
+    qd, kd, vd = (np64(x[n]) for n in ("q", "k", "v"))
+    oref, lref = oracle.forward(qd, kd, vd, scale, causal, mask)
+    res = {"o": check_out(np64(o), oref, dtype, where), "lse": check_lse(np64(lse), lref, where)}
+    if backward and dtype != "fp32":
+        do = x["do"].to(dev)
+        dq, dk, dv = binding.backward(q, k, v, o, lse, do, scale, causal, mt)
+        torch.cuda.synchronize()
+        rq, rk, rv = oracle.backward(qd, kd, vd, np64(x["do"]), scale, causal, mask)
+        res["dq"] = check_grad(np64(dq), rq, where + " dq")
+        res["dk"] = check_grad(np64(dk), rk, where + " dk")
+        res["dv"] = check_grad(np64(dv), rv, where + " dv")
+    return res

@@ -1,0 +1,134 @@
+"""The C-ABI library loads, exports every declared entry point and rejects bad
+arguments before it touches the HIP runtime (CPU only: no call here is valid,
+so nothing is ever launched)."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+LIB = os.path.join(ROOT, "exact_attention_110_amd", "libfa.so")
+
+OK, EINVAL, EUNSUP, EWS, EHIP = 0, -1, -2, -3, -4
+F32, F16, BF16 = 0, 1, 2
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.skip("libfa.so not built")
+    import torch  # noqa: F401  (the library binds to the HIP runtime torch loads)
+    from exact_attention_110_amd import binding
+    return binding.load()
+
+
+def test_header_constants_match_binding():
+    from exact_attention_110_amd import binding
+    src = open(HEADER).read()
+    consts = dict(re.findall(r"#define (FA_[A-Z_0-9]+) \(?(-?\d+)\)?", src))
+    assert int(consts["FA_F32"]) == binding.FA_F32
+    assert int(consts["FA_F16"]) == binding.FA_F16
+    assert int(consts["FA_BF16"]) == binding.FA_BF16
+    assert int(consts["FA_MASK_BLOCK"]) == binding.MASK_BLOCK == 128
+    assert [int(consts[k]) for k in ("FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED",
+                                     "FA_ERR_WORKSPACE", "FA_ERR_HIP")] == [OK, EINVAL, EUNSUP, EWS, EHIP]
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"fa_forward", "fa_backward", "fa_backward_workspace_size", "fa_backward_stage",
+            "fa_status_string", "fa_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for st in (OK, EINVAL, EUNSUP, EWS, EHIP, 12345):
+        s = lib.fa_status_string(st)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert lib.fa_status_string(EWS) != lib.fa_status_string(EINVAL)
+    assert lib.fa_version() >= 100
+
+
+P = ctypes.c_void_p
+GOOD = P(1 << 20)       # 16- and 256-byte aligned stand-in address; never dereferenced
+ODD = P((1 << 20) + 8)  # 8-byte aligned only
+
+
+def fwd(lib, q=GOOD, k=GOOD, v=GOOD, o=GOOD, lse=GOOD, B=1, H=2, Hkv=1, N=256, d=64, scale=0.125,
+        causal=1, mask=None, dtype=BF16):
+    return lib.fa_forward(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, mask, dtype, None)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(lse=None),
+    dict(q=ODD), dict(o=ODD), dict(lse=P((1 << 20) + 2)),
+    dict(B=0), dict(H=0), dict(Hkv=0), dict(N=0), dict(N=-5), dict(H=3, Hkv=2),
+    dict(d=16), dict(d=96), dict(d=256), dict(dtype=3), dict(dtype=-1),
+    dict(scale=float("nan")), dict(scale=float("inf")), dict(scale=-0.5),
+    dict(B=70000), dict(B=1 << 16, H=1 << 15, N=8),
+])
+def test_forward_rejects(lib, bad):
+    assert fwd(lib, **bad) == EINVAL
+
+
+def test_forward_mask_too_long_is_unsupported(lib):
+    # masks are compacted into on-chip lists of 2048 blocks, so N <= 262144 with a mask;
+    # the check returns before any launch
+    assert fwd(lib, N=2049 * 128, mask=GOOD) == EUNSUP
+    assert bwd(lib, N=2049 * 128, mask=GOOD) == EUNSUP
+    assert fwd(lib, N=2049 * 128, mask=GOOD, d=16) == EINVAL   # bad arguments are reported first
+
+
+def ws_size(lib, B=1, H=2, Hkv=1, N=256, d=64, dtype=BF16):
+    return lib.fa_backward_workspace_size(B, H, Hkv, N, d, dtype)
+
+
+def test_workspace_size_formula(lib):
+    def r(x):
+        return (x + 255) // 256 * 256
+    for B, H, Hkv, N, d in [(1, 2, 1, 256, 64), (8, 12, 12, 1024, 64), (1, 16, 16, 16384, 128),
+                            (1, 1, 1, 1, 32), (2, 3, 1, 77, 128)]:
+        assert ws_size(lib, B, H, Hkv, N, d) == r(B * H * N * 4) + r(B * H * N * d * 4)
+    # linear in N
+    a, b = ws_size(lib, N=4096), ws_size(lib, N=8192)
+    assert b == 2 * a
+    assert ws_size(lib, dtype=F32) == 0
+    assert ws_size(lib, d=48) == 0
+    assert ws_size(lib, H=3, Hkv=2) == 0
+
+
+def bwd(lib, stage=None, ws=GOOD, ws_bytes=None, dtype=BF16, N=256, d=64, mask=None, scale=0.125,
+        dq=GOOD, lse=GOOD):
+    if ws_bytes is None:
+        ws_bytes = ws_size(lib, N=N, d=d) if dtype != F32 else 1 << 30
+    args = [GOOD, GOOD, GOOD, GOOD, lse, GOOD, dq, GOOD, GOOD, 1, 2, 1, N, d, scale, 1, mask, dtype,
+            ws, ws_bytes, None]
+    if stage is None:
+        return lib.fa_backward(*args)
+    return lib.fa_backward_stage(stage, *args)
+
+
+def test_backward_rejects(lib):
+    assert bwd(lib, dtype=F32) == EUNSUP
+    assert bwd(lib, ws=None) == EWS
+    assert bwd(lib, ws=P((1 << 20) + 16)) == EWS
+    assert bwd(lib, ws_bytes=ws_size(lib) - 1) == EWS
+    assert bwd(lib, dq=None) == EINVAL
+    assert bwd(lib, lse=None) == EINVAL
+    assert bwd(lib, d=100) == EINVAL
+    assert bwd(lib, scale=float("nan")) == EINVAL
+    for st in (-1, 3, 99):
+        assert bwd(lib, stage=st) == EINVAL
+    assert bwd(lib, stage=1, ws=None) == EWS
+    assert bwd(lib, stage=0, dtype=F32) == EUNSUP

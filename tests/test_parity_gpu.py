@@ -1,0 +1,105 @@
+"""GPU parity on small shapes: every output element of the HIP path against the
+float64 oracle, on seeded inputs that span several tiles and ragged tails."""
+
+import numpy as np
+import pytest
+import torch
+
+import parity as PT
+from exact_attention_110_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu(gpu_lib):
+    yield
+
+
+SHAPES = [
+    # B, H, Hkv, N, d
+    (1, 1, 1, 1, 64),
+    (1, 2, 1, 17, 32),
+    (2, 2, 2, 64, 64),
+    (1, 3, 1, 127, 128),
+    (1, 2, 2, 128, 128),
+    (1, 4, 2, 129, 64),
+    (2, 4, 1, 300, 32),
+    (1, 2, 2, 513, 128),
+    (1, 8, 2, 1000, 64),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_dense(shape, causal, dtype):
+    B, H, Hkv, N, d = shape
+    seed = 1000 * B + 100 * H + 10 * Hkv + N + 7 * d + 3 * int(causal) + (1 if dtype == "fp16" else 0)
+    PT.run_small(B, H, Hkv, N, d, dtype, causal, seed=seed)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("N", [1, 100, 512, 700])
+def test_fp32_forward(N, d, causal):
+    PT.run_small(1, 2, 1, N, d, "fp32", causal, seed=N + d, backward=False)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,d,density,seed", [(300, 64, 0.5, 1), (700, 128, 0.3, 2), (1100, 32, 0.25, 3),
+                                              (1024, 64, 0.6, 4)])
+def test_block_sparse(N, d, density, seed, causal, dtype):
+    m = I.random_block_mask(N, density, seed, keep_diagonal=True)
+    PT.run_small(1, 4, 2, N, d, dtype, causal, mask=m, seed=seed)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_empty_rows(dtype):
+    """A block row of zeros: those queries see no key -> O = 0, LSE = -inf, zero dq."""
+    N = 400
+    m = np.ones((4, 4), dtype=np.uint8)
+    m[1, :] = 0
+    m[3, 3] = 0
+    m[3, 0] = 0
+    res = PT.run_small(1, 2, 1, N, 64, dtype, False, mask=m, seed=9, backward=True)
+    assert res["o"] <= (PT.TOL_F32 if dtype == "fp32" else PT.TOL_16)
+
+
+def test_scale_zero_is_uniform():
+    PT.run_small(1, 2, 2, 200, 64, "bf16", True, seed=5, scale=0.0)
+    PT.run_small(1, 1, 1, 150, 32, "fp32", False, seed=6, scale=0.0, backward=False)
+
+
+def test_forward_bitwise_deterministic(gpu_lib):
+    x = I.make_small(1, 4, 2, 1000, 128, "bf16", 11, with_grad=False)
+    q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    o1, l1 = gpu_lib.forward(q, k, v, None, True)
+    o2, l2 = gpu_lib.forward(q, k, v, None, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_forward_allocates_nothing(gpu_lib):
+    """With caller-owned outputs the library takes no device memory (O(N) memory:
+    only O and LSE are written)."""
+    x = I.make_small(1, 2, 2, 2048, 64, "bf16", 12, with_grad=False)
+    q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    before = torch.cuda.memory_allocated()
+    gpu_lib.forward(q, k, v, None, True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert torch.cuda.memory_allocated() == before
+    assert free1 == free0
+
+
+def test_noncontiguous_rejected(gpu_lib):
+    x = I.make_small(1, 2, 2, 64, 64, "bf16", 13, with_grad=False)
+    q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    with pytest.raises(ValueError):
+        gpu_lib.forward(q.transpose(1, 2), k, v)
