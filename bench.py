@@ -1,0 +1,203 @@
+"""Throughput of the attention hot path on one MI355X.
+
+A step is one forward pass (O and LSE) plus one backward pass (dq, dk, dv) of
+causal bf16 attention at B=1, H=16, N=16384, d=128 over seeded synthetic
+inputs already resident in device memory. The reported value is
+forward+backward TFLOP/s with the conventional count of 2 N^2 d FLOP per
+N x N x d contraction, two contractions forward and five backward (the
+recomputed QK^T included), halved for causal masking.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline] [--copy-mb MB]
+
+Prints one JSON line. Besides the headline it carries:
+* "roofline": the dominant kernel's algorithmic FLOP per launch over its mean
+  launch time, measured with HIP events on the stream the library launches on,
+  against the dense bf16 MFMA peak (2.5 PFLOP/s); "traffic" is filled from
+  rocprofv3 counter runs and is null here;
+* "cpu_baseline": the float64 CPU oracle timed on a bounded sample of the same
+  workload (one head, forward+backward), in the same unit.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def flops(w, backward=True):
+    """Algorithmic FLOP of one step: 2 N^2 d per contraction, x1/2 under causal masking."""
+    per = 2.0 * w.N * w.N * w.d * w.B * w.H
+    if w.causal:
+        per *= 0.5
+    if w.sparse:
+        raise ValueError("use sparse_flops for masked workloads")
+    return per * (2 + (5 if backward else 0))
+
+
+def sparse_flops(w, mask, backward=True):
+    blocks = float(mask.sum())
+    per = 2.0 * 128 * 128 * w.d * w.B * w.H * blocks
+    return per * (2 + (5 if backward else 0))
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_seq_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="after timing, run one device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, x):
+    """Time the float64 oracle on the workload's checked heads (at most two),
+    forward + backward, on the host cores."""
+    import oracle
+    from exact_attention_110_amd import inputs as I
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    heads = I.check_heads(w)[:2]
+    t0 = time.perf_counter()
+    for b, h in heads:
+        g = h // w.G
+        q = x["q"][b:b + 1, h:h + 1].double().numpy()
+        k = x["k"][b:b + 1, g:g + 1].double().numpy()
+        v = x["v"][b:b + 1, g:g + 1].double().numpy()
+        oracle.forward(q, k, v, w.scale, w.causal, x["mask"])
+        if w.backward:
+            do = x["do"][b:b + 1, h:h + 1].double().numpy()
+            oracle.backward(q, k, v, do, w.scale, w.causal, x["mask"])
+    dt = time.perf_counter() - t0
+    if w.sparse:
+        f = sparse_flops(w, x["mask"], w.backward) / (w.B * w.H)
+    else:
+        f = flops(w, w.backward) / (w.B * w.H)
+    f *= len(heads)
+    return {"value": round(f / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{w.name}: heads {heads} ({len(heads)} of {w.B * w.H}), forward"
+                      f"{'+backward' if w.backward else ''}, float64 numpy, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "heads and batches shard across GPUs without exchange, but this build "
+              "measures the single-GPU kernel only", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from exact_attention_110_amd import binding
+    from exact_attention_110_amd import inputs as I
+
+    w = I.WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    x = I.make(w)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    do = x["do"].to(dev) if w.backward else None
+    mask = torch.from_numpy(x["mask"]).to(dev) if x["mask"] is not None else None
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    if w.backward:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = binding.workspace(q, k)
+    total_flop = sparse_flops(w, x["mask"], w.backward) if w.sparse else flops(w, w.backward)
+    fwd_flop = sparse_flops(w, x["mask"], False) if w.sparse else flops(w, False)
+    bwd_flop = total_flop - fwd_flop
+
+    def step():
+        binding.forward(q, k, v, w.scale, w.causal, mask, out=o, lse=lse)
+        if w.backward:
+            binding.backward(q, k, v, o, lse, do, w.scale, w.causal, mask, ws=ws, grads=(dq, dk, dv))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed * 1e3 / args.steps
+    value = total_flop / (ms * 1e-3) / 1e12
+    print(f"[bench] {w.name}: {ms:.3f} ms/step, {value:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    # per-kernel times with HIP events on the library's stream (torch's current stream)
+    def event_time(fn, n):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(n):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / n  # ms
+
+    n_ev = max(args.steps, 5)
+    t_fwd = event_time(lambda: binding.forward(q, k, v, w.scale, w.causal, mask, out=o, lse=lse), n_ev)
+    kernels = {"fwd_kernel": (t_fwd, fwd_flop)}
+    if w.backward:
+        stage = lambda s: (lambda: binding.backward_stage(s, q, k, v, o, lse, do, dq, dk, dv, ws,  # noqa: E731
+                                                          w.scale, w.causal, mask))
+        t_pre = event_time(stage(0), n_ev)
+        t_kv = event_time(stage(1), n_ev)
+        t_cvt = event_time(stage(2), n_ev)
+        kernels["bwd_kv_kernel"] = (t_kv, bwd_flop)
+        print(f"[bench] forward {t_fwd:.3f} ms ({fwd_flop / t_fwd / 1e9:.1f} TFLOP/s); backward stages "
+              f"{t_pre:.3f} / {t_kv:.3f} / {t_cvt:.3f} ms ({bwd_flop / t_kv / 1e9:.1f} TFLOP/s in the "
+              f"key-block kernel)", file=sys.stderr, flush=True)
+    dom = max(kernels, key=lambda n: kernels[n][0])
+    t_dom, f_dom = kernels[dom]
+    achieved = f_dom / (t_dom * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "launch_ms": round(t_dom, 4), "flop_per_launch": f_dom}
+
+    if args.copy_mb:
+        src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    line = {
+        "metric": "attention fwd+bwd TFLOP/s (bf16, causal) and % of MFMA peak, N=16K d=128",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "block_sparse": w.sparse, "passes": "fwd+bwd" if w.backward else "fwd",
+                   "flop_per_step": total_flop, "mfma_peak_frac": round(value / PEAK_BF16_TFLOPS, 4)},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
