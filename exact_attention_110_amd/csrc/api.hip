@@ -24,7 +24,9 @@ int check_shape(int B, int H, int Hkv, int N, int d, float scale, int dtype) {
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
   const long long rows = (long long)B * H * N;
-  if (rows > INT32_MAX || (long long)N * d > INT32_MAX) return FA_ERR_INVALID_ARG;
+  // one head of a tensor (and of the float32 dq accumulator) must be addressable
+  // with 32-bit byte offsets: N * d * 4 < 2^32
+  if (rows > INT32_MAX || (long long)N * d >= (1LL << 30)) return FA_ERR_INVALID_ARG;
   if (B > 65535 || (N + 127) / 128 > 65535) return FA_ERR_INVALID_ARG;
   return FA_OK;
 }

@@ -72,27 +72,32 @@ __global__ __launch_bounds__(BWD_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
   constexpr int KP = D * 2 + 32;        // K row pitch (bytes)
   constexpr int SP = BWD_BQ * 2 + 32;   // dS row pitch: rows are keys, columns queries
   constexpr int QBUF = BWD_BQ * QP;
+  constexpr int SBUF = BWD_BKV * SP;
   constexpr int CH = D / 8;
   constexpr int PERQ = BWD_BQ * CH / (BWD_NW * 64);
   constexpr int PERK = BWD_BKV * CH / (BWD_NW * 64);
   static_assert(PERQ >= 1 && (BWD_BQ * CH) % (BWD_NW * 64) == 0, "query loader shape");
   static_assert(PERK >= 1 && (BWD_BKV * CH) % (BWD_NW * 64) == 0, "key loader shape");
+  static_assert(2 * BWD_BQ <= BWD_NW * 64, "row statistics loader shape");
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
   constexpr int NQT = BWD_BQ / 32;     // 32-row query tiles per step
   constexpr int NDQ = NQT * ND;        // 32x32 dQ tiles per step
 
-  __shared__ __attribute__((aligned(16))) char smem_raw[4 * QBUF + BWD_BKV * KP + BWD_BKV * SP +
-                                                        (MASK ? 2 * BWD_LIST + 16 : 16)];
+  // LDS: Q and dO blocks (double-buffered), per-row statistics (double-buffered),
+  // the K block, dS (double-buffered) and the compacted mask list
+  __shared__ __attribute__((aligned(16))) char smem_raw[4 * QBUF + 2 * 2 * BWD_BQ * 4 + BWD_BKV * KP +
+                                                        2 * SBUF + (MASK ? 2 * BWD_LIST + 16 : 16)];
   lds_t* smem = (lds_t*)smem_raw;
-  lds_t* qbuf = smem;                 // [2][BQ][QP]
-  lds_t* obuf = smem + 2 * QBUF;      // dO, [2][BQ][QP]
-  lds_t* kl = smem + 4 * QBUF;        // K block, [BKV][KP]
-  lds_t* dsl = kl + BWD_BKV * KP;     // dS, [BKV][SP]
+  lds_t* qbuf = smem;                      // [2][BQ][QP]
+  lds_t* obuf = qbuf + 2 * QBUF;           // dO, [2][BQ][QP]
+  lds_t* stat = obuf + 2 * QBUF;           // [2][2][BQ] float: log2-scaled LSE, D
+  lds_t* kl = stat + 2 * 2 * BWD_BQ * 4;   // K block, [BKV][KP]
+  lds_t* dsl = kl + BWD_BKV * KP;          // dS, [2][BKV][SP]
   __attribute__((address_space(3))) short* blist =
-      (__attribute__((address_space(3))) short*)(dsl + BWD_BKV * SP);
+      (__attribute__((address_space(3))) short*)(dsl + 2 * SBUF);
   __attribute__((address_space(3))) int* bcount =
-      (__attribute__((address_space(3))) int*)(dsl + BWD_BKV * SP + (MASK ? 2 * BWD_LIST : 0));
+      (__attribute__((address_space(3))) int*)(dsl + 2 * SBUF + (MASK ? 2 * BWD_LIST : 0));
 
   const AttnShape& s = a.s;
   const int N = s.N;
@@ -108,30 +113,25 @@ __global__ __launch_bounds__(BWD_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
   const float c = s.scale * kLog2e;
   const float scale = s.scale;
 
+  // per-head buffer resources: rows past N read as zeros, writes past N are dropped
+  const unsigned int head_bytes = (unsigned int)N * D * 2;
   const size_t krow0 = (size_t)(b * s.Hkv + hk) * N;
-  const unsigned short* K = (const unsigned short*)a.k + krow0 * D;
-  const unsigned short* V = (const unsigned short*)a.v + krow0 * D;
+  const rsrc_t rk = make_rsrc((const unsigned short*)a.k + krow0 * D, head_bytes);
+  const rsrc_t rv = make_rsrc((const unsigned short*)a.v + krow0 * D, head_bytes);
 
   // K^T and V^T operands: lane holds key kj, d = 16 ss + 8 hh + 0..7
   s16x8 kf[NS], vf[NS];
 #pragma unroll
   for (int ss = 0; ss < NS; ++ss) {
-    if (kj < N) {
-      kf[ss] = gload16(K + (size_t)kj * D + 16 * ss + 8 * hh);
-      vf[ss] = gload16(V + (size_t)kj * D + 16 * ss + 8 * hh);
-    } else {
-      kf[ss] = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
-      vf[ss] = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
-    }
+    kf[ss] = bload16(rk, (unsigned)(kj * D + 16 * ss + 8 * hh) * 2u);
+    vf[ss] = bload16(rv, (unsigned)(kj * D + 16 * ss + 8 * hh) * 2u);
   }
   // the whole K block in LDS for the dQ product
 #pragma unroll
   for (int r = 0; r < PERK; ++r) {
     const int ci = tid + r * (BWD_NW * 64);
     const int row = ci / CH, col = (ci % CH) * 8;
-    const int key = k0 + row;
-    const s16x8 v = key < N ? gload16(K + (size_t)key * D + col) : (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
-    lds_write16(kl + row * KP + col * 2, v);
+    lds_write16(kl + row * KP + col * 2, bload16(rk, (unsigned)((k0 + row) * D + col) * 2u));
   }
 
   // query blocks this key block meets
@@ -162,6 +162,9 @@ __global__ __launch_bounds__(BWD_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
     else return qb_first + e;
   };
   const int nsteps = nq * s.G;  // every query head of the group, every query block
+  // divisor for step -> (head, query block); a key block with no visible query
+  // block (nq = 0, block-sparse only) still issues its first, unused prefetch
+  const int nqd = nq > 0 ? nq : 1;
 
   f32x16 dka[ND], dva[ND];
 #pragma unroll
@@ -172,25 +175,33 @@ __global__ __launch_bounds__(BWD_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
       dva[dt][i] = 0.f;
     }
 
+  // prefetch of step e's Q and dO rows (registers) and its row statistics:
+  // threads 0..BQ-1 take log2-scaled LSE, threads BQ..2BQ-1 take D
   s16x8 qreg[PERQ], oreg[PERQ];
+  float sreg = 0.f;
   auto gload_q = [&](int e) {
-    const int h = hk * s.G + e / nq;
-    const int q0 = qblock_at(e % nq) * BWD_BQ;
+    const int h = hk * s.G + e / nqd;
+    const int q0 = qblock_at(e % nqd) * BWD_BQ;
     const size_t qrow0 = (size_t)(b * s.H + h) * N;
-    const unsigned short* Q = (const unsigned short*)a.q + qrow0 * D;
-    const unsigned short* G = (const unsigned short*)a.dO + qrow0 * D;
+    const rsrc_t rq = make_rsrc((const unsigned short*)a.q + qrow0 * D, head_bytes);
+    const rsrc_t rg = make_rsrc((const unsigned short*)a.dO + qrow0 * D, head_bytes);
 #pragma unroll
     for (int r = 0; r < PERQ; ++r) {
       const int ci = tid + r * (BWD_NW * 64);
       const int row = ci / CH, col = (ci % CH) * 8;
-      const int q = q0 + row;
-      if (q < N) {
-        qreg[r] = gload16(Q + (size_t)q * D + col);
-        oreg[r] = gload16(G + (size_t)q * D + col);
-      } else {
-        qreg[r] = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
-        oreg[r] = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
-      }
+      const unsigned int off = (unsigned)((q0 + row) * D + col) * 2u;
+      qreg[r] = bload16(rq, off);
+      oreg[r] = bload16(rg, off);
+    }
+    {
+      // threads 0..BQ-1: LSE in log2 units; BQ..2BQ-1: D. Rows past N, and rows
+      // that saw no key, get LSE = +inf so that their P is 0.
+      // (two wave-uniform resources; a per-lane choice of base would not be uniform)
+      const int q = q0 + (tid % BWD_BQ);
+      const float lv = bload_f32(make_rsrc(a.lse + qrow0, (unsigned)N * 4u), (unsigned)q * 4u);
+      const float dv = bload_f32(make_rsrc(a.dvec + qrow0, (unsigned)N * 4u), (unsigned)q * 4u);
+      const float L = (q < N && lv != -INFINITY) ? lv * kLog2e : INFINITY;
+      sreg = tid < BWD_BQ ? L : dv;
     }
   };
   auto lstore_q = [&](int buf) {
@@ -201,41 +212,56 @@ __global__ __launch_bounds__(BWD_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
       lds_write16(qbuf + buf * QBUF + row * QP + col * 2, qreg[r]);
       lds_write16(obuf + buf * QBUF + row * QP + col * 2, oreg[r]);
     }
+    if (tid < 2 * BWD_BQ)
+      *((__attribute__((address_space(3))) float*)(stat + buf * 2 * BWD_BQ * 4) + tid) = sreg;
   };
 
-  if (nsteps > 0) {
-    gload_q(0);
-    lstore_q(0);
-  }
+  // dQ(q x d) += dS(q x key) K(key x d) over the block's 128 keys for the step
+  // whose dS sits in buffer sb; each wave takes whole 32x32 tiles of the 64 x D result
+  auto dq_phase = [&](int e, int sb) {
+    const int h = hk * s.G + e / nqd;
+    const int q0 = qblock_at(e % nqd) * BWD_BQ;
+    const size_t qrow0 = (size_t)(b * s.H + h) * N;
+    const rsrc_t racc = make_rsrc(a.dqacc + qrow0 * D, (unsigned)N * D * 4u);
+    const lds_t* ds = dsl + sb * SBUF;
+    for (int ti = w; ti < NDQ; ti += BWD_NW) {
+      const int qt = ti % NQT, dt = ti / NQT;
+      f32x16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int u = 0; u < BWD_BKV / 16; ++u) {
+        const lds_t* sp = ds + (16 * u + roff) * SP + (32 * qt + coff) * 2;
+        const lds_t* kp = kl + (16 * u + roff) * KP + (32 * dt + coff) * 2;
+        const s16x8 sa = concat(lds_read_tr(sp), lds_read_tr(sp + 8 * SP));
+        const s16x8 kb = concat(lds_read_tr(kp), lds_read_tr(kp + 8 * KP));
+        acc = mfma32<T>(sa, kb, acc);
+      }
+      // acc: column d = 32 dt + l32, rows q0 + 32 qt + 8 (i / 4) + 4 hh + i % 4
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int q = q0 + 32 * qt + 8 * (i >> 2) + 4 * hh + (i & 3);
+        batomic_add(racc, (unsigned)(q * D + 32 * dt + l32) * 4u, acc[i]);
+      }
+    }
+  };
+
+  // loads are issued on every path (indices clamped; buffer loads make a
+  // redundant block harmless) so that outstanding loads are counted exactly
+  gload_q(0);
+  lstore_q(0);
   __syncthreads();
 
   for (int e = 0; e < nsteps; ++e) {
     const int buf = e & 1;
-    const int h = hk * s.G + e / nq;
-    const int q0 = qblock_at(e % nq) * BWD_BQ;
-    const size_t qrow0 = (size_t)(b * s.H + h) * N;
-    if (e + 1 < nsteps) gload_q(e + 1);
+    const int q0 = qblock_at(e % nqd) * BWD_BQ;
+    gload_q(e + 1 < nsteps ? e + 1 : e);
 
     const lds_t* qb = qbuf + buf * QBUF;
     const lds_t* ob = obuf + buf * QBUF;
-
-    // per-row statistics for the 16 rows of each query tile this lane holds:
-    // rows q0 + 32 qt + 8 j + 4 hh + r, r = 0..3
-    float lse2[NQT][16], dd[NQT][16];
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int q = q0 + 32 * qt + 8 * (i >> 2) + 4 * hh + (i & 3);
-        float L = INFINITY, Dv = 0.f;
-        if (q < N) {
-          L = a.lse[qrow0 + q];
-          Dv = a.dvec[qrow0 + q];
-          L = (L == -INFINITY) ? INFINITY : L * kLog2e;  // a row that saw no key keeps P = 0
-        }
-        lse2[qt][i] = L;
-        dd[qt][i] = Dv;
-      }
+    const __attribute__((address_space(3))) float* lsel =
+        (const __attribute__((address_space(3))) float*)(stat + buf * 2 * BWD_BQ * 4);
+    const __attribute__((address_space(3))) float* ddl = lsel + BWD_BQ;
 
     // S = Q K^T and dP = dO V^T for this wave's 32 keys
     f32x16 sc[NQT], dp[NQT];
@@ -262,29 +288,34 @@ __global__ __launch_bounds__(BWD_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float p[2], d2[2];
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const f32x4 L4 = *(const __attribute__((address_space(3))) f32x4*)(lsel + 32 * qt + 8 * j4 + 4 * hh);
+        const f32x4 D4 = *(const __attribute__((address_space(3))) f32x4*)(ddl + 32 * qt + 8 * j4 + 4 * hh);
+        float p[4], d2[4];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int i = 2 * j + t;
-          float pv = fast_exp2(fmaf(sc[qt][i], c, -lse2[qt][i]));
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * j4 + r;
+          float pv = fast_exp2(fmaf(sc[qt][i], c, -L4[r]));
           if (need_mask) {
-            const int q = q0 + 32 * qt + 8 * (i >> 2) + 4 * hh + (i & 3);
+            const int q = q0 + 32 * qt + 8 * j4 + 4 * hh + r;
             if ((CAUSAL && kj > q) || kj >= N) pv = 0.f;
           }
-          p[t] = pv;
-          d2[t] = pv * (dp[qt][i] - dd[qt][i]) * scale;
+          p[r] = pv;
+          d2[r] = pv * (dp[qt][i] - D4[r]) * scale;
         }
-        pk[qt][j] = pack2<T>(p[0], p[1]);
-        sk[qt][j] = pack2<T>(d2[0], d2[1]);
+        pk[qt][2 * j4] = pack2<T>(p[0], p[1]);
+        pk[qt][2 * j4 + 1] = pack2<T>(p[2], p[3]);
+        sk[qt][2 * j4] = pack2<T>(d2[0], d2[1]);
+        sk[qt][2 * j4 + 1] = pack2<T>(d2[2], d2[3]);
       }
     // dS into LDS as [key][query]: 4 consecutive queries per 8-byte write
+    lds_t* dsw = dsl + buf * SBUF;
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         u32x2 v2 = {sk[qt][2 * j], sk[qt][2 * j + 1]};
-        lds_write8(dsl + (32 * w + l32) * SP + (32 * qt + 8 * j + 4 * hh) * 2, v2);
+        lds_write8(dsw + (32 * w + l32) * SP + (32 * qt + 8 * j + 4 * hh) * 2, v2);
       }
 
     // dV^T(d x key) += dO^T(d x q) P(q x key); dK^T += Q^T dS. B operand k-slot j of
@@ -303,52 +334,31 @@ __global__ __launch_bounds__(BWD_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
           dka[dt] = mfma32<T>(qa, as_operand(sk[qt][4 * u], sk[qt][4 * u + 1], sk[qt][4 * u + 2],
                                              sk[qt][4 * u + 3]), dka[dt]);
         }
-    __syncthreads();  // dS of all four waves is in LDS
 
-    // dQ(q x d) += dS(q x key) K(key x d) over the block's 128 keys; each wave
-    // takes whole 32x32 tiles of the 64 x D result
-    for (int ti = w; ti < NDQ; ti += BWD_NW) {
-      const int qt = ti % NQT, dt = ti / NQT;
-      f32x16 acc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll
-      for (int u = 0; u < BWD_BKV / 16; ++u) {
-        const lds_t* sp = dsl + (16 * u + roff) * SP + (32 * qt + coff) * 2;
-        const lds_t* kp = kl + (16 * u + roff) * KP + (32 * dt + coff) * 2;
-        const s16x8 sa = concat(lds_read_tr(sp), lds_read_tr(sp + 8 * SP));
-        const s16x8 kb = concat(lds_read_tr(kp), lds_read_tr(kp + 8 * KP));
-        acc = mfma32<T>(sa, kb, acc);
-      }
-      // acc: column d = 32 dt + l32, rows q0 + 32 qt + 8 (i / 4) + 4 hh + i % 4
-      float* dq = a.dqacc + qrow0 * D + 32 * dt + l32;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int q = q0 + 32 * qt + 8 * (i >> 2) + 4 * hh + (i & 3);
-        if (q < N) unsafeAtomicAdd(dq + (size_t)q * D, acc[i]);
-      }
-    }
+    // dQ of the previous step: its dS was completed by every wave before the
+    // barrier that ended that step
+    if (e > 0) dq_phase(e - 1, buf ^ 1);
 
-    if (e + 1 < nsteps) lstore_q(buf ^ 1);
+    lstore_q(buf ^ 1);
     __syncthreads();
   }
+  if (nsteps > 0) dq_phase(nsteps - 1, (nsteps - 1) & 1);
 
   // dK^T / dV^T: lane holds key kj, d = 32 dt + 8 j + 4 hh + 0..3
-  if (kj < N) {
-    unsigned short* dK = (unsigned short*)a.dk + (krow0 + kj) * D;
-    unsigned short* dV = (unsigned short*)a.dv + (krow0 + kj) * D;
+  const rsrc_t rdk = make_rsrc((unsigned short*)a.dk + krow0 * D, head_bytes);
+  const rsrc_t rdv = make_rsrc((unsigned short*)a.dv + krow0 * D, head_bytes);
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
+  for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x2 kv = {pack2<T>(dka[dt][4 * j], dka[dt][4 * j + 1]),
-                    pack2<T>(dka[dt][4 * j + 2], dka[dt][4 * j + 3])};
-        u32x2 vv = {pack2<T>(dva[dt][4 * j], dva[dt][4 * j + 1]),
-                    pack2<T>(dva[dt][4 * j + 2], dva[dt][4 * j + 3])};
-        *reinterpret_cast<u32x2*>(dK + 32 * dt + 8 * j + 4 * hh) = kv;
-        *reinterpret_cast<u32x2*>(dV + 32 * dt + 8 * j + 4 * hh) = vv;
-      }
-  }
+    for (int j = 0; j < 4; ++j) {
+      u32x2 kv = {pack2<T>(dka[dt][4 * j], dka[dt][4 * j + 1]),
+                  pack2<T>(dka[dt][4 * j + 2], dka[dt][4 * j + 3])};
+      u32x2 vv = {pack2<T>(dva[dt][4 * j], dva[dt][4 * j + 1]),
+                  pack2<T>(dva[dt][4 * j + 2], dva[dt][4 * j + 3])};
+      const unsigned int off = (unsigned)(kj * D + 32 * dt + 8 * j + 4 * hh) * 2u;
+      bstore8(rdk, off, kv);
+      bstore8(rdv, off, vv);
+    }
 }
 
 // ---------------------------------------------------------------------------

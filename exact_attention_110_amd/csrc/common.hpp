@@ -124,4 +124,30 @@ __device__ __forceinline__ s16x8 gload16(const unsigned short* p) {
   return *reinterpret_cast<const s16x8*>(p);
 }
 
+// Buffer resources: a base address and a size in bytes. Loads past the size
+// return zeros and stores / atomics past it are dropped by the hardware, so
+// ragged tails need no branches (and the compiler can track every load).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format, no swizzle
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, unsigned int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ s16x8 bload16(rsrc_t r, unsigned int off) {
+  return __builtin_bit_cast(s16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float bload_f32(rsrc_t r, unsigned int off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void bstore8(rsrc_t r, unsigned int off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) int, v), r,
+                                        off, 0, 0);
+}
+__device__ __forceinline__ void bstore_f32(rsrc_t r, unsigned int off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, off, 0, 0);
+}
+__device__ __forceinline__ void batomic_add(rsrc_t r, unsigned int off, float v) {
+  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, off, 0, 0);
+}
+
 }  // namespace fa

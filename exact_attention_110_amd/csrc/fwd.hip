@@ -73,9 +73,11 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
   const int hk = h / s.G;
   const size_t qrow0 = (size_t)(b * s.H + h) * N;
   const size_t krow0 = (size_t)(b * s.Hkv + hk) * N;
-  const unsigned short* Q = (const unsigned short*)a.q + qrow0 * D;
-  const unsigned short* K = (const unsigned short*)a.k + krow0 * D;
-  const unsigned short* V = (const unsigned short*)a.v + krow0 * D;
+  // per-head buffer resources: rows past N read as zeros, stores past N are dropped
+  const unsigned int head_bytes = (unsigned int)N * D * 2;
+  const rsrc_t rq = make_rsrc((const unsigned short*)a.q + qrow0 * D, head_bytes);
+  const rsrc_t rk = make_rsrc((const unsigned short*)a.k + krow0 * D, head_bytes);
+  const rsrc_t rv = make_rsrc((const unsigned short*)a.v + krow0 * D, head_bytes);
   const int q0 = qb * FWD_BM;
   const int qw = q0 + 32 * w;   // first query row of this wave
   const int qi = qw + l32;      // query row of this lane's column
@@ -112,18 +114,20 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
   // Q^T operand: lane holds query qi, d = 16 * ss + 8 * hh + 0..7
   s16x8 qf[NS];
 #pragma unroll
-  for (int ss = 0; ss < NS; ++ss) {
-    if (qi < N) qf[ss] = gload16(Q + (size_t)qi * D + 16 * ss + 8 * hh);
-    else qf[ss] = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
-  }
+  for (int ss = 0; ss < NS; ++ss) qf[ss] = bload16(rq, (unsigned)(qi * D + 16 * ss + 8 * hh) * 2u);
 
   f32x16 acc[ND];
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
-  float m = -INFINITY;  // running maximum of S * c over the keys seen
-  float l = 0.f;        // this lane's share of the running sum (its half of the keys)
+  // Running reference m (in log2 units) and this lane's share l of the running
+  // sum (its half of the keys). m is raised only when a row of the wave
+  // exceeds it by more than kSlack, so most tiles skip the rescale; any common
+  // reference gives the same O / l and m + log2(l), and P stays <= 2^kSlack.
+  constexpr float kSlack = 8.f;
+  float m = -INFINITY;
+  float l = 0.f;
 
   // lane offsets for the transposing V reads (row = key, column = d)
   const int g16 = lane >> 4;
@@ -136,14 +140,9 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
     for (int r = 0; r < PER; ++r) {
       const int ci = tid + r * (FWD_NW * 64);
       const int row = ci / CH, col = (ci % CH) * 8;
-      const int key = t * FWD_BN + row;
-      if (key < N) {
-        kreg[r] = gload16(K + (size_t)key * D + col);
-        vreg[r] = gload16(V + (size_t)key * D + col);
-      } else {
-        kreg[r] = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
-        vreg[r] = (s16x8){0, 0, 0, 0, 0, 0, 0, 0};
-      }
+      const unsigned int off = (unsigned)((t * FWD_BN + row) * D + col) * 2u;
+      kreg[r] = bload16(rk, off);
+      vreg[r] = bload16(rv, off);
     }
   };
   auto lstore_tile = [&](int buf) {
@@ -156,16 +155,17 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
     }
   };
 
-  if (ntiles > 0) {
-    gload_tile(tile_at(0));
-    lstore_tile(0);
-  }
+  // Loads are issued on every path (indices clamped; buffer loads make a
+  // redundant or out-of-range tile harmless) so that the compiler can count
+  // outstanding loads exactly and never waits on a prefetch before computing.
+  gload_tile(ntiles > 0 ? tile_at(0) : 0);
+  lstore_tile(0);
   __syncthreads();
 
   for (int e = 0; e < ntiles; ++e) {
     const int buf = e & 1;
     const int ks = tile_at(e) * FWD_BN;
-    if (e + 1 < ntiles) gload_tile(tile_at(e + 1));
+    gload_tile(tile_at(e + 1 < ntiles ? e + 1 : e));
 
     const bool active = !(CAUSAL && ks > qw + 31);  // wave-uniform
     if (active) {
@@ -201,16 +201,18 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[0][i]);
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[1][i]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const float m_new = fmaxf(m, mx * c);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float corr = fast_exp2(m - m_use);
-      m = m_new;
-      l *= corr;
+      mx = fmaxf(mx, swap_halves(mx)) * c;
+      if (__any(mx > m + kSlack)) {  // wave-uniform: raise the reference, rescale
+        const float m_new = fmaxf(m, mx);
+        const float corr = fast_exp2(m - ((m_new == -INFINITY) ? 0.f : m_new));
+        m = m_new;
+        l *= corr;
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt)
+        for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[dt][i] *= corr;
+          for (int i = 0; i < 16; ++i) acc[dt][i] *= corr;
+      }
+      const float m_use = (m == -INFINITY) ? 0.f : m;  // a row with no visible key yet
 
       unsigned int pk[2][8];
 #pragma unroll
@@ -237,25 +239,23 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
             acc[dt] = mfma32<T>(va, pb, acc[dt]);
           }
     }
-    if (e + 1 < ntiles) lstore_tile(buf ^ 1);
+    lstore_tile(buf ^ 1);
     __syncthreads();
   }
 
   const float lt = l + swap_halves(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const float lse = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
-  if (qi < N) {
-    unsigned short* Op = (unsigned short*)a.o + (qrow0 + qi) * D;
+  const rsrc_t ro = make_rsrc((unsigned short*)a.o + qrow0 * D, head_bytes);
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
+  for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x2 v2 = {pack2<T>(acc[dt][4 * j] * inv, acc[dt][4 * j + 1] * inv),
-                    pack2<T>(acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv)};
-        *reinterpret_cast<u32x2*>(Op + 32 * dt + 8 * j + 4 * hh) = v2;
-      }
-    if (hh == 0) a.lse[qrow0 + qi] = lse;
-  }
+    for (int j = 0; j < 4; ++j) {
+      u32x2 v2 = {pack2<T>(acc[dt][4 * j] * inv, acc[dt][4 * j + 1] * inv),
+                  pack2<T>(acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv)};
+      bstore8(ro, (unsigned)(qi * D + 32 * dt + 8 * j + 4 * hh) * 2u, v2);
+    }
+  if (hh == 0) bstore_f32(make_rsrc(a.lse + qrow0, (unsigned)N * 4u), (unsigned)qi * 4u, lse);
 }
 
 // float32: one query row per lane, fp32 FMA for every product, keys in LDS tiles.

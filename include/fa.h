@@ -31,9 +31,12 @@
  *   q, o, dO, dq : [B][H][N][d]        k, v, dk, dv : [B][Hkv][N][d]
  *   lse          : [B][H][N] float32
  * q, k, v, o, dO, dq, dk, dv share one element type, FA_BF16, FA_F16 or FA_F32
- * (FA_F32: forward only). Every pointer must be 16-byte aligned. d is 32, 64
- * or 128; N >= 1 is any length (no multiple-of-tile restriction); H must be a
- * multiple of Hkv; scale must be finite and >= 0 (1/sqrt(d) is the usual one).
+ * (FA_F32: forward only). q, k, v, o, dO, dq, dk, dv must be 16-byte aligned,
+ * lse 4-byte aligned. d is 32, 64 or 128; N >= 1 is any length (no
+ * multiple-of-tile restriction) with N * d < 2^30 and B * H * N < 2^31; with a
+ * block mask, ceil(N / 128) <= 2048 (else FA_ERR_UNSUPPORTED); H must be a
+ * multiple of Hkv; B <= 65535; scale must be finite and >= 0 (1/sqrt(d) is the
+ * usual one).
  *
  * Ownership. The caller owns every buffer. The library allocates no device or
  * host memory and keeps no state between calls; outputs are overwritten, never

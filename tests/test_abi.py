@@ -76,7 +76,7 @@ def fwd(lib, q=GOOD, k=GOOD, v=GOOD, o=GOOD, lse=GOOD, B=1, H=2, Hkv=1, N=256, d
     dict(B=0), dict(H=0), dict(Hkv=0), dict(N=0), dict(N=-5), dict(H=3, Hkv=2),
     dict(d=16), dict(d=96), dict(d=256), dict(dtype=3), dict(dtype=-1),
     dict(scale=float("nan")), dict(scale=float("inf")), dict(scale=-0.5),
-    dict(B=70000), dict(B=1 << 16, H=1 << 15, N=8),
+    dict(B=70000), dict(B=1 << 16, H=1 << 15, N=8), dict(N=1 << 23, d=128), dict(N=(1 << 24) + 1, d=64),
 ])
 def test_forward_rejects(lib, bad):
     assert fwd(lib, **bad) == EINVAL
