@@ -24,8 +24,8 @@ int check_shape(int B, int H, int Hkv, int N, int d, float scale, int dtype) {
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
   const long long rows = (long long)B * H * N;
-  // one head of a tensor (and of the float32 dq accumulator) must be addressable
-  // with 32-bit byte offsets: N * d * 4 < 2^32
+  // one head of a tensor must be addressable with 32-bit byte offsets (with room
+  // to spare: N * d * 4 < 2^32)
   if (rows > INT32_MAX || (long long)N * d >= (1LL << 30)) return FA_ERR_INVALID_ARG;
   if (B > 65535 || (N + 127) / 128 > 65535) return FA_ERR_INVALID_ARG;
   return FA_OK;
@@ -51,9 +51,6 @@ fa::AttnShape make_shape(int B, int H, int Hkv, int N, int d, float scale, int c
 constexpr int kMaxMaskBlocks = 2048;
 
 size_t dvec_bytes(int B, int H, int N) { return round_up((size_t)B * H * N * sizeof(float)); }
-size_t dqacc_bytes(int B, int H, int N, int d) {
-  return round_up((size_t)B * H * N * d * sizeof(float));
-}
 
 int check_backward(const void* q, const void* k, const void* v, const void* o, const float* lse,
                    const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N,
@@ -68,7 +65,7 @@ int check_backward(const void* q, const void* k, const void* v, const void* o, c
   if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   if (block_mask && (N + 127) / 128 > kMaxMaskBlocks) return FA_ERR_UNSUPPORTED;
   if (!workspace || ((uintptr_t)workspace % kAlign) != 0) return FA_ERR_WORKSPACE;
-  if (workspace_bytes < dvec_bytes(B, H, N) + dqacc_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
+  if (workspace_bytes < dvec_bytes(B, H, N)) return FA_ERR_WORKSPACE;
   return FA_OK;
 }
 
@@ -98,7 +95,8 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
 
 size_t fa_backward_workspace_size(int B, int H, int Hkv, int N, int d, int dtype) {
   if (check_shape(B, H, Hkv, N, d, 1.0f, dtype) != FA_OK || dtype == FA_F32) return 0;
-  return dvec_bytes(B, H, N) + dqacc_bytes(B, H, N, d);
+  (void)d;
+  return dvec_bytes(B, H, N);
 }
 
 int fa_backward_stage(int stage, const void* q, const void* k, const void* v, const void* o,
@@ -121,7 +119,6 @@ int fa_backward_stage(int stage, const void* q, const void* k, const void* v, co
   a.dk = dk;
   a.dv = dv;
   a.dvec = (float*)workspace;
-  a.dqacc = (float*)((char*)workspace + dvec_bytes(B, H, N));
   (void)hipGetLastError();
   return fa::launch_backward_stage(stage, a, dtype, (hipStream_t)stream) == hipSuccess ? FA_OK
                                                                                         : FA_ERR_HIP;

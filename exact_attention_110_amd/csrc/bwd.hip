@@ -1,43 +1,50 @@
 // Backward pass of IO-aware exact attention on gfx950.
 //
-// The probabilities are never read back from memory: each key block
-// recomputes P = exp(S - LSE) tile by tile from Q, K and the saved per-row
-// log-sum-exp (nadeemcite.github.io summary "FlashAttention: Fast and
-// Memory-Efficient Exact Attention with IO-Awareness", Core Idea item 3; the
-// pranaymahendrakar.com lesson "FlashAttention", Researcher tier, "IO
-// complexity"). The gradient formulas are the chain rule through the row
-// softmax (not on the pages):
+// The probabilities are never read back from memory: they are recomputed tile
+// by tile as P = exp(S - LSE) from Q, K and the saved per-row log-sum-exp
+// (nadeemcite.github.io summary "FlashAttention: Fast and Memory-Efficient
+// Exact Attention with IO-Awareness", Core Idea item 3; the pranaymahendrakar.com
+// lesson "FlashAttention", Researcher tier, "IO complexity"). The gradient
+// formulas are the chain rule through the row softmax (not on the pages):
 //   dV_j = sum_i P_ij dO_i          dP_ij = dO_i . V_j
 //   D_i  = sum_d dO_id O_id         dS_ij = P_ij (dP_ij - D_i)
 //   dK_j = scale sum_i dS_ij Q_i    dQ_i  = scale sum_j dS_ij K_j
+// (dS is kept unscaled; dK and dQ take the scale once, at their final rounding)
 //
-// Three stages, all on the caller's stream:
-//  0. preprocess: D per query row (fp32) and a cleared fp32 dQ accumulator;
-//  1. key-block kernel: one workgroup per 128 keys of one (batch, kv head),
-//     four waves of 32 keys. K and V stay in registers as MFMA operands and dK,
-//     dV accumulate in registers across every query block (and every query head
-//     of a grouped-query group). For each 64-row query block it recomputes
-//     S = Q K^T and dP = dO V^T on v_mfma_f32_32x32x16, forms P and dS, adds
-//     dO^T P and Q^T dS into dV^T and dK^T (the 32x32 result layout of S is
-//     already the B operand of those products; dO^T and Q^T come from LDS with
-//     the gfx950 transposing read), stages dS in LDS and adds dS K into the
-//     fp32 dQ accumulator with global float atomics;
-//  2. convert: dQ = accumulator rounded to the element type.
-// Causal masking starts each key block at its diagonal query block; block
-// sparsity compacts the nonzero query blocks of the key block's mask column.
+// Three stages on the caller's stream, none with atomics (dq, dk and dv are
+// each written once, so the backward pass is bitwise reproducible):
+//  0. D per query row, in fp32;
+//  1. key-block kernel (dK, dV): one workgroup per 128 keys of one (batch, kv
+//     head), four waves of 32 keys. K^T and V^T stay in registers as MFMA
+//     operands and dK^T, dV^T accumulate in registers across every 32-row
+//     query block (and every query head of a grouped-query group). The
+//     32x32 result layout of S = Q K^T is already the B operand of dV^T =
+//     dO^T P and dK^T = Q^T dS; dO^T and Q^T come from LDS through the gfx950
+//     transposing read. The step loop is software-pipelined: S and dP of the
+//     next query block are issued while this block's P and dS are formed.
+//  2. query-block kernel (dQ): one workgroup per 128 query rows, four waves of
+//     32 rows, laid out like the forward pass: S^T = K Q^T and dP^T = V dO^T
+//     with Q^T and dO^T in registers, so a lane owns one query row and its LSE
+//     and D are two scalars; dQ^T += K^T dS^T with K^T read transposed from LDS.
+// Recomputing S and dP in stage 2 costs two more contractions than scattering
+// dQ from stage 1, but a scatter needs floating-point atomics, which on this
+// chip are executed past the L2 and cost more than the contractions they save.
+// Causal masking trims both kernels to their diagonal; block sparsity
+// compacts the nonzero blocks of the mask column (stage 1) or row (stage 2).
+#include <type_traits>
+
 #include "common.hpp"
 #include "params.hpp"
 
 namespace fa {
 
-constexpr int BWD_NW = 4;              // waves per workgroup
-constexpr int BWD_BKV = 32 * BWD_NW;   // keys per workgroup (= mask block)
-constexpr int BWD_BQ = 64;             // query rows per step
-constexpr int BWD_LIST = 2048;         // capacity of the compacted mask-row list
-static_assert(BWD_BKV == 128, "a key-block workgroup must cover exactly one mask block column");
+// LDS row pitch (bytes) of tiles read both with 16-byte row reads and with
+// transposing reads: rows land on distinct 16-byte bank groups for the first
+// and on distinct 32-byte groups for the second (64 banks of 4 bytes).
+constexpr int lds_pitch(int row_bytes) { return row_bytes == 128 ? 208 : row_bytes + 48; }
 
 // ---------------------------------------------------------------------------
-// stage 0: D = rowsum(dO * O) in fp32, and dq accumulator := 0
+// stage 0: D = rowsum(dO * O) in fp32
 // ---------------------------------------------------------------------------
 template <class T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int rows) {
@@ -54,9 +61,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int rows) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       sum = fmaf(to_f32<T>((unsigned short)o[j]), to_f32<T>((unsigned short)g[j]), sum);
-    f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4*>(a.dqacc + off) = z;
-    *reinterpret_cast<f32x4*>(a.dqacc + off + 4) = z;
   }
 #pragma unroll
   for (int msk = CH / 2; msk >= 1; msk >>= 1) sum += __shfl_xor(sum, msk, 64);
@@ -64,40 +68,45 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int rows) {
 }
 
 // ---------------------------------------------------------------------------
-// stage 1: per key block, recompute P; accumulate dV, dK; scatter dQ
+// stage 1: per key block, recompute P and dS; accumulate dV and dK
 // ---------------------------------------------------------------------------
+constexpr int KV_NW = 4;              // waves per workgroup
+constexpr int KV_BKV = 32 * KV_NW;    // keys per workgroup (= mask block)
+constexpr int KV_BQ = 32;             // query rows per step
+constexpr int KV_R = 128 / KV_BQ;     // steps per 128-row mask block
+constexpr int MASK_LIST = 2048;       // capacity of a compacted mask row / column
+static_assert(KV_BKV == 128, "a key-block workgroup must cover exactly one mask block column");
+
+// position of a step: query head h, index qi into the key block's query-block list
+struct StepPos {
+  int qi;
+  int h;
+};
+
 template <class T, int D, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(BWD_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
-  constexpr int QP = D * 2 + 32;        // Q / dO row pitch in LDS (bytes)
-  constexpr int KP = D * 2 + 32;        // K row pitch (bytes)
-  constexpr int SP = BWD_BQ * 2 + 32;   // dS row pitch: rows are keys, columns queries
-  constexpr int QBUF = BWD_BQ * QP;
-  constexpr int SBUF = BWD_BKV * SP;
+__global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
+  constexpr int BQ = KV_BQ;
+  constexpr int QP = lds_pitch(2 * D);   // Q / dO row pitch in LDS (bytes)
+  constexpr int QBUF = BQ * QP;
+  constexpr int NT = KV_NW * 64;         // threads
   constexpr int CH = D / 8;
-  constexpr int PERQ = BWD_BQ * CH / (BWD_NW * 64);
-  constexpr int PERK = BWD_BKV * CH / (BWD_NW * 64);
-  static_assert(PERQ >= 1 && (BWD_BQ * CH) % (BWD_NW * 64) == 0, "query loader shape");
-  static_assert(PERK >= 1 && (BWD_BKV * CH) % (BWD_NW * 64) == 0, "key loader shape");
-  static_assert(2 * BWD_BQ <= BWD_NW * 64, "row statistics loader shape");
+  constexpr int QCH = BQ * CH;           // 16-byte chunks per query block
+  constexpr int PERQ = (QCH + NT - 1) / NT;
+  static_assert(QCH % NT == 0 || QCH < NT, "query loader shape");
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
-  constexpr int NQT = BWD_BQ / 32;     // 32-row query tiles per step
-  constexpr int NDQ = NQT * ND;        // 32x32 dQ tiles per step
 
-  // LDS: Q and dO blocks (double-buffered), per-row statistics (double-buffered),
-  // the K block, dS (double-buffered) and the compacted mask list
-  __shared__ __attribute__((aligned(16))) char smem_raw[4 * QBUF + 2 * 2 * BWD_BQ * 4 + BWD_BKV * KP +
-                                                        2 * SBUF + (MASK ? 2 * BWD_LIST + 16 : 16)];
+  // LDS: Q, dO and row statistics in three rotating buffers (step e uses e % 3;
+  // while step e is consumed, step e + 1 is already resident and step e + 2 is
+  // written into the buffer step e - 1 used) and the compacted mask list
+  __shared__ __attribute__((aligned(16))) char smem_raw[6 * QBUF + 3 * NT * 4 + (MASK ? 2 * MASK_LIST + 16 : 16)];
   lds_t* smem = (lds_t*)smem_raw;
-  lds_t* qbuf = smem;                      // [2][BQ][QP]
-  lds_t* obuf = qbuf + 2 * QBUF;           // dO, [2][BQ][QP]
-  lds_t* stat = obuf + 2 * QBUF;           // [2][2][BQ] float: log2-scaled LSE, D
-  lds_t* kl = stat + 2 * 2 * BWD_BQ * 4;   // K block, [BKV][KP]
-  lds_t* dsl = kl + BWD_BKV * KP;          // dS, [2][BKV][SP]
-  __attribute__((address_space(3))) short* blist =
-      (__attribute__((address_space(3))) short*)(dsl + 2 * SBUF);
+  lds_t* qbuf = smem;                   // [3][BQ][QP]
+  lds_t* obuf = qbuf + 3 * QBUF;        // dO, [3][BQ][QP]
+  lds_t* stat = obuf + 3 * QBUF;        // [3][NT] float: log2-scaled LSE in 0..BQ-1, D in BQ..2BQ-1
+  __attribute__((address_space(3))) short* blist = (__attribute__((address_space(3))) short*)(stat + 3 * NT * 4);
   __attribute__((address_space(3))) int* bcount =
-      (__attribute__((address_space(3))) int*)(dsl + 2 * SBUF + (MASK ? 2 * BWD_LIST : 0));
+      (__attribute__((address_space(3))) int*)(stat + 3 * NT * 4 + (MASK ? 2 * MASK_LIST : 0));
 
   const AttnShape& s = a.s;
   const int N = s.N;
@@ -108,10 +117,9 @@ __global__ __launch_bounds__(BWD_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
   const int coff = 16 * (g16 & 1) + 4 * (lane & 3);       // transposing-read column offset
   // grid = (Hkv, key blocks, B); under causal masking block 0 has the most work
   const int hk = blockIdx.x, kblk = blockIdx.y, b = blockIdx.z;
-  const int k0 = kblk * BWD_BKV;
+  const int k0 = kblk * KV_BKV;
   const int kj = k0 + 32 * w + l32;  // this lane's key (its column of S)
   const float c = s.scale * kLog2e;
-  const float scale = s.scale;
 
   // per-head buffer resources: rows past N read as zeros, writes past N are dropped
   const unsigned int head_bytes = (unsigned int)N * D * 2;
@@ -119,28 +127,22 @@ __global__ __launch_bounds__(BWD_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
   const rsrc_t rk = make_rsrc((const unsigned short*)a.k + krow0 * D, head_bytes);
   const rsrc_t rv = make_rsrc((const unsigned short*)a.v + krow0 * D, head_bytes);
 
-  // K^T and V^T operands: lane holds key kj, d = 16 ss + 8 hh + 0..7
+  // K^T and V^T operands: lane holds key kj, d = 16 ss + 8 hh + 0..7. Keys past
+  // N read as zeros; their dK, dV are never stored.
   s16x8 kf[NS], vf[NS];
 #pragma unroll
   for (int ss = 0; ss < NS; ++ss) {
     kf[ss] = bload16(rk, (unsigned)(kj * D + 16 * ss + 8 * hh) * 2u);
     vf[ss] = bload16(rv, (unsigned)(kj * D + 16 * ss + 8 * hh) * 2u);
   }
-  // the whole K block in LDS for the dQ product
-#pragma unroll
-  for (int r = 0; r < PERK; ++r) {
-    const int ci = tid + r * (BWD_NW * 64);
-    const int row = ci / CH, col = (ci % CH) * 8;
-    lds_write16(kl + row * KP + col * 2, bload16(rk, (unsigned)((k0 + row) * D + col) * 2u));
-  }
 
   // query blocks this key block meets
-  const int nqb_all = (N + BWD_BQ - 1) / BWD_BQ;
-  const int qb_first = CAUSAL ? k0 / BWD_BQ : 0;
+  const int nqb_all = (N + BQ - 1) / BQ;
+  const int qb_first = CAUSAL ? k0 / BQ : 0;
   int nq = nqb_all - qb_first;
   if constexpr (MASK) {
-    // mask rows I (128 queries = 2 steps) with mask[I][kblk] != 0, from the first one needed
-    const int i_first = qb_first / 2;
+    // mask rows I with mask[I][kblk] != 0, from the first one needed
+    const int i_first = qb_first / KV_R;
     if (w == 0) {
       int cnt = 0;
       for (int j0 = i_first; j0 < s.nb; j0 += 64) {
@@ -154,17 +156,18 @@ __global__ __launch_bounds__(BWD_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
     }
     __syncthreads();
     const int cnt = *bcount;
-    nq = 2 * cnt;
-    if (cnt > 0 && 2 * blist[cnt - 1] + 1 >= nqb_all) nq -= 1;  // half block past N
+    nq = KV_R * cnt;
+    if (cnt > 0) nq -= max(0, KV_R * (blist[cnt - 1] + 1) - nqb_all);  // steps past N
   }
-  auto qblock_at = [&](int e) -> int {
-    if constexpr (MASK) return 2 * blist[e >> 1] + (e & 1);
-    else return qb_first + e;
+  auto qblock_at = [&](int qi) -> int {
+    if constexpr (MASK) return KV_R * blist[qi / KV_R] + qi % KV_R;
+    else return qb_first + qi;
   };
-  const int nsteps = nq * s.G;  // every query head of the group, every query block
-  // divisor for step -> (head, query block); a key block with no visible query
-  // block (nq = 0, block-sparse only) still issues its first, unused prefetch
-  const int nqd = nq > 0 ? nq : 1;
+  // steps run over every query block of the list for each query head of the group
+  const int nsteps = nq * s.G;
+  auto advance = [&](StepPos p) -> StepPos {
+    return p.qi + 1 < nq ? StepPos{p.qi + 1, p.h} : StepPos{0, p.h + 1};
+  };
 
   f32x16 dka[ND], dva[ND];
 #pragma unroll
@@ -175,184 +178,152 @@ __global__ __launch_bounds__(BWD_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
       dva[dt][i] = 0.f;
     }
 
-  // prefetch of step e's Q and dO rows (registers) and its row statistics:
+  // prefetch of a step's Q and dO rows (registers) and its row statistics:
   // threads 0..BQ-1 take log2-scaled LSE, threads BQ..2BQ-1 take D
   s16x8 qreg[PERQ], oreg[PERQ];
   float sreg = 0.f;
-  auto gload_q = [&](int e) {
-    const int h = hk * s.G + e / nqd;
-    const int q0 = qblock_at(e % nqd) * BWD_BQ;
-    const size_t qrow0 = (size_t)(b * s.H + h) * N;
+  auto gload_q = [&](StepPos p) {
+    const int q0 = qblock_at(p.qi) * BQ;
+    const size_t qrow0 = (size_t)(b * s.H + p.h) * N;
     const rsrc_t rq = make_rsrc((const unsigned short*)a.q + qrow0 * D, head_bytes);
     const rsrc_t rg = make_rsrc((const unsigned short*)a.dO + qrow0 * D, head_bytes);
 #pragma unroll
     for (int r = 0; r < PERQ; ++r) {
-      const int ci = tid + r * (BWD_NW * 64);
+      // spare threads of a small block repeat the last chunk (same data, same place)
+      const int ci = min(tid + r * NT, QCH - 1);
       const int row = ci / CH, col = (ci % CH) * 8;
       const unsigned int off = (unsigned)((q0 + row) * D + col) * 2u;
       qreg[r] = bload16(rq, off);
       oreg[r] = bload16(rg, off);
     }
-    {
-      // threads 0..BQ-1: LSE in log2 units; BQ..2BQ-1: D. Rows past N, and rows
-      // that saw no key, get LSE = +inf so that their P is 0.
-      // (two wave-uniform resources; a per-lane choice of base would not be uniform)
-      const int q = q0 + (tid % BWD_BQ);
-      const float lv = bload_f32(make_rsrc(a.lse + qrow0, (unsigned)N * 4u), (unsigned)q * 4u);
-      const float dv = bload_f32(make_rsrc(a.dvec + qrow0, (unsigned)N * 4u), (unsigned)q * 4u);
-      const float L = (q < N && lv != -INFINITY) ? lv * kLog2e : INFINITY;
-      sreg = tid < BWD_BQ ? L : dv;
-    }
+    // rows past N, and rows that saw no key, get LSE = +inf so that their P is 0
+    // (two wave-uniform resources; a per-lane choice of base would not be uniform)
+    const int q = q0 + (tid % BQ);
+    const float lv = bload_f32(make_rsrc(a.lse + qrow0, (unsigned)N * 4u), (unsigned)q * 4u);
+    const float dv = bload_f32(make_rsrc(a.dvec + qrow0, (unsigned)N * 4u), (unsigned)q * 4u);
+    const float L = (q < N && lv != -INFINITY) ? lv * kLog2e : INFINITY;
+    sreg = tid < BQ ? L : dv;
   };
   auto lstore_q = [&](int buf) {
 #pragma unroll
     for (int r = 0; r < PERQ; ++r) {
-      const int ci = tid + r * (BWD_NW * 64);
+      const int ci = min(tid + r * NT, QCH - 1);
       const int row = ci / CH, col = (ci % CH) * 8;
       lds_write16(qbuf + buf * QBUF + row * QP + col * 2, qreg[r]);
       lds_write16(obuf + buf * QBUF + row * QP + col * 2, oreg[r]);
     }
-    if (tid < 2 * BWD_BQ)
-      *((__attribute__((address_space(3))) float*)(stat + buf * 2 * BWD_BQ * 4) + tid) = sreg;
+    // every thread writes its slot (only the first 2 BQ are read)
+    *((__attribute__((address_space(3))) float*)(stat + buf * NT * 4) + tid) = sreg;
   };
 
-  // dQ(q x d) += dS(q x key) K(key x d) over the block's 128 keys for the step
-  // whose dS sits in buffer sb; each wave takes whole 32x32 tiles of the 64 x D result
-  auto dq_phase = [&](int e, int sb) {
-    const int h = hk * s.G + e / nqd;
-    const int q0 = qblock_at(e % nqd) * BWD_BQ;
-    const size_t qrow0 = (size_t)(b * s.H + h) * N;
-    const rsrc_t racc = make_rsrc(a.dqacc + qrow0 * D, (unsigned)N * D * 4u);
-    const lds_t* ds = dsl + sb * SBUF;
-    for (int ti = w; ti < NDQ; ti += BWD_NW) {
-      const int qt = ti % NQT, dt = ti / NQT;
-      f32x16 acc;
+  // S = Q K^T and dP = dO V^T of this wave's 32 keys, from Q / dO buffer qbi
+  auto sdp = [&](int qbi, f32x16& sc, f32x16& dp) {
+    const lds_t* qb = qbuf + qbi * QBUF;
+    const lds_t* ob = obuf + qbi * QBUF;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int i = 0; i < 16; ++i) {
+      sc[i] = 0.f;
+      dp[i] = 0.f;
+    }
 #pragma unroll
-      for (int u = 0; u < BWD_BKV / 16; ++u) {
-        const lds_t* sp = ds + (16 * u + roff) * SP + (32 * qt + coff) * 2;
-        const lds_t* kp = kl + (16 * u + roff) * KP + (32 * dt + coff) * 2;
-        const s16x8 sa = concat(lds_read_tr(sp), lds_read_tr(sp + 8 * SP));
-        const s16x8 kb = concat(lds_read_tr(kp), lds_read_tr(kp + 8 * KP));
-        acc = mfma32<T>(sa, kb, acc);
-      }
-      // acc: column d = 32 dt + l32, rows q0 + 32 qt + 8 (i / 4) + 4 hh + i % 4
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int q = q0 + 32 * qt + 8 * (i >> 2) + 4 * hh + (i & 3);
-        batomic_add(racc, (unsigned)(q * D + 32 * dt + l32) * 4u, acc[i]);
-      }
+    for (int ss = 0; ss < NS; ++ss) {
+      const s16x8 qa = lds_read16(qb + l32 * QP + (16 * ss + 8 * hh) * 2);
+      const s16x8 ga = lds_read16(ob + l32 * QP + (16 * ss + 8 * hh) * 2);
+      sc = mfma32<T>(qa, kf[ss], sc);
+      dp = mfma32<T>(ga, vf[ss], dp);
     }
   };
 
-  // loads are issued on every path (indices clamped; buffer loads make a
-  // redundant block harmless) so that outstanding loads are counted exactly
-  gload_q(0);
-  lstore_q(0);
-  __syncthreads();
-
-  for (int e = 0; e < nsteps; ++e) {
-    const int buf = e & 1;
-    const int q0 = qblock_at(e % nqd) * BWD_BQ;
-    gload_q(e + 1 < nsteps ? e + 1 : e);
-
-    const lds_t* qb = qbuf + buf * QBUF;
-    const lds_t* ob = obuf + buf * QBUF;
+  // P and dS (unscaled) of a step from its S, dP and statistics buffer. Element
+  // i is query q0 + 8 (i / 4) + 4 hh + i % 4 of key kj; under causal masking it
+  // is kept only if 8 (i / 4) + i % 4 >= kj - q0 - 4 hh. Keys past N need no
+  // mask: their K and V rows read as zeros and nothing of theirs is stored.
+  unsigned int pk[8], sk[8];
+  auto probs = [&](const f32x16& sc, const f32x16& dp, int q0, int stb) {
     const __attribute__((address_space(3))) float* lsel =
-        (const __attribute__((address_space(3))) float*)(stat + buf * 2 * BWD_BQ * 4);
-    const __attribute__((address_space(3))) float* ddl = lsel + BWD_BQ;
+        (const __attribute__((address_space(3))) float*)(stat + stb * NT * 4);
+    const __attribute__((address_space(3))) float* ddl = lsel + BQ;
+    const int thr = kj - q0 - 4 * hh;
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const f32x4 L4 = *(const __attribute__((address_space(3))) f32x4*)(lsel + 8 * j4 + 4 * hh);
+      const f32x4 D4 = *(const __attribute__((address_space(3))) f32x4*)(ddl + 8 * j4 + 4 * hh);
+      float p[4], d2[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * j4 + r;
+        float pv = fast_exp2(fmaf(sc[i], c, -L4[r]));
+        if constexpr (CAUSAL) pv = (8 * j4 + r < thr) ? 0.f : pv;
+        p[r] = pv;
+        d2[r] = pv * (dp[i] - D4[r]);
+      }
+      pk[2 * j4] = pack2<T>(p[0], p[1]);
+      pk[2 * j4 + 1] = pack2<T>(p[2], p[3]);
+      sk[2 * j4] = pack2<T>(d2[0], d2[1]);
+      sk[2 * j4 + 1] = pack2<T>(d2[2], d2[3]);
+    }
+  };
 
-    // S = Q K^T and dP = dO V^T for this wave's 32 keys
-    f32x16 sc[NQT], dp[NQT];
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sc[qt][i] = 0.f;
-        dp[qt][i] = 0.f;
-      }
-#pragma unroll
-    for (int ss = 0; ss < NS; ++ss)
-#pragma unroll
-      for (int qt = 0; qt < NQT; ++qt) {
-        const s16x8 qa = lds_read16(qb + (32 * qt + l32) * QP + (16 * ss + 8 * hh) * 2);
-        sc[qt] = mfma32<T>(qa, kf[ss], sc[qt]);
-        const s16x8 ga = lds_read16(ob + (32 * qt + l32) * QP + (16 * ss + 8 * hh) * 2);
-        dp[qt] = mfma32<T>(ga, vf[ss], dp[qt]);
-      }
-
-    // P and dS; element i of tile qt is query q0 + 32 qt + 8 (i / 4) + 4 hh + i % 4, key kj
-    const bool need_mask = (CAUSAL && q0 < k0 + BWD_BKV) || (k0 + BWD_BKV > N);
-    unsigned int pk[NQT][8], sk[NQT][8];
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt)
-#pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const f32x4 L4 = *(const __attribute__((address_space(3))) f32x4*)(lsel + 32 * qt + 8 * j4 + 4 * hh);
-        const f32x4 D4 = *(const __attribute__((address_space(3))) f32x4*)(ddl + 32 * qt + 8 * j4 + 4 * hh);
-        float p[4], d2[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 4 * j4 + r;
-          float pv = fast_exp2(fmaf(sc[qt][i], c, -L4[r]));
-          if (need_mask) {
-            const int q = q0 + 32 * qt + 8 * j4 + 4 * hh + r;
-            if ((CAUSAL && kj > q) || kj >= N) pv = 0.f;
-          }
-          p[r] = pv;
-          d2[r] = pv * (dp[qt][i] - D4[r]) * scale;
-        }
-        pk[qt][2 * j4] = pack2<T>(p[0], p[1]);
-        pk[qt][2 * j4 + 1] = pack2<T>(p[2], p[3]);
-        sk[qt][2 * j4] = pack2<T>(d2[0], d2[1]);
-        sk[qt][2 * j4 + 1] = pack2<T>(d2[2], d2[3]);
-      }
-    // dS into LDS as [key][query]: 4 consecutive queries per 8-byte write
-    lds_t* dsw = dsl + buf * SBUF;
-#pragma unroll
-    for (int qt = 0; qt < NQT; ++qt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x2 v2 = {sk[qt][2 * j], sk[qt][2 * j + 1]};
-        lds_write8(dsw + (32 * w + l32) * SP + (32 * qt + 8 * j + 4 * hh) * 2, v2);
-      }
-
-    // dV^T(d x key) += dO^T(d x q) P(q x key); dK^T += Q^T dS. B operand k-slot j of
-    // step (qt, u) is query 32 qt + 16 u + 8 (j / 4) + 4 hh + j % 4.
+  // dV^T(d x key) += dO^T(d x q) P(q x key); dK^T += Q^T dS. B operand k-slot j
+  // of step u is query 16 u + 8 (j / 4) + 4 hh + j % 4, matched by the reads.
+  auto dvdk = [&](int qbi) {
+    const lds_t* qb = qbuf + qbi * QBUF;
+    const lds_t* ob = obuf + qbi * QBUF;
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-      for (int qt = 0; qt < NQT; ++qt)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int off = (32 * qt + 16 * u + roff) * QP + (32 * dt + coff) * 2;
-          const s16x8 ga = concat(lds_read_tr(ob + off), lds_read_tr(ob + off + 8 * QP));
-          const s16x8 qa = concat(lds_read_tr(qb + off), lds_read_tr(qb + off + 8 * QP));
-          dva[dt] = mfma32<T>(ga, as_operand(pk[qt][4 * u], pk[qt][4 * u + 1], pk[qt][4 * u + 2],
-                                             pk[qt][4 * u + 3]), dva[dt]);
-          dka[dt] = mfma32<T>(qa, as_operand(sk[qt][4 * u], sk[qt][4 * u + 1], sk[qt][4 * u + 2],
-                                             sk[qt][4 * u + 3]), dka[dt]);
-        }
+      for (int u = 0; u < 2; ++u) {
+        const int off = (16 * u + roff) * QP + (32 * dt + coff) * 2;
+        const s16x8 ga = concat(lds_read_tr(ob + off), lds_read_tr(ob + off + 8 * QP));
+        const s16x8 qa = concat(lds_read_tr(qb + off), lds_read_tr(qb + off + 8 * QP));
+        dva[dt] = mfma32<T>(ga, as_operand(pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]), dva[dt]);
+        dka[dt] = mfma32<T>(qa, as_operand(sk[4 * u], sk[4 * u + 1], sk[4 * u + 2], sk[4 * u + 3]), dka[dt]);
+      }
+  };
 
-    // dQ of the previous step: its dS was completed by every wave before the
-    // barrier that ended that step
-    if (e > 0) dq_phase(e - 1, buf ^ 1);
-
-    lstore_q(buf ^ 1);
+  // Software pipeline. Iteration e: S and dP of step e + 1, P and dS of step e,
+  // dV and dK of step e, then step e + 2 into the buffer step e - 1 used; one
+  // barrier per step. Loads are issued on every path (indices clamped; buffer
+  // loads make a redundant block harmless) so the loop body stays one basic
+  // block and outstanding loads are counted exactly.
+  StepPos cur{0, hk * s.G};
+  StepPos nxt = nsteps > 1 ? advance(cur) : cur;
+  gload_q(cur);
+  lstore_q(0);
+  gload_q(nxt);
+  lstore_q(1);
+  __syncthreads();
+  f32x16 sc, dp;
+  sdp(0, sc, dp);
+  int b0 = 0;  // buffer of step e (e % 3)
+  for (int e = 0; e < nsteps; ++e) {
+    const int b1 = b0 == 2 ? 0 : b0 + 1;   // step e + 1
+    const int b2 = b1 == 2 ? 0 : b1 + 1;   // step e + 2 (= step e - 1's)
+    const StepPos nn = e + 2 < nsteps ? advance(nxt) : nxt;
+    gload_q(nn);
+    f32x16 sc_n, dp_n;
+    sdp(b1, sc_n, dp_n);
+    probs(sc, dp, qblock_at(cur.qi) * BQ, b0);
+    dvdk(b0);
+    lstore_q(b2);
     __syncthreads();
+    sc = sc_n;
+    dp = dp_n;
+    cur = nxt;
+    nxt = nn;
+    b0 = b1;
   }
-  if (nsteps > 0) dq_phase(nsteps - 1, (nsteps - 1) & 1);
 
-  // dK^T / dV^T: lane holds key kj, d = 32 dt + 8 j + 4 hh + 0..3
+  // dK^T / dV^T: lane holds key kj, d = 32 dt + 8 j + 4 hh + 0..3; dK takes the scale
+  const float scale = s.scale;
   const rsrc_t rdk = make_rsrc((unsigned short*)a.dk + krow0 * D, head_bytes);
   const rsrc_t rdv = make_rsrc((unsigned short*)a.dv + krow0 * D, head_bytes);
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      u32x2 kv = {pack2<T>(dka[dt][4 * j], dka[dt][4 * j + 1]),
-                  pack2<T>(dka[dt][4 * j + 2], dka[dt][4 * j + 3])};
+      u32x2 kv = {pack2<T>(dka[dt][4 * j] * scale, dka[dt][4 * j + 1] * scale),
+                  pack2<T>(dka[dt][4 * j + 2] * scale, dka[dt][4 * j + 3] * scale)};
       u32x2 vv = {pack2<T>(dva[dt][4 * j], dva[dt][4 * j + 1]),
                   pack2<T>(dva[dt][4 * j + 2], dva[dt][4 * j + 3])};
       const unsigned int off = (unsigned)(kj * D + 32 * dt + 8 * j + 4 * hh) * 2u;
@@ -362,23 +333,234 @@ __global__ __launch_bounds__(BWD_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// stage 2: dq = accumulator, rounded to the element type
+// stage 2: per query block, recompute P and dS; accumulate dQ
 // ---------------------------------------------------------------------------
-template <class T>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a, size_t n8) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
-    const f32x4 x = *reinterpret_cast<const f32x4*>(a.dqacc + 8 * i);
-    const f32x4 y = *reinterpret_cast<const f32x4*>(a.dqacc + 8 * i + 4);
-    u32x4 r = {pack2<T>(x[0], x[1]), pack2<T>(x[2], x[3]), pack2<T>(y[0], y[1]),
-               pack2<T>(y[2], y[3])};
-    *reinterpret_cast<u32x4*>((unsigned short*)a.dq + 8 * i) = r;
+constexpr int Q_NW = 4;              // waves per workgroup
+constexpr int Q_BM = 32 * Q_NW;      // query rows per workgroup (= mask block)
+#ifndef FA_Q_BN
+#define FA_Q_BN 32
+#endif
+#ifndef FA_Q_OCC
+#define FA_Q_OCC 2
+#endif
+constexpr int Q_BN = FA_Q_BN;        // keys per tile
+constexpr int Q_T2 = Q_BN / 32;      // 32-key halves per tile
+constexpr int Q_R = 128 / Q_BN;      // tiles per 128-key mask block
+static_assert(Q_BM == 128, "a query-block workgroup must cover exactly one mask block row");
+
+template <class T, int D, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
+  constexpr int KP = lds_pitch(2 * D);   // K: 16-byte row reads and transposing reads
+  constexpr int VP = D * 2 + 16;         // V: 16-byte row reads only
+  constexpr int KBUF = Q_BN * KP;
+  constexpr int VBUF = Q_BN * VP;
+  constexpr int NT = Q_NW * 64;
+  constexpr int CH = D / 8;
+  constexpr int TCH = Q_BN * CH;         // 16-byte chunks per tile per tensor
+  constexpr int PER = (TCH + NT - 1) / NT;
+  static_assert(TCH % NT == 0 || TCH < NT, "tile loader shape");
+  constexpr int NS = D / 16;
+  constexpr int ND = D / 32;
+
+  __shared__ __attribute__((aligned(16))) char smem_raw[2 * KBUF + 2 * VBUF + (MASK ? 2 * MASK_LIST + 16 : 16)];
+  lds_t* kbuf = (lds_t*)smem_raw;
+  lds_t* vbuf = kbuf + 2 * KBUF;
+  __attribute__((address_space(3))) short* blist = (__attribute__((address_space(3))) short*)(vbuf + 2 * VBUF);
+  __attribute__((address_space(3))) int* bcount =
+      (__attribute__((address_space(3))) int*)(vbuf + 2 * VBUF + (MASK ? 2 * MASK_LIST : 0));
+
+  const AttnShape& s = a.s;
+  const int N = s.N;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int g16 = lane >> 4;
+  const int roff = 4 * (g16 >> 1) + ((lane & 15) >> 2);
+  const int coff = 16 * (g16 & 1) + 4 * (lane & 3);
+  // grid = (H, query blocks, B), as in the forward pass
+  const int qb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+  const int h = blockIdx.x, b = blockIdx.z;
+  const int hk = h / s.G;
+  const size_t qrow0 = (size_t)(b * s.H + h) * N;
+  const size_t krow0 = (size_t)(b * s.Hkv + hk) * N;
+  const unsigned int head_bytes = (unsigned int)N * D * 2;
+  const rsrc_t rq = make_rsrc((const unsigned short*)a.q + qrow0 * D, head_bytes);
+  const rsrc_t rg = make_rsrc((const unsigned short*)a.dO + qrow0 * D, head_bytes);
+  const rsrc_t rk = make_rsrc((const unsigned short*)a.k + krow0 * D, head_bytes);
+  const rsrc_t rv = make_rsrc((const unsigned short*)a.v + krow0 * D, head_bytes);
+  const int q0 = qb * Q_BM;
+  const int qw = q0 + 32 * w;
+  const int qi = qw + l32;   // this lane's query row
+  const float c = s.scale * kLog2e;
+
+  // Q^T and dO^T operands: lane holds query qi, d = 16 ss + 8 hh + 0..7
+  s16x8 qf[NS], gf[NS];
+#pragma unroll
+  for (int ss = 0; ss < NS; ++ss) {
+    qf[ss] = bload16(rq, (unsigned)(qi * D + 16 * ss + 8 * hh) * 2u);
+    gf[ss] = bload16(rg, (unsigned)(qi * D + 16 * ss + 8 * hh) * 2u);
   }
+  // this lane's row statistics; a row past N, or one that saw no key, keeps P = 0
+  const float lv = bload_f32(make_rsrc(a.lse + qrow0, (unsigned)N * 4u), (unsigned)qi * 4u);
+  const float dd = bload_f32(make_rsrc(a.dvec + qrow0, (unsigned)N * 4u), (unsigned)qi * 4u);
+  const float lse2 = (qi < N && lv != -INFINITY) ? lv * kLog2e : INFINITY;
+
+  const int kend = CAUSAL ? min(N, q0 + Q_BM) : N;
+  const int ntile_all = (kend + Q_BN - 1) / Q_BN;
+  int ntiles = ntile_all;
+  if constexpr (MASK) {
+    const int nbk = (kend + 127) / 128;
+    if (w == 0) {
+      int cnt = 0;
+      for (int j0 = 0; j0 < nbk; j0 += 64) {
+        const int j = j0 + lane;
+        const bool keep = j < nbk && s.mask[(size_t)qb * s.nb + j] != 0;
+        const unsigned long long bal = __ballot(keep);
+        if (keep) blist[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (short)j;
+        cnt += __popcll(bal);
+      }
+      if (lane == 0) *bcount = cnt;
+    }
+    __syncthreads();
+    const int cnt = *bcount;
+    ntiles = Q_R * cnt;
+    if (cnt > 0) ntiles -= max(0, Q_R * (blist[cnt - 1] + 1) - ntile_all);  // tiles past kend
+  }
+  auto tile_at = [&](int e) -> int {
+    if constexpr (MASK) return Q_R * blist[e / Q_R] + e % Q_R;
+    else return e;
+  };
+
+  f32x16 acc[ND];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+
+  s16x8 kreg[PER], vreg[PER];
+  auto gload_tile = [&](int t) {
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      // spare threads of a small tile repeat the last chunk (same data, same place)
+      const int ci = min(tid + r * NT, TCH - 1);
+      const int row = ci / CH, col = (ci % CH) * 8;
+      const unsigned int off = (unsigned)((t * Q_BN + row) * D + col) * 2u;
+      kreg[r] = bload16(rk, off);
+      vreg[r] = bload16(rv, off);
+    }
+  };
+  auto lstore_tile = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int ci = min(tid + r * NT, TCH - 1);
+      const int row = ci / CH, col = (ci % CH) * 8;
+      lds_write16(kbuf + buf * KBUF + row * KP + col * 2, kreg[r]);
+      lds_write16(vbuf + buf * VBUF + row * VP + col * 2, vreg[r]);
+    }
+  };
+
+  gload_tile(ntiles > 0 ? tile_at(0) : 0);
+  lstore_tile(0);
+  __syncthreads();
+
+  for (int e = 0; e < ntiles; ++e) {
+    const int buf = e & 1;
+    const int ks = tile_at(e) * Q_BN;
+    gload_tile(tile_at(e + 1 < ntiles ? e + 1 : e));
+
+    const bool active = !(CAUSAL && ks > qw + 31);  // wave-uniform
+    if (active) {
+      const lds_t* kb = kbuf + buf * KBUF;
+      const lds_t* vb = vbuf + buf * VBUF;
+      // S^T = K Q^T and dP^T = V dO^T for the tile's keys (32-key halves)
+      f32x16 sc[Q_T2], dp[Q_T2];
+#pragma unroll
+      for (int t2 = 0; t2 < Q_T2; ++t2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sc[t2][i] = 0.f;
+          dp[t2][i] = 0.f;
+        }
+#pragma unroll
+      for (int ss = 0; ss < NS; ++ss)
+#pragma unroll
+        for (int t2 = 0; t2 < Q_T2; ++t2) {
+          const s16x8 ka = lds_read16(kb + (32 * t2 + l32) * KP + (16 * ss + 8 * hh) * 2);
+          const s16x8 va = lds_read16(vb + (32 * t2 + l32) * VP + (16 * ss + 8 * hh) * 2);
+          sc[t2] = mfma32<T>(ka, qf[ss], sc[t2]);
+          dp[t2] = mfma32<T>(va, gf[ss], dp[t2]);
+        }
+      // dS for query qi and key ks + 32 t2 + 8 (i / 4) + 4 hh + i % 4. Causal: kept
+      // only if 32 t2 + 8 (i / 4) + i % 4 <= qi - ks - 4 hh. Keys past N read as
+      // zeros, so their dS multiplies a zero row of K and needs no mask.
+      const bool diag = CAUSAL && ks + Q_BN - 1 > qw;
+      const int thr = qi - ks - 4 * hh;
+      unsigned int sk[Q_T2][8];
+      auto ds_tile = [&](auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
+#pragma unroll
+        for (int t2 = 0; t2 < Q_T2; ++t2)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            float v2[2];
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+              const int i = 2 * j + r;
+              float pv = fast_exp2(fmaf(sc[t2][i], c, -lse2));
+              if constexpr (MASKED) pv = (32 * t2 + 8 * (i >> 2) + (i & 3) > thr) ? 0.f : pv;
+              v2[r] = pv * (dp[t2][i] - dd);
+            }
+            sk[t2][j] = pack2<T>(v2[0], v2[1]);
+          }
+      };
+      if (diag) ds_tile(std::true_type{});
+      else ds_tile(std::false_type{});
+      // dQ^T(d x q) += K^T(d x key) dS^T(key x q); B operand k-slot j of step
+      // (t2, u) is key 32 t2 + 16 u + 8 (j / 4) + 4 hh + j % 4, matched by the
+      // transposing reads of K
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int t2 = 0; t2 < Q_T2; ++t2)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const lds_t* kp = kb + (32 * t2 + 16 * u + roff) * KP + (32 * dt + coff) * 2;
+            const s16x8 ka = concat(lds_read_tr(kp), lds_read_tr(kp + 8 * KP));
+            acc[dt] = mfma32<T>(ka, as_operand(sk[t2][4 * u], sk[t2][4 * u + 1], sk[t2][4 * u + 2],
+                                               sk[t2][4 * u + 3]), acc[dt]);
+          }
+    }
+    lstore_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // dQ = scale * acc; lane holds query qi, d = 32 dt + 8 j + 4 hh + 0..3
+  const float scale = s.scale;
+  const rsrc_t rdq = make_rsrc((unsigned short*)a.dq + qrow0 * D, head_bytes);
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x2 v2 = {pack2<T>(acc[dt][4 * j] * scale, acc[dt][4 * j + 1] * scale),
+                  pack2<T>(acc[dt][4 * j + 2] * scale, acc[dt][4 * j + 3] * scale)};
+      bstore8(rdq, (unsigned)(qi * D + 32 * dt + 8 * j + 4 * hh) * 2u, v2);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <class T, int D>
+static hipError_t launch_pre_t(const BwdArgs& a, hipStream_t st) {
+  const int rows = a.s.B * a.s.H * a.s.N;
+  const int rpb = 256 / (D / 8);
+  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((rows + rpb - 1) / rpb), dim3(256), 0, st, a, rows);
+  return hipGetLastError();
 }
 
 template <class T, int D>
 static hipError_t launch_kv_t(const BwdArgs& a, hipStream_t st) {
-  const dim3 grid(a.s.Hkv, (a.s.N + BWD_BKV - 1) / BWD_BKV, a.s.B);
-  const dim3 block(BWD_NW * 64);
+  const dim3 grid(a.s.Hkv, (a.s.N + KV_BKV - 1) / KV_BKV, a.s.B);
+  const dim3 block(KV_NW * 64);
   const bool causal = a.s.causal != 0, mask = a.s.mask != nullptr;
   if (causal && mask) hipLaunchKernelGGL((bwd_kv_kernel<T, D, true, true>), grid, block, 0, st, a);
   else if (causal) hipLaunchKernelGGL((bwd_kv_kernel<T, D, true, false>), grid, block, 0, st, a);
@@ -388,36 +570,29 @@ static hipError_t launch_kv_t(const BwdArgs& a, hipStream_t st) {
 }
 
 template <class T, int D>
-static hipError_t launch_pre_t(const BwdArgs& a, hipStream_t st) {
-  const int rows = a.s.B * a.s.H * a.s.N;
-  const int rpb = 256 / (D / 8);
-  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((rows + rpb - 1) / rpb), dim3(256), 0, st, a, rows);
+static hipError_t launch_q_t(const BwdArgs& a, hipStream_t st) {
+  const dim3 grid(a.s.H, (a.s.N + Q_BM - 1) / Q_BM, a.s.B);
+  const dim3 block(Q_NW * 64);
+  const bool causal = a.s.causal != 0, mask = a.s.mask != nullptr;
+  if (causal && mask) hipLaunchKernelGGL((bwd_q_kernel<T, D, true, true>), grid, block, 0, st, a);
+  else if (causal) hipLaunchKernelGGL((bwd_q_kernel<T, D, true, false>), grid, block, 0, st, a);
+  else if (mask) hipLaunchKernelGGL((bwd_q_kernel<T, D, false, true>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((bwd_q_kernel<T, D, false, false>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
-template <class T>
-static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
-  const size_t n8 = (size_t)a.s.B * a.s.H * a.s.N * a.s.d / 8;
-  size_t blocks = (n8 + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL((bwd_dq_kernel<T>), dim3((unsigned)blocks), dim3(256), 0, st, a, n8);
-  return hipGetLastError();
+template <class T, int D>
+static hipError_t stage_d(int stage, const BwdArgs& a, hipStream_t st) {
+  if (stage == 0) return launch_pre_t<T, D>(a, st);
+  if (stage == 1) return launch_kv_t<T, D>(a, st);
+  return launch_q_t<T, D>(a, st);
 }
 
 template <class T>
 static hipError_t stage_t(int stage, const BwdArgs& a, hipStream_t st) {
-  const int d = a.s.d;
-  if (stage == 0) {
-    if (d == 32) return launch_pre_t<T, 32>(a, st);
-    if (d == 64) return launch_pre_t<T, 64>(a, st);
-    return launch_pre_t<T, 128>(a, st);
-  }
-  if (stage == 1) {
-    if (d == 32) return launch_kv_t<T, 32>(a, st);
-    if (d == 64) return launch_kv_t<T, 64>(a, st);
-    return launch_kv_t<T, 128>(a, st);
-  }
-  return launch_dq_t<T>(a, st);
+  if (a.s.d == 32) return stage_d<T, 32>(stage, a, st);
+  if (a.s.d == 64) return stage_d<T, 64>(stage, a, st);
+  return stage_d<T, 128>(stage, a, st);
 }
 
 hipError_t launch_backward_stage(int stage, const BwdArgs& a, int dtype, hipStream_t st) {

@@ -38,7 +38,6 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dvec;    // workspace: D = rowsum(dO * O), [B][H][N]
-  float* dqacc;   // workspace: float32 dq accumulator, [B][H][N][d]
 };
 
 // Internal launchers (return a hipError_t from the launch).

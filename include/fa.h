@@ -91,9 +91,8 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * fa_backward_workspace_size: bytes of device scratch fa_backward needs for
- * these sizes: one float32 per query row (D = rowsum(dO * O)) plus a float32
- * [B][H][N][d] accumulator for dq, each rounded up to 256 bytes. Linear in N.
- * Returns 0 for arguments fa_backward would reject.
+ * these sizes: one float32 per query row (D = rowsum(dO * O)), rounded up to
+ * 256 bytes. Linear in N. Returns 0 for arguments fa_backward would reject.
  */
 size_t fa_backward_workspace_size(int B, int H, int Hkv, int N, int d, int dtype);
 
@@ -103,7 +102,8 @@ size_t fa_backward_workspace_size(int B, int H, int Hkv, int N, int d, int dtype
  * k and lse. For grouped-query attention dk and dv of a kv head are summed
  * over its group of query heads. dtype is FA_BF16 or FA_F16 (FA_F32 returns
  * FA_ERR_UNSUPPORTED). causal, block_mask and scale must be those of the
- * forward call that produced o and lse.
+ * forward call that produced o and lse. No atomics are used: every output
+ * element is written once, so results are bitwise reproducible.
  *   workspace        device buffer of at least fa_backward_workspace_size()
  *                    bytes, 256-byte aligned; its contents on entry do not
  *                    matter and on return are unspecified. Owned by the caller;
@@ -119,9 +119,10 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
 /*
  * fa_backward_stage: one of the three stages fa_backward runs, in this order,
  * with the same arguments and the same workspace:
- *   stage 0  D = rowsum(dO * O) per query row; clears the dq accumulator
- *   stage 1  per key block: recompute P, then dv, dk and the dq contributions
- *   stage 2  dq = accumulator, rounded to dtype
+ *   stage 0  D = rowsum(dO * O) per query row, into the workspace
+ *   stage 1  per key block: recompute P and dS, write dk and dv
+ *   stage 2  per query block: recompute P and dS, write dq
+ * Stages 1 and 2 both need stage 0's result and nothing from each other.
  * Running stages 0, 1, 2 in order equals one fa_backward call. It exists so
  * that each stage can be timed on its own. Returns FA_OK or a negative status
  * (FA_ERR_INVALID_ARG for a stage outside 0..2).
