@@ -13,10 +13,15 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 Prints one JSON line. Besides the headline it carries:
 * "roofline": the dominant kernel's algorithmic FLOP per launch over its mean
   launch time, measured with HIP events on the stream the library launches on,
-  against the dense bf16 MFMA peak (2.5 PFLOP/s); "traffic" is filled from
-  rocprofv3 counter runs and is null here;
+  against the dense bf16 MFMA peak (2.5 PFLOP/s). The backward pass runs a
+  key-block kernel (S and dP recomputed, dV and dK: 4 contractions) and a
+  query-block kernel (S and dP recomputed, dQ: 3 contractions); each kernel is
+  credited with the contractions it performs. "traffic" is the kernel's HBM
+  bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary
+  (profiles/*_hbm_traffic.md), or null once the kernel's sources have changed
+  since the counters were taken;
 * "cpu_baseline": the float64 CPU oracle timed on a bounded sample of the same
-  workload (one head, forward+backward), in the same unit.
+  workload (six heads, forward+backward), in the same unit.
 """
 
 import argparse
@@ -49,6 +54,34 @@ def sparse_flops(w, mask, backward=True):
     return per * (2 + (5 if backward else 0))
 
 
+KERNEL_SOURCES = {
+    "fwd_kernel": ["fwd.hip", "common.hpp", "params.hpp"],
+    "bwd_pre_kernel": ["bwd.hip", "common.hpp", "params.hpp"],
+    "bwd_kv_kernel": ["bwd.hip", "common.hpp", "params.hpp"],
+    "bwd_q_kernel": ["bwd.hip", "common.hpp", "params.hpp"],
+}
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when the kernel's sources changed since it was taken."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, []):
+        with open(os.path.join(ROOT, "exact_attention_110_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    sha = h.hexdigest()
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*_hbm_traffic.md")):
+        for line in open(path):
+            if not line.startswith("traffic:"):
+                continue
+            kv = dict(tok.split("=", 1) for tok in line.split()[1:])
+            if kv.get("kernel") == kernel and kv.get("workload") == workload and kv.get("source-sha256") == sha:
+                return float(kv["bytes"])
+    return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -61,9 +94,9 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(w, x):
-    """Time the float64 oracle on the workload's checked heads (at most two),
-    forward + backward, on the host cores."""
+def cpu_baseline(w, x, n_heads=6):
+    """Time the float64 oracle on the first few (b, h) heads of the workload,
+    forward (+ backward), on the host cores: a bounded sample of the same work."""
     import oracle
     from exact_attention_110_amd import inputs as I
     try:
@@ -71,7 +104,7 @@ def cpu_baseline(w, x):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = 1
-    heads = I.check_heads(w)[:2]
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:n_heads]
     t0 = time.perf_counter()
     for b, h in heads:
         g = h // w.G
@@ -151,24 +184,31 @@ def main():
         return s.elapsed_time(e) / n  # ms
 
     n_ev = max(args.steps, 5)
+    per_contraction = fwd_flop / 2.0  # one N x N x d contraction of the workload
     t_fwd = event_time(lambda: binding.forward(q, k, v, w.scale, w.causal, mask, out=o, lse=lse), n_ev)
-    kernels = {"fwd_kernel": (t_fwd, fwd_flop)}
+    # kernel -> (mean launch time in ms, algorithmic FLOP per launch)
+    kernels = {"fwd_kernel": (t_fwd, 2 * per_contraction)}
     if w.backward:
         stage = lambda s: (lambda: binding.backward_stage(s, q, k, v, o, lse, do, dq, dk, dv, ws,  # noqa: E731
                                                           w.scale, w.causal, mask))
         t_pre = event_time(stage(0), n_ev)
         t_kv = event_time(stage(1), n_ev)
-        t_cvt = event_time(stage(2), n_ev)
-        kernels["bwd_kv_kernel"] = (t_kv, bwd_flop)
-        print(f"[bench] forward {t_fwd:.3f} ms ({fwd_flop / t_fwd / 1e9:.1f} TFLOP/s); backward stages "
-              f"{t_pre:.3f} / {t_kv:.3f} / {t_cvt:.3f} ms ({bwd_flop / t_kv / 1e9:.1f} TFLOP/s in the "
-              f"key-block kernel)", file=sys.stderr, flush=True)
+        t_q = event_time(stage(2), n_ev)
+        # the key-block kernel recomputes S and dP and forms dV and dK (4 contractions);
+        # the query-block kernel recomputes S and dP and forms dQ (3 contractions)
+        kernels["bwd_kv_kernel"] = (t_kv, 4 * per_contraction)
+        kernels["bwd_q_kernel"] = (t_q, 3 * per_contraction)
+        print(f"[bench] forward {t_fwd:.3f} ms ({2 * per_contraction / t_fwd / 1e9:.1f} TFLOP/s); backward "
+              f"stages D {t_pre:.3f} / dK,dV {t_kv:.3f} ({4 * per_contraction / t_kv / 1e9:.1f} TFLOP/s) / "
+              f"dQ {t_q:.3f} ms ({3 * per_contraction / t_q / 1e9:.1f} TFLOP/s)", file=sys.stderr, flush=True)
     dom = max(kernels, key=lambda n: kernels[n][0])
     t_dom, f_dom = kernels[dom]
     achieved = f_dom / (t_dom * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "launch_ms": round(t_dom, 4), "flop_per_launch": f_dom}
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(dom, w.name),
+                "launch_ms": round(t_dom, 4), "flop_per_launch": f_dom,
+                "kernels_ms": {n: round(v[0], 4) for n, v in kernels.items()}}
 
     if args.copy_mb:
         src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)

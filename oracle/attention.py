@@ -171,7 +171,7 @@ def _heads(B, H, heads):
     return [(int(b), int(h)) for b, h in heads]
 
 
-def forward(q, k, v, scale, causal=False, block_mask=None, heads=None, rows=None):
+def forward(q, k, v, scale, causal=False, block_mask=None, heads=None, rows=None, chunk=256):
     """Attention forward over [B, H, N, d] queries and [B, Hkv, N, d] keys/values.
 
     Query head h reads kv head h // (H // Hkv). With ``heads=None`` returns full
@@ -186,7 +186,7 @@ def forward(q, k, v, scale, causal=False, block_mask=None, heads=None, rows=None
     hl = _heads(B, H, heads)
     outs, lses = [], []
     for b, h in hl:
-        o, l_ = head_forward(q[b, h], k[b, h // G], v[b, h // G], scale, causal, block_mask, rows)
+        o, l_ = head_forward(q[b, h], k[b, h // G], v[b, h // G], scale, causal, block_mask, rows, chunk)
         outs.append(o)
         lses.append(l_)
     o = np.stack(outs)
@@ -197,7 +197,7 @@ def forward(q, k, v, scale, causal=False, block_mask=None, heads=None, rows=None
     return o, lse
 
 
-def backward(q, k, v, do, scale, causal=False, block_mask=None, heads=None):
+def backward(q, k, v, do, scale, causal=False, block_mask=None, heads=None, chunk=256):
     """Gradients of sum(O * dO) with respect to q, k, v.
 
     With ``heads=None`` returns full dq [B, H, N, d], dk, dv [B, Hkv, N, d]
@@ -217,11 +217,11 @@ def backward(q, k, v, do, scale, causal=False, block_mask=None, heads=None):
         for b in range(B):
             for h in range(H):
                 a, bk, bv = head_backward(q[b, h], k[b, h // G], v[b, h // G], do[b, h],
-                                          scale, causal, block_mask)
+                                          scale, causal, block_mask, chunk)
                 dq[b, h] = a
                 dk[b, h // G] += bk
                 dv[b, h // G] += bv
         return dq, dk, dv
-    res = [head_backward(q[b, h], k[b, h // G], v[b, h // G], do[b, h], scale, causal, block_mask)
+    res = [head_backward(q[b, h], k[b, h // G], v[b, h // G], do[b, h], scale, causal, block_mask, chunk)
            for b, h in _heads(B, H, heads)]
     return tuple(np.stack(x) for x in zip(*res))

@@ -1,0 +1,120 @@
+"""GPU parity at the full sizes of the five attention workloads, in the launch
+configuration bench.py times, against the float64 oracle.
+
+* single_head_fp32 (1x1x512x32, fp32): every output element.
+* gpt2_small_bf16 (8x12x1024x64, causal): every output and gradient element.
+* long_seq_bf16 (1x16x16384x128, causal): the two seeded heads, every element of
+  O, LSE, dQ, dK, dV of those heads; the rest only checked finite.
+* gqa_bf16 (4x32(8)x8192x128, causal, forward): 16 seeded rows of every (b, h),
+  the last row of each head among them.
+* block_sparse_fp16 (1x8x65536x64, band + 5% mask): the seeded head, every
+  element of O, LSE, dQ, dK, dV.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity as PT
+from exact_attention_110_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu(gpu_lib):
+    yield
+
+
+def _run(w, lib):
+    x = I.make(w)
+    dev = torch.device("cuda", 0)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    mask = torch.from_numpy(x["mask"]).to(dev) if x["mask"] is not None else None
+    o, lse = lib.forward(q, k, v, w.scale, w.causal, mask)
+    grads = None
+    if w.backward:
+        do = x["do"].to(dev)
+        grads = lib.backward(q, k, v, o, lse, do, w.scale, w.causal, mask)
+    torch.cuda.synchronize()
+    return x, o, lse, grads
+
+
+def _head(t, b, h):
+    return PT.np64(t[b:b + 1, h:h + 1])
+
+
+def _check_heads(w, x, o, lse, grads, heads, chunk=256):
+    for b, h in heads:
+        g = h // w.G
+        where = f"{w.name} b={b} h={h}"
+        PT.say("checking", where)
+        qd, kd, vd = _head(x["q"], b, h), _head(x["k"], b, g), _head(x["v"], b, g)
+        oref, lref = oracle.forward(qd, kd, vd, w.scale, w.causal, x["mask"], chunk=chunk)
+        PT.check_out(_head(o, b, h)[0, 0], oref[0, 0], w.dtype, where)
+        PT.check_lse(_head(lse.unsqueeze(-1), b, h)[0, 0, :, 0], lref[0, 0], where)
+        if grads is not None:
+            dq, dk, dv = grads
+            rq, rk, rv = oracle.backward(qd, kd, vd, _head(x["do"], b, h), w.scale, w.causal, x["mask"],
+                                         chunk=chunk)
+            PT.check_grad(_head(dq, b, h)[0, 0], rq[0, 0], where + " dq")
+            if w.G == 1:  # with one query head per kv head, its dk, dv are complete
+                PT.check_grad(_head(dk, b, g)[0, 0], rk[0, 0], where + " dk")
+                PT.check_grad(_head(dv, b, g)[0, 0], rv[0, 0], where + " dv")
+
+
+@pytest.mark.timeout(600)
+def test_single_head_fp32(gpu_lib):
+    w = I.WORKLOADS["single_head_fp32"]
+    x, o, lse, _ = _run(w, gpu_lib)
+    _check_heads(w, x, o, lse, None, [(0, 0)])
+
+
+@pytest.mark.timeout(600)
+def test_gpt2_small_bf16(gpu_lib):
+    w = I.WORKLOADS["gpt2_small_bf16"]
+    x, o, lse, grads = _run(w, gpu_lib)
+    qd, kd, vd, dod = (PT.np64(x[n]) for n in ("q", "k", "v", "do"))
+    oref, lref = oracle.forward(qd, kd, vd, w.scale, w.causal)
+    PT.check_out(PT.np64(o), oref, w.dtype, w.name)
+    PT.check_lse(PT.np64(lse), lref, w.name)
+    rq, rk, rv = oracle.backward(qd, kd, vd, dod, w.scale, w.causal)
+    for name, got, ref in zip(("dq", "dk", "dv"), grads, (rq, rk, rv)):
+        PT.check_grad(PT.np64(got), ref, f"{w.name} {name}")
+
+
+@pytest.mark.timeout(900)
+def test_long_seq_bf16(gpu_lib):
+    w = I.WORKLOADS["long_seq_bf16"]
+    x, o, lse, grads = _run(w, gpu_lib)
+    for t in (o, lse, *grads):
+        assert torch.isfinite(t).all()
+    _check_heads(w, x, o, lse, grads, I.check_heads(w))
+
+
+@pytest.mark.timeout(900)
+def test_gqa_bf16_sampled_rows(gpu_lib):
+    w = I.WORKLOADS["gqa_bf16"]
+    x, o, lse, _ = _run(w, gpu_lib)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    rng = np.random.default_rng(w.seed + 300)
+    for b in range(w.B):
+        for h in range(w.H):
+            rows = np.unique(np.concatenate([rng.choice(w.N, 15, replace=False), [w.N - 1]]))
+            g = h // w.G
+            oref, lref = oracle.forward(_head(x["q"], b, h), _head(x["k"], b, g), _head(x["v"], b, g),
+                                        w.scale, w.causal, rows=rows)
+            where = f"{w.name} b={b} h={h} rows={rows.tolist()}"
+            PT.check_out(PT.np64(o[b, h, rows]), oref[0, 0], w.dtype, where)
+            PT.check_lse(PT.np64(lse[b, h, rows]), lref[0, 0], where)
+
+
+@pytest.mark.timeout(900)
+def test_block_sparse_fp16(gpu_lib):
+    w = I.WORKLOADS["block_sparse_fp16"]
+    x, o, lse, grads = _run(w, gpu_lib)
+    for t in (o, lse, *grads):
+        assert torch.isfinite(t).all()
+    # 128-row chunks: each chunk then gathers only its own mask row's key blocks
+    _check_heads(w, x, o, lse, grads, I.check_heads(w), chunk=128)
