@@ -20,8 +20,10 @@
 //     query block (and every query head of a grouped-query group). The
 //     32x32 result layout of S = Q K^T is already the B operand of dV^T =
 //     dO^T P and dK^T = Q^T dS; dO^T and Q^T come from LDS through the gfx950
-//     transposing read. The step loop is software-pipelined: S and dP of the
-//     next query block are issued while this block's P and dS are formed.
+//     transposing read. The step loop is software-pipelined three deep: one
+//     iteration issues S and dP of the next query block, P and dS of this
+//     block and dV, dK of the previous block, which do not depend on each
+//     other, so the MFMAs overlap the softmax arithmetic within one wave.
 //  2. query-block kernel (dQ): one workgroup per 128 query rows, four waves of
 //     32 rows, laid out like the forward pass: S^T = K Q^T and dP^T = V dO^T
 //     with Q^T and dO^T in registers, so a lane owns one query row and its LSE
@@ -96,17 +98,19 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
 
-  // LDS: Q, dO and row statistics in three rotating buffers (step e uses e % 3;
-  // while step e is consumed, step e + 1 is already resident and step e + 2 is
-  // written into the buffer step e - 1 used) and the compacted mask list
-  __shared__ __attribute__((aligned(16))) char smem_raw[6 * QBUF + 3 * NT * 4 + (MASK ? 2 * MASK_LIST + 16 : 16)];
+  // LDS: Q, dO and row statistics in a ring of four buffers (step e uses e % 4:
+  // during step e's iteration, step e + 1's buffer feeds S and dP, step e's
+  // statistics feed P and dS, step e - 1's buffer feeds dV and dK, and step
+  // e + 2 is written into the buffer step e - 2 used) and the compacted mask list
+  constexpr int NB = 4;
+  __shared__ __attribute__((aligned(16))) char smem_raw[2 * NB * QBUF + NB * NT * 4 + (MASK ? 2 * MASK_LIST + 16 : 16)];
   lds_t* smem = (lds_t*)smem_raw;
-  lds_t* qbuf = smem;                   // [3][BQ][QP]
-  lds_t* obuf = qbuf + 3 * QBUF;        // dO, [3][BQ][QP]
-  lds_t* stat = obuf + 3 * QBUF;        // [3][NT] float: log2-scaled LSE in 0..BQ-1, D in BQ..2BQ-1
-  __attribute__((address_space(3))) short* blist = (__attribute__((address_space(3))) short*)(stat + 3 * NT * 4);
+  lds_t* qbuf = smem;                   // [NB][BQ][QP]
+  lds_t* obuf = qbuf + NB * QBUF;       // dO, [NB][BQ][QP]
+  lds_t* stat = obuf + NB * QBUF;       // [NB][NT] float: log2-scaled LSE in 0..BQ-1, D in BQ..2BQ-1
+  __attribute__((address_space(3))) short* blist = (__attribute__((address_space(3))) short*)(stat + NB * NT * 4);
   __attribute__((address_space(3))) int* bcount =
-      (__attribute__((address_space(3))) int*)(stat + 3 * NT * 4 + (MASK ? 2 * MASK_LIST : 0));
+      (__attribute__((address_space(3))) int*)(stat + NB * NT * 4 + (MASK ? 2 * MASK_LIST : 0));
 
   const AttnShape& s = a.s;
   const int N = s.N;
@@ -238,8 +242,8 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
   // i is query q0 + 8 (i / 4) + 4 hh + i % 4 of key kj; under causal masking it
   // is kept only if 8 (i / 4) + i % 4 >= kj - q0 - 4 hh. Keys past N need no
   // mask: their K and V rows read as zeros and nothing of theirs is stored.
-  unsigned int pk[8], sk[8];
-  auto probs = [&](const f32x16& sc, const f32x16& dp, int q0, int stb) {
+  auto probs = [&](const f32x16& sc, const f32x16& dp, int q0, int stb, unsigned int (&pk)[8],
+                   unsigned int (&sk)[8]) {
     const __attribute__((address_space(3))) float* lsel =
         (const __attribute__((address_space(3))) float*)(stat + stb * NT * 4);
     const __attribute__((address_space(3))) float* ddl = lsel + BQ;
@@ -266,7 +270,7 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
 
   // dV^T(d x key) += dO^T(d x q) P(q x key); dK^T += Q^T dS. B operand k-slot j
   // of step u is query 16 u + 8 (j / 4) + 4 hh + j % 4, matched by the reads.
-  auto dvdk = [&](int qbi) {
+  auto dvdk = [&](int qbi, const unsigned int (&pk)[8], const unsigned int (&sk)[8]) {
     const lds_t* qb = qbuf + qbi * QBUF;
     const lds_t* ob = obuf + qbi * QBUF;
 #pragma unroll
@@ -281,11 +285,17 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
       }
   };
 
-  // Software pipeline. Iteration e: S and dP of step e + 1, P and dS of step e,
-  // dV and dK of step e, then step e + 2 into the buffer step e - 1 used; one
-  // barrier per step. Loads are issued on every path (indices clamped; buffer
-  // loads make a redundant block harmless) so the loop body stays one basic
-  // block and outstanding loads are counted exactly.
+  // Software pipeline. Iteration e issues three mutually independent pieces of
+  // work: S and dP of step e + 1, P and dS of step e, dV and dK of step e - 1;
+  // then step e + 2 goes into the buffer step e - 2 used, and one barrier ends
+  // the step. Loads are issued on every path (indices clamped; buffer loads make
+  // a redundant block harmless) so the loop body stays one basic block and
+  // outstanding loads are counted exactly. The first iteration's "step -1"
+  // multiplies zero P and dS with a zeroed buffer.
+  for (int i = tid; i < 2 * QBUF / 16; i += NT) {
+    const int t = i / (QBUF / 16), off = (i % (QBUF / 16)) * 16;
+    lds_write16((t ? obuf : qbuf) + (NB - 1) * QBUF + off, (s16x8){0, 0, 0, 0, 0, 0, 0, 0});
+  }
   StepPos cur{0, hk * s.G};
   StepPos nxt = nsteps > 1 ? advance(cur) : cur;
   gload_q(cur);
@@ -295,24 +305,32 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
   __syncthreads();
   f32x16 sc, dp;
   sdp(0, sc, dp);
-  int b0 = 0;  // buffer of step e (e % 3)
+  unsigned int pk[8] = {0, 0, 0, 0, 0, 0, 0, 0}, sk[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int e = 0; e < nsteps; ++e) {
-    const int b1 = b0 == 2 ? 0 : b0 + 1;   // step e + 1
-    const int b2 = b1 == 2 ? 0 : b1 + 1;   // step e + 2 (= step e - 1's)
+    const int bm = (e + NB - 1) % NB;   // step e - 1
+    const int b0 = e % NB;              // step e
+    const int b1 = (e + 1) % NB;        // step e + 1
+    const int b2 = (e + 2) % NB;        // step e + 2 (= step e - 2's)
     const StepPos nn = e + 2 < nsteps ? advance(nxt) : nxt;
     gload_q(nn);
     f32x16 sc_n, dp_n;
     sdp(b1, sc_n, dp_n);
-    probs(sc, dp, qblock_at(cur.qi) * BQ, b0);
-    dvdk(b0);
+    unsigned int pk_n[8], sk_n[8];
+    probs(sc, dp, qblock_at(cur.qi) * BQ, b0, pk_n, sk_n);
+    dvdk(bm, pk, sk);
     lstore_q(b2);
     __syncthreads();
     sc = sc_n;
     dp = dp_n;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pk[j] = pk_n[j];
+      sk[j] = sk_n[j];
+    }
     cur = nxt;
     nxt = nn;
-    b0 = b1;
   }
+  if (nsteps > 0) dvdk((nsteps - 1) % NB, pk, sk);
 
   // dK^T / dV^T: lane holds key kj, d = 32 dt + 8 j + 4 hh + 0..3; dK takes the scale
   const float scale = s.scale;
