@@ -56,6 +56,7 @@ def sparse_flops(w, mask, backward=True):
 
 KERNEL_SOURCES = {
     "fwd_kernel": ["fwd.hip", "common.hpp", "params.hpp"],
+    "fwd64_kernel": ["fwd.hip", "common.hpp", "params.hpp"],
     "bwd_pre_kernel": ["bwd.hip", "common.hpp", "params.hpp"],
     "bwd_kv_kernel": ["bwd.hip", "common.hpp", "params.hpp"],
     "bwd_q_kernel": ["bwd.hip", "common.hpp", "params.hpp"],
@@ -71,6 +72,8 @@ def measured_traffic(kernel, workload):
     for f in KERNEL_SOURCES.get(kernel, []):
         with open(os.path.join(ROOT, "exact_attention_110_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+    with open(os.path.join(ROOT, "exact_attention_110_amd", "build.py"), "rb") as fh:  # compiler flags
+        h.update(fh.read())
     sha = h.hexdigest()
     for path in glob.glob(os.path.join(ROOT, "profiles", "*_hbm_traffic.md")):
         for line in open(path):
@@ -187,7 +190,8 @@ def main():
     per_contraction = fwd_flop / 2.0  # one N x N x d contraction of the workload
     t_fwd = event_time(lambda: binding.forward(q, k, v, w.scale, w.causal, mask, out=o, lse=lse), n_ev)
     # kernel -> (mean launch time in ms, algorithmic FLOP per launch)
-    kernels = {"fwd_kernel": (t_fwd, 2 * per_contraction)}
+    # dense and causal inputs run the 64-row forward kernel, block-sparse ones the 32-row one
+    kernels = {("fwd_kernel" if mask is not None else "fwd64_kernel"): (t_fwd, 2 * per_contraction)}
     if w.backward:
         stage = lambda s: (lambda: binding.backward_stage(s, q, k, v, o, lse, do, dq, dk, dv, ws,  # noqa: E731
                                                           w.scale, w.causal, mask))

@@ -1,25 +1,27 @@
 // Forward pass of IO-aware exact attention on gfx950.
 //
-// One workgroup owns a block of 128 query rows of one (batch, head) and
-// streams the visible key/value tiles of its kv head through LDS, keeping the
-// running row maximum m, the running sum l of exponentials and the unnormalised
-// output in registers; whenever m grows the earlier partial sums are rescaled
-// by exp(m_old - m_new). This is the online-softmax recurrence of the
+// A workgroup owns a block of query rows of one (batch, head) and streams the
+// visible key/value tiles of its kv head through LDS, keeping a reference row
+// maximum m, the running sum l of exponentials and the unnormalised output in
+// registers; whenever m is raised the earlier partial sums are rescaled by
+// exp(m_old - m_new). This is the online-softmax recurrence of the
 // pranaymahendrakar.com lesson "FlashAttention" (Researcher tier, "Online
 // softmax"); the output is O / l and the saved statistic is m + ln(l).
 //
 // gfx950 mapping (16-bit inputs):
-//  * 4 waves x 32 query rows. Each wave computes S^T = K Q^T for a 64-key tile
-//    with v_mfma_f32_32x32x16 (Q^T is the B operand and stays in registers).
-//    In the 32x32 result layout a lane owns one query column, so the row
-//    maximum needs one cross-half exchange (permlane32 swap) and the row sum
-//    none until the end.
+//  * Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16 (Q^T is the B
+//    operand and stays in registers). In the 32x32 result layout a lane owns
+//    one query column, so a row maximum needs one cross-half exchange
+//    (permlane32 swap) and the row sum none until the end.
 //  * The probabilities, converted to 16 bits, are already laid out as the B
 //    operand of O^T = V^T P^T. The matching V^T operand comes from LDS with the
 //    gfx950 transposing read ds_read_b64_tr_b16, so V needs no transpose pass.
-//  * K and V tiles are double-buffered in LDS with a register-staged prefetch
-//    of the next tile; row pitches are padded so that the 16-byte row reads
-//    of K and the transposing reads of V are free of bank conflicts.
+//  * LDS row pitches are padded so that the 16-byte row reads of K and the
+//    transposing reads of V are free of bank conflicts.
+//  * Dense and causal inputs run fwd64_kernel (64 query rows per wave, one
+//    wave per SIMD, 256 rows per workgroup); block-sparse inputs run
+//    fwd_kernel (32 rows per wave, two waves per SIMD, 128 rows per
+//    workgroup = one mask block row).
 //  * Causal: a workgroup stops at its diagonal tile, waves skip tiles that lie
 //    wholly after their rows, and only diagonal and tail tiles are masked
 //    element by element. Heaviest query blocks are launched first.
@@ -258,6 +260,354 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
   if (hh == 0) bstore_f32(make_rsrc(a.lse + qrow0, (unsigned)N * 4u), (unsigned)qi * 4u, lse);
 }
 
+// acc *= s for an accumulator held in AGPRs, one element at a time through a
+// single temporary VGPR. Written out because the compiler otherwise moves all
+// accumulators of a wave into VGPRs at once, which the 64-row kernel cannot
+// afford. The leading s_nops cover the wait an AGPR read needs after the MFMA
+// that wrote it, the trailing ones the wait before an MFMA reads it again.
+__device__ __forceinline__ void scale_acc(f32x16& x, float s) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float e = x[i];
+    float t;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(e), "=&v"(t)
+                 : "v"(s));
+    x[i] = e;
+  }
+  asm volatile("s_nop 7" ::: "memory");
+}
+
+// Dense and causal inputs: 64 query rows per wave, one wave per SIMD.
+//
+// Each K fragment read from LDS feeds the two 32-row column blocks of the wave
+// and each V^T fragment the two matching output blocks, which halves LDS reads
+// per MFMA against 32 rows per wave (at 32 rows the reads of K and V^T cost as
+// much LDS time as the MFMAs take). The register file then holds one wave per
+// SIMD, so latency is hidden inside the wave: the tile loop is pipelined three
+// deep. Iteration j issues S of tile j + 1, the probabilities of tile j and
+// P V of tile j - 1, which are independent of each other, then stages tile
+// j + 2 in the LDS slot tile j - 2 used (a ring of four K/V slots) and ends
+// with one barrier. In this loop the reference maximum is fixed at the first
+// tile's row maximum (any reference gives the same O / l and m + log2 l), so
+// the loop body has no rescale and no branch and the compiler can interleave
+// the exponentials with the MFMAs. Only tiles that every row of the workgroup
+// sees in full run here; the diagonal tiles of causal attention and a ragged
+// last tile follow in a plain loop with element masks and lazy rescaling,
+// which also takes over the whole workgroup in the rare case that a later
+// score outgrows the fixed reference.
+constexpr int F64_NW = 4;                 // waves per workgroup
+constexpr int F64_RW = 64;                // query rows per wave
+constexpr int F64_BM = F64_NW * F64_RW;   // query rows per workgroup
+constexpr int F64_BN = 32;                // keys per tile
+constexpr int F64_NB = 4;                 // LDS ring slots
+
+template <class T, int D, bool CAUSAL>
+__global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
+  constexpr int KP = D * 2 + 16;  // K row pitch (bytes): conflict-free 16-byte row reads
+  constexpr int VP = D * 2 + 32;  // V row pitch (bytes): conflict-free transposing reads
+  constexpr int KBUF = F64_BN * KP;
+  constexpr int VBUF = F64_BN * VP;
+  constexpr int NT = F64_NW * 64;
+  constexpr int CH = D / 8;
+  constexpr int TCH = F64_BN * CH;            // 16-byte chunks per tile per tensor
+  constexpr int PER = (TCH + NT - 1) / NT;
+  static_assert(TCH % NT == 0 || TCH < NT, "tile loader shape");
+  constexpr int NS = D / 16;
+  constexpr int ND = D / 32;
+  constexpr float kSlack = 8.f;
+
+  __shared__ __attribute__((aligned(16))) char smem_raw[F64_NB * (KBUF + VBUF)];
+  lds_t* kbuf = (lds_t*)smem_raw;
+  lds_t* vbuf = kbuf + F64_NB * KBUF;
+
+  const AttnShape& s = a.s;
+  const int N = s.N;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int g16 = lane >> 4;
+  const int roff = 4 * (g16 >> 1) + ((lane & 15) >> 2);
+  const int coff = 16 * (g16 & 1) + 4 * (lane & 3);
+  // grid = (H, query blocks, B): heads spread over the XCDs; under causal
+  // masking the longest query blocks are dispatched first
+  const int qb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+  const int h = blockIdx.x, b = blockIdx.z;
+  const int hk = h / s.G;
+  const size_t qrow0 = (size_t)(b * s.H + h) * N;
+  const size_t krow0 = (size_t)(b * s.Hkv + hk) * N;
+  const unsigned int head_bytes = (unsigned int)N * D * 2;
+  const rsrc_t rq = make_rsrc((const unsigned short*)a.q + qrow0 * D, head_bytes);
+  const rsrc_t rk = make_rsrc((const unsigned short*)a.k + krow0 * D, head_bytes);
+  const rsrc_t rv = make_rsrc((const unsigned short*)a.v + krow0 * D, head_bytes);
+  const int q0 = qb * F64_BM;
+  const int qw = q0 + F64_RW * w;  // first query row of this wave; block rb holds rows qw + 32 rb + 0..31
+  const float c = fmaxf(s.scale * kLog2e, 1e-30f);
+
+  const int kend = CAUSAL ? min(N, q0 + F64_BM) : N;
+  const int ntiles = (kend + F64_BN - 1) / F64_BN;
+  // tiles whose keys every row of the workgroup sees (q0 is a multiple of the tile)
+  const int nfull = CAUSAL ? q0 / F64_BN : N / F64_BN;
+
+  // Q^T operands of both row blocks: lane holds query qw + 32 rb + l32, d = 16 ss + 8 hh + 0..7
+  s16x8 qf[2][NS];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int ss = 0; ss < NS; ++ss)
+      qf[rb][ss] = bload16(rq, (unsigned)((qw + 32 * rb + l32) * D + 16 * ss + 8 * hh) * 2u);
+
+  f32x16 acc[2][ND];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[rb][dt][i] = 0.f;
+  // running reference m (log2 units) and this lane's half of the running sum,
+  // per row block, raised lazily as in the 32-row kernel
+  float m[2] = {-INFINITY, -INFINITY};
+  float l[2] = {0.f, 0.f};
+
+  s16x8 kreg[PER], vreg[PER];
+  auto gload = [&](int t) {
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int ci = min(tid + r * NT, TCH - 1);  // spare threads repeat the last chunk
+      const int row = ci / CH, col = (ci % CH) * 8;
+      const unsigned int off = (unsigned)((t * F64_BN + row) * D + col) * 2u;
+      kreg[r] = bload16(rk, off);
+      vreg[r] = bload16(rv, off);
+    }
+  };
+  auto lstore = [&](int slot) {
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int ci = min(tid + r * NT, TCH - 1);
+      const int row = ci / CH, col = (ci % CH) * 8;
+      lds_write16(kbuf + slot * KBUF + row * KP + col * 2, kreg[r]);
+      lds_write16(vbuf + slot * VBUF + row * VP + col * 2, vreg[r]);
+    }
+  };
+  // S^T = K Q^T of the tile in a slot; st[rb][i] is S of query qw + 32 rb + l32
+  // and key 8 (i / 4) + 4 hh + i % 4 of the tile
+  auto s_tile = [&](int slot, f32x16 (&st)[2]) {
+    const lds_t* kb = kbuf + slot * KBUF + l32 * KP + 16 * hh;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      st[0][i] = 0.f;
+      st[1][i] = 0.f;
+    }
+#pragma unroll
+    for (int ss = 0; ss < NS; ++ss) {
+      const s16x8 ka = lds_read16(kb + 32 * ss);
+      st[0] = mfma32<T>(ka, qf[0][ss], st[0]);
+      st[1] = mfma32<T>(ka, qf[1][ss], st[1]);
+    }
+  };
+  // O^T += V^T P^T for the tile in a slot; B operand k-slot j of step u is key
+  // 16 u + 8 (j / 4) + 4 hh + j % 4, matched by the transposing reads of V
+  auto pv_tile = [&](int slot, const unsigned int (&pk)[2][8]) {
+    const lds_t* vb = vbuf + slot * VBUF;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const lds_t* vp = vb + (16 * u + roff) * VP + (32 * dt + coff) * 2;
+        const s16x8 va = concat(lds_read_tr(vp), lds_read_tr(vp + 8 * VP));
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          acc[rb][dt] = mfma32<T>(va, as_operand(pk[rb][4 * u], pk[rb][4 * u + 1], pk[rb][4 * u + 2],
+                                                 pk[rb][4 * u + 3]),
+                                  acc[rb][dt]);
+      }
+  };
+  // Softmax of one tile against the running reference: returns whether the
+  // reference rises (wave-uniform), with the new reference in mn, the 16-bit
+  // probabilities in pk and this lane's share of their row sums in ls.
+  auto softmax = [&](const f32x16 (&st)[2], float (&mn)[2], unsigned int (&pk)[2][8], float (&ls)[2]) {
+    float mx[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float x = st[rb][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) x = fmaxf(x, st[rb][i]);
+      mx[rb] = fmaxf(x, swap_halves(x)) * c;
+    }
+    const bool resc = __any(mx[0] > m[0] + kSlack || mx[1] > m[1] + kSlack);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      mn[rb] = resc ? fmaxf(m[rb], mx[rb]) : m[rb];
+      const float mu = mn[rb] == -INFINITY ? 0.f : mn[rb];  // a row with no visible key yet
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p0 = fast_exp2(fmaf(st[rb][2 * j], c, -mu));
+        const float p1 = fast_exp2(fmaf(st[rb][2 * j + 1], c, -mu));
+        sum += p0 + p1;
+        pk[rb][j] = pack2<T>(p0, p1);
+      }
+      ls[rb] = sum;
+    }
+    return resc;
+  };
+  // fold a tile's statistics into the running ones; when the reference rose,
+  // scale the output and the sum by exp(m_old - m_new) first
+  auto update = [&](bool resc, const float (&mn)[2], const float (&ls)[2]) {
+    if (resc) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const float corr = fast_exp2(m[rb] - (mn[rb] == -INFINITY ? 0.f : mn[rb]));
+        l[rb] *= corr;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) scale_acc(acc[rb][dt], corr);
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      l[rb] += ls[rb];
+      m[rb] = mn[rb];
+    }
+  };
+
+  // Prologue: tiles 0 and 1 in slots 0 and 1; the V half of slot 3 is zeroed
+  // because the first iteration multiplies it with zero probabilities.
+  for (int i = tid; i < VBUF / 16; i += NT)
+    lds_write16(vbuf + (F64_NB - 1) * VBUF + i * 16, (s16x8){0, 0, 0, 0, 0, 0, 0, 0});
+  gload(0);
+  lstore(0);
+  gload(min(1, ntiles - 1));
+  lstore(1);
+  __syncthreads();
+
+  // Main loop over the tiles that every row sees in full. The reference m is
+  // fixed at the first tile's row maximum, so the loop never rescales and has
+  // no branch: probabilities relative to that reference stay finite while no
+  // later score exceeds it by more than about 120 in log2 units, and the result
+  // O / l, m + log2(l) does not depend on the reference chosen. Should a row's
+  // sum end above 2^60 (some later score at least 60 above the first tile's
+  // maximum), the whole workgroup starts over in the general loop below, which
+  // raises the reference as it goes.
+  int j = 0;
+  if (nfull > 0) {
+    auto probs = [&](const f32x16 (&st)[2], unsigned int (&pk)[2][8]) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float sum = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const float p0 = fast_exp2(fmaf(st[rb][2 * jj], c, -m[rb]));
+          const float p1 = fast_exp2(fmaf(st[rb][2 * jj + 1], c, -m[rb]));
+          sum += p0 + p1;
+          pk[rb][jj] = pack2<T>(p0, p1);
+        }
+        l[rb] += sum;
+      }
+    };
+    // one iteration: S of tile jj + 1, probabilities of tile jj, P V of tile
+    // jj - 1 (mutually independent), then tile jj + 2 into the slot of tile
+    // jj - 2. Loads are issued on every path (tile index clamped; a redundant
+    // copy lands in a slot nobody reads).
+    auto iter = [&](int jj, const f32x16 (&scur)[2], f32x16 (&snext)[2], const unsigned int (&pprev)[2][8],
+                    unsigned int (&pcur)[2][8]) {
+      gload(min(jj + 2, ntiles - 1));
+      s_tile((jj + 1) & (F64_NB - 1), snext);
+      probs(scur, pcur);
+      pv_tile((jj + F64_NB - 1) & (F64_NB - 1), pprev);
+      lstore((jj + 2) & (F64_NB - 1));
+      __syncthreads();
+    };
+    f32x16 sa[2], sb[2];
+    unsigned int pa[2][8], pb[2][8];
+    s_tile(0, sa);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float x = sa[rb][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) x = fmaxf(x, sa[rb][i]);
+      m[rb] = fmaxf(x, swap_halves(x)) * c;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) pb[rb][jj] = 0u;
+    }
+    for (; j + 1 < nfull; j += 2) {
+      iter(j, sa, sb, pb, pa);
+      iter(j + 1, sb, sa, pa, pb);
+    }
+    if (j < nfull) {
+      iter(j, sa, sb, pb, pa);
+      pv_tile(j & (F64_NB - 1), pa);
+      ++j;
+    } else {
+      pv_tile((nfull - 1) & (F64_NB - 1), pb);
+    }
+    // workgroup-uniform decision (it also orders the reads above before any
+    // slot is refilled)
+    if (__syncthreads_or(l[0] > 0x1p60f || l[1] > 0x1p60f)) {
+      j = 0;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        m[rb] = -INFINITY;
+        l[rb] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[rb][dt][i] = 0.f;
+      }
+      gload(0);
+      lstore(0);
+      gload(min(1, ntiles - 1));
+      lstore(1);
+      __syncthreads();
+    }
+  }
+
+  // general loop (diagonal and ragged tiles, or a restart): element masks,
+  // lazy rescaling, waves without a visible key skip the tile
+  for (; j < ntiles; ++j) {
+    gload(min(j + 2, ntiles - 1));
+    const int ks = j * F64_BN;
+    if (!CAUSAL || ks <= qw + F64_RW - 1) {
+      f32x16 st[2];
+      s_tile(j & (F64_NB - 1), st);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int qi = qw + 32 * rb + l32;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = ks + 8 * (i >> 2) + 4 * hh + (i & 3);
+          if ((CAUSAL && key > qi) || key >= N) st[rb][i] = -INFINITY;
+        }
+      }
+      float mn[2], ls[2];
+      unsigned int pt[2][8];
+      const bool resc = softmax(st, mn, pt, ls);
+      update(resc, mn, ls);
+      pv_tile(j & (F64_NB - 1), pt);
+    }
+    lstore((j + 2) & (F64_NB - 1));
+    __syncthreads();
+  }
+
+  const rsrc_t ro = make_rsrc((unsigned short*)a.o + qrow0 * D, head_bytes);
+  const rsrc_t rl = make_rsrc(a.lse + qrow0, (unsigned)N * 4u);
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int qi = qw + 32 * rb + l32;
+    const float lt = l[rb] + swap_halves(l[rb]);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse = lt > 0.f ? (m[rb] + fast_log2(lt)) * kLn2 : -INFINITY;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2 v2 = {pack2<T>(acc[rb][dt][4 * j] * inv, acc[rb][dt][4 * j + 1] * inv),
+                    pack2<T>(acc[rb][dt][4 * j + 2] * inv, acc[rb][dt][4 * j + 3] * inv)};
+        bstore8(ro, (unsigned)(qi * D + 32 * dt + 8 * j + 4 * hh) * 2u, v2);
+      }
+    if (hh == 0) bstore_f32(rl, (unsigned)qi * 4u, lse);
+  }
+}
+
 // float32: one query row per lane, fp32 FMA for every product, keys in LDS tiles.
 constexpr int F32_ROWS = 64;
 constexpr int F32_BN = 32;
@@ -337,9 +687,15 @@ __global__ __launch_bounds__(F32_ROWS) void fwd_f32_kernel(FwdArgs a) {
 
 template <class T, int D>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
+  const bool causal = a.s.causal != 0, mask = a.s.mask != nullptr;
+  if (!mask) {
+    const dim3 grid(a.s.H, (a.s.N + F64_BM - 1) / F64_BM, a.s.B);
+    if (causal) hipLaunchKernelGGL((fwd64_kernel<T, D, true>), grid, dim3(F64_NW * 64), 0, st, a);
+    else hipLaunchKernelGGL((fwd64_kernel<T, D, false>), grid, dim3(F64_NW * 64), 0, st, a);
+    return hipGetLastError();
+  }
   const dim3 grid(a.s.H, (a.s.N + FWD_BM - 1) / FWD_BM, a.s.B);
   const dim3 block(FWD_NW * 64);
-  const bool causal = a.s.causal != 0, mask = a.s.mask != nullptr;
   if (causal && mask) hipLaunchKernelGGL((fwd_kernel<T, D, true, true>), grid, block, 0, st, a);
   else if (causal) hipLaunchKernelGGL((fwd_kernel<T, D, true, false>), grid, block, 0, st, a);
   else if (mask) hipLaunchKernelGGL((fwd_kernel<T, D, false, true>), grid, block, 0, st, a);

@@ -67,6 +67,30 @@ def test_empty_rows(dtype):
     assert res["o"] <= (PT.TOL_F32 if dtype == "fp32" else PT.TOL_16)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_late_dominant_scores(dtype, causal):
+    """Keys far into the sequence whose scores exceed every earlier one by far
+    more than the forward's fixed-reference range (keys 400..410: about 90 in
+    log2 units above the first tile's maximum, forcing a restart with lazy
+    rescaling) or its rescale slack (key 350: about 46 above). The large keys
+    keep their random part: with identical key rows the exact dQ of every row
+    that attends to them would be zero (the dS of a row sums to zero), and any
+    rounding of dS would make the relative error meaningless."""
+    N, d = 600, 64
+    x = I.make_small(1, 2, 1, N, d, dtype, 21)
+    x["q"] = x["q"] + 1.0
+    x["k"][:, :, 400:411, :] += 8.0
+    x["k"][:, :, 350, :] += 4.0
+    # LSE reaches about 65 here, where one float32 ulp is 7.6e-6: the absolute
+    # 1e-5 bar is below what a float32 result can resolve, so this case allows
+    # 4 ulps of the largest LSE on top of it
+    q, k = (PT.np64(x[n]) for n in ("q", "k"))
+    big = float(np.abs(q @ np.swapaxes(k, -1, -2)).max()) / np.sqrt(d)
+    tol = PT.TOL_LSE + 4 * 2.0 ** -23 * big
+    PT.run_given(x, dtype, causal, where=f"late dominant scores {dtype} causal={causal}", lse_tol=tol)
+
+
 def test_scale_zero_is_uniform():
     PT.run_small(1, 2, 2, 200, 64, "bf16", True, seed=5, scale=0.0)
     PT.run_small(1, 1, 1, 150, 32, "fp32", False, seed=6, scale=0.0, backward=False)
