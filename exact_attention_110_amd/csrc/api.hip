@@ -50,7 +50,12 @@ fa::AttnShape make_shape(int B, int H, int Hkv, int N, int d, float scale, int c
 // Block masks are compacted per row / column in LDS lists of 2048 entries.
 constexpr int kMaxMaskBlocks = 2048;
 
-size_t dvec_bytes(int B, int H, int N) { return round_up((size_t)B * H * N * sizeof(float)); }
+// Backward workspace: per (b, h) two float planes (log2-scaled LSE and D) of
+// npad = N rounded up to 128 rows, so that whole 128-row blocks load in bounds.
+int stats_rows(int N) { return (N + 127) / 128 * 128; }
+size_t stats_bytes(int B, int H, int N) {
+  return round_up((size_t)B * H * 2 * stats_rows(N) * sizeof(float));
+}
 
 int check_backward(const void* q, const void* k, const void* v, const void* o, const float* lse,
                    const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N,
@@ -65,7 +70,8 @@ int check_backward(const void* q, const void* k, const void* v, const void* o, c
   if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   if (block_mask && (N + 127) / 128 > kMaxMaskBlocks) return FA_ERR_UNSUPPORTED;
   if (!workspace || ((uintptr_t)workspace % kAlign) != 0) return FA_ERR_WORKSPACE;
-  if (workspace_bytes < dvec_bytes(B, H, N)) return FA_ERR_WORKSPACE;
+  if ((long long)B * H * 2 * stats_rows(N) > INT32_MAX) return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < stats_bytes(B, H, N)) return FA_ERR_WORKSPACE;
   return FA_OK;
 }
 
@@ -96,7 +102,8 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
 size_t fa_backward_workspace_size(int B, int H, int Hkv, int N, int d, int dtype) {
   if (check_shape(B, H, Hkv, N, d, 1.0f, dtype) != FA_OK || dtype == FA_F32) return 0;
   (void)d;
-  return dvec_bytes(B, H, N);
+  if ((long long)B * H * 2 * stats_rows(N) > INT32_MAX) return 0;
+  return stats_bytes(B, H, N);
 }
 
 int fa_backward_stage(int stage, const void* q, const void* k, const void* v, const void* o,
@@ -118,7 +125,8 @@ int fa_backward_stage(int stage, const void* q, const void* k, const void* v, co
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.dvec = (float*)workspace;
+  a.stats = (float*)workspace;
+  a.npad = stats_rows(N);
   (void)hipGetLastError();
   return fa::launch_backward_stage(stage, a, dtype, (hipStream_t)stream) == hipSuccess ? FA_OK
                                                                                         : FA_ERR_HIP;

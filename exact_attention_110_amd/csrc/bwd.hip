@@ -46,18 +46,22 @@ namespace fa {
 constexpr int lds_pitch(int row_bytes) { return row_bytes == 128 ? 208 : row_bytes + 48; }
 
 // ---------------------------------------------------------------------------
-// stage 0: D = rowsum(dO * O) in fp32
+// stage 0: per query row, D = rowsum(dO * O) in fp32 and the log2-scaled LSE,
+// into the workspace's two planes (padding rows N..npad-1 included)
 // ---------------------------------------------------------------------------
 template <class T, int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int rows) {
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   constexpr int CH = D / 8;  // lanes per row, 8 elements each
   constexpr int RPB = 256 / CH;
   const int tid = threadIdx.x;
-  const int row = blockIdx.x * RPB + tid / CH;
+  const int nblk = (a.npad + RPB - 1) / RPB;  // blocks per (b, h) head
+  const int bh = blockIdx.x / nblk;
+  const int r = (blockIdx.x % nblk) * RPB + tid / CH;  // row within the head
   const int part = tid % CH;
+  const int N = a.s.N;
   float sum = 0.f;
-  if (row < rows) {
-    const size_t off = (size_t)row * D + part * 8;
+  if (r < N) {
+    const size_t off = ((size_t)bh * N + r) * D + part * 8;
     const s16x8 o = gload16((const unsigned short*)a.o + off);
     const s16x8 g = gload16((const unsigned short*)a.dO + off);
 #pragma unroll
@@ -66,7 +70,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int rows) {
   }
 #pragma unroll
   for (int msk = CH / 2; msk >= 1; msk >>= 1) sum += __shfl_xor(sum, msk, 64);
-  if (row < rows && part == 0) a.dvec[row] = sum;
+  if (r < a.npad && part == 0) {
+    // a row past N, or one that saw no key, gets +inf so that its P is 0
+    const float lv = r < N ? a.lse[(size_t)bh * N + r] : -INFINITY;
+    float* st = a.stats + (size_t)bh * 2 * a.npad;
+    st[r] = lv != -INFINITY ? lv * kLog2e : INFINITY;
+    st[a.npad + r] = sum;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -79,38 +89,36 @@ constexpr int KV_R = 128 / KV_BQ;     // steps per 128-row mask block
 constexpr int MASK_LIST = 2048;       // capacity of a compacted mask row / column
 static_assert(KV_BKV == 128, "a key-block workgroup must cover exactly one mask block column");
 
-// position of a step: query head h, index qi into the key block's query-block list
+// position of a step: index qi into the key block's query-block list, and the
+// query head's element offset in Q / dO and float offset in the statistics
 struct StepPos {
   int qi;
-  int h;
+  int soff;
+  unsigned long long qoff;
 };
 
 template <class T, int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
   constexpr int BQ = KV_BQ;
-  constexpr int QP = lds_pitch(2 * D);   // Q / dO row pitch in LDS (bytes)
-  constexpr int QBUF = BQ * QP;
-  constexpr int NT = KV_NW * 64;         // threads
-  constexpr int CH = D / 8;
-  constexpr int QCH = BQ * CH;           // 16-byte chunks per query block
-  constexpr int PERQ = (QCH + NT - 1) / NT;
-  static_assert(QCH % NT == 0 || QCH < NT, "query loader shape");
+  constexpr int QBUF = BQ * 2 * D;       // one Q or dO block, swizzled rows without padding
+  constexpr int STB = 2 * BQ * 4;        // one statistics block: BQ log2-scaled LSE, then BQ D
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
 
   // LDS: Q, dO and row statistics in a ring of four buffers (step e uses e % 4:
   // during step e's iteration, step e + 1's buffer feeds S and dP, step e's
   // statistics feed P and dS, step e - 1's buffer feeds dV and dK, and step
-  // e + 2 is written into the buffer step e - 2 used) and the compacted mask list
+  // e + 2 is loaded into the buffer step e - 2 used) and the compacted mask
+  // list. The buffers are filled by LDS DMA, straight from memory.
   constexpr int NB = 4;
-  __shared__ __attribute__((aligned(16))) char smem_raw[2 * NB * QBUF + NB * NT * 4 + (MASK ? 2 * MASK_LIST + 16 : 16)];
+  __shared__ __attribute__((aligned(16))) char smem_raw[2 * NB * QBUF + NB * STB + (MASK ? 2 * MASK_LIST + 16 : 16)];
   lds_t* smem = (lds_t*)smem_raw;
-  lds_t* qbuf = smem;                   // [NB][BQ][QP]
-  lds_t* obuf = qbuf + NB * QBUF;       // dO, [NB][BQ][QP]
-  lds_t* stat = obuf + NB * QBUF;       // [NB][NT] float: log2-scaled LSE in 0..BQ-1, D in BQ..2BQ-1
-  __attribute__((address_space(3))) short* blist = (__attribute__((address_space(3))) short*)(stat + NB * NT * 4);
+  lds_t* qbuf = smem;                   // [NB][BQ rows, swizzled]
+  lds_t* obuf = qbuf + NB * QBUF;       // dO, [NB][BQ rows, swizzled]
+  lds_t* stat = obuf + NB * QBUF;       // [NB][2 BQ] float
+  __attribute__((address_space(3))) short* blist = (__attribute__((address_space(3))) short*)(stat + NB * STB);
   __attribute__((address_space(3))) int* bcount =
-      (__attribute__((address_space(3))) int*)(stat + NB * NT * 4 + (MASK ? 2 * MASK_LIST : 0));
+      (__attribute__((address_space(3))) int*)(stat + NB * STB + (MASK ? 2 * MASK_LIST : 0));
 
   const AttnShape& s = a.s;
   const int N = s.N;
@@ -170,7 +178,9 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
   // steps run over every query block of the list for each query head of the group
   const int nsteps = nq * s.G;
   auto advance = [&](StepPos p) -> StepPos {
-    return p.qi + 1 < nq ? StepPos{p.qi + 1, p.h} : StepPos{0, p.h + 1};
+    const bool next_head = p.qi + 1 >= nq;
+    return StepPos{next_head ? 0 : p.qi + 1, next_head ? p.soff + 2 * a.npad : p.soff,
+                   next_head ? p.qoff + (unsigned long long)N * D : p.qoff};
   };
 
   f32x16 dka[ND], dva[ND];
@@ -182,42 +192,20 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
       dva[dt][i] = 0.f;
     }
 
-  // prefetch of a step's Q and dO rows (registers) and its row statistics:
-  // threads 0..BQ-1 take log2-scaled LSE, threads BQ..2BQ-1 take D
-  s16x8 qreg[PERQ], oreg[PERQ];
-  float sreg = 0.f;
-  auto gload_q = [&](StepPos p) {
+  // A step's Q and dO rows and its row statistics, by LDS DMA into ring buffer
+  // buf: every wave moves its share of the 1 KB segments; the last wave also
+  // moves the statistics (lanes 0..31 the LSE plane, 32..63 the D plane; rows
+  // up to the padded length are in range).
+  auto dma_q = [&](StepPos p, int buf) {
     const int q0 = qblock_at(p.qi) * BQ;
-    const size_t qrow0 = (size_t)(b * s.H + p.h) * N;
-    const rsrc_t rq = make_rsrc((const unsigned short*)a.q + qrow0 * D, head_bytes);
-    const rsrc_t rg = make_rsrc((const unsigned short*)a.dO + qrow0 * D, head_bytes);
-#pragma unroll
-    for (int r = 0; r < PERQ; ++r) {
-      // spare threads of a small block repeat the last chunk (same data, same place)
-      const int ci = min(tid + r * NT, QCH - 1);
-      const int row = ci / CH, col = (ci % CH) * 8;
-      const unsigned int off = (unsigned)((q0 + row) * D + col) * 2u;
-      qreg[r] = bload16(rq, off);
-      oreg[r] = bload16(rg, off);
+    const i32x4 rq = rsrc_words((const unsigned short*)a.q + p.qoff, head_bytes);
+    const i32x4 rg = rsrc_words((const unsigned short*)a.dO + p.qoff, head_bytes);
+    dma_tile<D, BQ, KV_NW>(rq, q0, qbuf + buf * QBUF, w, lane);
+    dma_tile<D, BQ, KV_NW>(rg, q0, obuf + buf * QBUF, w, lane);
+    if (w == KV_NW - 1) {
+      const i32x4 rs = rsrc_words(a.stats + p.soff, (unsigned)a.npad * 8u);
+      dma4(rs, (unsigned)(((lane >> 5) * a.npad + q0 + (lane & 31)) * 4), stat + buf * STB);
     }
-    // rows past N, and rows that saw no key, get LSE = +inf so that their P is 0
-    // (two wave-uniform resources; a per-lane choice of base would not be uniform)
-    const int q = q0 + (tid % BQ);
-    const float lv = bload_f32(make_rsrc(a.lse + qrow0, (unsigned)N * 4u), (unsigned)q * 4u);
-    const float dv = bload_f32(make_rsrc(a.dvec + qrow0, (unsigned)N * 4u), (unsigned)q * 4u);
-    const float L = (q < N && lv != -INFINITY) ? lv * kLog2e : INFINITY;
-    sreg = tid < BQ ? L : dv;
-  };
-  auto lstore_q = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < PERQ; ++r) {
-      const int ci = min(tid + r * NT, QCH - 1);
-      const int row = ci / CH, col = (ci % CH) * 8;
-      lds_write16(qbuf + buf * QBUF + row * QP + col * 2, qreg[r]);
-      lds_write16(obuf + buf * QBUF + row * QP + col * 2, oreg[r]);
-    }
-    // every thread writes its slot (only the first 2 BQ are read)
-    *((__attribute__((address_space(3))) float*)(stat + buf * NT * 4) + tid) = sreg;
   };
 
   // S = Q K^T and dP = dO V^T of this wave's 32 keys, from Q / dO buffer qbi
@@ -231,8 +219,9 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int ss = 0; ss < NS; ++ss) {
-      const s16x8 qa = lds_read16(qb + l32 * QP + (16 * ss + 8 * hh) * 2);
-      const s16x8 ga = lds_read16(ob + l32 * QP + (16 * ss + 8 * hh) * 2);
+      const int off = swz_off<D>(l32, 2 * ss + hh);
+      const s16x8 qa = lds_read16(qb + off);
+      const s16x8 ga = lds_read16(ob + off);
       sc = mfma32<T>(qa, kf[ss], sc);
       dp = mfma32<T>(ga, vf[ss], dp);
     }
@@ -242,10 +231,11 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
   // i is query q0 + 8 (i / 4) + 4 hh + i % 4 of key kj; under causal masking it
   // is kept only if 8 (i / 4) + i % 4 >= kj - q0 - 4 hh. Keys past N need no
   // mask: their K and V rows read as zeros and nothing of theirs is stored.
-  auto probs = [&](const f32x16& sc, const f32x16& dp, int q0, int stb, unsigned int (&pk)[8],
+  auto probs = [&](auto masked, const f32x16& sc, const f32x16& dp, int q0, int stb, unsigned int (&pk)[8],
                    unsigned int (&sk)[8]) {
+    constexpr bool MASKED = decltype(masked)::value;
     const __attribute__((address_space(3))) float* lsel =
-        (const __attribute__((address_space(3))) float*)(stat + stb * NT * 4);
+        (const __attribute__((address_space(3))) float*)(stat + stb * STB);
     const __attribute__((address_space(3))) float* ddl = lsel + BQ;
     const int thr = kj - q0 - 4 * hh;
 #pragma unroll
@@ -257,7 +247,7 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * j4 + r;
         float pv = fast_exp2(fmaf(sc[i], c, -L4[r]));
-        if constexpr (CAUSAL) pv = (8 * j4 + r < thr) ? 0.f : pv;
+        if constexpr (MASKED) pv = (8 * j4 + r < thr) ? 0.f : pv;
         p[r] = pv;
         d2[r] = pv * (dp[i] - D4[r]);
       }
@@ -277,9 +267,12 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
     for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int off = (16 * u + roff) * QP + (32 * dt + coff) * 2;
-        const s16x8 ga = concat(lds_read_tr(ob + off), lds_read_tr(ob + off + 8 * QP));
-        const s16x8 qa = concat(lds_read_tr(qb + off), lds_read_tr(qb + off + 8 * QP));
+        // rows 16 u + roff and 8 below it, columns 32 dt + coff .. + 3
+        const int c = 4 * dt + (coff >> 3), within = 2 * (coff & 7);
+        const int off0 = swz_off<D>(16 * u + roff, c) + within;
+        const int off1 = swz_off<D>(16 * u + roff + 8, c) + within;
+        const s16x8 ga = concat(lds_read_tr(ob + off0), lds_read_tr(ob + off1));
+        const s16x8 qa = concat(lds_read_tr(qb + off0), lds_read_tr(qb + off1));
         dva[dt] = mfma32<T>(ga, as_operand(pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]), dva[dt]);
         dka[dt] = mfma32<T>(qa, as_operand(sk[4 * u], sk[4 * u + 1], sk[4 * u + 2], sk[4 * u + 3]), dka[dt]);
       }
@@ -287,50 +280,80 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
 
   // Software pipeline. Iteration e issues three mutually independent pieces of
   // work: S and dP of step e + 1, P and dS of step e, dV and dK of step e - 1;
-  // then step e + 2 goes into the buffer step e - 2 used, and one barrier ends
-  // the step. Loads are issued on every path (indices clamped; buffer loads make
-  // a redundant block harmless) so the loop body stays one basic block and
-  // outstanding loads are counted exactly. The first iteration's "step -1"
-  // multiplies zero P and dS with a zeroed buffer.
-  for (int i = tid; i < 2 * QBUF / 16; i += NT) {
+  // step e + 2 is loaded into the buffer step e - 2 used, and one barrier ends
+  // the step. Loads are issued on every path (indices clamped; a redundant
+  // block lands in a buffer nobody reads). The first iteration's "step -1"
+  // multiplies zero P and dS with a zeroed buffer. Only the first KV_R steps of
+  // each query head can meet the causal diagonal; they run a masked variant,
+  // the others none, and the unmasked steps alternate between two register
+  // sets so that nothing is copied from one step to the next.
+  for (int i = tid; i < 2 * QBUF / 16; i += KV_NW * 64) {
     const int t = i / (QBUF / 16), off = (i % (QBUF / 16)) * 16;
     lds_write16((t ? obuf : qbuf) + (NB - 1) * QBUF + off, (s16x8){0, 0, 0, 0, 0, 0, 0, 0});
   }
-  StepPos cur{0, hk * s.G};
+  const int hb0 = b * s.H + hk * s.G;  // first query head of the group, batch included
+  StepPos cur{0, hb0 * 2 * a.npad, (unsigned long long)hb0 * N * D};
   StepPos nxt = nsteps > 1 ? advance(cur) : cur;
-  gload_q(cur);
-  lstore_q(0);
-  gload_q(nxt);
-  lstore_q(1);
+  dma_q(cur, 0);
+  dma_q(nxt, 1);
+  dma_wait();
   __syncthreads();
-  f32x16 sc, dp;
-  sdp(0, sc, dp);
-  unsigned int pk[8] = {0, 0, 0, 0, 0, 0, 0, 0}, sk[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int e = 0; e < nsteps; ++e) {
-    const int bm = (e + NB - 1) % NB;   // step e - 1
-    const int b0 = e % NB;              // step e
-    const int b1 = (e + 1) % NB;        // step e + 1
-    const int b2 = (e + 2) % NB;        // step e + 2 (= step e - 2's)
+  // iteration e: (sc, dp) = S, dP of step e; (pk, sk) = P, dS of step e - 1;
+  // fills (scn, dpn) with step e + 1 and (pkn, skn) with step e
+  auto iter = [&](int e, auto masked, const f32x16& sc, const f32x16& dp, const unsigned int (&pk)[8],
+                  const unsigned int (&sk)[8], f32x16& scn, f32x16& dpn, unsigned int (&pkn)[8],
+                  unsigned int (&skn)[8]) {
     const StepPos nn = e + 2 < nsteps ? advance(nxt) : nxt;
-    gload_q(nn);
-    f32x16 sc_n, dp_n;
-    sdp(b1, sc_n, dp_n);
-    unsigned int pk_n[8], sk_n[8];
-    probs(sc, dp, qblock_at(cur.qi) * BQ, b0, pk_n, sk_n);
-    dvdk(bm, pk, sk);
-    lstore_q(b2);
+    dma_q(nn, (e + 2) & (NB - 1));
+    sdp((e + 1) & (NB - 1), scn, dpn);
+    probs(masked, sc, dp, qblock_at(cur.qi) * BQ, e & (NB - 1), pkn, skn);
+    dvdk((e + NB - 1) & (NB - 1), pk, sk);
+    dma_wait();
     __syncthreads();
-    sc = sc_n;
-    dp = dp_n;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pk[j] = pk_n[j];
-      sk[j] = sk_n[j];
-    }
     cur = nxt;
     nxt = nn;
+  };
+  f32x16 scA, dpA, scB, dpB;
+  unsigned int pkA[8], skA[8], pkB[8], skB[8];
+  sdp(0, scA, dpA);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    pkA[j] = 0u;
+    skA[j] = 0u;
   }
-  if (nsteps > 0) dvdk((nsteps - 1) % NB, pk, sk);
+  auto b_to_a = [&]() {
+    scA = scB;
+    dpA = dpB;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pkA[j] = pkB[j];
+      skA[j] = skB[j];
+    }
+  };
+  // steps at the start of each head's list that touch the diagonal block
+  int ndiag = 0;
+  if constexpr (CAUSAL) {
+    if constexpr (MASK) ndiag = (nq > 0 && blist[0] == kblk) ? min(nq, KV_R) : 0;
+    else ndiag = min(nq, KV_R);
+  }
+  int e = 0;
+  for (int hg = 0; hg < s.G; ++hg) {
+    for (int t = 0; t < ndiag; ++t, ++e) {
+      iter(e, std::true_type{}, scA, dpA, pkA, skA, scB, dpB, pkB, skB);
+      b_to_a();
+    }
+    int t = ndiag;
+    for (; t + 1 < nq; t += 2, e += 2) {
+      iter(e, std::false_type{}, scA, dpA, pkA, skA, scB, dpB, pkB, skB);
+      iter(e + 1, std::false_type{}, scB, dpB, pkB, skB, scA, dpA, pkA, skA);
+    }
+    if (t < nq) {
+      iter(e, std::false_type{}, scA, dpA, pkA, skA, scB, dpB, pkB, skB);
+      b_to_a();
+      ++e;
+    }
+  }
+  if (nsteps > 0) dvdk((nsteps - 1) & (NB - 1), pkA, skA);
 
   // dK^T / dV^T: lane holds key kj, d = 32 dt + 8 j + 4 hh + 0..3; dK takes the scale
   const float scale = s.scale;
@@ -417,10 +440,11 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
     qf[ss] = bload16(rq, (unsigned)(qi * D + 16 * ss + 8 * hh) * 2u);
     gf[ss] = bload16(rg, (unsigned)(qi * D + 16 * ss + 8 * hh) * 2u);
   }
-  // this lane's row statistics; a row past N, or one that saw no key, keeps P = 0
-  const float lv = bload_f32(make_rsrc(a.lse + qrow0, (unsigned)N * 4u), (unsigned)qi * 4u);
-  const float dd = bload_f32(make_rsrc(a.dvec + qrow0, (unsigned)N * 4u), (unsigned)qi * 4u);
-  const float lse2 = (qi < N && lv != -INFINITY) ? lv * kLog2e : INFINITY;
+  // this lane's row statistics from stage 0 (qi < npad); a row past N, or one
+  // that saw no key, has LSE +inf and so P = 0
+  const float* st = a.stats + ((size_t)b * s.H + h) * 2 * a.npad;
+  const float lse2 = st[qi];
+  const float dd = st[a.npad + qi];
 
   const int kend = CAUSAL ? min(N, q0 + Q_BM) : N;
   const int ntile_all = (kend + Q_BN - 1) / Q_BN;
@@ -569,9 +593,9 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 template <class T, int D>
 static hipError_t launch_pre_t(const BwdArgs& a, hipStream_t st) {
-  const int rows = a.s.B * a.s.H * a.s.N;
   const int rpb = 256 / (D / 8);
-  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((rows + rpb - 1) / rpb), dim3(256), 0, st, a, rows);
+  const unsigned int blocks = (unsigned)((a.npad + rpb - 1) / rpb) * (unsigned)(a.s.B * a.s.H);
+  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

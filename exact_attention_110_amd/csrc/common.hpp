@@ -150,4 +150,88 @@ __device__ __forceinline__ void batomic_add(rsrc_t r, unsigned int off, float v)
   __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, off, 0, 0);
 }
 
+// ---------------------------------------------------------------------------
+// Tiles staged by LDS DMA (buffer_load ... lds): one wave instruction copies
+// 64 x 16 bytes from per-lane global offsets into 1024 contiguous LDS bytes
+// (lane L at M0 + 16 L); out-of-range lanes deposit zeros. Rows therefore have
+// no padding; instead the 16-byte chunk c of row r is stored at chunk position
+// c ^ swz<D>(r) of that row. The swizzle keeps both access patterns of the
+// MFMA operands free of bank conflicts (64 banks of 4 bytes = 16 chunk slots
+// per 256-byte line):
+//  * 16-byte row reads: 16 lanes read chunk c of 16 consecutive rows, and the
+//    16 (line row, c ^ swz) slots they hit are all distinct;
+//  * transposing reads: 8 consecutive rows x 4 consecutive chunks (64 bytes of
+//    a row); each half of the wave covers 4 rows, whose chunks land in 16
+//    distinct slots.
+// Rows of D 16-bit values; D = 32, 64 or 128. swz has period 16 in r.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  constexpr int RP = 128 / D;  // rows per 256-byte line
+  constexpr int CPR = D / 8;   // 16-byte chunks per row
+  return (4 * ((r / RP) & 3) + ((r >> 2) & 3)) & (CPR - 1);
+}
+// byte offset of chunk c (16-byte units, logical) of row r in a swizzled tile
+template <int D>
+__device__ __forceinline__ int swz_off(int r, int c) {
+  return r * 2 * D + 16 * (c ^ swz<D>(r));
+}
+
+// The DMA loads are written as inline assembly on purpose: the compiler
+// cannot tell which LDS bytes an in-flight LDS DMA will write, so for the
+// builtin it waits for the load to finish before the next LDS read of any
+// buffer, which would expose the full memory latency on every pipeline step.
+// Issued from assembly the loads are invisible to its wait counting; the
+// caller waits for them explicitly (dma_wait) before the barrier that
+// publishes the buffer. M0 (the LDS address) is saved and restored around
+// each load; s_nop 4 covers both the M0 write and a descriptor or offset just
+// written by a VALU instruction.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, unsigned int bytes) {
+  const unsigned long long p = (unsigned long long)base;
+  return (i32x4){(int)(unsigned)p, (int)((p >> 32) & 0xffffu), (int)bytes, kRsrcWord3};
+}
+__device__ __forceinline__ void dma16(i32x4 r, unsigned int voff, lds_t* dst) {
+  const int m0 = __builtin_amdgcn_readfirstlane((int)(size_t)dst);
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 4\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(voff), "s"(r)
+      : "memory");
+}
+// 4 bytes per lane at a per-lane byte offset into dst + 4 lane.
+__device__ __forceinline__ void dma4(i32x4 r, unsigned int voff, lds_t* dst) {
+  const int m0 = __builtin_amdgcn_readfirstlane((int)(size_t)dst);
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 4\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(voff), "s"(r)
+      : "memory");
+}
+// wait until every DMA load of this wave has landed in LDS
+__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Copy rows [row0, row0 + ROWS) of a [*, D] 16-bit tensor (buffer words r,
+// row-major) into the swizzled LDS tile at dst. NW waves share the 1 KB
+// segments; wave w takes segments w, w + NW, ...
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void dma_tile(i32x4 r, int row0, lds_t* dst, int w, int lane) {
+  constexpr int SEG = ROWS * 2 * D / 1024;
+  constexpr int RPS = 1024 / (2 * D);  // rows per segment
+  constexpr int CPR = D / 8;
+  static_assert(SEG >= 1 && (ROWS * 2 * D) % 1024 == 0, "tile must be whole 1 KB segments");
+#pragma unroll
+  for (int sg = 0; sg < (SEG + NW - 1) / NW; ++sg) {
+    const int seg = w + sg * NW;
+    if (SEG % NW == 0 || seg < SEG) {
+      const int row = seg * RPS + lane / CPR;
+      const int c = (lane % CPR) ^ swz<D>(row);
+      dma16(r, (unsigned)((row0 + row) * 2 * D + 16 * c), dst + seg * 1024);
+    }
+  }
+}
+
 }  // namespace fa

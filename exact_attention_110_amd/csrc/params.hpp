@@ -37,7 +37,11 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dvec;    // workspace: D = rowsum(dO * O), [B][H][N]
+  // workspace, [B][H][2][npad] float: plane 0 the log2-scaled LSE (+inf for a
+  // row that saw no key and for the padding rows N..npad-1), plane 1 D =
+  // rowsum(dO * O) (0 for padding rows); npad = N rounded up to 128
+  float* stats;
+  int npad;
 };
 
 // Internal launchers (return a hipError_t from the launch).

@@ -91,8 +91,10 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * fa_backward_workspace_size: bytes of device scratch fa_backward needs for
- * these sizes: one float32 per query row (D = rowsum(dO * O)), rounded up to
- * 256 bytes. Linear in N. Returns 0 for arguments fa_backward would reject.
+ * these sizes: two float32 per query row (D = rowsum(dO * O) and the log-sum-
+ * exp in base 2) for N rounded up to a multiple of 128 rows, per (batch, head),
+ * rounded up to 256 bytes: 8 * B * H * roundup(N, 128). Linear in N. Returns
+ * 0 for arguments fa_backward would reject.
  */
 size_t fa_backward_workspace_size(int B, int H, int Hkv, int N, int d, int dtype);
 
@@ -119,7 +121,8 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
 /*
  * fa_backward_stage: one of the three stages fa_backward runs, in this order,
  * with the same arguments and the same workspace:
- *   stage 0  D = rowsum(dO * O) per query row, into the workspace
+ *   stage 0  D = rowsum(dO * O) and the base-2 LSE per query row, into the
+ *            workspace
  *   stage 1  per key block: recompute P and dS, write dk and dv
  *   stage 2  per query block: recompute P and dS, write dq
  * Stages 1 and 2 both need stage 0's result and nothing from each other.

@@ -99,7 +99,7 @@ def test_workspace_size_formula(lib):
         return (x + 255) // 256 * 256
     for B, H, Hkv, N, d in [(1, 2, 1, 256, 64), (8, 12, 12, 1024, 64), (1, 16, 16, 16384, 128),
                             (1, 1, 1, 1, 32), (2, 3, 1, 77, 128)]:
-        assert ws_size(lib, B, H, Hkv, N, d) == r(B * H * N * 4)
+        assert ws_size(lib, B, H, Hkv, N, d) == r(B * H * 2 * ((N + 127) // 128 * 128) * 4)
     # linear in N
     a, b = ws_size(lib, N=4096), ws_size(lib, N=8192)
     assert b == 2 * a
