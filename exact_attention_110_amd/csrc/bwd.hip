@@ -40,10 +40,6 @@
 
 namespace fa {
 
-// LDS row pitch (bytes) of tiles read both with 16-byte row reads and with
-// transposing reads: rows land on distinct 16-byte bank groups for the first
-// and on distinct 32-byte groups for the second (64 banks of 4 bytes).
-constexpr int lds_pitch(int row_bytes) { return row_bytes == 128 ? 208 : row_bytes + 48; }
 
 // ---------------------------------------------------------------------------
 // stage 0: per query row, D = rowsum(dO * O) in fp32 and the log2-scaled LSE,
@@ -391,15 +387,8 @@ static_assert(Q_BM == 128, "a query-block workgroup must cover exactly one mask 
 
 template <class T, int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
-  constexpr int KP = lds_pitch(2 * D);   // K: 16-byte row reads and transposing reads
-  constexpr int VP = D * 2 + 16;         // V: 16-byte row reads only
-  constexpr int KBUF = Q_BN * KP;
-  constexpr int VBUF = Q_BN * VP;
-  constexpr int NT = Q_NW * 64;
-  constexpr int CH = D / 8;
-  constexpr int TCH = Q_BN * CH;         // 16-byte chunks per tile per tensor
-  constexpr int PER = (TCH + NT - 1) / NT;
-  static_assert(TCH % NT == 0 || TCH < NT, "tile loader shape");
+  constexpr int KBUF = Q_BN * 2 * D;     // K tile: swizzled rows, row reads and transposing reads
+  constexpr int VBUF = Q_BN * 2 * D;     // V tile: swizzled rows, row reads
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
 
@@ -426,8 +415,8 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
   const unsigned int head_bytes = (unsigned int)N * D * 2;
   const rsrc_t rq = make_rsrc((const unsigned short*)a.q + qrow0 * D, head_bytes);
   const rsrc_t rg = make_rsrc((const unsigned short*)a.dO + qrow0 * D, head_bytes);
-  const rsrc_t rk = make_rsrc((const unsigned short*)a.k + krow0 * D, head_bytes);
-  const rsrc_t rv = make_rsrc((const unsigned short*)a.v + krow0 * D, head_bytes);
+  const i32x4 rk = rsrc_words((const unsigned short*)a.k + krow0 * D, head_bytes);
+  const i32x4 rv = rsrc_words((const unsigned short*)a.v + krow0 * D, head_bytes);
   const int q0 = qb * Q_BM;
   const int qw = q0 + 32 * w;
   const int qi = qw + l32;   // this lane's query row
@@ -478,36 +467,21 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
-  s16x8 kreg[PER], vreg[PER];
-  auto gload_tile = [&](int t) {
-#pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      // spare threads of a small tile repeat the last chunk (same data, same place)
-      const int ci = min(tid + r * NT, TCH - 1);
-      const int row = ci / CH, col = (ci % CH) * 8;
-      const unsigned int off = (unsigned)((t * Q_BN + row) * D + col) * 2u;
-      kreg[r] = bload16(rk, off);
-      vreg[r] = bload16(rv, off);
-    }
-  };
-  auto lstore_tile = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const int ci = min(tid + r * NT, TCH - 1);
-      const int row = ci / CH, col = (ci % CH) * 8;
-      lds_write16(kbuf + buf * KBUF + row * KP + col * 2, kreg[r]);
-      lds_write16(vbuf + buf * VBUF + row * VP + col * 2, vreg[r]);
-    }
+  // K and V tiles by LDS DMA into the buffer the previous step read (the
+  // barrier that ended it has passed); rows past N arrive as zeros
+  auto dma_kv = [&](int t, int buf) {
+    dma_tile<D, Q_BN, Q_NW>(rk, t * Q_BN, kbuf + buf * KBUF, w, lane);
+    dma_tile<D, Q_BN, Q_NW>(rv, t * Q_BN, vbuf + buf * VBUF, w, lane);
   };
 
-  gload_tile(ntiles > 0 ? tile_at(0) : 0);
-  lstore_tile(0);
+  dma_kv(ntiles > 0 ? tile_at(0) : 0, 0);
+  dma_wait();
   __syncthreads();
 
   for (int e = 0; e < ntiles; ++e) {
     const int buf = e & 1;
     const int ks = tile_at(e) * Q_BN;
-    gload_tile(tile_at(e + 1 < ntiles ? e + 1 : e));
+    dma_kv(tile_at(e + 1 < ntiles ? e + 1 : e), buf ^ 1);
 
     const bool active = !(CAUSAL && ks > qw + 31);  // wave-uniform
     if (active) {
@@ -526,8 +500,9 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
       for (int ss = 0; ss < NS; ++ss)
 #pragma unroll
         for (int t2 = 0; t2 < Q_T2; ++t2) {
-          const s16x8 ka = lds_read16(kb + (32 * t2 + l32) * KP + (16 * ss + 8 * hh) * 2);
-          const s16x8 va = lds_read16(vb + (32 * t2 + l32) * VP + (16 * ss + 8 * hh) * 2);
+          const int off = swz_off<D>(32 * t2 + l32, 2 * ss + hh);
+          const s16x8 ka = lds_read16(kb + off);
+          const s16x8 va = lds_read16(vb + off);
           sc[t2] = mfma32<T>(ka, qf[ss], sc[t2]);
           dp[t2] = mfma32<T>(va, gf[ss], dp[t2]);
         }
@@ -565,13 +540,16 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
         for (int t2 = 0; t2 < Q_T2; ++t2)
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            const lds_t* kp = kb + (32 * t2 + 16 * u + roff) * KP + (32 * dt + coff) * 2;
-            const s16x8 ka = concat(lds_read_tr(kp), lds_read_tr(kp + 8 * KP));
+            // rows 32 t2 + 16 u + roff and 8 below it, columns 32 dt + coff .. + 3
+            const int c = 4 * dt + (coff >> 3), within = 2 * (coff & 7);
+            const int r0 = 32 * t2 + 16 * u + roff;
+            const s16x8 ka = concat(lds_read_tr(kb + swz_off<D>(r0, c) + within),
+                                    lds_read_tr(kb + swz_off<D>(r0 + 8, c) + within));
             acc[dt] = mfma32<T>(ka, as_operand(sk[t2][4 * u], sk[t2][4 * u + 1], sk[t2][4 * u + 2],
                                                sk[t2][4 * u + 3]), acc[dt]);
           }
     }
-    lstore_tile(buf ^ 1);
+    dma_wait();
     __syncthreads();
   }
 
