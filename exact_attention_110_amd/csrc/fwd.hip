@@ -18,10 +18,10 @@
 //    gfx950 transposing read ds_read_b64_tr_b16, so V needs no transpose pass.
 //  * LDS row pitches are padded so that the 16-byte row reads of K and the
 //    transposing reads of V are free of bank conflicts.
-//  * Dense and causal inputs run fwd64_kernel (64 query rows per wave, one
-//    wave per SIMD, 256 rows per workgroup); block-sparse inputs run
-//    fwd_kernel (32 rows per wave, two waves per SIMD, 128 rows per
-//    workgroup = one mask block row).
+//  * Long dense or causal inputs over few heads run fwd64_kernel (64 query
+//    rows per wave, one wave per SIMD, 256 rows per workgroup); the others,
+//    and all block-sparse inputs, run fwd_kernel (32 rows per wave, two waves
+//    per SIMD, 128 rows per workgroup = one mask block row).
 //  * Causal: a workgroup stops at its diagonal tile, waves skip tiles that lie
 //    wholly after their rows, and only diagonal and tail tiles are masked
 //    element by element. Heaviest query blocks are launched first.
@@ -31,6 +31,8 @@
 //
 // float32 inputs take a separate VALU kernel (fp32 FMA throughout) that runs
 // the same recurrence one query row per lane.
+#include <stdlib.h>
+
 #include "common.hpp"
 #include "params.hpp"
 
@@ -608,17 +610,25 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
   }
 }
 
-// float32: one query row per lane, fp32 FMA for every product, keys in LDS tiles.
-constexpr int F32_ROWS = 64;
-constexpr int F32_BN = 32;
+// float32: fp32 FMA for every product. The float32 inputs are small (the
+// worked example is one 512 x 32 head), so the kernel is built for latency:
+// each query row is split over F32_S threads that run the online recurrence
+// over interleaved 4-key chunks of the row's keys, each keeping its own
+// (m, l, o); the partial states of a row are then merged through LDS with the
+// same correction factors, m = max m_s, l = sum l_s exp(m_s - m),
+// o = sum o_s exp(m_s - m), each thread of the row finishing D / F32_S
+// output columns.
+constexpr int F32_R = 8;    // query rows per workgroup (divides the 128-row mask block)
+constexpr int F32_S = 16;   // threads (key splits) per row
+constexpr int F32_C = 4;    // keys per chunk
 
 template <int D>
-__global__ __launch_bounds__(F32_ROWS) void fwd_f32_kernel(FwdArgs a) {
-  __shared__ float Ks[F32_BN][D];
-  __shared__ float Vs[F32_BN][D];
+__global__ __launch_bounds__(F32_R * F32_S) void fwd_f32_kernel(FwdArgs a) {
+  __shared__ float part[F32_R][F32_S][D + 2];  // o[0..D), m, l of each split
   const AttnShape& s = a.s;
   const int N = s.N;
   const int tid = threadIdx.x;
+  const int r = tid % F32_R, sp = tid / F32_R;  // a wave holds 8 splits of the 8 rows
   const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int hk = h / s.G;
   const size_t qrow0 = (size_t)(b * s.H + h) * N;
@@ -626,10 +636,10 @@ __global__ __launch_bounds__(F32_ROWS) void fwd_f32_kernel(FwdArgs a) {
   const float* Q = (const float*)a.q + qrow0 * D;
   const float* K = (const float*)a.k + krow0 * D;
   const float* V = (const float*)a.v + krow0 * D;
-  const int q0 = qb * F32_ROWS;
-  const int qi = q0 + tid;
+  const int q0 = qb * F32_R;
+  const int qi = q0 + r;
   const float c = fmaxf(s.scale * kLog2e, 1e-30f);
-  const int mrow = q0 / 128;  // the 64 rows of a workgroup lie in one mask block row
+  const int mrow = q0 / 128;  // every row of the workgroup is in this mask block row
 
   float q[D], o[D];
 #pragma unroll
@@ -638,57 +648,104 @@ __global__ __launch_bounds__(F32_ROWS) void fwd_f32_kernel(FwdArgs a) {
     o[dd] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
-  const int kend = s.causal ? min(N, q0 + F32_ROWS) : N;
-  for (int ks = 0; ks < kend; ks += F32_BN) {
-    if (s.mask && s.mask[(size_t)mrow * s.nb + ks / 128] == 0) continue;  // uniform
-    __syncthreads();
-    for (int i = tid; i < F32_BN * D; i += F32_ROWS) {
-      const int r = i / D, cc = i % D;
-      const int key = ks + r;
-      Ks[r][cc] = key < N ? K[(size_t)key * D + cc] : 0.f;
-      Vs[r][cc] = key < N ? V[(size_t)key * D + cc] : 0.f;
-    }
-    __syncthreads();
-    float x[F32_BN];
+  const int kend_row = s.causal ? min(N, qi + 1) : N;
+  const int kend = s.causal ? min(N, q0 + F32_R) : N;  // bound for the workgroup
+  for (int j0 = sp * F32_C; j0 < kend; j0 += F32_S * F32_C) {
+    float x[F32_C];
     float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < F32_BN; ++j) {
+    for (int t = 0; t < F32_C; ++t) {
+      const int j = j0 + t;
+      const bool vis = j < kend_row && (!s.mask || s.mask[(size_t)mrow * s.nb + j / 128] != 0);
       float dot = 0.f;
+      if (vis) {
+        const float4* kr = (const float4*)(K + (size_t)j * D);
 #pragma unroll
-      for (int dd = 0; dd < D; ++dd) dot = fmaf(q[dd], Ks[j][dd], dot);
-      const int key = ks + j;
-      const bool vis = key < N && (!s.causal || key <= qi);
-      x[j] = vis ? dot * c : -INFINITY;
-      mx = fmaxf(mx, x[j]);
+        for (int d4 = 0; d4 < D / 4; ++d4) {
+          const float4 kv = kr[d4];
+          dot = fmaf(q[4 * d4], kv.x, dot);
+          dot = fmaf(q[4 * d4 + 1], kv.y, dot);
+          dot = fmaf(q[4 * d4 + 2], kv.z, dot);
+          dot = fmaf(q[4 * d4 + 3], kv.w, dot);
+        }
+      }
+      x[t] = vis ? dot * c : -INFINITY;
+      mx = fmaxf(mx, x[t]);
     }
-    const float m_new = fmaxf(m, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float corr = fast_exp2(m - m_use);
-    m = m_new;
-    l *= corr;
+    if (mx == -INFINITY) continue;  // nothing visible in this chunk for this row
+    if (mx > m) {
+      const float corr = fast_exp2(m - mx);  // 0 while m is still -inf
+      l *= corr;
 #pragma unroll
-    for (int dd = 0; dd < D; ++dd) o[dd] *= corr;
+      for (int dd = 0; dd < D; ++dd) o[dd] *= corr;
+      m = mx;
+    }
 #pragma unroll
-    for (int j = 0; j < F32_BN; ++j) {
-      const float p = fast_exp2(x[j] - m_use);
+    for (int t = 0; t < F32_C; ++t) {
+      const float p = fast_exp2(x[t] - m);  // 0 for hidden keys
+      if (p == 0.f) continue;
       l += p;
+      const float4* vr = (const float4*)(V + (size_t)(j0 + t) * D);
 #pragma unroll
-      for (int dd = 0; dd < D; ++dd) o[dd] = fmaf(p, Vs[j][dd], o[dd]);
+      for (int d4 = 0; d4 < D / 4; ++d4) {
+        const float4 vv = vr[d4];
+        o[4 * d4] = fmaf(p, vv.x, o[4 * d4]);
+        o[4 * d4 + 1] = fmaf(p, vv.y, o[4 * d4 + 1]);
+        o[4 * d4 + 2] = fmaf(p, vv.z, o[4 * d4 + 2]);
+        o[4 * d4 + 3] = fmaf(p, vv.w, o[4 * d4 + 3]);
+      }
     }
   }
-  if (qi < N) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    float* Op = (float*)a.o + (qrow0 + qi) * D;
+
+  // merge the F32_S partial states of each row
 #pragma unroll
-    for (int dd = 0; dd < D; ++dd) Op[dd] = o[dd] * inv;
-    a.lse[qrow0 + qi] = l > 0.f ? (m + fast_log2(l)) * kLn2 : -INFINITY;
+  for (int dd = 0; dd < D; ++dd) part[r][sp][dd] = o[dd];
+  part[r][sp][D] = m;
+  part[r][sp][D + 1] = l;
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < F32_S; ++t) M = fmaxf(M, part[r][t][D]);
+  const float Mu = M == -INFINITY ? 0.f : M;
+  float wgt[F32_S];
+  float L = 0.f;
+#pragma unroll
+  for (int t = 0; t < F32_S; ++t) {
+    wgt[t] = fast_exp2(part[r][t][D] - Mu);  // 0 for a split that saw no key
+    L = fmaf(part[r][t][D + 1], wgt[t], L);
+  }
+  if (qi < N) {
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    constexpr int DS = D / F32_S;  // output columns finished by each split
+    float* Op = (float*)a.o + (qrow0 + qi) * D + sp * DS;
+#pragma unroll
+    for (int dd = 0; dd < DS; ++dd) {
+      float acc = 0.f;
+#pragma unroll
+      for (int t = 0; t < F32_S; ++t) acc = fmaf(part[r][t][sp * DS + dd], wgt[t], acc);
+      Op[dd] = acc * inv;
+    }
+    if (sp == 0) a.lse[qrow0 + qi] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
   }
 }
 
 template <class T, int D>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   const bool causal = a.s.causal != 0, mask = a.s.mask != nullptr;
-  if (!mask) {
+  // The 64-row kernel pays off for long sequences over few heads (measured:
+  // N = 16384 x 16 heads, 4% faster). With many workgroups the 32-row kernel's
+  // two waves per SIMD balance better (4 x 32 heads at N = 8192: 6% faster),
+  // and short rows spend much of their time in the 64-row kernel's diagonal
+  // tail (N = 1024: 1.8x faster with 32 rows).
+  // FA_FORWARD_ROWS_PER_WAVE=64 or 32 overrides the choice (tests use it to
+  // cover both kernels at every size).
+  const long long wg64 = (long long)a.s.B * a.s.H * ((a.s.N + F64_BM - 1) / F64_BM);
+  bool use64 = a.s.N >= 8192 && wg64 <= 2048;
+  if (const char* env = getenv("FA_FORWARD_ROWS_PER_WAVE")) {
+    if (env[0] == '6' && env[1] == '4' && env[2] == 0) use64 = true;
+    if (env[0] == '3' && env[1] == '2' && env[2] == 0) use64 = false;
+  }
+  if (!mask && use64) {
     const dim3 grid(a.s.H, (a.s.N + F64_BM - 1) / F64_BM, a.s.B);
     if (causal) hipLaunchKernelGGL((fwd64_kernel<T, D, true>), grid, dim3(F64_NW * 64), 0, st, a);
     else hipLaunchKernelGGL((fwd64_kernel<T, D, false>), grid, dim3(F64_NW * 64), 0, st, a);
@@ -705,8 +762,8 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
 
 template <int D>
 static hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st) {
-  const dim3 grid((a.s.N + F32_ROWS - 1) / F32_ROWS, a.s.H, a.s.B);
-  hipLaunchKernelGGL((fwd_f32_kernel<D>), grid, dim3(F32_ROWS), 0, st, a);
+  const dim3 grid((a.s.N + F32_R - 1) / F32_R, a.s.H, a.s.B);
+  hipLaunchKernelGGL((fwd_f32_kernel<D>), grid, dim3(F32_R * F32_S), 0, st, a);
   return hipGetLastError();
 }
 

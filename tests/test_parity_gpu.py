@@ -40,6 +40,16 @@ def test_dense(shape, causal, dtype):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_dense_64_rows_per_wave(shape, causal, monkeypatch):
+    """The 64-row forward kernel (chosen by the library for long sequences over
+    few heads) at every small shape, forced through its override."""
+    monkeypatch.setenv("FA_FORWARD_ROWS_PER_WAVE", "64")
+    B, H, Hkv, N, d = shape
+    PT.run_small(B, H, Hkv, N, d, "bf16", causal, seed=5000 + N + d + int(causal), backward=False)
+
+
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("N", [1, 100, 512, 700])
 def test_fp32_forward(N, d, causal):
@@ -67,9 +77,10 @@ def test_empty_rows(dtype):
     assert res["o"] <= (PT.TOL_F32 if dtype == "fp32" else PT.TOL_16)
 
 
+@pytest.mark.parametrize("rows", ["64", "32"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_late_dominant_scores(dtype, causal):
+def test_late_dominant_scores(dtype, causal, rows, monkeypatch):
     """Keys far into the sequence whose scores exceed every earlier one by far
     more than the forward's fixed-reference range (keys 400..410: about 90 in
     log2 units above the first tile's maximum, forcing a restart with lazy
@@ -77,6 +88,7 @@ def test_late_dominant_scores(dtype, causal):
     keep their random part: with identical key rows the exact dQ of every row
     that attends to them would be zero (the dS of a row sums to zero), and any
     rounding of dS would make the relative error meaningless."""
+    monkeypatch.setenv("FA_FORWARD_ROWS_PER_WAVE", rows)
     N, d = 600, 64
     x = I.make_small(1, 2, 1, N, d, dtype, 21)
     x["q"] = x["q"] + 1.0
@@ -88,7 +100,7 @@ def test_late_dominant_scores(dtype, causal):
     q, k = (PT.np64(x[n]) for n in ("q", "k"))
     big = float(np.abs(q @ np.swapaxes(k, -1, -2)).max()) / np.sqrt(d)
     tol = PT.TOL_LSE + 4 * 2.0 ** -23 * big
-    PT.run_given(x, dtype, causal, where=f"late dominant scores {dtype} causal={causal}", lse_tol=tol)
+    PT.run_given(x, dtype, causal, where=f"late dominant scores {dtype} causal={causal} rows={rows}", lse_tol=tol)
 
 
 def test_scale_zero_is_uniform():
