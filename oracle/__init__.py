@@ -12,10 +12,16 @@ the one on the pranaymahendrakar.com lesson "FlashAttention" (Researcher tier,
 "The problem being solved", the equation for O). Every function in
 ``oracle.attention`` says which passage it follows.
 
+``oracle.dropout`` adds dropout on the probabilities (Philox4x32-10 keep
+decisions addressed by batch-head, query and key), used by the forward and
+backward functions when a positive rate is given.
+
 Parity pins: every function is checked in ``tests/test_oracle.py`` against values
 or facts that do not come from the oracle itself (the lesson's worked example,
-brute force with scalar loops, closed forms, invariants, finite differences and
-PyTorch's own float64 CPU attention). No function here is "parity unpinned".
+brute force with scalar loops, closed forms, invariants, finite differences,
+PyTorch's own float64 CPU attention, the generator's published known-answer
+vectors and the statistics of its keep decisions). No function here is
+"parity unpinned".
 """
 
 from .attention import (  # noqa: F401
@@ -28,3 +34,4 @@ from .attention import (  # noqa: F401
     forward,
     backward,
 )
+from . import dropout  # noqa: F401

@@ -35,6 +35,8 @@ differences in the tests.
 
 import numpy as np
 
+from . import dropout as _dropout
+
 MASK_BLOCK = 128  # block-mask granularity in rows and columns
 
 
@@ -113,8 +115,22 @@ def head_probabilities(q, k, scale, causal=False, block_mask=None, rows=None):
     return p, lse
 
 
-def head_forward(q, k, v, scale, causal=False, block_mask=None, rows=None, chunk=256):
-    """O and L for the given query rows of one head (q: [N, d], k, v: [N, d])."""
+def _drop(p, rows, keys, dropout):
+    """p with dropout applied (kept values scaled), or p unchanged when dropout is None.
+
+    dropout = (rate, seed, bh): see ``oracle.dropout``."""
+    if dropout is None:
+        return p
+    rate, seed, bh = dropout
+    z = _dropout.keep_mask(seed, bh, rows, keys, rate)
+    return np.where(z, p * _dropout.keep_scale(rate), 0.0)
+
+
+def head_forward(q, k, v, scale, causal=False, block_mask=None, rows=None, chunk=256, dropout=None):
+    """O and L for the given query rows of one head (q: [N, d], k, v: [N, d]).
+
+    With dropout = (rate, seed, bh) the probabilities are dropped and rescaled
+    before they weight V; L is still that of the scores before dropout."""
     n = k.shape[0]
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
     o = np.zeros((rows.size, v.shape[1]))
@@ -125,18 +141,20 @@ def head_forward(q, k, v, scale, causal=False, block_mask=None, rows=None, chunk
         if keys.size:
             vis = visible(ch, keys, causal, block_mask)
             _, p, l_ = _row_softmax(q[ch], k[keys], scale, vis)
-            o[pos:pos + ch.size] = p @ v[keys]
+            o[pos:pos + ch.size] = _drop(p, ch, keys, dropout) @ v[keys]
             lse[pos:pos + ch.size] = l_
         pos += ch.size
     return o, lse
 
 
-def head_backward(q, k, v, do, scale, causal=False, block_mask=None, chunk=256):
+def head_backward(q, k, v, do, scale, causal=False, block_mask=None, chunk=256, dropout=None):
     """Gradients of sum(O * dO) for one query head.
 
-    With p the probability rows and g = dO:
-      dV_j += sum_i p_ij g_i
-      dP_ij = g_i . v_j
+    With p the probability rows, g = dO, and (under dropout) r the dropped and
+    rescaled probabilities r_ij = p_ij z_ij c (z the keep decision, c the keep
+    scale; without dropout r = p and z c = 1):
+      dV_j += sum_i r_ij g_i
+      dP_ij = z_ij c (g_i . v_j)          (gradient with respect to p_ij)
       D_i   = sum_j p_ij dP_ij            (equals g_i . o_i)
       dS_ij = p_ij (dP_ij - D_i)          (softmax Jacobian)
       dQ_i  = scale * sum_j dS_ij k_j
@@ -156,8 +174,8 @@ def head_backward(q, k, v, do, scale, causal=False, block_mask=None, chunk=256):
         vis = visible(ch, keys, causal, block_mask)
         _, p, _ = _row_softmax(q[ch], k[keys], scale, vis)
         g = do[ch]
-        dv[keys] += p.T @ g
-        dp = g @ v[keys].T
+        dv[keys] += _drop(p, ch, keys, dropout).T @ g
+        dp = _drop(g @ v[keys].T, ch, keys, dropout)
         dd = (p * dp).sum(axis=1)
         ds = p * (dp - dd[:, None])
         dq[ch] = scale * (ds @ k[keys])
@@ -171,12 +189,15 @@ def _heads(B, H, heads):
     return [(int(b), int(h)) for b, h in heads]
 
 
-def forward(q, k, v, scale, causal=False, block_mask=None, heads=None, rows=None, chunk=256):
+def forward(q, k, v, scale, causal=False, block_mask=None, heads=None, rows=None, chunk=256,
+            dropout_rate=0.0, seed=0):
     """Attention forward over [B, H, N, d] queries and [B, Hkv, N, d] keys/values.
 
     Query head h reads kv head h // (H // Hkv). With ``heads=None`` returns full
     o [B, H, R, d] and lse [B, H, R] (R = len(rows) or N); otherwise arrays
     stacked in the order of ``heads`` (a list of (b, h)): o [nh, R, d], lse [nh, R].
+    A positive ``dropout_rate`` applies dropout with the generator keyed by
+    ``seed`` (``oracle.dropout``); query head (b, h) draws stream b * H + h.
     """
     B, H, N, d = q.shape
     Hkv = k.shape[1]
@@ -186,7 +207,8 @@ def forward(q, k, v, scale, causal=False, block_mask=None, heads=None, rows=None
     hl = _heads(B, H, heads)
     outs, lses = [], []
     for b, h in hl:
-        o, l_ = head_forward(q[b, h], k[b, h // G], v[b, h // G], scale, causal, block_mask, rows, chunk)
+        dr = (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None
+        o, l_ = head_forward(q[b, h], k[b, h // G], v[b, h // G], scale, causal, block_mask, rows, chunk, dr)
         outs.append(o)
         lses.append(l_)
     o = np.stack(outs)
@@ -197,8 +219,9 @@ def forward(q, k, v, scale, causal=False, block_mask=None, heads=None, rows=None
     return o, lse
 
 
-def backward(q, k, v, do, scale, causal=False, block_mask=None, heads=None, chunk=256):
-    """Gradients of sum(O * dO) with respect to q, k, v.
+def backward(q, k, v, do, scale, causal=False, block_mask=None, heads=None, chunk=256,
+             dropout_rate=0.0, seed=0):
+    """Gradients of sum(O * dO) with respect to q, k, v (dropout as in ``forward``).
 
     With ``heads=None`` returns full dq [B, H, N, d], dk, dv [B, Hkv, N, d]
     (dk, dv summed over each kv head's group of query heads). With a list of
@@ -216,12 +239,14 @@ def backward(q, k, v, do, scale, causal=False, block_mask=None, heads=None, chun
         dv = np.zeros_like(v)
         for b in range(B):
             for h in range(H):
+                dr = (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None
                 a, bk, bv = head_backward(q[b, h], k[b, h // G], v[b, h // G], do[b, h],
-                                          scale, causal, block_mask, chunk)
+                                          scale, causal, block_mask, chunk, dr)
                 dq[b, h] = a
                 dk[b, h // G] += bk
                 dv[b, h // G] += bv
         return dq, dk, dv
-    res = [head_backward(q[b, h], k[b, h // G], v[b, h // G], do[b, h], scale, causal, block_mask, chunk)
+    res = [head_backward(q[b, h], k[b, h // G], v[b, h // G], do[b, h], scale, causal, block_mask, chunk,
+                         (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None)
            for b, h in _heads(B, H, heads)]
     return tuple(np.stack(x) for x in zip(*res))

@@ -274,18 +274,19 @@ def pin_causal_locality():
 # ----------------------------------------------------------------------------------------------
 # P-9: analytic gradients against central finite differences of f = sum(O * dO)
 # ----------------------------------------------------------------------------------------------
-def _fd_case(B, H, Hkv, n, d, causal, bm, seed, ncoord=24, h=1e-6):
+def _fd_case(B, H, Hkv, n, d, causal, bm, seed, ncoord=24, h=1e-6, rate=0.0):
     q = _rand((B, H, n, d), seed)
     k = _rand((B, Hkv, n, d), seed + 1)
     v = _rand((B, Hkv, n, d), seed + 2)
     g = _rand((B, H, n, d), seed + 3)
     scale = 0.6
+    drop_seed = 1234567 + seed  # a fixed keep mask: the output is then differentiable
 
     def f(q_, k_, v_):
-        o, _ = A.forward(q_, k_, v_, scale, causal, bm)
+        o, _ = A.forward(q_, k_, v_, scale, causal, bm, dropout_rate=rate, seed=drop_seed)
         return float((o * g).sum())
 
-    grads = A.backward(q, k, v, g, scale, causal, bm)
+    grads = A.backward(q, k, v, g, scale, causal, bm, dropout_rate=rate, seed=drop_seed)
     rng = np.random.default_rng(seed + 4)
     for which, x in enumerate((q, k, v)):
         num, ana = [], []
@@ -438,6 +439,81 @@ def pin_torch_sdpa():
         assert np.abs(l_ - torch.logsumexp(s, dim=-1).numpy()).max() <= 1e-12
 
 
+# ----------------------------------------------------------------------------------------------
+# Dropout (fused into the kernel per the chipfoundryservices.com glossary "flash attention
+# algorithm", "Kernel Fusion"; reading and generator in oracle/dropout.py)
+# ----------------------------------------------------------------------------------------------
+def pin_philox_known_answers():
+    """The generator reproduces Philox4x32-10's published known-answer vectors."""
+    from oracle import dropout as Dr
+    kat = json.load(open(os.path.join(GOLDEN, "philox4x32_10_kat.json")))
+    for vec in kat["vectors"]:
+        ctr = np.array([int(x, 16) for x in vec["counter"]], dtype=np.uint64)
+        key = [int(x, 16) for x in vec["key"]]
+        out = Dr.philox4x32(ctr, key)
+        assert [int(x) for x in out] == [int(x, 16) for x in vec["output"]], vec
+
+
+def pin_dropout_statistics():
+    """Keep decisions: the rate they realise, uniform bytes, no correlation between
+    neighbouring elements, and every (seed, head, row, key) addressed on its own."""
+    from oracle import dropout as Dr
+    rows, keys = np.arange(256), np.arange(512)
+    b0 = Dr.random_bytes(7, 0, rows, keys).astype(np.int64)
+    b1 = Dr.random_bytes(7, 1, rows, keys).astype(np.int64)
+    allb = np.concatenate([b0.ravel(), b1.ravel()])
+    n = allb.size
+    hist = np.bincount(allb, minlength=256)
+    chi2 = float(((hist - n / 256) ** 2 / (n / 256)).sum())
+    assert chi2 < 255 + 6 * math.sqrt(2 * 255), chi2          # 255 degrees of freedom
+    for rate in (0.1, 0.3, 0.5, 0.9):
+        t = Dr.threshold(rate)
+        kept = float((allb >= t).mean())
+        p = (256 - t) / 256
+        assert abs(kept - p) < 6 * math.sqrt(p * (1 - p) / n), (rate, kept, p)
+    z = (b0 >= 128).astype(np.float64) - 0.5
+    for a, bb in ((z[:, :-1], z[:, 1:]), (z[:-1], z[1:]), (z[:, :-4], z[:, 4:]), (z[:-4], z[4:])):
+        assert abs(float((a * bb).mean())) < 6 * 0.25 / math.sqrt(a.size)
+    assert float((b0 == b1).mean()) < 0.01                     # heads draw different streams
+    assert float((b0 == Dr.random_bytes(8, 0, rows, keys)).mean()) < 0.01
+    # counter addressing: any subset of rows and keys gives the same bytes
+    sub = Dr.random_bytes(7, 0, rows[37:101:3], keys[5:300:7])
+    assert np.array_equal(sub, b0[37:101:3][:, 5:300:7])
+    # quantised rate: t = round(256 rate), keep scale 256 / (256 - t)
+    assert Dr.threshold(0.0) == 0 and Dr.threshold(0.5) == 128 and Dr.threshold(0.999) == 255
+    assert Dr.keep_scale(0.25) == 256.0 / 192.0
+
+
+def pin_dropout_expectation():
+    """Averaged over seeds, the dropped output equals the output without dropout
+    (kept probabilities are rescaled by the inverse keep probability), and the
+    saved log-sum-exp is that of the scores before dropout."""
+    q, k, v = _rand((1, 1, 6, 3), 501), _rand((1, 1, 6, 3), 502), _rand((1, 1, 6, 3), 503)
+    o_ref, l_ref = A.forward(q, k, v, 0.8, True)
+    acc = np.zeros_like(o_ref)
+    nseed = 3000
+    for sd in range(nseed):
+        o, l_ = A.forward(q, k, v, 0.8, True, dropout_rate=0.5, seed=sd)
+        assert np.array_equal(l_, l_ref)
+        acc += o
+    # per element the dropped output has variance below max|v|^2 / keep = 2 max|v|^2
+    bound = 6 * math.sqrt(2.0) * np.abs(v).max() / math.sqrt(nseed)
+    assert np.abs(acc / nseed - o_ref).max() < bound
+    # a rate that rounds to t = 0 keeps everything, unscaled
+    o0, l0 = A.forward(q, k, v, 0.8, True, dropout_rate=0.001, seed=3)
+    assert np.array_equal(o0, o_ref) and np.array_equal(l0, l_ref)
+
+
+def pin_dropout_finite_differences():
+    """With a fixed keep mask the dropped output is a smooth function of q, k, v;
+    its analytic gradients match central differences."""
+    _fd_case(1, 1, 1, 12, 4, False, None, 140, rate=0.3)
+    _fd_case(1, 2, 2, 12, 4, True, None, 150, rate=0.5)
+    _fd_case(2, 4, 2, 10, 3, True, None, 160, rate=0.2)
+
+
 ALL_PINS = [pin_worked_example, pin_recurrence, pin_brute_force, pin_rows_sum_to_one, pin_zero_query,
             pin_dominant_score, pin_permutation, pin_causal_locality, pin_finite_differences,
-            pin_gqa_repeat, pin_mask_semantics, pin_empty_rows, pin_scale_zero, pin_torch_sdpa]
+            pin_gqa_repeat, pin_mask_semantics, pin_empty_rows, pin_scale_zero, pin_torch_sdpa,
+            pin_philox_known_answers, pin_dropout_statistics, pin_dropout_expectation,
+            pin_dropout_finite_differences]

@@ -23,8 +23,9 @@ MUTANTS = {
                         "bm[(keys // block)[None, :], (rows // block)[:, None]]"),
     "scale_dropped": ("s = scale * (q_rows @ k_keys.T)", "s = q_rows @ k_keys.T"),
     "lse_without_max": ("m0 + np.log(np.where(has, ssum, 1.0))", "np.log(np.where(has, ssum, 1.0))"),
-    "output_uses_keys": ("o[pos:pos + ch.size] = p @ v[keys]", "o[pos:pos + ch.size] = p @ k[keys]"),
-    "dv_wrong_operand": ("dv[keys] += p.T @ g", "dv[keys] += p.T @ q[ch]"),
+    "output_uses_keys": ("o[pos:pos + ch.size] = _drop(p, ch, keys, dropout) @ v[keys]",
+                         "o[pos:pos + ch.size] = _drop(p, ch, keys, dropout) @ k[keys]"),
+    "dv_wrong_operand": ("dv[keys] += _drop(p, ch, keys, dropout).T @ g", "dv[keys] += _drop(p, ch, keys, dropout).T @ q[ch]"),
     "ds_sign": ("ds = p * (dp - dd[:, None])", "ds = p * (dp + dd[:, None])"),
     "ds_drops_p": ("ds = p * (dp - dd[:, None])", "ds = (dp - dd[:, None])"),
     "dd_drops_p": ("dd = (p * dp).sum(axis=1)", "dd = dp.sum(axis=1)"),
@@ -34,6 +35,14 @@ MUTANTS = {
                    "o, l_ = head_forward(q[b, h], k[b, h % Hkv], v[b, h % Hkv]"),
     "gqa_backward_modulo": ("dk[b, h // G] += bk", "dk[b, h % Hkv] += bk"),
     "candidate_keys_short": ("keys = keys[keys <= rows.max()]", "keys = keys[keys < rows.max()]"),
+    "dropout_unscaled": ("return np.where(z, p * _dropout.keep_scale(rate), 0.0)", "return np.where(z, p, 0.0)"),
+    "dropout_scaled_by_rate": ("return np.where(z, p * _dropout.keep_scale(rate), 0.0)",
+                               "return np.where(z, p / rate, 0.0)"),
+    "dropout_dp_unmasked": ("dp = _drop(g @ v[keys].T, ch, keys, dropout)", "dp = g @ v[keys].T"),
+    "dropout_dv_undropped": ("dv[keys] += _drop(p, ch, keys, dropout).T @ g", "dv[keys] += p.T @ g"),
+    "dropout_before_softmax": ("o[pos:pos + ch.size] = _drop(p, ch, keys, dropout) @ v[keys]",
+                               "o[pos:pos + ch.size] = (lambda r: r / np.maximum(r.sum(1, keepdims=True), 1e-300))"
+                               "(_drop(p, ch, keys, dropout)) @ v[keys]"),
 }
 
 
@@ -41,8 +50,9 @@ def _load_mutant(old, new):
     src = open(SRC).read()
     assert src.count(old) >= 1, old
     src = src.replace(old, new)
-    mod = types.ModuleType("oracle_mutant")
+    mod = types.ModuleType("oracle.attention_mutant")
     mod.__file__ = SRC
+    mod.__package__ = "oracle"  # its relative import of oracle.dropout resolves
     exec(compile(src, SRC + " (mutant)", "exec"), mod.__dict__)
     return mod
 
