@@ -92,6 +92,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long_seq_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="run the fused-dropout kernels at this rate (not the headline configuration)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after timing, run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -157,10 +159,12 @@ def main():
     fwd_flop = sparse_flops(w, x["mask"], False) if w.sparse else flops(w, False)
     bwd_flop = total_flop - fwd_flop
 
+    drop = dict(dropout_rate=args.dropout, seed=1234) if args.dropout else {}
+
     def step():
-        binding.forward(q, k, v, w.scale, w.causal, mask, out=o, lse=lse)
+        binding.forward(q, k, v, w.scale, w.causal, mask, out=o, lse=lse, **drop)
         if w.backward:
-            binding.backward(q, k, v, o, lse, do, w.scale, w.causal, mask, ws=ws, grads=(dq, dk, dv))
+            binding.backward(q, k, v, o, lse, do, w.scale, w.causal, mask, ws=ws, grads=(dq, dk, dv), **drop)
 
     for _ in range(args.warmup):
         step()
@@ -188,13 +192,13 @@ def main():
 
     n_ev = max(args.steps, 5)
     per_contraction = fwd_flop / 2.0  # one N x N x d contraction of the workload
-    t_fwd = event_time(lambda: binding.forward(q, k, v, w.scale, w.causal, mask, out=o, lse=lse), n_ev)
+    t_fwd = event_time(lambda: binding.forward(q, k, v, w.scale, w.causal, mask, out=o, lse=lse, **drop), n_ev)
     # kernel -> (mean launch time in ms, algorithmic FLOP per launch)
     # dense and causal inputs run the 64-row forward kernel, block-sparse ones the 32-row one
     kernels = {("fwd_kernel" if mask is not None else "fwd64_kernel"): (t_fwd, 2 * per_contraction)}
     if w.backward:
         stage = lambda s: (lambda: binding.backward_stage(s, q, k, v, o, lse, do, dq, dk, dv, ws,  # noqa: E731
-                                                          w.scale, w.causal, mask))
+                                                          w.scale, w.causal, mask, **drop))
         t_pre = event_time(stage(0), n_ev)
         t_kv = event_time(stage(1), n_ev)
         t_q = event_time(stage(2), n_ev)
@@ -210,7 +214,7 @@ def main():
     achieved = f_dom / (t_dom * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic(dom, w.name),
+                "traffic": None if args.dropout else measured_traffic(dom, w.name),
                 "launch_ms": round(t_dom, 4), "flop_per_launch": f_dom,
                 "kernels_ms": {n: round(v[0], 4) for n, v in kernels.items()}}
 
@@ -235,7 +239,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
                    "causal": w.causal, "block_sparse": w.sparse, "passes": "fwd+bwd" if w.backward else "fwd",
-                   "flop_per_step": total_flop, "mfma_peak_frac": round(value / PEAK_BF16_TFLOPS, 4)},
+                   "flop_per_step": total_flop, "mfma_peak_frac": round(value / PEAK_BF16_TFLOPS, 4),
+                   "dropout": args.dropout},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

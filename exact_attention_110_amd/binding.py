@@ -49,6 +49,14 @@ def load():
     lib.fa_backward.restype = I
     lib.fa_backward_stage.argtypes = [I] + bw
     lib.fa_backward_stage.restype = I
+    U64 = ctypes.c_ulonglong
+    lib.fa_forward_dropout.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, I, F, U64, P]
+    lib.fa_forward_dropout.restype = I
+    bwd_drop = bw[:18] + [F, U64] + bw[18:]
+    lib.fa_backward_dropout.argtypes = bwd_drop
+    lib.fa_backward_dropout.restype = I
+    lib.fa_backward_stage_dropout.argtypes = [I] + bwd_drop
+    lib.fa_backward_stage_dropout.restype = I
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -94,17 +102,26 @@ def _mask(block_mask, N, device):
     return block_mask.to(device).contiguous()
 
 
-def forward(q, k, v, scale=None, causal=False, block_mask=None, out=None, lse=None):
-    """O, LSE = attention(q, k, v); q [B,H,N,d], k, v [B,Hkv,N,d] on the GPU."""
+def forward(q, k, v, scale=None, causal=False, block_mask=None, out=None, lse=None, dropout_rate=0.0,
+            seed=0):
+    """O, LSE = attention(q, k, v); q [B,H,N,d], k, v [B,Hkv,N,d] on the GPU.
+
+    A positive dropout_rate calls fa_forward_dropout with the 64-bit seed."""
     B, H, Hkv, N, d = _shape(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     m = _mask(block_mask, N, q.device)
-    st = load().fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, Hkv, N, d, scale,
-                           int(bool(causal)), _ptr(m), _DTYPES[q.dtype], _stream(q.device))
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, Hkv, N, d, scale, int(bool(causal)), _ptr(m),
+            _DTYPES[q.dtype]]
+    if dropout_rate:
+        st = load().fa_forward_dropout(*args, float(dropout_rate), int(seed) & (2**64 - 1), _stream(q.device))
+        where = "fa_forward_dropout"
+    else:
+        st = load().fa_forward(*args, _stream(q.device))
+        where = "fa_forward"
     if st != 0:
-        raise FAError(st, "fa_forward")
+        raise FAError(st, where)
     return o, lse_t
 
 
@@ -120,15 +137,18 @@ def workspace(q, k):
     return torch.empty(n, dtype=torch.uint8, device=q.device)
 
 
-def _bwd_args(q, k, v, o, lse, do, dq, dk, dv, scale, causal, m, ws):
+def _bwd_args(q, k, v, o, lse, do, dq, dk, dv, scale, causal, m, ws, drop=None):
     B, H, Hkv, N, d = _shape(q, k, v)
-    return [_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
-            B, H, Hkv, N, d, scale, int(bool(causal)), _ptr(m), _DTYPES[q.dtype], _ptr(ws),
-            ws.numel(), _stream(q.device)]
+    head = [_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+            B, H, Hkv, N, d, scale, int(bool(causal)), _ptr(m), _DTYPES[q.dtype]]
+    mid = [] if drop is None else [float(drop[0]), int(drop[1]) & (2**64 - 1)]
+    return head + mid + [_ptr(ws), ws.numel(), _stream(q.device)]
 
 
-def backward(q, k, v, o, lse, do, scale=None, causal=False, block_mask=None, ws=None, grads=None):
-    """dq, dk, dv of sum(O * do), recomputing P from q, k and lse."""
+def backward(q, k, v, o, lse, do, scale=None, causal=False, block_mask=None, ws=None, grads=None,
+             dropout_rate=0.0, seed=0):
+    """dq, dk, dv of sum(O * do), recomputing P from q, k and lse (and, with a
+    positive dropout_rate, the forward call's keep decisions from seed)."""
     B, H, Hkv, N, d = _shape(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     for name, t in (("o", o), ("do", do)):
@@ -137,17 +157,29 @@ def backward(q, k, v, o, lse, do, scale=None, causal=False, block_mask=None, ws=
     m = _mask(block_mask, N, q.device)
     ws = workspace(q, k) if ws is None else ws
     dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
-    st = load().fa_backward(*_bwd_args(q, k, v, o, lse, do, dq, dk, dv, scale, causal, m, ws))
+    if dropout_rate:
+        st = load().fa_backward_dropout(*_bwd_args(q, k, v, o, lse, do, dq, dk, dv, scale, causal, m, ws,
+                                                   (dropout_rate, seed)))
+        where = "fa_backward_dropout"
+    else:
+        st = load().fa_backward(*_bwd_args(q, k, v, o, lse, do, dq, dk, dv, scale, causal, m, ws))
+        where = "fa_backward"
     if st != 0:
-        raise FAError(st, "fa_backward")
+        raise FAError(st, where)
     return dq, dk, dv
 
 
-def backward_stage(stage, q, k, v, o, lse, do, dq, dk, dv, ws, scale=None, causal=False, block_mask=None):
+def backward_stage(stage, q, k, v, o, lse, do, dq, dk, dv, ws, scale=None, causal=False, block_mask=None,
+                   dropout_rate=0.0, seed=0):
     """Run one stage (0, 1 or 2) of the backward pass; see fa_backward_stage."""
     d = q.shape[3]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     m = _mask(block_mask, q.shape[2], q.device)
-    st = load().fa_backward_stage(int(stage), *_bwd_args(q, k, v, o, lse, do, dq, dk, dv, scale, causal, m, ws))
+    if dropout_rate:
+        st = load().fa_backward_stage_dropout(int(stage), *_bwd_args(q, k, v, o, lse, do, dq, dk, dv, scale,
+                                                                     causal, m, ws, (dropout_rate, seed)))
+    else:
+        st = load().fa_backward_stage(int(stage), *_bwd_args(q, k, v, o, lse, do, dq, dk, dv, scale, causal,
+                                                             m, ws))
     if st != 0:
         raise FAError(st, f"fa_backward_stage({stage})")

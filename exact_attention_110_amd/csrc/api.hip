@@ -44,7 +44,24 @@ fa::AttnShape make_shape(int B, int H, int Hkv, int N, int d, float scale, int c
   s.causal = causal != 0;
   s.mask = mask;
   s.nb = (N + 127) / 128;
+  s.drop_t = 0;
+  s.drop_scale = 1.f;
+  s.seed0 = s.seed1 = 0;
   return s;
+}
+
+// Dropout rate -> byte threshold t = round(256 rate), at most 255 (keep
+// probability (256 - t) / 256, kept values scaled by 256 / (256 - t)).
+// Returns false for a rate outside [0, 1) or not finite.
+bool set_dropout(fa::AttnShape& s, float rate, unsigned long long seed) {
+  if (!(rate >= 0.f && rate < 1.f)) return false;  // also rejects NaN
+  int t = (int)floorf(rate * 256.f + 0.5f);
+  if (t > 255) t = 255;
+  s.drop_t = t;
+  s.drop_scale = 256.f / (float)(256 - t);
+  s.seed0 = (unsigned int)(seed & 0xffffffffull);
+  s.seed1 = (unsigned int)(seed >> 32);
+  return true;
 }
 
 // Block masks are compacted per row / column in LDS lists of 2048 entries.
@@ -75,13 +92,9 @@ int check_backward(const void* q, const void* k, const void* v, const void* o, c
   return FA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-               int Hkv, int N, int d, float scale, int causal, const uint8_t* block_mask,
-               int dtype, void* stream) {
+int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int Hkv, int N, int d, float scale, int causal, const uint8_t* block_mask, int dtype,
+                 float rate, unsigned long long seed, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u))
     return FA_ERR_INVALID_ARG;
@@ -90,6 +103,8 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
   if (block_mask && (N + 127) / 128 > kMaxMaskBlocks) return FA_ERR_UNSUPPORTED;
   fa::FwdArgs a;
   a.s = make_shape(B, H, Hkv, N, d, scale, causal, block_mask);
+  if (!set_dropout(a.s, rate, seed)) return FA_ERR_INVALID_ARG;
+  if (a.s.drop_t > 0 && dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -99,23 +114,17 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
   return fa::launch_forward(a, dtype, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-size_t fa_backward_workspace_size(int B, int H, int Hkv, int N, int d, int dtype) {
-  if (check_shape(B, H, Hkv, N, d, 1.0f, dtype) != FA_OK || dtype == FA_F32) return 0;
-  (void)d;
-  if ((long long)B * H * 2 * stats_rows(N) > INT32_MAX) return 0;
-  return stats_bytes(B, H, N);
-}
-
-int fa_backward_stage(int stage, const void* q, const void* k, const void* v, const void* o,
-                      const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H,
-                      int Hkv, int N, int d, float scale, int causal, const uint8_t* block_mask,
-                      int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+int stage_impl(int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
+               float scale, int causal, const uint8_t* block_mask, int dtype, float rate,
+               unsigned long long seed, void* workspace, size_t workspace_bytes, void* stream) {
   if (stage < 0 || stage > 2) return FA_ERR_INVALID_ARG;
   int st = check_backward(q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, N, d, scale, block_mask,
                           dtype, workspace, workspace_bytes);
   if (st != FA_OK) return st;
   fa::BwdArgs a;
   a.s = make_shape(B, H, Hkv, N, d, scale, causal, block_mask);
+  if (!set_dropout(a.s, rate, seed)) return FA_ERR_INVALID_ARG;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -132,16 +141,78 @@ int fa_backward_stage(int stage, const void* q, const void* k, const void* v, co
                                                                                         : FA_ERR_HIP;
 }
 
+int backward_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
+                  float scale, int causal, const uint8_t* block_mask, int dtype, float rate,
+                  unsigned long long seed, void* workspace, size_t workspace_bytes, void* stream) {
+  for (int stage = 0; stage < 3; ++stage) {
+    int st = stage_impl(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, N, d, scale, causal,
+                        block_mask, dtype, rate, seed, workspace, workspace_bytes, stream);
+    if (st != FA_OK) return st;
+  }
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_backward_workspace_size(int B, int H, int Hkv, int N, int d, int dtype) {
+  if (check_shape(B, H, Hkv, N, d, 1.0f, dtype) != FA_OK || dtype == FA_F32) return 0;
+  (void)d;
+  if ((long long)B * H * 2 * stats_rows(N) > INT32_MAX) return 0;
+  return stats_bytes(B, H, N);
+}
+
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int Hkv, int N, int d, float scale, int causal, const uint8_t* block_mask,
+               int dtype, void* stream) {
+  return forward_impl(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, block_mask, dtype, 0.f, 0ull,
+                      stream);
+}
+
+int fa_forward_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                       int H, int Hkv, int N, int d, float scale, int causal,
+                       const uint8_t* block_mask, int dtype, float dropout_rate,
+                       unsigned long long seed, void* stream) {
+  return forward_impl(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, block_mask, dtype,
+                      dropout_rate, seed, stream);
+}
+
+int fa_backward_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H,
+                      int Hkv, int N, int d, float scale, int causal, const uint8_t* block_mask,
+                      int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return stage_impl(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, N, d, scale, causal,
+                    block_mask, dtype, 0.f, 0ull, workspace, workspace_bytes, stream);
+}
+
+int fa_backward_stage_dropout(int stage, const void* q, const void* k, const void* v,
+                              const void* o, const float* lse, const void* dO, void* dq, void* dk,
+                              void* dv, int B, int H, int Hkv, int N, int d, float scale,
+                              int causal, const uint8_t* block_mask, int dtype,
+                              float dropout_rate, unsigned long long seed, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return stage_impl(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, N, d, scale, causal,
+                    block_mask, dtype, dropout_rate, seed, workspace, workspace_bytes, stream);
+}
+
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const float* lse,
                 const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
                 float scale, int causal, const uint8_t* block_mask, int dtype, void* workspace,
                 size_t workspace_bytes, void* stream) {
-  for (int stage = 0; stage < 3; ++stage) {
-    int st = fa_backward_stage(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, N, d, scale,
-                               causal, block_mask, dtype, workspace, workspace_bytes, stream);
-    if (st != FA_OK) return st;
-  }
-  return FA_OK;
+  return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, N, d, scale, causal, block_mask,
+                       dtype, 0.f, 0ull, workspace, workspace_bytes, stream);
+}
+
+int fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dO, void* dq, void* dk, void* dv, int B,
+                        int H, int Hkv, int N, int d, float scale, int causal,
+                        const uint8_t* block_mask, int dtype, float dropout_rate,
+                        unsigned long long seed, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, N, d, scale, causal, block_mask,
+                       dtype, dropout_rate, seed, workspace, workspace_bytes, stream);
 }
 
 const char* fa_status_string(int status) {
@@ -155,6 +226,6 @@ const char* fa_status_string(int status) {
   }
 }
 
-int fa_version(void) { return 100; }
+int fa_version(void) { return 101; }
 
 }  // extern "C"

@@ -89,11 +89,12 @@ static_assert(KV_BKV == 128, "a key-block workgroup must cover exactly one mask 
 // query head's element offset in Q / dO and float offset in the statistics
 struct StepPos {
   int qi;
+  int hb;  // query head b * H + h
   int soff;
   unsigned long long qoff;
 };
 
-template <class T, int D, bool CAUSAL, bool MASK>
+template <class T, int D, bool CAUSAL, bool MASK, bool DROP>
 __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
   constexpr int BQ = KV_BQ;
   constexpr int QBUF = BQ * 2 * D;       // one Q or dO block, swizzled rows without padding
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
   const int nsteps = nq * s.G;
   auto advance = [&](StepPos p) -> StepPos {
     const bool next_head = p.qi + 1 >= nq;
-    return StepPos{next_head ? 0 : p.qi + 1, next_head ? p.soff + 2 * a.npad : p.soff,
+    return StepPos{next_head ? 0 : p.qi + 1, next_head ? p.hb + 1 : p.hb, next_head ? p.soff + 2 * a.npad : p.soff,
                    next_head ? p.qoff + (unsigned long long)N * D : p.qoff};
   };
 
@@ -227,7 +228,9 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
   // i is query q0 + 8 (i / 4) + 4 hh + i % 4 of key kj; under causal masking it
   // is kept only if 8 (i / 4) + i % 4 >= kj - q0 - 4 hh. Keys past N need no
   // mask: their K and V rows read as zeros and nothing of theirs is stored.
-  auto probs = [&](auto masked, const f32x16& sc, const f32x16& dp, int q0, int stb, unsigned int (&pk)[8],
+  // With dropout (z the keep decision, c its scale): P V uses z c P, and
+  // dS = P (z c dP - D), the gradient flowing to P through the dropped values.
+  auto probs = [&](auto masked, const f32x16& sc, const f32x16& dp, int q0, int stb, int bh, unsigned int (&pk)[8],
                    unsigned int (&sk)[8]) {
     constexpr bool MASKED = decltype(masked)::value;
     const __attribute__((address_space(3))) float* lsel =
@@ -239,13 +242,23 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
       const f32x4 L4 = *(const __attribute__((address_space(3))) f32x4*)(lsel + 8 * j4 + 4 * hh);
       const f32x4 D4 = *(const __attribute__((address_space(3))) f32x4*)(ddl + 8 * j4 + 4 * hh);
       float p[4], d2[4];
+      Philox4 rnd;
+      if constexpr (DROP)  // queries q0 + 8 j4 + 4 hh + 0..3 of key kj: one call, byte kj & 3 of each word
+        rnd = philox4x32_10((unsigned)(q0 + 8 * j4 + 4 * hh) >> 2, (unsigned)kj >> 2, (unsigned)bh, 0u, s.seed0,
+                            s.seed1);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * j4 + r;
         float pv = fast_exp2(fmaf(sc[i], c, -L4[r]));
         if constexpr (MASKED) pv = (8 * j4 + r < thr) ? 0.f : pv;
-        p[r] = pv;
-        d2[r] = pv * (dp[i] - D4[r]);
+        if constexpr (DROP) {
+          const bool z = drop_keep(rnd.v[r], kj & 3, s.drop_t);
+          p[r] = z ? pv * s.drop_scale : 0.f;
+          d2[r] = pv * ((z ? dp[i] * s.drop_scale : 0.f) - D4[r]);
+        } else {
+          p[r] = pv;
+          d2[r] = pv * (dp[i] - D4[r]);
+        }
       }
       pk[2 * j4] = pack2<T>(p[0], p[1]);
       pk[2 * j4 + 1] = pack2<T>(p[2], p[3]);
@@ -288,7 +301,7 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
     lds_write16((t ? obuf : qbuf) + (NB - 1) * QBUF + off, (s16x8){0, 0, 0, 0, 0, 0, 0, 0});
   }
   const int hb0 = b * s.H + hk * s.G;  // first query head of the group, batch included
-  StepPos cur{0, hb0 * 2 * a.npad, (unsigned long long)hb0 * N * D};
+  StepPos cur{0, hb0, hb0 * 2 * a.npad, (unsigned long long)hb0 * N * D};
   StepPos nxt = nsteps > 1 ? advance(cur) : cur;
   dma_q(cur, 0);
   dma_q(nxt, 1);
@@ -302,7 +315,7 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
     const StepPos nn = e + 2 < nsteps ? advance(nxt) : nxt;
     dma_q(nn, (e + 2) & (NB - 1));
     sdp((e + 1) & (NB - 1), scn, dpn);
-    probs(masked, sc, dp, qblock_at(cur.qi) * BQ, e & (NB - 1), pkn, skn);
+    probs(masked, sc, dp, qblock_at(cur.qi) * BQ, e & (NB - 1), cur.hb, pkn, skn);
     dvdk((e + NB - 1) & (NB - 1), pk, sk);
     dma_wait();
     __syncthreads();
@@ -385,7 +398,7 @@ constexpr int Q_T2 = Q_BN / 32;      // 32-key halves per tile
 constexpr int Q_R = 128 / Q_BN;      // tiles per 128-key mask block
 static_assert(Q_BM == 128, "a query-block workgroup must cover exactly one mask block row");
 
-template <class T, int D, bool CAUSAL, bool MASK>
+template <class T, int D, bool CAUSAL, bool MASK, bool DROP>
 __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
   constexpr int KBUF = Q_BN * 2 * D;     // K tile: swizzled rows, row reads and transposing reads
   constexpr int VBUF = Q_BN * 2 * D;     // V tile: swizzled rows, row reads
@@ -519,12 +532,18 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             float v2[2];
+            unsigned int wd = 0;
+            if constexpr (DROP)  // keys ks + 32 t2 + 8 (j / 2) + 4 hh + 0..3 of row qi
+              wd = drop_row_word(s.seed0, s.seed1, b * s.H + h, qi, ks + 32 * t2 + 8 * (j >> 1) + 4 * hh);
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
               const int i = 2 * j + r;
               float pv = fast_exp2(fmaf(sc[t2][i], c, -lse2));
               if constexpr (MASKED) pv = (32 * t2 + 8 * (i >> 2) + (i & 3) > thr) ? 0.f : pv;
-              v2[r] = pv * (dp[t2][i] - dd);
+              if constexpr (DROP)
+                v2[r] = pv * ((drop_keep(wd, i & 3, s.drop_t) ? dp[t2][i] * s.drop_scale : 0.f) - dd);
+              else
+                v2[r] = pv * (dp[t2][i] - dd);
             }
             sk[t2][j] = pack2<T>(v2[0], v2[1]);
           }
@@ -577,28 +596,38 @@ static hipError_t launch_pre_t(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <class T, int D>
-static hipError_t launch_kv_t(const BwdArgs& a, hipStream_t st) {
+template <class T, int D, bool DROP>
+static hipError_t launch_kv_t2(const BwdArgs& a, hipStream_t st) {
   const dim3 grid(a.s.Hkv, (a.s.N + KV_BKV - 1) / KV_BKV, a.s.B);
   const dim3 block(KV_NW * 64);
   const bool causal = a.s.causal != 0, mask = a.s.mask != nullptr;
-  if (causal && mask) hipLaunchKernelGGL((bwd_kv_kernel<T, D, true, true>), grid, block, 0, st, a);
-  else if (causal) hipLaunchKernelGGL((bwd_kv_kernel<T, D, true, false>), grid, block, 0, st, a);
-  else if (mask) hipLaunchKernelGGL((bwd_kv_kernel<T, D, false, true>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((bwd_kv_kernel<T, D, false, false>), grid, block, 0, st, a);
+  if (causal && mask) hipLaunchKernelGGL((bwd_kv_kernel<T, D, true, true, DROP>), grid, block, 0, st, a);
+  else if (causal) hipLaunchKernelGGL((bwd_kv_kernel<T, D, true, false, DROP>), grid, block, 0, st, a);
+  else if (mask) hipLaunchKernelGGL((bwd_kv_kernel<T, D, false, true, DROP>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((bwd_kv_kernel<T, D, false, false, DROP>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+template <class T, int D>
+static hipError_t launch_kv_t(const BwdArgs& a, hipStream_t st) {
+  return a.s.drop_t > 0 ? launch_kv_t2<T, D, true>(a, st) : launch_kv_t2<T, D, false>(a, st);
+}
+
+template <class T, int D, bool DROP>
+static hipError_t launch_q_t2(const BwdArgs& a, hipStream_t st) {
+  const dim3 grid(a.s.H, (a.s.N + Q_BM - 1) / Q_BM, a.s.B);
+  const dim3 block(Q_NW * 64);
+  const bool causal = a.s.causal != 0, mask = a.s.mask != nullptr;
+  if (causal && mask) hipLaunchKernelGGL((bwd_q_kernel<T, D, true, true, DROP>), grid, block, 0, st, a);
+  else if (causal) hipLaunchKernelGGL((bwd_q_kernel<T, D, true, false, DROP>), grid, block, 0, st, a);
+  else if (mask) hipLaunchKernelGGL((bwd_q_kernel<T, D, false, true, DROP>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((bwd_q_kernel<T, D, false, false, DROP>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
 template <class T, int D>
 static hipError_t launch_q_t(const BwdArgs& a, hipStream_t st) {
-  const dim3 grid(a.s.H, (a.s.N + Q_BM - 1) / Q_BM, a.s.B);
-  const dim3 block(Q_NW * 64);
-  const bool causal = a.s.causal != 0, mask = a.s.mask != nullptr;
-  if (causal && mask) hipLaunchKernelGGL((bwd_q_kernel<T, D, true, true>), grid, block, 0, st, a);
-  else if (causal) hipLaunchKernelGGL((bwd_q_kernel<T, D, true, false>), grid, block, 0, st, a);
-  else if (mask) hipLaunchKernelGGL((bwd_q_kernel<T, D, false, true>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((bwd_q_kernel<T, D, false, false>), grid, block, 0, st, a);
-  return hipGetLastError();
+  return a.s.drop_t > 0 ? launch_q_t2<T, D, true>(a, st) : launch_q_t2<T, D, false>(a, st);
 }
 
 template <class T, int D>

@@ -151,6 +151,44 @@ __device__ __forceinline__ void batomic_add(rsrc_t r, unsigned int off, float v)
 }
 
 // ---------------------------------------------------------------------------
+// Dropout keep decisions: Philox4x32-10 (Salmon, Moraes, Dror and Shaw,
+// "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11), a counter-based
+// generator, so that the forward and backward passes draw the same bits for an
+// element without storing a mask. Element (query i, key j) of query head
+// bh = b * H + h uses counter (i >> 2, j >> 2, bh, 0) under the call's 64-bit
+// key, word i & 3 and byte j & 3 of the output: one call decides a 4 x 4 block,
+// so four consecutive keys of a row, or four consecutive queries of a column,
+// come from one call.
+struct Philox4 {
+  unsigned int v[4];
+};
+__device__ __forceinline__ Philox4 philox4x32_10(unsigned int c0, unsigned int c1, unsigned int c2,
+                                                 unsigned int c3, unsigned int k0, unsigned int k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const unsigned int lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const unsigned int lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;  // key schedule between rounds
+    k1 += 0xBB67AE85u;
+  }
+  return {{c0, c1, c2, c3}};
+}
+// The word holding keys kg .. kg + 3 (kg a multiple of 4) of query row qi.
+__device__ __forceinline__ unsigned int drop_row_word(unsigned int k0, unsigned int k1, int bh, int qi, int kg) {
+  const Philox4 r = philox4x32_10((unsigned)qi >> 2, (unsigned)kg >> 2, (unsigned)bh, 0u, k0, k1);
+  const int w = qi & 3;
+  return w == 0 ? r.v[0] : w == 1 ? r.v[1] : w == 2 ? r.v[2] : r.v[3];
+}
+// keep decision of byte t (0..3) of a word
+__device__ __forceinline__ bool drop_keep(unsigned int word, int t, int thr) {
+  return ((word >> (8 * t)) & 0xffu) >= (unsigned)thr;
+}
+
+// ---------------------------------------------------------------------------
 // Tiles staged by LDS DMA (buffer_load ... lds): one wave instruction copies
 // 64 x 16 bytes from per-lane global offsets into 1024 contiguous LDS bytes
 // (lane L at M0 + 16 L); out-of-range lanes deposit zeros. Rows therefore have

@@ -44,7 +44,7 @@ constexpr int FWD_BN = 64;            // keys per tile
 constexpr int FWD_LIST = 2048;        // capacity of the compacted mask-block list
 static_assert(FWD_BM == 128, "a forward workgroup must cover exactly one mask block row");
 
-template <class T, int D, bool CAUSAL, bool MASK>
+template <class T, int D, bool CAUSAL, bool MASK, bool DROP>
 __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
   constexpr int KP = D * 2 + 16;  // K row pitch in LDS, bytes (16 mod 128: conflict-free 16-byte reads)
   constexpr int VP = D * 2 + 32;  // V row pitch in LDS, bytes (32 mod 128: conflict-free transposing reads)
@@ -225,8 +225,17 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
         for (int j = 0; j < 8; ++j) {
           const float p0 = fast_exp2(fmaf(sc[t2][2 * j], c, -m_use));
           const float p1 = fast_exp2(fmaf(sc[t2][2 * j + 1], c, -m_use));
-          l += p0 + p1;
-          pk[t2][j] = pack2<T>(p0, p1);
+          l += p0 + p1;  // the normaliser sums the probabilities before dropout
+          if constexpr (DROP) {
+            // elements 2j, 2j + 1 are keys kg + (2j & 3) + 0, 1 of group kg
+            const unsigned int wd =
+                drop_row_word(s.seed0, s.seed1, b * s.H + h, qi, ks + 32 * t2 + 8 * (j >> 1) + 4 * hh);
+            const int t0 = (2 * j) & 3;
+            pk[t2][j] = pack2<T>(drop_keep(wd, t0, s.drop_t) ? p0 * s.drop_scale : 0.f,
+                                 drop_keep(wd, t0 + 1, s.drop_t) ? p1 * s.drop_scale : 0.f);
+          } else {
+            pk[t2][j] = pack2<T>(p0, p1);
+          }
         }
       // O^T(d x q) += V^T(d x key) P^T(key x q); B operand k-slot j of step (t2, u)
       // is key 32 t2 + 16 u + 8 (j / 4) + 4 hh + j % 4, matched by the V^T reads
@@ -305,7 +314,7 @@ constexpr int F64_BM = F64_NW * F64_RW;   // query rows per workgroup
 constexpr int F64_BN = 32;                // keys per tile
 constexpr int F64_NB = 4;                 // LDS ring slots
 
-template <class T, int D, bool CAUSAL>
+template <class T, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
   constexpr int KP = D * 2 + 16;  // K row pitch (bytes): conflict-free 16-byte row reads
   constexpr int VP = D * 2 + 32;  // V row pitch (bytes): conflict-free transposing reads
@@ -427,7 +436,20 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
   // Softmax of one tile against the running reference: returns whether the
   // reference rises (wave-uniform), with the new reference in mn, the 16-bit
   // probabilities in pk and this lane's share of their row sums in ls.
-  auto softmax = [&](const f32x16 (&st)[2], float (&mn)[2], unsigned int (&pk)[2][8], float (&ls)[2]) {
+  // 16-bit probabilities of elements 2 jj, 2 jj + 1 of row block rb, with dropout
+  // when built for it (keys ks + 8 (jj / 2) + 4 hh + (2 jj & 3) + 0, 1)
+  auto pack_p = [&](float p0, float p1, int rb, int jj, int ks) -> unsigned int {
+    if constexpr (DROP) {
+      const unsigned int wd =
+          drop_row_word(s.seed0, s.seed1, b * s.H + h, qw + 32 * rb + l32, ks + 8 * (jj >> 1) + 4 * hh);
+      const int t0 = (2 * jj) & 3;
+      return pack2<T>(drop_keep(wd, t0, s.drop_t) ? p0 * s.drop_scale : 0.f,
+                      drop_keep(wd, t0 + 1, s.drop_t) ? p1 * s.drop_scale : 0.f);
+    } else {
+      return pack2<T>(p0, p1);
+    }
+  };
+  auto softmax = [&](const f32x16 (&st)[2], float (&mn)[2], unsigned int (&pk)[2][8], float (&ls)[2], int ks) {
     float mx[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
@@ -447,7 +469,7 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
         const float p0 = fast_exp2(fmaf(st[rb][2 * j], c, -mu));
         const float p1 = fast_exp2(fmaf(st[rb][2 * j + 1], c, -mu));
         sum += p0 + p1;
-        pk[rb][j] = pack2<T>(p0, p1);
+        pk[rb][j] = pack_p(p0, p1, rb, j, ks);
       }
       ls[rb] = sum;
     }
@@ -492,7 +514,7 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
   // raises the reference as it goes.
   int j = 0;
   if (nfull > 0) {
-    auto probs = [&](const f32x16 (&st)[2], unsigned int (&pk)[2][8]) {
+    auto probs = [&](const f32x16 (&st)[2], unsigned int (&pk)[2][8], int ks) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         float sum = 0.f;
@@ -501,7 +523,7 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
           const float p0 = fast_exp2(fmaf(st[rb][2 * jj], c, -m[rb]));
           const float p1 = fast_exp2(fmaf(st[rb][2 * jj + 1], c, -m[rb]));
           sum += p0 + p1;
-          pk[rb][jj] = pack2<T>(p0, p1);
+          pk[rb][jj] = pack_p(p0, p1, rb, jj, ks);
         }
         l[rb] += sum;
       }
@@ -514,7 +536,7 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
                     unsigned int (&pcur)[2][8]) {
       gload(min(jj + 2, ntiles - 1));
       s_tile((jj + 1) & (F64_NB - 1), snext);
-      probs(scur, pcur);
+      probs(scur, pcur, jj * F64_BN);
       pv_tile((jj + F64_NB - 1) & (F64_NB - 1), pprev);
       lstore((jj + 2) & (F64_NB - 1));
       __syncthreads();
@@ -582,7 +604,7 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
       }
       float mn[2], ls[2];
       unsigned int pt[2][8];
-      const bool resc = softmax(st, mn, pt, ls);
+      const bool resc = softmax(st, mn, pt, ls, ks);
       update(resc, mn, ls);
       pv_tile(j & (F64_NB - 1), pt);
     }
@@ -729,6 +751,23 @@ __global__ __launch_bounds__(F32_R * F32_S) void fwd_f32_kernel(FwdArgs a) {
   }
 }
 
+template <class T, int D, bool DROP>
+static hipError_t launch_fwd_t2(const FwdArgs& a, hipStream_t st, bool causal, bool mask, bool use64) {
+  if (!mask && use64) {
+    const dim3 grid(a.s.H, (a.s.N + F64_BM - 1) / F64_BM, a.s.B);
+    if (causal) hipLaunchKernelGGL((fwd64_kernel<T, D, true, DROP>), grid, dim3(F64_NW * 64), 0, st, a);
+    else hipLaunchKernelGGL((fwd64_kernel<T, D, false, DROP>), grid, dim3(F64_NW * 64), 0, st, a);
+    return hipGetLastError();
+  }
+  const dim3 grid(a.s.H, (a.s.N + FWD_BM - 1) / FWD_BM, a.s.B);
+  const dim3 block(FWD_NW * 64);
+  if (causal && mask) hipLaunchKernelGGL((fwd_kernel<T, D, true, true, DROP>), grid, block, 0, st, a);
+  else if (causal) hipLaunchKernelGGL((fwd_kernel<T, D, true, false, DROP>), grid, block, 0, st, a);
+  else if (mask) hipLaunchKernelGGL((fwd_kernel<T, D, false, true, DROP>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((fwd_kernel<T, D, false, false, DROP>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
 template <class T, int D>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   const bool causal = a.s.causal != 0, mask = a.s.mask != nullptr;
@@ -745,19 +784,8 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
     if (env[0] == '6' && env[1] == '4' && env[2] == 0) use64 = true;
     if (env[0] == '3' && env[1] == '2' && env[2] == 0) use64 = false;
   }
-  if (!mask && use64) {
-    const dim3 grid(a.s.H, (a.s.N + F64_BM - 1) / F64_BM, a.s.B);
-    if (causal) hipLaunchKernelGGL((fwd64_kernel<T, D, true>), grid, dim3(F64_NW * 64), 0, st, a);
-    else hipLaunchKernelGGL((fwd64_kernel<T, D, false>), grid, dim3(F64_NW * 64), 0, st, a);
-    return hipGetLastError();
-  }
-  const dim3 grid(a.s.H, (a.s.N + FWD_BM - 1) / FWD_BM, a.s.B);
-  const dim3 block(FWD_NW * 64);
-  if (causal && mask) hipLaunchKernelGGL((fwd_kernel<T, D, true, true>), grid, block, 0, st, a);
-  else if (causal) hipLaunchKernelGGL((fwd_kernel<T, D, true, false>), grid, block, 0, st, a);
-  else if (mask) hipLaunchKernelGGL((fwd_kernel<T, D, false, true>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((fwd_kernel<T, D, false, false>), grid, block, 0, st, a);
-  return hipGetLastError();
+  if (a.s.drop_t > 0) return launch_fwd_t2<T, D, true>(a, st, causal, mask, use64);
+  return launch_fwd_t2<T, D, false>(a, st, causal, mask, use64);
 }
 
 template <int D>

@@ -15,6 +15,13 @@ struct AttnShape {
   int causal;     // key j visible to query i only if j <= i
   const uint8_t* mask;  // NULL or uint8 [nb][nb], nb = ceil(N / 128)
   int nb;         // ceil(N / 128)
+  // dropout on the probabilities (used only by the kernels built for it): an
+  // element is kept iff its generator byte >= drop_t, and kept values are
+  // multiplied by drop_scale = 256 / (256 - drop_t); the generator key is
+  // (seed0, seed1)
+  int drop_t;
+  float drop_scale;
+  unsigned int seed0, seed1;
 };
 
 struct FwdArgs {

@@ -136,6 +136,44 @@ int fa_backward_stage(int stage, const void* q, const void* k, const void* v, co
                       const uint8_t* block_mask, int dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Dropout on the attention probabilities, fused into the same kernels
+ * (chipfoundryservices.com glossary "flash attention algorithm", "Kernel
+ * Fusion", lists dropout among the operations fused into one kernel; the
+ * pages do not define it, so the usual reading is taken): after the row
+ * softmax each probability is kept with probability (256 - t) / 256 and then
+ * multiplied by 256 / (256 - t), or set to 0, where t = round(256 *
+ * dropout_rate), at most 255 (the rate is quantised to multiples of 1/256).
+ * lse is still the log-sum-exp of the scaled scores before dropout. The keep
+ * decision of element (query i, key j) of query head h of batch b is byte
+ * j & 3 of word i & 3 of Philox4x32-10 (Salmon et al., SC'11) at counter
+ * (i >> 2, j >> 2, b * H + h, 0) under key (seed & 0xffffffff, seed >> 32),
+ * kept iff that byte >= t: the forward and backward calls with the same seed
+ * and rate draw the same decisions, and nothing is stored.
+ *   dropout_rate    in [0, 1); a rate that rounds to t = 0 is no dropout
+ *   seed            64-bit generator key
+ * Other arguments, layouts, ownership and errors as for fa_forward /
+ * fa_backward / fa_backward_stage, plus FA_ERR_INVALID_ARG for a rate outside
+ * [0, 1) and FA_ERR_UNSUPPORTED for FA_F32 with dropout (t > 0).
+ */
+int fa_forward_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int Hkv, int N, int d, float scale, int causal,
+                       const uint8_t* block_mask, int dtype,
+                       float dropout_rate, unsigned long long seed, void* stream);
+int fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                        int B, int H, int Hkv, int N, int d, float scale, int causal,
+                        const uint8_t* block_mask, int dtype,
+                        float dropout_rate, unsigned long long seed,
+                        void* workspace, size_t workspace_bytes, void* stream);
+int fa_backward_stage_dropout(int stage, const void* q, const void* k, const void* v,
+                              const void* o, const float* lse, const void* dO,
+                              void* dq, void* dk, void* dv,
+                              int B, int H, int Hkv, int N, int d, float scale, int causal,
+                              const uint8_t* block_mask, int dtype,
+                              float dropout_rate, unsigned long long seed,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* fa_status_string: a static, human-readable description of a status code. */
 const char* fa_status_string(int status);
 

@@ -70,31 +70,39 @@ def check_grad(g, ref, where):
     return err
 
 
-def run_small(B, H, Hkv, N, d, dtype, causal, mask=None, seed=0, sigma=1.0, backward=True, scale=None):
+def run_small(B, H, Hkv, N, d, dtype, causal, mask=None, seed=0, sigma=1.0, backward=True, scale=None,
+              dropout_rate=0.0, drop_seed=0):
     """Full comparison (every output element) for a small seeded case."""
     where = f"B{B} H{H} Hkv{Hkv} N{N} d{d} {dtype} causal={causal} mask={mask is not None} seed={seed}"
+    if dropout_rate:
+        where += f" dropout={dropout_rate} drop_seed={drop_seed}"
     x = I.make_small(B, H, Hkv, N, d, dtype, seed, sigma, with_grad=backward)
-    return run_given(x, dtype, causal, mask, backward, scale, where)
+    return run_given(x, dtype, causal, mask, backward, scale, where, dropout_rate=dropout_rate,
+                     drop_seed=drop_seed)
 
 
-def run_given(x, dtype, causal, mask=None, backward=True, scale=None, where="", lse_tol=TOL_LSE):
-    """Full comparison (every output element) on given CPU tensors q, k, v (and do)."""
+def run_given(x, dtype, causal, mask=None, backward=True, scale=None, where="", lse_tol=TOL_LSE,
+              dropout_rate=0.0, drop_seed=0):
+    """Full comparison (every output element) on given CPU tensors q, k, v (and do);
+    with a positive dropout_rate both sides drop with the generator keyed by drop_seed."""
     say("case", where)
     d = x["q"].shape[-1]
     dev = torch.device("cuda", 0)
     q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     mt = None if mask is None else torch.from_numpy(mask).to(dev)
-    o, lse = binding.forward(q, k, v, scale, causal, mt)
+    o, lse = binding.forward(q, k, v, scale, causal, mt, dropout_rate=dropout_rate, seed=drop_seed)
     torch.cuda.synchronize()
     qd, kd, vd = (np64(x[n]) for n in ("q", "k", "v"))
-    oref, lref = oracle.forward(qd, kd, vd, scale, causal, mask)
+    oref, lref = oracle.forward(qd, kd, vd, scale, causal, mask, dropout_rate=dropout_rate, seed=drop_seed)
     res = {"o": check_out(np64(o), oref, dtype, where), "lse": check_lse(np64(lse), lref, where, lse_tol)}
     if backward and dtype != "fp32":
         do = x["do"].to(dev)
-        dq, dk, dv = binding.backward(q, k, v, o, lse, do, scale, causal, mt)
+        dq, dk, dv = binding.backward(q, k, v, o, lse, do, scale, causal, mt, dropout_rate=dropout_rate,
+                                      seed=drop_seed)
         torch.cuda.synchronize()
-        rq, rk, rv = oracle.backward(qd, kd, vd, np64(x["do"]), scale, causal, mask)
+        rq, rk, rv = oracle.backward(qd, kd, vd, np64(x["do"]), scale, causal, mask, dropout_rate=dropout_rate,
+                                     seed=drop_seed)
         res["dq"] = check_grad(np64(dq), rq, where + " dq")
         res["dk"] = check_grad(np64(dk), rk, where + " dk")
         res["dv"] = check_grad(np64(dv), rv, where + " dv")

@@ -47,7 +47,8 @@ def test_header_constants_match_binding():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"fa_forward", "fa_backward", "fa_backward_workspace_size", "fa_backward_stage",
-            "fa_status_string", "fa_version"} <= set(names)
+            "fa_status_string", "fa_version", "fa_forward_dropout", "fa_backward_dropout",
+            "fa_backward_stage_dropout"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -132,3 +133,32 @@ def test_backward_rejects(lib):
         assert bwd(lib, stage=st) == EINVAL
     assert bwd(lib, stage=1, ws=None) == EWS
     assert bwd(lib, stage=0, dtype=F32) == EUNSUP
+
+
+def fwd_drop(lib, rate, dtype=BF16, d=64, seed=7):
+    return lib.fa_forward_dropout(GOOD, GOOD, GOOD, GOOD, GOOD, 1, 2, 1, 256, d, 0.125, 1, None, dtype,
+                                  rate, seed, None)
+
+
+def bwd_drop(lib, rate, stage=None, dtype=BF16, seed=7):
+    ws_bytes = ws_size(lib) if dtype != F32 else 1 << 30
+    args = [GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 1, 2, 1, 256, 64, 0.125, 1, None, dtype,
+            rate, seed, GOOD, ws_bytes, None]
+    if stage is None:
+        return lib.fa_backward_dropout(*args)
+    return lib.fa_backward_stage_dropout(stage, *args)
+
+
+@pytest.mark.parametrize("rate", [-0.1, 1.0, 1.5, float("nan"), float("inf"), float("-inf")])
+def test_dropout_rate_rejected(lib, rate):
+    """A dropout rate outside [0, 1) is an invalid argument, before any launch."""
+    assert fwd_drop(lib, rate) == EINVAL
+    assert bwd_drop(lib, rate) == EINVAL
+    assert bwd_drop(lib, rate, stage=1) == EINVAL
+
+
+def test_dropout_argument_order(lib):
+    assert fwd_drop(lib, 0.5, dtype=F32) == EUNSUP     # no float32 dropout kernel
+    assert fwd_drop(lib, 0.5, d=16) == EINVAL          # bad shape reported first
+    assert bwd_drop(lib, 0.5, dtype=F32) == EUNSUP
+    assert bwd_drop(lib, 0.2, stage=3) == EINVAL

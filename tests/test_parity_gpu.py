@@ -103,6 +103,50 @@ def test_late_dominant_scores(dtype, causal, rows, monkeypatch):
     PT.run_given(x, dtype, causal, where=f"late dominant scores {dtype} causal={causal} rows={rows}", lse_tol=tol)
 
 
+DROP_SHAPES = [(1, 2, 1, 17, 32), (2, 2, 2, 64, 64), (1, 3, 1, 127, 128), (1, 4, 2, 300, 64),
+               (1, 2, 2, 513, 128)]
+
+
+@pytest.mark.parametrize("rows", ["64", "32"])
+@pytest.mark.parametrize("rate", [0.1, 0.5])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", DROP_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_dropout(shape, causal, rate, rows, monkeypatch):
+    """Dropout fused into every 16-bit kernel: O, LSE and gradients against the
+    oracle drawing the same Philox keep decisions (both forward kernels)."""
+    monkeypatch.setenv("FA_FORWARD_ROWS_PER_WAVE", rows)
+    B, H, Hkv, N, d = shape
+    dtype = "bf16" if N % 2 else "fp16"
+    PT.run_small(B, H, Hkv, N, d, dtype, causal, seed=7000 + N + d, dropout_rate=rate,
+                 drop_seed=(0x123456789 * (N + 1)) & (2**64 - 1))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_block_sparse(causal):
+    m = I.random_block_mask(700, 0.5, 3, keep_diagonal=True)
+    PT.run_small(1, 4, 2, 700, 64, "bf16", causal, mask=m, seed=31, dropout_rate=0.25, drop_seed=99)
+
+
+def test_dropout_seed_determinism(gpu_lib):
+    """Same seed, same result bit for bit; another seed, other decisions; a rate
+    that rounds to no dropout equals the plain kernels."""
+    x = I.make_small(1, 2, 2, 300, 64, "bf16", 41)
+    q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
+    o1, l1 = gpu_lib.forward(q, k, v, None, True, dropout_rate=0.3, seed=5)
+    o2, l2 = gpu_lib.forward(q, k, v, None, True, dropout_rate=0.3, seed=5)
+    o3, _ = gpu_lib.forward(q, k, v, None, True, dropout_rate=0.3, seed=6)
+    g1 = gpu_lib.backward(q, k, v, o1, l1, do, None, True, dropout_rate=0.3, seed=5)
+    g2 = gpu_lib.backward(q, k, v, o2, l2, do, None, True, dropout_rate=0.3, seed=5)
+    o0, l0 = gpu_lib.forward(q, k, v, None, True)
+    oz, lz = gpu_lib.forward(q, k, v, None, True, dropout_rate=0.001, seed=5)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert all(torch.equal(a, b) for a, b in zip(g1, g2))
+    assert not torch.equal(o1, o3)
+    assert torch.equal(l1, l0)                      # LSE is that of the undropped scores
+    assert torch.equal(oz, o0) and torch.equal(lz, l0)
+
+
 def test_scale_zero_is_uniform():
     PT.run_small(1, 2, 2, 200, 64, "bf16", True, seed=5, scale=0.0)
     PT.run_small(1, 1, 1, 150, 32, "fp32", False, seed=6, scale=0.0, backward=False)
