@@ -19,7 +19,15 @@ Sources (cited by page title and section):
   log-sum-exp of a row's scaled scores, so that P = exp(S - L).
 * Causal masking: the lesson's Beginner tier ("What was broken before") says a
   word attends to earlier words; read here as key j visible to query i iff
-  j <= i (self included).
+  j <= i (self included). With Nq queries over Nk keys the queries are read
+  as the last Nq positions of the sequence (the chipfoundryservices.com
+  glossary "flash attention algorithm", "Inference Optimization": attention
+  run beside a KV cache), so key j is visible to query i iff
+  j <= i + (Nk - Nq); rows with i + (Nk - Nq) < 0 see no key.
+* Variable-length batches: the same glossary, "Sequence Length Flexibility"
+  (arbitrary lengths, no padding). Read here as sequences packed one after
+  another per head, each attending only within itself
+  (``forward_varlen``, ``backward_varlen``).
 * Block-sparse masking: the nadeemcite summary, Key Method Details,
   "Block-sparse extension": a mask over blocks. Read here as a uint8 matrix of
   128 x 128 blocks, nonzero = keep, shared by every batch and head, combined
@@ -40,24 +48,24 @@ from . import dropout as _dropout
 MASK_BLOCK = 128  # block-mask granularity in rows and columns
 
 
-def visible(rows, keys, causal, block_mask, block=MASK_BLOCK):
+def visible(rows, keys, causal, block_mask, block=MASK_BLOCK, offset=0):
     """Boolean matrix a[r, c]: is key ``keys[c]`` visible to query ``rows[r]``.
 
-    Causal: j <= i. Block mask: mask[i // block][j // block] != 0. Both, when
-    given, must hold.
+    Causal: j <= i + offset (offset = Nk - Nq, 0 for square attention). Block
+    mask: mask[i // block][j // block] != 0. Both, when given, must hold.
     """
     rows = np.asarray(rows, dtype=np.int64)
     keys = np.asarray(keys, dtype=np.int64)
     a = np.ones((rows.size, keys.size), dtype=bool)
     if causal:
-        a &= keys[None, :] <= rows[:, None]
+        a &= keys[None, :] <= rows[:, None] + offset
     if block_mask is not None:
         bm = np.asarray(block_mask) != 0
         a &= bm[(rows // block)[:, None], (keys // block)[None, :]]
     return a
 
 
-def candidate_keys(rows, n_keys, causal, block_mask, block=MASK_BLOCK):
+def candidate_keys(rows, n_keys, causal, block_mask, block=MASK_BLOCK, offset=0):
     """Keys that at least one of ``rows`` may see (a superset used to gather K, V).
 
     Keys outside this set are invisible to every row of the chunk, so leaving
@@ -68,7 +76,7 @@ def candidate_keys(rows, n_keys, causal, block_mask, block=MASK_BLOCK):
     if rows.size == 0:
         return keys[:0]
     if causal:
-        keys = keys[keys <= rows.max()]
+        keys = keys[keys <= rows.max() + offset]
     if block_mask is not None:
         bm = np.asarray(block_mask) != 0
         any_row = bm[np.unique(rows // block)].any(axis=0)
@@ -103,14 +111,14 @@ def _row_softmax(q_rows, k_keys, scale, vis):
 
 
 def head_probabilities(q, k, scale, causal=False, block_mask=None, rows=None):
-    """Full probability rows P[rows, :] (N keys wide) of one query head.
+    """Full probability rows P[rows, :] (Nk keys wide) of one query head.
 
-    q: [N, d] float64 query rows of the head, k: [N, d] keys of its kv head.
+    q: [Nq, d] float64 query rows of the head, k: [Nk, d] keys of its kv head.
     """
     n = k.shape[0]
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
     keys = np.arange(n)
-    vis = visible(rows, keys, causal, block_mask)
+    vis = visible(rows, keys, causal, block_mask, offset=n - q.shape[0])
     _, p, lse = _row_softmax(q[rows], k, scale, vis)
     return p, lse
 
@@ -127,19 +135,20 @@ def _drop(p, rows, keys, dropout):
 
 
 def head_forward(q, k, v, scale, causal=False, block_mask=None, rows=None, chunk=256, dropout=None):
-    """O and L for the given query rows of one head (q: [N, d], k, v: [N, d]).
+    """O and L for the given query rows of one head (q: [Nq, d], k, v: [Nk, d]).
 
     With dropout = (rate, seed, bh) the probabilities are dropped and rescaled
     before they weight V; L is still that of the scores before dropout."""
     n = k.shape[0]
+    off = n - q.shape[0]
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
     o = np.zeros((rows.size, v.shape[1]))
     lse = np.full(rows.size, -np.inf)
     pos = 0
     for ch in _chunks(rows, chunk):
-        keys = candidate_keys(ch, n, causal, block_mask)
+        keys = candidate_keys(ch, n, causal, block_mask, offset=off)
         if keys.size:
-            vis = visible(ch, keys, causal, block_mask)
+            vis = visible(ch, keys, causal, block_mask, offset=off)
             _, p, l_ = _row_softmax(q[ch], k[keys], scale, vis)
             o[pos:pos + ch.size] = _drop(p, ch, keys, dropout) @ v[keys]
             lse[pos:pos + ch.size] = l_
@@ -159,19 +168,20 @@ def head_backward(q, k, v, do, scale, causal=False, block_mask=None, chunk=256, 
       dS_ij = p_ij (dP_ij - D_i)          (softmax Jacobian)
       dQ_i  = scale * sum_j dS_ij k_j
       dK_j += scale * sum_i dS_ij q_i
-    Returns dq [N, d] and this head's contributions dk, dv [N, d] to its kv
+    Returns dq [Nq, d] and this head's contributions dk, dv [Nk, d] to its kv
     head (callers sum them over a grouped-query group).
     """
     n = k.shape[0]
+    off = n - q.shape[0]
     rows = np.arange(q.shape[0], dtype=np.int64)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     for ch in _chunks(rows, chunk):
-        keys = candidate_keys(ch, n, causal, block_mask)
+        keys = candidate_keys(ch, n, causal, block_mask, offset=off)
         if keys.size == 0:
             continue
-        vis = visible(ch, keys, causal, block_mask)
+        vis = visible(ch, keys, causal, block_mask, offset=off)
         _, p, _ = _row_softmax(q[ch], k[keys], scale, vis)
         g = do[ch]
         dv[keys] += _drop(p, ch, keys, dropout).T @ g
@@ -191,15 +201,16 @@ def _heads(B, H, heads):
 
 def forward(q, k, v, scale, causal=False, block_mask=None, heads=None, rows=None, chunk=256,
             dropout_rate=0.0, seed=0):
-    """Attention forward over [B, H, N, d] queries and [B, Hkv, N, d] keys/values.
+    """Attention forward over [B, H, Nq, d] queries and [B, Hkv, Nk, d] keys/values.
 
-    Query head h reads kv head h // (H // Hkv). With ``heads=None`` returns full
-    o [B, H, R, d] and lse [B, H, R] (R = len(rows) or N); otherwise arrays
+    Query head h reads kv head h // (H // Hkv). A block mask has
+    ceil(Nq / 128) x ceil(Nk / 128) entries. With ``heads=None`` returns full
+    o [B, H, R, d] and lse [B, H, R] (R = len(rows) or Nq); otherwise arrays
     stacked in the order of ``heads`` (a list of (b, h)): o [nh, R, d], lse [nh, R].
     A positive ``dropout_rate`` applies dropout with the generator keyed by
     ``seed`` (``oracle.dropout``); query head (b, h) draws stream b * H + h.
     """
-    B, H, N, d = q.shape
+    B, H, _, d = q.shape
     Hkv = k.shape[1]
     if H % Hkv:
         raise ValueError("H must be a multiple of Hkv")
@@ -215,7 +226,7 @@ def forward(q, k, v, scale, causal=False, block_mask=None, heads=None, rows=None
     lse = np.stack(lses)
     if heads is None:
         R = o.shape[1]
-        return o.reshape(B, H, R, d), lse.reshape(B, H, R)
+        return o.reshape(B, H, R, o.shape[-1]), lse.reshape(B, H, R)
     return o, lse
 
 
@@ -223,12 +234,12 @@ def backward(q, k, v, do, scale, causal=False, block_mask=None, heads=None, chun
              dropout_rate=0.0, seed=0):
     """Gradients of sum(O * dO) with respect to q, k, v (dropout as in ``forward``).
 
-    With ``heads=None`` returns full dq [B, H, N, d], dk, dv [B, Hkv, N, d]
+    With ``heads=None`` returns full dq [B, H, Nq, d], dk, dv [B, Hkv, Nk, d]
     (dk, dv summed over each kv head's group of query heads). With a list of
-    (b, h) returns per-head arrays [nh, N, d]: dq and that query head's
-    contributions to dk and dv.
+    (b, h) returns per-head arrays: dq [nh, Nq, d] and that query head's
+    contributions to dk and dv [nh, Nk, d].
     """
-    B, H, N, d = q.shape
+    B, H, _, d = q.shape
     Hkv = k.shape[1]
     if H % Hkv:
         raise ValueError("H must be a multiple of Hkv")
@@ -250,3 +261,65 @@ def backward(q, k, v, do, scale, causal=False, block_mask=None, heads=None, chun
                          (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None)
            for b, h in _heads(B, H, heads)]
     return tuple(np.stack(x) for x in zip(*res))
+
+
+def _spans(cu, total):
+    cu = np.asarray(cu, dtype=np.int64)
+    if cu.ndim != 1 or cu.size < 2 or cu[0] != 0 or cu[-1] != total or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must rise from 0 to the packed length")
+    return [(int(a), int(b)) for a, b in zip(cu[:-1], cu[1:])]
+
+
+def forward_varlen(q, k, v, cu_q, cu_k, scale, causal=False, dropout_rate=0.0, seed=0):
+    """Attention over packed variable-length sequences.
+
+    q: [H, Tq, d], k, v: [Hkv, Tk, d]: per head, the rows of every sequence one
+    after another; sequence b holds query rows cu_q[b]:cu_q[b + 1] and keys
+    cu_k[b]:cu_k[b + 1]. Each sequence is an independent attention problem
+    (causal alignment as in ``visible``, with that sequence's own lengths);
+    with dropout, query head h of sequence b draws stream b * H + h, indexed by
+    row and key positions within the sequence. Returns o [H, Tq, d], lse [H, Tq].
+    """
+    H, Tq, d = q.shape
+    Hkv, Tk = k.shape[0], k.shape[1]
+    if H % Hkv:
+        raise ValueError("H must be a multiple of Hkv")
+    G = H // Hkv
+    qs, ks = _spans(cu_q, Tq), _spans(cu_k, Tk)
+    if len(qs) != len(ks):
+        raise ValueError("cu_seqlens_q and cu_seqlens_k name different batch sizes")
+    o = np.zeros((H, Tq, v.shape[2]))
+    lse = np.full((H, Tq), -np.inf)
+    for b, ((q0, q1), (k0, k1)) in enumerate(zip(qs, ks)):
+        if q1 == q0:
+            continue
+        for h in range(H):
+            dr = (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None
+            o[h, q0:q1], lse[h, q0:q1] = head_forward(q[h, q0:q1], k[h // G, k0:k1], v[h // G, k0:k1], scale,
+                                                      causal, None, None, 256, dr)
+    return o, lse
+
+
+def backward_varlen(q, k, v, do, cu_q, cu_k, scale, causal=False, dropout_rate=0.0, seed=0):
+    """Gradients of sum(O * dO) for ``forward_varlen``: dq [H, Tq, d],
+    dk, dv [Hkv, Tk, d] (summed over each kv head's group of query heads)."""
+    H, Tq, d = q.shape
+    Hkv, Tk = k.shape[0], k.shape[1]
+    if H % Hkv:
+        raise ValueError("H must be a multiple of Hkv")
+    G = H // Hkv
+    qs, ks = _spans(cu_q, Tq), _spans(cu_k, Tk)
+    if len(qs) != len(ks):
+        raise ValueError("cu_seqlens_q and cu_seqlens_k name different batch sizes")
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b, ((q0, q1), (k0, k1)) in enumerate(zip(qs, ks)):
+        for h in range(H):
+            dr = (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None
+            a, bk, bv = head_backward(q[h, q0:q1], k[h // G, k0:k1], v[h // G, k0:k1], do[h, q0:q1], scale,
+                                      causal, None, 256, dr)
+            dq[h, q0:q1] = a
+            dk[h // G, k0:k1] += bk
+            dv[h // G, k0:k1] += bv
+    return dq, dk, dv

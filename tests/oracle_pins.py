@@ -143,11 +143,19 @@ def pin_recurrence():
 # P-3: brute force with scalar loops on tiny inputs, and the two-key closed form
 # ----------------------------------------------------------------------------------------------
 def brute_force(q, k, v, scale, causal):
+    """Scalar loops. With fewer queries than keys the queries are the last
+    positions of the sequence: query i stands at position i + len(k) - len(q)
+    and, under causal masking, sees the keys at or before that position."""
     n, d = len(q), len(q[0])
     dv = len(v[0])
     outs, lses = [], []
     for i in range(n):
-        keys = [j for j in range(len(k)) if (not causal or j <= i)]
+        pos = i + len(k) - n
+        keys = [j for j in range(len(k)) if (not causal or j <= pos)]
+        if not keys:
+            outs.append([0.0] * dv)
+            lses.append(-math.inf)
+            continue
         sc = [scale * sum(q[i][t] * k[j][t] for t in range(d)) for j in keys]
         mx = max(sc)
         w = [math.exp(s - mx) for s in sc]
@@ -274,10 +282,11 @@ def pin_causal_locality():
 # ----------------------------------------------------------------------------------------------
 # P-9: analytic gradients against central finite differences of f = sum(O * dO)
 # ----------------------------------------------------------------------------------------------
-def _fd_case(B, H, Hkv, n, d, causal, bm, seed, ncoord=24, h=1e-6, rate=0.0):
+def _fd_case(B, H, Hkv, n, d, causal, bm, seed, ncoord=24, h=1e-6, rate=0.0, nk=None):
+    nk = n if nk is None else nk
     q = _rand((B, H, n, d), seed)
-    k = _rand((B, Hkv, n, d), seed + 1)
-    v = _rand((B, Hkv, n, d), seed + 2)
+    k = _rand((B, Hkv, nk, d), seed + 1)
+    v = _rand((B, Hkv, nk, d), seed + 2)
     g = _rand((B, H, n, d), seed + 3)
     scale = 0.6
     drop_seed = 1234567 + seed  # a fixed keep mask: the output is then differentiable
@@ -512,8 +521,164 @@ def pin_dropout_finite_differences():
     _fd_case(2, 4, 2, 10, 3, True, None, 160, rate=0.2)
 
 
+# ----------------------------------------------------------------------------------------------
+# P-15: unequal query and key lengths (queries at the end of the sequence, as beside a KV cache)
+# ----------------------------------------------------------------------------------------------
+def pin_cross_lengths_brute_force():
+    seed = 600
+    for nq in (1, 2, 3, 5):
+        for nk in (1, 2, 4, 6):
+            for causal in (False, True):
+                seed += 1
+                q, k, v = _rand((nq, 3), seed), _rand((nk, 3), seed + 100), _rand((nk, 2), seed + 200)
+                o, l_ = A.forward(q[None, None], k[None, None], v[None, None], 0.9, causal)
+                ob, lb = brute_force(q.tolist(), k.tolist(), v.tolist(), 0.9, causal)
+                assert np.abs(o[0, 0] - ob).max() <= 1e-12, (nq, nk, causal)
+                assert np.array_equal(np.isinf(l_[0, 0]), np.isinf(lb)), (nq, nk, causal)
+                fin = np.isfinite(lb)
+                assert np.abs(l_[0, 0][fin] - lb[fin]).max(initial=0.0) <= 1e-12, (nq, nk, causal)
+
+
+def pin_cross_lengths_suffix():
+    """Nq < Nk: the result is the last Nq rows of square causal attention whose
+    earlier query rows are anything; with dO zero on those rows the key and
+    value gradients agree too. Nq > Nk: the first Nq - Nk rows see nothing and
+    the rest is square causal attention over all Nk keys."""
+    nk, d = 300, 6
+    k, v = _rand((1, 1, nk, d), 71), _rand((1, 1, nk, d), 72)
+    for nq in (1, 37, 129, 299):
+        qf = _rand((1, 1, nk, d), 73 + nq)
+        gf = _rand((1, 1, nk, d), 74 + nq)
+        gf[:, :, :nk - nq] = 0.0
+        q, g = qf[:, :, nk - nq:], gf[:, :, nk - nq:]
+        o, l_ = A.forward(q, k, v, 0.4, True)
+        of, lf = A.forward(qf, k, v, 0.4, True)
+        assert np.abs(o - of[:, :, nk - nq:]).max() <= 1e-13
+        assert np.abs(l_ - lf[:, :, nk - nq:]).max() <= 1e-13
+        dq, dk, dv = A.backward(q, k, v, g, 0.4, True)
+        dqf, dkf, dvf = A.backward(qf, k, v, gf, 0.4, True)
+        assert np.abs(dq - dqf[:, :, nk - nq:]).max() <= 1e-12
+        assert np.abs(dk - dkf).max() <= 1e-12 and np.abs(dv - dvf).max() <= 1e-12
+    # more queries than keys
+    nq = 200
+    nk2 = 70
+    q = _rand((1, 1, nq, d), 81)
+    g = _rand((1, 1, nq, d), 82)
+    o, l_ = A.forward(q, k[:, :, :nk2], v[:, :, :nk2], 0.4, True)
+    assert np.all(o[0, 0, :nq - nk2] == 0) and np.all(l_[0, 0, :nq - nk2] == -np.inf)
+    o2, l2 = A.forward(q[:, :, nq - nk2:], k[:, :, :nk2], v[:, :, :nk2], 0.4, True)
+    assert np.abs(o[:, :, nq - nk2:] - o2).max() <= 1e-13 and np.abs(l_[:, :, nq - nk2:] - l2).max() <= 1e-13
+    dq, dk, dv = A.backward(q, k[:, :, :nk2], v[:, :, :nk2], g, 0.4, True)
+    assert np.all(dq[0, 0, :nq - nk2] == 0)
+    dq2, dk2, dv2 = A.backward(q[:, :, nq - nk2:], k[:, :, :nk2], v[:, :, :nk2], g[:, :, nq - nk2:], 0.4, True)
+    assert np.abs(dq[:, :, nq - nk2:] - dq2).max() <= 1e-12
+    assert np.abs(dk - dk2).max() <= 1e-12 and np.abs(dv - dv2).max() <= 1e-12
+    # a single query (decoding) sees every key
+    q1 = _rand((1, 1, 1, d), 83)
+    o1, l1 = A.forward(q1, k, v, 0.4, True)
+    on, ln_ = A.forward(q1, k, v, 0.4, False)
+    assert np.array_equal(o1, on) and np.array_equal(l1, ln_)
+
+
+def pin_cross_lengths_finite_differences():
+    _fd_case(1, 2, 1, 5, 3, True, None, 610, nk=9)
+    _fd_case(1, 1, 1, 9, 3, True, None, 620, nk=4)
+    _fd_case(2, 2, 2, 6, 2, False, None, 630, nk=11)
+    mask = np.array([[1, 0, 1]], dtype=np.uint8)
+    _fd_case(1, 1, 1, 100, 2, True, mask, 640, ncoord=16, nk=300)   # 1 x 3 block mask
+
+
+# ----------------------------------------------------------------------------------------------
+# P-16: packed variable-length batches equal attention over the concatenation with
+# visibility restricted to each sequence (brute force over the whole packed rows)
+# ----------------------------------------------------------------------------------------------
+def _packed_brute_force(q, k, v, cu_q, cu_k, scale, causal):
+    """q: [Tq, d], k, v: [Tk, d] of one head; scalar loops over packed positions."""
+    tq, dv = len(q), len(v[0])
+    outs, lses = [], []
+    for i in range(tq):
+        b = max(x for x in range(len(cu_q) - 1) if cu_q[x] <= i)
+        while cu_q[b + 1] <= i:
+            b += 1
+        nq, nk = cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]
+        pos = (i - cu_q[b]) + nk - nq   # the row's position within its own sequence
+        keys = [j for j in range(len(k)) if cu_k[b] <= j < cu_k[b + 1] and (not causal or j - cu_k[b] <= pos)]
+        if not keys:
+            outs.append([0.0] * dv)
+            lses.append(-math.inf)
+            continue
+        sc = [scale * sum(a * c for a, c in zip(q[i], k[j])) for j in keys]
+        mx = max(sc)
+        w = [math.exp(x - mx) for x in sc]
+        z = sum(w)
+        outs.append([sum(w[a] * v[j][t] for a, j in enumerate(keys)) / z for t in range(dv)])
+        lses.append(mx + math.log(z))
+    return np.array(outs), np.array(lses)
+
+
+def pin_varlen_brute_force():
+    cases = [([0, 3, 3, 8, 9], [0, 5, 7, 9, 9]),      # an empty query run and an empty key run
+             ([0, 4, 10], [0, 4, 10]),
+             ([0, 1, 2, 3], [0, 6, 7, 12])]
+    for n, (cu_q, cu_k) in enumerate(cases):
+        H, Hkv, d = 2, 1, 3
+        q = _rand((H, cu_q[-1], d), 700 + n)
+        k = _rand((Hkv, cu_k[-1], d), 710 + n)
+        v = _rand((Hkv, cu_k[-1], d), 720 + n)
+        for causal in (False, True):
+            o, l_ = A.forward_varlen(q, k, v, cu_q, cu_k, 0.8, causal)
+            for h in range(H):
+                ob, lb = _packed_brute_force(q[h].tolist(), k[0].tolist(), v[0].tolist(), cu_q, cu_k, 0.8, causal)
+                assert np.abs(o[h] - ob).max(initial=0.0) <= 1e-12, (n, causal)
+                assert np.array_equal(np.isinf(l_[h]), np.isinf(lb))
+                fin = np.isfinite(lb)
+                assert np.abs(l_[h][fin] - lb[fin]).max(initial=0.0) <= 1e-12
+
+
+def pin_varlen_finite_differences():
+    cu_q, cu_k = [0, 3, 7, 7, 12], [0, 6, 8, 10, 13]
+    H, Hkv, d, scale = 2, 1, 2, 0.7
+    q = _rand((H, 12, d), 730)
+    k = _rand((Hkv, 13, d), 731)
+    v = _rand((Hkv, 13, d), 732)
+    g = _rand((H, 12, d), 733)
+    for causal, rate in ((True, 0.0), (False, 0.0), (True, 0.4)):
+        def f(q_, k_, v_):
+            o, _ = A.forward_varlen(q_, k_, v_, cu_q, cu_k, scale, causal, rate, 99)
+            return float((o * g).sum())
+
+        grads = A.backward_varlen(q, k, v, g, cu_q, cu_k, scale, causal, rate, 99)
+        rng = np.random.default_rng(734)
+        for which, x in enumerate((q, k, v)):
+            for flat in rng.choice(x.size, size=16, replace=False):
+                idx = np.unravel_index(flat, x.shape)
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += 1e-6
+                xm[idx] -= 1e-6
+                ap, am = [q, k, v], [q, k, v]
+                ap[which], am[which] = xp, xm
+                num = (f(*ap) - f(*am)) / 2e-6
+                assert abs(num - grads[which][idx]) <= 1e-6 * max(1.0, abs(num)), ("qkv"[which], causal, rate)
+
+
+def pin_varlen_dropout_streams():
+    """Sequence b of a packed batch draws the same keep decisions as batch
+    entry b of a fixed-length batch of the same lengths (stream b * H + h,
+    positions within the sequence)."""
+    B, H, n, d = 3, 2, 20, 4
+    q, k, v = (_rand((B, H, n, d), s) for s in (741, 742, 743))
+    o, l_ = A.forward(q, k, v, 0.5, True, dropout_rate=0.3, seed=5)
+    cu = [0, n, 2 * n, 3 * n]
+    pack = lambda x: np.ascontiguousarray(x.transpose(1, 0, 2, 3).reshape(H, B * n, d))
+    ov, lv = A.forward_varlen(pack(q), pack(k), pack(v), cu, cu, 0.5, True, 0.3, 5)
+    assert np.abs(ov - pack(o)).max() <= 1e-15
+    assert np.abs(lv - l_.transpose(1, 0, 2).reshape(H, B * n)).max() <= 1e-15
+
+
 ALL_PINS = [pin_worked_example, pin_recurrence, pin_brute_force, pin_rows_sum_to_one, pin_zero_query,
             pin_dominant_score, pin_permutation, pin_causal_locality, pin_finite_differences,
             pin_gqa_repeat, pin_mask_semantics, pin_empty_rows, pin_scale_zero, pin_torch_sdpa,
             pin_philox_known_answers, pin_dropout_statistics, pin_dropout_expectation,
-            pin_dropout_finite_differences]
+            pin_dropout_finite_differences, pin_cross_lengths_brute_force, pin_cross_lengths_suffix,
+            pin_cross_lengths_finite_differences, pin_varlen_brute_force, pin_varlen_finite_differences,
+            pin_varlen_dropout_streams]

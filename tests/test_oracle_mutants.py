@@ -34,7 +34,18 @@ MUTANTS = {
     "gqa_modulo": ("o, l_ = head_forward(q[b, h], k[b, h // G], v[b, h // G]",
                    "o, l_ = head_forward(q[b, h], k[b, h % Hkv], v[b, h % Hkv]"),
     "gqa_backward_modulo": ("dk[b, h // G] += bk", "dk[b, h % Hkv] += bk"),
-    "candidate_keys_short": ("keys = keys[keys <= rows.max()]", "keys = keys[keys < rows.max()]"),
+    "candidate_keys_short": ("keys = keys[keys <= rows.max() + offset]", "keys = keys[keys < rows.max() + offset]"),
+    "candidate_keys_no_offset": ("keys = keys[keys <= rows.max() + offset]", "keys = keys[keys <= rows.max()]"),
+    "offset_sign": ("off = n - q.shape[0]", "off = q.shape[0] - n"),
+    "offset_top_left_forward": ("        if keys.size:\n            vis = visible(ch, keys, causal, block_mask, offset=off)",
+                                "        if keys.size:\n            vis = visible(ch, keys, causal, block_mask)"),
+    "offset_top_left_backward": ("        vis = visible(ch, keys, causal, block_mask, offset=off)\n        _, p, _ =",
+                                 "        vis = visible(ch, keys, causal, block_mask)\n        _, p, _ ="),
+    "varlen_keys_from_query_spans": ("head_forward(q[h, q0:q1], k[h // G, k0:k1], v[h // G, k0:k1]",
+                                     "head_forward(q[h, q0:q1], k[h // G, q0:q1], v[h // G, q0:q1]"),
+    "varlen_dk_overwrite": ("dk[h // G, k0:k1] += bk", "dk[h // G, k0:k1] = bk"),
+    "varlen_dropout_stream": ("dr = (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None\n            o[h, q0:q1]",
+                              "dr = (dropout_rate, seed, h) if dropout_rate > 0 else None\n            o[h, q0:q1]"),
     "dropout_unscaled": ("return np.where(z, p * _dropout.keep_scale(rate), 0.0)", "return np.where(z, p, 0.0)"),
     "dropout_scaled_by_rate": ("return np.where(z, p * _dropout.keep_scale(rate), 0.0)",
                                "return np.where(z, p / rate, 0.0)"),
