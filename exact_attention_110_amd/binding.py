@@ -57,6 +57,15 @@ def load():
     lib.fa_backward_dropout.restype = I
     lib.fa_backward_stage_dropout.argtypes = [I] + bwd_drop
     lib.fa_backward_stage_dropout.restype = I
+    lib.fa_forward_qk.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, F, U64, P]
+    lib.fa_forward_qk.restype = I
+    lib.fa_backward_qk.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, F, U64, P, S, P]
+    lib.fa_backward_qk.restype = I
+    lib.fa_forward_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, I, F, U64, P]
+    lib.fa_forward_varlen.restype = I
+    lib.fa_backward_varlen.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, I, F, U64,
+                                       P, S, P]
+    lib.fa_backward_varlen.restype = I
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -77,45 +86,71 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _shape(q, k, v):
+def _check_tensors(tensors, dtype):
+    for name, t in tensors:
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != dtype:
+            raise ValueError(f"{name} must be a contiguous device tensor of dtype {dtype}")
+    if dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dtype}")
+
+
+def _shape4(q, k, v):
+    """B, H, Hkv, Nq, Nk, d of q [B, H, Nq, d] and k, v [B, Hkv, Nk, d]."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
-        raise ValueError("q, k, v must be [B, H, N, d] / [B, Hkv, N, d]")
-    B, H, N, d = q.shape
-    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError("q, k, v must be [B, H, Nq, d] / [B, Hkv, Nk, d]")
+    B, H, Nq, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
-            raise ValueError(f"{name} must be a contiguous device tensor of dtype {q.dtype}")
-    if q.dtype not in _DTYPES:
-        raise ValueError(f"unsupported dtype {q.dtype}")
-    return B, H, k.shape[1], N, d
+    _check_tensors((("q", q), ("k", k), ("v", v)), q.dtype)
+    return B, H, k.shape[1], Nq, k.shape[2], d
 
 
-def _mask(block_mask, N, device):
+def _shape(q, k, v):
+    B, H, Hkv, Nq, Nk, d = _shape4(q, k, v)
+    if Nq != Nk:
+        raise ValueError("q and k have different lengths")
+    return B, H, Hkv, Nq, d
+
+
+def _mask(block_mask, Nq, device, Nk=None):
     if block_mask is None:
         return None
-    nb = -(-N // MASK_BLOCK)
+    nbq = -(-Nq // MASK_BLOCK)
+    nbk = nbq if Nk is None else -(-Nk // MASK_BLOCK)
     if not isinstance(block_mask, torch.Tensor):
         block_mask = torch.as_tensor(block_mask)
-    if tuple(block_mask.shape) != (nb, nb) or block_mask.dtype != torch.uint8:
-        raise ValueError(f"block_mask must be uint8 [{nb}, {nb}]")
+    if tuple(block_mask.shape) != (nbq, nbk) or block_mask.dtype != torch.uint8:
+        raise ValueError(f"block_mask must be uint8 [{nbq}, {nbk}]")
     return block_mask.to(device).contiguous()
+
+
+def _seed(seed):
+    return int(seed) & (2**64 - 1)
 
 
 def forward(q, k, v, scale=None, causal=False, block_mask=None, out=None, lse=None, dropout_rate=0.0,
             seed=0):
-    """O, LSE = attention(q, k, v); q [B,H,N,d], k, v [B,Hkv,N,d] on the GPU.
+    """O, LSE = attention(q, k, v); q [B,H,Nq,d], k, v [B,Hkv,Nk,d] on the GPU.
 
-    A positive dropout_rate calls fa_forward_dropout with the 64-bit seed."""
-    B, H, Hkv, N, d = _shape(q, k, v)
+    Nq == Nk calls fa_forward (fa_forward_dropout with a positive
+    dropout_rate); Nq != Nk calls fa_forward_qk (causal masking aligned to
+    the last query)."""
+    B, H, Hkv, N, Nk, d = _shape4(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    m = _mask(block_mask, N, q.device)
+    m = _mask(block_mask, N, q.device, Nk)
+    if Nk != N:
+        st = load().fa_forward_qk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, Hkv, N, Nk, d, scale,
+                                  int(bool(causal)), _ptr(m), _DTYPES[q.dtype], float(dropout_rate), _seed(seed),
+                                  _stream(q.device))
+        if st != 0:
+            raise FAError(st, "fa_forward_qk")
+        return o, lse_t
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, Hkv, N, d, scale, int(bool(causal)), _ptr(m),
             _DTYPES[q.dtype]]
     if dropout_rate:
-        st = load().fa_forward_dropout(*args, float(dropout_rate), int(seed) & (2**64 - 1), _stream(q.device))
+        st = load().fa_forward_dropout(*args, float(dropout_rate), _seed(seed), _stream(q.device))
         where = "fa_forward_dropout"
     else:
         st = load().fa_forward(*args, _stream(q.device))
@@ -141,22 +176,31 @@ def _bwd_args(q, k, v, o, lse, do, dq, dk, dv, scale, causal, m, ws, drop=None):
     B, H, Hkv, N, d = _shape(q, k, v)
     head = [_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
             B, H, Hkv, N, d, scale, int(bool(causal)), _ptr(m), _DTYPES[q.dtype]]
-    mid = [] if drop is None else [float(drop[0]), int(drop[1]) & (2**64 - 1)]
+    mid = [] if drop is None else [float(drop[0]), _seed(drop[1])]
     return head + mid + [_ptr(ws), ws.numel(), _stream(q.device)]
 
 
 def backward(q, k, v, o, lse, do, scale=None, causal=False, block_mask=None, ws=None, grads=None,
              dropout_rate=0.0, seed=0):
     """dq, dk, dv of sum(O * do), recomputing P from q, k and lse (and, with a
-    positive dropout_rate, the forward call's keep decisions from seed)."""
-    B, H, Hkv, N, d = _shape(q, k, v)
+    positive dropout_rate, the forward call's keep decisions from seed).
+    Nq != Nk calls fa_backward_qk."""
+    B, H, Hkv, N, Nk, d = _shape4(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     for name, t in (("o", o), ("do", do)):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
             raise ValueError(f"{name} must match q")
-    m = _mask(block_mask, N, q.device)
+    m = _mask(block_mask, N, q.device, Nk)
     ws = workspace(q, k) if ws is None else ws
     dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    if Nk != N:
+        st = load().fa_backward_qk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                                   _ptr(dv), B, H, Hkv, N, Nk, d, scale, int(bool(causal)), _ptr(m),
+                                   _DTYPES[q.dtype], float(dropout_rate), _seed(seed), _ptr(ws), ws.numel(),
+                                   _stream(q.device))
+        if st != 0:
+            raise FAError(st, "fa_backward_qk")
+        return dq, dk, dv
     if dropout_rate:
         st = load().fa_backward_dropout(*_bwd_args(q, k, v, o, lse, do, dq, dk, dv, scale, causal, m, ws,
                                                    (dropout_rate, seed)))
@@ -183,3 +227,58 @@ def backward_stage(stage, q, k, v, o, lse, do, dq, dk, dv, ws, scale=None, causa
                                                              m, ws))
     if st != 0:
         raise FAError(st, f"fa_backward_stage({stage})")
+
+
+def _varlen_shape(q, k, v, cu_seqlens_q, cu_seqlens_k):
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("packed q, k, v must be [H, total_q, d] / [Hkv, total_k, d]")
+    H, tq, d = q.shape
+    if k.shape != v.shape or k.shape[2] != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    _check_tensors((("q", q), ("k", k), ("v", v)), q.dtype)
+    for name, c in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if c.dtype != torch.int32 or c.dim() != 1 or not c.is_cuda or not c.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 device vector")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 offsets")
+    return cu_seqlens_q.numel() - 1, H, k.shape[0], tq, k.shape[1], d
+
+
+def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale=None, causal=False,
+                   out=None, lse=None, dropout_rate=0.0, seed=0):
+    """O [H, total_q, d], LSE [H, total_q] of packed sequences (fa_forward_varlen)."""
+    B, H, Hkv, tq, tk, d = _varlen_shape(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((H, tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = load().fa_forward_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), _ptr(cu_seqlens_q),
+                                  _ptr(cu_seqlens_k), B, H, Hkv, tq, tk, int(max_seqlen_q), int(max_seqlen_k), d,
+                                  scale, int(bool(causal)), _DTYPES[q.dtype], float(dropout_rate), _seed(seed),
+                                  _stream(q.device))
+    if st != 0:
+        raise FAError(st, "fa_forward_varlen")
+    return o, lse_t
+
+
+def backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale=None,
+                    causal=False, ws=None, grads=None, dropout_rate=0.0, seed=0):
+    """dq, dk, dv of packed sequences (fa_backward_varlen)."""
+    B, H, Hkv, tq, tk, d = _varlen_shape(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    for name, t in (("o", o), ("do", do)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must match q")
+    if ws is None:
+        n = workspace_size(B, H, Hkv, int(max_seqlen_q), d, q.dtype)
+        if n == 0:
+            raise ValueError("no backward for these arguments")
+        ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    st = load().fa_backward_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                                   _ptr(dv), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, H, Hkv, tq, tk,
+                                   int(max_seqlen_q), int(max_seqlen_k), d, scale, int(bool(causal)),
+                                   _DTYPES[q.dtype], float(dropout_rate), _seed(seed), _ptr(ws), ws.numel(),
+                                   _stream(q.device))
+    if st != 0:
+        raise FAError(st, "fa_backward_varlen")
+    return dq, dk, dv

@@ -15,35 +15,65 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Shape checks shared by every entry point. Sizes must keep per-head offsets
-// and row counts inside 32-bit signed range and fit the launch grid.
-int check_shape(int B, int H, int Hkv, int N, int d, float scale, int dtype) {
-  if (B < 1 || H < 1 || Hkv < 1 || N < 1) return FA_ERR_INVALID_ARG;
-  if (H % Hkv != 0) return FA_ERR_INVALID_ARG;
-  if (d != 32 && d != 64 && d != 128) return FA_ERR_INVALID_ARG;
+// Sequence geometry of a call: fixed lengths (cu_q == NULL; Q [B][H][Nq][d],
+// K and V [B][Hkv][Nk][d]) or a packed batch (Q [H][tq][d], K and V
+// [Hkv][tk][d], sequence b at rows cu_q[b], cu_k[b], Nq and Nk its longest).
+struct Geo {
+  int B, H, Hkv, Nq, Nk, d;
+  const int* cu_q;
+  const int* cu_k;
+  int tq, tk;
+};
+
+Geo fixed_geo(int B, int H, int Hkv, int Nq, int Nk, int d) {
+  return Geo{B, H, Hkv, Nq, Nk, d, nullptr, nullptr, 0, 0};
+}
+
+// Shape checks shared by every entry point. Sizes must keep per-sequence byte
+// offsets inside 32 bits, row counts inside 32-bit signed range and the
+// launch grid inside its limits.
+int check_shape(const Geo& g, float scale, int dtype) {
+  if (g.B < 1 || g.H < 1 || g.Hkv < 1 || g.Nq < 1 || g.Nk < 1) return FA_ERR_INVALID_ARG;
+  if (g.H % g.Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (g.d != 32 && g.d != 64 && g.d != 128) return FA_ERR_INVALID_ARG;
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
-  const long long rows = (long long)B * H * N;
-  // one head of a tensor must be addressable with 32-bit byte offsets (with room
-  // to spare: N * d * 4 < 2^32)
-  if (rows > INT32_MAX || (long long)N * d >= (1LL << 30)) return FA_ERR_INVALID_ARG;
-  if (B > 65535 || (N + 127) / 128 > 65535) return FA_ERR_INVALID_ARG;
+  long long rq, rk;
+  if (g.cu_q || g.cu_k) {
+    if (!g.cu_q || !g.cu_k || ((uintptr_t)g.cu_q & 3u) || ((uintptr_t)g.cu_k & 3u)) return FA_ERR_INVALID_ARG;
+    if (g.tq < 0 || g.tk < 0) return FA_ERR_INVALID_ARG;
+    rq = (long long)g.H * g.tq;
+    rk = (long long)g.Hkv * g.tk;
+  } else {
+    rq = (long long)g.B * g.H * g.Nq;
+    rk = (long long)g.B * g.Hkv * g.Nk;
+  }
+  // one sequence of a head must be addressable with 32-bit byte offsets (with
+  // room to spare: n * d * 4 < 2^32)
+  if (rq > INT32_MAX || rk > INT32_MAX) return FA_ERR_INVALID_ARG;
+  if ((long long)g.Nq * g.d >= (1LL << 30) || (long long)g.Nk * g.d >= (1LL << 30)) return FA_ERR_INVALID_ARG;
+  if (g.B > 65535 || (g.Nq + 127) / 128 > 65535 || (g.Nk + 127) / 128 > 65535) return FA_ERR_INVALID_ARG;
   return FA_OK;
 }
 
-fa::AttnShape make_shape(int B, int H, int Hkv, int N, int d, float scale, int causal,
-                         const uint8_t* mask) {
+fa::AttnShape make_shape(const Geo& g, float scale, int causal, const uint8_t* mask) {
   fa::AttnShape s;
-  s.B = B;
-  s.H = H;
-  s.Hkv = Hkv;
-  s.N = N;
-  s.d = d;
-  s.G = H / Hkv;
+  s.B = g.B;
+  s.H = g.H;
+  s.Hkv = g.Hkv;
+  s.Nq = g.Nq;
+  s.Nk = g.Nk;
+  s.d = g.d;
+  s.G = g.H / g.Hkv;
   s.scale = scale;
   s.causal = causal != 0;
   s.mask = mask;
-  s.nb = (N + 127) / 128;
+  s.nbq = (g.Nq + 127) / 128;
+  s.nbk = (g.Nk + 127) / 128;
+  s.cu_q = g.cu_q;
+  s.cu_k = g.cu_k;
+  s.tq = g.tq;
+  s.tk = g.tk;
   s.drop_t = 0;
   s.drop_scale = 1.f;
   s.seed0 = s.seed1 = 0;
@@ -67,42 +97,45 @@ bool set_dropout(fa::AttnShape& s, float rate, unsigned long long seed) {
 // Block masks are compacted per row / column in LDS lists of 2048 entries.
 constexpr int kMaxMaskBlocks = 2048;
 
+bool mask_too_long(const Geo& g, const uint8_t* mask) {
+  return mask && ((g.Nq + 127) / 128 > kMaxMaskBlocks || (g.Nk + 127) / 128 > kMaxMaskBlocks);
+}
+
 // Backward workspace: per (b, h) two float planes (log2-scaled LSE and D) of
-// npad = N rounded up to 128 rows, so that whole 128-row blocks load in bounds.
+// npad = Nq rounded up to 128 rows, so that whole 128-row blocks load in bounds.
 int stats_rows(int N) { return (N + 127) / 128 * 128; }
 size_t stats_bytes(int B, int H, int N) {
   return round_up((size_t)B * H * 2 * stats_rows(N) * sizeof(float));
 }
 
 int check_backward(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                   const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N,
-                   int d, float scale, const uint8_t* block_mask, int dtype, void* workspace,
-                   size_t workspace_bytes) {
+                   const void* dO, void* dq, void* dk, void* dv, const Geo& g, float scale,
+                   const uint8_t* block_mask, int dtype, void* workspace, size_t workspace_bytes) {
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3u))
     return FA_ERR_INVALID_ARG;
-  int st = check_shape(B, H, Hkv, N, d, scale, dtype);
+  int st = check_shape(g, scale, dtype);
   if (st != FA_OK) return st;
   if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
-  if (block_mask && (N + 127) / 128 > kMaxMaskBlocks) return FA_ERR_UNSUPPORTED;
+  if (mask_too_long(g, block_mask)) return FA_ERR_UNSUPPORTED;
   if (!workspace || ((uintptr_t)workspace % kAlign) != 0) return FA_ERR_WORKSPACE;
-  if ((long long)B * H * 2 * stats_rows(N) > INT32_MAX) return FA_ERR_INVALID_ARG;
-  if (workspace_bytes < stats_bytes(B, H, N)) return FA_ERR_WORKSPACE;
+  if ((long long)g.B * g.H * 2 * stats_rows(g.Nq) > INT32_MAX) return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < stats_bytes(g.B, g.H, g.Nq)) return FA_ERR_WORKSPACE;
   return FA_OK;
 }
 
-int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                 int Hkv, int N, int d, float scale, int causal, const uint8_t* block_mask, int dtype,
-                 float rate, unsigned long long seed, void* stream) {
+int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, const Geo& g,
+                 float scale, int causal, const uint8_t* block_mask, int dtype, float rate,
+                 unsigned long long seed, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u))
     return FA_ERR_INVALID_ARG;
-  int st = check_shape(B, H, Hkv, N, d, scale, dtype);
+  int st = check_shape(g, scale, dtype);
   if (st != FA_OK) return st;
-  if (block_mask && (N + 127) / 128 > kMaxMaskBlocks) return FA_ERR_UNSUPPORTED;
+  if (mask_too_long(g, block_mask)) return FA_ERR_UNSUPPORTED;
   fa::FwdArgs a;
-  a.s = make_shape(B, H, Hkv, N, d, scale, causal, block_mask);
+  a.s = make_shape(g, scale, causal, block_mask);
   if (!set_dropout(a.s, rate, seed)) return FA_ERR_INVALID_ARG;
   if (a.s.drop_t > 0 && dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   a.q = q;
@@ -115,15 +148,15 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
 }
 
 int stage_impl(int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,
-               const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
-               float scale, int causal, const uint8_t* block_mask, int dtype, float rate,
-               unsigned long long seed, void* workspace, size_t workspace_bytes, void* stream) {
+               const void* dO, void* dq, void* dk, void* dv, const Geo& g, float scale, int causal,
+               const uint8_t* block_mask, int dtype, float rate, unsigned long long seed, void* workspace,
+               size_t workspace_bytes, void* stream) {
   if (stage < 0 || stage > 2) return FA_ERR_INVALID_ARG;
-  int st = check_backward(q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, N, d, scale, block_mask,
-                          dtype, workspace, workspace_bytes);
+  int st = check_backward(q, k, v, o, lse, dO, dq, dk, dv, g, scale, block_mask, dtype, workspace,
+                          workspace_bytes);
   if (st != FA_OK) return st;
   fa::BwdArgs a;
-  a.s = make_shape(B, H, Hkv, N, d, scale, causal, block_mask);
+  a.s = make_shape(g, scale, causal, block_mask);
   if (!set_dropout(a.s, rate, seed)) return FA_ERR_INVALID_ARG;
   a.q = q;
   a.k = k;
@@ -135,19 +168,19 @@ int stage_impl(int stage, const void* q, const void* k, const void* v, const voi
   a.dk = dk;
   a.dv = dv;
   a.stats = (float*)workspace;
-  a.npad = stats_rows(N);
+  a.npad = stats_rows(g.Nq);
   (void)hipGetLastError();
   return fa::launch_backward_stage(stage, a, dtype, (hipStream_t)stream) == hipSuccess ? FA_OK
                                                                                         : FA_ERR_HIP;
 }
 
 int backward_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                  const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
-                  float scale, int causal, const uint8_t* block_mask, int dtype, float rate,
-                  unsigned long long seed, void* workspace, size_t workspace_bytes, void* stream) {
+                  const void* dO, void* dq, void* dk, void* dv, const Geo& g, float scale, int causal,
+                  const uint8_t* block_mask, int dtype, float rate, unsigned long long seed,
+                  void* workspace, size_t workspace_bytes, void* stream) {
   for (int stage = 0; stage < 3; ++stage) {
-    int st = stage_impl(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, N, d, scale, causal,
-                        block_mask, dtype, rate, seed, workspace, workspace_bytes, stream);
+    int st = stage_impl(stage, q, k, v, o, lse, dO, dq, dk, dv, g, scale, causal, block_mask, dtype, rate,
+                        seed, workspace, workspace_bytes, stream);
     if (st != FA_OK) return st;
   }
   return FA_OK;
@@ -158,8 +191,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
 extern "C" {
 
 size_t fa_backward_workspace_size(int B, int H, int Hkv, int N, int d, int dtype) {
-  if (check_shape(B, H, Hkv, N, d, 1.0f, dtype) != FA_OK || dtype == FA_F32) return 0;
-  (void)d;
+  if (check_shape(fixed_geo(B, H, Hkv, N, N, d), 1.0f, dtype) != FA_OK || dtype == FA_F32) return 0;
   if ((long long)B * H * 2 * stats_rows(N) > INT32_MAX) return 0;
   return stats_bytes(B, H, N);
 }
@@ -167,23 +199,40 @@ size_t fa_backward_workspace_size(int B, int H, int Hkv, int N, int d, int dtype
 int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                int Hkv, int N, int d, float scale, int causal, const uint8_t* block_mask,
                int dtype, void* stream) {
-  return forward_impl(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, block_mask, dtype, 0.f, 0ull,
-                      stream);
+  return forward_impl(q, k, v, o, lse, fixed_geo(B, H, Hkv, N, N, d), scale, causal, block_mask, dtype, 0.f,
+                      0ull, stream);
 }
 
 int fa_forward_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                        int H, int Hkv, int N, int d, float scale, int causal,
                        const uint8_t* block_mask, int dtype, float dropout_rate,
                        unsigned long long seed, void* stream) {
-  return forward_impl(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, block_mask, dtype,
+  return forward_impl(q, k, v, o, lse, fixed_geo(B, H, Hkv, N, N, d), scale, causal, block_mask, dtype,
                       dropout_rate, seed, stream);
+}
+
+int fa_forward_qk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                  int Hkv, int Nq, int Nk, int d, float scale, int causal, const uint8_t* block_mask,
+                  int dtype, float dropout_rate, unsigned long long seed, void* stream) {
+  return forward_impl(q, k, v, o, lse, fixed_geo(B, H, Hkv, Nq, Nk, d), scale, causal, block_mask, dtype,
+                      dropout_rate, seed, stream);
+}
+
+int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H, int Hkv,
+                      int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d,
+                      float scale, int causal, int dtype, float dropout_rate,
+                      unsigned long long seed, void* stream) {
+  if (!cu_seqlens_q || !cu_seqlens_k) return FA_ERR_INVALID_ARG;
+  const Geo g{B, H, Hkv, max_seqlen_q, max_seqlen_k, d, cu_seqlens_q, cu_seqlens_k, total_q, total_k};
+  return forward_impl(q, k, v, o, lse, g, scale, causal, nullptr, dtype, dropout_rate, seed, stream);
 }
 
 int fa_backward_stage(int stage, const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H,
                       int Hkv, int N, int d, float scale, int causal, const uint8_t* block_mask,
                       int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  return stage_impl(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, N, d, scale, causal,
+  return stage_impl(stage, q, k, v, o, lse, dO, dq, dk, dv, fixed_geo(B, H, Hkv, N, N, d), scale, causal,
                     block_mask, dtype, 0.f, 0ull, workspace, workspace_bytes, stream);
 }
 
@@ -193,7 +242,7 @@ int fa_backward_stage_dropout(int stage, const void* q, const void* k, const voi
                               int causal, const uint8_t* block_mask, int dtype,
                               float dropout_rate, unsigned long long seed, void* workspace,
                               size_t workspace_bytes, void* stream) {
-  return stage_impl(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, N, d, scale, causal,
+  return stage_impl(stage, q, k, v, o, lse, dO, dq, dk, dv, fixed_geo(B, H, Hkv, N, N, d), scale, causal,
                     block_mask, dtype, dropout_rate, seed, workspace, workspace_bytes, stream);
 }
 
@@ -201,8 +250,8 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                 const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
                 float scale, int causal, const uint8_t* block_mask, int dtype, void* workspace,
                 size_t workspace_bytes, void* stream) {
-  return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, N, d, scale, causal, block_mask,
-                       dtype, 0.f, 0ull, workspace, workspace_bytes, stream);
+  return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, fixed_geo(B, H, Hkv, N, N, d), scale, causal,
+                       block_mask, dtype, 0.f, 0ull, workspace, workspace_bytes, stream);
 }
 
 int fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,
@@ -211,8 +260,30 @@ int fa_backward_dropout(const void* q, const void* k, const void* v, const void*
                         const uint8_t* block_mask, int dtype, float dropout_rate,
                         unsigned long long seed, void* workspace, size_t workspace_bytes,
                         void* stream) {
-  return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, Hkv, N, d, scale, causal, block_mask,
-                       dtype, dropout_rate, seed, workspace, workspace_bytes, stream);
+  return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, fixed_geo(B, H, Hkv, N, N, d), scale, causal,
+                       block_mask, dtype, dropout_rate, seed, workspace, workspace_bytes, stream);
+}
+
+int fa_backward_qk(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int Nq,
+                   int Nk, int d, float scale, int causal, const uint8_t* block_mask, int dtype,
+                   float dropout_rate, unsigned long long seed, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, fixed_geo(B, H, Hkv, Nq, Nk, d), scale, causal,
+                       block_mask, dtype, dropout_rate, seed, workspace, workspace_bytes, stream);
+}
+
+int fa_backward_varlen(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                       const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H, int Hkv,
+                       int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d,
+                       float scale, int causal, int dtype, float dropout_rate,
+                       unsigned long long seed, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (!cu_seqlens_q || !cu_seqlens_k) return FA_ERR_INVALID_ARG;
+  const Geo g{B, H, Hkv, max_seqlen_q, max_seqlen_k, d, cu_seqlens_q, cu_seqlens_k, total_q, total_k};
+  return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, g, scale, causal, nullptr, dtype, dropout_rate, seed,
+                       workspace, workspace_bytes, stream);
 }
 
 const char* fa_status_string(int status) {
@@ -226,6 +297,6 @@ const char* fa_status_string(int status) {
   }
 }
 
-int fa_version(void) { return 101; }
+int fa_version(void) { return 102; }
 
 }  // extern "C"

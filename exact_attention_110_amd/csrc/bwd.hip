@@ -43,7 +43,7 @@ namespace fa {
 
 // ---------------------------------------------------------------------------
 // stage 0: per query row, D = rowsum(dO * O) in fp32 and the log2-scaled LSE,
-// into the workspace's two planes (padding rows N..npad-1 included)
+// into the workspace's two planes (padding rows past the sequence up to npad included)
 // ---------------------------------------------------------------------------
 template <class T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
@@ -52,12 +52,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int nblk = (a.npad + RPB - 1) / RPB;  // blocks per (b, h) head
   const int bh = blockIdx.x / nblk;
-  const int r = (blockIdx.x % nblk) * RPB + tid / CH;  // row within the head
+  const int r = (blockIdx.x % nblk) * RPB + tid / CH;  // row within the sequence
   const int part = tid % CH;
-  const int N = a.s.N;
+  const int h = bh % a.s.H;
+  const SeqView sv = seq_view(a.s, bh / a.s.H, h, h / a.s.G);
+  const int nq = sv.nq;
   float sum = 0.f;
-  if (r < N) {
-    const size_t off = ((size_t)bh * N + r) * D + part * 8;
+  if (r < nq) {
+    const size_t off = (sv.qrow0 + r) * D + part * 8;
     const s16x8 o = gload16((const unsigned short*)a.o + off);
     const s16x8 g = gload16((const unsigned short*)a.dO + off);
 #pragma unroll
@@ -67,8 +69,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 #pragma unroll
   for (int msk = CH / 2; msk >= 1; msk >>= 1) sum += __shfl_xor(sum, msk, 64);
   if (r < a.npad && part == 0) {
-    // a row past N, or one that saw no key, gets +inf so that its P is 0
-    const float lv = r < N ? a.lse[(size_t)bh * N + r] : -INFINITY;
+    // a row past the sequence, or one that saw no key, gets +inf so that its P is 0
+    const float lv = r < nq ? a.lse[sv.qrow0 + r] : -INFINITY;
     float* st = a.stats + (size_t)bh * 2 * a.npad;
     st[r] = lv != -INFINITY ? lv * kLog2e : INFINITY;
     st[a.npad + r] = sum;
@@ -118,7 +120,6 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
       (__attribute__((address_space(3))) int*)(stat + NB * STB + (MASK ? 2 * MASK_LIST : 0));
 
   const AttnShape& s = a.s;
-  const int N = s.N;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
   const int g16 = lane >> 4;
@@ -126,18 +127,23 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
   const int coff = 16 * (g16 & 1) + 4 * (lane & 3);       // transposing-read column offset
   // grid = (Hkv, key blocks, B); under causal masking block 0 has the most work
   const int hk = blockIdx.x, kblk = blockIdx.y, b = blockIdx.z;
+  // the sequence as seen from the group's first query head
+  const SeqView sv = seq_view(s, b, hk * s.G, hk);
+  const int len_q = sv.nq, len_k = sv.nk, off = sv.off;
   const int k0 = kblk * KV_BKV;
+  if (k0 >= len_k) return;  // a sequence shorter than the grid (packed batches)
   const int kj = k0 + 32 * w + l32;  // this lane's key (its column of S)
   const float c = s.scale * kLog2e;
 
-  // per-head buffer resources: rows past N read as zeros, writes past N are dropped
-  const unsigned int head_bytes = (unsigned int)N * D * 2;
-  const size_t krow0 = (size_t)(b * s.Hkv + hk) * N;
-  const rsrc_t rk = make_rsrc((const unsigned short*)a.k + krow0 * D, head_bytes);
-  const rsrc_t rv = make_rsrc((const unsigned short*)a.v + krow0 * D, head_bytes);
+  // per-sequence buffer resources: rows past the sequence read as zeros, writes
+  // past it are dropped
+  const unsigned int qbytes = (unsigned int)len_q * D * 2, kbytes = (unsigned int)len_k * D * 2;
+  const size_t krow0 = sv.krow0;
+  const rsrc_t rk = make_rsrc((const unsigned short*)a.k + krow0 * D, kbytes);
+  const rsrc_t rv = make_rsrc((const unsigned short*)a.v + krow0 * D, kbytes);
 
   // K^T and V^T operands: lane holds key kj, d = 16 ss + 8 hh + 0..7. Keys past
-  // N read as zeros; their dK, dV are never stored.
+  // the sequence read as zeros; their dK, dV are never stored.
   s16x8 kf[NS], vf[NS];
 #pragma unroll
   for (int ss = 0; ss < NS; ++ss) {
@@ -145,18 +151,18 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
     vf[ss] = bload16(rv, (unsigned)(kj * D + 16 * ss + 8 * hh) * 2u);
   }
 
-  // query blocks this key block meets
-  const int nqb_all = (N + BQ - 1) / BQ;
-  const int qb_first = CAUSAL ? k0 / BQ : 0;
+  // query blocks this key block meets: under causal masking, rows from k0 - off on
+  const int nqb_all = (len_q + BQ - 1) / BQ;
+  const int qb_first = CAUSAL ? max(0, k0 - off) / BQ : 0;
   int nq = nqb_all - qb_first;
   if constexpr (MASK) {
     // mask rows I with mask[I][kblk] != 0, from the first one needed
     const int i_first = qb_first / KV_R;
     if (w == 0) {
       int cnt = 0;
-      for (int j0 = i_first; j0 < s.nb; j0 += 64) {
+      for (int j0 = i_first; j0 < s.nbq; j0 += 64) {
         const int j = j0 + lane;
-        const bool keep = j < s.nb && s.mask[(size_t)j * s.nb + kblk] != 0;
+        const bool keep = j < s.nbq && s.mask[(size_t)j * s.nbk + kblk] != 0;
         const unsigned long long bal = __ballot(keep);
         if (keep) blist[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (short)j;
         cnt += __popcll(bal);
@@ -166,7 +172,7 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
     __syncthreads();
     const int cnt = *bcount;
     nq = KV_R * cnt;
-    if (cnt > 0) nq -= max(0, KV_R * (blist[cnt - 1] + 1) - nqb_all);  // steps past N
+    if (cnt > 0) nq -= max(0, KV_R * (blist[cnt - 1] + 1) - nqb_all);  // steps past the sequence
   }
   auto qblock_at = [&](int qi) -> int {
     if constexpr (MASK) return KV_R * blist[qi / KV_R] + qi % KV_R;
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
   auto advance = [&](StepPos p) -> StepPos {
     const bool next_head = p.qi + 1 >= nq;
     return StepPos{next_head ? 0 : p.qi + 1, next_head ? p.hb + 1 : p.hb, next_head ? p.soff + 2 * a.npad : p.soff,
-                   next_head ? p.qoff + (unsigned long long)N * D : p.qoff};
+                   next_head ? p.qoff + (unsigned long long)sv.qstride * D : p.qoff};
   };
 
   f32x16 dka[ND], dva[ND];
@@ -195,8 +201,8 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
   // up to the padded length are in range).
   auto dma_q = [&](StepPos p, int buf) {
     const int q0 = qblock_at(p.qi) * BQ;
-    const i32x4 rq = rsrc_words((const unsigned short*)a.q + p.qoff, head_bytes);
-    const i32x4 rg = rsrc_words((const unsigned short*)a.dO + p.qoff, head_bytes);
+    const i32x4 rq = rsrc_words((const unsigned short*)a.q + p.qoff, qbytes);
+    const i32x4 rg = rsrc_words((const unsigned short*)a.dO + p.qoff, qbytes);
     dma_tile<D, BQ, KV_NW>(rq, q0, qbuf + buf * QBUF, w, lane);
     dma_tile<D, BQ, KV_NW>(rg, q0, obuf + buf * QBUF, w, lane);
     if (w == KV_NW - 1) {
@@ -226,8 +232,9 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
 
   // P and dS (unscaled) of a step from its S, dP and statistics buffer. Element
   // i is query q0 + 8 (i / 4) + 4 hh + i % 4 of key kj; under causal masking it
-  // is kept only if 8 (i / 4) + i % 4 >= kj - q0 - 4 hh. Keys past N need no
-  // mask: their K and V rows read as zeros and nothing of theirs is stored.
+  // is kept only if 8 (i / 4) + i % 4 >= kj - off - q0 - 4 hh. Keys past the
+  // sequence need no mask: their K and V rows read as zeros and nothing of
+  // theirs is stored.
   // With dropout (z the keep decision, c its scale): P V uses z c P, and
   // dS = P (z c dP - D), the gradient flowing to P through the dropped values.
   auto probs = [&](auto masked, const f32x16& sc, const f32x16& dp, int q0, int stb, int bh, unsigned int (&pk)[8],
@@ -236,7 +243,7 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
     const __attribute__((address_space(3))) float* lsel =
         (const __attribute__((address_space(3))) float*)(stat + stb * STB);
     const __attribute__((address_space(3))) float* ddl = lsel + BQ;
-    const int thr = kj - q0 - 4 * hh;
+    const int thr = kj - off - q0 - 4 * hh;
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       const f32x4 L4 = *(const __attribute__((address_space(3))) f32x4*)(lsel + 8 * j4 + 4 * hh);
@@ -301,7 +308,7 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
     lds_write16((t ? obuf : qbuf) + (NB - 1) * QBUF + off, (s16x8){0, 0, 0, 0, 0, 0, 0, 0});
   }
   const int hb0 = b * s.H + hk * s.G;  // first query head of the group, batch included
-  StepPos cur{0, hb0, hb0 * 2 * a.npad, (unsigned long long)hb0 * N * D};
+  StepPos cur{0, hb0, hb0 * 2 * a.npad, (unsigned long long)sv.qrow0 * D};
   StepPos nxt = nsteps > 1 ? advance(cur) : cur;
   dma_q(cur, 0);
   dma_q(nxt, 1);
@@ -339,11 +346,14 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
       skA[j] = skB[j];
     }
   };
-  // steps at the start of each head's list that touch the diagonal block
+  // steps at the start of each head's list that cross the causal diagonal: a
+  // query block from q0 needs masking while q0 + off < k0 + 127 (the block's
+  // last key). The list rises, so they form a prefix (at most five steps
+  // without a mask, two mask rows with one).
   int ndiag = 0;
   if constexpr (CAUSAL) {
-    if constexpr (MASK) ndiag = (nq > 0 && blist[0] == kblk) ? min(nq, KV_R) : 0;
-    else ndiag = min(nq, KV_R);
+    const int lim = k0 + KV_BKV - 1 - off;
+    while (ndiag < nq && qblock_at(ndiag) * BQ < lim) ++ndiag;
   }
   int e = 0;
   for (int hg = 0; hg < s.G; ++hg) {
@@ -366,8 +376,8 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
 
   // dK^T / dV^T: lane holds key kj, d = 32 dt + 8 j + 4 hh + 0..3; dK takes the scale
   const float scale = s.scale;
-  const rsrc_t rdk = make_rsrc((unsigned short*)a.dk + krow0 * D, head_bytes);
-  const rsrc_t rdv = make_rsrc((unsigned short*)a.dv + krow0 * D, head_bytes);
+  const rsrc_t rdk = make_rsrc((unsigned short*)a.dk + krow0 * D, kbytes);
+  const rsrc_t rdv = make_rsrc((unsigned short*)a.dv + krow0 * D, kbytes);
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
@@ -413,7 +423,6 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
       (__attribute__((address_space(3))) int*)(vbuf + 2 * VBUF + (MASK ? 2 * MASK_LIST : 0));
 
   const AttnShape& s = a.s;
-  const int N = s.N;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
   const int g16 = lane >> 4;
@@ -423,14 +432,16 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
   const int qb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
   const int h = blockIdx.x, b = blockIdx.z;
   const int hk = h / s.G;
-  const size_t qrow0 = (size_t)(b * s.H + h) * N;
-  const size_t krow0 = (size_t)(b * s.Hkv + hk) * N;
-  const unsigned int head_bytes = (unsigned int)N * D * 2;
-  const rsrc_t rq = make_rsrc((const unsigned short*)a.q + qrow0 * D, head_bytes);
-  const rsrc_t rg = make_rsrc((const unsigned short*)a.dO + qrow0 * D, head_bytes);
-  const i32x4 rk = rsrc_words((const unsigned short*)a.k + krow0 * D, head_bytes);
-  const i32x4 rv = rsrc_words((const unsigned short*)a.v + krow0 * D, head_bytes);
+  const SeqView sv = seq_view(s, b, h, hk);
+  const int len_q = sv.nq, len_k = sv.nk, off = sv.off;
   const int q0 = qb * Q_BM;
+  if (q0 >= len_q) return;  // a sequence shorter than the grid (packed batches)
+  const size_t qrow0 = sv.qrow0, krow0 = sv.krow0;
+  const unsigned int qbytes = (unsigned int)len_q * D * 2, kbytes = (unsigned int)len_k * D * 2;
+  const rsrc_t rq = make_rsrc((const unsigned short*)a.q + qrow0 * D, qbytes);
+  const rsrc_t rg = make_rsrc((const unsigned short*)a.dO + qrow0 * D, qbytes);
+  const i32x4 rk = rsrc_words((const unsigned short*)a.k + krow0 * D, kbytes);
+  const i32x4 rv = rsrc_words((const unsigned short*)a.v + krow0 * D, kbytes);
   const int qw = q0 + 32 * w;
   const int qi = qw + l32;   // this lane's query row
   const float c = s.scale * kLog2e;
@@ -442,13 +453,13 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
     qf[ss] = bload16(rq, (unsigned)(qi * D + 16 * ss + 8 * hh) * 2u);
     gf[ss] = bload16(rg, (unsigned)(qi * D + 16 * ss + 8 * hh) * 2u);
   }
-  // this lane's row statistics from stage 0 (qi < npad); a row past N, or one
-  // that saw no key, has LSE +inf and so P = 0
+  // this lane's row statistics from stage 0 (qi < npad); a row past the
+  // sequence, or one that saw no key, has LSE +inf and so P = 0
   const float* st = a.stats + ((size_t)b * s.H + h) * 2 * a.npad;
   const float lse2 = st[qi];
   const float dd = st[a.npad + qi];
 
-  const int kend = CAUSAL ? min(N, q0 + Q_BM) : N;
+  const int kend = CAUSAL ? min(len_k, max(0, q0 + Q_BM + off)) : len_k;
   const int ntile_all = (kend + Q_BN - 1) / Q_BN;
   int ntiles = ntile_all;
   if constexpr (MASK) {
@@ -457,7 +468,7 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
       int cnt = 0;
       for (int j0 = 0; j0 < nbk; j0 += 64) {
         const int j = j0 + lane;
-        const bool keep = j < nbk && s.mask[(size_t)qb * s.nb + j] != 0;
+        const bool keep = j < nbk && s.mask[(size_t)qb * s.nbk + j] != 0;
         const unsigned long long bal = __ballot(keep);
         if (keep) blist[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (short)j;
         cnt += __popcll(bal);
@@ -481,7 +492,7 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
   // K and V tiles by LDS DMA into the buffer the previous step read (the
-  // barrier that ended it has passed); rows past N arrive as zeros
+  // barrier that ended it has passed); rows past the sequence arrive as zeros
   auto dma_kv = [&](int t, int buf) {
     dma_tile<D, Q_BN, Q_NW>(rk, t * Q_BN, kbuf + buf * KBUF, w, lane);
     dma_tile<D, Q_BN, Q_NW>(rv, t * Q_BN, vbuf + buf * VBUF, w, lane);
@@ -496,7 +507,7 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
     const int ks = tile_at(e) * Q_BN;
     dma_kv(tile_at(e + 1 < ntiles ? e + 1 : e), buf ^ 1);
 
-    const bool active = !(CAUSAL && ks > qw + 31);  // wave-uniform
+    const bool active = !(CAUSAL && ks > qw + 31 + off);  // wave-uniform
     if (active) {
       const lds_t* kb = kbuf + buf * KBUF;
       const lds_t* vb = vbuf + buf * VBUF;
@@ -520,10 +531,11 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
           dp[t2] = mfma32<T>(va, gf[ss], dp[t2]);
         }
       // dS for query qi and key ks + 32 t2 + 8 (i / 4) + 4 hh + i % 4. Causal: kept
-      // only if 32 t2 + 8 (i / 4) + i % 4 <= qi - ks - 4 hh. Keys past N read as
-      // zeros, so their dS multiplies a zero row of K and needs no mask.
-      const bool diag = CAUSAL && ks + Q_BN - 1 > qw;
-      const int thr = qi - ks - 4 * hh;
+      // only if 32 t2 + 8 (i / 4) + i % 4 <= qi + off - ks - 4 hh. Keys past the
+      // sequence read as zeros, so their dS multiplies a zero row of K and needs
+      // no mask.
+      const bool diag = CAUSAL && ks + Q_BN - 1 > qw + off;
+      const int thr = qi + off - ks - 4 * hh;
       unsigned int sk[Q_T2][8];
       auto ds_tile = [&](auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
@@ -574,7 +586,7 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
 
   // dQ = scale * acc; lane holds query qi, d = 32 dt + 8 j + 4 hh + 0..3
   const float scale = s.scale;
-  const rsrc_t rdq = make_rsrc((unsigned short*)a.dq + qrow0 * D, head_bytes);
+  const rsrc_t rdq = make_rsrc((unsigned short*)a.dq + qrow0 * D, qbytes);
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
@@ -598,7 +610,7 @@ static hipError_t launch_pre_t(const BwdArgs& a, hipStream_t st) {
 
 template <class T, int D, bool DROP>
 static hipError_t launch_kv_t2(const BwdArgs& a, hipStream_t st) {
-  const dim3 grid(a.s.Hkv, (a.s.N + KV_BKV - 1) / KV_BKV, a.s.B);
+  const dim3 grid(a.s.Hkv, (a.s.Nk + KV_BKV - 1) / KV_BKV, a.s.B);
   const dim3 block(KV_NW * 64);
   const bool causal = a.s.causal != 0, mask = a.s.mask != nullptr;
   if (causal && mask) hipLaunchKernelGGL((bwd_kv_kernel<T, D, true, true, DROP>), grid, block, 0, st, a);
@@ -615,7 +627,7 @@ static hipError_t launch_kv_t(const BwdArgs& a, hipStream_t st) {
 
 template <class T, int D, bool DROP>
 static hipError_t launch_q_t2(const BwdArgs& a, hipStream_t st) {
-  const dim3 grid(a.s.H, (a.s.N + Q_BM - 1) / Q_BM, a.s.B);
+  const dim3 grid(a.s.H, (a.s.Nq + Q_BM - 1) / Q_BM, a.s.B);
   const dim3 block(Q_NW * 64);
   const bool causal = a.s.causal != 0, mask = a.s.mask != nullptr;
   if (causal && mask) hipLaunchKernelGGL((bwd_q_kernel<T, D, true, true, DROP>), grid, block, 0, st, a);

@@ -66,7 +66,6 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
       (__attribute__((address_space(3))) int*)(smem + 2 * KBUF + 2 * VBUF + (MASK ? 2 * FWD_LIST : 0));
 
   const AttnShape& s = a.s;
-  const int N = s.N;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
   // grid = (H, query blocks, B): consecutive workgroups take different heads, so
@@ -75,21 +74,24 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
   const int qb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
   const int h = blockIdx.x, b = blockIdx.z;
   const int hk = h / s.G;
-  const size_t qrow0 = (size_t)(b * s.H + h) * N;
-  const size_t krow0 = (size_t)(b * s.Hkv + hk) * N;
-  // per-head buffer resources: rows past N read as zeros, stores past N are dropped
-  const unsigned int head_bytes = (unsigned int)N * D * 2;
-  const rsrc_t rq = make_rsrc((const unsigned short*)a.q + qrow0 * D, head_bytes);
-  const rsrc_t rk = make_rsrc((const unsigned short*)a.k + krow0 * D, head_bytes);
-  const rsrc_t rv = make_rsrc((const unsigned short*)a.v + krow0 * D, head_bytes);
+  const SeqView sv = seq_view(s, b, h, hk);
+  const int nq = sv.nq, nk = sv.nk, off = sv.off;
   const int q0 = qb * FWD_BM;
+  if (q0 >= nq) return;  // a sequence shorter than the grid (packed batches)
+  const size_t qrow0 = sv.qrow0, krow0 = sv.krow0;
+  // per-sequence buffer resources: rows past the sequence read as zeros, stores
+  // past it are dropped
+  const unsigned int qbytes = (unsigned int)nq * D * 2, kbytes = (unsigned int)nk * D * 2;
+  const rsrc_t rq = make_rsrc((const unsigned short*)a.q + qrow0 * D, qbytes);
+  const rsrc_t rk = make_rsrc((const unsigned short*)a.k + krow0 * D, kbytes);
+  const rsrc_t rv = make_rsrc((const unsigned short*)a.v + krow0 * D, kbytes);
   const int qw = q0 + 32 * w;   // first query row of this wave
   const int qi = qw + l32;      // query row of this lane's column
   // exponent scale: S * c is the score in log2 units; a zero scale is kept just
   // above zero so that masked entries stay -inf (-inf * 0 would be NaN)
   const float c = fmaxf(s.scale * kLog2e, 1e-30f);
 
-  const int kend = CAUSAL ? min(N, q0 + FWD_BM) : N;
+  const int kend = CAUSAL ? min(nk, max(0, q0 + FWD_BM + off)) : nk;
   const int ntile_all = (kend + FWD_BN - 1) / FWD_BN;
   int ntiles = ntile_all;
   if constexpr (MASK) {
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
       int cnt = 0;
       for (int j0 = 0; j0 < nbk; j0 += 64) {
         const int j = j0 + lane;
-        const bool keep = j < nbk && s.mask[(size_t)qb * s.nb + j] != 0;
+        const bool keep = j < nbk && s.mask[(size_t)qb * s.nbk + j] != 0;
         const unsigned long long bal = __ballot(keep);
         if (keep) blist[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (short)j;
         cnt += __popcll(bal);
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
     const int ks = tile_at(e) * FWD_BN;
     gload_tile(tile_at(e + 1 < ntiles ? e + 1 : e));
 
-    const bool active = !(CAUSAL && ks > qw + 31);  // wave-uniform
+    const bool active = !(CAUSAL && ks > qw + 31 + off);  // wave-uniform
     if (active) {
       const lds_t* kb = kbuf + buf * KBUF;
       const lds_t* vb = vbuf + buf * VBUF;
@@ -190,14 +192,14 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
         }
       }
       // sc[t2][i] is S for query qi and key ks + 32 t2 + 8 (i / 4) + 4 hh + i % 4
-      const bool need_mask = (CAUSAL && ks + FWD_BN - 1 > qw) || (ks + FWD_BN > N);
+      const bool need_mask = (CAUSAL && ks + FWD_BN - 1 > qw + off) || (ks + FWD_BN > nk);
       if (need_mask) {
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = ks + 32 * t2 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            if ((CAUSAL && key > qi) || key >= N) sc[t2][i] = -INFINITY;
+            if ((CAUSAL && key > qi + off) || key >= nk) sc[t2][i] = -INFINITY;
           }
       }
       float mx = sc[0][0];
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
   const float lt = l + swap_halves(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const float lse = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
-  const rsrc_t ro = make_rsrc((unsigned short*)a.o + qrow0 * D, head_bytes);
+  const rsrc_t ro = make_rsrc((unsigned short*)a.o + qrow0 * D, qbytes);
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
@@ -268,7 +270,7 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
                   pack2<T>(acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv)};
       bstore8(ro, (unsigned)(qi * D + 32 * dt + 8 * j + 4 * hh) * 2u, v2);
     }
-  if (hh == 0) bstore_f32(make_rsrc(a.lse + qrow0, (unsigned)N * 4u), (unsigned)qi * 4u, lse);
+  if (hh == 0) bstore_f32(make_rsrc(a.lse + qrow0, (unsigned)nq * 4u), (unsigned)qi * 4u, lse);
 }
 
 // acc *= s for an accumulator held in AGPRs, one element at a time through a
@@ -334,7 +336,6 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
   lds_t* vbuf = kbuf + F64_NB * KBUF;
 
   const AttnShape& s = a.s;
-  const int N = s.N;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
   const int g16 = lane >> 4;
@@ -345,20 +346,22 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
   const int qb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
   const int h = blockIdx.x, b = blockIdx.z;
   const int hk = h / s.G;
-  const size_t qrow0 = (size_t)(b * s.H + h) * N;
-  const size_t krow0 = (size_t)(b * s.Hkv + hk) * N;
-  const unsigned int head_bytes = (unsigned int)N * D * 2;
-  const rsrc_t rq = make_rsrc((const unsigned short*)a.q + qrow0 * D, head_bytes);
-  const rsrc_t rk = make_rsrc((const unsigned short*)a.k + krow0 * D, head_bytes);
-  const rsrc_t rv = make_rsrc((const unsigned short*)a.v + krow0 * D, head_bytes);
+  const SeqView sv = seq_view(s, b, h, hk);
+  const int nq = sv.nq, nk = sv.nk, off = sv.off;
   const int q0 = qb * F64_BM;
+  if (q0 >= nq) return;  // a sequence shorter than the grid (packed batches)
+  const size_t qrow0 = sv.qrow0, krow0 = sv.krow0;
+  const unsigned int qbytes = (unsigned int)nq * D * 2, kbytes = (unsigned int)nk * D * 2;
+  const rsrc_t rq = make_rsrc((const unsigned short*)a.q + qrow0 * D, qbytes);
+  const rsrc_t rk = make_rsrc((const unsigned short*)a.k + krow0 * D, kbytes);
+  const rsrc_t rv = make_rsrc((const unsigned short*)a.v + krow0 * D, kbytes);
   const int qw = q0 + F64_RW * w;  // first query row of this wave; block rb holds rows qw + 32 rb + 0..31
   const float c = fmaxf(s.scale * kLog2e, 1e-30f);
 
-  const int kend = CAUSAL ? min(N, q0 + F64_BM) : N;
+  const int kend = CAUSAL ? min(nk, max(0, q0 + F64_BM + off)) : nk;
   const int ntiles = (kend + F64_BN - 1) / F64_BN;
-  // tiles whose keys every row of the workgroup sees (q0 is a multiple of the tile)
-  const int nfull = CAUSAL ? q0 / F64_BN : N / F64_BN;
+  // tiles whose keys every row of the workgroup sees: row q0 sees keys up to q0 + off
+  const int nfull = CAUSAL ? min(max(0, q0 + off + 1) / F64_BN, nk / F64_BN) : nk / F64_BN;
 
   // Q^T operands of both row blocks: lane holds query qw + 32 rb + l32, d = 16 ss + 8 hh + 0..7
   s16x8 qf[2][NS];
@@ -500,7 +503,7 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
     lds_write16(vbuf + (F64_NB - 1) * VBUF + i * 16, (s16x8){0, 0, 0, 0, 0, 0, 0, 0});
   gload(0);
   lstore(0);
-  gload(min(1, ntiles - 1));
+  gload(max(0, min(1, ntiles - 1)));
   lstore(1);
   __syncthreads();
 
@@ -579,7 +582,7 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
       }
       gload(0);
       lstore(0);
-      gload(min(1, ntiles - 1));
+      gload(max(0, min(1, ntiles - 1)));
       lstore(1);
       __syncthreads();
     }
@@ -590,7 +593,7 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
   for (; j < ntiles; ++j) {
     gload(min(j + 2, ntiles - 1));
     const int ks = j * F64_BN;
-    if (!CAUSAL || ks <= qw + F64_RW - 1) {
+    if (!CAUSAL || ks <= qw + F64_RW - 1 + off) {
       f32x16 st[2];
       s_tile(j & (F64_NB - 1), st);
 #pragma unroll
@@ -599,7 +602,7 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = ks + 8 * (i >> 2) + 4 * hh + (i & 3);
-          if ((CAUSAL && key > qi) || key >= N) st[rb][i] = -INFINITY;
+          if ((CAUSAL && key > qi + off) || key >= nk) st[rb][i] = -INFINITY;
         }
       }
       float mn[2], ls[2];
@@ -612,8 +615,8 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
     __syncthreads();
   }
 
-  const rsrc_t ro = make_rsrc((unsigned short*)a.o + qrow0 * D, head_bytes);
-  const rsrc_t rl = make_rsrc(a.lse + qrow0, (unsigned)N * 4u);
+  const rsrc_t ro = make_rsrc((unsigned short*)a.o + qrow0 * D, qbytes);
+  const rsrc_t rl = make_rsrc(a.lse + qrow0, (unsigned)nq * 4u);
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int qi = qw + 32 * rb + l32;
@@ -648,17 +651,18 @@ template <int D>
 __global__ __launch_bounds__(F32_R * F32_S) void fwd_f32_kernel(FwdArgs a) {
   __shared__ float part[F32_R][F32_S][D + 2];  // o[0..D), m, l of each split
   const AttnShape& s = a.s;
-  const int N = s.N;
   const int tid = threadIdx.x;
   const int r = tid % F32_R, sp = tid / F32_R;  // a wave holds 8 splits of the 8 rows
   const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int hk = h / s.G;
-  const size_t qrow0 = (size_t)(b * s.H + h) * N;
-  const size_t krow0 = (size_t)(b * s.Hkv + hk) * N;
+  const SeqView sv = seq_view(s, b, h, hk);
+  const int nq = sv.nq, nk = sv.nk, off = sv.off;
+  const int q0 = qb * F32_R;
+  if (q0 >= nq) return;  // a sequence shorter than the grid (packed batches)
+  const size_t qrow0 = sv.qrow0, krow0 = sv.krow0;
   const float* Q = (const float*)a.q + qrow0 * D;
   const float* K = (const float*)a.k + krow0 * D;
   const float* V = (const float*)a.v + krow0 * D;
-  const int q0 = qb * F32_R;
   const int qi = q0 + r;
   const float c = fmaxf(s.scale * kLog2e, 1e-30f);
   const int mrow = q0 / 128;  // every row of the workgroup is in this mask block row
@@ -666,19 +670,19 @@ __global__ __launch_bounds__(F32_R * F32_S) void fwd_f32_kernel(FwdArgs a) {
   float q[D], o[D];
 #pragma unroll
   for (int dd = 0; dd < D; ++dd) {
-    q[dd] = qi < N ? Q[(size_t)qi * D + dd] : 0.f;
+    q[dd] = qi < nq ? Q[(size_t)qi * D + dd] : 0.f;
     o[dd] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
-  const int kend_row = s.causal ? min(N, qi + 1) : N;
-  const int kend = s.causal ? min(N, q0 + F32_R) : N;  // bound for the workgroup
+  const int kend_row = s.causal ? min(nk, max(0, qi + 1 + off)) : nk;
+  const int kend = s.causal ? min(nk, max(0, q0 + F32_R + off)) : nk;  // bound for the workgroup
   for (int j0 = sp * F32_C; j0 < kend; j0 += F32_S * F32_C) {
     float x[F32_C];
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < F32_C; ++t) {
       const int j = j0 + t;
-      const bool vis = j < kend_row && (!s.mask || s.mask[(size_t)mrow * s.nb + j / 128] != 0);
+      const bool vis = j < kend_row && (!s.mask || s.mask[(size_t)mrow * s.nbk + j / 128] != 0);
       float dot = 0.f;
       if (vis) {
         const float4* kr = (const float4*)(K + (size_t)j * D);
@@ -736,7 +740,7 @@ __global__ __launch_bounds__(F32_R * F32_S) void fwd_f32_kernel(FwdArgs a) {
     wgt[t] = fast_exp2(part[r][t][D] - Mu);  // 0 for a split that saw no key
     L = fmaf(part[r][t][D + 1], wgt[t], L);
   }
-  if (qi < N) {
+  if (qi < nq) {
     const float inv = L > 0.f ? 1.f / L : 0.f;
     constexpr int DS = D / F32_S;  // output columns finished by each split
     float* Op = (float*)a.o + (qrow0 + qi) * D + sp * DS;
@@ -754,12 +758,12 @@ __global__ __launch_bounds__(F32_R * F32_S) void fwd_f32_kernel(FwdArgs a) {
 template <class T, int D, bool DROP>
 static hipError_t launch_fwd_t2(const FwdArgs& a, hipStream_t st, bool causal, bool mask, bool use64) {
   if (!mask && use64) {
-    const dim3 grid(a.s.H, (a.s.N + F64_BM - 1) / F64_BM, a.s.B);
+    const dim3 grid(a.s.H, (a.s.Nq + F64_BM - 1) / F64_BM, a.s.B);
     if (causal) hipLaunchKernelGGL((fwd64_kernel<T, D, true, DROP>), grid, dim3(F64_NW * 64), 0, st, a);
     else hipLaunchKernelGGL((fwd64_kernel<T, D, false, DROP>), grid, dim3(F64_NW * 64), 0, st, a);
     return hipGetLastError();
   }
-  const dim3 grid(a.s.H, (a.s.N + FWD_BM - 1) / FWD_BM, a.s.B);
+  const dim3 grid(a.s.H, (a.s.Nq + FWD_BM - 1) / FWD_BM, a.s.B);
   const dim3 block(FWD_NW * 64);
   if (causal && mask) hipLaunchKernelGGL((fwd_kernel<T, D, true, true, DROP>), grid, block, 0, st, a);
   else if (causal) hipLaunchKernelGGL((fwd_kernel<T, D, true, false, DROP>), grid, block, 0, st, a);
@@ -778,8 +782,8 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   // tail (N = 1024: 1.8x faster with 32 rows).
   // FA_FORWARD_ROWS_PER_WAVE=64 or 32 overrides the choice (tests use it to
   // cover both kernels at every size).
-  const long long wg64 = (long long)a.s.B * a.s.H * ((a.s.N + F64_BM - 1) / F64_BM);
-  bool use64 = a.s.N >= 8192 && wg64 <= 2048;
+  const long long wg64 = (long long)a.s.B * a.s.H * ((a.s.Nq + F64_BM - 1) / F64_BM);
+  bool use64 = min(a.s.Nq, a.s.Nk) >= 8192 && wg64 <= 2048;
   if (const char* env = getenv("FA_FORWARD_ROWS_PER_WAVE")) {
     if (env[0] == '6' && env[1] == '4' && env[2] == 0) use64 = true;
     if (env[0] == '3' && env[1] == '2' && env[2] == 0) use64 = false;
@@ -790,7 +794,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
 
 template <int D>
 static hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st) {
-  const dim3 grid((a.s.N + F32_R - 1) / F32_R, a.s.H, a.s.B);
+  const dim3 grid((a.s.Nq + F32_R - 1) / F32_R, a.s.H, a.s.B);
   hipLaunchKernelGGL((fwd_f32_kernel<D>), grid, dim3(F32_R * F32_S), 0, st, a);
   return hipGetLastError();
 }

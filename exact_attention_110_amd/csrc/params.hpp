@@ -9,12 +9,20 @@
 namespace fa {
 
 struct AttnShape {
-  int B, H, Hkv, N, d;
+  int B, H, Hkv;
+  int Nq, Nk;     // query rows and keys per sequence (packed batches: the longest)
+  int d;
   int G;          // H / Hkv, query heads per kv head
   float scale;    // multiplies Q K^T
-  int causal;     // key j visible to query i only if j <= i
-  const uint8_t* mask;  // NULL or uint8 [nb][nb], nb = ceil(N / 128)
-  int nb;         // ceil(N / 128)
+  int causal;     // key j visible to query i only if j <= i + (nk - nq) of its sequence
+  const uint8_t* mask;  // NULL or uint8 [nbq][nbk] (fixed lengths only)
+  int nbq, nbk;   // ceil(Nq / 128), ceil(Nk / 128)
+  // packed variable-length batches (NULL for fixed lengths): sequence b holds
+  // rows cu_q[b] .. cu_q[b + 1] - 1 of every query head's [tq][d] plane and
+  // keys cu_k[b] .. cu_k[b + 1] - 1 of every kv head's [tk][d] plane
+  const int* cu_q;
+  const int* cu_k;
+  int tq, tk;
   // dropout on the probabilities (used only by the kernels built for it): an
   // element is kept iff its generator byte >= drop_t, and kept values are
   // multiplied by drop_scale = 256 / (256 - drop_t); the generator key is
@@ -45,11 +53,46 @@ struct BwdArgs {
   void* dk;
   void* dv;
   // workspace, [B][H][2][npad] float: plane 0 the log2-scaled LSE (+inf for a
-  // row that saw no key and for the padding rows N..npad-1), plane 1 D =
-  // rowsum(dO * O) (0 for padding rows); npad = N rounded up to 128
+  // row that saw no key and for the padding rows past the sequence), plane 1
+  // D = rowsum(dO * O) (0 for padding rows); npad = Nq rounded up to 128
   float* stats;
   int npad;
 };
+
+// One sequence of a batch as seen by a workgroup: its lengths, the causal
+// offset and where its rows start. Fixed lengths: Q is [B][H][Nq][d], K and V
+// [B][Hkv][Nk][d]. Packed batches: Q is [H][tq][d], K and V [Hkv][tk][d], with
+// the sequence's rows at cu_q[b] and cu_k[b]. The offsets read from cu_q and
+// cu_k are clamped to the planes and the lengths to Nq, Nk, so that offsets
+// that break their contract cannot move an access outside the buffers.
+struct SeqView {
+  int nq, nk;       // query rows and keys of this sequence
+  int off;          // nk - nq: a causal query i sees keys j <= i + off
+  size_t qrow0;     // first row of query head h (rows of d elements)
+  size_t krow0;     // first row of kv head hk
+  size_t qstride;   // rows from one query head to the next
+};
+
+__device__ __forceinline__ SeqView seq_view(const AttnShape& s, int b, int h, int hk) {
+  SeqView v;
+  if (s.cu_q) {
+    const int q0 = min(max(s.cu_q[b], 0), s.tq), q1 = min(max(s.cu_q[b + 1], q0), s.tq);
+    const int k0 = min(max(s.cu_k[b], 0), s.tk), k1 = min(max(s.cu_k[b + 1], k0), s.tk);
+    v.nq = min(q1 - q0, s.Nq);
+    v.nk = min(k1 - k0, s.Nk);
+    v.qrow0 = (size_t)h * s.tq + q0;
+    v.krow0 = (size_t)hk * s.tk + k0;
+    v.qstride = (size_t)s.tq;
+  } else {
+    v.nq = s.Nq;
+    v.nk = s.Nk;
+    v.qrow0 = (size_t)(b * s.H + h) * s.Nq;
+    v.krow0 = (size_t)(b * s.Hkv + hk) * s.Nk;
+    v.qstride = (size_t)s.Nq;
+  }
+  v.off = v.nk - v.nq;
+  return v;
+}
 
 // Internal launchers (return a hipError_t from the launch).
 hipError_t launch_forward(const FwdArgs& a, int dtype, hipStream_t stream);

@@ -141,10 +141,57 @@ def make_small(B, H, Hkv, N, d, dtype, seed, sigma=1.0, with_grad=True):
     return out
 
 
-def random_block_mask(n, density, seed, block=MASK_BLOCK, keep_diagonal=False):
-    """uint8 [nb, nb] mask with i.i.d. Bernoulli(density) blocks (for small tests)."""
+def random_block_mask(n, density, seed, block=MASK_BLOCK, keep_diagonal=False, n_keys=None):
+    """uint8 [ceil(n / block), ceil(n_keys / block)] mask with i.i.d.
+    Bernoulli(density) blocks (for small tests); n_keys defaults to n."""
     nb = -(-n // block)
-    m = (np.random.default_rng(seed).random((nb, nb)) < density).astype(np.uint8)
+    nbk = nb if n_keys is None else -(-n_keys // block)
+    m = (np.random.default_rng(seed).random((nb, nbk)) < density).astype(np.uint8)
     if keep_diagonal:
         np.fill_diagonal(m, 1)
     return m
+
+
+def make_cross(B, H, Hkv, Nq, Nk, d, dtype, seed, sigma=1.0, with_grad=True):
+    """Seeded inputs with Nq query rows and Nk keys (same recipe as ``make_small``):
+    q, do [B, H, Nq, d]; k, v [B, Hkv, Nk, d]."""
+    rng = np.random.default_rng(seed)
+    out = {
+        "q": round_to(draw((B, H, Nq, d), rng, sigma), dtype),
+        "k": round_to(draw((B, Hkv, Nk, d), rng, sigma), dtype),
+        "v": round_to(draw((B, Hkv, Nk, d), rng, sigma), dtype),
+    }
+    if with_grad:
+        out["do"] = round_to(draw((B, H, Nq, d), rng, sigma), dtype)
+    return out
+
+
+def offsets(lengths):
+    """int32 [len + 1] running offsets 0, l0, l0 + l1, ... of a list of lengths."""
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))]).astype(np.int32)
+
+
+def make_packed(lens_q, lens_k, H, Hkv, d, dtype, seed, sigma=1.0, with_grad=True):
+    """Seeded packed variable-length inputs: sequence b has lens_q[b] query rows
+    and lens_k[b] keys, stored one after another per head (q, do [H, Tq, d];
+    k, v [Hkv, Tk, d]); also returns the offsets cu_q, cu_k (int32 numpy)."""
+    rng = np.random.default_rng(seed)
+    cu_q, cu_k = offsets(lens_q), offsets(lens_k)
+    tq, tk = int(cu_q[-1]), int(cu_k[-1])
+    out = {
+        "q": round_to(draw((H, tq, d), rng, sigma), dtype),
+        "k": round_to(draw((Hkv, tk, d), rng, sigma), dtype),
+        "v": round_to(draw((Hkv, tk, d), rng, sigma), dtype),
+        "cu_q": cu_q,
+        "cu_k": cu_k,
+    }
+    if with_grad:
+        out["do"] = round_to(draw((H, tq, d), rng, sigma), dtype)
+    return out
+
+
+def length_mix(batch, mean, seed, lo=1):
+    """A batch of sequence lengths with a document-like spread: lengths drawn
+    from an exponential distribution of the given mean, at least lo."""
+    x = np.random.default_rng(seed).exponential(mean, size=batch)
+    return [max(lo, int(round(v))) for v in x]

@@ -174,6 +174,73 @@ int fa_backward_stage_dropout(int stage, const void* q, const void* k, const voi
                               float dropout_rate, unsigned long long seed,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Unequal query and key lengths (chipfoundryservices.com glossary "flash
+ * attention algorithm", "Inference Optimization": attention beside a KV cache,
+ * where a few new queries meet many cached keys). The Nq queries are read as
+ * the last Nq positions of a sequence of Nk keys, so under causal masking key
+ * j is visible to query i iff j <= i + (Nk - Nq) ("bottom-right" alignment;
+ * the pages do not fix it, this is the reading that fits a KV cache). With
+ * Nq > Nk the first Nq - Nk queries see no key (O = 0, LSE = -inf, zero
+ * gradients). Nq == Nk is exactly fa_forward / fa_backward.
+ *   q, o, dO, dq : [B][H][Nq][d]       k, v, dk, dv : [B][Hkv][Nk][d]
+ *   lse          : [B][H][Nq] float32
+ *   block_mask   NULL or uint8 [ceil(Nq/128)][ceil(Nk/128)] (both <= 2048)
+ *   workspace    fa_backward_workspace_size(B, H, Hkv, Nq, d, dtype) bytes
+ * dropout_rate 0 is no dropout; dropout otherwise as described above. Other
+ * arguments, limits (each of Nq and Nk as N), ownership and errors as for
+ * fa_forward / fa_backward.
+ */
+int fa_forward_qk(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                  const uint8_t* block_mask, int dtype,
+                  float dropout_rate, unsigned long long seed, void* stream);
+int fa_backward_qk(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                   int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                   const uint8_t* block_mask, int dtype,
+                   float dropout_rate, unsigned long long seed,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Packed variable-length batches (the same glossary, "Sequence Length
+ * Flexibility": any lengths, no padding). B sequences are stored one after
+ * another per head, with no padding between them:
+ *   q, o, dO, dq : [H][total_q][d]     k, v, dk, dv : [Hkv][total_k][d]
+ *   lse          : [H][total_q] float32
+ * Sequence b holds query rows cu_seqlens_q[b] .. cu_seqlens_q[b + 1] - 1 and
+ * keys cu_seqlens_k[b] .. cu_seqlens_k[b + 1] - 1 of every head; each is an
+ * independent attention problem (causal alignment as for fa_forward_qk, with
+ * the sequence's own lengths; a sequence may have no queries or no keys).
+ *   cu_seqlens_q, cu_seqlens_k   device int32 [B + 1], 4-byte aligned, rising
+ *                                from 0 to total_q / total_k
+ *   max_seqlen_q, max_seqlen_k   >= 1 and >= every sequence's length; the
+ *                                launch grid and the limits (as N) use these
+ *   total_q, total_k             >= 0, rows of each head's plane
+ *   workspace                    fa_backward_workspace_size(B, H, Hkv,
+ *                                max_seqlen_q, d, dtype) bytes
+ * Dropout draws stream b * H + h for query head h of sequence b, indexed by
+ * positions within the sequence. No block mask. The offsets live in device
+ * memory and are not checked by the host; the kernels clamp them to the
+ * planes and the lengths to max_seqlen_*, so offsets that break the contract
+ * give wrong results but no access outside the buffers. Other arguments,
+ * ownership and errors as for fa_forward / fa_backward; FA_ERR_INVALID_ARG
+ * also for a NULL or misaligned offset array, H * total_q or Hkv * total_k of
+ * 2^31 or more.
+ */
+int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const int* cu_seqlens_q, const int* cu_seqlens_k,
+                      int B, int H, int Hkv, int total_q, int total_k,
+                      int max_seqlen_q, int max_seqlen_k, int d, float scale, int causal,
+                      int dtype, float dropout_rate, unsigned long long seed, void* stream);
+int fa_backward_varlen(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                       const int* cu_seqlens_q, const int* cu_seqlens_k,
+                       int B, int H, int Hkv, int total_q, int total_k,
+                       int max_seqlen_q, int max_seqlen_k, int d, float scale, int causal,
+                       int dtype, float dropout_rate, unsigned long long seed,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* fa_status_string: a static, human-readable description of a status code. */
 const char* fa_status_string(int status);
 

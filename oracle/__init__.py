@@ -33,5 +33,7 @@ from .attention import (  # noqa: F401
     head_backward,
     forward,
     backward,
+    forward_varlen,
+    backward_varlen,
 )
 from . import dropout  # noqa: F401

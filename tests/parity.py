@@ -107,3 +107,51 @@ def run_given(x, dtype, causal, mask=None, backward=True, scale=None, where="", 
         res["dk"] = check_grad(np64(dk), rk, where + " dk")
         res["dv"] = check_grad(np64(dv), rv, where + " dv")
     return res
+
+
+def run_cross(B, H, Hkv, Nq, Nk, d, dtype, causal, mask=None, seed=0, backward=True, dropout_rate=0.0,
+              drop_seed=0):
+    """Full comparison for Nq query rows over Nk keys (fa_forward_qk / fa_backward_qk)."""
+    where = (f"B{B} H{H} Hkv{Hkv} Nq{Nq} Nk{Nk} d{d} {dtype} causal={causal} mask={mask is not None} "
+             f"seed={seed}")
+    if dropout_rate:
+        where += f" dropout={dropout_rate} drop_seed={drop_seed}"
+    x = I.make_cross(B, H, Hkv, Nq, Nk, d, dtype, seed, with_grad=backward)
+    return run_given(x, dtype, causal, mask, backward, None, where, dropout_rate=dropout_rate,
+                     drop_seed=drop_seed)
+
+
+def run_varlen(lens_q, lens_k, H, Hkv, d, dtype, causal, seed=0, backward=True, dropout_rate=0.0,
+               drop_seed=0, max_q=None, max_k=None):
+    """Full comparison for a packed variable-length batch (fa_forward_varlen /
+    fa_backward_varlen) against the oracle's per-sequence attention."""
+    where = (f"lens_q={list(lens_q)} lens_k={list(lens_k)} H{H} Hkv{Hkv} d{d} {dtype} causal={causal} "
+             f"seed={seed}")
+    if dropout_rate:
+        where += f" dropout={dropout_rate} drop_seed={drop_seed}"
+    say("case", where)
+    x = I.make_packed(lens_q, lens_k, H, Hkv, d, dtype, seed, with_grad=backward)
+    dev = torch.device("cuda", 0)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    cq = torch.from_numpy(x["cu_q"]).to(dev)
+    ck = torch.from_numpy(x["cu_k"]).to(dev)
+    mq = max(1, max(lens_q)) if max_q is None else max_q
+    mk = max(1, max(lens_k)) if max_k is None else max_k
+    scale = 1.0 / math.sqrt(d)
+    o, lse = binding.forward_varlen(q, k, v, cq, ck, mq, mk, scale, causal, dropout_rate=dropout_rate,
+                                    seed=drop_seed)
+    torch.cuda.synchronize()
+    qd, kd, vd = (np64(x[n]) for n in ("q", "k", "v"))
+    oref, lref = oracle.forward_varlen(qd, kd, vd, x["cu_q"], x["cu_k"], scale, causal, dropout_rate, drop_seed)
+    res = {"o": check_out(np64(o), oref, dtype, where), "lse": check_lse(np64(lse), lref, where)}
+    if backward and dtype != "fp32":
+        do = x["do"].to(dev)
+        dq, dk, dv = binding.backward_varlen(q, k, v, o, lse, do, cq, ck, mq, mk, scale, causal,
+                                             dropout_rate=dropout_rate, seed=drop_seed)
+        torch.cuda.synchronize()
+        rq, rk, rv = oracle.backward_varlen(qd, kd, vd, np64(x["do"]), x["cu_q"], x["cu_k"], scale, causal,
+                                            dropout_rate, drop_seed)
+        res["dq"] = check_grad(np64(dq), rq, where + " dq")
+        res["dk"] = check_grad(np64(dk), rk, where + " dk")
+        res["dv"] = check_grad(np64(dv), rv, where + " dv")
+    return res

@@ -48,7 +48,8 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"fa_forward", "fa_backward", "fa_backward_workspace_size", "fa_backward_stage",
             "fa_status_string", "fa_version", "fa_forward_dropout", "fa_backward_dropout",
-            "fa_backward_stage_dropout"} <= set(names)
+            "fa_backward_stage_dropout", "fa_forward_qk", "fa_backward_qk", "fa_forward_varlen",
+            "fa_backward_varlen"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -162,3 +163,61 @@ def test_dropout_argument_order(lib):
     assert fwd_drop(lib, 0.5, d=16) == EINVAL          # bad shape reported first
     assert bwd_drop(lib, 0.5, dtype=F32) == EUNSUP
     assert bwd_drop(lib, 0.2, stage=3) == EINVAL
+
+
+def fwd_qk(lib, Nq=256, Nk=512, d=64, mask=None, dtype=BF16, rate=0.0, B=1, H=2, Hkv=1):
+    return lib.fa_forward_qk(GOOD, GOOD, GOOD, GOOD, GOOD, B, H, Hkv, Nq, Nk, d, 0.125, 1, mask, dtype, rate, 3,
+                             None)
+
+
+def bwd_qk(lib, Nq=256, Nk=512, d=64, mask=None, dtype=BF16, ws_bytes=None, rate=0.0):
+    if ws_bytes is None:
+        ws_bytes = ws_size(lib, N=Nq, d=d)
+    return lib.fa_backward_qk(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 1, 2, 1, Nq, Nk, d, 0.125, 1,
+                              mask, dtype, rate, 3, GOOD, ws_bytes, None)
+
+
+@pytest.mark.parametrize("bad", [dict(Nq=0), dict(Nk=0), dict(Nk=-3), dict(d=48), dict(rate=1.0),
+                                 dict(Nq=1 << 23, d=128), dict(Nk=1 << 23, d=128), dict(B=1 << 16),
+                                 dict(H=3, Hkv=2)])
+def test_forward_qk_rejects(lib, bad):
+    assert fwd_qk(lib, **bad) == EINVAL
+
+
+def test_qk_mask_and_workspace(lib):
+    # a mask longer than the on-chip lists on either side is unsupported
+    assert fwd_qk(lib, Nq=256, Nk=2049 * 128, mask=GOOD) == EUNSUP
+    assert fwd_qk(lib, Nq=2049 * 128, Nk=256, mask=GOOD) == EUNSUP
+    assert bwd_qk(lib, Nq=256, Nk=2049 * 128, mask=GOOD) == EUNSUP
+    # the backward workspace follows the query length
+    assert bwd_qk(lib, Nq=256, Nk=4096, ws_bytes=ws_size(lib, N=256) - 1) == EWS
+    assert bwd_qk(lib, Nq=1000, Nk=10, ws_bytes=ws_size(lib, N=10)) == EWS
+    assert bwd_qk(lib, dtype=F32) == EUNSUP
+
+
+def fwd_var(lib, cu_q=GOOD, cu_k=GOOD, B=3, H=2, Hkv=1, tq=100, tk=200, mq=50, mk=90, d=64, dtype=BF16,
+            rate=0.0):
+    return lib.fa_forward_varlen(GOOD, GOOD, GOOD, GOOD, GOOD, cu_q, cu_k, B, H, Hkv, tq, tk, mq, mk, d, 0.125, 1,
+                                 dtype, rate, 0, None)
+
+
+def bwd_var(lib, cu_q=GOOD, cu_k=GOOD, mq=50, ws_bytes=None, dtype=BF16, tq=100):
+    if ws_bytes is None:
+        ws_bytes = ws_size(lib, B=3, N=mq)
+    return lib.fa_backward_varlen(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, cu_q, cu_k, 3, 2, 1, tq,
+                                  200, mq, 90, 64, 0.125, 1, dtype, 0.0, 0, GOOD, ws_bytes, None)
+
+
+@pytest.mark.parametrize("bad", [dict(cu_q=None), dict(cu_k=None), dict(cu_q=P((1 << 20) + 2)),
+                                 dict(cu_k=P((1 << 20) + 1)), dict(tq=-1), dict(tk=-5), dict(mq=0), dict(mk=0),
+                                 dict(B=0), dict(d=16), dict(H=1 << 16, tq=1 << 15), dict(rate=-0.5),
+                                 dict(dtype=7)])
+def test_forward_varlen_rejects(lib, bad):
+    assert fwd_var(lib, **bad) == EINVAL
+
+
+def test_varlen_backward_checks(lib):
+    assert bwd_var(lib, cu_q=None) == EINVAL
+    assert bwd_var(lib, dtype=F32) == EUNSUP
+    assert bwd_var(lib, ws_bytes=ws_size(lib, B=3, N=50) - 1) == EWS
+    assert bwd_var(lib, mq=0) == EINVAL
