@@ -8,7 +8,14 @@ N x N x d contraction, two contractions forward and five backward (the
 recomputed QK^T included), halved for causal masking.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--copy-mb MB]
+                       [--no-cpu-baseline] [--copy-mb MB] [--dropout RATE] [--packed]
+
+--packed splits the workload's B * N tokens per head into a seeded
+document-like mix of sequence lengths and times the packed variable-length
+calls (fa_forward_varlen, fa_backward_varlen), with the same batch padded to
+its longest sequence and run through the fixed-length calls beside it; FLOP
+are counted per sequence (n^2 d per contraction under causal masking). It is
+not the headline configuration.
 
 Prints one JSON line. Besides the headline it carries:
 * "roofline": the dominant kernel's algorithmic FLOP per launch over its mean
@@ -94,6 +101,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="run the fused-dropout kernels at this rate (not the headline configuration)")
+    ap.add_argument("--packed", action="store_true",
+                    help="time packed variable-length batches of the workload's tokens (not the headline)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after timing, run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -145,6 +154,8 @@ def main():
     from exact_attention_110_amd import inputs as I
 
     w = I.WORKLOADS[args.workload]
+    if args.packed:
+        return packed_main(args, w)
     dev = torch.device("cuda", 0)
     x = I.make(w)
     q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
@@ -245,6 +256,123 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(line), flush=True)
+
+
+def packed_lengths(total, mean, seed):
+    """Exponential lengths of the given mean (at least 16) until they sum to total."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    out = []
+    while sum(out) < total:
+        out.append(max(16, int(round(rng.exponential(mean)))))
+    out[-1] -= sum(out) - total
+    if out[-1] < 1:
+        out.pop()
+        out[-1] += total - sum(out)
+    return out
+
+
+def packed_main(args, w):
+    """Packed variable-length batch of the workload's tokens against the same
+    sequences padded to the longest one."""
+    import torch
+    from exact_attention_110_amd import binding
+    from exact_attention_110_amd import inputs as I
+
+    if w.sparse or w.dtype == "fp32":
+        print("--packed needs a dense 16-bit workload", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda", 0)
+    lens = packed_lengths(w.B * w.N, w.N / 8, w.seed + 300)
+    x = I.make_packed(lens, lens, w.H, w.Hkv, w.d, w.dtype, w.seed, with_grad=True)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    cu = torch.from_numpy(x["cu_q"]).to(dev)
+    mx = max(lens)
+    o, lse = torch.empty_like(q), torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    ws = torch.empty(binding.workspace_size(len(lens), w.H, w.Hkv, mx, w.d, q.dtype), dtype=torch.uint8,
+                     device=dev)
+    per_seq = sum(2.0 * n * n * w.d * w.H * (0.5 if w.causal else 1.0) for n in lens)
+    total_flop = 7 * per_seq
+
+    def fwd():
+        binding.forward_varlen(q, k, v, cu, cu, mx, mx, w.scale, w.causal, out=o, lse=lse)
+
+    def bwd():
+        binding.backward_varlen(q, k, v, o, lse, do, cu, cu, mx, mx, w.scale, w.causal, ws=ws, grads=grads)
+
+    # the same sequences padded to the longest one, through the fixed-length calls
+    B = len(lens)
+    qp = torch.zeros((B, w.H, mx, w.d), dtype=q.dtype, device=dev)
+    kp = torch.zeros((B, w.Hkv, mx, w.d), dtype=q.dtype, device=dev)
+    vp, dop = torch.zeros_like(kp), torch.zeros_like(qp)
+    for b, (a, n) in enumerate(zip(x["cu_q"][:-1].tolist(), lens)):
+        qp[b, :, :n] = q[:, a:a + n]
+        kp[b, :, :n] = k[:, a:a + n]
+        vp[b, :, :n] = v[:, a:a + n]
+        dop[b, :, :n] = do[:, a:a + n]
+    op, lp = torch.empty_like(qp), torch.empty(qp.shape[:3], dtype=torch.float32, device=dev)
+    gp = (torch.empty_like(qp), torch.empty_like(kp), torch.empty_like(vp))
+    wsp = binding.workspace(qp, kp)
+
+    def step_padded():
+        binding.forward(qp, kp, vp, w.scale, w.causal, None, out=op, lse=lp)
+        binding.backward(qp, kp, vp, op, lp, dop, w.scale, w.causal, None, ws=wsp, grads=gp)
+
+    def timed(fn, n):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(n):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / n
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    value = total_flop / (ms * 1e-3) / 1e12
+    t_fwd = timed(fwd, max(args.steps, 5))
+    t_bwd = timed(bwd, max(args.steps, 5))
+    t_pad = timed(step_padded, max(args.steps, 5))
+    print(f"[bench] packed {w.name}: {len(lens)} sequences (longest {mx}), {ms:.3f} ms/step, {value:.1f} TFLOP/s; "
+          f"padded to the longest: {t_pad:.3f} ms/step", file=sys.stderr, flush=True)
+    achieved = 2 * per_seq / (t_fwd * 1e-3) / 1e12
+    line = {
+        "metric": "packed variable-length attention fwd+bwd TFLOP/s (per-sequence FLOP)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name + "_packed", "sequences": len(lens), "tokens_per_head": w.B * w.N,
+                   "longest": mx, "H": w.H, "Hkv": w.Hkv, "d": w.d, "causal": w.causal,
+                   "length_mix": f"exponential, mean {w.N // 8}, at least 16, seed {w.seed + 300}",
+                   "flop_per_step": total_flop, "padded_ms_per_step": round(t_pad, 4),
+                   "fwd_ms": round(t_fwd, 4), "bwd_ms": round(t_bwd, 4)},
+        "roofline": {"bound": "mfma", "kernel": "forward (one launch)", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "launch_ms": round(t_fwd, 4), "flop_per_launch": 2 * per_seq},
+    }
     print(json.dumps(line), flush=True)
 
 
