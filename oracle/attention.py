@@ -24,6 +24,13 @@ Sources (cited by page title and section):
   glossary "flash attention algorithm", "Inference Optimization": attention
   run beside a KV cache), so key j is visible to query i iff
   j <= i + (Nk - Nq); rows with i + (Nk - Nq) < 0 see no key.
+* Sliding-window (local) masks: the lesson's Researcher tier, "Beyond
+  hand-written kernels" (one tiled kernel serving many masks) and its pointer
+  to sparse and block attention patterns. Read here as a band
+  window = (left, right) around the query's position p = i + (Nk - Nq): key j
+  is visible iff p - left <= j <= p + right, -1 meaning unbounded on that
+  side; causal masking is the right bound 0. Band, causal and block masks
+  combine by intersection.
 * Variable-length batches: the same glossary, "Sequence Length Flexibility"
   (arbitrary lengths, no padding). Read here as sequences packed one after
   another per head, each attending only within itself
@@ -48,24 +55,31 @@ from . import dropout as _dropout
 MASK_BLOCK = 128  # block-mask granularity in rows and columns
 
 
-def visible(rows, keys, causal, block_mask, block=MASK_BLOCK, offset=0):
+def visible(rows, keys, causal, block_mask, block=MASK_BLOCK, offset=0, window=(-1, -1)):
     """Boolean matrix a[r, c]: is key ``keys[c]`` visible to query ``rows[r]``.
 
-    Causal: j <= i + offset (offset = Nk - Nq, 0 for square attention). Block
-    mask: mask[i // block][j // block] != 0. Both, when given, must hold.
+    Causal: j <= i + offset (offset = Nk - Nq, 0 for square attention). Window
+    (left, right): i + offset - left <= j <= i + offset + right, a negative
+    bound unbounded. Block mask: mask[i // block][j // block] != 0. All that
+    are given must hold.
     """
     rows = np.asarray(rows, dtype=np.int64)
     keys = np.asarray(keys, dtype=np.int64)
     a = np.ones((rows.size, keys.size), dtype=bool)
     if causal:
         a &= keys[None, :] <= rows[:, None] + offset
+    left, right = window
+    if left >= 0:
+        a &= keys[None, :] >= rows[:, None] + offset - left
+    if right >= 0:
+        a &= keys[None, :] <= rows[:, None] + offset + right
     if block_mask is not None:
         bm = np.asarray(block_mask) != 0
         a &= bm[(rows // block)[:, None], (keys // block)[None, :]]
     return a
 
 
-def candidate_keys(rows, n_keys, causal, block_mask, block=MASK_BLOCK, offset=0):
+def candidate_keys(rows, n_keys, causal, block_mask, block=MASK_BLOCK, offset=0, window=(-1, -1)):
     """Keys that at least one of ``rows`` may see (a superset used to gather K, V).
 
     Keys outside this set are invisible to every row of the chunk, so leaving
@@ -77,6 +91,10 @@ def candidate_keys(rows, n_keys, causal, block_mask, block=MASK_BLOCK, offset=0)
         return keys[:0]
     if causal:
         keys = keys[keys <= rows.max() + offset]
+    if window[0] >= 0:
+        keys = keys[keys >= rows.min() + offset - window[0]]
+    if window[1] >= 0:
+        keys = keys[keys <= rows.max() + offset + window[1]]
     if block_mask is not None:
         bm = np.asarray(block_mask) != 0
         any_row = bm[np.unique(rows // block)].any(axis=0)
@@ -110,7 +128,7 @@ def _row_softmax(q_rows, k_keys, scale, vis):
     return s, p, lse
 
 
-def head_probabilities(q, k, scale, causal=False, block_mask=None, rows=None):
+def head_probabilities(q, k, scale, causal=False, block_mask=None, rows=None, window=(-1, -1)):
     """Full probability rows P[rows, :] (Nk keys wide) of one query head.
 
     q: [Nq, d] float64 query rows of the head, k: [Nk, d] keys of its kv head.
@@ -118,7 +136,7 @@ def head_probabilities(q, k, scale, causal=False, block_mask=None, rows=None):
     n = k.shape[0]
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
     keys = np.arange(n)
-    vis = visible(rows, keys, causal, block_mask, offset=n - q.shape[0])
+    vis = visible(rows, keys, causal, block_mask, offset=n - q.shape[0], window=window)
     _, p, lse = _row_softmax(q[rows], k, scale, vis)
     return p, lse
 
@@ -134,7 +152,8 @@ def _drop(p, rows, keys, dropout):
     return np.where(z, p * _dropout.keep_scale(rate), 0.0)
 
 
-def head_forward(q, k, v, scale, causal=False, block_mask=None, rows=None, chunk=256, dropout=None):
+def head_forward(q, k, v, scale, causal=False, block_mask=None, rows=None, chunk=256, dropout=None,
+                 window=(-1, -1)):
     """O and L for the given query rows of one head (q: [Nq, d], k, v: [Nk, d]).
 
     With dropout = (rate, seed, bh) the probabilities are dropped and rescaled
@@ -146,9 +165,9 @@ def head_forward(q, k, v, scale, causal=False, block_mask=None, rows=None, chunk
     lse = np.full(rows.size, -np.inf)
     pos = 0
     for ch in _chunks(rows, chunk):
-        keys = candidate_keys(ch, n, causal, block_mask, offset=off)
+        keys = candidate_keys(ch, n, causal, block_mask, offset=off, window=window)
         if keys.size:
-            vis = visible(ch, keys, causal, block_mask, offset=off)
+            vis = visible(ch, keys, causal, block_mask, offset=off, window=window)
             _, p, l_ = _row_softmax(q[ch], k[keys], scale, vis)
             o[pos:pos + ch.size] = _drop(p, ch, keys, dropout) @ v[keys]
             lse[pos:pos + ch.size] = l_
@@ -156,7 +175,7 @@ def head_forward(q, k, v, scale, causal=False, block_mask=None, rows=None, chunk
     return o, lse
 
 
-def head_backward(q, k, v, do, scale, causal=False, block_mask=None, chunk=256, dropout=None):
+def head_backward(q, k, v, do, scale, causal=False, block_mask=None, chunk=256, dropout=None, window=(-1, -1)):
     """Gradients of sum(O * dO) for one query head.
 
     With p the probability rows, g = dO, and (under dropout) r the dropped and
@@ -178,10 +197,10 @@ def head_backward(q, k, v, do, scale, causal=False, block_mask=None, chunk=256, 
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     for ch in _chunks(rows, chunk):
-        keys = candidate_keys(ch, n, causal, block_mask, offset=off)
+        keys = candidate_keys(ch, n, causal, block_mask, offset=off, window=window)
         if keys.size == 0:
             continue
-        vis = visible(ch, keys, causal, block_mask, offset=off)
+        vis = visible(ch, keys, causal, block_mask, offset=off, window=window)
         _, p, _ = _row_softmax(q[ch], k[keys], scale, vis)
         g = do[ch]
         dv[keys] += _drop(p, ch, keys, dropout).T @ g
@@ -200,7 +219,7 @@ def _heads(B, H, heads):
 
 
 def forward(q, k, v, scale, causal=False, block_mask=None, heads=None, rows=None, chunk=256,
-            dropout_rate=0.0, seed=0):
+            dropout_rate=0.0, seed=0, window=(-1, -1)):
     """Attention forward over [B, H, Nq, d] queries and [B, Hkv, Nk, d] keys/values.
 
     Query head h reads kv head h // (H // Hkv). A block mask has
@@ -219,7 +238,8 @@ def forward(q, k, v, scale, causal=False, block_mask=None, heads=None, rows=None
     outs, lses = [], []
     for b, h in hl:
         dr = (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None
-        o, l_ = head_forward(q[b, h], k[b, h // G], v[b, h // G], scale, causal, block_mask, rows, chunk, dr)
+        o, l_ = head_forward(q[b, h], k[b, h // G], v[b, h // G], scale, causal, block_mask, rows, chunk, dr,
+                             window)
         outs.append(o)
         lses.append(l_)
     o = np.stack(outs)
@@ -231,7 +251,7 @@ def forward(q, k, v, scale, causal=False, block_mask=None, heads=None, rows=None
 
 
 def backward(q, k, v, do, scale, causal=False, block_mask=None, heads=None, chunk=256,
-             dropout_rate=0.0, seed=0):
+             dropout_rate=0.0, seed=0, window=(-1, -1)):
     """Gradients of sum(O * dO) with respect to q, k, v (dropout as in ``forward``).
 
     With ``heads=None`` returns full dq [B, H, Nq, d], dk, dv [B, Hkv, Nk, d]
@@ -252,13 +272,13 @@ def backward(q, k, v, do, scale, causal=False, block_mask=None, heads=None, chun
             for h in range(H):
                 dr = (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None
                 a, bk, bv = head_backward(q[b, h], k[b, h // G], v[b, h // G], do[b, h],
-                                          scale, causal, block_mask, chunk, dr)
+                                          scale, causal, block_mask, chunk, dr, window)
                 dq[b, h] = a
                 dk[b, h // G] += bk
                 dv[b, h // G] += bv
         return dq, dk, dv
     res = [head_backward(q[b, h], k[b, h // G], v[b, h // G], do[b, h], scale, causal, block_mask, chunk,
-                         (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None)
+                         (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None, window)
            for b, h in _heads(B, H, heads)]
     return tuple(np.stack(x) for x in zip(*res))
 
@@ -270,7 +290,7 @@ def _spans(cu, total):
     return [(int(a), int(b)) for a, b in zip(cu[:-1], cu[1:])]
 
 
-def forward_varlen(q, k, v, cu_q, cu_k, scale, causal=False, dropout_rate=0.0, seed=0):
+def forward_varlen(q, k, v, cu_q, cu_k, scale, causal=False, dropout_rate=0.0, seed=0, window=(-1, -1)):
     """Attention over packed variable-length sequences.
 
     q: [H, Tq, d], k, v: [Hkv, Tk, d]: per head, the rows of every sequence one
@@ -296,11 +316,11 @@ def forward_varlen(q, k, v, cu_q, cu_k, scale, causal=False, dropout_rate=0.0, s
         for h in range(H):
             dr = (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None
             o[h, q0:q1], lse[h, q0:q1] = head_forward(q[h, q0:q1], k[h // G, k0:k1], v[h // G, k0:k1], scale,
-                                                      causal, None, None, 256, dr)
+                                                      causal, None, None, 256, dr, window)
     return o, lse
 
 
-def backward_varlen(q, k, v, do, cu_q, cu_k, scale, causal=False, dropout_rate=0.0, seed=0):
+def backward_varlen(q, k, v, do, cu_q, cu_k, scale, causal=False, dropout_rate=0.0, seed=0, window=(-1, -1)):
     """Gradients of sum(O * dO) for ``forward_varlen``: dq [H, Tq, d],
     dk, dv [Hkv, Tk, d] (summed over each kv head's group of query heads)."""
     H, Tq, d = q.shape
@@ -318,7 +338,7 @@ def backward_varlen(q, k, v, do, cu_q, cu_k, scale, causal=False, dropout_rate=0
         for h in range(H):
             dr = (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None
             a, bk, bv = head_backward(q[h, q0:q1], k[h // G, k0:k1], v[h // G, k0:k1], do[h, q0:q1], scale,
-                                      causal, None, 256, dr)
+                                      causal, None, 256, dr, window)
             dq[h, q0:q1] = a
             dk[h // G, k0:k1] += bk
             dv[h // G, k0:k1] += bv

@@ -675,10 +675,147 @@ def pin_varlen_dropout_streams():
     assert np.abs(lv - l_.transpose(1, 0, 2).reshape(H, B * n)).max() <= 1e-15
 
 
+# ----------------------------------------------------------------------------------------------
+# P-17: sliding-window (band) masks: p - left <= j <= p + right around the query's position p
+# ----------------------------------------------------------------------------------------------
+def _window_brute_force(q, k, v, scale, causal, left, right):
+    nq, nk, dv = len(q), len(k), len(v[0])
+    outs, lses = [], []
+    for i in range(nq):
+        pos = i + nk - nq
+        keys = []
+        for j in range(nk):
+            if causal and j > pos:
+                continue
+            if left >= 0 and j < pos - left:
+                continue
+            if right >= 0 and j > pos + right:
+                continue
+            keys.append(j)
+        if not keys:
+            outs.append([0.0] * dv)
+            lses.append(-math.inf)
+            continue
+        sc = [scale * sum(a * b for a, b in zip(q[i], k[j])) for j in keys]
+        mx = max(sc)
+        w = [math.exp(x - mx) for x in sc]
+        z = sum(w)
+        outs.append([sum(w[a] * v[j][t] for a, j in enumerate(keys)) / z for t in range(dv)])
+        lses.append(mx + math.log(z))
+    return np.array(outs), np.array(lses)
+
+
+def pin_window_brute_force():
+    seed = 800
+    for nq, nk in ((1, 1), (3, 3), (5, 5), (2, 6), (6, 3)):
+        for left, right in ((-1, -1), (0, 0), (1, 0), (2, 1), (-1, 2), (3, -1), (0, -1)):
+            for causal in (False, True):
+                seed += 1
+                q, k, v = _rand((nq, 3), seed), _rand((nk, 3), seed + 50), _rand((nk, 2), seed + 90)
+                o, l_ = A.forward(q[None, None], k[None, None], v[None, None], 0.8, causal, window=(left, right))
+                ob, lb = _window_brute_force(q.tolist(), k.tolist(), v.tolist(), 0.8, causal, left, right)
+                assert np.abs(o[0, 0] - ob).max() <= 1e-12, (nq, nk, left, right, causal)
+                assert np.array_equal(np.isinf(l_[0, 0]), np.isinf(lb))
+                fin = np.isfinite(lb)
+                assert np.abs(l_[0, 0][fin] - lb[fin]).max(initial=0.0) <= 1e-12
+
+
+def pin_window_torch_sdpa():
+    """Against PyTorch's float64 CPU attention with an explicit boolean mask
+    written out element by element, gradients through autograd."""
+    import torch
+    import torch.nn.functional as F
+    for (B, H, Hkv, nq, nk, d, causal, left, right, seed) in [
+            (1, 2, 2, 150, 150, 8, True, 40, 0, 811), (2, 4, 2, 90, 200, 8, False, 17, 5, 812),
+            (1, 2, 1, 200, 70, 4, True, 0, -1, 813), (1, 1, 1, 257, 257, 16, False, 128, 128, 814)]:
+        q, k, v = _rand((B, H, nq, d), seed), _rand((B, Hkv, nk, d), seed + 1), _rand((B, Hkv, nk, d), seed + 2)
+        g = _rand((B, H, nq, d), seed + 3)
+        allow = np.zeros((nq, nk), dtype=bool)
+        for i in range(nq):
+            pos = i + nk - nq
+            for j in range(nk):
+                ok = (not causal or j <= pos) and (left < 0 or j >= pos - left) and (right < 0 or j <= pos + right)
+                allow[i, j] = ok
+        rows_any = allow.any(axis=1)
+        G = H // Hkv
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        kk, vv = tk.repeat_interleave(G, dim=1), tv.repeat_interleave(G, dim=1)
+        # torch returns NaN for rows with no visible key; those rows are checked separately
+        to = F.scaled_dot_product_attention(tq, kk, vv, attn_mask=torch.tensor(allow), scale=0.3)
+        to = torch.where(torch.tensor(rows_any)[:, None], to, torch.zeros_like(to))
+        to.backward(torch.tensor(g))
+        o, l_ = A.forward(q, k, v, 0.3, causal, window=(left, right))
+        dq, dk, dv = A.backward(q, k, v, g, 0.3, causal, window=(left, right))
+        assert np.abs(o - to.detach().numpy()).max() <= 1e-12
+        assert np.all(o[:, :, ~rows_any] == 0) and np.all(np.isneginf(l_[:, :, ~rows_any]))
+        for a, b in ((dq, tq), (dk, tk), (dv, tv)):
+            gr = np.nan_to_num(b.grad.numpy())
+            assert np.abs(a - gr).max() <= 1e-12
+        s = (torch.tensor(q) @ torch.tensor(np.repeat(k, G, axis=1)).transpose(-1, -2) * 0.3)
+        s = s.masked_fill(~torch.tensor(allow), float("-inf"))
+        ref = torch.logsumexp(s, dim=-1).numpy()
+        assert np.abs(l_[:, :, rows_any] - ref[:, :, rows_any]).max() <= 1e-12
+
+
+def pin_window_limits():
+    n, d = 300, 5
+    q, k, v, g = (_rand((1, 2, n, d), s) for s in (821, 822, 823, 824))
+    # a band wider than the sequence changes nothing; (-1, 0) is causal masking
+    for causal in (False, True):
+        o, l_ = A.forward(q, k, v, 0.5, causal)
+        o2, l2 = A.forward(q, k, v, 0.5, causal, window=(n, n))
+        assert np.array_equal(o, o2) and np.array_equal(l_, l2)
+    o, l_ = A.forward(q, k, v, 0.5, True)
+    o2, l2 = A.forward(q, k, v, 0.5, False, window=(-1, 0))
+    assert np.array_equal(o, o2) and np.array_equal(l_, l2)
+    # (0, 0): each query sees exactly its own key
+    o, l_ = A.forward(q, k, v, 0.5, False, window=(0, 0))
+    assert np.abs(o - v).max() <= 1e-15
+    assert np.abs(l_ - 0.5 * (q * k).sum(-1)).max() <= 1e-13
+    dq, dk, dv = A.backward(q, k, v, g, 0.5, False, window=(0, 0))
+    assert np.abs(dv - g).max() <= 1e-15 and np.abs(dq).max() <= 1e-15 and np.abs(dk).max() <= 1e-15
+    # (1, 0) with causal: two keys per row but row 0, the sigmoid closed form
+    o, _ = A.forward(q, k, v, 0.5, True, window=(1, 0))
+    i = 7
+    s0, s1 = 0.5 * q[0, 0, i] @ k[0, 0, i - 1], 0.5 * q[0, 0, i] @ k[0, 0, i]
+    sig = 1.0 / (1.0 + math.exp(s1 - s0))
+    assert np.abs(o[0, 0, i] - (sig * v[0, 0, i - 1] + (1 - sig) * v[0, 0, i])).max() <= 1e-14
+
+
+def pin_window_finite_differences():
+    def case(nq, nk, causal, window, seed, bm=None):
+        q = _rand((1, 2, nq, 3), seed)
+        k = _rand((1, 1, nk, 3), seed + 1)
+        v = _rand((1, 1, nk, 3), seed + 2)
+        g = _rand((1, 2, nq, 3), seed + 3)
+
+        def f(q_, k_, v_):
+            o, _ = A.forward(q_, k_, v_, 0.6, causal, bm, window=window)
+            return float((o * g).sum())
+
+        grads = A.backward(q, k, v, g, 0.6, causal, bm, window=window)
+        rng = np.random.default_rng(seed + 4)
+        for which, x in enumerate((q, k, v)):
+            for flat in rng.choice(x.size, size=16, replace=False):
+                idx = np.unravel_index(flat, x.shape)
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += 1e-6
+                xm[idx] -= 1e-6
+                ap, am = [q, k, v], [q, k, v]
+                ap[which], am[which] = xp, xm
+                num = (f(*ap) - f(*am)) / 2e-6
+                assert abs(num - grads[which][idx]) <= 1e-6 * max(1.0, abs(num)), ("qkv"[which], window)
+    case(12, 12, True, (3, -1), 830)
+    case(9, 14, False, (2, 3), 840)
+    case(14, 9, True, (4, 0), 850)
+    case(140, 140, False, (60, 10), 860, np.array([[1, 1], [0, 1]], dtype=np.uint8))
+
+
 ALL_PINS = [pin_worked_example, pin_recurrence, pin_brute_force, pin_rows_sum_to_one, pin_zero_query,
             pin_dominant_score, pin_permutation, pin_causal_locality, pin_finite_differences,
             pin_gqa_repeat, pin_mask_semantics, pin_empty_rows, pin_scale_zero, pin_torch_sdpa,
             pin_philox_known_answers, pin_dropout_statistics, pin_dropout_expectation,
             pin_dropout_finite_differences, pin_cross_lengths_brute_force, pin_cross_lengths_suffix,
             pin_cross_lengths_finite_differences, pin_varlen_brute_force, pin_varlen_finite_differences,
-            pin_varlen_dropout_streams]
+            pin_varlen_dropout_streams, pin_window_brute_force, pin_window_torch_sdpa, pin_window_limits,
+            pin_window_finite_differences]

@@ -37,12 +37,22 @@ MUTANTS = {
     "candidate_keys_short": ("keys = keys[keys <= rows.max() + offset]", "keys = keys[keys < rows.max() + offset]"),
     "candidate_keys_no_offset": ("keys = keys[keys <= rows.max() + offset]", "keys = keys[keys <= rows.max()]"),
     "offset_sign": ("off = n - q.shape[0]", "off = q.shape[0] - n"),
-    "offset_top_left_forward": ("        if keys.size:\n            vis = visible(ch, keys, causal, block_mask, offset=off)",
-                                "        if keys.size:\n            vis = visible(ch, keys, causal, block_mask)"),
-    "offset_top_left_backward": ("        vis = visible(ch, keys, causal, block_mask, offset=off)\n        _, p, _ =",
-                                 "        vis = visible(ch, keys, causal, block_mask)\n        _, p, _ ="),
+    "offset_top_left_forward": ("        if keys.size:\n            vis = visible(ch, keys, causal, block_mask, offset=off, window=window)",
+                                "        if keys.size:\n            vis = visible(ch, keys, causal, block_mask, window=window)"),
+    "offset_top_left_backward": ("        vis = visible(ch, keys, causal, block_mask, offset=off, window=window)\n        _, p, _ =",
+                                 "        vis = visible(ch, keys, causal, block_mask, window=window)\n        _, p, _ ="),
     "varlen_keys_from_query_spans": ("head_forward(q[h, q0:q1], k[h // G, k0:k1], v[h // G, k0:k1]",
                                      "head_forward(q[h, q0:q1], k[h // G, q0:q1], v[h // G, q0:q1]"),
+    "window_left_strict": ("a &= keys[None, :] >= rows[:, None] + offset - left",
+                           "a &= keys[None, :] > rows[:, None] + offset - left"),
+    "window_left_sign": ("a &= keys[None, :] >= rows[:, None] + offset - left",
+                         "a &= keys[None, :] >= rows[:, None] + offset + left"),
+    "window_right_ignores_offset": ("a &= keys[None, :] <= rows[:, None] + offset + right",
+                                    "a &= keys[None, :] <= rows[:, None] + right"),
+    "window_candidates_short": ("keys = keys[keys >= rows.min() + offset - window[0]]",
+                                "keys = keys[keys > rows.min() + offset - window[0]]"),
+    "window_dropped_in_backward": ("        vis = visible(ch, keys, causal, block_mask, offset=off, window=window)\n        _, p, _ =",
+                                   "        vis = visible(ch, keys, causal, block_mask, offset=off)\n        _, p, _ ="),
     "varlen_dk_overwrite": ("dk[h // G, k0:k1] += bk", "dk[h // G, k0:k1] = bk"),
     "varlen_dropout_stream": ("dr = (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None\n            o[h, q0:q1]",
                               "dr = (dropout_rate, seed, h) if dropout_rate > 0 else None\n            o[h, q0:q1]"),
