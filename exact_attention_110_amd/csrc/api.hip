@@ -56,7 +56,25 @@ int check_shape(const Geo& g, float scale, int dtype) {
   return FA_OK;
 }
 
-fa::AttnShape make_shape(const Geo& g, float scale, int causal, const uint8_t* mask) {
+// Band limits from the causal flag and a (left, right) window, -1 unbounded:
+// causal masking is the right limit 0. on: 0 no band, 1 upper edge only, 2 a
+// lower edge too. Returns false for a limit below -1.
+struct Band {
+  int on, wl, wr;
+};
+
+bool make_band(int causal, int window_left, int window_right, Band* b) {
+  if (window_left < -1 || window_right < -1) return false;
+  const int wl = window_left < 0 ? fa::kUnbounded : (window_left < fa::kUnbounded ? window_left : fa::kUnbounded);
+  int wr = window_right < 0 ? fa::kUnbounded : (window_right < fa::kUnbounded ? window_right : fa::kUnbounded);
+  if (causal) wr = 0;
+  b->on = window_left >= 0 ? 2 : (causal || window_right >= 0 ? 1 : 0);
+  b->wl = wl;
+  b->wr = wr;
+  return true;
+}
+
+fa::AttnShape make_shape(const Geo& g, float scale, const Band& band, const uint8_t* mask) {
   fa::AttnShape s;
   s.B = g.B;
   s.H = g.H;
@@ -66,7 +84,9 @@ fa::AttnShape make_shape(const Geo& g, float scale, int causal, const uint8_t* m
   s.d = g.d;
   s.G = g.H / g.Hkv;
   s.scale = scale;
-  s.causal = causal != 0;
+  s.band = band.on;
+  s.wl = band.wl;
+  s.wr = band.wr;
   s.mask = mask;
   s.nbq = (g.Nq + 127) / 128;
   s.nbk = (g.Nk + 127) / 128;
@@ -126,16 +146,18 @@ int check_backward(const void* q, const void* k, const void* v, const void* o, c
 }
 
 int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, const Geo& g,
-                 float scale, int causal, const uint8_t* block_mask, int dtype, float rate,
-                 unsigned long long seed, void* stream) {
+                 float scale, int causal, int window_left, int window_right, const uint8_t* block_mask,
+                 int dtype, float rate, unsigned long long seed, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u))
     return FA_ERR_INVALID_ARG;
   int st = check_shape(g, scale, dtype);
   if (st != FA_OK) return st;
   if (mask_too_long(g, block_mask)) return FA_ERR_UNSUPPORTED;
+  Band band;
+  if (!make_band(causal, window_left, window_right, &band)) return FA_ERR_INVALID_ARG;
   fa::FwdArgs a;
-  a.s = make_shape(g, scale, causal, block_mask);
+  a.s = make_shape(g, scale, band, block_mask);
   if (!set_dropout(a.s, rate, seed)) return FA_ERR_INVALID_ARG;
   if (a.s.drop_t > 0 && dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   a.q = q;
@@ -149,14 +171,16 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
 
 int stage_impl(int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dO, void* dq, void* dk, void* dv, const Geo& g, float scale, int causal,
-               const uint8_t* block_mask, int dtype, float rate, unsigned long long seed, void* workspace,
-               size_t workspace_bytes, void* stream) {
+               int window_left, int window_right, const uint8_t* block_mask, int dtype, float rate,
+               unsigned long long seed, void* workspace, size_t workspace_bytes, void* stream) {
   if (stage < 0 || stage > 2) return FA_ERR_INVALID_ARG;
   int st = check_backward(q, k, v, o, lse, dO, dq, dk, dv, g, scale, block_mask, dtype, workspace,
                           workspace_bytes);
   if (st != FA_OK) return st;
+  Band band;
+  if (!make_band(causal, window_left, window_right, &band)) return FA_ERR_INVALID_ARG;
   fa::BwdArgs a;
-  a.s = make_shape(g, scale, causal, block_mask);
+  a.s = make_shape(g, scale, band, block_mask);
   if (!set_dropout(a.s, rate, seed)) return FA_ERR_INVALID_ARG;
   a.q = q;
   a.k = k;
@@ -176,11 +200,11 @@ int stage_impl(int stage, const void* q, const void* k, const void* v, const voi
 
 int backward_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
                   const void* dO, void* dq, void* dk, void* dv, const Geo& g, float scale, int causal,
-                  const uint8_t* block_mask, int dtype, float rate, unsigned long long seed,
-                  void* workspace, size_t workspace_bytes, void* stream) {
+                  int window_left, int window_right, const uint8_t* block_mask, int dtype, float rate,
+                  unsigned long long seed, void* workspace, size_t workspace_bytes, void* stream) {
   for (int stage = 0; stage < 3; ++stage) {
-    int st = stage_impl(stage, q, k, v, o, lse, dO, dq, dk, dv, g, scale, causal, block_mask, dtype, rate,
-                        seed, workspace, workspace_bytes, stream);
+    int st = stage_impl(stage, q, k, v, o, lse, dO, dq, dk, dv, g, scale, causal, window_left, window_right,
+                        block_mask, dtype, rate, seed, workspace, workspace_bytes, stream);
     if (st != FA_OK) return st;
   }
   return FA_OK;
@@ -199,33 +223,35 @@ size_t fa_backward_workspace_size(int B, int H, int Hkv, int N, int d, int dtype
 int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                int Hkv, int N, int d, float scale, int causal, const uint8_t* block_mask,
                int dtype, void* stream) {
-  return forward_impl(q, k, v, o, lse, fixed_geo(B, H, Hkv, N, N, d), scale, causal, block_mask, dtype, 0.f,
-                      0ull, stream);
+  return forward_impl(q, k, v, o, lse, fixed_geo(B, H, Hkv, N, N, d), scale, causal, -1, -1, block_mask, dtype,
+                      0.f, 0ull, stream);
 }
 
 int fa_forward_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                        int H, int Hkv, int N, int d, float scale, int causal,
                        const uint8_t* block_mask, int dtype, float dropout_rate,
                        unsigned long long seed, void* stream) {
-  return forward_impl(q, k, v, o, lse, fixed_geo(B, H, Hkv, N, N, d), scale, causal, block_mask, dtype,
+  return forward_impl(q, k, v, o, lse, fixed_geo(B, H, Hkv, N, N, d), scale, causal, -1, -1, block_mask, dtype,
                       dropout_rate, seed, stream);
 }
 
 int fa_forward_qk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                  int Hkv, int Nq, int Nk, int d, float scale, int causal, const uint8_t* block_mask,
-                  int dtype, float dropout_rate, unsigned long long seed, void* stream) {
-  return forward_impl(q, k, v, o, lse, fixed_geo(B, H, Hkv, Nq, Nk, d), scale, causal, block_mask, dtype,
-                      dropout_rate, seed, stream);
+                  int Hkv, int Nq, int Nk, int d, float scale, int causal, int window_left,
+                  int window_right, const uint8_t* block_mask, int dtype, float dropout_rate,
+                  unsigned long long seed, void* stream) {
+  return forward_impl(q, k, v, o, lse, fixed_geo(B, H, Hkv, Nq, Nk, d), scale, causal, window_left, window_right,
+                      block_mask, dtype, dropout_rate, seed, stream);
 }
 
 int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                       const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H, int Hkv,
                       int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d,
-                      float scale, int causal, int dtype, float dropout_rate,
-                      unsigned long long seed, void* stream) {
+                      float scale, int causal, int window_left, int window_right, int dtype,
+                      float dropout_rate, unsigned long long seed, void* stream) {
   if (!cu_seqlens_q || !cu_seqlens_k) return FA_ERR_INVALID_ARG;
   const Geo g{B, H, Hkv, max_seqlen_q, max_seqlen_k, d, cu_seqlens_q, cu_seqlens_k, total_q, total_k};
-  return forward_impl(q, k, v, o, lse, g, scale, causal, nullptr, dtype, dropout_rate, seed, stream);
+  return forward_impl(q, k, v, o, lse, g, scale, causal, window_left, window_right, nullptr, dtype, dropout_rate,
+                      seed, stream);
 }
 
 int fa_backward_stage(int stage, const void* q, const void* k, const void* v, const void* o,
@@ -233,7 +259,7 @@ int fa_backward_stage(int stage, const void* q, const void* k, const void* v, co
                       int Hkv, int N, int d, float scale, int causal, const uint8_t* block_mask,
                       int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return stage_impl(stage, q, k, v, o, lse, dO, dq, dk, dv, fixed_geo(B, H, Hkv, N, N, d), scale, causal,
-                    block_mask, dtype, 0.f, 0ull, workspace, workspace_bytes, stream);
+                    -1, -1, block_mask, dtype, 0.f, 0ull, workspace, workspace_bytes, stream);
 }
 
 int fa_backward_stage_dropout(int stage, const void* q, const void* k, const void* v,
@@ -243,7 +269,7 @@ int fa_backward_stage_dropout(int stage, const void* q, const void* k, const voi
                               float dropout_rate, unsigned long long seed, void* workspace,
                               size_t workspace_bytes, void* stream) {
   return stage_impl(stage, q, k, v, o, lse, dO, dq, dk, dv, fixed_geo(B, H, Hkv, N, N, d), scale, causal,
-                    block_mask, dtype, dropout_rate, seed, workspace, workspace_bytes, stream);
+                    -1, -1, block_mask, dtype, dropout_rate, seed, workspace, workspace_bytes, stream);
 }
 
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -251,7 +277,7 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                 float scale, int causal, const uint8_t* block_mask, int dtype, void* workspace,
                 size_t workspace_bytes, void* stream) {
   return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, fixed_geo(B, H, Hkv, N, N, d), scale, causal,
-                       block_mask, dtype, 0.f, 0ull, workspace, workspace_bytes, stream);
+                       -1, -1, block_mask, dtype, 0.f, 0ull, workspace, workspace_bytes, stream);
 }
 
 int fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,
@@ -261,29 +287,31 @@ int fa_backward_dropout(const void* q, const void* k, const void* v, const void*
                         unsigned long long seed, void* workspace, size_t workspace_bytes,
                         void* stream) {
   return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, fixed_geo(B, H, Hkv, N, N, d), scale, causal,
-                       block_mask, dtype, dropout_rate, seed, workspace, workspace_bytes, stream);
+                       -1, -1, block_mask, dtype, dropout_rate, seed, workspace, workspace_bytes, stream);
 }
 
 int fa_backward_qk(const void* q, const void* k, const void* v, const void* o, const float* lse,
                    const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int Nq,
-                   int Nk, int d, float scale, int causal, const uint8_t* block_mask, int dtype,
-                   float dropout_rate, unsigned long long seed, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+                   int Nk, int d, float scale, int causal, int window_left, int window_right,
+                   const uint8_t* block_mask, int dtype, float dropout_rate,
+                   unsigned long long seed, void* workspace, size_t workspace_bytes,
+                   void* stream) {
   return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, fixed_geo(B, H, Hkv, Nq, Nk, d), scale, causal,
-                       block_mask, dtype, dropout_rate, seed, workspace, workspace_bytes, stream);
+                       window_left, window_right, block_mask, dtype, dropout_rate, seed, workspace,
+                       workspace_bytes, stream);
 }
 
 int fa_backward_varlen(const void* q, const void* k, const void* v, const void* o,
                        const float* lse, const void* dO, void* dq, void* dk, void* dv,
                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H, int Hkv,
                        int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d,
-                       float scale, int causal, int dtype, float dropout_rate,
-                       unsigned long long seed, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+                       float scale, int causal, int window_left, int window_right, int dtype,
+                       float dropout_rate, unsigned long long seed, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   if (!cu_seqlens_q || !cu_seqlens_k) return FA_ERR_INVALID_ARG;
   const Geo g{B, H, Hkv, max_seqlen_q, max_seqlen_k, d, cu_seqlens_q, cu_seqlens_k, total_q, total_k};
-  return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, g, scale, causal, nullptr, dtype, dropout_rate, seed,
-                       workspace, workspace_bytes, stream);
+  return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, g, scale, causal, window_left, window_right, nullptr,
+                       dtype, dropout_rate, seed, workspace, workspace_bytes, stream);
 }
 
 const char* fa_status_string(int status) {
@@ -297,6 +325,6 @@ const char* fa_status_string(int status) {
   }
 }
 
-int fa_version(void) { return 102; }
+int fa_version(void) { return 103; }
 
 }  // extern "C"

@@ -96,7 +96,7 @@ struct StepPos {
   unsigned long long qoff;
 };
 
-template <class T, int D, bool CAUSAL, bool MASK, bool DROP>
+template <class T, int D, int BAND, bool MASK, bool DROP>
 __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
   constexpr int BQ = KV_BQ;
   constexpr int QBUF = BQ * 2 * D;       // one Q or dO block, swizzled rows without padding
@@ -151,18 +151,25 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
     vf[ss] = bload16(rv, (unsigned)(kj * D + 16 * ss + 8 * hh) * 2u);
   }
 
-  // query blocks this key block meets: under causal masking, rows from k0 - off on
+  // query blocks this key block meets: a band keeps key j for rows
+  // j - off - wr <= i <= j - off + wl, so rows from k0 - off - wr up to
+  // k0 + 127 - off + wl (offu = off + wr, offl = off - wl; offl binds only with a
+  // lower edge)
+  constexpr bool LOWER = BAND == 2;
+  const int offu = off + s.wr, offl = off - s.wl;
   const int nqb_all = (len_q + BQ - 1) / BQ;
-  const int qb_first = CAUSAL ? max(0, k0 - off) / BQ : 0;
-  int nq = nqb_all - qb_first;
+  const int qb_first = BAND ? max(0, k0 - offu) / BQ : 0;
+  const int qb_end = LOWER ? min(nqb_all, (max(0, k0 + KV_BKV - offl) + BQ - 1) / BQ) : nqb_all;
+  int nq = max(0, qb_end - qb_first);
   if constexpr (MASK) {
-    // mask rows I with mask[I][kblk] != 0, from the first one needed
+    // mask rows I with mask[I][kblk] != 0, from the first one needed to the last
     const int i_first = qb_first / KV_R;
+    const int i_end = min(s.nbq, (qb_end + KV_R - 1) / KV_R);
     if (w == 0) {
       int cnt = 0;
-      for (int j0 = i_first; j0 < s.nbq; j0 += 64) {
+      for (int j0 = i_first; j0 < i_end; j0 += 64) {
         const int j = j0 + lane;
-        const bool keep = j < s.nbq && s.mask[(size_t)j * s.nbk + kblk] != 0;
+        const bool keep = j < i_end && s.mask[(size_t)j * s.nbk + kblk] != 0;
         const unsigned long long bal = __ballot(keep);
         if (keep) blist[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (short)j;
         cnt += __popcll(bal);
@@ -172,7 +179,7 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
     __syncthreads();
     const int cnt = *bcount;
     nq = KV_R * cnt;
-    if (cnt > 0) nq -= max(0, KV_R * (blist[cnt - 1] + 1) - nqb_all);  // steps past the sequence
+    if (cnt > 0) nq -= max(0, KV_R * (blist[cnt - 1] + 1) - qb_end);  // steps past the band or the sequence
   }
   auto qblock_at = [&](int qi) -> int {
     if constexpr (MASK) return KV_R * blist[qi / KV_R] + qi % KV_R;
@@ -231,10 +238,10 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
   };
 
   // P and dS (unscaled) of a step from its S, dP and statistics buffer. Element
-  // i is query q0 + 8 (i / 4) + 4 hh + i % 4 of key kj; under causal masking it
-  // is kept only if 8 (i / 4) + i % 4 >= kj - off - q0 - 4 hh. Keys past the
-  // sequence need no mask: their K and V rows read as zeros and nothing of
-  // theirs is stored.
+  // i is query q0 + 8 (i / 4) + 4 hh + i % 4 of key kj; under a band mask it is
+  // kept only if kj - off - wr <= q0 + 4 hh + 8 (i / 4) + i % 4 <= kj - off + wl.
+  // Keys past the sequence need no mask: their K and V rows read as zeros and
+  // nothing of theirs is stored.
   // With dropout (z the keep decision, c its scale): P V uses z c P, and
   // dS = P (z c dP - D), the gradient flowing to P through the dropped values.
   auto probs = [&](auto masked, const f32x16& sc, const f32x16& dp, int q0, int stb, int bh, unsigned int (&pk)[8],
@@ -243,7 +250,8 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
     const __attribute__((address_space(3))) float* lsel =
         (const __attribute__((address_space(3))) float*)(stat + stb * STB);
     const __attribute__((address_space(3))) float* ddl = lsel + BQ;
-    const int thr = kj - off - q0 - 4 * hh;
+    const int thr = kj - offu - q0 - 4 * hh;   // first kept 8 (i / 4) + i % 4
+    const int thr2 = kj - offl - q0 - 4 * hh;  // last kept (with a lower edge)
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       const f32x4 L4 = *(const __attribute__((address_space(3))) f32x4*)(lsel + 8 * j4 + 4 * hh);
@@ -257,7 +265,7 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * j4 + r;
         float pv = fast_exp2(fmaf(sc[i], c, -L4[r]));
-        if constexpr (MASKED) pv = (8 * j4 + r < thr) ? 0.f : pv;
+        if constexpr (MASKED) pv = (8 * j4 + r < thr || (LOWER && 8 * j4 + r > thr2)) ? 0.f : pv;
         if constexpr (DROP) {
           const bool z = drop_keep(rnd.v[r], kj & 3, s.drop_t);
           p[r] = z ? pv * s.drop_scale : 0.f;
@@ -299,10 +307,11 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
   // step e + 2 is loaded into the buffer step e - 2 used, and one barrier ends
   // the step. Loads are issued on every path (indices clamped; a redundant
   // block lands in a buffer nobody reads). The first iteration's "step -1"
-  // multiplies zero P and dS with a zeroed buffer. Only the first KV_R steps of
-  // each query head can meet the causal diagonal; they run a masked variant,
-  // the others none, and the unmasked steps alternate between two register
-  // sets so that nothing is copied from one step to the next.
+  // multiplies zero P and dS with a zeroed buffer. Only a few steps at the start
+  // of each query head's list (the band's upper edge, the causal diagonal) and
+  // at its end (the band's lower edge) cross a band edge; they run a masked
+  // variant, the others none, and the unmasked steps alternate between two
+  // register sets so that nothing is copied from one step to the next.
   for (int i = tid; i < 2 * QBUF / 16; i += KV_NW * 64) {
     const int t = i / (QBUF / 16), off = (i % (QBUF / 16)) * 16;
     lds_write16((t ? obuf : qbuf) + (NB - 1) * QBUF + off, (s16x8){0, 0, 0, 0, 0, 0, 0, 0});
@@ -346,15 +355,21 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
       skA[j] = skB[j];
     }
   };
-  // steps at the start of each head's list that cross the causal diagonal: a
-  // query block from q0 needs masking while q0 + off < k0 + 127 (the block's
-  // last key). The list rises, so they form a prefix (at most five steps
-  // without a mask, two mask rows with one).
-  int ndiag = 0;
-  if constexpr (CAUSAL) {
-    const int lim = k0 + KV_BKV - 1 - off;
+  // Masked steps: a query block from q0 crosses the band's upper edge while
+  // q0 + off + wr < k0 + 127 (the block's last key) and its lower edge while
+  // q0 + 31 + off - wl > k0 (its first key). The list rises, so the former
+  // form a prefix and the latter a suffix (each at most five steps without a
+  // block mask, two mask rows with one).
+  int ndiag = 0, nsuf = 0;
+  if constexpr (BAND) {
+    const int lim = k0 + KV_BKV - 1 - offu;
     while (ndiag < nq && qblock_at(ndiag) * BQ < lim) ++ndiag;
   }
+  if constexpr (LOWER) {
+    const int lim2 = k0 - (BQ - 1) - offl;
+    while (nsuf < nq - ndiag && qblock_at(nq - 1 - nsuf) * BQ > lim2) ++nsuf;
+  }
+  const int nmid_end = nq - nsuf;
   int e = 0;
   for (int hg = 0; hg < s.G; ++hg) {
     for (int t = 0; t < ndiag; ++t, ++e) {
@@ -362,14 +377,21 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
       b_to_a();
     }
     int t = ndiag;
-    for (; t + 1 < nq; t += 2, e += 2) {
+    for (; t + 1 < nmid_end; t += 2, e += 2) {
       iter(e, std::false_type{}, scA, dpA, pkA, skA, scB, dpB, pkB, skB);
       iter(e + 1, std::false_type{}, scB, dpB, pkB, skB, scA, dpA, pkA, skA);
     }
-    if (t < nq) {
+    if (t < nmid_end) {
       iter(e, std::false_type{}, scA, dpA, pkA, skA, scB, dpB, pkB, skB);
       b_to_a();
       ++e;
+      ++t;
+    }
+    if constexpr (LOWER) {
+      for (; t < nq; ++t, ++e) {
+        iter(e, std::true_type{}, scA, dpA, pkA, skA, scB, dpB, pkB, skB);
+        b_to_a();
+      }
     }
   }
   if (nsteps > 0) dvdk((nsteps - 1) & (NB - 1), pkA, skA);
@@ -408,7 +430,7 @@ constexpr int Q_T2 = Q_BN / 32;      // 32-key halves per tile
 constexpr int Q_R = 128 / Q_BN;      // tiles per 128-key mask block
 static_assert(Q_BM == 128, "a query-block workgroup must cover exactly one mask block row");
 
-template <class T, int D, bool CAUSAL, bool MASK, bool DROP>
+template <class T, int D, int BAND, bool MASK, bool DROP>
 __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
   constexpr int KBUF = Q_BN * 2 * D;     // K tile: swizzled rows, row reads and transposing reads
   constexpr int VBUF = Q_BN * 2 * D;     // V tile: swizzled rows, row reads
@@ -429,7 +451,7 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
   const int roff = 4 * (g16 >> 1) + ((lane & 15) >> 2);
   const int coff = 16 * (g16 & 1) + 4 * (lane & 3);
   // grid = (H, query blocks, B), as in the forward pass
-  const int qb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+  const int qb = BAND ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
   const int h = blockIdx.x, b = blockIdx.z;
   const int hk = h / s.G;
   const SeqView sv = seq_view(s, b, h, hk);
@@ -459,14 +481,19 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
   const float lse2 = st[qi];
   const float dd = st[a.npad + qi];
 
-  const int kend = CAUSAL ? min(len_k, max(0, q0 + Q_BM + off)) : len_k;
+  // keys [kbeg, kend) are seen by some row of the block (band as in the forward pass)
+  constexpr bool LOWER = BAND == 2;
+  const int offu = off + s.wr, offl = off - s.wl;
+  const int kbeg = LOWER ? max(0, q0 + offl) : 0;
+  const int kend = BAND ? min(len_k, max(0, q0 + Q_BM + offu)) : len_k;
+  const int tbeg = kbeg / Q_BN;
   const int ntile_all = (kend + Q_BN - 1) / Q_BN;
-  int ntiles = ntile_all;
+  int ntiles = max(0, ntile_all - tbeg);
   if constexpr (MASK) {
     const int nbk = (kend + 127) / 128;
     if (w == 0) {
       int cnt = 0;
-      for (int j0 = 0; j0 < nbk; j0 += 64) {
+      for (int j0 = kbeg / 128; j0 < nbk; j0 += 64) {
         const int j = j0 + lane;
         const bool keep = j < nbk && s.mask[(size_t)qb * s.nbk + j] != 0;
         const unsigned long long bal = __ballot(keep);
@@ -482,7 +509,7 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
   }
   auto tile_at = [&](int e) -> int {
     if constexpr (MASK) return Q_R * blist[e / Q_R] + e % Q_R;
-    else return e;
+    else return tbeg + e;
   };
 
   f32x16 acc[ND];
@@ -507,7 +534,8 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
     const int ks = tile_at(e) * Q_BN;
     dma_kv(tile_at(e + 1 < ntiles ? e + 1 : e), buf ^ 1);
 
-    const bool active = !(CAUSAL && ks > qw + 31 + off);  // wave-uniform
+    // wave-uniform: does any row of the wave see a key of the tile
+    const bool active = !(BAND && ks > qw + 31 + offu) && !(LOWER && ks + Q_BN - 1 < qw + offl);
     if (active) {
       const lds_t* kb = kbuf + buf * KBUF;
       const lds_t* vb = vbuf + buf * VBUF;
@@ -530,12 +558,12 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
           sc[t2] = mfma32<T>(ka, qf[ss], sc[t2]);
           dp[t2] = mfma32<T>(va, gf[ss], dp[t2]);
         }
-      // dS for query qi and key ks + 32 t2 + 8 (i / 4) + 4 hh + i % 4. Causal: kept
-      // only if 32 t2 + 8 (i / 4) + i % 4 <= qi + off - ks - 4 hh. Keys past the
-      // sequence read as zeros, so their dS multiplies a zero row of K and needs
-      // no mask.
-      const bool diag = CAUSAL && ks + Q_BN - 1 > qw + off;
-      const int thr = qi + off - ks - 4 * hh;
+      // dS for query qi and key ks + 32 t2 + 8 (i / 4) + 4 hh + i % 4. Band: kept
+      // only if qi + off - wl <= key <= qi + off + wr. Keys past the sequence read
+      // as zeros, so their dS multiplies a zero row of K and needs no mask.
+      const bool diag = (BAND && ks + Q_BN - 1 > qw + offu) || (LOWER && ks < qw + 31 + offl);
+      const int thr = qi + offu - ks - 4 * hh;   // last kept 32 t2 + 8 (i / 4) + i % 4
+      const int thr2 = qi + offl - ks - 4 * hh;  // first kept (with a lower edge)
       unsigned int sk[Q_T2][8];
       auto ds_tile = [&](auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
@@ -551,7 +579,10 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
             for (int r = 0; r < 2; ++r) {
               const int i = 2 * j + r;
               float pv = fast_exp2(fmaf(sc[t2][i], c, -lse2));
-              if constexpr (MASKED) pv = (32 * t2 + 8 * (i >> 2) + (i & 3) > thr) ? 0.f : pv;
+              if constexpr (MASKED) {
+                const int kidx = 32 * t2 + 8 * (i >> 2) + (i & 3);
+                pv = (kidx > thr || (LOWER && kidx < thr2)) ? 0.f : pv;
+              }
               if constexpr (DROP)
                 v2[r] = pv * ((drop_keep(wd, i & 3, s.drop_t) ? dp[t2][i] * s.drop_scale : 0.f) - dd);
               else
@@ -608,16 +639,20 @@ static hipError_t launch_pre_t(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <class T, int D, bool DROP>
-static hipError_t launch_kv_t2(const BwdArgs& a, hipStream_t st) {
+template <class T, int D, int BAND, bool DROP>
+static hipError_t launch_kv_t3(const BwdArgs& a, hipStream_t st) {
   const dim3 grid(a.s.Hkv, (a.s.Nk + KV_BKV - 1) / KV_BKV, a.s.B);
   const dim3 block(KV_NW * 64);
-  const bool causal = a.s.causal != 0, mask = a.s.mask != nullptr;
-  if (causal && mask) hipLaunchKernelGGL((bwd_kv_kernel<T, D, true, true, DROP>), grid, block, 0, st, a);
-  else if (causal) hipLaunchKernelGGL((bwd_kv_kernel<T, D, true, false, DROP>), grid, block, 0, st, a);
-  else if (mask) hipLaunchKernelGGL((bwd_kv_kernel<T, D, false, true, DROP>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((bwd_kv_kernel<T, D, false, false, DROP>), grid, block, 0, st, a);
+  if (a.s.mask) hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, true, DROP>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, false, DROP>), grid, block, 0, st, a);
   return hipGetLastError();
+}
+
+template <class T, int D, bool DROP>
+static hipError_t launch_kv_t2(const BwdArgs& a, hipStream_t st) {
+  if (a.s.band == 2) return launch_kv_t3<T, D, 2, DROP>(a, st);
+  if (a.s.band == 1) return launch_kv_t3<T, D, 1, DROP>(a, st);
+  return launch_kv_t3<T, D, 0, DROP>(a, st);
 }
 
 template <class T, int D>
@@ -625,16 +660,20 @@ static hipError_t launch_kv_t(const BwdArgs& a, hipStream_t st) {
   return a.s.drop_t > 0 ? launch_kv_t2<T, D, true>(a, st) : launch_kv_t2<T, D, false>(a, st);
 }
 
-template <class T, int D, bool DROP>
-static hipError_t launch_q_t2(const BwdArgs& a, hipStream_t st) {
+template <class T, int D, int BAND, bool DROP>
+static hipError_t launch_q_t3(const BwdArgs& a, hipStream_t st) {
   const dim3 grid(a.s.H, (a.s.Nq + Q_BM - 1) / Q_BM, a.s.B);
   const dim3 block(Q_NW * 64);
-  const bool causal = a.s.causal != 0, mask = a.s.mask != nullptr;
-  if (causal && mask) hipLaunchKernelGGL((bwd_q_kernel<T, D, true, true, DROP>), grid, block, 0, st, a);
-  else if (causal) hipLaunchKernelGGL((bwd_q_kernel<T, D, true, false, DROP>), grid, block, 0, st, a);
-  else if (mask) hipLaunchKernelGGL((bwd_q_kernel<T, D, false, true, DROP>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((bwd_q_kernel<T, D, false, false, DROP>), grid, block, 0, st, a);
+  if (a.s.mask) hipLaunchKernelGGL((bwd_q_kernel<T, D, BAND, true, DROP>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((bwd_q_kernel<T, D, BAND, false, DROP>), grid, block, 0, st, a);
   return hipGetLastError();
+}
+
+template <class T, int D, bool DROP>
+static hipError_t launch_q_t2(const BwdArgs& a, hipStream_t st) {
+  if (a.s.band == 2) return launch_q_t3<T, D, 2, DROP>(a, st);
+  if (a.s.band == 1) return launch_q_t3<T, D, 1, DROP>(a, st);
+  return launch_q_t3<T, D, 0, DROP>(a, st);
 }
 
 template <class T, int D>

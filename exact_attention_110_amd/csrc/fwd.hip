@@ -44,7 +44,7 @@ constexpr int FWD_BN = 64;            // keys per tile
 constexpr int FWD_LIST = 2048;        // capacity of the compacted mask-block list
 static_assert(FWD_BM == 128, "a forward workgroup must cover exactly one mask block row");
 
-template <class T, int D, bool CAUSAL, bool MASK, bool DROP>
+template <class T, int D, int BAND, bool MASK, bool DROP>
 __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
   constexpr int KP = D * 2 + 16;  // K row pitch in LDS, bytes (16 mod 128: conflict-free 16-byte reads)
   constexpr int VP = D * 2 + 32;  // V row pitch in LDS, bytes (32 mod 128: conflict-free transposing reads)
@@ -70,8 +70,9 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
   const int l32 = lane & 31, hh = lane >> 5;
   // grid = (H, query blocks, B): consecutive workgroups take different heads, so
   // the round-robin spread over the 8 XCDs keeps each head on one XCD's L2;
-  // under causal masking the longest query blocks are dispatched first
-  const int qb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+  // under a band mask the later (under causal masking, longer) query blocks
+  // are dispatched first
+  const int qb = BAND ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
   const int h = blockIdx.x, b = blockIdx.z;
   const int hk = h / s.G;
   const SeqView sv = seq_view(s, b, h, hk);
@@ -91,14 +92,21 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
   // above zero so that masked entries stay -inf (-inf * 0 would be NaN)
   const float c = fmaxf(s.scale * kLog2e, 1e-30f);
 
-  const int kend = CAUSAL ? min(nk, max(0, q0 + FWD_BM + off)) : nk;
+  // keys [kbeg, kend) are seen by some row of the workgroup: row q0 has the
+  // lowest band start, the last row the highest band end
+  // (band: row i sees keys i + offl .. i + offu; offl binds only with a lower edge)
+  constexpr bool LOWER = BAND == 2;
+  const int offu = off + s.wr, offl = off - s.wl;
+  const int kbeg = LOWER ? max(0, q0 + offl) : 0;
+  const int kend = BAND ? min(nk, max(0, q0 + FWD_BM + offu)) : nk;
+  const int tbeg = kbeg / FWD_BN;
   const int ntile_all = (kend + FWD_BN - 1) / FWD_BN;
-  int ntiles = ntile_all;
+  int ntiles = max(0, ntile_all - tbeg);
   if constexpr (MASK) {
     const int nbk = (kend + 127) / 128;
     if (w == 0) {
       int cnt = 0;
-      for (int j0 = 0; j0 < nbk; j0 += 64) {
+      for (int j0 = kbeg / 128; j0 < nbk; j0 += 64) {
         const int j = j0 + lane;
         const bool keep = j < nbk && s.mask[(size_t)qb * s.nbk + j] != 0;
         const unsigned long long bal = __ballot(keep);
@@ -114,7 +122,7 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
   }
   auto tile_at = [&](int e) -> int {
     if constexpr (MASK) return 2 * blist[e >> 1] + (e & 1);
-    else return e;
+    else return tbeg + e;
   };
 
   // Q^T operand: lane holds query qi, d = 16 * ss + 8 * hh + 0..7
@@ -173,7 +181,8 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
     const int ks = tile_at(e) * FWD_BN;
     gload_tile(tile_at(e + 1 < ntiles ? e + 1 : e));
 
-    const bool active = !(CAUSAL && ks > qw + 31 + off);  // wave-uniform
+    // wave-uniform: does any row of the wave see a key of the tile
+    const bool active = !(BAND && ks > qw + 31 + offu) && !(LOWER && ks + FWD_BN - 1 < qw + offl);
     if (active) {
       const lds_t* kb = kbuf + buf * KBUF;
       const lds_t* vb = vbuf + buf * VBUF;
@@ -192,14 +201,15 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
         }
       }
       // sc[t2][i] is S for query qi and key ks + 32 t2 + 8 (i / 4) + 4 hh + i % 4
-      const bool need_mask = (CAUSAL && ks + FWD_BN - 1 > qw + off) || (ks + FWD_BN > nk);
+      const bool need_mask =
+          (BAND && ks + FWD_BN - 1 > qw + offu) || (LOWER && ks < qw + 31 + offl) || (ks + FWD_BN > nk);
       if (need_mask) {
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = ks + 32 * t2 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            if ((CAUSAL && key > qi + off) || key >= nk) sc[t2][i] = -INFINITY;
+            if ((BAND && key > qi + offu) || (LOWER && key < qi + offl) || key >= nk) sc[t2][i] = -INFINITY;
           }
       }
       float mx = sc[0][0];
@@ -316,7 +326,7 @@ constexpr int F64_BM = F64_NW * F64_RW;   // query rows per workgroup
 constexpr int F64_BN = 32;                // keys per tile
 constexpr int F64_NB = 4;                 // LDS ring slots
 
-template <class T, int D, bool CAUSAL, bool DROP>
+template <class T, int D, int BAND, bool DROP>
 __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
   constexpr int KP = D * 2 + 16;  // K row pitch (bytes): conflict-free 16-byte row reads
   constexpr int VP = D * 2 + 32;  // V row pitch (bytes): conflict-free transposing reads
@@ -341,9 +351,9 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
   const int g16 = lane >> 4;
   const int roff = 4 * (g16 >> 1) + ((lane & 15) >> 2);
   const int coff = 16 * (g16 & 1) + 4 * (lane & 3);
-  // grid = (H, query blocks, B): heads spread over the XCDs; under causal
-  // masking the longest query blocks are dispatched first
-  const int qb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+  // grid = (H, query blocks, B): heads spread over the XCDs; under a band
+  // mask the later (under causal masking, longer) query blocks are dispatched first
+  const int qb = BAND ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
   const int h = blockIdx.x, b = blockIdx.z;
   const int hk = h / s.G;
   const SeqView sv = seq_view(s, b, h, hk);
@@ -358,10 +368,32 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
   const int qw = q0 + F64_RW * w;  // first query row of this wave; block rb holds rows qw + 32 rb + 0..31
   const float c = fmaxf(s.scale * kLog2e, 1e-30f);
 
-  const int kend = CAUSAL ? min(nk, max(0, q0 + F64_BM + off)) : nk;
-  const int ntiles = (kend + F64_BN - 1) / F64_BN;
-  // tiles whose keys every row of the workgroup sees: row q0 sees keys up to q0 + off
-  const int nfull = CAUSAL ? min(max(0, q0 + off + 1) / F64_BN, nk / F64_BN) : nk / F64_BN;
+  // tiles [tbeg, tbeg + ntiles) hold every key some row of the workgroup sees
+  // (row q0's band starts lowest, the last row's ends highest); tiles
+  // [fbeg, fend) hold only keys that every row sees (the last row's band starts
+  // highest, row q0's ends lowest)
+  // (band: row i sees keys i + offl .. i + offu; offl binds only with a lower edge)
+  constexpr bool LOWER = BAND == 2;
+  const int offu = off + s.wr, offl = off - s.wl;
+  const int kbeg = LOWER ? max(0, q0 + offl) : 0;
+  const int kend = BAND ? min(nk, max(0, q0 + F64_BM + offu)) : nk;
+  const int tbeg = kbeg / F64_BN;
+  const int ntiles = max(0, (kend + F64_BN - 1) / F64_BN - tbeg);
+  // (clamped to the tile range: padding rows past the sequence can put the
+  // last row's band start beyond the last key)
+  const int fbeg =
+      LOWER ? min(tbeg + ntiles, max(tbeg, (max(0, q0 + F64_BM - 1 + offl) + F64_BN - 1) / F64_BN)) : 0;
+  const int fend = BAND ? max(fbeg, min(max(0, q0 + offu + 1) / F64_BN, nk / F64_BN)) : nk / F64_BN;
+  const int nfull = fend - fbeg;
+  // processing order e = 0, 1, ...: the full tiles, then the partial tiles
+  // above them (together the run fbeg, fbeg + 1, ...), then those below (the
+  // result does not depend on the order); without a lower edge the order is
+  // simply the tile index
+  const int nhead = tbeg + ntiles - fbeg;
+  auto tile_of = [&](int e) -> int {
+    if constexpr (LOWER) return e < nhead ? fbeg + e : tbeg + (e - nhead);
+    else return e;
+  };
 
   // Q^T operands of both row blocks: lane holds query qw + 32 rb + l32, d = 16 ss + 8 hh + 0..7
   s16x8 qf[2][NS];
@@ -501,9 +533,9 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
   // because the first iteration multiplies it with zero probabilities.
   for (int i = tid; i < VBUF / 16; i += NT)
     lds_write16(vbuf + (F64_NB - 1) * VBUF + i * 16, (s16x8){0, 0, 0, 0, 0, 0, 0, 0});
-  gload(0);
+  gload(tile_of(0));
   lstore(0);
-  gload(max(0, min(1, ntiles - 1)));
+  gload(tile_of(max(0, min(1, ntiles - 1))));
   lstore(1);
   __syncthreads();
 
@@ -537,9 +569,9 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
     // copy lands in a slot nobody reads).
     auto iter = [&](int jj, const f32x16 (&scur)[2], f32x16 (&snext)[2], const unsigned int (&pprev)[2][8],
                     unsigned int (&pcur)[2][8]) {
-      gload(min(jj + 2, ntiles - 1));
+      gload(tile_of(min(jj + 2, ntiles - 1)));
       s_tile((jj + 1) & (F64_NB - 1), snext);
-      probs(scur, pcur, jj * F64_BN);
+      probs(scur, pcur, (fbeg + jj) * F64_BN);
       pv_tile((jj + F64_NB - 1) & (F64_NB - 1), pprev);
       lstore((jj + 2) & (F64_NB - 1));
       __syncthreads();
@@ -580,9 +612,9 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[rb][dt][i] = 0.f;
       }
-      gload(0);
+      gload(tile_of(0));
       lstore(0);
-      gload(max(0, min(1, ntiles - 1)));
+      gload(tile_of(max(0, min(1, ntiles - 1))));
       lstore(1);
       __syncthreads();
     }
@@ -591,9 +623,9 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
   // general loop (diagonal and ragged tiles, or a restart): element masks,
   // lazy rescaling, waves without a visible key skip the tile
   for (; j < ntiles; ++j) {
-    gload(min(j + 2, ntiles - 1));
-    const int ks = j * F64_BN;
-    if (!CAUSAL || ks <= qw + F64_RW - 1 + off) {
+    gload(tile_of(min(j + 2, ntiles - 1)));
+    const int ks = tile_of(j) * F64_BN;
+    if ((!BAND || ks <= qw + F64_RW - 1 + offu) && (!LOWER || ks + F64_BN - 1 >= qw + offl)) {
       f32x16 st[2];
       s_tile(j & (F64_NB - 1), st);
 #pragma unroll
@@ -602,7 +634,7 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = ks + 8 * (i >> 2) + 4 * hh + (i & 3);
-          if ((CAUSAL && key > qi + off) || key >= nk) st[rb][i] = -INFINITY;
+          if ((BAND && key > qi + offu) || (LOWER && key < qi + offl) || key >= nk) st[rb][i] = -INFINITY;
         }
       }
       float mn[2], ls[2];
@@ -674,15 +706,19 @@ __global__ __launch_bounds__(F32_R * F32_S) void fwd_f32_kernel(FwdArgs a) {
     o[dd] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
-  const int kend_row = s.causal ? min(nk, max(0, qi + 1 + off)) : nk;
-  const int kend = s.causal ? min(nk, max(0, q0 + F32_R + off)) : nk;  // bound for the workgroup
-  for (int j0 = sp * F32_C; j0 < kend; j0 += F32_S * F32_C) {
+  // this row's band [kbeg_row, kend_row) and the workgroup's [kbeg, kend)
+  const int kbeg_row = s.band ? max(0, qi + off - s.wl) : 0;
+  const int kend_row = s.band ? min(nk, max(0, qi + 1 + off + s.wr)) : nk;
+  const int kbeg = s.band ? max(0, q0 + off - s.wl) : 0;
+  const int kend = s.band ? min(nk, max(0, q0 + F32_R + off + s.wr)) : nk;
+  constexpr int STRIDE = F32_S * F32_C;
+  for (int j0 = kbeg / STRIDE * STRIDE + sp * F32_C; j0 < kend; j0 += STRIDE) {
     float x[F32_C];
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < F32_C; ++t) {
       const int j = j0 + t;
-      const bool vis = j < kend_row && (!s.mask || s.mask[(size_t)mrow * s.nbk + j / 128] != 0);
+      const bool vis = j >= kbeg_row && j < kend_row && (!s.mask || s.mask[(size_t)mrow * s.nbk + j / 128] != 0);
       float dot = 0.f;
       if (vis) {
         const float4* kr = (const float4*)(K + (size_t)j * D);
@@ -755,26 +791,31 @@ __global__ __launch_bounds__(F32_R * F32_S) void fwd_f32_kernel(FwdArgs a) {
   }
 }
 
-template <class T, int D, bool DROP>
-static hipError_t launch_fwd_t2(const FwdArgs& a, hipStream_t st, bool causal, bool mask, bool use64) {
+template <class T, int D, int BAND, bool DROP>
+static hipError_t launch_fwd_t3(const FwdArgs& a, hipStream_t st, bool mask, bool use64) {
   if (!mask && use64) {
     const dim3 grid(a.s.H, (a.s.Nq + F64_BM - 1) / F64_BM, a.s.B);
-    if (causal) hipLaunchKernelGGL((fwd64_kernel<T, D, true, DROP>), grid, dim3(F64_NW * 64), 0, st, a);
-    else hipLaunchKernelGGL((fwd64_kernel<T, D, false, DROP>), grid, dim3(F64_NW * 64), 0, st, a);
+    hipLaunchKernelGGL((fwd64_kernel<T, D, BAND, DROP>), grid, dim3(F64_NW * 64), 0, st, a);
     return hipGetLastError();
   }
   const dim3 grid(a.s.H, (a.s.Nq + FWD_BM - 1) / FWD_BM, a.s.B);
   const dim3 block(FWD_NW * 64);
-  if (causal && mask) hipLaunchKernelGGL((fwd_kernel<T, D, true, true, DROP>), grid, block, 0, st, a);
-  else if (causal) hipLaunchKernelGGL((fwd_kernel<T, D, true, false, DROP>), grid, block, 0, st, a);
-  else if (mask) hipLaunchKernelGGL((fwd_kernel<T, D, false, true, DROP>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((fwd_kernel<T, D, false, false, DROP>), grid, block, 0, st, a);
+  if (mask) hipLaunchKernelGGL((fwd_kernel<T, D, BAND, true, DROP>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((fwd_kernel<T, D, BAND, false, DROP>), grid, block, 0, st, a);
   return hipGetLastError();
+}
+
+template <class T, int D, bool DROP>
+static hipError_t launch_fwd_t2(const FwdArgs& a, hipStream_t st, int band, bool mask, bool use64) {
+  if (band == 2) return launch_fwd_t3<T, D, 2, DROP>(a, st, mask, use64);
+  if (band == 1) return launch_fwd_t3<T, D, 1, DROP>(a, st, mask, use64);
+  return launch_fwd_t3<T, D, 0, DROP>(a, st, mask, use64);
 }
 
 template <class T, int D>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
-  const bool causal = a.s.causal != 0, mask = a.s.mask != nullptr;
+  const int band = a.s.band;
+  const bool mask = a.s.mask != nullptr;
   // The 64-row kernel pays off for long sequences over few heads (measured:
   // N = 16384 x 16 heads, 4% faster). With many workgroups the 32-row kernel's
   // two waves per SIMD balance better (4 x 32 heads at N = 8192: 6% faster),
@@ -788,8 +829,8 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
     if (env[0] == '6' && env[1] == '4' && env[2] == 0) use64 = true;
     if (env[0] == '3' && env[1] == '2' && env[2] == 0) use64 = false;
   }
-  if (a.s.drop_t > 0) return launch_fwd_t2<T, D, true>(a, st, causal, mask, use64);
-  return launch_fwd_t2<T, D, false>(a, st, causal, mask, use64);
+  if (a.s.drop_t > 0) return launch_fwd_t2<T, D, true>(a, st, band, mask, use64);
+  return launch_fwd_t2<T, D, false>(a, st, band, mask, use64);
 }
 
 template <int D>

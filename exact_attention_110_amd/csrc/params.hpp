@@ -8,13 +8,24 @@
 
 namespace fa {
 
+// A band side that never binds: larger than any sequence, small enough that
+// row + offset +- kUnbounded stays inside int32.
+constexpr int kUnbounded = 1 << 30;
+
 struct AttnShape {
   int B, H, Hkv;
   int Nq, Nk;     // query rows and keys per sequence (packed batches: the longest)
   int d;
   int G;          // H / Hkv, query heads per kv head
   float scale;    // multiplies Q K^T
-  int causal;     // key j visible to query i only if j <= i + (nk - nq) of its sequence
+  // band mask around the query's position p = i + (nk - nq) of its sequence:
+  // key j visible only if p - wl <= j <= p + wr; an unbounded side holds
+  // kUnbounded. band: 0 none (every key visible), 1 upper edge only (wl
+  // unbounded; causal masking is wr = 0), 2 both edges. The kernels are
+  // instantiated per band kind, so causal attention pays nothing for the
+  // lower edge.
+  int band;
+  int wl, wr;
   const uint8_t* mask;  // NULL or uint8 [nbq][nbk] (fixed lengths only)
   int nbq, nbk;   // ceil(Nq / 128), ceil(Nk / 128)
   // packed variable-length batches (NULL for fixed lengths): sequence b holds

@@ -187,18 +187,28 @@ int fa_backward_stage_dropout(int stage, const void* q, const void* k, const voi
  *   lse          : [B][H][Nq] float32
  *   block_mask   NULL or uint8 [ceil(Nq/128)][ceil(Nk/128)] (both <= 2048)
  *   workspace    fa_backward_workspace_size(B, H, Hkv, Nq, d, dtype) bytes
+ * Sliding-window (local) masks, one family of the many masks a single tiled
+ * kernel can serve (pranaymahendrakar.com lesson "FlashAttention", Researcher
+ * tier, "Beyond hand-written kernels"; the pages fix no convention, this is
+ * the reading taken): with the query at position p = i + (Nk - Nq), key j is
+ * visible only if p - window_left <= j <= p + window_right; -1 leaves that
+ * side unbounded, and causal != 0 sets the right limit to 0 (so causal with
+ * window_left = W - 1 keeps the query and the W - 1 keys before it). Band,
+ * causal and block masks intersect. The kernels skip the tiles outside the
+ * band and mask elements only in tiles that straddle its edges.
+ *   window_left, window_right   >= -1 (FA_ERR_INVALID_ARG below -1)
  * dropout_rate 0 is no dropout; dropout otherwise as described above. Other
  * arguments, limits (each of Nq and Nk as N), ownership and errors as for
  * fa_forward / fa_backward.
  */
 int fa_forward_qk(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
-                  const uint8_t* block_mask, int dtype,
+                  int window_left, int window_right, const uint8_t* block_mask, int dtype,
                   float dropout_rate, unsigned long long seed, void* stream);
 int fa_backward_qk(const void* q, const void* k, const void* v, const void* o,
                    const float* lse, const void* dO, void* dq, void* dk, void* dv,
                    int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
-                   const uint8_t* block_mask, int dtype,
+                   int window_left, int window_right, const uint8_t* block_mask, int dtype,
                    float dropout_rate, unsigned long long seed,
                    void* workspace, size_t workspace_bytes, void* stream);
 
@@ -210,8 +220,9 @@ int fa_backward_qk(const void* q, const void* k, const void* v, const void* o,
  *   lse          : [H][total_q] float32
  * Sequence b holds query rows cu_seqlens_q[b] .. cu_seqlens_q[b + 1] - 1 and
  * keys cu_seqlens_k[b] .. cu_seqlens_k[b + 1] - 1 of every head; each is an
- * independent attention problem (causal alignment as for fa_forward_qk, with
- * the sequence's own lengths; a sequence may have no queries or no keys).
+ * independent attention problem (causal alignment and windows as for
+ * fa_forward_qk, with the sequence's own lengths; a sequence may have no
+ * queries or no keys).
  *   cu_seqlens_q, cu_seqlens_k   device int32 [B + 1], 4-byte aligned, rising
  *                                from 0 to total_q / total_k
  *   max_seqlen_q, max_seqlen_k   >= 1 and >= every sequence's length; the
@@ -232,14 +243,16 @@ int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, floa
                       const int* cu_seqlens_q, const int* cu_seqlens_k,
                       int B, int H, int Hkv, int total_q, int total_k,
                       int max_seqlen_q, int max_seqlen_k, int d, float scale, int causal,
-                      int dtype, float dropout_rate, unsigned long long seed, void* stream);
+                      int window_left, int window_right, int dtype, float dropout_rate,
+                      unsigned long long seed, void* stream);
 int fa_backward_varlen(const void* q, const void* k, const void* v, const void* o,
                        const float* lse, const void* dO, void* dq, void* dk, void* dv,
                        const int* cu_seqlens_q, const int* cu_seqlens_k,
                        int B, int H, int Hkv, int total_q, int total_k,
                        int max_seqlen_q, int max_seqlen_k, int d, float scale, int causal,
-                       int dtype, float dropout_rate, unsigned long long seed,
-                       void* workspace, size_t workspace_bytes, void* stream);
+                       int window_left, int window_right, int dtype, float dropout_rate,
+                       unsigned long long seed, void* workspace, size_t workspace_bytes,
+                       void* stream);
 
 /* fa_status_string: a static, human-readable description of a status code. */
 const char* fa_status_string(int status);

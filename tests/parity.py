@@ -122,11 +122,11 @@ def run_cross(B, H, Hkv, Nq, Nk, d, dtype, causal, mask=None, seed=0, backward=T
 
 
 def run_varlen(lens_q, lens_k, H, Hkv, d, dtype, causal, seed=0, backward=True, dropout_rate=0.0,
-               drop_seed=0, max_q=None, max_k=None):
+               drop_seed=0, max_q=None, max_k=None, window=(-1, -1)):
     """Full comparison for a packed variable-length batch (fa_forward_varlen /
     fa_backward_varlen) against the oracle's per-sequence attention."""
     where = (f"lens_q={list(lens_q)} lens_k={list(lens_k)} H{H} Hkv{Hkv} d{d} {dtype} causal={causal} "
-             f"seed={seed}")
+             f"window={tuple(window)} seed={seed}")
     if dropout_rate:
         where += f" dropout={dropout_rate} drop_seed={drop_seed}"
     say("case", where)
@@ -139,18 +139,51 @@ def run_varlen(lens_q, lens_k, H, Hkv, d, dtype, causal, seed=0, backward=True, 
     mk = max(1, max(lens_k)) if max_k is None else max_k
     scale = 1.0 / math.sqrt(d)
     o, lse = binding.forward_varlen(q, k, v, cq, ck, mq, mk, scale, causal, dropout_rate=dropout_rate,
-                                    seed=drop_seed)
+                                    seed=drop_seed, window=window)
     torch.cuda.synchronize()
     qd, kd, vd = (np64(x[n]) for n in ("q", "k", "v"))
-    oref, lref = oracle.forward_varlen(qd, kd, vd, x["cu_q"], x["cu_k"], scale, causal, dropout_rate, drop_seed)
+    oref, lref = oracle.forward_varlen(qd, kd, vd, x["cu_q"], x["cu_k"], scale, causal, dropout_rate, drop_seed,
+                                       tuple(window))
     res = {"o": check_out(np64(o), oref, dtype, where), "lse": check_lse(np64(lse), lref, where)}
     if backward and dtype != "fp32":
         do = x["do"].to(dev)
         dq, dk, dv = binding.backward_varlen(q, k, v, o, lse, do, cq, ck, mq, mk, scale, causal,
-                                             dropout_rate=dropout_rate, seed=drop_seed)
+                                             dropout_rate=dropout_rate, seed=drop_seed, window=window)
         torch.cuda.synchronize()
         rq, rk, rv = oracle.backward_varlen(qd, kd, vd, np64(x["do"]), x["cu_q"], x["cu_k"], scale, causal,
-                                            dropout_rate, drop_seed)
+                                            dropout_rate, drop_seed, tuple(window))
+        res["dq"] = check_grad(np64(dq), rq, where + " dq")
+        res["dk"] = check_grad(np64(dk), rk, where + " dk")
+        res["dv"] = check_grad(np64(dv), rv, where + " dv")
+    return res
+
+
+def run_window(B, H, Hkv, Nq, Nk, d, dtype, causal, window, mask=None, seed=0, backward=True, dropout_rate=0.0,
+               drop_seed=0):
+    """Full comparison with a sliding-window band (fa_forward_qk / fa_backward_qk)."""
+    where = (f"B{B} H{H} Hkv{Hkv} Nq{Nq} Nk{Nk} d{d} {dtype} causal={causal} window={tuple(window)} "
+             f"mask={mask is not None} seed={seed}")
+    if dropout_rate:
+        where += f" dropout={dropout_rate} drop_seed={drop_seed}"
+    say("case", where)
+    x = I.make_cross(B, H, Hkv, Nq, Nk, d, dtype, seed, with_grad=backward)
+    dev = torch.device("cuda", 0)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    scale = 1.0 / math.sqrt(d)
+    mt = None if mask is None else torch.from_numpy(mask).to(dev)
+    o, lse = binding.forward(q, k, v, scale, causal, mt, dropout_rate=dropout_rate, seed=drop_seed, window=window)
+    torch.cuda.synchronize()
+    qd, kd, vd = (np64(x[n]) for n in ("q", "k", "v"))
+    oref, lref = oracle.forward(qd, kd, vd, scale, causal, mask, dropout_rate=dropout_rate, seed=drop_seed,
+                                window=tuple(window))
+    res = {"o": check_out(np64(o), oref, dtype, where), "lse": check_lse(np64(lse), lref, where)}
+    if backward and dtype != "fp32":
+        do = x["do"].to(dev)
+        dq, dk, dv = binding.backward(q, k, v, o, lse, do, scale, causal, mt, dropout_rate=dropout_rate,
+                                      seed=drop_seed, window=window)
+        torch.cuda.synchronize()
+        rq, rk, rv = oracle.backward(qd, kd, vd, np64(x["do"]), scale, causal, mask, dropout_rate=dropout_rate,
+                                     seed=drop_seed, window=tuple(window))
         res["dq"] = check_grad(np64(dq), rq, where + " dq")
         res["dk"] = check_grad(np64(dk), rk, where + " dk")
         res["dv"] = check_grad(np64(dv), rv, where + " dv")
