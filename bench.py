@@ -9,6 +9,11 @@ recomputed QK^T included), halved for causal masking.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--copy-mb MB] [--dropout RATE] [--packed]
+                       [--window W]
+
+--window W times sliding-window causal attention (each query sees itself and
+the W - 1 keys before it) on the workload's shape, FLOP counted from the
+visible pairs; not the headline configuration.
 
 --packed splits the workload's B * N tokens per head into a seeded
 document-like mix of sequence lengths and times the packed variable-length
@@ -101,6 +106,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="run the fused-dropout kernels at this rate (not the headline configuration)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding-window causal attention over the last W keys of each query (not the headline)")
     ap.add_argument("--packed", action="store_true",
                     help="time packed variable-length batches of the workload's tokens (not the headline)")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -156,6 +163,8 @@ def main():
     w = I.WORKLOADS[args.workload]
     if args.packed:
         return packed_main(args, w)
+    if args.window:
+        return window_main(args, w)
     dev = torch.device("cuda", 0)
     x = I.make(w)
     q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
@@ -256,6 +265,86 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(line), flush=True)
+
+
+def window_main(args, w):
+    """Sliding-window causal attention: each query sees itself and the W - 1
+    keys before it. FLOP are counted from the visible pairs, sum_i min(i + 1, W)
+    per (batch, head), 2 d FLOP per pair and contraction."""
+    import torch
+    from exact_attention_110_amd import binding
+    from exact_attention_110_amd import inputs as I
+
+    if w.sparse or w.dtype == "fp32" or not w.causal:
+        print("--window needs a dense causal 16-bit workload", file=sys.stderr)
+        sys.exit(2)
+    W = args.window
+    window = (W - 1, 0)
+    dev = torch.device("cuda", 0)
+    x = I.make(w, with_grad=True)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    ws = binding.workspace(q, k)
+    n = w.N
+    pairs = (W * (W + 1) // 2 + (n - W) * W) if n >= W else n * (n + 1) // 2
+    per = 2.0 * pairs * w.d * w.B * w.H
+    total_flop = 7 * per
+
+    def fwd():
+        binding.forward(q, k, v, w.scale, True, None, out=o, lse=lse, window=window)
+
+    def bwd():
+        binding.backward(q, k, v, o, lse, do, w.scale, True, None, ws=ws, grads=grads, window=window)
+
+    def timed(fn, n_it):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(n_it):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / n_it
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    value = total_flop / (ms * 1e-3) / 1e12
+    t_fwd = timed(fwd, max(args.steps, 5))
+    t_bwd = timed(bwd, max(args.steps, 5))
+    print(f"[bench] {w.name} window {W}: {ms:.3f} ms/step, {value:.1f} TFLOP/s (forward {t_fwd:.3f} ms, "
+          f"backward {t_bwd:.3f} ms)", file=sys.stderr, flush=True)
+    achieved = 2 * per / (t_fwd * 1e-3) / 1e12
+    line = {
+        "metric": "sliding-window causal attention fwd+bwd TFLOP/s (visible-pair FLOP)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}_window{W}", "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "window": [W - 1, 0], "flop_per_step": total_flop, "fwd_ms": round(t_fwd, 4),
+                   "bwd_ms": round(t_bwd, 4)},
+        "roofline": {"bound": "mfma", "kernel": "forward (one launch)", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "launch_ms": round(t_fwd, 4), "flop_per_launch": 2 * per},
+    }
     print(json.dumps(line), flush=True)
 
 
