@@ -195,3 +195,26 @@ def length_mix(batch, mean, seed, lo=1):
     from an exponential distribution of the given mean, at least lo."""
     x = np.random.default_rng(seed).exponential(mean, size=batch)
     return [max(lo, int(round(v))) for v in x]
+
+
+def quantize_e4m3(x):
+    """Per-tensor FP8 (E4M3) quantisation of a float32 numpy array: descale =
+    max|x| / 448 (the format's largest finite value), codes = x / descale
+    rounded to nearest-even by PyTorch's float8_e4m3fn conversion. Returns
+    (uint8 CPU torch tensor of codes, descale)."""
+    import torch
+    amax = float(np.abs(x).max()) if x.size else 0.0
+    descale = amax / 448.0 if amax > 0 else 1.0
+    codes = torch.from_numpy(np.ascontiguousarray(x / np.float32(descale), dtype=np.float32))
+    return codes.to(torch.float8_e4m3fn).view(torch.uint8), descale
+
+
+def make_fp8(B, H, Hkv, N, d, seed, sigma=1.0):
+    """Seeded FP8 inputs: the same normal draws as ``make_small`` (Q, K, V in
+    that order), each quantised per tensor with ``quantize_e4m3``. Returns a
+    dict with q, k, v (uint8 codes) and q_descale, k_descale, v_descale."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name, shape in (("q", (B, H, N, d)), ("k", (B, Hkv, N, d)), ("v", (B, Hkv, N, d))):
+        out[name], out[name + "_descale"] = quantize_e4m3(draw(shape, rng, sigma))
+    return out

@@ -37,3 +37,4 @@ from .attention import (  # noqa: F401
     backward_varlen,
 )
 from . import dropout  # noqa: F401
+from . import fp8  # noqa: F401

@@ -811,6 +811,50 @@ def pin_window_finite_differences():
     case(140, 140, False, (60, 10), 860, np.array([[1, 1], [0, 1]], dtype=np.uint8))
 
 
+# ----------------------------------------------------------------------------------------------
+# P-18: FP8 (E4M3) inputs: the decoder against PyTorch's float8_e4m3fn and the format's closed
+# forms; the per-tensor descales enter as the definition says
+# ----------------------------------------------------------------------------------------------
+def pin_e4m3_decode():
+    import torch
+    import oracle.fp8 as F8
+    codes = np.arange(256, dtype=np.uint8)
+    ours = F8.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+    assert np.array_equal(np.signbit(ours[fin]), np.signbit(ref[fin]))      # -0 for 0x80
+    assert ours[0x38] == 1.0 and ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6
+    assert np.isnan(ours[0x7F]) and np.isnan(ours[0xFF]) and ours[0xC0] == -2.0
+    # codes round-trip through PyTorch's encoder
+    vals = ours[fin & (codes != 0x80)]
+    back = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(F8.e4m3_decode(back), vals)
+
+
+def pin_fp8_descales():
+    import torch
+    import oracle.fp8 as F8
+    rng = np.random.default_rng(901)
+    B, H, n, d = 1, 2, 150, 16
+    q8, k8, v8 = (torch.from_numpy(rng.normal(0, 2, size=(B, H, n, d))).to(torch.float8_e4m3fn)
+                  .view(torch.uint8).numpy() for _ in range(3))
+    o1, l1 = F8.forward_fp8(q8, k8, v8, 0.3, 1.0, 1.0, 1.0, True)
+    # the same as attention of the decoded values, which are those PyTorch decodes
+    dec = [torch.from_numpy(x).view(torch.float8_e4m3fn).to(torch.float64).numpy() for x in (q8, k8, v8)]
+    o0, l0 = A.forward(dec[0], dec[1], dec[2], 0.3, True)
+    assert np.array_equal(o1, o0) and np.array_equal(l1, l0)
+    # q and k descales enter the scores only through their product with the scale
+    o2, l2 = F8.forward_fp8(q8, k8, v8, 0.3, 4.0, 0.25, 1.0, True)
+    o3, l3 = F8.forward_fp8(q8, k8, v8, 0.6, 1.0, 0.5, 1.0, True)
+    assert np.abs(o2 - o1).max() <= 1e-13 and np.abs(l2 - l1).max() <= 1e-13
+    assert np.abs(o3 - o1).max() <= 1e-13 and np.abs(l3 - l1).max() <= 1e-13
+    # the value descale scales the output only
+    o4, l4 = F8.forward_fp8(q8, k8, v8, 0.3, 1.0, 1.0, 3.0, True)
+    assert np.abs(o4 - 3.0 * o1).max() <= 1e-13 and np.array_equal(l4, l1)
+
+
 ALL_PINS = [pin_worked_example, pin_recurrence, pin_brute_force, pin_rows_sum_to_one, pin_zero_query,
             pin_dominant_score, pin_permutation, pin_causal_locality, pin_finite_differences,
             pin_gqa_repeat, pin_mask_semantics, pin_empty_rows, pin_scale_zero, pin_torch_sdpa,
@@ -818,4 +862,4 @@ ALL_PINS = [pin_worked_example, pin_recurrence, pin_brute_force, pin_rows_sum_to
             pin_dropout_finite_differences, pin_cross_lengths_brute_force, pin_cross_lengths_suffix,
             pin_cross_lengths_finite_differences, pin_varlen_brute_force, pin_varlen_finite_differences,
             pin_varlen_dropout_streams, pin_window_brute_force, pin_window_torch_sdpa, pin_window_limits,
-            pin_window_finite_differences]
+            pin_window_finite_differences, pin_e4m3_decode, pin_fp8_descales]

@@ -89,3 +89,38 @@ def test_mutant_is_caught(name, monkeypatch):
         except Exception:          # an assertion or a crash both expose the mistake
             caught.append(pin.__name__)
     assert caught, f"no pin detects mutant {name}"
+
+
+SRC_FP8 = os.path.join(os.path.dirname(SRC), "fp8.py")
+
+MUTANTS_FP8 = {
+    "e4m3_bias_8": ("(e - 7)", "(e - 8)"),
+    "e4m3_subnormal_exponent": ("np.ldexp(m / 8.0, -6)", "np.ldexp(m / 8.0, -7)"),
+    "e4m3_no_nan": ("return np.where((c & 0x7F) == 0x7F, np.nan, v)", "return v"),
+    "e4m3_sign_lost": ("sign = np.where(c & 0x80, -1.0, 1.0)", "sign = 1.0"),
+    "fp8_k_descale_dropped": ("k = e4m3_decode(k8) * float(k_descale)", "k = e4m3_decode(k8)"),
+    "fp8_v_descale_on_q": ("q = e4m3_decode(q8) * float(q_descale)",
+                           "q = e4m3_decode(q8) * float(q_descale) * float(v_descale)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS_FP8))
+def test_fp8_mutant_is_caught(name, monkeypatch):
+    import sys
+    import oracle
+    old, new = MUTANTS_FP8[name]
+    src = open(SRC_FP8).read()
+    assert src.count(old) >= 1, old
+    mod = types.ModuleType("oracle.fp8")
+    mod.__file__ = SRC_FP8
+    mod.__package__ = "oracle"
+    exec(compile(src.replace(old, new), SRC_FP8 + " (mutant)", "exec"), mod.__dict__)
+    monkeypatch.setitem(sys.modules, "oracle.fp8", mod)
+    monkeypatch.setattr(oracle, "fp8", mod)
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            pin()
+        except Exception:
+            caught.append(pin.__name__)
+    assert caught, f"no pin detects mutant {name}"
