@@ -9,8 +9,10 @@ recomputed QK^T included), halved for causal masking.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--copy-mb MB] [--dropout RATE] [--packed]
-                       [--window W]
+                       [--window W] [--fp8]
 
+--fp8 times the FP8 (E4M3) forward pass (fa_forward_fp8) on the workload's
+shape against the 16-bit forward; not the headline configuration.
 --window W times sliding-window causal attention (each query sees itself and
 the W - 1 keys before it) on the workload's shape, FLOP counted from the
 visible pairs; not the headline configuration.
@@ -106,6 +108,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="run the fused-dropout kernels at this rate (not the headline configuration)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the FP8 (E4M3) forward pass on the workload's shape (not the headline)")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding-window causal attention over the last W keys of each query (not the headline)")
     ap.add_argument("--packed", action="store_true",
@@ -165,6 +169,8 @@ def main():
         return packed_main(args, w)
     if args.window:
         return window_main(args, w)
+    if args.fp8:
+        return fp8_main(args, w)
     dev = torch.device("cuda", 0)
     x = I.make(w)
     q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
@@ -265,6 +271,79 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(line), flush=True)
+
+
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 MFMA
+
+
+def fp8_main(args, w):
+    """FP8 (E4M3) forward pass over the workload's shape: inputs quantised per
+    tensor from the same seeded draws; the 16-bit forward of the unquantised
+    inputs is timed beside it. FLOP as for the forward of the headline (two
+    contractions, halved under causal masking)."""
+    import torch
+    from exact_attention_110_amd import binding
+    from exact_attention_110_amd import inputs as I
+
+    if w.sparse or w.dtype == "fp32" or w.d not in (64, 128):
+        print("--fp8 needs a dense 16-bit workload with d 64 or 128", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda", 0)
+    x8 = I.make_fp8(w.B, w.H, w.Hkv, w.N, w.d, w.seed)
+    q8, k8, v8 = (x8[n].to(dev) for n in ("q", "k", "v"))
+    o8 = torch.empty(q8.shape, dtype=torch.bfloat16, device=dev)
+    l8 = torch.empty(q8.shape[:3], dtype=torch.float32, device=dev)
+    x = I.make(w, with_grad=False)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    o, lse = torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    fwd_flop = flops(w, False)
+
+    def f8():
+        binding.forward_fp8(q8, k8, v8, x8["q_descale"], x8["k_descale"], x8["v_descale"], w.scale, w.causal,
+                            out=o8, lse=l8)
+
+    def f16():
+        binding.forward(q, k, v, w.scale, w.causal, None, out=o, lse=lse)
+
+    def timed(fn, n_it):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(n_it):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / n_it
+
+    t8 = timed(f8, max(args.steps, 5))
+    t16 = timed(f16, max(args.steps, 5))
+    v8 = fwd_flop / (t8 * 1e-3) / 1e12
+    v16 = fwd_flop / (t16 * 1e-3) / 1e12
+    print(f"[bench] {w.name} forward: fp8 {t8:.3f} ms ({v8:.1f} TFLOP/s), {w.dtype} {t16:.3f} ms ({v16:.1f} TFLOP/s)",
+          file=sys.stderr, flush=True)
+    line = {
+        "metric": "FP8 (E4M3) attention forward TFLOP/s",
+        "value": round(v8, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": max(args.steps, 5),
+        "warmup": args.warmup,
+        "ms_per_step": round(t8, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}_fp8_forward", "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "passes": "fwd", "flop_per_step": fwd_flop,
+                   "forward_16bit_ms": round(t16, 4), "forward_16bit_tflops": round(v16, 2)},
+        "roofline": {"bound": "mfma", "kernel": "fwd_fp8_kernel", "achieved": round(v8, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(v8 / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                     "launch_ms": round(t8, 4), "flop_per_launch": fwd_flop},
+    }
     print(json.dumps(line), flush=True)
 
 

@@ -67,6 +67,8 @@ def load():
     lib.fa_backward_varlen.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, I, I, I, F,
                                        U64, P, S, P]
     lib.fa_backward_varlen.restype = I
+    lib.fa_forward_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, F, F, F, F, I, I, P]
+    lib.fa_forward_fp8.restype = I
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -285,3 +287,29 @@ def backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_
     if st != 0:
         raise FAError(st, "fa_backward_varlen")
     return dq, dk, dv
+
+
+def forward_fp8(q, k, v, q_descale, k_descale, v_descale, scale=None, causal=False, out_dtype=torch.bfloat16,
+                out=None, lse=None):
+    """O, LSE of attention over FP8 (E4M3) inputs (fa_forward_fp8).
+
+    q [B,H,N,d], k, v [B,Hkv,N,d]: uint8 codes (or float8_e4m3fn tensors);
+    the real inputs are codes times their descales. O has out_dtype."""
+    q, k, v = (t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t for t in (q, k, v))
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[2:] != q.shape[2:]:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.uint8:
+            raise ValueError(f"{name} must be a contiguous device tensor of E4M3 codes")
+    if out_dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("out_dtype must be bfloat16 or float16")
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty(q.shape, dtype=out_dtype, device=q.device) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = load().fa_forward_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, k.shape[1], N, d, scale,
+                               float(q_descale), float(k_descale), float(v_descale), int(bool(causal)),
+                               _DTYPES[out_dtype], _stream(q.device))
+    if st != 0:
+        raise FAError(st, "fa_forward_fp8")
+    return o, lse_t

@@ -15,11 +15,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfa.so")
-SOURCES = ["api.hip", "fwd.hip", "bwd.hip"]
+SOURCES = ["api.hip", "fwd.hip", "bwd.hip", "fp8.hip"]
 # Kernel translation units never produce or test for NaN on purpose, so the
 # compiler may drop the NaN quieting it otherwise inserts around every float
 # max; the argument checks in api.hip keep full IEEE semantics.
-PER_FILE = {"fwd.hip": ["-fno-honor-nans"], "bwd.hip": ["-fno-honor-nans"]}
+PER_FILE = {"fwd.hip": ["-fno-honor-nans"], "bwd.hip": ["-fno-honor-nans"], "fp8.hip": ["-fno-honor-nans"]}
 
 ARCH = "gfx950"
 FLAGS = [

@@ -314,6 +314,35 @@ int fa_backward_varlen(const void* q, const void* k, const void* v, const void* 
                        dtype, dropout_rate, seed, workspace, workspace_bytes, stream);
 }
 
+int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int Hkv, int N, int d, float scale, float q_descale, float k_descale,
+                   float v_descale, int causal, int out_dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u))
+    return FA_ERR_INVALID_ARG;
+  if (out_dtype != FA_BF16 && out_dtype != FA_F16) return FA_ERR_INVALID_ARG;
+  const Geo g = fixed_geo(B, H, Hkv, N, N, d);
+  int st = check_shape(g, scale, out_dtype);
+  if (st != FA_OK) return st;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;  // the FP8 contraction takes 64 values at a time
+  for (float x : {q_descale, k_descale, v_descale})
+    if (!isfinite(x) || !(x > 0.f)) return FA_ERR_INVALID_ARG;
+  Band band;
+  make_band(causal, -1, -1, &band);
+  fa::Fp8FwdArgs a;
+  a.s = make_shape(g, scale, band, nullptr);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.q_descale = q_descale;
+  a.k_descale = k_descale;
+  a.v_descale = v_descale;
+  (void)hipGetLastError();
+  return fa::launch_forward_fp8(a, out_dtype, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
@@ -325,6 +354,6 @@ const char* fa_status_string(int status) {
   }
 }
 
-int fa_version(void) { return 103; }
+int fa_version(void) { return 104; }
 
 }  // extern "C"

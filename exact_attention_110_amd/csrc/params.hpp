@@ -105,8 +105,21 @@ __device__ __forceinline__ SeqView seq_view(const AttnShape& s, int b, int h, in
   return v;
 }
 
+// FP8 forward: q, k, v hold OCP E4M3 codes; the real inputs are code value
+// times the tensor's descale. o is 16-bit (out dtype), lse float.
+struct Fp8FwdArgs {
+  AttnShape s;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float q_descale, k_descale, v_descale;
+};
+
 // Internal launchers (return a hipError_t from the launch).
 hipError_t launch_forward(const FwdArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_forward_fp8(const Fp8FwdArgs& a, int out_dtype, hipStream_t stream);
 hipError_t launch_backward_stage(int stage, const BwdArgs& a, int dtype, hipStream_t stream);
 
 }  // namespace fa

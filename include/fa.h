@@ -254,6 +254,31 @@ int fa_backward_varlen(const void* q, const void* k, const void* v, const void* 
                        unsigned long long seed, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/*
+ * FP8 forward (pranaymahendrakar.com lesson "FlashAttention", version lineage:
+ * FlashAttention-3 adds an FP8 forward pass; the pages fix no format, so this
+ * is the reading taken). q, k, v hold OCP E4M3 codes (one byte each: sign,
+ * exponent bias 7, 3 mantissa bits, subnormals, 0x7F / 0xFF NaN, largest
+ * finite 448) with one float descale per tensor: the attention computed is
+ * that of the real inputs code * q_descale, code * k_descale and
+ * code * v_descale, with S = scale * Q K^T as for fa_forward. Both
+ * contractions run on the FP8 matrix cores; the probabilities are rounded to
+ * E4M3 (nearest even) before they weight V, the running sum and LSE use them
+ * unrounded, so O carries that rounding (relative 2^-4 per probability at
+ * most) and LSE does not.
+ *   q : [B][H][N][d] bytes     k, v : [B][Hkv][N][d] bytes (16-byte aligned)
+ *   o : [B][H][N][d] of out_dtype (FA_BF16 or FA_F16)   lse : [B][H][N] float
+ *   d : 64 or 128 (others FA_ERR_UNSUPPORTED)
+ *   q_descale, k_descale, v_descale : finite and > 0
+ *   causal : as for fa_forward
+ * Other limits, ownership and errors as for fa_forward; no block mask,
+ * window or dropout, and no backward pass.
+ */
+int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Hkv, int N, int d, float scale,
+                   float q_descale, float k_descale, float v_descale,
+                   int causal, int out_dtype, void* stream);
+
 /* fa_status_string: a static, human-readable description of a status code. */
 const char* fa_status_string(int status);
 

@@ -188,3 +188,92 @@ def run_window(B, H, Hkv, Nq, Nk, d, dtype, causal, window, mask=None, seed=0, b
         res["dk"] = check_grad(np64(dk), rk, where + " dk")
         res["dv"] = check_grad(np64(dv), rv, where + " dv")
     return res
+
+
+# The FP8 matrix instruction (v_mfma_f32_32x32x64_f8f6f4) sums its 64 exact
+# E4M3 products less precisely than float32 does: measured over 65536 random
+# dot products, its error reached 2294 * 2^-24 * sum|products| (a sequential
+# float32 sum: 2.45 * 2^-24). The bars below take FP8_SUM = 2^-11 relative to
+# sum|products|, 3.6 times the largest measured, per score.
+FP8_SUM = 2.0 ** -11
+
+
+def fp8_score_error(qd, kd, scale, rows=None):
+    """Per-row bound on the error of any of the row's scores."""
+    qs = qd if rows is None else qd[rows]
+    return FP8_SUM * scale * (np.abs(qs) @ np.abs(kd).T).max(axis=1)
+
+
+def fp8_bound(qd, kd, vd, scale, causal, o_ref, rows=None):
+    """Per-element bound on |O - O_ref| of the FP8 forward, derived from its
+    arithmetic: each probability p (relative to its row maximum) is rounded to
+    E4M3 before it weights V: at most 2^-4 p for a normal code, and for
+    p < 2^-6, where the code may be subnormal (spacing 2^-9), at most
+    max(2^-4 p, min(p, 2^-10)). The row is divided by l = 1 / (normalised
+    maximum), so that part is P_max[r] * sum_j e_j |v_jc|. Score errors ds
+    (``fp8_score_error``) change every weight by a factor within exp(+-2 ds)
+    (the score and the normaliser), adding 2.1 ds sum_j P_j |v_jc|; the 16-bit
+    rounding of O adds 2^-8 |O| (half an ulp and the float32 sums), and 2e-5
+    covers the float32 exponentials."""
+    p, _ = oracle.head_probabilities(qd, kd, scale, causal, rows=rows)
+    pmax = p.max(axis=1, keepdims=True)
+    rel = np.divide(p, pmax, out=np.zeros_like(p), where=pmax > 0)
+    e = np.where(rel >= 2.0 ** -6, 2.0 ** -4 * rel, np.maximum(2.0 ** -4 * rel, np.minimum(rel, 2.0 ** -10)))
+    ds = fp8_score_error(qd, kd, scale, rows)[:, None]
+    return pmax * (e @ np.abs(vd)) + 2.1 * ds * (p @ np.abs(vd)) + 2.0 ** -8 * np.abs(o_ref) + 2e-5
+
+
+def fp8_lse_bound(qd, kd, scale, lse_ref, rows=None):
+    """Bound on |LSE - LSE_ref| of the FP8 forward: LSE moves no more than its
+    largest score error (``fp8_score_error``); the float32 running sum of n
+    probabilities adds n 2^-24 relative to l, and the float32 steps of the
+    scale product, exp2, log2 and the final multiply a few ulps of |LSE|. The
+    float32 bar 1e-5 applies where it is the larger."""
+    n = kd.shape[0]
+    b = (fp8_score_error(qd, kd, scale, rows) + (n + 8) * 2.0 ** -24
+         + 8 * 2.0 ** -24 * np.abs(np.nan_to_num(lse_ref)) + 1e-6)
+    return np.maximum(b, TOL_LSE)
+
+
+def run_fp8(B, H, Hkv, N, d, causal, seed=0, out_dtype="bf16", heads=None, rows=None):
+    """FP8 forward against the oracle on the decoded inputs: O within the
+    derived per-element bound, LSE within 1e-5."""
+    where = f"fp8 B{B} H{H} Hkv{Hkv} N{N} d{d} causal={causal} out={out_dtype} seed={seed}"
+    say("case", where)
+    import oracle.fp8 as F8
+    x = I.make_fp8(B, H, Hkv, N, d, seed)
+    dev = torch.device("cuda", 0)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    scale = 1.0 / math.sqrt(d)
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[out_dtype]
+    o, lse = binding.forward_fp8(q, k, v, x["q_descale"], x["k_descale"], x["v_descale"], scale, causal,
+                                 out_dtype=tdt)
+    torch.cuda.synchronize()
+    o, lse = np64(o), np64(lse)
+    G = H // Hkv
+    hl = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    worst = 0.0
+    for b, h in hl:
+        qd = F8.e4m3_decode(x["q"][b, h].numpy()) * x["q_descale"]
+        kd = F8.e4m3_decode(x["k"][b, h // G].numpy()) * x["k_descale"]
+        vd = F8.e4m3_decode(x["v"][b, h // G].numpy()) * x["v_descale"]
+        oref, lref = oracle.head_forward(qd, kd, vd, scale, causal, rows=rows)
+        ob = o[b, h] if rows is None else o[b, h][rows]
+        lb = lse[b, h] if rows is None else lse[b, h][rows]
+        assert np.all(np.isfinite(ob)), f"{where}: non-finite O"
+        bound = fp8_bound(qd, kd, vd, scale, causal, oref, rows)
+        err = np.abs(ob - oref)
+        ratio = float((err / bound).max())
+        worst = max(worst, ratio)
+        assert ratio <= 1.0, f"{where} head ({b},{h}): O error {float(err.max()):.3g} exceeds its bound (ratio {ratio:.3g})"
+        lb_tol = fp8_lse_bound(qd, kd, scale, lref, rows)
+        fin = np.isfinite(lref)
+        assert np.array_equal(np.isneginf(lb), np.isneginf(lref)), f"{where}: -inf rows differ"
+        lerr = np.abs(lb[fin] - lref[fin])
+        if not np.all(lerr <= lb_tol[fin]):
+            rr = np.flatnonzero(fin)[np.argmax(lerr - lb_tol[fin])]
+            raise AssertionError(f"{where} head ({b},{h}): LSE error {float(np.abs(lb[rr] - lref[rr])):.3g} at row "
+                                 f"{rr} (LSE {float(lref[rr]):.4f}, kernel {float(lb[rr]):.6f}) exceeds its bound "
+                                 f"{float(lb_tol[rr]):.3g}; rows over the bound: {int((lerr > lb_tol[fin]).sum())}")
+    say(f"  worst error / bound {worst:.3f}")
+    return worst

@@ -49,7 +49,7 @@ def test_exports_every_declared_symbol(lib):
     assert {"fa_forward", "fa_backward", "fa_backward_workspace_size", "fa_backward_stage",
             "fa_status_string", "fa_version", "fa_forward_dropout", "fa_backward_dropout",
             "fa_backward_stage_dropout", "fa_forward_qk", "fa_backward_qk", "fa_forward_varlen",
-            "fa_backward_varlen"} <= set(names)
+            "fa_backward_varlen", "fa_forward_fp8"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -227,3 +227,18 @@ def test_varlen_backward_checks(lib):
     assert bwd_var(lib, dtype=F32) == EUNSUP
     assert bwd_var(lib, ws_bytes=ws_size(lib, B=3, N=50) - 1) == EWS
     assert bwd_var(lib, mq=0) == EINVAL
+
+
+def fwd8(lib, d=128, out=BF16, qd=1.0, kd=1.0, vd=1.0, N=256, q=GOOD, lse=GOOD):
+    return lib.fa_forward_fp8(q, GOOD, GOOD, GOOD, lse, 1, 2, 1, N, d, 0.125, qd, kd, vd, 1, out, None)
+
+
+@pytest.mark.parametrize("bad", [dict(out=F32), dict(out=7), dict(qd=0.0), dict(kd=-1.0), dict(vd=float("nan")),
+                                 dict(qd=float("inf")), dict(N=0), dict(d=48), dict(q=None), dict(q=ODD),
+                                 dict(lse=P((1 << 20) + 2))])
+def test_fp8_rejects(lib, bad):
+    assert fwd8(lib, **bad) == EINVAL
+
+
+def test_fp8_head_sizes(lib):
+    assert fwd8(lib, d=32) == EUNSUP   # the FP8 contraction takes 64 values at a time
