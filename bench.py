@@ -74,6 +74,7 @@ KERNEL_SOURCES = {
     "bwd_pre_kernel": ["bwd.hip", "common.hpp", "params.hpp"],
     "bwd_kv_kernel": ["bwd.hip", "common.hpp", "params.hpp"],
     "bwd_q_kernel": ["bwd.hip", "common.hpp", "params.hpp"],
+    "fwd_fp8_kernel": ["fp8.hip", "common.hpp", "params.hpp"],
 }
 
 
