@@ -252,22 +252,21 @@ __global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
     const __attribute__((address_space(3))) float* ddl = lsel + BQ;
     const int thr = kj - offu - q0 - 4 * hh;   // first kept 8 (i / 4) + i % 4
     const int thr2 = kj - offl - q0 - 4 * hh;  // last kept (with a lower edge)
+    // dropout: byte r of dwc[j4] decides query q0 + 8 j4 + 4 hh + r of key kj
+    unsigned int dwc[4];
+    if constexpr (DROP) drop_words_col4(s.seed0, s.seed1, bh, kj, q0 + 4 * hh, 8, dwc);
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       const f32x4 L4 = *(const __attribute__((address_space(3))) f32x4*)(lsel + 8 * j4 + 4 * hh);
       const f32x4 D4 = *(const __attribute__((address_space(3))) f32x4*)(ddl + 8 * j4 + 4 * hh);
       float p[4], d2[4];
-      Philox4 rnd;
-      if constexpr (DROP)  // queries q0 + 8 j4 + 4 hh + 0..3 of key kj: one call, byte kj & 3 of each word
-        rnd = philox4x32_10((unsigned)(q0 + 8 * j4 + 4 * hh) >> 2, (unsigned)kj >> 2, (unsigned)bh, 0u, s.seed0,
-                            s.seed1);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * j4 + r;
         float pv = fast_exp2(fmaf(sc[i], c, -L4[r]));
         if constexpr (MASKED) pv = (8 * j4 + r < thr || (LOWER && 8 * j4 + r > thr2)) ? 0.f : pv;
         if constexpr (DROP) {
-          const bool z = drop_keep(rnd.v[r], kj & 3, s.drop_t);
+          const bool z = drop_keep(dwc[j4], r, s.drop_t);
           p[r] = z ? pv * s.drop_scale : 0.f;
           d2[r] = pv * ((z ? dp[i] * s.drop_scale : 0.f) - D4[r]);
         } else {
@@ -565,6 +564,13 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
       const int thr = qi + offu - ks - 4 * hh;   // last kept 32 t2 + 8 (i / 4) + i % 4
       const int thr2 = qi + offl - ks - 4 * hh;  // first kept (with a lower edge)
       unsigned int sk[Q_T2][8];
+      // dropout words of row qi for key groups ks + 32 t2 + 8 g + 4 hh (g = 0..3)
+      unsigned int dwq[Q_T2][4];
+      if constexpr (DROP) {
+#pragma unroll
+        for (int t2 = 0; t2 < Q_T2; ++t2)
+          drop_words_row4(s.seed0, s.seed1, b * s.H + h, qi, ks + 32 * t2 + 4 * hh, 8, dwq[t2]);
+      }
       auto ds_tile = [&](auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
@@ -573,8 +579,7 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
           for (int j = 0; j < 8; ++j) {
             float v2[2];
             unsigned int wd = 0;
-            if constexpr (DROP)  // keys ks + 32 t2 + 8 (j / 2) + 4 hh + 0..3 of row qi
-              wd = drop_row_word(s.seed0, s.seed1, b * s.H + h, qi, ks + 32 * t2 + 8 * (j >> 1) + 4 * hh);
+            if constexpr (DROP) wd = dwq[t2][j >> 1];  // keys ks + 32 t2 + 8 (j / 2) + 4 hh + 0..3 of row qi
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
               const int i = 2 * j + r;

@@ -177,12 +177,66 @@ __device__ __forceinline__ Philox4 philox4x32_10(unsigned int c0, unsigned int c
   }
   return {{c0, c1, c2, c3}};
 }
-// The word holding keys kg .. kg + 3 (kg a multiple of 4) of query row qi.
-__device__ __forceinline__ unsigned int drop_row_word(unsigned int k0, unsigned int k1, int bh, int qi, int kg) {
-  const Philox4 r = philox4x32_10((unsigned)qi >> 2, (unsigned)kg >> 2, (unsigned)bh, 0u, k0, k1);
-  const int w = qi & 3;
-  return w == 0 ? r.v[0] : w == 1 ? r.v[1] : w == 2 ? r.v[2] : r.v[3];
+// The generator shared across a quad. In every kernel layout the four lanes
+// of a quad (lanes 4a .. 4a + 3) cover four consecutive query rows (or keys)
+// of one generator block and need the same four Philox calls; each lane
+// computes one of them and a 4 x 4 transpose across the quad hands every lane
+// its words, a quarter of the generator work.
+
+// x[c] of lane r becomes x[r] of lane c (r = lane & 3): two stages that swap
+// across lane distance 1 and 2 with quad-permute DPP moves.
+template <int CTRL>
+__device__ __forceinline__ unsigned int dpp_quad(unsigned int v) {
+  return (unsigned int)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
 }
+__device__ __forceinline__ void quad_transpose(unsigned int (&x)[4], int r) {
+  const bool h1 = (r & 1) != 0, h2 = (r & 2) != 0;
+#pragma unroll
+  for (int c0 = 0; c0 < 4; c0 += 2) {  // lanes r, r ^ 1 swap elements c0 + 1 and c0
+    const unsigned int t = dpp_quad<0xB1>(h1 ? x[c0] : x[c0 + 1]);
+    x[c0] = h1 ? t : x[c0];
+    x[c0 + 1] = h1 ? x[c0 + 1] : t;
+  }
+#pragma unroll
+  for (int c0 = 0; c0 < 2; ++c0) {     // lanes r, r ^ 2 swap elements c0 + 2 and c0
+    const unsigned int t = dpp_quad<0x4E>(h2 ? x[c0] : x[c0 + 2]);
+    x[c0] = h2 ? t : x[c0];
+    x[c0 + 2] = h2 ? x[c0 + 2] : t;
+  }
+}
+
+// Lane holds query row qi (qi & 3 == lane & 3) and needs, for the four key
+// groups kg0 + gs g (g = 0..3, kg0 and gs multiples of 4, equal across the
+// quad), the word of its row: w[g] afterwards.
+__device__ __forceinline__ void drop_words_row4(unsigned int k0, unsigned int k1, int bh, int qi, int kg0, int gs,
+                                                unsigned int (&w)[4]) {
+  const int r = qi & 3;
+  const Philox4 p = philox4x32_10((unsigned)qi >> 2, (unsigned)(kg0 + gs * r) >> 2, (unsigned)bh, 0u, k0, k1);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) w[c] = p.v[c];
+  quad_transpose(w, r);
+}
+
+// Lane holds key kj (kj & 3 == lane & 3) and needs, for the four query groups
+// qg0 + qs j (j = 0..3, multiples of 4, equal across the quad), the decisions
+// of rows qg0 + qs j + 0..3 for its key: byte r of w[j] afterwards is the byte
+// of row qg0 + qs j + r (a byte transpose inside the lane, then the quad's).
+__device__ __forceinline__ void drop_words_col4(unsigned int k0, unsigned int k1, int bh, int kj, int qg0, int qs,
+                                                unsigned int (&w)[4]) {
+  const int r = kj & 3;
+  const Philox4 p = philox4x32_10((unsigned)(qg0 + qs * r) >> 2, (unsigned)kj >> 2, (unsigned)bh, 0u, k0, k1);
+  // byte b of p.v[k] -> byte k of w[b]; perm(a, b, sel) picks bytes 0-3 from b, 4-7 from a
+  const unsigned int lo01 = __builtin_amdgcn_perm(p.v[1], p.v[0], 0x05010400u);  // v0.0 v1.0 v0.1 v1.1
+  const unsigned int hi01 = __builtin_amdgcn_perm(p.v[1], p.v[0], 0x07030602u);  // v0.2 v1.2 v0.3 v1.3
+  const unsigned int lo23 = __builtin_amdgcn_perm(p.v[3], p.v[2], 0x05010400u);
+  const unsigned int hi23 = __builtin_amdgcn_perm(p.v[3], p.v[2], 0x07030602u);
+  w[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+  w[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+  w[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+  w[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+  quad_transpose(w, r);
+}
+
 // keep decision of byte t (0..3) of a word
 __device__ __forceinline__ bool drop_keep(unsigned int word, int t, int thr) {
   return ((word >> (8 * t)) & 0xffu) >= (unsigned)thr;

@@ -231,6 +231,12 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
       const float m_use = (m == -INFINITY) ? 0.f : m;  // a row with no visible key yet
 
       unsigned int pk[2][8];
+      // dropout words of this row for key groups ks + 32 t2 + 8 g + 4 hh (g = 0..3)
+      unsigned int dw[2][4];
+      if constexpr (DROP) {
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) drop_words_row4(s.seed0, s.seed1, b * s.H + h, qi, ks + 32 * t2 + 4 * hh, 8, dw[t2]);
+      }
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
@@ -240,8 +246,7 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
           l += p0 + p1;  // the normaliser sums the probabilities before dropout
           if constexpr (DROP) {
             // elements 2j, 2j + 1 are keys kg + (2j & 3) + 0, 1 of group kg
-            const unsigned int wd =
-                drop_row_word(s.seed0, s.seed1, b * s.H + h, qi, ks + 32 * t2 + 8 * (j >> 1) + 4 * hh);
+            const unsigned int wd = dw[t2][j >> 1];
             const int t0 = (2 * j) & 3;
             pk[t2][j] = pack2<T>(drop_keep(wd, t0, s.drop_t) ? p0 * s.drop_scale : 0.f,
                                  drop_keep(wd, t0 + 1, s.drop_t) ? p1 * s.drop_scale : 0.f);
@@ -473,10 +478,11 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
   // probabilities in pk and this lane's share of their row sums in ls.
   // 16-bit probabilities of elements 2 jj, 2 jj + 1 of row block rb, with dropout
   // when built for it (keys ks + 8 (jj / 2) + 4 hh + (2 jj & 3) + 0, 1)
-  auto pack_p = [&](float p0, float p1, int rb, int jj, int ks) -> unsigned int {
+  // (dw: this row's dropout words for key groups ks + 8 g + 4 hh, g = 0..3,
+  // from drop_words_row4)
+  auto pack_p = [&](float p0, float p1, int jj, const unsigned int (&dw)[4]) -> unsigned int {
     if constexpr (DROP) {
-      const unsigned int wd =
-          drop_row_word(s.seed0, s.seed1, b * s.H + h, qw + 32 * rb + l32, ks + 8 * (jj >> 1) + 4 * hh);
+      const unsigned int wd = dw[jj >> 1];
       const int t0 = (2 * jj) & 3;
       return pack2<T>(drop_keep(wd, t0, s.drop_t) ? p0 * s.drop_scale : 0.f,
                       drop_keep(wd, t0 + 1, s.drop_t) ? p1 * s.drop_scale : 0.f);
@@ -499,12 +505,14 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
       mn[rb] = resc ? fmaxf(m[rb], mx[rb]) : m[rb];
       const float mu = mn[rb] == -INFINITY ? 0.f : mn[rb];  // a row with no visible key yet
       float sum = 0.f;
+      unsigned int dw[4];
+      if constexpr (DROP) drop_words_row4(s.seed0, s.seed1, b * s.H + h, qw + 32 * rb + l32, ks + 4 * hh, 8, dw);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float p0 = fast_exp2(fmaf(st[rb][2 * j], c, -mu));
         const float p1 = fast_exp2(fmaf(st[rb][2 * j + 1], c, -mu));
         sum += p0 + p1;
-        pk[rb][j] = pack_p(p0, p1, rb, j, ks);
+        pk[rb][j] = pack_p(p0, p1, j, dw);
       }
       ls[rb] = sum;
     }
@@ -553,12 +561,14 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         float sum = 0.f;
+        unsigned int dw[4];
+        if constexpr (DROP) drop_words_row4(s.seed0, s.seed1, b * s.H + h, qw + 32 * rb + l32, ks + 4 * hh, 8, dw);
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
           const float p0 = fast_exp2(fmaf(st[rb][2 * jj], c, -m[rb]));
           const float p1 = fast_exp2(fmaf(st[rb][2 * jj + 1], c, -m[rb]));
           sum += p0 + p1;
-          pk[rb][jj] = pack_p(p0, p1, rb, jj, ks);
+          pk[rb][jj] = pack_p(p0, p1, jj, dw);
         }
         l[rb] += sum;
       }
