@@ -96,8 +96,9 @@ struct StepPos {
   unsigned long long qoff;
 };
 
+// (d <= 64 halves the register operands and accumulators: two workgroups per CU)
 template <class T, int D, int BAND, bool MASK, bool DROP>
-__global__ __launch_bounds__(KV_NW * 64, 1) void bwd_kv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(KV_NW * 64, D <= 64 ? 2 : 1) void bwd_kv_kernel(BwdArgs a) {
   constexpr int BQ = KV_BQ;
   constexpr int QBUF = BQ * 2 * D;       // one Q or dO block, swizzled rows without padding
   constexpr int STB = 2 * BQ * 4;        // one statistics block: BQ log2-scaled LSE, then BQ D
