@@ -255,7 +255,11 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
           }
         }
       // O^T(d x q) += V^T(d x key) P^T(key x q); B operand k-slot j of step (t2, u)
-      // is key 32 t2 + 16 u + 8 (j / 4) + 4 hh + j % 4, matched by the V^T reads
+      // is key 32 t2 + 16 u + 8 (j / 4) + 4 hh + j % 4, matched by the V^T reads.
+      // The two waves of a SIMD run this block at raised priority, so that one
+      // wave's P V products issue back to back while the other computes its
+      // exponentials (measured: 5% faster at 32 heads x 8192, same-box)
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
@@ -268,6 +272,7 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
                                         pk[t2][4 * u + 3]);
             acc[dt] = mfma32<T>(va, pb, acc[dt]);
           }
+      __builtin_amdgcn_s_setprio(0);
     }
     lstore_tile(buf ^ 1);
     __syncthreads();
