@@ -31,6 +31,11 @@ Sources (cited by page title and section):
   is visible iff p - left <= j <= p + right, -1 meaning unbounded on that
   side; causal masking is the right bound 0. Band, causal and block masks
   combine by intersection.
+* Score modification: the same lesson section speaks of user functions that
+  modify scores (score_mod) inside the one tiled kernel, naming none. Read
+  here as the linear distance bias of ALiBi (Press, Smith and Lewis, 2022),
+  one slope per query head: s_ij += -slope_h * |i + (Nk - Nq) - j|, added to
+  the scaled score before the softmax; it has no gradient of its own.
 * Variable-length batches: the same glossary, "Sequence Length Flexibility"
   (arbitrary lengths, no padding). Read here as sequences packed one after
   another per head, each attending only within itself
@@ -107,15 +112,18 @@ def _chunks(rows, size):
         yield rows[i:i + size]
 
 
-def _row_softmax(q_rows, k_keys, scale, vis):
+def _row_softmax(q_rows, k_keys, scale, vis, bias=None):
     """Scores, probabilities and log-sum-exp of one chunk of rows.
 
-    s = scale * q k^T over the gathered keys, -inf where a key is invisible.
-    L = m + ln(sum exp(s - m)) with m the row maximum (the safe-softmax shift of
-    ``naive_attention``); p = exp(s - L). A row with no visible key has
-    L = -inf and p = 0 (nothing to attend to, so it contributes nothing).
+    s = scale * q k^T (+ bias) over the gathered keys, -inf where a key is
+    invisible. L = m + ln(sum exp(s - m)) with m the row maximum (the
+    safe-softmax shift of ``naive_attention``); p = exp(s - L). A row with no
+    visible key has L = -inf and p = 0 (nothing to attend to, so it
+    contributes nothing).
     """
     s = scale * (q_rows @ k_keys.T)
+    if bias is not None:
+        s = s + bias
     s = np.where(vis, s, -np.inf)
     m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
     has = np.isfinite(m)
@@ -128,16 +136,27 @@ def _row_softmax(q_rows, k_keys, scale, vis):
     return s, p, lse
 
 
-def head_probabilities(q, k, scale, causal=False, block_mask=None, rows=None, window=(-1, -1)):
+def alibi_bias(rows, keys, slope, offset):
+    """-slope * |i + offset - j| for query rows i and keys j (None for no slope)."""
+    if slope is None:
+        return None
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+    return -float(slope) * np.abs((rows[:, None] + offset) - keys[None, :]).astype(np.float64)
+
+
+def head_probabilities(q, k, scale, causal=False, block_mask=None, rows=None, window=(-1, -1), alibi=None):
     """Full probability rows P[rows, :] (Nk keys wide) of one query head.
 
-    q: [Nq, d] float64 query rows of the head, k: [Nk, d] keys of its kv head.
+    q: [Nq, d] float64 query rows of the head, k: [Nk, d] keys of its kv head;
+    alibi: this head's slope or None.
     """
     n = k.shape[0]
+    off = n - q.shape[0]
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
     keys = np.arange(n)
-    vis = visible(rows, keys, causal, block_mask, offset=n - q.shape[0], window=window)
-    _, p, lse = _row_softmax(q[rows], k, scale, vis)
+    vis = visible(rows, keys, causal, block_mask, offset=off, window=window)
+    _, p, lse = _row_softmax(q[rows], k, scale, vis, alibi_bias(rows, keys, alibi, off))
     return p, lse
 
 
@@ -153,7 +172,7 @@ def _drop(p, rows, keys, dropout):
 
 
 def head_forward(q, k, v, scale, causal=False, block_mask=None, rows=None, chunk=256, dropout=None,
-                 window=(-1, -1)):
+                 window=(-1, -1), alibi=None):
     """O and L for the given query rows of one head (q: [Nq, d], k, v: [Nk, d]).
 
     With dropout = (rate, seed, bh) the probabilities are dropped and rescaled
@@ -168,14 +187,15 @@ def head_forward(q, k, v, scale, causal=False, block_mask=None, rows=None, chunk
         keys = candidate_keys(ch, n, causal, block_mask, offset=off, window=window)
         if keys.size:
             vis = visible(ch, keys, causal, block_mask, offset=off, window=window)
-            _, p, l_ = _row_softmax(q[ch], k[keys], scale, vis)
+            _, p, l_ = _row_softmax(q[ch], k[keys], scale, vis, alibi_bias(ch, keys, alibi, off))
             o[pos:pos + ch.size] = _drop(p, ch, keys, dropout) @ v[keys]
             lse[pos:pos + ch.size] = l_
         pos += ch.size
     return o, lse
 
 
-def head_backward(q, k, v, do, scale, causal=False, block_mask=None, chunk=256, dropout=None, window=(-1, -1)):
+def head_backward(q, k, v, do, scale, causal=False, block_mask=None, chunk=256, dropout=None, window=(-1, -1),
+                  alibi=None):
     """Gradients of sum(O * dO) for one query head.
 
     With p the probability rows, g = dO, and (under dropout) r the dropped and
@@ -201,7 +221,7 @@ def head_backward(q, k, v, do, scale, causal=False, block_mask=None, chunk=256, 
         if keys.size == 0:
             continue
         vis = visible(ch, keys, causal, block_mask, offset=off, window=window)
-        _, p, _ = _row_softmax(q[ch], k[keys], scale, vis)
+        _, p, _ = _row_softmax(q[ch], k[keys], scale, vis, alibi_bias(ch, keys, alibi, off))
         g = do[ch]
         dv[keys] += _drop(p, ch, keys, dropout).T @ g
         dp = _drop(g @ v[keys].T, ch, keys, dropout)
@@ -219,7 +239,7 @@ def _heads(B, H, heads):
 
 
 def forward(q, k, v, scale, causal=False, block_mask=None, heads=None, rows=None, chunk=256,
-            dropout_rate=0.0, seed=0, window=(-1, -1)):
+            dropout_rate=0.0, seed=0, window=(-1, -1), alibi_slopes=None):
     """Attention forward over [B, H, Nq, d] queries and [B, Hkv, Nk, d] keys/values.
 
     Query head h reads kv head h // (H // Hkv). A block mask has
@@ -239,7 +259,7 @@ def forward(q, k, v, scale, causal=False, block_mask=None, heads=None, rows=None
     for b, h in hl:
         dr = (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None
         o, l_ = head_forward(q[b, h], k[b, h // G], v[b, h // G], scale, causal, block_mask, rows, chunk, dr,
-                             window)
+                             window, None if alibi_slopes is None else alibi_slopes[h])
         outs.append(o)
         lses.append(l_)
     o = np.stack(outs)
@@ -251,7 +271,7 @@ def forward(q, k, v, scale, causal=False, block_mask=None, heads=None, rows=None
 
 
 def backward(q, k, v, do, scale, causal=False, block_mask=None, heads=None, chunk=256,
-             dropout_rate=0.0, seed=0, window=(-1, -1)):
+             dropout_rate=0.0, seed=0, window=(-1, -1), alibi_slopes=None):
     """Gradients of sum(O * dO) with respect to q, k, v (dropout as in ``forward``).
 
     With ``heads=None`` returns full dq [B, H, Nq, d], dk, dv [B, Hkv, Nk, d]
@@ -272,13 +292,15 @@ def backward(q, k, v, do, scale, causal=False, block_mask=None, heads=None, chun
             for h in range(H):
                 dr = (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None
                 a, bk, bv = head_backward(q[b, h], k[b, h // G], v[b, h // G], do[b, h],
-                                          scale, causal, block_mask, chunk, dr, window)
+                                          scale, causal, block_mask, chunk, dr, window,
+                                          None if alibi_slopes is None else alibi_slopes[h])
                 dq[b, h] = a
                 dk[b, h // G] += bk
                 dv[b, h // G] += bv
         return dq, dk, dv
     res = [head_backward(q[b, h], k[b, h // G], v[b, h // G], do[b, h], scale, causal, block_mask, chunk,
-                         (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None, window)
+                         (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None, window,
+                         None if alibi_slopes is None else alibi_slopes[h])
            for b, h in _heads(B, H, heads)]
     return tuple(np.stack(x) for x in zip(*res))
 
@@ -290,7 +312,8 @@ def _spans(cu, total):
     return [(int(a), int(b)) for a, b in zip(cu[:-1], cu[1:])]
 
 
-def forward_varlen(q, k, v, cu_q, cu_k, scale, causal=False, dropout_rate=0.0, seed=0, window=(-1, -1)):
+def forward_varlen(q, k, v, cu_q, cu_k, scale, causal=False, dropout_rate=0.0, seed=0, window=(-1, -1),
+                   alibi_slopes=None):
     """Attention over packed variable-length sequences.
 
     q: [H, Tq, d], k, v: [Hkv, Tk, d]: per head, the rows of every sequence one
@@ -316,11 +339,13 @@ def forward_varlen(q, k, v, cu_q, cu_k, scale, causal=False, dropout_rate=0.0, s
         for h in range(H):
             dr = (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None
             o[h, q0:q1], lse[h, q0:q1] = head_forward(q[h, q0:q1], k[h // G, k0:k1], v[h // G, k0:k1], scale,
-                                                      causal, None, None, 256, dr, window)
+                                                      causal, None, None, 256, dr, window,
+                                                      None if alibi_slopes is None else alibi_slopes[h])
     return o, lse
 
 
-def backward_varlen(q, k, v, do, cu_q, cu_k, scale, causal=False, dropout_rate=0.0, seed=0, window=(-1, -1)):
+def backward_varlen(q, k, v, do, cu_q, cu_k, scale, causal=False, dropout_rate=0.0, seed=0, window=(-1, -1),
+                    alibi_slopes=None):
     """Gradients of sum(O * dO) for ``forward_varlen``: dq [H, Tq, d],
     dk, dv [Hkv, Tk, d] (summed over each kv head's group of query heads)."""
     H, Tq, d = q.shape
@@ -338,7 +363,8 @@ def backward_varlen(q, k, v, do, cu_q, cu_k, scale, causal=False, dropout_rate=0
         for h in range(H):
             dr = (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None
             a, bk, bv = head_backward(q[h, q0:q1], k[h // G, k0:k1], v[h // G, k0:k1], do[h, q0:q1], scale,
-                                      causal, None, 256, dr, window)
+                                      causal, None, 256, dr, window,
+                                      None if alibi_slopes is None else alibi_slopes[h])
             dq[h, q0:q1] = a
             dk[h // G, k0:k1] += bk
             dv[h // G, k0:k1] += bv

@@ -855,6 +855,123 @@ def pin_fp8_descales():
     assert np.abs(o4 - 3.0 * o1).max() <= 1e-13 and np.array_equal(l4, l1)
 
 
+# ----------------------------------------------------------------------------------------------
+# P-19: score modification, the ALiBi distance bias: s_ij += -slope_h |i + (Nk - Nq) - j|
+# ----------------------------------------------------------------------------------------------
+def _alibi_brute_force(q, k, v, scale, causal, slope, window=(-1, -1)):
+    nq, nk, dv = len(q), len(k), len(v[0])
+    outs, lses = [], []
+    for i in range(nq):
+        pos = i + nk - nq
+        keys = [j for j in range(nk) if (not causal or j <= pos) and (window[0] < 0 or j >= pos - window[0])
+                and (window[1] < 0 or j <= pos + window[1])]
+        if not keys:
+            outs.append([0.0] * dv)
+            lses.append(-math.inf)
+            continue
+        sc = [scale * sum(a * b for a, b in zip(q[i], k[j])) - slope * abs(pos - j) for j in keys]
+        mx = max(sc)
+        w = [math.exp(x - mx) for x in sc]
+        z = sum(w)
+        outs.append([sum(w[a] * v[j][t] for a, j in enumerate(keys)) / z for t in range(dv)])
+        lses.append(mx + math.log(z))
+    return np.array(outs), np.array(lses)
+
+
+def pin_alibi_brute_force():
+    seed = 950
+    for nq, nk in ((1, 1), (4, 4), (3, 7), (6, 2)):
+        for causal in (False, True):
+            for slope, window in ((0.5, (-1, -1)), (0.125, (2, -1)), (2.0, (-1, 1))):
+                seed += 1
+                q, k, v = _rand((nq, 3), seed), _rand((nk, 3), seed + 40), _rand((nk, 2), seed + 80)
+                o, l_ = A.forward(q[None, None], k[None, None], v[None, None], 0.7, causal, window=window,
+                                  alibi_slopes=[slope])
+                ob, lb = _alibi_brute_force(q.tolist(), k.tolist(), v.tolist(), 0.7, causal, slope, window)
+                assert np.abs(o[0, 0] - ob).max() <= 1e-12, (nq, nk, causal, slope, window)
+                fin = np.isfinite(lb)
+                assert np.array_equal(np.isinf(l_[0, 0]), ~fin)
+                assert np.abs(l_[0, 0][fin] - lb[fin]).max(initial=0.0) <= 1e-12
+
+
+def pin_alibi_torch_sdpa():
+    """PyTorch's float64 attention with the bias as an additive mask written out
+    element by element (-inf where causal masking hides a key); gradients
+    through autograd."""
+    import torch
+    import torch.nn.functional as F
+    for (B, H, Hkv, nq, nk, d, causal, seed) in [(1, 4, 2, 70, 70, 8, True, 961), (2, 2, 1, 40, 90, 4, False, 962),
+                                                 (1, 2, 2, 90, 40, 8, True, 963)]:
+        slopes = [2.0 ** (-8.0 * (h + 1) / H) for h in range(H)]
+        q, k, v = _rand((B, H, nq, d), seed), _rand((B, Hkv, nk, d), seed + 1), _rand((B, Hkv, nk, d), seed + 2)
+        g = _rand((B, H, nq, d), seed + 3)
+        bias = np.zeros((H, nq, nk))
+        for h in range(H):
+            for i in range(nq):
+                pos = i + nk - nq
+                for j in range(nk):
+                    bias[h, i, j] = -math.inf if (causal and j > pos) else -slopes[h] * abs(pos - j)
+        rows_any = np.isfinite(bias).any(axis=2)
+        G = H // Hkv
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        kk, vv = tk.repeat_interleave(G, dim=1), tv.repeat_interleave(G, dim=1)
+        to = F.scaled_dot_product_attention(tq, kk, vv, attn_mask=torch.tensor(bias)[None], scale=0.4)
+        to = torch.where(torch.tensor(rows_any)[None, :, :, None], to, torch.zeros_like(to))
+        to.backward(torch.tensor(g))
+        o, l_ = A.forward(q, k, v, 0.4, causal, alibi_slopes=slopes)
+        dq, dk, dv = A.backward(q, k, v, g, 0.4, causal, alibi_slopes=slopes)
+        assert np.abs(o - to.detach().numpy()).max() <= 1e-12
+        for a, b in ((dq, tq), (dk, tk), (dv, tv)):
+            assert np.abs(a - np.nan_to_num(b.grad.numpy())).max() <= 1e-12
+        sc = torch.tensor(q) @ torch.tensor(np.repeat(k, G, axis=1)).transpose(-1, -2) * 0.4 + torch.tensor(bias)[None]
+        ref = torch.logsumexp(sc, dim=-1).numpy()
+        fin = np.broadcast_to(rows_any[None], ref.shape)
+        assert np.abs(l_[fin] - ref[fin]).max() <= 1e-12
+
+
+def pin_alibi_limits():
+    n, d = 200, 6
+    q, k, v = (_rand((1, 2, n, d), s) for s in (971, 972, 973))
+    for causal in (False, True):
+        o0, l0 = A.forward(q, k, v, 0.5, causal)
+        o1, l1 = A.forward(q, k, v, 0.5, causal, alibi_slopes=[0.0, 0.0])
+        assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+        # a steep slope leaves (almost) only the key at distance 0: O -> v_i within 2 sum_j exp(-gap_j)
+        slope = 60.0
+        o2, _ = A.forward(q, k, v, 0.5, causal, alibi_slopes=[slope, slope])
+        s_ = 0.5 * np.einsum("bhid,bhjd->bhij", q, k)
+        gap = s_.diagonal(axis1=2, axis2=3)[..., None] - s_ + slope * np.abs(np.arange(n)[:, None] - np.arange(n)[None])
+        np.einsum("bhii->bhi", gap)[...] = np.inf
+        bound = 2 * np.exp(-gap).sum(axis=-1)[..., None] * np.abs(v).max()
+        assert np.all(np.abs(o2 - v) <= bound)
+
+
+def pin_alibi_finite_differences():
+    for causal, nq, nk, seed in ((True, 8, 8, 980), (False, 6, 11, 981)):
+        q = _rand((1, 2, nq, 3), seed)
+        k = _rand((1, 1, nk, 3), seed + 1)
+        v = _rand((1, 1, nk, 3), seed + 2)
+        g = _rand((1, 2, nq, 3), seed + 3)
+        sl = [0.7, 0.2]
+
+        def f(q_, k_, v_):
+            o, _ = A.forward(q_, k_, v_, 0.6, causal, alibi_slopes=sl)
+            return float((o * g).sum())
+
+        grads = A.backward(q, k, v, g, 0.6, causal, alibi_slopes=sl)
+        rng = np.random.default_rng(seed + 4)
+        for which, x in enumerate((q, k, v)):
+            for flat in rng.choice(x.size, size=12, replace=False):
+                idx = np.unravel_index(flat, x.shape)
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += 1e-6
+                xm[idx] -= 1e-6
+                ap, am = [q, k, v], [q, k, v]
+                ap[which], am[which] = xp, xm
+                num = (f(*ap) - f(*am)) / 2e-6
+                assert abs(num - grads[which][idx]) <= 1e-6 * max(1.0, abs(num)), ("qkv"[which], causal)
+
+
 ALL_PINS = [pin_worked_example, pin_recurrence, pin_brute_force, pin_rows_sum_to_one, pin_zero_query,
             pin_dominant_score, pin_permutation, pin_causal_locality, pin_finite_differences,
             pin_gqa_repeat, pin_mask_semantics, pin_empty_rows, pin_scale_zero, pin_torch_sdpa,
@@ -862,4 +979,5 @@ ALL_PINS = [pin_worked_example, pin_recurrence, pin_brute_force, pin_rows_sum_to
             pin_dropout_finite_differences, pin_cross_lengths_brute_force, pin_cross_lengths_suffix,
             pin_cross_lengths_finite_differences, pin_varlen_brute_force, pin_varlen_finite_differences,
             pin_varlen_dropout_streams, pin_window_brute_force, pin_window_torch_sdpa, pin_window_limits,
-            pin_window_finite_differences, pin_e4m3_decode, pin_fp8_descales]
+            pin_window_finite_differences, pin_e4m3_decode, pin_fp8_descales, pin_alibi_brute_force,
+            pin_alibi_torch_sdpa, pin_alibi_limits, pin_alibi_finite_differences]

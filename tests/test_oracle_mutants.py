@@ -53,6 +53,12 @@ MUTANTS = {
                                 "keys = keys[keys > rows.min() + offset - window[0]]"),
     "window_dropped_in_backward": ("        vis = visible(ch, keys, causal, block_mask, offset=off, window=window)\n        _, p, _ =",
                                    "        vis = visible(ch, keys, causal, block_mask, offset=off)\n        _, p, _ ="),
+    "alibi_sign": ("return -float(slope) * np.abs(", "return float(slope) * np.abs("),
+    "alibi_no_abs": ("np.abs((rows[:, None] + offset) - keys[None, :]).astype(np.float64)",
+                     "((rows[:, None] + offset) - keys[None, :]).astype(np.float64)"),
+    "alibi_no_offset": ("np.abs((rows[:, None] + offset) - keys[None, :])", "np.abs((rows[:, None]) - keys[None, :])"),
+    "alibi_dropped_in_backward": ("_, p, _ = _row_softmax(q[ch], k[keys], scale, vis, alibi_bias(ch, keys, alibi, off))",
+                                  "_, p, _ = _row_softmax(q[ch], k[keys], scale, vis)"),
     "varlen_dk_overwrite": ("dk[h // G, k0:k1] += bk", "dk[h // G, k0:k1] = bk"),
     "varlen_dropout_stream": ("dr = (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None\n            o[h, q0:q1]",
                               "dr = (dropout_rate, seed, h) if dropout_rate > 0 else None\n            o[h, q0:q1]"),
