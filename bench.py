@@ -9,13 +9,15 @@ recomputed QK^T included), halved for causal masking.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--copy-mb MB] [--dropout RATE] [--packed]
-                       [--window W] [--fp8]
+                       [--window W] [--alibi] [--fp8]
 
 --fp8 times the FP8 (E4M3) forward pass (fa_forward_fp8) on the workload's
 shape against the 16-bit forward; not the headline configuration.
 --window W times sliding-window causal attention (each query sees itself and
 the W - 1 keys before it) on the workload's shape, FLOP counted from the
 visible pairs; not the headline configuration.
+--alibi times causal attention with ALiBi's geometric slopes (one per head) on
+the workload's shape, alone or with --window; not the headline configuration.
 
 --packed splits the workload's B * N tokens per head into a seeded
 document-like mix of sequence lengths and times the packed variable-length
@@ -113,6 +115,8 @@ def parse():
                     help="time the FP8 (E4M3) forward pass on the workload's shape (not the headline)")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding-window causal attention over the last W keys of each query (not the headline)")
+    ap.add_argument("--alibi", action="store_true",
+                    help="causal attention with ALiBi's geometric slopes, one per head (not the headline)")
     ap.add_argument("--packed", action="store_true",
                     help="time packed variable-length batches of the workload's tokens (not the headline)")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -168,7 +172,7 @@ def main():
     w = I.WORKLOADS[args.workload]
     if args.packed:
         return packed_main(args, w)
-    if args.window:
+    if args.window or args.alibi:
         return window_main(args, w)
     if args.fp8:
         return fp8_main(args, w)
@@ -349,34 +353,38 @@ def fp8_main(args, w):
 
 
 def window_main(args, w):
-    """Sliding-window causal attention: each query sees itself and the W - 1
-    keys before it. FLOP are counted from the visible pairs, sum_i min(i + 1, W)
-    per (batch, head), 2 d FLOP per pair and contraction."""
+    """Sliding-window and / or ALiBi causal attention: with --window W each
+    query sees itself and the W - 1 keys before it, else every earlier key;
+    with --alibi the scores carry the distance bias of ALiBi's geometric slopes.
+    FLOP are counted from the visible pairs, sum_i min(i + 1, W) per
+    (batch, head), 2 d FLOP per pair and contraction."""
     import torch
     from exact_attention_110_amd import binding
     from exact_attention_110_amd import inputs as I
 
     if w.sparse or w.dtype == "fp32" or not w.causal:
-        print("--window needs a dense causal 16-bit workload", file=sys.stderr)
+        print("--window / --alibi need a dense causal 16-bit workload", file=sys.stderr)
         sys.exit(2)
-    W = args.window
-    window = (W - 1, 0)
+    n = w.N
+    W = args.window if args.window else n
+    window = (W - 1, 0) if args.window else (-1, -1)
     dev = torch.device("cuda", 0)
+    slopes = torch.from_numpy(I.geometric_slopes(w.H)).to(dev) if args.alibi else None
     x = I.make(w, with_grad=True)
     q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
     o, lse = torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     ws = binding.workspace(q, k)
-    n = w.N
     pairs = (W * (W + 1) // 2 + (n - W) * W) if n >= W else n * (n + 1) // 2
     per = 2.0 * pairs * w.d * w.B * w.H
     total_flop = 7 * per
 
     def fwd():
-        binding.forward(q, k, v, w.scale, True, None, out=o, lse=lse, window=window)
+        binding.forward(q, k, v, w.scale, True, None, out=o, lse=lse, window=window, alibi_slopes=slopes)
 
     def bwd():
-        binding.backward(q, k, v, o, lse, do, w.scale, True, None, ws=ws, grads=grads, window=window)
+        binding.backward(q, k, v, o, lse, do, w.scale, True, None, ws=ws, grads=grads, window=window,
+                         alibi_slopes=slopes)
 
     def timed(fn, n_it):
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -402,11 +410,13 @@ def window_main(args, w):
     value = total_flop / (ms * 1e-3) / 1e12
     t_fwd = timed(fwd, max(args.steps, 5))
     t_bwd = timed(bwd, max(args.steps, 5))
-    print(f"[bench] {w.name} window {W}: {ms:.3f} ms/step, {value:.1f} TFLOP/s (forward {t_fwd:.3f} ms, "
+    name = w.name + (f"_window{W}" if args.window else "") + ("_alibi" if args.alibi else "")
+    print(f"[bench] {name}: {ms:.3f} ms/step, {value:.1f} TFLOP/s (forward {t_fwd:.3f} ms, "
           f"backward {t_bwd:.3f} ms)", file=sys.stderr, flush=True)
     achieved = 2 * per / (t_fwd * 1e-3) / 1e12
+    kind = " ".join(x for x in ("sliding-window" if args.window else "", "ALiBi" if args.alibi else "") if x)
     line = {
-        "metric": "sliding-window causal attention fwd+bwd TFLOP/s (visible-pair FLOP)",
+        "metric": f"{kind} causal attention fwd+bwd TFLOP/s (visible-pair FLOP)",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -418,9 +428,9 @@ def window_main(args, w):
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{w.name}_window{W}", "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
-                   "window": [W - 1, 0], "flop_per_step": total_flop, "fwd_ms": round(t_fwd, 4),
-                   "bwd_ms": round(t_bwd, 4)},
+        "config": {"workload": name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "window": list(window), "alibi": "geometric" if args.alibi else None,
+                   "flop_per_step": total_flop, "fwd_ms": round(t_fwd, 4), "bwd_ms": round(t_bwd, 4)},
         "roofline": {"bound": "mfma", "kernel": "forward (one launch)", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "launch_ms": round(t_fwd, 4), "flop_per_launch": 2 * per},

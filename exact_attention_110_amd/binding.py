@@ -57,15 +57,15 @@ def load():
     lib.fa_backward_dropout.restype = I
     lib.fa_backward_stage_dropout.argtypes = [I] + bwd_drop
     lib.fa_backward_stage_dropout.restype = I
-    lib.fa_forward_qk.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, P, I, F, U64, P]
+    lib.fa_forward_qk.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, P, P, I, F, U64, P]
     lib.fa_forward_qk.restype = I
-    lib.fa_backward_qk.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, P, I, F, U64, P, S,
-                                   P]
+    lib.fa_backward_qk.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, P, P, I, F, U64, P,
+                                   S, P]
     lib.fa_backward_qk.restype = I
-    lib.fa_forward_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, I, I, I, F, U64, P]
+    lib.fa_forward_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, I, I, P, I, F, U64, P]
     lib.fa_forward_varlen.restype = I
-    lib.fa_backward_varlen.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, I, I, I, F,
-                                       U64, P, S, P]
+    lib.fa_backward_varlen.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, I, I, P, I,
+                                       F, U64, P, S, P]
     lib.fa_backward_varlen.restype = I
     lib.fa_forward_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, F, F, F, F, I, I, P]
     lib.fa_forward_fp8.restype = I
@@ -131,23 +131,35 @@ def _seed(seed):
     return int(seed) & (2**64 - 1)
 
 
+def _slopes(alibi_slopes, H, device):
+    """None, or the ALiBi slopes as a contiguous float32 [H] device tensor."""
+    if alibi_slopes is None:
+        return None
+    t = torch.as_tensor(alibi_slopes, dtype=torch.float32).to(device).contiguous()
+    if t.dim() != 1 or t.numel() != H:
+        raise ValueError(f"alibi_slopes must hold one slope per query head ({H})")
+    return t
+
+
 def forward(q, k, v, scale=None, causal=False, block_mask=None, out=None, lse=None, dropout_rate=0.0,
-            seed=0, window=(-1, -1)):
+            seed=0, window=(-1, -1), alibi_slopes=None):
     """O, LSE = attention(q, k, v); q [B,H,Nq,d], k, v [B,Hkv,Nk,d] on the GPU.
 
-    Nq == Nk without a window calls fa_forward (fa_forward_dropout with a
-    positive dropout_rate); otherwise fa_forward_qk (causal masking aligned to
-    the last query; window = (left, right), -1 unbounded)."""
+    Nq == Nk without a window or ALiBi slopes calls fa_forward
+    (fa_forward_dropout with a positive dropout_rate); otherwise fa_forward_qk
+    (causal masking aligned to the last query; window = (left, right), -1
+    unbounded; alibi_slopes: one slope per query head)."""
     B, H, Hkv, N, Nk, d = _shape4(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     m = _mask(block_mask, N, q.device, Nk)
     wl, wr = (int(x) for x in window)
-    if Nk != N or (wl, wr) != (-1, -1):
+    al = _slopes(alibi_slopes, H, q.device)
+    if Nk != N or (wl, wr) != (-1, -1) or al is not None:
         st = load().fa_forward_qk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, Hkv, N, Nk, d, scale,
-                                  int(bool(causal)), wl, wr, _ptr(m), _DTYPES[q.dtype], float(dropout_rate),
-                                  _seed(seed), _stream(q.device))
+                                  int(bool(causal)), wl, wr, _ptr(al), _ptr(m), _DTYPES[q.dtype],
+                                  float(dropout_rate), _seed(seed), _stream(q.device))
         if st != 0:
             raise FAError(st, "fa_forward_qk")
         return o, lse_t
@@ -185,10 +197,10 @@ def _bwd_args(q, k, v, o, lse, do, dq, dk, dv, scale, causal, m, ws, drop=None):
 
 
 def backward(q, k, v, o, lse, do, scale=None, causal=False, block_mask=None, ws=None, grads=None,
-             dropout_rate=0.0, seed=0, window=(-1, -1)):
+             dropout_rate=0.0, seed=0, window=(-1, -1), alibi_slopes=None):
     """dq, dk, dv of sum(O * do), recomputing P from q, k and lse (and, with a
     positive dropout_rate, the forward call's keep decisions from seed).
-    Nq != Nk or a window calls fa_backward_qk."""
+    Nq != Nk, a window or ALiBi slopes call fa_backward_qk."""
     B, H, Hkv, N, Nk, d = _shape4(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     for name, t in (("o", o), ("do", do)):
@@ -198,11 +210,12 @@ def backward(q, k, v, o, lse, do, scale=None, causal=False, block_mask=None, ws=
     ws = workspace(q, k) if ws is None else ws
     dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     wl, wr = (int(x) for x in window)
-    if Nk != N or (wl, wr) != (-1, -1):
+    al = _slopes(alibi_slopes, H, q.device)
+    if Nk != N or (wl, wr) != (-1, -1) or al is not None:
         st = load().fa_backward_qk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
-                                   _ptr(dv), B, H, Hkv, N, Nk, d, scale, int(bool(causal)), wl, wr, _ptr(m),
-                                   _DTYPES[q.dtype], float(dropout_rate), _seed(seed), _ptr(ws), ws.numel(),
-                                   _stream(q.device))
+                                   _ptr(dv), B, H, Hkv, N, Nk, d, scale, int(bool(causal)), wl, wr, _ptr(al),
+                                   _ptr(m), _DTYPES[q.dtype], float(dropout_rate), _seed(seed), _ptr(ws),
+                                   ws.numel(), _stream(q.device))
         if st != 0:
             raise FAError(st, "fa_backward_qk")
         return dq, dk, dv
@@ -250,23 +263,25 @@ def _varlen_shape(q, k, v, cu_seqlens_q, cu_seqlens_k):
 
 
 def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale=None, causal=False,
-                   out=None, lse=None, dropout_rate=0.0, seed=0, window=(-1, -1)):
+                   out=None, lse=None, dropout_rate=0.0, seed=0, window=(-1, -1), alibi_slopes=None):
     """O [H, total_q, d], LSE [H, total_q] of packed sequences (fa_forward_varlen)."""
     B, H, Hkv, tq, tk, d = _varlen_shape(q, k, v, cu_seqlens_q, cu_seqlens_k)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((H, tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    al = _slopes(alibi_slopes, H, q.device)
     st = load().fa_forward_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), _ptr(cu_seqlens_q),
                                   _ptr(cu_seqlens_k), B, H, Hkv, tq, tk, int(max_seqlen_q), int(max_seqlen_k), d,
-                                  scale, int(bool(causal)), int(window[0]), int(window[1]), _DTYPES[q.dtype],
-                                  float(dropout_rate), _seed(seed), _stream(q.device))
+                                  scale, int(bool(causal)), int(window[0]), int(window[1]), _ptr(al),
+                                  _DTYPES[q.dtype], float(dropout_rate), _seed(seed), _stream(q.device))
     if st != 0:
         raise FAError(st, "fa_forward_varlen")
     return o, lse_t
 
 
 def backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale=None,
-                    causal=False, ws=None, grads=None, dropout_rate=0.0, seed=0, window=(-1, -1)):
+                    causal=False, ws=None, grads=None, dropout_rate=0.0, seed=0, window=(-1, -1),
+                    alibi_slopes=None):
     """dq, dk, dv of packed sequences (fa_backward_varlen)."""
     B, H, Hkv, tq, tk, d = _varlen_shape(q, k, v, cu_seqlens_q, cu_seqlens_k)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -279,11 +294,12 @@ def backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_
             raise ValueError("no backward for these arguments")
         ws = torch.empty(n, dtype=torch.uint8, device=q.device)
     dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    al = _slopes(alibi_slopes, H, q.device)
     st = load().fa_backward_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
                                    _ptr(dv), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, H, Hkv, tq, tk,
                                    int(max_seqlen_q), int(max_seqlen_k), d, scale, int(bool(causal)),
-                                   int(window[0]), int(window[1]), _DTYPES[q.dtype], float(dropout_rate),
-                                   _seed(seed), _ptr(ws), ws.numel(), _stream(q.device))
+                                   int(window[0]), int(window[1]), _ptr(al), _DTYPES[q.dtype],
+                                   float(dropout_rate), _seed(seed), _ptr(ws), ws.numel(), _stream(q.device))
     if st != 0:
         raise FAError(st, "fa_backward_varlen")
     return dq, dk, dv

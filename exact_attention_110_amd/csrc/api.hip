@@ -97,6 +97,7 @@ fa::AttnShape make_shape(const Geo& g, float scale, const Band& band, const uint
   s.drop_t = 0;
   s.drop_scale = 1.f;
   s.seed0 = s.seed1 = 0;
+  s.alibi = nullptr;
   return s;
 }
 
@@ -146,10 +147,11 @@ int check_backward(const void* q, const void* k, const void* v, const void* o, c
 }
 
 int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, const Geo& g,
-                 float scale, int causal, int window_left, int window_right, const uint8_t* block_mask,
-                 int dtype, float rate, unsigned long long seed, void* stream) {
+                 float scale, int causal, int window_left, int window_right, const float* alibi,
+                 const uint8_t* block_mask, int dtype, float rate, unsigned long long seed, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u))
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u) ||
+      ((uintptr_t)alibi & 3u))
     return FA_ERR_INVALID_ARG;
   int st = check_shape(g, scale, dtype);
   if (st != FA_OK) return st;
@@ -158,6 +160,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   if (!make_band(causal, window_left, window_right, &band)) return FA_ERR_INVALID_ARG;
   fa::FwdArgs a;
   a.s = make_shape(g, scale, band, block_mask);
+  a.s.alibi = alibi;
   if (!set_dropout(a.s, rate, seed)) return FA_ERR_INVALID_ARG;
   if (a.s.drop_t > 0 && dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   a.q = q;
@@ -171,9 +174,10 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
 
 int stage_impl(int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dO, void* dq, void* dk, void* dv, const Geo& g, float scale, int causal,
-               int window_left, int window_right, const uint8_t* block_mask, int dtype, float rate,
-               unsigned long long seed, void* workspace, size_t workspace_bytes, void* stream) {
+               int window_left, int window_right, const float* alibi, const uint8_t* block_mask, int dtype,
+               float rate, unsigned long long seed, void* workspace, size_t workspace_bytes, void* stream) {
   if (stage < 0 || stage > 2) return FA_ERR_INVALID_ARG;
+  if ((uintptr_t)alibi & 3u) return FA_ERR_INVALID_ARG;
   int st = check_backward(q, k, v, o, lse, dO, dq, dk, dv, g, scale, block_mask, dtype, workspace,
                           workspace_bytes);
   if (st != FA_OK) return st;
@@ -181,6 +185,7 @@ int stage_impl(int stage, const void* q, const void* k, const void* v, const voi
   if (!make_band(causal, window_left, window_right, &band)) return FA_ERR_INVALID_ARG;
   fa::BwdArgs a;
   a.s = make_shape(g, scale, band, block_mask);
+  a.s.alibi = alibi;
   if (!set_dropout(a.s, rate, seed)) return FA_ERR_INVALID_ARG;
   a.q = q;
   a.k = k;
@@ -200,11 +205,12 @@ int stage_impl(int stage, const void* q, const void* k, const void* v, const voi
 
 int backward_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
                   const void* dO, void* dq, void* dk, void* dv, const Geo& g, float scale, int causal,
-                  int window_left, int window_right, const uint8_t* block_mask, int dtype, float rate,
-                  unsigned long long seed, void* workspace, size_t workspace_bytes, void* stream) {
+                  int window_left, int window_right, const float* alibi, const uint8_t* block_mask,
+                  int dtype, float rate, unsigned long long seed, void* workspace, size_t workspace_bytes,
+                  void* stream) {
   for (int stage = 0; stage < 3; ++stage) {
     int st = stage_impl(stage, q, k, v, o, lse, dO, dq, dk, dv, g, scale, causal, window_left, window_right,
-                        block_mask, dtype, rate, seed, workspace, workspace_bytes, stream);
+                        alibi, block_mask, dtype, rate, seed, workspace, workspace_bytes, stream);
     if (st != FA_OK) return st;
   }
   return FA_OK;
@@ -223,7 +229,7 @@ size_t fa_backward_workspace_size(int B, int H, int Hkv, int N, int d, int dtype
 int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                int Hkv, int N, int d, float scale, int causal, const uint8_t* block_mask,
                int dtype, void* stream) {
-  return forward_impl(q, k, v, o, lse, fixed_geo(B, H, Hkv, N, N, d), scale, causal, -1, -1, block_mask, dtype,
+  return forward_impl(q, k, v, o, lse, fixed_geo(B, H, Hkv, N, N, d), scale, causal, -1, -1, nullptr, block_mask, dtype,
                       0.f, 0ull, stream);
 }
 
@@ -231,27 +237,28 @@ int fa_forward_dropout(const void* q, const void* k, const void* v, void* o, flo
                        int H, int Hkv, int N, int d, float scale, int causal,
                        const uint8_t* block_mask, int dtype, float dropout_rate,
                        unsigned long long seed, void* stream) {
-  return forward_impl(q, k, v, o, lse, fixed_geo(B, H, Hkv, N, N, d), scale, causal, -1, -1, block_mask, dtype,
+  return forward_impl(q, k, v, o, lse, fixed_geo(B, H, Hkv, N, N, d), scale, causal, -1, -1, nullptr, block_mask, dtype,
                       dropout_rate, seed, stream);
 }
 
 int fa_forward_qk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                   int Hkv, int Nq, int Nk, int d, float scale, int causal, int window_left,
-                  int window_right, const uint8_t* block_mask, int dtype, float dropout_rate,
-                  unsigned long long seed, void* stream) {
+                  int window_right, const float* alibi_slopes, const uint8_t* block_mask, int dtype,
+                  float dropout_rate, unsigned long long seed, void* stream) {
   return forward_impl(q, k, v, o, lse, fixed_geo(B, H, Hkv, Nq, Nk, d), scale, causal, window_left, window_right,
-                      block_mask, dtype, dropout_rate, seed, stream);
+                      alibi_slopes, block_mask, dtype, dropout_rate, seed, stream);
 }
 
 int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                       const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H, int Hkv,
                       int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d,
-                      float scale, int causal, int window_left, int window_right, int dtype,
-                      float dropout_rate, unsigned long long seed, void* stream) {
+                      float scale, int causal, int window_left, int window_right,
+                      const float* alibi_slopes, int dtype, float dropout_rate, unsigned long long seed,
+                      void* stream) {
   if (!cu_seqlens_q || !cu_seqlens_k) return FA_ERR_INVALID_ARG;
   const Geo g{B, H, Hkv, max_seqlen_q, max_seqlen_k, d, cu_seqlens_q, cu_seqlens_k, total_q, total_k};
-  return forward_impl(q, k, v, o, lse, g, scale, causal, window_left, window_right, nullptr, dtype, dropout_rate,
-                      seed, stream);
+  return forward_impl(q, k, v, o, lse, g, scale, causal, window_left, window_right, alibi_slopes, nullptr, dtype,
+                      dropout_rate, seed, stream);
 }
 
 int fa_backward_stage(int stage, const void* q, const void* k, const void* v, const void* o,
@@ -259,7 +266,7 @@ int fa_backward_stage(int stage, const void* q, const void* k, const void* v, co
                       int Hkv, int N, int d, float scale, int causal, const uint8_t* block_mask,
                       int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return stage_impl(stage, q, k, v, o, lse, dO, dq, dk, dv, fixed_geo(B, H, Hkv, N, N, d), scale, causal,
-                    -1, -1, block_mask, dtype, 0.f, 0ull, workspace, workspace_bytes, stream);
+                    -1, -1, nullptr, block_mask, dtype, 0.f, 0ull, workspace, workspace_bytes, stream);
 }
 
 int fa_backward_stage_dropout(int stage, const void* q, const void* k, const void* v,
@@ -269,7 +276,7 @@ int fa_backward_stage_dropout(int stage, const void* q, const void* k, const voi
                               float dropout_rate, unsigned long long seed, void* workspace,
                               size_t workspace_bytes, void* stream) {
   return stage_impl(stage, q, k, v, o, lse, dO, dq, dk, dv, fixed_geo(B, H, Hkv, N, N, d), scale, causal,
-                    -1, -1, block_mask, dtype, dropout_rate, seed, workspace, workspace_bytes, stream);
+                    -1, -1, nullptr, block_mask, dtype, dropout_rate, seed, workspace, workspace_bytes, stream);
 }
 
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -277,7 +284,7 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                 float scale, int causal, const uint8_t* block_mask, int dtype, void* workspace,
                 size_t workspace_bytes, void* stream) {
   return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, fixed_geo(B, H, Hkv, N, N, d), scale, causal,
-                       -1, -1, block_mask, dtype, 0.f, 0ull, workspace, workspace_bytes, stream);
+                       -1, -1, nullptr, block_mask, dtype, 0.f, 0ull, workspace, workspace_bytes, stream);
 }
 
 int fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,
@@ -287,17 +294,17 @@ int fa_backward_dropout(const void* q, const void* k, const void* v, const void*
                         unsigned long long seed, void* workspace, size_t workspace_bytes,
                         void* stream) {
   return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, fixed_geo(B, H, Hkv, N, N, d), scale, causal,
-                       -1, -1, block_mask, dtype, dropout_rate, seed, workspace, workspace_bytes, stream);
+                       -1, -1, nullptr, block_mask, dtype, dropout_rate, seed, workspace, workspace_bytes, stream);
 }
 
 int fa_backward_qk(const void* q, const void* k, const void* v, const void* o, const float* lse,
                    const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int Nq,
                    int Nk, int d, float scale, int causal, int window_left, int window_right,
-                   const uint8_t* block_mask, int dtype, float dropout_rate,
+                   const float* alibi_slopes, const uint8_t* block_mask, int dtype, float dropout_rate,
                    unsigned long long seed, void* workspace, size_t workspace_bytes,
                    void* stream) {
   return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, fixed_geo(B, H, Hkv, Nq, Nk, d), scale, causal,
-                       window_left, window_right, block_mask, dtype, dropout_rate, seed, workspace,
+                       window_left, window_right, alibi_slopes, block_mask, dtype, dropout_rate, seed, workspace,
                        workspace_bytes, stream);
 }
 
@@ -305,13 +312,13 @@ int fa_backward_varlen(const void* q, const void* k, const void* v, const void* 
                        const float* lse, const void* dO, void* dq, void* dk, void* dv,
                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int H, int Hkv,
                        int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d,
-                       float scale, int causal, int window_left, int window_right, int dtype,
-                       float dropout_rate, unsigned long long seed, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       float scale, int causal, int window_left, int window_right,
+                       const float* alibi_slopes, int dtype, float dropout_rate, unsigned long long seed,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   if (!cu_seqlens_q || !cu_seqlens_k) return FA_ERR_INVALID_ARG;
   const Geo g{B, H, Hkv, max_seqlen_q, max_seqlen_k, d, cu_seqlens_q, cu_seqlens_k, total_q, total_k};
-  return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, g, scale, causal, window_left, window_right, nullptr,
-                       dtype, dropout_rate, seed, workspace, workspace_bytes, stream);
+  return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, g, scale, causal, window_left, window_right,
+                       alibi_slopes, nullptr, dtype, dropout_rate, seed, workspace, workspace_bytes, stream);
 }
 
 int fa_forward_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -354,6 +361,6 @@ const char* fa_status_string(int status) {
   }
 }
 
-int fa_version(void) { return 104; }
+int fa_version(void) { return 105; }
 
 }  // extern "C"

@@ -97,7 +97,7 @@ struct StepPos {
 };
 
 // (d <= 64 halves the register operands and accumulators: two workgroups per CU)
-template <class T, int D, int BAND, bool MASK, bool DROP>
+template <class T, int D, int BAND, bool MASK, bool DROP, bool ALIBI>
 __global__ __launch_bounds__(KV_NW * 64, D <= 64 ? 2 : 1) void bwd_kv_kernel(BwdArgs a) {
   constexpr int BQ = KV_BQ;
   constexpr int QBUF = BQ * 2 * D;       // one Q or dO block, swizzled rows without padding
@@ -245,6 +245,8 @@ __global__ __launch_bounds__(KV_NW * 64, D <= 64 ? 2 : 1) void bwd_kv_kernel(Bwd
   // nothing of theirs is stored.
   // With dropout (z the keep decision, c its scale): P V uses z c P, and
   // dS = P (z c dP - D), the gradient flowing to P through the dropped values.
+  // ALiBi adds -slope log2(e) |query + off - kj| of the step's query head to
+  // the log2-unit score (a constant bias: dS is unchanged in form).
   auto probs = [&](auto masked, const f32x16& sc, const f32x16& dp, int q0, int stb, int bh, unsigned int (&pk)[8],
                    unsigned int (&sk)[8]) {
     constexpr bool MASKED = decltype(masked)::value;
@@ -256,6 +258,8 @@ __global__ __launch_bounds__(KV_NW * 64, D <= 64 ? 2 : 1) void bwd_kv_kernel(Bwd
     // dropout: byte r of dwc[j4] decides query q0 + 8 j4 + 4 hh + r of key kj
     unsigned int dwc[4];
     if constexpr (DROP) drop_words_col4(s.seed0, s.seed1, bh, kj, q0 + 4 * hh, 8, dwc);
+    const float nsl2 = ALIBI ? -s.alibi[bh - b * s.H] * kLog2e : 0.f;
+    const int dbase = q0 + 4 * hh + off - kj;  // query + off - kj less 8 (i / 4) + i % 4
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       const f32x4 L4 = *(const __attribute__((address_space(3))) f32x4*)(lsel + 8 * j4 + 4 * hh);
@@ -264,7 +268,8 @@ __global__ __launch_bounds__(KV_NW * 64, D <= 64 ? 2 : 1) void bwd_kv_kernel(Bwd
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * j4 + r;
-        float pv = fast_exp2(fmaf(sc[i], c, -L4[r]));
+        const float sh = ALIBI ? fmaf(nsl2, fabsf((float)(dbase + 8 * j4 + r)), -L4[r]) : -L4[r];
+        float pv = fast_exp2(fmaf(sc[i], c, sh));
         if constexpr (MASKED) pv = (8 * j4 + r < thr || (LOWER && 8 * j4 + r > thr2)) ? 0.f : pv;
         if constexpr (DROP) {
           const bool z = drop_keep(dwc[j4], r, s.drop_t);
@@ -430,7 +435,7 @@ constexpr int Q_T2 = Q_BN / 32;      // 32-key halves per tile
 constexpr int Q_R = 128 / Q_BN;      // tiles per 128-key mask block
 static_assert(Q_BM == 128, "a query-block workgroup must cover exactly one mask block row");
 
-template <class T, int D, int BAND, bool MASK, bool DROP>
+template <class T, int D, int BAND, bool MASK, bool DROP, bool ALIBI>
 __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
   constexpr int KBUF = Q_BN * 2 * D;     // K tile: swizzled rows, row reads and transposing reads
   constexpr int VBUF = Q_BN * 2 * D;     // V tile: swizzled rows, row reads
@@ -467,6 +472,7 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
   const int qw = q0 + 32 * w;
   const int qi = qw + l32;   // this lane's query row
   const float c = s.scale * kLog2e;
+  const float nsl2 = ALIBI ? -s.alibi[h] * kLog2e : 0.f;  // ALiBi slope, log2 units
 
   // Q^T and dO^T operands: lane holds query qi, d = 16 ss + 8 hh + 0..7
   s16x8 qf[NS], gf[NS];
@@ -572,6 +578,7 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
         for (int t2 = 0; t2 < Q_T2; ++t2)
           drop_words_row4(s.seed0, s.seed1, b * s.H + h, qi, ks + 32 * t2 + 4 * hh, 8, dwq[t2]);
       }
+      const float dqf = (float)(qi + off - ks - 4 * hh);  // ALiBi distance less the element's key offset
       auto ds_tile = [&](auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
@@ -584,7 +591,9 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
               const int i = 2 * j + r;
-              float pv = fast_exp2(fmaf(sc[t2][i], c, -lse2));
+              const float kofs = (float)(32 * t2 + 8 * (i >> 2) + (i & 3));
+              const float sh = ALIBI ? fmaf(nsl2, fabsf(dqf - kofs), -lse2) : -lse2;
+              float pv = fast_exp2(fmaf(sc[t2][i], c, sh));
               if constexpr (MASKED) {
                 const int kidx = 32 * t2 + 8 * (i >> 2) + (i & 3);
                 pv = (kidx > thr || (LOWER && kidx < thr2)) ? 0.f : pv;
@@ -649,8 +658,13 @@ template <class T, int D, int BAND, bool DROP>
 static hipError_t launch_kv_t3(const BwdArgs& a, hipStream_t st) {
   const dim3 grid(a.s.Hkv, (a.s.Nk + KV_BKV - 1) / KV_BKV, a.s.B);
   const dim3 block(KV_NW * 64);
-  if (a.s.mask) hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, true, DROP>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, false, DROP>), grid, block, 0, st, a);
+  if (a.s.alibi) {
+    if (a.s.mask) hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, true, DROP, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, false, DROP, true>), grid, block, 0, st, a);
+  } else {
+    if (a.s.mask) hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, true, DROP, false>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, false, DROP, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 
@@ -670,8 +684,13 @@ template <class T, int D, int BAND, bool DROP>
 static hipError_t launch_q_t3(const BwdArgs& a, hipStream_t st) {
   const dim3 grid(a.s.H, (a.s.Nq + Q_BM - 1) / Q_BM, a.s.B);
   const dim3 block(Q_NW * 64);
-  if (a.s.mask) hipLaunchKernelGGL((bwd_q_kernel<T, D, BAND, true, DROP>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((bwd_q_kernel<T, D, BAND, false, DROP>), grid, block, 0, st, a);
+  if (a.s.alibi) {
+    if (a.s.mask) hipLaunchKernelGGL((bwd_q_kernel<T, D, BAND, true, DROP, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((bwd_q_kernel<T, D, BAND, false, DROP, true>), grid, block, 0, st, a);
+  } else {
+    if (a.s.mask) hipLaunchKernelGGL((bwd_q_kernel<T, D, BAND, true, DROP, false>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((bwd_q_kernel<T, D, BAND, false, DROP, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 

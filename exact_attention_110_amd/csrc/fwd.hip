@@ -44,7 +44,7 @@ constexpr int FWD_BN = 64;            // keys per tile
 constexpr int FWD_LIST = 2048;        // capacity of the compacted mask-block list
 static_assert(FWD_BM == 128, "a forward workgroup must cover exactly one mask block row");
 
-template <class T, int D, int BAND, bool MASK, bool DROP>
+template <class T, int D, int BAND, bool MASK, bool DROP, bool ALIBI>
 __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
   constexpr int KP = D * 2 + 16;  // K row pitch in LDS, bytes (16 mod 128: conflict-free 16-byte reads)
   constexpr int VP = D * 2 + 32;  // V row pitch in LDS, bytes (32 mod 128: conflict-free transposing reads)
@@ -91,6 +91,12 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
   // exponent scale: S * c is the score in log2 units; a zero scale is kept just
   // above zero so that masked entries stay -inf (-inf * 0 would be NaN)
   const float c = fmaxf(s.scale * kLog2e, 1e-30f);
+  const float nsl2 = ALIBI ? -s.alibi[h] * kLog2e : 0.f;  // ALiBi slope of this head, log2 units
+  // Distance from the row to its nearest key, max(0, -(qi + off)): the bias is
+  // taken relative to it, which the softmax does not see, so that fp32 scores
+  // stay small where every key lies far from the diagonal (more queries than
+  // keys); the LSE gets the shift back at the end
+  const float dmin = ALIBI ? (float)max(0, -(qi + off)) : 0.f;
 
   // keys [kbeg, kend) are seen by some row of the workgroup: row q0 has the
   // lowest band start, the last row the highest band end
@@ -212,12 +218,25 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
             if ((BAND && key > qi + offu) || (LOWER && key < qi + offl) || key >= nk) sc[t2][i] = -INFINITY;
           }
       }
+      // ALiBi: the scores move to log2 units with the bias added, -slope log2(e)
+      // (|qi + off - key| - dmin); key - ks - 4 hh is a constant of the element
+      float cs = c;
+      if constexpr (ALIBI) {
+        const float dqf = (float)(qi + off - ks - 4 * hh);
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            sc[t2][i] = fmaf(sc[t2][i], c,
+                             nsl2 * (fabsf(dqf - (float)(32 * t2 + 8 * (i >> 2) + (i & 3))) - dmin));
+        cs = 1.f;
+      }
       float mx = sc[0][0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[0][i]);
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[1][i]);
-      mx = fmaxf(mx, swap_halves(mx)) * c;
+      mx = fmaxf(mx, swap_halves(mx)) * cs;
       if (__any(mx > m + kSlack)) {  // wave-uniform: raise the reference, rescale
         const float m_new = fmaxf(m, mx);
         const float corr = fast_exp2(m - ((m_new == -INFINITY) ? 0.f : m_new));
@@ -241,8 +260,8 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float p0 = fast_exp2(fmaf(sc[t2][2 * j], c, -m_use));
-          const float p1 = fast_exp2(fmaf(sc[t2][2 * j + 1], c, -m_use));
+          const float p0 = fast_exp2(fmaf(sc[t2][2 * j], cs, -m_use));
+          const float p1 = fast_exp2(fmaf(sc[t2][2 * j + 1], cs, -m_use));
           l += p0 + p1;  // the normaliser sums the probabilities before dropout
           if constexpr (DROP) {
             // elements 2j, 2j + 1 are keys kg + (2j & 3) + 0, 1 of group kg
@@ -280,7 +299,8 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
 
   const float lt = l + swap_halves(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  const float lse = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
+  float lse = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
+  if constexpr (ALIBI) lse = fmaf(-s.alibi[h], dmin, lse);
   const rsrc_t ro = make_rsrc((unsigned short*)a.o + qrow0 * D, qbytes);
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt)
@@ -712,6 +732,10 @@ __global__ __launch_bounds__(F32_R * F32_S) void fwd_f32_kernel(FwdArgs a) {
   const float* V = (const float*)a.v + krow0 * D;
   const int qi = q0 + r;
   const float c = fmaxf(s.scale * kLog2e, 1e-30f);
+  const float nsl2 = s.alibi ? -s.alibi[h] * kLog2e : 0.f;  // ALiBi slope, log2 units
+  // the bias is taken relative to the row's nearest key, max(0, -(qi + off))
+  // away, and the LSE gets that shift back (fp32 scores stay small)
+  const int dmin = s.alibi ? max(0, -(qi + off)) : 0;
   const int mrow = q0 / 128;  // every row of the workgroup is in this mask block row
 
   float q[D], o[D];
@@ -746,7 +770,7 @@ __global__ __launch_bounds__(F32_R * F32_S) void fwd_f32_kernel(FwdArgs a) {
           dot = fmaf(q[4 * d4 + 3], kv.w, dot);
         }
       }
-      x[t] = vis ? dot * c : -INFINITY;
+      x[t] = vis ? (s.alibi ? fmaf(dot, c, nsl2 * (float)(abs(qi + off - j) - dmin)) : dot * c) : -INFINITY;
       mx = fmaxf(mx, x[t]);
     }
     if (mx == -INFINITY) continue;  // nothing visible in this chunk for this row
@@ -802,21 +826,30 @@ __global__ __launch_bounds__(F32_R * F32_S) void fwd_f32_kernel(FwdArgs a) {
       for (int t = 0; t < F32_S; ++t) acc = fmaf(part[r][t][sp * DS + dd], wgt[t], acc);
       Op[dd] = acc * inv;
     }
-    if (sp == 0) a.lse[qrow0 + qi] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+    if (sp == 0) {
+      const float lse = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+      a.lse[qrow0 + qi] = s.alibi ? fmaf(-s.alibi[h], (float)dmin, lse) : lse;
+    }
   }
 }
 
 template <class T, int D, int BAND, bool DROP>
 static hipError_t launch_fwd_t3(const FwdArgs& a, hipStream_t st, bool mask, bool use64) {
-  if (!mask && use64) {
+  const bool alibi = a.s.alibi != nullptr;
+  if (!mask && use64 && !alibi) {  // the 64-row kernel takes no score bias
     const dim3 grid(a.s.H, (a.s.Nq + F64_BM - 1) / F64_BM, a.s.B);
     hipLaunchKernelGGL((fwd64_kernel<T, D, BAND, DROP>), grid, dim3(F64_NW * 64), 0, st, a);
     return hipGetLastError();
   }
   const dim3 grid(a.s.H, (a.s.Nq + FWD_BM - 1) / FWD_BM, a.s.B);
   const dim3 block(FWD_NW * 64);
-  if (mask) hipLaunchKernelGGL((fwd_kernel<T, D, BAND, true, DROP>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((fwd_kernel<T, D, BAND, false, DROP>), grid, block, 0, st, a);
+  if (alibi) {
+    if (mask) hipLaunchKernelGGL((fwd_kernel<T, D, BAND, true, DROP, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<T, D, BAND, false, DROP, true>), grid, block, 0, st, a);
+  } else {
+    if (mask) hipLaunchKernelGGL((fwd_kernel<T, D, BAND, true, DROP, false>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<T, D, BAND, false, DROP, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 

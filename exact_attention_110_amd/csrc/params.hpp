@@ -27,6 +27,8 @@ struct AttnShape {
   int band;
   int wl, wr;
   const uint8_t* mask;  // NULL or uint8 [nbq][nbk] (fixed lengths only)
+  // NULL or float [H]: ALiBi slopes, s_ij += -alibi[h] * |i + (nk - nq) - j|
+  const float* alibi;
   int nbq, nbk;   // ceil(Nq / 128), ceil(Nk / 128)
   // packed variable-length batches (NULL for fixed lengths): sequence b holds
   // rows cu_q[b] .. cu_q[b + 1] - 1 of every query head's [tq][d] plane and

@@ -190,6 +190,18 @@ def make_packed(lens_q, lens_k, H, Hkv, d, dtype, seed, sigma=1.0, with_grad=Tru
     return out
 
 
+def geometric_slopes(H):
+    """ALiBi's slope set for H heads (Press, Smith and Lewis, 2022): the
+    geometric sequence 2^(-8 (h + 1) / H), h = 0 .. H - 1, float32 values."""
+    return (2.0 ** (-8.0 * (np.arange(H) + 1) / H)).astype(np.float32)
+
+
+def random_slopes(H, seed, hi=1.0):
+    """Seeded ALiBi slopes uniform in [0, hi), float32 (steeper and flatter
+    than the geometric set, to reach the distance bias's extremes)."""
+    return np.random.default_rng(seed).uniform(0.0, hi, size=H).astype(np.float32)
+
+
 def length_mix(batch, mean, seed, lo=1):
     """A batch of sequence lengths with a document-like spread: lengths drawn
     from an exponential distribution of the given mean, at least lo."""

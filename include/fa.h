@@ -197,20 +197,34 @@ int fa_backward_stage_dropout(int stage, const void* q, const void* k, const voi
  * causal and block masks intersect. The kernels skip the tiles outside the
  * band and mask elements only in tiles that straddle its edges.
  *   window_left, window_right   >= -1 (FA_ERR_INVALID_ARG below -1)
+ * Score modification, the other half of that lesson section (functions that
+ * change scores inside the tiled kernel; it names none, and the one taken is
+ * ALiBi's linear distance bias, Press, Smith and Lewis 2022): with
+ * alibi_slopes not NULL, the scaled score of query i and key j becomes
+ * scale * q_i . k_j - alibi_slopes[h] * |i + (Nk - Nq) - j| for query head h
+ * before the softmax, masks applied as before; LSE is that of the biased
+ * scores and the bias has no gradient of its own. The backward call must get
+ * the slopes the forward call got.
+ *   alibi_slopes   NULL, or device float32 [H], 4-byte aligned (else
+ *                  FA_ERR_INVALID_ARG); finite values, not checked (they
+ *                  live in device memory). The forward pass uses its 32-row
+ *                  kernel for these calls.
  * dropout_rate 0 is no dropout; dropout otherwise as described above. Other
  * arguments, limits (each of Nq and Nk as N), ownership and errors as for
  * fa_forward / fa_backward.
  */
 int fa_forward_qk(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
-                  int window_left, int window_right, const uint8_t* block_mask, int dtype,
-                  float dropout_rate, unsigned long long seed, void* stream);
+                  int window_left, int window_right, const float* alibi_slopes,
+                  const uint8_t* block_mask, int dtype, float dropout_rate,
+                  unsigned long long seed, void* stream);
 int fa_backward_qk(const void* q, const void* k, const void* v, const void* o,
                    const float* lse, const void* dO, void* dq, void* dk, void* dv,
                    int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
-                   int window_left, int window_right, const uint8_t* block_mask, int dtype,
-                   float dropout_rate, unsigned long long seed,
-                   void* workspace, size_t workspace_bytes, void* stream);
+                   int window_left, int window_right, const float* alibi_slopes,
+                   const uint8_t* block_mask, int dtype, float dropout_rate,
+                   unsigned long long seed, void* workspace, size_t workspace_bytes,
+                   void* stream);
 
 /*
  * Packed variable-length batches (the same glossary, "Sequence Length
@@ -222,7 +236,8 @@ int fa_backward_qk(const void* q, const void* k, const void* v, const void* o,
  * keys cu_seqlens_k[b] .. cu_seqlens_k[b + 1] - 1 of every head; each is an
  * independent attention problem (causal alignment and windows as for
  * fa_forward_qk, with the sequence's own lengths; a sequence may have no
- * queries or no keys).
+ * queries or no keys). alibi_slopes as for fa_forward_qk, the distance
+ * taken within the sequence.
  *   cu_seqlens_q, cu_seqlens_k   device int32 [B + 1], 4-byte aligned, rising
  *                                from 0 to total_q / total_k
  *   max_seqlen_q, max_seqlen_k   >= 1 and >= every sequence's length; the
@@ -243,16 +258,16 @@ int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, floa
                       const int* cu_seqlens_q, const int* cu_seqlens_k,
                       int B, int H, int Hkv, int total_q, int total_k,
                       int max_seqlen_q, int max_seqlen_k, int d, float scale, int causal,
-                      int window_left, int window_right, int dtype, float dropout_rate,
-                      unsigned long long seed, void* stream);
+                      int window_left, int window_right, const float* alibi_slopes,
+                      int dtype, float dropout_rate, unsigned long long seed, void* stream);
 int fa_backward_varlen(const void* q, const void* k, const void* v, const void* o,
                        const float* lse, const void* dO, void* dq, void* dk, void* dv,
                        const int* cu_seqlens_q, const int* cu_seqlens_k,
                        int B, int H, int Hkv, int total_q, int total_k,
                        int max_seqlen_q, int max_seqlen_k, int d, float scale, int causal,
-                       int window_left, int window_right, int dtype, float dropout_rate,
-                       unsigned long long seed, void* workspace, size_t workspace_bytes,
-                       void* stream);
+                       int window_left, int window_right, const float* alibi_slopes,
+                       int dtype, float dropout_rate, unsigned long long seed,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * FP8 forward (pranaymahendrakar.com lesson "FlashAttention", version lineage:

@@ -165,16 +165,16 @@ def test_dropout_argument_order(lib):
     assert bwd_drop(lib, 0.2, stage=3) == EINVAL
 
 
-def fwd_qk(lib, Nq=256, Nk=512, d=64, mask=None, dtype=BF16, rate=0.0, B=1, H=2, Hkv=1, wl=-1, wr=-1):
-    return lib.fa_forward_qk(GOOD, GOOD, GOOD, GOOD, GOOD, B, H, Hkv, Nq, Nk, d, 0.125, 1, wl, wr, mask, dtype, rate,
-                             3, None)
+def fwd_qk(lib, Nq=256, Nk=512, d=64, mask=None, dtype=BF16, rate=0.0, B=1, H=2, Hkv=1, wl=-1, wr=-1, alibi=None):
+    return lib.fa_forward_qk(GOOD, GOOD, GOOD, GOOD, GOOD, B, H, Hkv, Nq, Nk, d, 0.125, 1, wl, wr, alibi, mask, dtype,
+                             rate, 3, None)
 
 
-def bwd_qk(lib, Nq=256, Nk=512, d=64, mask=None, dtype=BF16, ws_bytes=None, rate=0.0, wl=-1, wr=-1):
+def bwd_qk(lib, Nq=256, Nk=512, d=64, mask=None, dtype=BF16, ws_bytes=None, rate=0.0, wl=-1, wr=-1, alibi=None):
     if ws_bytes is None:
         ws_bytes = ws_size(lib, N=Nq, d=d)
     return lib.fa_backward_qk(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 1, 2, 1, Nq, Nk, d, 0.125, 1,
-                              wl, wr, mask, dtype, rate, 3, GOOD, ws_bytes, None)
+                              wl, wr, alibi, mask, dtype, rate, 3, GOOD, ws_bytes, None)
 
 
 @pytest.mark.parametrize("bad", [dict(Nq=0), dict(Nk=0), dict(Nk=-3), dict(d=48), dict(rate=1.0),
@@ -182,6 +182,19 @@ def bwd_qk(lib, Nq=256, Nk=512, d=64, mask=None, dtype=BF16, ws_bytes=None, rate
                                  dict(H=3, Hkv=2), dict(wl=-2), dict(wr=-7)])
 def test_forward_qk_rejects(lib, bad):
     assert fwd_qk(lib, **bad) == EINVAL
+
+
+def test_alibi_slopes_alignment(lib):
+    """The slopes are float32 read on the device: a pointer off a 4-byte
+    boundary is an invalid argument in every call that takes one."""
+    for bad in (P((1 << 20) + 2), P((1 << 20) + 1)):
+        assert fwd_qk(lib, alibi=bad) == EINVAL
+        assert bwd_qk(lib, alibi=bad) == EINVAL
+        assert fwd_var(lib, alibi=bad) == EINVAL
+        assert bwd_var(lib, alibi=bad) == EINVAL
+    # argument errors elsewhere still come first with well-aligned slopes
+    assert fwd_qk(lib, alibi=GOOD, d=48) == EINVAL
+    assert bwd_qk(lib, alibi=GOOD, dtype=F32) == EUNSUP
 
 
 def test_window_limits_rejected_in_backward(lib):
@@ -202,16 +215,16 @@ def test_qk_mask_and_workspace(lib):
 
 
 def fwd_var(lib, cu_q=GOOD, cu_k=GOOD, B=3, H=2, Hkv=1, tq=100, tk=200, mq=50, mk=90, d=64, dtype=BF16,
-            rate=0.0, wl=-1, wr=-1):
+            rate=0.0, wl=-1, wr=-1, alibi=None):
     return lib.fa_forward_varlen(GOOD, GOOD, GOOD, GOOD, GOOD, cu_q, cu_k, B, H, Hkv, tq, tk, mq, mk, d, 0.125, 1,
-                                 wl, wr, dtype, rate, 0, None)
+                                 wl, wr, alibi, dtype, rate, 0, None)
 
 
-def bwd_var(lib, cu_q=GOOD, cu_k=GOOD, mq=50, ws_bytes=None, dtype=BF16, tq=100, wl=-1, wr=-1):
+def bwd_var(lib, cu_q=GOOD, cu_k=GOOD, mq=50, ws_bytes=None, dtype=BF16, tq=100, wl=-1, wr=-1, alibi=None):
     if ws_bytes is None:
         ws_bytes = ws_size(lib, B=3, N=mq)
     return lib.fa_backward_varlen(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, cu_q, cu_k, 3, 2, 1, tq,
-                                  200, mq, 90, 64, 0.125, 1, wl, wr, dtype, 0.0, 0, GOOD, ws_bytes, None)
+                                  200, mq, 90, 64, 0.125, 1, wl, wr, alibi, dtype, 0.0, 0, GOOD, ws_bytes, None)
 
 
 @pytest.mark.parametrize("bad", [dict(cu_q=None), dict(cu_k=None), dict(cu_q=P((1 << 20) + 2)),
