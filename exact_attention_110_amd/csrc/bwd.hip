@@ -126,8 +126,10 @@ __global__ __launch_bounds__(KV_NW * 64, D <= 64 ? 2 : 1) void bwd_kv_kernel(Bwd
   const int g16 = lane >> 4;
   const int roff = 4 * (g16 >> 1) + ((lane & 15) >> 2);   // transposing-read row offset
   const int coff = 16 * (g16 & 1) + 4 * (lane & 3);       // transposing-read column offset
-  // grid = (Hkv, key blocks, B); under causal masking block 0 has the most work
-  const int hk = blockIdx.x, kblk = blockIdx.y, b = blockIdx.z;
+  // grid (tile_grid over kv heads and key blocks); under causal masking block 0
+  // has the most work and is dispatched first
+  const GridPos gp = grid_pos(s);
+  const int hk = blockIdx.x, b = gp.b, kblk = gp.blk;
   // the sequence as seen from the group's first query head
   const SeqView sv = seq_view(s, b, hk * s.G, hk);
   const int len_q = sv.nq, len_k = sv.nk, off = sv.off;
@@ -455,9 +457,10 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
   const int g16 = lane >> 4;
   const int roff = 4 * (g16 >> 1) + ((lane & 15) >> 2);
   const int coff = 16 * (g16 & 1) + 4 * (lane & 3);
-  // grid = (H, query blocks, B), as in the forward pass
-  const int qb = BAND ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
-  const int h = blockIdx.x, b = blockIdx.z;
+  // grid (tile_grid), as in the forward pass
+  const GridPos gp = grid_pos(s);
+  const int qb = BAND ? gp.nblk - 1 - gp.blk : gp.blk;
+  const int h = blockIdx.x, b = gp.b;
   const int hk = h / s.G;
   const SeqView sv = seq_view(s, b, h, hk);
   const int len_q = sv.nq, len_k = sv.nk, off = sv.off;
@@ -656,14 +659,15 @@ static hipError_t launch_pre_t(const BwdArgs& a, hipStream_t st) {
 
 template <class T, int D, int BAND, bool DROP>
 static hipError_t launch_kv_t3(const BwdArgs& a, hipStream_t st) {
-  const dim3 grid(a.s.Hkv, (a.s.Nk + KV_BKV - 1) / KV_BKV, a.s.B);
+  BwdArgs la = a;
+  const dim3 grid = tile_grid(la.s, a.s.Hkv, (a.s.Nk + KV_BKV - 1) / KV_BKV);
   const dim3 block(KV_NW * 64);
   if (a.s.alibi) {
-    if (a.s.mask) hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, true, DROP, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, false, DROP, true>), grid, block, 0, st, a);
+    if (a.s.mask) hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, true, DROP, true>), grid, block, 0, st, la);
+    else hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, false, DROP, true>), grid, block, 0, st, la);
   } else {
-    if (a.s.mask) hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, true, DROP, false>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, false, DROP, false>), grid, block, 0, st, a);
+    if (a.s.mask) hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, true, DROP, false>), grid, block, 0, st, la);
+    else hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, false, DROP, false>), grid, block, 0, st, la);
   }
   return hipGetLastError();
 }
@@ -682,14 +686,15 @@ static hipError_t launch_kv_t(const BwdArgs& a, hipStream_t st) {
 
 template <class T, int D, int BAND, bool DROP>
 static hipError_t launch_q_t3(const BwdArgs& a, hipStream_t st) {
-  const dim3 grid(a.s.H, (a.s.Nq + Q_BM - 1) / Q_BM, a.s.B);
+  BwdArgs la = a;
+  const dim3 grid = tile_grid(la.s, a.s.H, (a.s.Nq + Q_BM - 1) / Q_BM);
   const dim3 block(Q_NW * 64);
   if (a.s.alibi) {
-    if (a.s.mask) hipLaunchKernelGGL((bwd_q_kernel<T, D, BAND, true, DROP, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((bwd_q_kernel<T, D, BAND, false, DROP, true>), grid, block, 0, st, a);
+    if (a.s.mask) hipLaunchKernelGGL((bwd_q_kernel<T, D, BAND, true, DROP, true>), grid, block, 0, st, la);
+    else hipLaunchKernelGGL((bwd_q_kernel<T, D, BAND, false, DROP, true>), grid, block, 0, st, la);
   } else {
-    if (a.s.mask) hipLaunchKernelGGL((bwd_q_kernel<T, D, BAND, true, DROP, false>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((bwd_q_kernel<T, D, BAND, false, DROP, false>), grid, block, 0, st, a);
+    if (a.s.mask) hipLaunchKernelGGL((bwd_q_kernel<T, D, BAND, true, DROP, false>), grid, block, 0, st, la);
+    else hipLaunchKernelGGL((bwd_q_kernel<T, D, BAND, false, DROP, false>), grid, block, 0, st, la);
   }
   return hipGetLastError();
 }

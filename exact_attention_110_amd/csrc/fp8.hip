@@ -82,9 +82,10 @@ __global__ __launch_bounds__(F8_NW * 64, 2) void fwd_fp8_kernel(Fp8FwdArgs a) {
   const AttnShape& s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  // grid = (H, query blocks, B); under causal masking the longest blocks first
-  const int qb = BAND ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
-  const int h = blockIdx.x, b = blockIdx.z;
+  // grid (tile_grid); under causal masking the longest blocks first
+  const GridPos gp = grid_pos(s);
+  const int qb = BAND ? gp.nblk - 1 - gp.blk : gp.blk;
+  const int h = blockIdx.x, b = gp.b;
   const int hk = h / s.G;
   const SeqView sv = seq_view(s, b, h, hk);
   const int nq = sv.nq, nk = sv.nk;
@@ -246,9 +247,10 @@ __global__ __launch_bounds__(F8_NW * 64, 2) void fwd_fp8_kernel(Fp8FwdArgs a) {
 
 template <class TO, int D>
 static hipError_t launch_fp8_t(const Fp8FwdArgs& a, hipStream_t st) {
-  const dim3 grid(a.s.H, (a.s.Nq + F8_BM - 1) / F8_BM, a.s.B);
-  if (a.s.band) hipLaunchKernelGGL((fwd_fp8_kernel<TO, D, 1>), grid, dim3(F8_NW * 64), 0, st, a);
-  else hipLaunchKernelGGL((fwd_fp8_kernel<TO, D, 0>), grid, dim3(F8_NW * 64), 0, st, a);
+  Fp8FwdArgs la = a;
+  const dim3 grid = tile_grid(la.s, a.s.H, (a.s.Nq + F8_BM - 1) / F8_BM);
+  if (a.s.band) hipLaunchKernelGGL((fwd_fp8_kernel<TO, D, 1>), grid, dim3(F8_NW * 64), 0, st, la);
+  else hipLaunchKernelGGL((fwd_fp8_kernel<TO, D, 0>), grid, dim3(F8_NW * 64), 0, st, la);
   return hipGetLastError();
 }
 

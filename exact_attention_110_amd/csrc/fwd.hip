@@ -68,12 +68,11 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
   const AttnShape& s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  // grid = (H, query blocks, B): consecutive workgroups take different heads, so
-  // the round-robin spread over the 8 XCDs keeps each head on one XCD's L2;
-  // under a band mask the later (under causal masking, longer) query blocks
-  // are dispatched first
-  const int qb = BAND ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
-  const int h = blockIdx.x, b = blockIdx.z;
+  // grid (tile_grid): heads fastest; under a band mask the later (under causal
+  // masking, longer) query blocks are dispatched first
+  const GridPos gp = grid_pos(s);
+  const int qb = BAND ? gp.nblk - 1 - gp.blk : gp.blk;
+  const int h = blockIdx.x, b = gp.b;
   const int hk = h / s.G;
   const SeqView sv = seq_view(s, b, h, hk);
   const int nq = sv.nq, nk = sv.nk, off = sv.off;
@@ -381,10 +380,11 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
   const int g16 = lane >> 4;
   const int roff = 4 * (g16 >> 1) + ((lane & 15) >> 2);
   const int coff = 16 * (g16 & 1) + 4 * (lane & 3);
-  // grid = (H, query blocks, B): heads spread over the XCDs; under a band
-  // mask the later (under causal masking, longer) query blocks are dispatched first
-  const int qb = BAND ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
-  const int h = blockIdx.x, b = blockIdx.z;
+  // grid (tile_grid): heads fastest; under a band mask the later (under causal
+  // masking, longer) query blocks are dispatched first
+  const GridPos gp = grid_pos(s);
+  const int qb = BAND ? gp.nblk - 1 - gp.blk : gp.blk;
+  const int h = blockIdx.x, b = gp.b;
   const int hk = h / s.G;
   const SeqView sv = seq_view(s, b, h, hk);
   const int nq = sv.nq, nk = sv.nk, off = sv.off;
@@ -837,18 +837,20 @@ template <class T, int D, int BAND, bool DROP>
 static hipError_t launch_fwd_t3(const FwdArgs& a, hipStream_t st, bool mask, bool use64) {
   const bool alibi = a.s.alibi != nullptr;
   if (!mask && use64 && !alibi) {  // the 64-row kernel takes no score bias
-    const dim3 grid(a.s.H, (a.s.Nq + F64_BM - 1) / F64_BM, a.s.B);
-    hipLaunchKernelGGL((fwd64_kernel<T, D, BAND, DROP>), grid, dim3(F64_NW * 64), 0, st, a);
+    FwdArgs la = a;
+    const dim3 grid = tile_grid(la.s, a.s.H, (a.s.Nq + F64_BM - 1) / F64_BM);
+    hipLaunchKernelGGL((fwd64_kernel<T, D, BAND, DROP>), grid, dim3(F64_NW * 64), 0, st, la);
     return hipGetLastError();
   }
-  const dim3 grid(a.s.H, (a.s.Nq + FWD_BM - 1) / FWD_BM, a.s.B);
+  FwdArgs la = a;
+  const dim3 grid = tile_grid(la.s, a.s.H, (a.s.Nq + FWD_BM - 1) / FWD_BM);
   const dim3 block(FWD_NW * 64);
   if (alibi) {
-    if (mask) hipLaunchKernelGGL((fwd_kernel<T, D, BAND, true, DROP, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((fwd_kernel<T, D, BAND, false, DROP, true>), grid, block, 0, st, a);
+    if (mask) hipLaunchKernelGGL((fwd_kernel<T, D, BAND, true, DROP, true>), grid, block, 0, st, la);
+    else hipLaunchKernelGGL((fwd_kernel<T, D, BAND, false, DROP, true>), grid, block, 0, st, la);
   } else {
-    if (mask) hipLaunchKernelGGL((fwd_kernel<T, D, BAND, true, DROP, false>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((fwd_kernel<T, D, BAND, false, DROP, false>), grid, block, 0, st, a);
+    if (mask) hipLaunchKernelGGL((fwd_kernel<T, D, BAND, true, DROP, false>), grid, block, 0, st, la);
+    else hipLaunchKernelGGL((fwd_kernel<T, D, BAND, false, DROP, false>), grid, block, 0, st, la);
   }
   return hipGetLastError();
 }

@@ -43,6 +43,9 @@ struct AttnShape {
   int drop_t;
   float drop_scale;
   unsigned int seed0, seed1;
+  // launch-grid layout, set by the launcher (tile_grid): 0 = (heads, B, blocks),
+  // 1 = (heads, blocks, B)
+  int batch_outer;
 };
 
 struct FwdArgs {
@@ -105,6 +108,33 @@ __device__ __forceinline__ SeqView seq_view(const AttnShape& s, int b, int h, in
   }
   v.off = v.nk - v.nq;
   return v;
+}
+
+// Launch grid of the tiled kernels, one workgroup per (head, batch, 128- or
+// 256-row block). Consecutive workgroups take different heads, so the
+// round-robin over the 8 XCDs keeps each head on one XCD's L2. The block index
+// varies slowest, (heads, B, blocks), so that under causal masking every head
+// and batch starts its costliest block before any cheaper one; when one batch
+// alone holds FA_BATCH_OUTER_MIN workgroups or more (several times what the chip
+// runs at once, so the order within a batch already balances the load) the
+// batch varies slowest instead, (heads, blocks, B), which keeps the running
+// workgroups on fewer batches and so fewer K/V heads per XCD's L2.
+#ifndef FA_BATCH_OUTER_MIN
+#define FA_BATCH_OUTER_MIN 1024
+#endif
+inline dim3 tile_grid(AttnShape& s, int heads, int nblk) {
+  s.batch_outer = (long long)heads * nblk >= FA_BATCH_OUTER_MIN ? 1 : 0;
+  return s.batch_outer ? dim3(heads, nblk, s.B) : dim3(heads, s.B, nblk);
+}
+
+struct GridPos {
+  int b;     // batch (sequence)
+  int blk;   // block index in launch order
+  int nblk;  // blocks per head
+};
+__device__ __forceinline__ GridPos grid_pos(const AttnShape& s) {
+  return s.batch_outer ? GridPos{(int)blockIdx.z, (int)blockIdx.y, (int)gridDim.y}
+                       : GridPos{(int)blockIdx.y, (int)blockIdx.z, (int)gridDim.z};
 }
 
 // FP8 forward: q, k, v hold OCP E4M3 codes; the real inputs are code value
