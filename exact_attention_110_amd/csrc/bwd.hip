@@ -87,6 +87,11 @@ constexpr int KV_R = 128 / KV_BQ;     // steps per 128-row mask block
 constexpr int MASK_LIST = 2048;       // capacity of a compacted mask row / column
 static_assert(KV_BKV == 128, "a key-block workgroup must cover exactly one mask block column");
 
+// position of a step in the key-block kernel's ring of LDS buffers, when known
+// at compile time (-1: known only at run time)
+template <int P>
+using RingAt = std::integral_constant<int, P>;
+
 // position of a step: index qi into the key block's query-block list, and the
 // query head's element offset in Q / dO and float offset in the statistics
 struct StepPos {
@@ -110,7 +115,7 @@ __global__ __launch_bounds__(KV_NW * 64, D <= 64 ? 2 : 1) void bwd_kv_kernel(Bwd
   // statistics feed P and dS, step e - 1's buffer feeds dV and dK, and step
   // e + 2 is loaded into the buffer step e - 2 used) and the compacted mask
   // list. The buffers are filled by LDS DMA, straight from memory.
-  constexpr int NB = 4;
+  constexpr int NB = 4;  // the unrolled step loop below covers the ring once per pass
   __shared__ __attribute__((aligned(16))) char smem_raw[2 * NB * QBUF + NB * STB + (MASK ? 2 * MASK_LIST + 16 : 16)];
   lds_t* smem = (lds_t*)smem_raw;
   lds_t* qbuf = smem;                   // [NB][BQ rows, swizzled]
@@ -331,15 +336,20 @@ __global__ __launch_bounds__(KV_NW * 64, D <= 64 ? 2 : 1) void bwd_kv_kernel(Bwd
   dma_wait();
   __syncthreads();
   // iteration e: (sc, dp) = S, dP of step e; (pk, sk) = P, dS of step e - 1;
-  // fills (scn, dpn) with step e + 1 and (pkn, skn) with step e
-  auto iter = [&](int e, auto masked, const f32x16& sc, const f32x16& dp, const unsigned int (&pk)[8],
+  // fills (scn, dpn) with step e + 1 and (pkn, skn) with step e. phase is
+  // RingAt<e % NB> where the caller knows it at compile time (the buffers are
+  // then fixed LDS offsets, folded into the reads' immediate offsets instead
+  // of an address add per read), RingAt<-1> otherwise.
+  auto iter = [&](int e, auto masked, auto phase, const f32x16& sc, const f32x16& dp, const unsigned int (&pk)[8],
                   const unsigned int (&sk)[8], f32x16& scn, f32x16& dpn, unsigned int (&pkn)[8],
                   unsigned int (&skn)[8]) {
+    constexpr int P = decltype(phase)::value;
+    const int er = P >= 0 ? P : e;  // congruent to e modulo NB
     const StepPos nn = e + 2 < nsteps ? advance(nxt) : nxt;
-    dma_q(nn, (e + 2) & (NB - 1));
-    sdp((e + 1) & (NB - 1), scn, dpn);
-    probs(masked, sc, dp, qblock_at(cur.qi) * BQ, e & (NB - 1), cur.hb, pkn, skn);
-    dvdk((e + NB - 1) & (NB - 1), pk, sk);
+    dma_q(nn, (er + 2) & (NB - 1));
+    sdp((er + 1) & (NB - 1), scn, dpn);
+    probs(masked, sc, dp, qblock_at(cur.qi) * BQ, er & (NB - 1), cur.hb, pkn, skn);
+    dvdk((er + NB - 1) & (NB - 1), pk, sk);
     dma_wait();
     __syncthreads();
     cur = nxt;
@@ -377,26 +387,52 @@ __global__ __launch_bounds__(KV_NW * 64, D <= 64 ? 2 : 1) void bwd_kv_kernel(Bwd
     while (nsuf < nq - ndiag && qblock_at(nq - 1 - nsuf) * BQ > lim2) ++nsuf;
   }
   const int nmid_end = nq - nsuf;
+  const std::true_type masked;
+  const std::false_type plain;
+  const RingAt<-1> rt;
   int e = 0;
   for (int hg = 0; hg < s.G; ++hg) {
     for (int t = 0; t < ndiag; ++t, ++e) {
-      iter(e, std::true_type{}, scA, dpA, pkA, skA, scB, dpB, pkB, skB);
+      iter(e, masked, rt, scA, dpA, pkA, skA, scB, dpB, pkB, skB);
       b_to_a();
     }
     int t = ndiag;
+    // unmasked steps: first up to three to bring e to a multiple of NB, then
+    // four at a time with the ring position fixed at compile time, then the
+    // rest; pairs alternate the register sets, a single step copies them back
+    if ((e & 1) && t < nmid_end) {
+      iter(e, plain, rt, scA, dpA, pkA, skA, scB, dpB, pkB, skB);
+      b_to_a();
+      ++e;
+      ++t;
+    }
+    if ((e & 2) && t + 1 < nmid_end) {
+      iter(e, plain, rt, scA, dpA, pkA, skA, scB, dpB, pkB, skB);
+      iter(e + 1, plain, rt, scB, dpB, pkB, skB, scA, dpA, pkA, skA);
+      e += 2;
+      t += 2;
+    }
+    if ((e & (NB - 1)) == 0) {
+      for (; t + 3 < nmid_end; t += 4, e += 4) {
+        iter(e, plain, RingAt<0>{}, scA, dpA, pkA, skA, scB, dpB, pkB, skB);
+        iter(e + 1, plain, RingAt<1>{}, scB, dpB, pkB, skB, scA, dpA, pkA, skA);
+        iter(e + 2, plain, RingAt<2>{}, scA, dpA, pkA, skA, scB, dpB, pkB, skB);
+        iter(e + 3, plain, RingAt<3>{}, scB, dpB, pkB, skB, scA, dpA, pkA, skA);
+      }
+    }
     for (; t + 1 < nmid_end; t += 2, e += 2) {
-      iter(e, std::false_type{}, scA, dpA, pkA, skA, scB, dpB, pkB, skB);
-      iter(e + 1, std::false_type{}, scB, dpB, pkB, skB, scA, dpA, pkA, skA);
+      iter(e, plain, rt, scA, dpA, pkA, skA, scB, dpB, pkB, skB);
+      iter(e + 1, plain, rt, scB, dpB, pkB, skB, scA, dpA, pkA, skA);
     }
     if (t < nmid_end) {
-      iter(e, std::false_type{}, scA, dpA, pkA, skA, scB, dpB, pkB, skB);
+      iter(e, plain, rt, scA, dpA, pkA, skA, scB, dpB, pkB, skB);
       b_to_a();
       ++e;
       ++t;
     }
     if constexpr (LOWER) {
       for (; t < nq; ++t, ++e) {
-        iter(e, std::true_type{}, scA, dpA, pkA, skA, scB, dpB, pkB, skB);
+        iter(e, masked, rt, scA, dpA, pkA, skA, scB, dpB, pkB, skB);
         b_to_a();
       }
     }
