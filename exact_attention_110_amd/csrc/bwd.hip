@@ -574,8 +574,11 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
   dma_wait();
   __syncthreads();
 
-  for (int e = 0; e < ntiles; ++e) {
-    const int buf = e & 1;
+  // tile e reads buffer e % 2 and loads tile e + 1 into the other; tiles go in
+  // pairs so that each knows its buffer at compile time (fixed LDS offsets in
+  // the reads' immediate fields rather than an address add per read)
+  auto tile = [&](int e, auto phase) {
+    constexpr int buf = decltype(phase)::value;
     const int ks = tile_at(e) * Q_BN;
     dma_kv(tile_at(e + 1 < ntiles ? e + 1 : e), buf ^ 1);
 
@@ -667,7 +670,13 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
     }
     dma_wait();
     __syncthreads();
+  };
+  int e = 0;
+  for (; e + 1 < ntiles; e += 2) {
+    tile(e, RingAt<0>{});
+    tile(e + 1, RingAt<1>{});
   }
+  if (e < ntiles) tile(e, RingAt<0>{});
 
   // dQ = scale * acc; lane holds query qi, d = 32 dt + 8 j + 4 hh + 0..3
   const float scale = s.scale;
