@@ -118,3 +118,29 @@ def test_block_sparse_fp16(gpu_lib):
         assert torch.isfinite(t).all()
     # 128-row chunks: each chunk then gathers only its own mask row's key blocks
     _check_heads(w, x, o, lse, grads, I.check_heads(w), chunk=128)
+
+
+@pytest.mark.timeout(900)
+def test_batch_outer_grids_bf16(gpu_lib):
+    """Two batches at a size where the dK/dV and dQ grids take the batch as
+    their slowest index (8 kv heads x 128 key blocks = 1024 workgroups per
+    batch) and the 64-row forward grid the block (8 x 64 = 512): every element
+    of O, LSE, dQ, dK, dV of one head in each batch against the oracle."""
+    B, H, N, d = 2, 8, 16384, 64
+    x = I.make_small(B, H, H, N, d, "bf16", seed=11)
+    dev = torch.device("cuda", 0)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    scale = 1.0 / np.sqrt(d)
+    o, lse = gpu_lib.forward(q, k, v, scale, True, None)
+    dq, dk, dv = gpu_lib.backward(q, k, v, o, lse, do, scale, True, None)
+    torch.cuda.synchronize()
+    for b, h in ((0, 5), (1, 2)):
+        where = f"batch-outer b={b} h={h}"
+        PT.say("checking", where)
+        qd, kd, vd, dod = (_head(x[n], b, h) for n in ("q", "k", "v", "do"))
+        oref, lref = oracle.forward(qd, kd, vd, scale, True, chunk=256)
+        PT.check_out(_head(o, b, h)[0, 0], oref[0, 0], "bf16", where)
+        PT.check_lse(_head(lse.unsqueeze(-1), b, h)[0, 0, :, 0], lref[0, 0], where)
+        rq, rk, rv = oracle.backward(qd, kd, vd, dod, scale, True, chunk=256)
+        for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+            PT.check_grad(_head(got, b, h)[0, 0], ref[0, 0], f"{where} {name}")
