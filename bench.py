@@ -32,7 +32,9 @@ Prints one JSON line. Besides the headline it carries:
   against the dense bf16 MFMA peak (2.5 PFLOP/s). The backward pass runs a
   key-block kernel (S and dP recomputed, dV and dK: 4 contractions) and a
   query-block kernel (S and dP recomputed, dQ: 3 contractions); each kernel is
-  credited with the contractions it performs. "traffic" is the kernel's HBM
+  credited with the contractions it performs. For d <= 64 without a block mask
+  the library runs both as one launch (7 contractions), which is then the
+  kernel reported. "traffic" is the kernel's HBM
   bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary
   (profiles/*_hbm_traffic.md), or null once the kernel's sources have changed
   since the counters were taken;
@@ -73,9 +75,11 @@ def sparse_flops(w, mask, backward=True):
 KERNEL_SOURCES = {
     "fwd_kernel": ["fwd.hip", "common.hpp", "params.hpp"],
     "fwd64_kernel": ["fwd.hip", "common.hpp", "params.hpp"],
+    "fwd_f32_kernel": ["fwd.hip", "common.hpp", "params.hpp"],
     "bwd_pre_kernel": ["bwd.hip", "common.hpp", "params.hpp"],
     "bwd_kv_kernel": ["bwd.hip", "common.hpp", "params.hpp"],
     "bwd_q_kernel": ["bwd.hip", "common.hpp", "params.hpp"],
+    "bwd_fused_kernel": ["bwd.hip", "common.hpp", "params.hpp"],
     "fwd_fp8_kernel": ["fp8.hip", "common.hpp", "params.hpp"],
 }
 
@@ -225,8 +229,16 @@ def main():
     per_contraction = fwd_flop / 2.0  # one N x N x d contraction of the workload
     t_fwd = event_time(lambda: binding.forward(q, k, v, w.scale, w.causal, mask, out=o, lse=lse, **drop), n_ev)
     # kernel -> (mean launch time in ms, algorithmic FLOP per launch)
-    # dense and causal inputs run the 64-row forward kernel, block-sparse ones the 32-row one
-    kernels = {("fwd_kernel" if mask is not None else "fwd64_kernel"): (t_fwd, 2 * per_contraction)}
+    # the library's choice of forward kernel: 64 query rows per wave for long
+    # dense rows over few workgroups (N >= 8192, B*H*ceil(N/256) <= 2048), else 32
+    env_rows = os.environ.get("FA_FORWARD_ROWS_PER_WAVE")
+    use64 = mask is None and ((w.N >= 8192 and w.B * w.H * -(-w.N // 256) <= 2048) if env_rows not in ("32", "64")
+                              else env_rows == "64")
+    if w.dtype == "fp32":
+        fwd_name = "fwd_f32_kernel"
+    else:
+        fwd_name = "fwd64_kernel" if use64 else "fwd_kernel"
+    kernels = {fwd_name: (t_fwd, 2 * per_contraction)}
     if w.backward:
         stage = lambda s: (lambda: binding.backward_stage(s, q, k, v, o, lse, do, dq, dk, dv, ws,  # noqa: E731
                                                           w.scale, w.causal, mask, **drop))
@@ -235,11 +247,18 @@ def main():
         t_q = event_time(stage(2), n_ev)
         # the key-block kernel recomputes S and dP and forms dV and dK (4 contractions);
         # the query-block kernel recomputes S and dP and forms dQ (3 contractions)
-        kernels["bwd_kv_kernel"] = (t_kv, 4 * per_contraction)
-        kernels["bwd_q_kernel"] = (t_q, 3 * per_contraction)
         print(f"[bench] forward {t_fwd:.3f} ms ({2 * per_contraction / t_fwd / 1e9:.1f} TFLOP/s); backward "
               f"stages D {t_pre:.3f} / dK,dV {t_kv:.3f} ({4 * per_contraction / t_kv / 1e9:.1f} TFLOP/s) / "
               f"dQ {t_q:.3f} ms ({3 * per_contraction / t_q / 1e9:.1f} TFLOP/s)", file=sys.stderr, flush=True)
+        if w.d <= 64 and mask is None and not args.dropout:
+            # fa_backward runs both as one launch here (stage 3): that is the kernel of the step
+            t_f = event_time(stage(3), n_ev)
+            kernels["bwd_fused_kernel"] = (t_f, 7 * per_contraction)
+            print(f"[bench] dK,dV + dQ in one launch (the step's kernel) {t_f:.3f} ms "
+                  f"({7 * per_contraction / t_f / 1e9:.1f} TFLOP/s)", file=sys.stderr, flush=True)
+        else:
+            kernels["bwd_kv_kernel"] = (t_kv, 4 * per_contraction)
+            kernels["bwd_q_kernel"] = (t_q, 3 * per_contraction)
     dom = max(kernels, key=lambda n: kernels[n][0])
     t_dom, f_dom = kernels[dom]
     achieved = f_dom / (t_dom * 1e-3) / 1e12

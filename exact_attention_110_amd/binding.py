@@ -233,7 +233,8 @@ def backward(q, k, v, o, lse, do, scale=None, causal=False, block_mask=None, ws=
 
 def backward_stage(stage, q, k, v, o, lse, do, dq, dk, dv, ws, scale=None, causal=False, block_mask=None,
                    dropout_rate=0.0, seed=0):
-    """Run one stage (0, 1 or 2) of the backward pass; see fa_backward_stage."""
+    """Run one stage of the backward pass (0, 1, 2, or 3 = stages 1 and 2 in one
+    launch where fa_backward uses it); see fa_backward_stage."""
     d = q.shape[3]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     m = _mask(block_mask, q.shape[2], q.device)

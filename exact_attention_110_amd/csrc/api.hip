@@ -176,7 +176,7 @@ int stage_impl(int stage, const void* q, const void* k, const void* v, const voi
                const void* dO, void* dq, void* dk, void* dv, const Geo& g, float scale, int causal,
                int window_left, int window_right, const float* alibi, const uint8_t* block_mask, int dtype,
                float rate, unsigned long long seed, void* workspace, size_t workspace_bytes, void* stream) {
-  if (stage < 0 || stage > 2) return FA_ERR_INVALID_ARG;
+  if (stage < 0 || stage > 3) return FA_ERR_INVALID_ARG;
   if ((uintptr_t)alibi & 3u) return FA_ERR_INVALID_ARG;
   int st = check_backward(q, k, v, o, lse, dO, dq, dk, dv, g, scale, block_mask, dtype, workspace,
                           workspace_bytes);
@@ -187,6 +187,7 @@ int stage_impl(int stage, const void* q, const void* k, const void* v, const voi
   a.s = make_shape(g, scale, band, block_mask);
   a.s.alibi = alibi;
   if (!set_dropout(a.s, rate, seed)) return FA_ERR_INVALID_ARG;
+  if (stage == 3 && (g.d > 64 || a.s.drop_t > 0 || alibi || block_mask)) return FA_ERR_UNSUPPORTED;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -208,7 +209,14 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
                   int window_left, int window_right, const float* alibi, const uint8_t* block_mask,
                   int dtype, float rate, unsigned long long seed, void* workspace, size_t workspace_bytes,
                   void* stream) {
-  for (int stage = 0; stage < 3; ++stage) {
+  // For d <= 64 without dropout, score bias or block mask, the dK/dV and dQ
+  // kernels run two workgroups per CU each and go out as one launch (stage 3),
+  // so the dQ workgroups fill the CUs the dK/dV kernel's causal tail leaves
+  // idle (a block-sparse grid is balanced already and gains nothing).
+  const bool fused = g.d <= 64 && rate == 0.f && alibi == nullptr && block_mask == nullptr;
+  const int stages[3] = {0, fused ? 3 : 1, 2};
+  for (int i = 0; i < (fused ? 2 : 3); ++i) {
+    const int stage = stages[i];
     int st = stage_impl(stage, q, k, v, o, lse, dO, dq, dk, dv, g, scale, causal, window_left, window_right,
                         alibi, block_mask, dtype, rate, seed, workspace, workspace_bytes, stream);
     if (st != FA_OK) return st;
@@ -265,6 +273,7 @@ int fa_backward_stage(int stage, const void* q, const void* k, const void* v, co
                       const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H,
                       int Hkv, int N, int d, float scale, int causal, const uint8_t* block_mask,
                       int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (stage < 0 || stage > 3) return FA_ERR_INVALID_ARG;
   return stage_impl(stage, q, k, v, o, lse, dO, dq, dk, dv, fixed_geo(B, H, Hkv, N, N, d), scale, causal,
                     -1, -1, nullptr, block_mask, dtype, 0.f, 0ull, workspace, workspace_bytes, stream);
 }
@@ -275,6 +284,7 @@ int fa_backward_stage_dropout(int stage, const void* q, const void* k, const voi
                               int causal, const uint8_t* block_mask, int dtype,
                               float dropout_rate, unsigned long long seed, void* workspace,
                               size_t workspace_bytes, void* stream) {
+  if (stage < 0 || stage > 3) return FA_ERR_INVALID_ARG;
   return stage_impl(stage, q, k, v, o, lse, dO, dq, dk, dv, fixed_geo(B, H, Hkv, N, N, d), scale, causal,
                     -1, -1, nullptr, block_mask, dtype, dropout_rate, seed, workspace, workspace_bytes, stream);
 }

@@ -103,7 +103,7 @@ struct StepPos {
 
 // (d <= 64 halves the register operands and accumulators: two workgroups per CU)
 template <class T, int D, int BAND, bool MASK, bool DROP, bool ALIBI>
-__global__ __launch_bounds__(KV_NW * 64, D <= 64 ? 2 : 1) void bwd_kv_kernel(BwdArgs a) {
+__device__ __forceinline__ void bwd_kv_body(const BwdArgs& a, const int hk, const int b, const int kblk) {
   constexpr int BQ = KV_BQ;
   constexpr int QBUF = BQ * 2 * D;       // one Q or dO block, swizzled rows without padding
   constexpr int STB = 2 * BQ * 4;        // one statistics block: BQ log2-scaled LSE, then BQ D
@@ -131,10 +131,8 @@ __global__ __launch_bounds__(KV_NW * 64, D <= 64 ? 2 : 1) void bwd_kv_kernel(Bwd
   const int g16 = lane >> 4;
   const int roff = 4 * (g16 >> 1) + ((lane & 15) >> 2);   // transposing-read row offset
   const int coff = 16 * (g16 & 1) + 4 * (lane & 3);       // transposing-read column offset
-  // grid (tile_grid over kv heads and key blocks); under causal masking block 0
-  // has the most work and is dispatched first
-  const GridPos gp = grid_pos(s);
-  const int hk = blockIdx.x, b = gp.b, kblk = gp.blk;
+  // workgroup: kv head hk, batch b, key block kblk (under causal masking block 0
+  // has the most work and is dispatched first)
   // the sequence as seen from the group's first query head
   const SeqView sv = seq_view(s, b, hk * s.G, hk);
   const int len_q = sv.nq, len_k = sv.nk, off = sv.off;
@@ -457,6 +455,12 @@ __global__ __launch_bounds__(KV_NW * 64, D <= 64 ? 2 : 1) void bwd_kv_kernel(Bwd
     }
 }
 
+template <class T, int D, int BAND, bool MASK, bool DROP, bool ALIBI>
+__global__ __launch_bounds__(KV_NW * 64, D <= 64 ? 2 : 1) void bwd_kv_kernel(BwdArgs a) {
+  const GridPos gp = grid_pos(a.s);  // grid: tile_grid over kv heads and key blocks
+  bwd_kv_body<T, D, BAND, MASK, DROP, ALIBI>(a, blockIdx.x, gp.b, gp.blk);
+}
+
 // ---------------------------------------------------------------------------
 // stage 2: per query block, recompute P and dS; accumulate dQ
 // ---------------------------------------------------------------------------
@@ -474,7 +478,8 @@ constexpr int Q_R = 128 / Q_BN;      // tiles per 128-key mask block
 static_assert(Q_BM == 128, "a query-block workgroup must cover exactly one mask block row");
 
 template <class T, int D, int BAND, bool MASK, bool DROP, bool ALIBI>
-__global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
+__device__ __forceinline__ void bwd_q_body(const BwdArgs& a, const int h, const int b, const int blk,
+                                           const int nblk) {
   constexpr int KBUF = Q_BN * 2 * D;     // K tile: swizzled rows, row reads and transposing reads
   constexpr int VBUF = Q_BN * 2 * D;     // V tile: swizzled rows, row reads
   constexpr int NS = D / 16;
@@ -494,9 +499,9 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
   const int roff = 4 * (g16 >> 1) + ((lane & 15) >> 2);
   const int coff = 16 * (g16 & 1) + 4 * (lane & 3);
   // grid (tile_grid), as in the forward pass
-  const GridPos gp = grid_pos(s);
-  const int qb = BAND ? gp.nblk - 1 - gp.blk : gp.blk;
-  const int h = blockIdx.x, b = gp.b;
+  // workgroup: query head h, batch b, block blk of nblk in launch order; under
+  // a band mask the later (under causal masking, longer) query blocks first
+  const int qb = BAND ? nblk - 1 - blk : blk;
   const int hk = h / s.G;
   const SeqView sv = seq_view(s, b, h, hk);
   const int len_q = sv.nq, len_k = sv.nk, off = sv.off;
@@ -691,6 +696,38 @@ __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
     }
 }
 
+template <class T, int D, int BAND, bool MASK, bool DROP, bool ALIBI>
+__global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
+  const GridPos gp = grid_pos(a.s);  // grid: tile_grid over query heads and query blocks
+  bwd_q_body<T, D, BAND, MASK, DROP, ALIBI>(a, blockIdx.x, gp.b, gp.blk, gp.nblk);
+}
+
+// ---------------------------------------------------------------------------
+// stages 1 + 2 in one launch (d <= 64; no dropout, score bias or block mask): at these
+// head sizes both kernels run two workgroups per CU, so one grid of the
+// key-block workgroups followed by the query-block workgroups (each set
+// costliest first) lets the query blocks fill the CUs the key blocks' causal
+// tail leaves idle. Workgroup ids: [0, nkv) key blocks, then query blocks, each
+// set heads fastest, then batch and block in the order tile_grid would choose
+// (bo = batch slowest).
+// ---------------------------------------------------------------------------
+static_assert(KV_NW == Q_NW && FA_Q_OCC == 2, "the fused launch assumes both kernels' workgroup shape");
+template <class T, int D, int BAND>
+__global__ __launch_bounds__(KV_NW * 64, 2) void bwd_fused_kernel(BwdArgs a, int nkv, int kv_bo, int q_bo) {
+  static_assert(D <= 64, "two workgroups per CU only for d <= 64");
+  const int id = blockIdx.x;
+  if (id < nkv) {
+    const int nkb = (a.s.Nk + KV_BKV - 1) / KV_BKV;
+    const int hk = id % a.s.Hkv, r = id / a.s.Hkv;
+    bwd_kv_body<T, D, BAND, false, false, false>(a, hk, kv_bo ? r / nkb : r % a.s.B, kv_bo ? r % nkb : r / a.s.B);
+  } else {
+    const int nqb = (a.s.Nq + Q_BM - 1) / Q_BM;
+    const int i = id - nkv;
+    const int h = i % a.s.H, r = i / a.s.H;
+    bwd_q_body<T, D, BAND, false, false, false>(a, h, q_bo ? r / nqb : r % a.s.B, q_bo ? r % nqb : r / a.s.B, nqb);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -756,10 +793,34 @@ static hipError_t launch_q_t(const BwdArgs& a, hipStream_t st) {
   return a.s.drop_t > 0 ? launch_q_t2<T, D, true>(a, st) : launch_q_t2<T, D, false>(a, st);
 }
 
+template <class T, int D, int BAND>
+static hipError_t launch_fused_t3(const BwdArgs& a, hipStream_t st) {
+  const int nkb = (a.s.Nk + KV_BKV - 1) / KV_BKV, nqb = (a.s.Nq + Q_BM - 1) / Q_BM;
+  const int kv_bo = (long long)a.s.Hkv * nkb >= FA_BATCH_OUTER_MIN ? 1 : 0;
+  const int q_bo = (long long)a.s.H * nqb >= FA_BATCH_OUTER_MIN ? 1 : 0;
+  const int nkv = a.s.Hkv * a.s.B * nkb, nq = a.s.H * a.s.B * nqb;
+  const dim3 grid((unsigned)(nkv + nq)), block(KV_NW * 64);
+  hipLaunchKernelGGL((bwd_fused_kernel<T, D, BAND>), grid, block, 0, st, a, nkv, kv_bo, q_bo);
+  return hipGetLastError();
+}
+
+template <class T, int D>
+static hipError_t launch_fused_t(const BwdArgs& a, hipStream_t st) {
+  if constexpr (D <= 64) {
+    if (a.s.drop_t > 0 || a.s.alibi || a.s.mask) return hipErrorInvalidValue;
+    if (a.s.band == 2) return launch_fused_t3<T, D, 2>(a, st);
+    if (a.s.band == 1) return launch_fused_t3<T, D, 1>(a, st);
+    return launch_fused_t3<T, D, 0>(a, st);
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
 template <class T, int D>
 static hipError_t stage_d(int stage, const BwdArgs& a, hipStream_t st) {
   if (stage == 0) return launch_pre_t<T, D>(a, st);
   if (stage == 1) return launch_kv_t<T, D>(a, st);
+  if (stage == 3) return launch_fused_t<T, D>(a, st);
   return launch_q_t<T, D>(a, st);
 }
 

@@ -152,6 +152,8 @@ struct Fp8FwdArgs {
 // Internal launchers (return a hipError_t from the launch).
 hipError_t launch_forward(const FwdArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_forward_fp8(const Fp8FwdArgs& a, int out_dtype, hipStream_t stream);
+// stage 0: D and the log2-scaled LSE; 1: dK, dV; 2: dQ; 3: stages 1 and 2 in one
+// launch (d <= 64; no dropout, score bias or block mask)
 hipError_t launch_backward_stage(int stage, const BwdArgs& a, int dtype, hipStream_t stream);
 
 }  // namespace fa

@@ -119,16 +119,20 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * fa_backward_stage: one of the three stages fa_backward runs, in this order,
- * with the same arguments and the same workspace:
+ * fa_backward_stage: one of the stages fa_backward runs, with the same
+ * arguments and the same workspace:
  *   stage 0  D = rowsum(dO * O) and the base-2 LSE per query row, into the
  *            workspace
  *   stage 1  per key block: recompute P and dS, write dk and dv
  *   stage 2  per query block: recompute P and dS, write dq
+ *   stage 3  stages 1 and 2 in one launch (key-block workgroups first, then
+ *            query-block ones); only for d <= 64 without a block mask, the
+ *            case where fa_backward runs stages 0, 3 instead of 0, 1, 2
+ *            (FA_ERR_UNSUPPORTED otherwise)
  * Stages 1 and 2 both need stage 0's result and nothing from each other.
- * Running stages 0, 1, 2 in order equals one fa_backward call. It exists so
- * that each stage can be timed on its own. Returns FA_OK or a negative status
- * (FA_ERR_INVALID_ARG for a stage outside 0..2).
+ * Running stages 0, 1, 2 (or 0, 3) in order equals one fa_backward call. It
+ * exists so that each stage can be timed on its own. Returns FA_OK or a
+ * negative status (FA_ERR_INVALID_ARG for a stage outside 0..3).
  */
 int fa_backward_stage(int stage, const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dO, void* dq, void* dk, void* dv,

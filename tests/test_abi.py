@@ -130,10 +130,14 @@ def test_backward_rejects(lib):
     assert bwd(lib, lse=None) == EINVAL
     assert bwd(lib, d=100) == EINVAL
     assert bwd(lib, scale=float("nan")) == EINVAL
-    for st in (-1, 3, 99):
+    for st in (-1, 4, 99):
         assert bwd(lib, stage=st) == EINVAL
     assert bwd(lib, stage=1, ws=None) == EWS
     assert bwd(lib, stage=0, dtype=F32) == EUNSUP
+    # stage 3 (dK/dV and dQ in one launch) only where fa_backward uses it
+    assert bwd(lib, stage=3, d=128) == EUNSUP
+    assert bwd(lib, stage=3, mask=GOOD) == EUNSUP
+    assert bwd(lib, stage=3, ws=None) == EWS
 
 
 def fwd_drop(lib, rate, dtype=BF16, d=64, seed=7):
@@ -162,7 +166,8 @@ def test_dropout_argument_order(lib):
     assert fwd_drop(lib, 0.5, dtype=F32) == EUNSUP     # no float32 dropout kernel
     assert fwd_drop(lib, 0.5, d=16) == EINVAL          # bad shape reported first
     assert bwd_drop(lib, 0.5, dtype=F32) == EUNSUP
-    assert bwd_drop(lib, 0.2, stage=3) == EINVAL
+    assert bwd_drop(lib, 0.2, stage=4) == EINVAL
+    assert bwd_drop(lib, 0.2, stage=3) == EUNSUP       # no one-launch variant with dropout
 
 
 def fwd_qk(lib, Nq=256, Nk=512, d=64, mask=None, dtype=BF16, rate=0.0, B=1, H=2, Hkv=1, wl=-1, wr=-1, alibi=None):
