@@ -172,6 +172,14 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   return fa::launch_forward(a, dtype, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+// The one-launch backward (stage 3) covers d <= 64 without dropout, score bias
+// or block mask, with all its workgroups in one grid dimension.
+bool fused_ok(const Geo& g, float rate, const float* alibi, const uint8_t* block_mask) {
+  const long long nkb = (g.Nk + 127) / 128, nqb = (g.Nq + 127) / 128;
+  const long long wgs = (long long)g.B * ((long long)g.Hkv * nkb + (long long)g.H * nqb);
+  return g.d <= 64 && rate == 0.f && alibi == nullptr && block_mask == nullptr && wgs <= 0x7fffffffLL;
+}
+
 int stage_impl(int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dO, void* dq, void* dk, void* dv, const Geo& g, float scale, int causal,
                int window_left, int window_right, const float* alibi, const uint8_t* block_mask, int dtype,
@@ -187,7 +195,7 @@ int stage_impl(int stage, const void* q, const void* k, const void* v, const voi
   a.s = make_shape(g, scale, band, block_mask);
   a.s.alibi = alibi;
   if (!set_dropout(a.s, rate, seed)) return FA_ERR_INVALID_ARG;
-  if (stage == 3 && (g.d > 64 || a.s.drop_t > 0 || alibi || block_mask)) return FA_ERR_UNSUPPORTED;
+  if (stage == 3 && (!fused_ok(g, 0.f, alibi, block_mask) || a.s.drop_t > 0)) return FA_ERR_UNSUPPORTED;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -213,7 +221,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   // kernels run two workgroups per CU each and go out as one launch (stage 3),
   // so the dQ workgroups fill the CUs the dK/dV kernel's causal tail leaves
   // idle (a block-sparse grid is balanced already and gains nothing).
-  const bool fused = g.d <= 64 && rate == 0.f && alibi == nullptr && block_mask == nullptr;
+  const bool fused = fused_ok(g, rate, alibi, block_mask);
   const int stages[3] = {0, fused ? 3 : 1, 2};
   for (int i = 0; i < (fused ? 2 : 3); ++i) {
     const int stage = stages[i];

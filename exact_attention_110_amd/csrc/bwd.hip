@@ -798,9 +798,10 @@ static hipError_t launch_fused_t3(const BwdArgs& a, hipStream_t st) {
   const int nkb = (a.s.Nk + KV_BKV - 1) / KV_BKV, nqb = (a.s.Nq + Q_BM - 1) / Q_BM;
   const int kv_bo = (long long)a.s.Hkv * nkb >= FA_BATCH_OUTER_MIN ? 1 : 0;
   const int q_bo = (long long)a.s.H * nqb >= FA_BATCH_OUTER_MIN ? 1 : 0;
-  const int nkv = a.s.Hkv * a.s.B * nkb, nq = a.s.H * a.s.B * nqb;
+  const long long nkv = (long long)a.s.Hkv * a.s.B * nkb, nq = (long long)a.s.H * a.s.B * nqb;
+  if (nkv + nq > 0x7fffffffLL) return hipErrorInvalidValue;  // the caller checks this first
   const dim3 grid((unsigned)(nkv + nq)), block(KV_NW * 64);
-  hipLaunchKernelGGL((bwd_fused_kernel<T, D, BAND>), grid, block, 0, st, a, nkv, kv_bo, q_bo);
+  hipLaunchKernelGGL((bwd_fused_kernel<T, D, BAND>), grid, block, 0, st, a, (int)nkv, kv_bo, q_bo);
   return hipGetLastError();
 }
 
