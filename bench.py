@@ -38,6 +38,10 @@ Prints one JSON line. Besides the headline it carries:
   bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary
   (profiles/*_hbm_traffic.md), or null once the kernel's sources have changed
   since the counters were taken;
+  "roofline.hbm" sets the same kernel against the 8 TB/s HBM peak (those
+  counter bytes over the launch time); "config.effective_hbm_gbs" is the
+  step's compulsory bytes (every input read once, every output written once)
+  over the step time — the rates short sequences are judged by;
 * "cpu_baseline": the float64 CPU oracle timed on a bounded sample of the same
   workload (six heads, forward+backward), in the same unit.
 """
@@ -262,17 +266,31 @@ def main():
     dom = max(kernels, key=lambda n: kernels[n][0])
     t_dom, f_dom = kernels[dom]
     achieved = f_dom / (t_dom * 1e-3) / 1e12
+    traffic = None if args.dropout else measured_traffic(dom, w.name)
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None if args.dropout else measured_traffic(dom, w.name),
+                "traffic": traffic,
                 "launch_ms": round(t_dom, 4), "flop_per_launch": f_dom,
                 "kernels_ms": {n: round(v[0], 4) for n, v in kernels.items()}}
+    # the same kernel against the HBM roofline: its counter-measured bytes per
+    # launch over the launch time (what short sequences are judged by)
+    if traffic is not None:
+        hbm = traffic / (t_dom * 1e-3) / 1e9
+        roofline["hbm"] = {"achieved": round(hbm, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": round(hbm / PEAK_HBM_GBS, 4)}
 
     if args.copy_mb:
         src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
+
+    # compulsory HBM bytes of a step: every input read once, every output written
+    # once (forward: q, k, v in, o and lse out; backward: q, k, v, o, lse, dO in,
+    # dq, dk, dv out)
+    el = q.element_size()
+    qb, kb, lb = q.numel() * el, k.numel() * el, lse.numel() * 4
+    step_bytes = (2 * qb + 2 * kb + lb) + ((3 * qb + 2 * kb + lb) + (qb + 2 * kb) if w.backward else 0)
 
     line = {
         "metric": "attention fwd+bwd TFLOP/s (bf16, causal) and % of MFMA peak, N=16K d=128",
@@ -290,6 +308,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
                    "causal": w.causal, "block_sparse": w.sparse, "passes": "fwd+bwd" if w.backward else "fwd",
                    "flop_per_step": total_flop, "mfma_peak_frac": round(value / PEAK_BF16_TFLOPS, 4),
+                   "compulsory_bytes_per_step": step_bytes,
+                   "effective_hbm_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 1),
                    "dropout": args.dropout},
         "roofline": roofline,
     }
