@@ -41,7 +41,8 @@ Prints one JSON line. Besides the headline it carries:
   "roofline.hbm" sets the same kernel against the 8 TB/s HBM peak (those
   counter bytes over the launch time); "config.effective_hbm_gbs" is the
   step's compulsory bytes (every input read once, every output written once)
-  over the step time — the rates short sequences are judged by;
+  over the step time — the rates that describe short sequences, whose kernels
+  reach neither roofline;
 * "cpu_baseline": the float64 CPU oracle timed on a bounded sample of the same
   workload (six heads, forward+backward), in the same unit.
 """
@@ -273,7 +274,7 @@ def main():
                 "launch_ms": round(t_dom, 4), "flop_per_launch": f_dom,
                 "kernels_ms": {n: round(v[0], 4) for n, v in kernels.items()}}
     # the same kernel against the HBM roofline: its counter-measured bytes per
-    # launch over the launch time (what short sequences are judged by)
+    # launch over the launch time (the rate that describes short sequences)
     if traffic is not None:
         hbm = traffic / (t_dom * 1e-3) / 1e9
         roofline["hbm"] = {"achieved": round(hbm, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
