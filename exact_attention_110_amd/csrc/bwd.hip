@@ -699,7 +699,7 @@ __device__ __forceinline__ void bwd_q_body(const BwdArgs& a, const int h, const 
 template <class T, int D, int BAND, bool MASK, bool DROP, bool ALIBI>
 __global__ __launch_bounds__(Q_NW * 64, FA_Q_OCC) void bwd_q_kernel(BwdArgs a) {
   const GridPos gp = grid_pos(a.s);  // grid: tile_grid over query heads and query blocks
-  bwd_q_body<T, D, BAND, MASK, DROP, ALIBI>(a, blockIdx.x, gp.b, gp.blk, gp.nblk);
+  bwd_q_body<T, D, BAND, MASK, DROP, ALIBI>(a, query_head(a.s, blockIdx.x), gp.b, gp.blk, gp.nblk);
 }
 
 // ---------------------------------------------------------------------------
@@ -723,7 +723,7 @@ __global__ __launch_bounds__(KV_NW * 64, 2) void bwd_fused_kernel(BwdArgs a, int
   } else {
     const int nqb = (a.s.Nq + Q_BM - 1) / Q_BM;
     const int i = id - nkv;
-    const int h = i % a.s.H, r = i / a.s.H;
+    const int h = query_head(a.s, i % a.s.H), r = i / a.s.H;
     bwd_q_body<T, D, BAND, false, false, false>(a, h, q_bo ? r / nqb : r % a.s.B, q_bo ? r % nqb : r / a.s.B, nqb);
   }
 }

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(F8_NW * 64, 2) void fwd_fp8_kernel(Fp8FwdArgs a) {
   // grid (tile_grid); under causal masking the longest blocks first
   const GridPos gp = grid_pos(s);
   const int qb = BAND ? gp.nblk - 1 - gp.blk : gp.blk;
-  const int h = blockIdx.x, b = gp.b;
+  const int h = query_head(s, blockIdx.x), b = gp.b;
   const int hk = h / s.G;
   const SeqView sv = seq_view(s, b, h, hk);
   const int nq = sv.nq, nk = sv.nk;

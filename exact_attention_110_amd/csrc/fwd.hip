@@ -72,7 +72,7 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
   // masking, longer) query blocks are dispatched first
   const GridPos gp = grid_pos(s);
   const int qb = BAND ? gp.nblk - 1 - gp.blk : gp.blk;
-  const int h = blockIdx.x, b = gp.b;
+  const int h = query_head(s, blockIdx.x), b = gp.b;
   const int hk = h / s.G;
   const SeqView sv = seq_view(s, b, h, hk);
   const int nq = sv.nq, nk = sv.nk, off = sv.off;
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
   // masking, longer) query blocks are dispatched first
   const GridPos gp = grid_pos(s);
   const int qb = BAND ? gp.nblk - 1 - gp.blk : gp.blk;
-  const int h = blockIdx.x, b = gp.b;
+  const int h = query_head(s, blockIdx.x), b = gp.b;
   const int hk = h / s.G;
   const SeqView sv = seq_view(s, b, h, hk);
   const int nq = sv.nq, nk = sv.nk, off = sv.off;

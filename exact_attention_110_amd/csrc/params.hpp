@@ -127,6 +127,17 @@ inline dim3 tile_grid(AttnShape& s, int heads, int nblk) {
   return s.batch_outer ? dim3(heads, nblk, s.B) : dim3(heads, s.B, nblk);
 }
 
+// Query head of grid column x (columns run fastest): the G query heads of kv
+// head g take columns g, g + Hkv, g + 2 Hkv, ..., so with the round-robin over
+// the 8 XCDs a group's heads share one XCD's L2 and its K/V tiles instead of
+// each XCD fetching them; the identity when G = 1.
+#ifndef FA_GROUP_HEADS_BY_XCD
+#define FA_GROUP_HEADS_BY_XCD 1
+#endif
+__device__ __forceinline__ int query_head(const AttnShape& s, int x) {
+  return FA_GROUP_HEADS_BY_XCD ? (x % s.Hkv) * s.G + x / s.Hkv : x;
+}
+
 struct GridPos {
   int b;     // batch (sequence)
   int blk;   // block index in launch order
