@@ -868,9 +868,9 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   const bool mask = a.s.mask != nullptr;
   // The 64-row kernel pays off for long sequences over few heads (measured:
   // N = 16384 x 16 heads, 4% faster). With many workgroups the 32-row kernel's
-  // two waves per SIMD balance better (4 x 32 heads at N = 8192: 6% faster),
-  // and short rows spend much of their time in the 64-row kernel's diagonal
-  // tail (N = 1024: 1.8x faster with 32 rows).
+  // two waves per SIMD balance better (4 x 32 heads over 8 kv heads at
+  // N = 8192: 1% faster), and short rows spend much of their time in the
+  // 64-row kernel's diagonal tail (N = 1024: 1.8x faster with 32 rows).
   // FA_FORWARD_ROWS_PER_WAVE=64 or 32 overrides the choice (tests use it to
   // cover both kernels at every size).
   const long long wg64 = (long long)a.s.B * a.s.H * ((a.s.Nq + F64_BM - 1) / F64_BM);
