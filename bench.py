@@ -8,8 +8,8 @@ N x N x d contraction, two contractions forward and five backward (the
 recomputed QK^T included), halved for causal masking.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--copy-mb MB] [--dropout RATE] [--packed]
-                       [--window W] [--alibi] [--fp8]
+                       [--no-cpu-baseline] [--flush-mb MB] [--copy-mb MB] [--dropout RATE]
+                       [--packed] [--window W] [--alibi] [--fp8]
 
 --fp8 times the FP8 (E4M3) forward pass (fa_forward_fp8) on the workload's
 shape against the 16-bit forward; not the headline configuration.
@@ -28,8 +28,10 @@ not the headline configuration.
 
 Prints one JSON line. Besides the headline it carries:
 * "roofline": the dominant kernel's algorithmic FLOP per launch over its mean
-  launch time, measured with HIP events on the stream the library launches on,
-  against the dense bf16 MFMA peak (2.5 PFLOP/s). The backward pass runs a
+  duration inside the step loop, measured with HIP events between the step's
+  kernels on the stream the library launches on, against the dense bf16 MFMA
+  peak (2.5 PFLOP/s); the same kernel's mean when run back to back is given
+  beside it ("launch_ms_back_to_back", "frac_back_to_back"). The backward pass runs a
   key-block kernel (S and dP recomputed, dV and dK: 4 contractions) and a
   query-block kernel (S and dP recomputed, dQ: 3 contractions); each kernel is
   credited with the contractions it performs. For d <= 64 without a block mask
@@ -43,6 +45,10 @@ Prints one JSON line. Besides the headline it carries:
   step's compulsory bytes (every input read once, every output written once)
   over the step time — the rates that describe short sequences, whose kernels
   reach neither roofline;
+* "config.event_step_ms": mean, median and minimum step time from HIP events
+  (the step's kernels run as the stages of fa_backward, in its order); with
+  --flush-mb MB, "config.flushed" repeats them for steps that each follow a
+  write of MB MiB (cold caches), with the effective HBM rates of both;
 * "cpu_baseline": the float64 CPU oracle timed on a bounded sample of the same
   workload (six heads, forward+backward), in the same unit.
 """
@@ -128,6 +134,8 @@ def parse():
                     help="causal attention with ALiBi's geometric slopes, one per head (not the headline)")
     ap.add_argument("--packed", action="store_true",
                     help="time packed variable-length batches of the workload's tokens (not the headline)")
+    ap.add_argument("--flush-mb", type=int, default=0,
+                    help="also time steps that each start after writing this many MiB (cold caches)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after timing, run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -218,7 +226,47 @@ def main():
     value = total_flop / (ms * 1e-3) / 1e12
     print(f"[bench] {w.name}: {ms:.3f} ms/step, {value:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
-    # per-kernel times with HIP events on the library's stream (torch's current stream)
+    # The same step again with HIP events between its kernels (on torch's
+    # current stream, which the library launches on): the forward call, then
+    # the stages fa_backward runs, in its order (D, then dK/dV and dQ, or for
+    # d <= 64 without a block mask or dropout both in one launch). This gives
+    # each kernel's duration inside the step loop, and each step's duration for
+    # the median and minimum. With --flush-mb, a write of that many MiB runs
+    # before each step, outside the events, so that the step starts from caches
+    # holding none of its inputs.
+    stages = binding.backward_stages(w.B, w.H, w.Hkv, w.N, w.N, w.d, args.dropout, block_mask=mask is not None,
+                                     dtype=q.dtype) if w.backward else []
+    stage = lambda s: (lambda: binding.backward_stage(s, q, k, v, o, lse, do, dq, dk, dv, ws,  # noqa: E731
+                                                      w.scale, w.causal, mask, **drop))
+    parts = [lambda: binding.forward(q, k, v, w.scale, w.causal, mask, out=o, lse=lse, **drop)]
+    parts += [stage(sg) for sg in stages]
+    flush = torch.empty(args.flush_mb << 20, dtype=torch.uint8, device=dev) if args.flush_mb else None
+
+    def event_steps(n, flushed):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(n)]
+        for i in range(n):
+            if flushed:
+                flush.fill_(i & 0xff)
+            evs[i][0].record()
+            for j, fn in enumerate(parts):
+                fn()
+                evs[i][j + 1].record()
+        torch.cuda.synchronize()
+        per = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(len(parts))] for i in range(n)])
+        return per  # ms, [step][kernel]
+
+    def step_stats(per):
+        tot = per.sum(axis=1)
+        return {"mean": round(float(tot.mean()), 4), "median": round(float(np.median(tot)), 4),
+                "min": round(float(tot.min()), 4)}
+
+    per_step = event_steps(args.steps, False)
+    in_step = per_step.mean(axis=0)
+    st_warm = step_stats(per_step)
+    print(f"[bench] event-timed steps: mean {st_warm['mean']:.3f} / median {st_warm['median']:.3f} / "
+          f"min {st_warm['min']:.3f} ms", file=sys.stderr, flush=True)
+
+    # per-kernel times with HIP events, each kernel back to back on its own
     def event_time(fn, n):
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         fn()
@@ -232,47 +280,36 @@ def main():
 
     n_ev = max(args.steps, 5)
     per_contraction = fwd_flop / 2.0  # one N x N x d contraction of the workload
-    t_fwd = event_time(lambda: binding.forward(q, k, v, w.scale, w.causal, mask, out=o, lse=lse, **drop), n_ev)
-    # kernel -> (mean launch time in ms, algorithmic FLOP per launch)
-    # the library's choice of forward kernel: 64 query rows per wave for long
-    # dense rows over few workgroups (N >= 8192, B*H*ceil(N/256) <= 2048), else 32
-    env_rows = os.environ.get("FA_FORWARD_ROWS_PER_WAVE")
-    use64 = mask is None and ((w.N >= 8192 and w.B * w.H * -(-w.N // 256) <= 2048) if env_rows not in ("32", "64")
-                              else env_rows == "64")
-    if w.dtype == "fp32":
-        fwd_name = "fwd_f32_kernel"
-    else:
-        fwd_name = "fwd64_kernel" if use64 else "fwd_kernel"
-    kernels = {fwd_name: (t_fwd, 2 * per_contraction)}
-    if w.backward:
-        stage = lambda s: (lambda: binding.backward_stage(s, q, k, v, o, lse, do, dq, dk, dv, ws,  # noqa: E731
-                                                          w.scale, w.causal, mask, **drop))
-        t_pre = event_time(stage(0), n_ev)
-        t_kv = event_time(stage(1), n_ev)
-        t_q = event_time(stage(2), n_ev)
-        # the key-block kernel recomputes S and dP and forms dV and dK (4 contractions);
-        # the query-block kernel recomputes S and dP and forms dQ (3 contractions)
-        print(f"[bench] forward {t_fwd:.3f} ms ({2 * per_contraction / t_fwd / 1e9:.1f} TFLOP/s); backward "
-              f"stages D {t_pre:.3f} / dK,dV {t_kv:.3f} ({4 * per_contraction / t_kv / 1e9:.1f} TFLOP/s) / "
-              f"dQ {t_q:.3f} ms ({3 * per_contraction / t_q / 1e9:.1f} TFLOP/s)", file=sys.stderr, flush=True)
-        if w.d <= 64 and mask is None and not args.dropout:
-            # fa_backward runs both as one launch here (stage 3): that is the kernel of the step
-            t_f = event_time(stage(3), n_ev)
-            kernels["bwd_fused_kernel"] = (t_f, 7 * per_contraction)
-            print(f"[bench] dK,dV + dQ in one launch (the step's kernel) {t_f:.3f} ms "
-                  f"({7 * per_contraction / t_f / 1e9:.1f} TFLOP/s)", file=sys.stderr, flush=True)
-        else:
-            kernels["bwd_kv_kernel"] = (t_kv, 4 * per_contraction)
-            kernels["bwd_q_kernel"] = (t_q, 3 * per_contraction)
+    # the forward kernel the library launches for this call
+    rows = binding.forward_kernel_rows(w.B, w.H, w.Hkv, w.N, w.N, w.d, w.causal, block_mask=mask is not None,
+                                       dtype=q.dtype)
+    fwd_name = {0: "fwd_f32_kernel", 32: "fwd_kernel", 64: "fwd64_kernel"}[rows]
+    names = [fwd_name] + [{0: "bwd_pre_kernel", 1: "bwd_kv_kernel", 2: "bwd_q_kernel",
+                           3: "bwd_fused_kernel"}[sg] for sg in stages]
+    # algorithmic FLOP per launch: the forward forms S and P V (2 contractions);
+    # the key-block kernel recomputes S and dP and forms dV and dK (4); the
+    # query-block kernel recomputes S and dP and forms dQ (3); the one-launch
+    # backward does both (7); D is not a contraction
+    credit = {fwd_name: 2, "bwd_pre_kernel": 0, "bwd_kv_kernel": 4, "bwd_q_kernel": 3, "bwd_fused_kernel": 7}
+    isolated = [event_time(fn, n_ev) for fn in parts]
+    kernels = {n: (float(in_step[j]), isolated[j], credit[n] * per_contraction) for j, n in enumerate(names)}
+    msg = "; ".join(f"{n} {t:.3f} ms in the step ({f / (t * 1e-3) / 1e12 if f else 0:.1f} TFLOP/s), "
+                    f"{ti:.3f} ms back to back" for n, (t, ti, f) in kernels.items())
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
     dom = max(kernels, key=lambda n: kernels[n][0])
-    t_dom, f_dom = kernels[dom]
+    t_dom, t_iso, f_dom = kernels[dom]
     achieved = f_dom / (t_dom * 1e-3) / 1e12
     traffic = None if args.dropout else measured_traffic(dom, w.name)
+    # frac uses the kernel's mean duration inside the step loop; the mean of the
+    # same kernel run back to back (warmer caches) is reported beside it
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic,
-                "launch_ms": round(t_dom, 4), "flop_per_launch": f_dom,
-                "kernels_ms": {n: round(v[0], 4) for n, v in kernels.items()}}
+                "launch_ms": round(t_dom, 4), "launch_ms_back_to_back": round(t_iso, 4),
+                "frac_back_to_back": round(f_dom / (t_iso * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "flop_per_launch": f_dom,
+                "kernels_ms": {n: round(v[0], 4) for n, v in kernels.items()},
+                "kernels_ms_back_to_back": {n: round(v[1], 4) for n, v in kernels.items()}}
     # the same kernel against the HBM roofline: its counter-measured bytes per
     # launch over the launch time (the rate that describes short sequences)
     if traffic is not None:
@@ -311,9 +348,21 @@ def main():
                    "flop_per_step": total_flop, "mfma_peak_frac": round(value / PEAK_BF16_TFLOPS, 4),
                    "compulsory_bytes_per_step": step_bytes,
                    "effective_hbm_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 1),
-                   "dropout": args.dropout},
+                   "dropout": args.dropout,
+                   "event_step_ms": st_warm},
         "roofline": roofline,
     }
+    if args.flush_mb:
+        # cold-cache steps: each starts after a write of flush_mb MiB (larger than
+        # the 4 MB per-XCD L2 caches and the 256 MB memory-side cache together)
+        st_cold = step_stats(event_steps(args.steps, True))
+        line["config"]["flushed"] = {
+            "flush_mb": args.flush_mb, "event_step_ms": st_cold,
+            "effective_hbm_gbs": {k: round(step_bytes / (t * 1e-3) / 1e9, 1) for k, t in st_cold.items()}}
+        line["config"]["warm_effective_hbm_gbs"] = {k: round(step_bytes / (t * 1e-3) / 1e9, 1)
+                                                    for k, t in st_warm.items()}
+        print(f"[bench] flushed steps ({args.flush_mb} MiB written before each): mean {st_cold['mean']:.3f} / "
+              f"median {st_cold['median']:.3f} / min {st_cold['min']:.3f} ms", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, x)
     print(json.dumps(line), flush=True)
@@ -478,20 +527,6 @@ def window_main(args, w):
     print(json.dumps(line), flush=True)
 
 
-def packed_lengths(total, mean, seed):
-    """Exponential lengths of the given mean (at least 16) until they sum to total."""
-    import numpy as np
-    rng = np.random.default_rng(seed)
-    out = []
-    while sum(out) < total:
-        out.append(max(16, int(round(rng.exponential(mean)))))
-    out[-1] -= sum(out) - total
-    if out[-1] < 1:
-        out.pop()
-        out[-1] += total - sum(out)
-    return out
-
-
 def packed_main(args, w):
     """Packed variable-length batch of the workload's tokens against the same
     sequences padded to the longest one."""
@@ -503,7 +538,7 @@ def packed_main(args, w):
         print("--packed needs a dense 16-bit workload", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda", 0)
-    lens = packed_lengths(w.B * w.N, w.N / 8, w.seed + 300)
+    lens = I.packed_lengths(w.B * w.N, w.N / 8, w.seed + 300)
     x = I.make_packed(lens, lens, w.H, w.Hkv, w.d, w.dtype, w.seed, with_grad=True)
     q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
     cu = torch.from_numpy(x["cu_q"]).to(dev)

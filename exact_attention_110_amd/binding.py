@@ -67,6 +67,12 @@ def load():
     lib.fa_backward_varlen.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, I, I, P, I,
                                        F, U64, P, S, P]
     lib.fa_backward_varlen.restype = I
+    lib.fa_forward_select.argtypes = [I, P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, P, P, I, F, U64, P]
+    lib.fa_forward_select.restype = I
+    lib.fa_forward_kernel_rows.argtypes = [I] * 12
+    lib.fa_forward_kernel_rows.restype = I
+    lib.fa_backward_launches.argtypes = [I, I, I, I, I, I, F, I, I, I]
+    lib.fa_backward_launches.restype = I
     lib.fa_forward_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, F, F, F, F, I, I, P]
     lib.fa_forward_fp8.restype = I
     lib.fa_status_string.argtypes = [I]
@@ -141,14 +147,36 @@ def _slopes(alibi_slopes, H, device):
     return t
 
 
+def forward_kernel_rows(B, H, Hkv, Nq, Nk, d, causal=False, window=(-1, -1), alibi=False, block_mask=False,
+                        dtype=torch.bfloat16):
+    """Rows per wave of the forward kernel the library takes for these
+    arguments (64 or 32; 0 for float32 inputs): fa_forward_kernel_rows."""
+    r = load().fa_forward_kernel_rows(B, H, Hkv, Nq, Nk, d, int(bool(causal)), int(window[0]), int(window[1]),
+                                      int(bool(alibi)), int(bool(block_mask)), _DTYPES[dtype])
+    if r < 0:
+        raise FAError(r, "fa_forward_kernel_rows")
+    return r
+
+
+def backward_stages(B, H, Hkv, Nq, Nk, d, dropout_rate=0.0, alibi=False, block_mask=False, dtype=torch.bfloat16):
+    """The stages fa_backward runs for these arguments, in order: [0, 1, 2],
+    or [0, 3] where dK/dV and dQ go out as one launch (fa_backward_launches)."""
+    n = load().fa_backward_launches(B, H, Hkv, Nq, Nk, d, float(dropout_rate), int(bool(alibi)),
+                                    int(bool(block_mask)), _DTYPES[dtype])
+    if n < 0:
+        raise FAError(n, "fa_backward_launches")
+    return [0, 3] if n == 2 else [0, 1, 2]
+
+
 def forward(q, k, v, scale=None, causal=False, block_mask=None, out=None, lse=None, dropout_rate=0.0,
-            seed=0, window=(-1, -1), alibi_slopes=None):
+            seed=0, window=(-1, -1), alibi_slopes=None, rows_per_wave=0):
     """O, LSE = attention(q, k, v); q [B,H,Nq,d], k, v [B,Hkv,Nk,d] on the GPU.
 
     Nq == Nk without a window or ALiBi slopes calls fa_forward
     (fa_forward_dropout with a positive dropout_rate); otherwise fa_forward_qk
     (causal masking aligned to the last query; window = (left, right), -1
-    unbounded; alibi_slopes: one slope per query head)."""
+    unbounded; alibi_slopes: one slope per query head). rows_per_wave 32 or
+    64 forces that 16-bit forward kernel (fa_forward_select)."""
     B, H, Hkv, N, Nk, d = _shape4(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
@@ -156,6 +184,13 @@ def forward(q, k, v, scale=None, causal=False, block_mask=None, out=None, lse=No
     m = _mask(block_mask, N, q.device, Nk)
     wl, wr = (int(x) for x in window)
     al = _slopes(alibi_slopes, H, q.device)
+    if rows_per_wave:
+        st = load().fa_forward_select(int(rows_per_wave), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H,
+                                      Hkv, N, Nk, d, scale, int(bool(causal)), wl, wr, _ptr(al), _ptr(m),
+                                      _DTYPES[q.dtype], float(dropout_rate), _seed(seed), _stream(q.device))
+        if st != 0:
+            raise FAError(st, "fa_forward_select")
+        return o, lse_t
     if Nk != N or (wl, wr) != (-1, -1) or al is not None:
         st = load().fa_forward_qk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, Hkv, N, Nk, d, scale,
                                   int(bool(causal)), wl, wr, _ptr(al), _ptr(m), _DTYPES[q.dtype],

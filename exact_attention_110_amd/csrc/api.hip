@@ -148,7 +148,8 @@ int check_backward(const void* q, const void* k, const void* v, const void* o, c
 
 int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, const Geo& g,
                  float scale, int causal, int window_left, int window_right, const float* alibi,
-                 const uint8_t* block_mask, int dtype, float rate, unsigned long long seed, void* stream) {
+                 const uint8_t* block_mask, int dtype, float rate, unsigned long long seed, void* stream,
+                 int rows = 0) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u) ||
       ((uintptr_t)alibi & 3u))
@@ -168,8 +169,11 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   a.v = v;
   a.o = o;
   a.lse = lse;
+  if (rows != 0 && rows != 32 && rows != 64) return FA_ERR_INVALID_ARG;
+  if (dtype == FA_F32 && rows != 0) return FA_ERR_UNSUPPORTED;
+  if (rows == 64 && (block_mask || alibi)) return FA_ERR_UNSUPPORTED;
   (void)hipGetLastError();  // clear a stale error so the check below sees only this launch
-  return fa::launch_forward(a, dtype, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return fa::launch_forward(a, dtype, (hipStream_t)stream, rows) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 // The one-launch backward (stage 3) covers d <= 64 without dropout, score bias
@@ -221,7 +225,9 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   // kernels run two workgroups per CU each and go out as one launch (stage 3),
   // so the dQ workgroups fill the CUs the dK/dV kernel's causal tail leaves
   // idle (a block-sparse grid is balanced already and gains nothing).
-  const bool fused = fused_ok(g, rate, alibi, block_mask);
+  fa::AttnShape probe = make_shape(g, scale, Band{0, 0, 0}, nullptr);
+  if (!set_dropout(probe, rate, seed)) return FA_ERR_INVALID_ARG;
+  const bool fused = fused_ok(g, probe.drop_t > 0 ? rate : 0.f, alibi, block_mask);
   const int stages[3] = {0, fused ? 3 : 1, 2};
   for (int i = 0; i < (fused ? 2 : 3); ++i) {
     const int stage = stages[i];
@@ -263,6 +269,42 @@ int fa_forward_qk(const void* q, const void* k, const void* v, void* o, float* l
                   float dropout_rate, unsigned long long seed, void* stream) {
   return forward_impl(q, k, v, o, lse, fixed_geo(B, H, Hkv, Nq, Nk, d), scale, causal, window_left, window_right,
                       alibi_slopes, block_mask, dtype, dropout_rate, seed, stream);
+}
+
+int fa_forward_select(int rows_per_wave, const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                      int window_left, int window_right, const float* alibi_slopes,
+                      const uint8_t* block_mask, int dtype, float dropout_rate,
+                      unsigned long long seed, void* stream) {
+  if (rows_per_wave != 0 && rows_per_wave != 32 && rows_per_wave != 64) return FA_ERR_INVALID_ARG;
+  return forward_impl(q, k, v, o, lse, fixed_geo(B, H, Hkv, Nq, Nk, d), scale, causal, window_left, window_right,
+                      alibi_slopes, block_mask, dtype, dropout_rate, seed, stream, rows_per_wave);
+}
+
+int fa_forward_kernel_rows(int B, int H, int Hkv, int Nq, int Nk, int d, int causal, int window_left,
+                           int window_right, int has_alibi, int has_block_mask, int dtype) {
+  const Geo g = fixed_geo(B, H, Hkv, Nq, Nk, d);
+  int st = check_shape(g, 1.0f, dtype);
+  if (st != FA_OK) return st;
+  Band band;
+  if (!make_band(causal, window_left, window_right, &band)) return FA_ERR_INVALID_ARG;
+  fa::AttnShape s = make_shape(g, 1.0f, band, has_block_mask ? (const uint8_t*)1 : nullptr);
+  s.alibi = has_alibi ? (const float*)1 : nullptr;  // only tested for NULL
+  return fa::forward_rows(s, dtype);
+}
+
+int fa_backward_launches(int B, int H, int Hkv, int Nq, int Nk, int d, float dropout_rate, int has_alibi,
+                         int has_block_mask, int dtype) {
+  const Geo g = fixed_geo(B, H, Hkv, Nq, Nk, d);
+  int st = check_shape(g, 1.0f, dtype);
+  if (st != FA_OK) return st;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (!(dropout_rate >= 0.f && dropout_rate < 1.f)) return FA_ERR_INVALID_ARG;
+  fa::AttnShape s = make_shape(g, 1.0f, Band{0, 0, 0}, nullptr);
+  set_dropout(s, dropout_rate, 0ull);
+  const bool fused = fused_ok(g, s.drop_t > 0 ? dropout_rate : 0.f, has_alibi ? (const float*)1 : nullptr,
+                              has_block_mask ? (const uint8_t*)1 : nullptr);
+  return fused ? 2 : 3;
 }
 
 int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -31,8 +31,6 @@
 //
 // float32 inputs take a separate VALU kernel (fp32 FMA throughout) that runs
 // the same recurrence one query row per lane.
-#include <stdlib.h>
-
 #include "common.hpp"
 #include "params.hpp"
 
@@ -836,7 +834,7 @@ __global__ __launch_bounds__(F32_R * F32_S) void fwd_f32_kernel(FwdArgs a) {
 template <class T, int D, int BAND, bool DROP>
 static hipError_t launch_fwd_t3(const FwdArgs& a, hipStream_t st, bool mask, bool use64) {
   const bool alibi = a.s.alibi != nullptr;
-  if (!mask && use64 && !alibi) {  // the 64-row kernel takes no score bias
+  if (use64) {  // the caller has checked: no block mask, no score bias
     FwdArgs la = a;
     const dim3 grid = tile_grid(la.s, a.s.H, (a.s.Nq + F64_BM - 1) / F64_BM);
     hipLaunchKernelGGL((fwd64_kernel<T, D, BAND, DROP>), grid, dim3(F64_NW * 64), 0, st, la);
@@ -863,22 +861,11 @@ static hipError_t launch_fwd_t2(const FwdArgs& a, hipStream_t st, int band, bool
 }
 
 template <class T, int D>
-static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st, int rows) {
   const int band = a.s.band;
   const bool mask = a.s.mask != nullptr;
-  // The 64-row kernel pays off for long sequences over few heads (measured:
-  // N = 16384 x 16 heads, 4% faster). With many workgroups the 32-row kernel's
-  // two waves per SIMD balance better (4 x 32 heads over 8 kv heads at
-  // N = 8192: 1% faster), and short rows spend much of their time in the
-  // 64-row kernel's diagonal tail (N = 1024: 1.8x faster with 32 rows).
-  // FA_FORWARD_ROWS_PER_WAVE=64 or 32 overrides the choice (tests use it to
-  // cover both kernels at every size).
-  const long long wg64 = (long long)a.s.B * a.s.H * ((a.s.Nq + F64_BM - 1) / F64_BM);
-  bool use64 = min(a.s.Nq, a.s.Nk) >= 8192 && wg64 <= 2048;
-  if (const char* env = getenv("FA_FORWARD_ROWS_PER_WAVE")) {
-    if (env[0] == '6' && env[1] == '4' && env[2] == 0) use64 = true;
-    if (env[0] == '3' && env[1] == '2' && env[2] == 0) use64 = false;
-  }
+  const bool use64 = rows == 64;
+  if (use64 && (mask || a.s.alibi)) return hipErrorInvalidValue;  // the 64-row kernel has neither
   if (a.s.drop_t > 0) return launch_fwd_t2<T, D, true>(a, st, band, mask, use64);
   return launch_fwd_t2<T, D, false>(a, st, band, mask, use64);
 }
@@ -890,21 +877,36 @@ static hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_forward(const FwdArgs& a, int dtype, hipStream_t st) {
+// Which 16-bit kernel a forward call takes by default. The 64-row kernel pays
+// off for long sequences over few heads (measured: N = 16384 x 16 heads, 4%
+// faster). With many workgroups the 32-row kernel's two waves per SIMD balance
+// better (4 x 32 heads over 8 kv heads at N = 8192: 1% faster), and short rows
+// spend much of their time in the 64-row kernel's diagonal tail (N = 1024:
+// 1.8x faster with 32 rows). Block masks and score biases always take the
+// 32-row kernel. Float32 inputs take the float32 kernel (0).
+int forward_rows(const AttnShape& s, int dtype) {
+  if (dtype == 0) return 0;
+  if (s.mask || s.alibi) return 32;
+  const long long wg64 = (long long)s.B * s.H * ((s.Nq + F64_BM - 1) / F64_BM);
+  return (min(s.Nq, s.Nk) >= 8192 && wg64 <= 2048) ? 64 : 32;
+}
+
+hipError_t launch_forward(const FwdArgs& a, int dtype, hipStream_t st, int rows) {
   const int d = a.s.d;
   if (dtype == 0) {
     if (d == 32) return launch_fwd_f32<32>(a, st);
     if (d == 64) return launch_fwd_f32<64>(a, st);
     return launch_fwd_f32<128>(a, st);
   }
+  if (rows == 0) rows = forward_rows(a.s, dtype);
   if (dtype == 2) {
-    if (d == 32) return launch_fwd_t<BF16, 32>(a, st);
-    if (d == 64) return launch_fwd_t<BF16, 64>(a, st);
-    return launch_fwd_t<BF16, 128>(a, st);
+    if (d == 32) return launch_fwd_t<BF16, 32>(a, st, rows);
+    if (d == 64) return launch_fwd_t<BF16, 64>(a, st, rows);
+    return launch_fwd_t<BF16, 128>(a, st, rows);
   }
-  if (d == 32) return launch_fwd_t<F16, 32>(a, st);
-  if (d == 64) return launch_fwd_t<F16, 64>(a, st);
-  return launch_fwd_t<F16, 128>(a, st);
+  if (d == 32) return launch_fwd_t<F16, 32>(a, st, rows);
+  if (d == 64) return launch_fwd_t<F16, 64>(a, st, rows);
+  return launch_fwd_t<F16, 128>(a, st, rows);
 }
 
 }  // namespace fa

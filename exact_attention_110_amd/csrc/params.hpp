@@ -161,7 +161,12 @@ struct Fp8FwdArgs {
 };
 
 // Internal launchers (return a hipError_t from the launch).
-hipError_t launch_forward(const FwdArgs& a, int dtype, hipStream_t stream);
+// forward_rows: query rows per wave of the 16-bit forward kernel a call takes
+// by default (64 or 32; 0 for float32 inputs). launch_forward: rows 0 takes
+// that choice, 32 or 64 forces a kernel (64 with a block mask or score bias is
+// hipErrorInvalidValue; the caller rejects it first).
+int forward_rows(const AttnShape& s, int dtype);
+hipError_t launch_forward(const FwdArgs& a, int dtype, hipStream_t stream, int rows);
 hipError_t launch_forward_fp8(const Fp8FwdArgs& a, int out_dtype, hipStream_t stream);
 // stage 0: D and the log2-scaled LSE; 1: dK, dV; 2: dQ; 3: stages 1 and 2 in one
 // launch (d <= 64; no dropout, score bias or block mask)

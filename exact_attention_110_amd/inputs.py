@@ -209,6 +209,22 @@ def length_mix(batch, mean, seed, lo=1):
     return [max(lo, int(round(v))) for v in x]
 
 
+def packed_lengths(total, mean, seed):
+    """Sequence lengths for a packed batch of ``total`` tokens per head:
+    exponential lengths of the given mean (at least 16), drawn until they sum
+    to ``total``, the last one trimmed (or merged into its neighbour) so that
+    they sum to it exactly."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while sum(out) < total:
+        out.append(max(16, int(round(rng.exponential(mean)))))
+    out[-1] -= sum(out) - total
+    if out[-1] < 1:
+        out.pop()
+        out[-1] += total - sum(out)
+    return out
+
+
 def quantize_e4m3(x):
     """Per-tensor FP8 (E4M3) quantisation of a float32 numpy array: descale =
     max|x| / 448 (the format's largest finite value), codes = x / descale

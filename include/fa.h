@@ -141,6 +141,17 @@ int fa_backward_stage(int stage, const void* q, const void* k, const void* v, co
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_backward_launches: how many kernels fa_backward (and fa_backward_qk,
+ * fa_backward_dropout) enqueues for these arguments: 3 for stages 0, 1, 2, or
+ * 2 for stages 0, 3 (d <= 64 without dropout, ALiBi slopes or a block mask),
+ * or a negative status for arguments the backward calls reject. A rate that
+ * rounds to no dropout counts as none. has_alibi and has_block_mask say
+ * whether slopes or a mask would be passed. Touches no device.
+ */
+int fa_backward_launches(int B, int H, int Hkv, int Nq, int Nk, int d, float dropout_rate, int has_alibi,
+                         int has_block_mask, int dtype);
+
+/*
  * Dropout on the attention probabilities, fused into the same kernels
  * (chipfoundryservices.com glossary "flash attention algorithm", "Kernel
  * Fusion", lists dropout among the operations fused into one kernel; the
@@ -212,7 +223,7 @@ int fa_backward_stage_dropout(int stage, const void* q, const void* k, const voi
  *   alibi_slopes   NULL, or device float32 [H], 4-byte aligned (else
  *                  FA_ERR_INVALID_ARG); finite values, not checked (they
  *                  live in device memory). The forward pass uses its 32-row
- *                  kernel for these calls.
+ *                  kernel for these calls (see fa_forward_kernel_rows).
  * dropout_rate 0 is no dropout; dropout otherwise as described above. Other
  * arguments, limits (each of Nq and Nk as N), ownership and errors as for
  * fa_forward / fa_backward.
@@ -229,6 +240,33 @@ int fa_backward_qk(const void* q, const void* k, const void* v, const void* o,
                    const uint8_t* block_mask, int dtype, float dropout_rate,
                    unsigned long long seed, void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/*
+ * Forward kernel choice. The 16-bit forward pass has two kernels: one with 64
+ * query rows per wave (one wave per SIMD; long dense or causal rows over few
+ * heads) and one with 32 rows per wave (two waves per SIMD; everything else,
+ * and every call with a block mask or score bias). Both compute the same
+ * attention (results agree within the tolerances, not bit for bit).
+ *
+ * fa_forward_kernel_rows: the rows per wave of the kernel that fa_forward /
+ * fa_forward_qk / fa_forward_dropout take for these arguments: 64 or 32, 0
+ * for FA_F32 (the float32 kernel), or a negative status for arguments they
+ * would reject. has_alibi and has_block_mask say whether slopes or a mask
+ * would be passed (any nonzero value = yes). Touches no device.
+ *
+ * fa_forward_select: fa_forward_qk with the kernel forced: rows_per_wave 0
+ * takes the library's choice, 32 or 64 force that kernel (64 with a block
+ * mask or ALiBi slopes is FA_ERR_UNSUPPORTED, as is a nonzero value with
+ * FA_F32; other values are FA_ERR_INVALID_ARG). For tests and benchmarks
+ * that compare the two kernels. Other arguments as for fa_forward_qk.
+ */
+int fa_forward_kernel_rows(int B, int H, int Hkv, int Nq, int Nk, int d, int causal, int window_left,
+                           int window_right, int has_alibi, int has_block_mask, int dtype);
+int fa_forward_select(int rows_per_wave, const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                      int window_left, int window_right, const float* alibi_slopes,
+                      const uint8_t* block_mask, int dtype, float dropout_rate,
+                      unsigned long long seed, void* stream);
 
 /*
  * Packed variable-length batches (the same glossary, "Sequence Length

@@ -84,27 +84,31 @@ def check_grad(g, ref, where):
 
 
 def run_small(B, H, Hkv, N, d, dtype, causal, mask=None, seed=0, sigma=1.0, backward=True, scale=None,
-              dropout_rate=0.0, drop_seed=0):
-    """Full comparison (every output element) for a small seeded case."""
+              dropout_rate=0.0, drop_seed=0, rows_per_wave=0):
+    """Full comparison (every output element) for a small seeded case;
+    rows_per_wave 32 or 64 forces that 16-bit forward kernel."""
     where = f"B{B} H{H} Hkv{Hkv} N{N} d{d} {dtype} causal={causal} mask={mask is not None} seed={seed}"
     if dropout_rate:
         where += f" dropout={dropout_rate} drop_seed={drop_seed}"
     x = I.make_small(B, H, Hkv, N, d, dtype, seed, sigma, with_grad=backward)
     return run_given(x, dtype, causal, mask, backward, scale, where, dropout_rate=dropout_rate,
-                     drop_seed=drop_seed)
+                     drop_seed=drop_seed, rows_per_wave=rows_per_wave)
 
 
 def run_given(x, dtype, causal, mask=None, backward=True, scale=None, where="", lse_tol=TOL_LSE,
-              dropout_rate=0.0, drop_seed=0):
+              dropout_rate=0.0, drop_seed=0, rows_per_wave=0):
     """Full comparison (every output element) on given CPU tensors q, k, v (and do);
     with a positive dropout_rate both sides drop with the generator keyed by drop_seed."""
+    if rows_per_wave:
+        where += f" rows_per_wave={rows_per_wave}"
     say("case", where)
     d = x["q"].shape[-1]
     dev = torch.device("cuda", 0)
     q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     mt = None if mask is None else torch.from_numpy(mask).to(dev)
-    o, lse = binding.forward(q, k, v, scale, causal, mt, dropout_rate=dropout_rate, seed=drop_seed)
+    o, lse = binding.forward(q, k, v, scale, causal, mt, dropout_rate=dropout_rate, seed=drop_seed,
+                             rows_per_wave=rows_per_wave)
     torch.cuda.synchronize()
     qd, kd, vd = (np64(x[n]) for n in ("q", "k", "v"))
     oref, lref = oracle.forward(qd, kd, vd, scale, causal, mask, dropout_rate=dropout_rate, seed=drop_seed)
@@ -123,7 +127,7 @@ def run_given(x, dtype, causal, mask=None, backward=True, scale=None, where="", 
 
 
 def run_cross(B, H, Hkv, Nq, Nk, d, dtype, causal, mask=None, seed=0, backward=True, dropout_rate=0.0,
-              drop_seed=0):
+              drop_seed=0, rows_per_wave=0):
     """Full comparison for Nq query rows over Nk keys (fa_forward_qk / fa_backward_qk)."""
     where = (f"B{B} H{H} Hkv{Hkv} Nq{Nq} Nk{Nk} d{d} {dtype} causal={causal} mask={mask is not None} "
              f"seed={seed}")
@@ -131,7 +135,7 @@ def run_cross(B, H, Hkv, Nq, Nk, d, dtype, causal, mask=None, seed=0, backward=T
         where += f" dropout={dropout_rate} drop_seed={drop_seed}"
     x = I.make_cross(B, H, Hkv, Nq, Nk, d, dtype, seed, with_grad=backward)
     return run_given(x, dtype, causal, mask, backward, None, where, dropout_rate=dropout_rate,
-                     drop_seed=drop_seed)
+                     drop_seed=drop_seed, rows_per_wave=rows_per_wave)
 
 
 def run_varlen(lens_q, lens_k, H, Hkv, d, dtype, causal, seed=0, backward=True, dropout_rate=0.0,
@@ -177,10 +181,10 @@ def run_varlen(lens_q, lens_k, H, Hkv, d, dtype, causal, seed=0, backward=True, 
 
 
 def run_window(B, H, Hkv, Nq, Nk, d, dtype, causal, window, mask=None, seed=0, backward=True, dropout_rate=0.0,
-               drop_seed=0):
+               drop_seed=0, rows_per_wave=0):
     """Full comparison with a sliding-window band (fa_forward_qk / fa_backward_qk)."""
     where = (f"B{B} H{H} Hkv{Hkv} Nq{Nq} Nk{Nk} d{d} {dtype} causal={causal} window={tuple(window)} "
-             f"mask={mask is not None} seed={seed}")
+             f"mask={mask is not None} seed={seed} rows_per_wave={rows_per_wave}")
     if dropout_rate:
         where += f" dropout={dropout_rate} drop_seed={drop_seed}"
     say("case", where)
@@ -189,7 +193,8 @@ def run_window(B, H, Hkv, Nq, Nk, d, dtype, causal, window, mask=None, seed=0, b
     q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
     scale = 1.0 / math.sqrt(d)
     mt = None if mask is None else torch.from_numpy(mask).to(dev)
-    o, lse = binding.forward(q, k, v, scale, causal, mt, dropout_rate=dropout_rate, seed=drop_seed, window=window)
+    o, lse = binding.forward(q, k, v, scale, causal, mt, dropout_rate=dropout_rate, seed=drop_seed, window=window,
+                             rows_per_wave=rows_per_wave)
     torch.cuda.synchronize()
     qd, kd, vd = (np64(x[n]) for n in ("q", "k", "v"))
     oref, lref = oracle.forward(qd, kd, vd, scale, causal, mask, dropout_rate=dropout_rate, seed=drop_seed,

@@ -260,3 +260,53 @@ def test_fp8_rejects(lib, bad):
 
 def test_fp8_head_sizes(lib):
     assert fwd8(lib, d=32) == EUNSUP   # the FP8 contraction takes 64 values at a time
+
+
+def test_forward_kernel_rows(lib):
+    """The library's forward-kernel choice, as bench.py reads it: 64 rows per
+    wave for long dense or causal rows over few workgroups, 32 otherwise and
+    always with a block mask or score bias, 0 (the float32 kernel) for FA_F32;
+    negative statuses for arguments the forward calls reject."""
+    rows = lambda *a: lib.fa_forward_kernel_rows(*a)  # noqa: E731
+    # B, H, Hkv, Nq, Nk, d, causal, wl, wr, alibi, mask, dtype
+    assert rows(1, 16, 16, 16384, 16384, 128, 1, -1, -1, 0, 0, BF16) == 64
+    assert rows(1, 16, 16, 16384, 16384, 128, 1, -1, -1, 1, 0, BF16) == 32
+    assert rows(1, 16, 16, 16384, 16384, 128, 1, -1, -1, 0, 1, BF16) == 32
+    assert rows(4, 32, 8, 8192, 8192, 128, 1, -1, -1, 0, 0, BF16) == 32   # 4096 workgroups of 256 rows
+    assert rows(8, 12, 12, 1024, 1024, 64, 1, -1, -1, 0, 0, BF16) == 32
+    assert rows(1, 8, 8, 8192, 8191, 64, 0, -1, -1, 0, 0, F16) == 32      # the shorter side decides
+    assert rows(1, 8, 8, 8192, 8192, 64, 0, -1, -1, 0, 0, F16) == 64
+    assert rows(1, 1, 1, 512, 512, 32, 0, -1, -1, 0, 0, F32) == 0
+    assert rows(1, 2, 1, 256, 256, 96, 1, -1, -1, 0, 0, BF16) == EINVAL
+    assert rows(1, 2, 1, 256, 256, 64, 1, -2, -1, 0, 0, BF16) == EINVAL
+    assert rows(1, 3, 2, 256, 256, 64, 1, -1, -1, 0, 0, BF16) == EINVAL
+
+
+@pytest.mark.parametrize("r,kw,want", [
+    (16, {}, EINVAL), (128, {}, EINVAL), (-32, {}, EINVAL),
+    (64, dict(mask=GOOD), EUNSUP), (64, dict(alibi=GOOD), EUNSUP), (32, dict(dtype=F32), EUNSUP),
+    (64, dict(q=None), EINVAL), (32, dict(d=96), EINVAL),
+])
+def test_forward_select_rejects(lib, r, kw, want):
+    a = dict(q=GOOD, k=GOOD, v=GOOD, o=GOOD, lse=GOOD, mask=None, alibi=None, d=64, dtype=BF16)
+    a.update(kw)
+    st = lib.fa_forward_select(r, a["q"], a["k"], a["v"], a["o"], a["lse"], 1, 2, 1, 256, 256, a["d"], 0.125, 1,
+                               -1, -1, a["alibi"], a["mask"], a["dtype"], 0.0, 0, None)
+    assert st == want
+
+
+def test_backward_launches(lib):
+    """Stages fa_backward runs: 0, 3 (one launch for dK/dV and dQ) for d <= 64
+    without dropout, slopes or mask; 0, 1, 2 otherwise."""
+    n = lambda *a: lib.fa_backward_launches(*a)  # noqa: E731
+    # B, H, Hkv, Nq, Nk, d, rate, alibi, mask, dtype
+    assert n(8, 12, 12, 1024, 1024, 64, 0.0, 0, 0, BF16) == 2
+    assert n(8, 12, 12, 1024, 1024, 64, 0.001, 0, 0, BF16) == 2   # rounds to no dropout
+    assert n(8, 12, 12, 1024, 1024, 64, 0.1, 0, 0, BF16) == 3
+    assert n(8, 12, 12, 1024, 1024, 64, 0.0, 1, 0, BF16) == 3
+    assert n(1, 8, 8, 65536, 65536, 64, 0.0, 0, 1, F16) == 3
+    assert n(1, 16, 16, 16384, 16384, 128, 0.0, 0, 0, BF16) == 3
+    assert n(1, 1, 1, 512, 512, 32, 0.0, 0, 0, F32) == EUNSUP
+    assert n(1, 2, 1, 256, 256, 64, 1.0, 0, 0, BF16) == EINVAL
+    assert n(1, 2, 1, 256, 256, 96, 0.0, 0, 0, BF16) == EINVAL
+

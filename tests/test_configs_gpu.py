@@ -5,10 +5,15 @@ configuration bench.py times, against the float64 oracle.
 * gpt2_small_bf16 (8x12x1024x64, causal): every output and gradient element.
 * long_seq_bf16 (1x16x16384x128, causal): the two seeded heads, every element of
   O, LSE, dQ, dK, dV of those heads; the rest only checked finite.
-* gqa_bf16 (4x32(8)x8192x128, causal, forward): 16 seeded rows of every (b, h),
-  the last row of each head among them.
+* gqa_bf16 (4x32(8)x8192x128, causal, forward): every element of O and LSE of
+  all 128 (b, h).
 * block_sparse_fp16 (1x8x65536x64, band + 5% mask): the seeded head, every
   element of O, LSE, dQ, dK, dV.
+
+Two modes are also checked at the size bench.py measures them:
+* dropout 0.1 on long_seq_bf16: the two seeded heads, every element;
+* the packed batch of long_seq_bf16's tokens (bench.py --packed): two whole
+  sequences (the longest and a short one), every head.
 """
 
 import numpy as np
@@ -94,20 +99,20 @@ def test_long_seq_bf16(gpu_lib):
 
 
 @pytest.mark.timeout(900)
-def test_gqa_bf16_sampled_rows(gpu_lib):
+def test_gqa_bf16(gpu_lib):
     w = I.WORKLOADS["gqa_bf16"]
     x, o, lse, _ = _run(w, gpu_lib)
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
-    rng = np.random.default_rng(w.seed + 300)
+    worst_o = worst_l = 0.0
     for b in range(w.B):
         for h in range(w.H):
-            rows = np.unique(np.concatenate([rng.choice(w.N, 15, replace=False), [w.N - 1]]))
             g = h // w.G
             oref, lref = oracle.forward(_head(x["q"], b, h), _head(x["k"], b, g), _head(x["v"], b, g),
-                                        w.scale, w.causal, rows=rows)
-            where = f"{w.name} b={b} h={h} rows={rows.tolist()}"
-            PT.check_out(PT.np64(o[b, h, rows]), oref[0, 0], w.dtype, where)
-            PT.check_lse(PT.np64(lse[b, h, rows]), lref[0, 0], where)
+                                        w.scale, w.causal, chunk=512)
+            where = f"{w.name} b={b} h={h}"
+            worst_o = max(worst_o, PT.check_out(PT.np64(o[b, h]), oref[0, 0], w.dtype, where))
+            worst_l = max(worst_l, PT.check_lse(PT.np64(lse[b, h]), lref[0, 0], where))
+    PT.say(f"{w.name}: all {w.B * w.H} (b, h), every row: max abs err O {worst_o:.3g}, LSE {worst_l:.3g}")
 
 
 @pytest.mark.timeout(900)
@@ -144,3 +149,60 @@ def test_batch_outer_grids_bf16(gpu_lib):
         rq, rk, rv = oracle.backward(qd, kd, vd, dod, scale, True, chunk=256)
         for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
             PT.check_grad(_head(got, b, h)[0, 0], ref[0, 0], f"{where} {name}")
+
+
+@pytest.mark.timeout(900)
+def test_long_seq_bf16_dropout(gpu_lib):
+    """Dropout 0.1 at the long-sequence workload (bench.py --dropout 0.1): the
+    two seeded heads, every element, against the oracle drawing the same
+    Philox keep decisions."""
+    w = I.WORKLOADS["long_seq_bf16"]
+    rate, seed = 0.1, 1234
+    x = I.make(w)
+    dev = torch.device("cuda", 0)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = gpu_lib.forward(q, k, v, w.scale, True, None, dropout_rate=rate, seed=seed)
+    dq, dk, dv = gpu_lib.backward(q, k, v, o, lse, do, w.scale, True, None, dropout_rate=rate, seed=seed)
+    torch.cuda.synchronize()
+    # the oracle takes the whole tensors so that its dropout stream for head
+    # (b, h) is keyed by b * H + h, as the kernels' is
+    qd, kd, vd, dod = (PT.np64(x[n]) for n in ("q", "k", "v", "do"))
+    for b, h in I.check_heads(w):
+        where = f"{w.name} dropout {rate} b={b} h={h}"
+        PT.say("checking", where)
+        oref, lref = oracle.forward(qd, kd, vd, w.scale, True, heads=[(b, h)], dropout_rate=rate, seed=seed)
+        PT.check_out(_head(o, b, h)[0, 0], oref[0], w.dtype, where)
+        PT.check_lse(_head(lse.unsqueeze(-1), b, h)[0, 0, :, 0], lref[0], where)
+        rq, rk, rv = oracle.backward(qd, kd, vd, dod, w.scale, True, heads=[(b, h)], dropout_rate=rate, seed=seed)
+        # G = 1: the head's dK and dV contributions are the whole gradients
+        for name, got, ref, hh in (("dq", dq, rq, h), ("dk", dk, rk, h // w.G), ("dv", dv, rv, h // w.G)):
+            PT.check_grad(_head(got, b, hh)[0, 0], ref[0], f"{where} {name}")
+
+
+@pytest.mark.timeout(900)
+def test_long_seq_bf16_packed(gpu_lib):
+    """The packed batch bench.py --packed times on the long-sequence
+    workload's tokens: every head of two whole sequences (the longest and the
+    shortest) against the oracle, forward and backward."""
+    w = I.WORKLOADS["long_seq_bf16"]
+    lens = I.packed_lengths(w.B * w.N, w.N / 8, w.seed + 300)
+    x = I.make_packed(lens, lens, w.H, w.Hkv, w.d, w.dtype, w.seed, with_grad=True)
+    dev = torch.device("cuda", 0)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    cu = torch.from_numpy(x["cu_q"]).to(dev)
+    mx = max(lens)
+    o, lse = gpu_lib.forward_varlen(q, k, v, cu, cu, mx, mx, w.scale, True)
+    dq, dk, dv = gpu_lib.backward_varlen(q, k, v, o, lse, do, cu, cu, mx, mx, w.scale, True)
+    torch.cuda.synchronize()
+    for s in (int(np.argmax(lens)), int(np.argmin(lens))):
+        a, n = int(x["cu_q"][s]), lens[s]
+        where = f"{w.name} packed: sequence {s} of {len(lens)} (rows {a}..{a + n - 1})"
+        PT.say("checking", where)
+        sl = slice(a, a + n)
+        qd, kd, vd, dod = (PT.np64(x[t][:, sl])[None] for t in ("q", "k", "v", "do"))
+        oref, lref = oracle.forward(qd, kd, vd, w.scale, True, chunk=256)
+        PT.check_out(PT.np64(o[:, sl]), oref[0], w.dtype, where)
+        PT.check_lse(PT.np64(lse[:, sl]), lref[0], where)
+        rq, rk, rv = oracle.backward(qd, kd, vd, dod, w.scale, True, chunk=256)
+        for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+            PT.check_grad(PT.np64(got[:, sl]), ref[0], f"{where} {name}")

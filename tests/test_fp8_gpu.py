@@ -70,3 +70,33 @@ def test_fp8_large_sampled():
     FP8: two heads' sampled rows against the oracle and the derived bound."""
     rows = np.sort(np.random.default_rng(91).choice(16384, size=48, replace=False))
     PT.run_fp8(1, 16, 16, 16384, 128, True, seed=90, heads=[(0, 3), (0, 12)], rows=rows)
+
+
+def test_fp8_summing_precision(gpu_lib):
+    """The measurement behind the FP8 bars' summing term (FP8_SUM in
+    tests/parity.py): 65536 rows that each see exactly one key (N = 1), so
+    that the kernel's LSE is that row's single score, scale * q . k, with unit
+    descales. Against the exact float64 dot product of the decoded codes, the
+    error left after the float32 steps that follow the matrix instruction (the
+    scale, log2 e and ln 2 products: at most 4 ulps of |LSE|) is the
+    instruction's summing error; relative to sum_d |q_d k_d| it must stay
+    within FP8_SUM, and the largest value found is printed."""
+    import oracle.fp8 as F8
+    B, H, d = 64, 1024, 128
+    x = I.make_fp8(B, H, H, 1, d, seed=77)
+    dev = torch.device("cuda", 0)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    _, lse = binding.forward_fp8(q, k, v, 1.0, 1.0, 1.0, scale=1.0, causal=False)
+    torch.cuda.synchronize()
+    got = PT.np64(lse).reshape(-1)
+    qd = F8.e4m3_decode(x["q"].numpy()).reshape(-1, d)
+    kd = F8.e4m3_decode(x["k"].numpy()).reshape(-1, d)
+    exact = (qd * kd).sum(axis=1)
+    mag = np.abs(qd * kd).sum(axis=1)
+    resid = np.maximum(np.abs(got - exact) - 4 * 2.0 ** -24 * np.abs(got), 0.0)
+    rel = resid / np.maximum(mag, 1e-30)
+    worst = float(rel.max())
+    PT.say(f"FP8 summing error: max {worst / 2.0 ** -24:.0f} * 2^-24 * sum|products| over {rel.size} dot products "
+           f"(bar FP8_SUM = 2^-11 = {PT.FP8_SUM / 2.0 ** -24:.0f} * 2^-24; ratio {worst / PT.FP8_SUM:.3f})")
+    assert np.all(np.isfinite(got))
+    assert worst <= PT.FP8_SUM

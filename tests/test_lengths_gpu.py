@@ -50,11 +50,11 @@ def test_cross_lengths(shape, causal, dtype):
 @pytest.mark.parametrize("rows", ["64", "32"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", CROSS_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_cross_lengths_forward_kernels(shape, causal, rows, monkeypatch):
-    """Both 16-bit forward kernels, forced through their override."""
-    monkeypatch.setenv("FA_FORWARD_ROWS_PER_WAVE", rows)
+def test_cross_lengths_forward_kernels(shape, causal, rows):
+    """Both 16-bit forward kernels, forced through fa_forward_select."""
     B, H, Hkv, Nq, Nk, d = shape
-    PT.run_cross(B, H, Hkv, Nq, Nk, d, "bf16", causal, seed=_seed(*shape, causal, 7), backward=False)
+    PT.run_cross(B, H, Hkv, Nq, Nk, d, "bf16", causal, seed=_seed(*shape, causal, 7), backward=False,
+                 rows_per_wave=int(rows))
 
 
 @pytest.mark.parametrize("causal", [False, True])

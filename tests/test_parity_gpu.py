@@ -41,12 +41,12 @@ def test_dense(shape, causal, dtype):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_dense_64_rows_per_wave(shape, causal, monkeypatch):
+def test_dense_64_rows_per_wave(shape, causal):
     """The 64-row forward kernel (chosen by the library for long sequences over
-    few heads) at every small shape, forced through its override."""
-    monkeypatch.setenv("FA_FORWARD_ROWS_PER_WAVE", "64")
+    few heads) at every small shape, forced through fa_forward_select."""
     B, H, Hkv, N, d = shape
-    PT.run_small(B, H, Hkv, N, d, "bf16", causal, seed=5000 + N + d + int(causal), backward=False)
+    PT.run_small(B, H, Hkv, N, d, "bf16", causal, seed=5000 + N + d + int(causal), backward=False,
+                 rows_per_wave=64)
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -80,7 +80,7 @@ def test_empty_rows(dtype):
 @pytest.mark.parametrize("rows", ["64", "32"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_late_dominant_scores(dtype, causal, rows, monkeypatch):
+def test_late_dominant_scores(dtype, causal, rows):
     """Keys far into the sequence whose scores exceed every earlier one by far
     more than the forward's fixed-reference range (keys 400..410: about 90 in
     log2 units above the first tile's maximum, forcing a restart with lazy
@@ -88,7 +88,6 @@ def test_late_dominant_scores(dtype, causal, rows, monkeypatch):
     keep their random part: with identical key rows the exact dQ of every row
     that attends to them would be zero (the dS of a row sums to zero), and any
     rounding of dS would make the relative error meaningless."""
-    monkeypatch.setenv("FA_FORWARD_ROWS_PER_WAVE", rows)
     N, d = 600, 64
     x = I.make_small(1, 2, 1, N, d, dtype, 21)
     x["q"] = x["q"] + 1.0
@@ -100,7 +99,8 @@ def test_late_dominant_scores(dtype, causal, rows, monkeypatch):
     q, k = (PT.np64(x[n]) for n in ("q", "k"))
     big = float(np.abs(q @ np.swapaxes(k, -1, -2)).max()) / np.sqrt(d)
     tol = PT.TOL_LSE + 4 * 2.0 ** -23 * big
-    PT.run_given(x, dtype, causal, where=f"late dominant scores {dtype} causal={causal} rows={rows}", lse_tol=tol)
+    PT.run_given(x, dtype, causal, where=f"late dominant scores {dtype} causal={causal}", lse_tol=tol,
+                 rows_per_wave=int(rows))
 
 
 DROP_SHAPES = [(1, 2, 1, 17, 32), (2, 2, 2, 64, 64), (1, 3, 1, 127, 128), (1, 4, 2, 300, 64),
@@ -111,14 +111,13 @@ DROP_SHAPES = [(1, 2, 1, 17, 32), (2, 2, 2, 64, 64), (1, 3, 1, 127, 128), (1, 4,
 @pytest.mark.parametrize("rate", [0.1, 0.5])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", DROP_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_dropout(shape, causal, rate, rows, monkeypatch):
+def test_dropout(shape, causal, rate, rows):
     """Dropout fused into every 16-bit kernel: O, LSE and gradients against the
     oracle drawing the same Philox keep decisions (both forward kernels)."""
-    monkeypatch.setenv("FA_FORWARD_ROWS_PER_WAVE", rows)
     B, H, Hkv, N, d = shape
     dtype = "bf16" if N % 2 else "fp16"
     PT.run_small(B, H, Hkv, N, d, dtype, causal, seed=7000 + N + d, dropout_rate=rate,
-                 drop_seed=(0x123456789 * (N + 1)) & (2**64 - 1))
+                 drop_seed=(0x123456789 * (N + 1)) & (2**64 - 1), rows_per_wave=int(rows))
 
 
 @pytest.mark.parametrize("causal", [False, True])

@@ -46,12 +46,11 @@ def test_window(shape, window, causal):
 
 @pytest.mark.parametrize("rows", ["64", "32"])
 @pytest.mark.parametrize("window", WINDOWS, ids=str)
-def test_window_forward_kernels(window, rows, monkeypatch):
-    """Both 16-bit forward kernels, forced through their override, over a
+def test_window_forward_kernels(window, rows):
+    """Both 16-bit forward kernels, forced through fa_forward_select, over a
     sequence long enough for full tiles inside the band."""
-    monkeypatch.setenv("FA_FORWARD_ROWS_PER_WAVE", rows)
     PT.run_window(1, 2, 1, 1100, 1300, 128, "fp16", False, window, seed=_seed(*window, int(rows)),
-                  backward=False)
+                  backward=False, rows_per_wave=int(rows))
 
 
 @pytest.mark.parametrize("window", [(64, 0), (17, 5), (0, 0), (300, -1)], ids=str)
