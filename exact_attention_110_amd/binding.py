@@ -47,6 +47,8 @@ def load():
     bw = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, P, I, P, S, P]
     lib.fa_backward.argtypes = bw
     lib.fa_backward.restype = I
+    lib.fa_backward_noalloc.argtypes = bw[:18] + [P]
+    lib.fa_backward_noalloc.restype = I
     lib.fa_backward_stage.argtypes = [I] + bw
     lib.fa_backward_stage.restype = I
     U64 = ctypes.c_ulonglong
@@ -263,6 +265,25 @@ def backward(q, k, v, o, lse, do, scale=None, causal=False, block_mask=None, ws=
         where = "fa_backward"
     if st != 0:
         raise FAError(st, where)
+    return dq, dk, dv
+
+
+def backward_noalloc(q, k, v, o, lse, do, scale=None, causal=False, block_mask=None, grads=None):
+    """dq, dk, dv as ``backward``, through fa_backward_noalloc: no workspace,
+    the library's per-GPU scratch array instead (calls overlapping on one GPU
+    race)."""
+    B, H, Hkv, N, d = _shape(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    for name, t in (("o", o), ("do", do)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must match q")
+    m = _mask(block_mask, N, q.device)
+    dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    st = load().fa_backward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), B, H, Hkv, N, d, scale, int(bool(causal)), _ptr(m), _DTYPES[q.dtype],
+                                    _stream(q.device))
+    if st != 0:
+        raise FAError(st, "fa_backward_noalloc")
     return dq, dk, dv
 
 

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/fa.h"
 #include "params.hpp"
 
@@ -238,6 +240,32 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   return FA_OK;
 }
 
+// Device scratch of the allocation-free backward entry point: the two
+// statistics planes of the backward workspace, in a file-scope device array
+// that every GPU the library runs on holds until the process ends. Host code
+// never passes `scratch` itself (on the host it only names the symbol): the
+// first call on a device looks up the array's device address with
+// hipGetSymbolAddress (with that device current) and keeps it per device.
+constexpr size_t kScratchBytes = (size_t)FA_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch[kMaxDevices] = {};
+
+// The scratch array's device address on the current device, or NULL.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -345,6 +373,25 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                 size_t workspace_bytes, void* stream) {
   return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, fixed_geo(B, H, Hkv, N, N, d), scale, causal,
                        -1, -1, nullptr, block_mask, dtype, 0.f, 0ull, workspace, workspace_bytes, stream);
+}
+
+int fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
+                        float scale, int causal, const uint8_t* block_mask, int dtype, void* stream) {
+  const Geo g = fixed_geo(B, H, Hkv, N, N, d);
+  // the full argument check first, with a stand-in workspace of the scratch
+  // array's size (aligned, never dereferenced): nothing touches the runtime
+  // before the arguments are known to be good
+  int st = check_backward(q, k, v, o, lse, dO, dq, dk, dv, g, scale, block_mask, dtype, (void*)kAlign,
+                          kScratchBytes);
+  if (st == FA_ERR_WORKSPACE) return FA_ERR_UNSUPPORTED;  // needs more than the scratch array holds
+  if (st != FA_OK) return st;
+  Band band;
+  if (!make_band(causal, -1, -1, &band)) return FA_ERR_INVALID_ARG;
+  void* ws = scratch_ptr();
+  if (!ws) return FA_ERR_HIP;
+  return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, g, scale, causal, -1, -1, nullptr, block_mask, dtype,
+                       0.f, 0ull, ws, kScratchBytes, stream);
 }
 
 int fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,

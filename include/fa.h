@@ -119,6 +119,27 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_backward_noalloc: fa_backward for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments, results and errors as fa_backward, minus
+ * the workspace: the per-row statistics go to a device array of
+ * FA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends. Arguments whose fa_backward_workspace_size exceeds
+ * it return FA_ERR_UNSUPPORTED (16 MiB: B * H * roundup(N, 128) up to 2^21
+ * query rows). The call allocates nothing; its first call on a device looks
+ * up the array's address there (with that device current). Every call on one
+ * GPU uses the same array: two calls that overlap on one GPU (on different
+ * streams, or from threads without ordering between them) race and give
+ * wrong results; calls in order on one stream are safe. The array needs no
+ * clearing: each call writes every statistic it reads.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dO, void* dq, void* dk, void* dv,
+                        int B, int H, int Hkv, int N, int d, float scale, int causal,
+                        const uint8_t* block_mask, int dtype, void* stream);
+
+/*
  * fa_backward_stage: one of the stages fa_backward runs, with the same
  * arguments and the same workspace:
  *   stage 0  D = rowsum(dO * O) and the base-2 LSE per query row, into the

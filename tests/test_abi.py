@@ -310,3 +310,25 @@ def test_backward_launches(lib):
     assert n(1, 2, 1, 256, 256, 64, 1.0, 0, 0, BF16) == EINVAL
     assert n(1, 2, 1, 256, 256, 96, 0.0, 0, 0, BF16) == EINVAL
 
+
+def test_backward_noalloc_rejects(lib):
+    """The allocation-free backward checks every argument before it touches
+    the runtime: bad arguments as fa_backward, and sizes whose statistics
+    exceed the scratch array (FA_NOALLOC_SCRATCH_BYTES) are unsupported."""
+    src = open(HEADER).read()
+    cap = eval(re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src).group(0)
+               .split(" ", 2)[2].replace("u", ""))
+    assert cap == 16 << 20
+
+    def call(B=1, H=2, Hkv=1, N=256, d=64, dtype=BF16, q=GOOD, lse=GOOD, mask=None, scale=0.125):
+        return lib.fa_backward_noalloc(q, GOOD, GOOD, GOOD, lse, GOOD, GOOD, GOOD, GOOD, B, H, Hkv, N, d, scale, 1,
+                                       mask, dtype, None)
+    assert call(q=None) == EINVAL
+    assert call(q=ODD) == EINVAL
+    assert call(d=96) == EINVAL
+    assert call(H=3, Hkv=2) == EINVAL
+    assert call(scale=float("nan")) == EINVAL
+    assert call(dtype=F32) == EUNSUP
+    # 8 bytes of statistics per (b, h, padded row): 2^21 rows fit, one block more does not
+    assert call(B=1, H=64, Hkv=1, N=65536, d=32) == EUNSUP
+    assert call(B=1, H=32, Hkv=1, N=65536 + 128, d=32) == EUNSUP
