@@ -43,7 +43,9 @@ namespace fa {
 
 // ---------------------------------------------------------------------------
 // stage 0: per query row, D = rowsum(dO * O) in fp32 and the log2-scaled LSE,
-// into the workspace's two planes (padding rows past the sequence up to npad included)
+// into the workspace's two planes (padding rows past the sequence up to npad
+// included). The plane holds -D: the key-block kernel starts its dP
+// accumulators at it, so that dP - D comes straight out of the MFMA.
 // ---------------------------------------------------------------------------
 template <class T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     const float lv = r < nq ? a.lse[sv.qrow0 + r] : -INFINITY;
     float* st = a.stats + (size_t)bh * 2 * a.npad;
     st[r] = lv != -INFINITY ? lv * kLog2e : INFINITY;
-    st[a.npad + r] = sum;
+    st[a.npad + r] = -sum;
   }
 }
 
@@ -110,23 +112,26 @@ __device__ __forceinline__ void bwd_kv_body(const BwdArgs& a, const int hk, cons
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
 
-  // LDS: Q, dO and row statistics in a ring of four buffers (step e uses e % 4:
+  // LDS: row statistics, Q and dO in a ring of four buffers (step e uses e % 4:
   // during step e's iteration, step e + 1's buffer feeds S and dP, step e's
   // statistics feed P and dS, step e - 1's buffer feeds dV and dK, and step
   // e + 2 is loaded into the buffer step e - 2 used) and the compacted mask
-  // list. The buffers are filled by LDS DMA, straight from memory.
+  // list. The buffers are filled by LDS DMA, straight from memory. The
+  // statistics come first, so that every read of them addresses its ring
+  // buffer with the instruction's immediate offset (offsets reach 64 KB).
   constexpr int NB = 4;  // the unrolled step loop below covers the ring once per pass
   __shared__ __attribute__((aligned(16))) char smem_raw[2 * NB * QBUF + NB * STB + (MASK ? 2 * MASK_LIST + 16 : 16)];
   lds_t* smem = (lds_t*)smem_raw;
-  lds_t* qbuf = smem;                   // [NB][BQ rows, swizzled]
+  lds_t* stat = smem;                   // [NB][2 BQ] float
+  lds_t* qbuf = stat + NB * STB;        // [NB][BQ rows, swizzled]
   lds_t* obuf = qbuf + NB * QBUF;       // dO, [NB][BQ rows, swizzled]
-  lds_t* stat = obuf + NB * QBUF;       // [NB][2 BQ] float
-  __attribute__((address_space(3))) short* blist = (__attribute__((address_space(3))) short*)(stat + NB * STB);
+  __attribute__((address_space(3))) short* blist = (__attribute__((address_space(3))) short*)(obuf + NB * QBUF);
   __attribute__((address_space(3))) int* bcount =
-      (__attribute__((address_space(3))) int*)(stat + NB * STB + (MASK ? 2 * MASK_LIST : 0));
+      (__attribute__((address_space(3))) int*)(obuf + NB * QBUF + (MASK ? 2 * MASK_LIST : 0));
 
   const AttnShape& s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index as a scalar
   const int l32 = lane & 31, hh = lane >> 5;
   const int g16 = lane >> 4;
   const int roff = 4 * (g16 >> 1) + ((lane & 15) >> 2);   // transposing-read row offset
@@ -216,22 +221,31 @@ __device__ __forceinline__ void bwd_kv_body(const BwdArgs& a, const int hk, cons
     const int q0 = qblock_at(p.qi) * BQ;
     const i32x4 rq = rsrc_words((const unsigned short*)a.q + p.qoff, qbytes);
     const i32x4 rg = rsrc_words((const unsigned short*)a.dO + p.qoff, qbytes);
-    dma_tile<D, BQ, KV_NW>(rq, q0, qbuf + buf * QBUF, w, lane);
-    dma_tile<D, BQ, KV_NW>(rg, q0, obuf + buf * QBUF, w, lane);
-    if (w == KV_NW - 1) {
+    dma_tile<D, BQ, KV_NW>(rq, q0, qbuf + buf * QBUF, wu, lane);
+    dma_tile<D, BQ, KV_NW>(rg, q0, obuf + buf * QBUF, wu, lane);
+    if (wu == KV_NW - 1) {
       const i32x4 rs = rsrc_words(a.stats + p.soff, (unsigned)a.npad * 8u);
-      dma4(rs, (unsigned)(((lane >> 5) * a.npad + q0 + (lane & 31)) * 4), stat + buf * STB);
+      dma4(rs, (unsigned)(((lane >> 5) * a.npad + q0 + (lane & 31)) * 4), lds_addr(stat + buf * STB));
     }
   };
 
-  // S = Q K^T and dP = dO V^T of this wave's 32 keys, from Q / dO buffer qbi
+  // S = Q K^T and dP = dO V^T of this wave's 32 keys, from Q / dO buffer qbi.
+  // Without dropout dP starts at -D (the statistics plane holds -D; element i
+  // is row 8 (i / 4) + 4 hh + i % 4), so the MFMAs leave dP - D behind.
   auto sdp = [&](int qbi, f32x16& sc, f32x16& dp) {
     const lds_t* qb = qbuf + qbi * QBUF;
     const lds_t* ob = obuf + qbi * QBUF;
+    const __attribute__((address_space(3))) float* ndl =
+        (const __attribute__((address_space(3))) float*)(stat + qbi * STB) + BQ;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sc[i] = 0.f;
-      dp[i] = 0.f;
+    for (int j4 = 0; j4 < 4; ++j4) {
+      f32x4 n4 = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (!DROP) n4 = *(const __attribute__((address_space(3))) f32x4*)(ndl + 8 * j4 + 4 * hh);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sc[4 * j4 + r] = 0.f;
+        dp[4 * j4 + r] = n4[r];
+      }
     }
 #pragma unroll
     for (int ss = 0; ss < NS; ++ss) {
@@ -243,7 +257,8 @@ __device__ __forceinline__ void bwd_kv_body(const BwdArgs& a, const int hk, cons
     }
   };
 
-  // P and dS (unscaled) of a step from its S, dP and statistics buffer. Element
+  // P and dS (unscaled) of a step from its S, dP - D (dP alone with dropout)
+  // and statistics buffer. Element
   // i is query q0 + 8 (i / 4) + 4 hh + i % 4 of key kj; under a band mask it is
   // kept only if kj - off - wr <= q0 + 4 hh + 8 (i / 4) + i % 4 <= kj - off + wl.
   // Keys past the sequence need no mask: their K and V rows read as zeros and
@@ -257,7 +272,7 @@ __device__ __forceinline__ void bwd_kv_body(const BwdArgs& a, const int hk, cons
     constexpr bool MASKED = decltype(masked)::value;
     const __attribute__((address_space(3))) float* lsel =
         (const __attribute__((address_space(3))) float*)(stat + stb * STB);
-    const __attribute__((address_space(3))) float* ddl = lsel + BQ;
+    const __attribute__((address_space(3))) float* ndl = lsel + BQ;  // -D
     const int thr = kj - offu - q0 - 4 * hh;   // first kept 8 (i / 4) + i % 4
     const int thr2 = kj - offl - q0 - 4 * hh;  // last kept (with a lower edge)
     // dropout: byte r of dwc[j4] decides query q0 + 8 j4 + 4 hh + r of key kj
@@ -268,7 +283,8 @@ __device__ __forceinline__ void bwd_kv_body(const BwdArgs& a, const int hk, cons
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       const f32x4 L4 = *(const __attribute__((address_space(3))) f32x4*)(lsel + 8 * j4 + 4 * hh);
-      const f32x4 D4 = *(const __attribute__((address_space(3))) f32x4*)(ddl + 8 * j4 + 4 * hh);
+      f32x4 nd4 = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (DROP) nd4 = *(const __attribute__((address_space(3))) f32x4*)(ndl + 8 * j4 + 4 * hh);
       float p[4], d2[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -279,10 +295,10 @@ __device__ __forceinline__ void bwd_kv_body(const BwdArgs& a, const int hk, cons
         if constexpr (DROP) {
           const bool z = drop_keep(dwc[j4], r, s.drop_t);
           p[r] = z ? pv * s.drop_scale : 0.f;
-          d2[r] = pv * ((z ? dp[i] * s.drop_scale : 0.f) - D4[r]);
+          d2[r] = pv * ((z ? dp[i] * s.drop_scale : 0.f) + nd4[r]);
         } else {
           p[r] = pv;
-          d2[r] = pv * (dp[i] - D4[r]);
+          d2[r] = pv * dp[i];
         }
       }
       pk[2 * j4] = pack2<T>(p[0], p[1]);
@@ -494,6 +510,7 @@ __device__ __forceinline__ void bwd_q_body(const BwdArgs& a, const int h, const 
 
   const AttnShape& s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index as a scalar
   const int l32 = lane & 31, hh = lane >> 5;
   const int g16 = lane >> 4;
   const int roff = 4 * (g16 >> 1) + ((lane & 15) >> 2);
@@ -529,7 +546,7 @@ __device__ __forceinline__ void bwd_q_body(const BwdArgs& a, const int h, const 
   // sequence, or one that saw no key, has LSE +inf and so P = 0
   const float* st = a.stats + ((size_t)b * s.H + h) * 2 * a.npad;
   const float lse2 = st[qi];
-  const float dd = st[a.npad + qi];
+  const float ndd = st[a.npad + qi];  // -D
 
   // keys [kbeg, kend) are seen by some row of the block (band as in the forward pass)
   constexpr bool LOWER = BAND == 2;
@@ -571,8 +588,8 @@ __device__ __forceinline__ void bwd_q_body(const BwdArgs& a, const int h, const 
   // K and V tiles by LDS DMA into the buffer the previous step read (the
   // barrier that ended it has passed); rows past the sequence arrive as zeros
   auto dma_kv = [&](int t, int buf) {
-    dma_tile<D, Q_BN, Q_NW>(rk, t * Q_BN, kbuf + buf * KBUF, w, lane);
-    dma_tile<D, Q_BN, Q_NW>(rv, t * Q_BN, vbuf + buf * VBUF, w, lane);
+    dma_tile<D, Q_BN, Q_NW>(rk, t * Q_BN, kbuf + buf * KBUF, wu, lane);
+    dma_tile<D, Q_BN, Q_NW>(rv, t * Q_BN, vbuf + buf * VBUF, wu, lane);
   };
 
   dma_kv(ntiles > 0 ? tile_at(0) : 0, 0);
@@ -646,9 +663,9 @@ __device__ __forceinline__ void bwd_q_body(const BwdArgs& a, const int h, const 
                 pv = (kidx > thr || (LOWER && kidx < thr2)) ? 0.f : pv;
               }
               if constexpr (DROP)
-                v2[r] = pv * ((drop_keep(wd, i & 3, s.drop_t) ? dp[t2][i] * s.drop_scale : 0.f) - dd);
+                v2[r] = pv * ((drop_keep(wd, i & 3, s.drop_t) ? dp[t2][i] * s.drop_scale : 0.f) + ndd);
               else
-                v2[r] = pv * (dp[t2][i] - dd);
+                v2[r] = pv * (dp[t2][i] + ndd);
             }
             sk[t2][j] = pack2<T>(v2[0], v2[1]);
           }

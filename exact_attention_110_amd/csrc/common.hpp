@@ -275,53 +275,58 @@ __device__ __forceinline__ int swz_off(int r, int c) {
 // Issued from assembly the loads are invisible to its wait counting; the
 // caller waits for them explicitly (dma_wait) before the barrier that
 // publishes the buffer. M0 (the LDS address) is saved and restored around
-// each load; s_nop 4 covers both the M0 write and a descriptor or offset just
-// written by a VALU instruction.
+// each load. The LDS address is a wave-uniform value computed by scalar
+// instructions (the callers pass the wave index as a scalar), so M0 is
+// written from an SGPR that no vector instruction produced, and the
+// descriptor likewise comes from scalar arithmetic; one wait state separates
+// the M0 write from the load.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4 rsrc_words(const void* base, unsigned int bytes) {
   const unsigned long long p = (unsigned long long)base;
   return (i32x4){(int)(unsigned)p, (int)((p >> 32) & 0xffffu), (int)bytes, kRsrcWord3};
 }
-__device__ __forceinline__ void dma16(i32x4 r, unsigned int voff, lds_t* dst) {
-  const int m0 = __builtin_amdgcn_readfirstlane((int)(size_t)dst);
+// 16 bytes per lane at a per-lane byte offset into LDS address m0 + 16 lane
+__device__ __forceinline__ void dma16(i32x4 r, unsigned int voff, int m0) {
   int saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 4\n\t"
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
       "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
       : "=&s"(saved)
       : "s"(m0), "v"(voff), "s"(r)
       : "memory");
 }
-// 4 bytes per lane at a per-lane byte offset into dst + 4 lane.
-__device__ __forceinline__ void dma4(i32x4 r, unsigned int voff, lds_t* dst) {
-  const int m0 = __builtin_amdgcn_readfirstlane((int)(size_t)dst);
+// 4 bytes per lane at a per-lane byte offset into LDS address m0 + 4 lane
+__device__ __forceinline__ void dma4(i32x4 r, unsigned int voff, int m0) {
   int saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 4\n\t"
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
       "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
       : "=&s"(saved)
       : "s"(m0), "v"(voff), "s"(r)
       : "memory");
 }
+// LDS byte address of an LDS pointer, for M0
+__device__ __forceinline__ int lds_addr(const lds_t* p) { return (int)(size_t)p; }
 // wait until every DMA load of this wave has landed in LDS
 __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Copy rows [row0, row0 + ROWS) of a [*, D] 16-bit tensor (buffer words r,
 // row-major) into the swizzled LDS tile at dst. NW waves share the 1 KB
-// segments; wave w takes segments w, w + NW, ...
+// segments; wave ws (wave-uniform, from readfirstlane) takes segments
+// ws, ws + NW, ...
 template <int D, int ROWS, int NW>
-__device__ __forceinline__ void dma_tile(i32x4 r, int row0, lds_t* dst, int w, int lane) {
+__device__ __forceinline__ void dma_tile(i32x4 r, int row0, lds_t* dst, int ws, int lane) {
   constexpr int SEG = ROWS * 2 * D / 1024;
   constexpr int RPS = 1024 / (2 * D);  // rows per segment
   constexpr int CPR = D / 8;
   static_assert(SEG >= 1 && (ROWS * 2 * D) % 1024 == 0, "tile must be whole 1 KB segments");
 #pragma unroll
   for (int sg = 0; sg < (SEG + NW - 1) / NW; ++sg) {
-    const int seg = w + sg * NW;
+    const int seg = ws + sg * NW;
     if (SEG % NW == 0 || seg < SEG) {
       const int row = seg * RPS + lane / CPR;
       const int c = (lane % CPR) ^ swz<D>(row);
-      dma16(r, (unsigned)((row0 + row) * 2 * D + 16 * c), dst + seg * 1024);
+      dma16(r, (unsigned)((row0 + row) * 2 * D + 16 * c), lds_addr(dst) + seg * 1024);
     }
   }
 }

@@ -70,7 +70,7 @@ struct BwdArgs {
   void* dv;
   // workspace, [B][H][2][npad] float: plane 0 the log2-scaled LSE (+inf for a
   // row that saw no key and for the padding rows past the sequence), plane 1
-  // D = rowsum(dO * O) (0 for padding rows); npad = Nq rounded up to 128
+  // -D = -rowsum(dO * O) (0 for padding rows); npad = Nq rounded up to 128
   float* stats;
   int npad;
 };
