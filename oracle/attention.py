@@ -31,6 +31,13 @@ Sources (cited by page title and section):
   is visible iff p - left <= j <= p + right, -1 meaning unbounded on that
   side; causal masking is the right bound 0. Band, causal and block masks
   combine by intersection.
+* Element masks: the same lesson section describes one tiled kernel serving
+  user mask functions (mask_mod) evaluated per (query, key) pair. Read here
+  as an arbitrary boolean predicate, given to the oracle written out as a
+  dense [Nq, Nk] matrix (True = visible), shared by every batch and head and
+  intersected with every other mask (``elem_mask``). Examples: a document
+  mask (query and key in the same document), a prefix-LM mask, a random
+  mask.
 * Score modification: the same lesson section speaks of user functions that
   modify scores (score_mod) inside the one tiled kernel, naming none. Read
   here as the linear distance bias of ALiBi (Press, Smith and Lewis, 2022),
@@ -60,13 +67,13 @@ from . import dropout as _dropout
 MASK_BLOCK = 128  # block-mask granularity in rows and columns
 
 
-def visible(rows, keys, causal, block_mask, block=MASK_BLOCK, offset=0, window=(-1, -1)):
+def visible(rows, keys, causal, block_mask, block=MASK_BLOCK, offset=0, window=(-1, -1), elem_mask=None):
     """Boolean matrix a[r, c]: is key ``keys[c]`` visible to query ``rows[r]``.
 
     Causal: j <= i + offset (offset = Nk - Nq, 0 for square attention). Window
     (left, right): i + offset - left <= j <= i + offset + right, a negative
-    bound unbounded. Block mask: mask[i // block][j // block] != 0. All that
-    are given must hold.
+    bound unbounded. Block mask: mask[i // block][j // block] != 0. Element
+    mask: elem_mask[i][j] true. All that are given must hold.
     """
     rows = np.asarray(rows, dtype=np.int64)
     keys = np.asarray(keys, dtype=np.int64)
@@ -81,10 +88,12 @@ def visible(rows, keys, causal, block_mask, block=MASK_BLOCK, offset=0, window=(
     if block_mask is not None:
         bm = np.asarray(block_mask) != 0
         a &= bm[(rows // block)[:, None], (keys // block)[None, :]]
+    if elem_mask is not None:
+        a &= np.asarray(elem_mask, dtype=bool)[rows[:, None], keys[None, :]]
     return a
 
 
-def candidate_keys(rows, n_keys, causal, block_mask, block=MASK_BLOCK, offset=0, window=(-1, -1)):
+def candidate_keys(rows, n_keys, causal, block_mask, block=MASK_BLOCK, offset=0, window=(-1, -1), elem_mask=None):
     """Keys that at least one of ``rows`` may see (a superset used to gather K, V).
 
     Keys outside this set are invisible to every row of the chunk, so leaving
@@ -104,6 +113,8 @@ def candidate_keys(rows, n_keys, causal, block_mask, block=MASK_BLOCK, offset=0,
         bm = np.asarray(block_mask) != 0
         any_row = bm[np.unique(rows // block)].any(axis=0)
         keys = keys[any_row[keys // block]]
+    if elem_mask is not None:
+        keys = keys[np.asarray(elem_mask, dtype=bool)[rows].any(axis=0)[keys]]
     return keys
 
 
@@ -145,7 +156,8 @@ def alibi_bias(rows, keys, slope, offset):
     return -float(slope) * np.abs((rows[:, None] + offset) - keys[None, :]).astype(np.float64)
 
 
-def head_probabilities(q, k, scale, causal=False, block_mask=None, rows=None, window=(-1, -1), alibi=None):
+def head_probabilities(q, k, scale, causal=False, block_mask=None, rows=None, window=(-1, -1), alibi=None,
+                       elem_mask=None):
     """Full probability rows P[rows, :] (Nk keys wide) of one query head.
 
     q: [Nq, d] float64 query rows of the head, k: [Nk, d] keys of its kv head;
@@ -155,7 +167,7 @@ def head_probabilities(q, k, scale, causal=False, block_mask=None, rows=None, wi
     off = n - q.shape[0]
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
     keys = np.arange(n)
-    vis = visible(rows, keys, causal, block_mask, offset=off, window=window)
+    vis = visible(rows, keys, causal, block_mask, offset=off, window=window, elem_mask=elem_mask)
     _, p, lse = _row_softmax(q[rows], k, scale, vis, alibi_bias(rows, keys, alibi, off))
     return p, lse
 
@@ -172,7 +184,7 @@ def _drop(p, rows, keys, dropout):
 
 
 def head_forward(q, k, v, scale, causal=False, block_mask=None, rows=None, chunk=256, dropout=None,
-                 window=(-1, -1), alibi=None):
+                 window=(-1, -1), alibi=None, elem_mask=None):
     """O and L for the given query rows of one head (q: [Nq, d], k, v: [Nk, d]).
 
     With dropout = (rate, seed, bh) the probabilities are dropped and rescaled
@@ -184,9 +196,9 @@ def head_forward(q, k, v, scale, causal=False, block_mask=None, rows=None, chunk
     lse = np.full(rows.size, -np.inf)
     pos = 0
     for ch in _chunks(rows, chunk):
-        keys = candidate_keys(ch, n, causal, block_mask, offset=off, window=window)
+        keys = candidate_keys(ch, n, causal, block_mask, offset=off, window=window, elem_mask=elem_mask)
         if keys.size:
-            vis = visible(ch, keys, causal, block_mask, offset=off, window=window)
+            vis = visible(ch, keys, causal, block_mask, offset=off, window=window, elem_mask=elem_mask)
             _, p, l_ = _row_softmax(q[ch], k[keys], scale, vis, alibi_bias(ch, keys, alibi, off))
             o[pos:pos + ch.size] = _drop(p, ch, keys, dropout) @ v[keys]
             lse[pos:pos + ch.size] = l_
@@ -195,7 +207,7 @@ def head_forward(q, k, v, scale, causal=False, block_mask=None, rows=None, chunk
 
 
 def head_backward(q, k, v, do, scale, causal=False, block_mask=None, chunk=256, dropout=None, window=(-1, -1),
-                  alibi=None):
+                  alibi=None, elem_mask=None):
     """Gradients of sum(O * dO) for one query head.
 
     With p the probability rows, g = dO, and (under dropout) r the dropped and
@@ -217,10 +229,10 @@ def head_backward(q, k, v, do, scale, causal=False, block_mask=None, chunk=256, 
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     for ch in _chunks(rows, chunk):
-        keys = candidate_keys(ch, n, causal, block_mask, offset=off, window=window)
+        keys = candidate_keys(ch, n, causal, block_mask, offset=off, window=window, elem_mask=elem_mask)
         if keys.size == 0:
             continue
-        vis = visible(ch, keys, causal, block_mask, offset=off, window=window)
+        vis = visible(ch, keys, causal, block_mask, offset=off, window=window, elem_mask=elem_mask)
         _, p, _ = _row_softmax(q[ch], k[keys], scale, vis, alibi_bias(ch, keys, alibi, off))
         g = do[ch]
         dv[keys] += _drop(p, ch, keys, dropout).T @ g
@@ -239,7 +251,7 @@ def _heads(B, H, heads):
 
 
 def forward(q, k, v, scale, causal=False, block_mask=None, heads=None, rows=None, chunk=256,
-            dropout_rate=0.0, seed=0, window=(-1, -1), alibi_slopes=None):
+            dropout_rate=0.0, seed=0, window=(-1, -1), alibi_slopes=None, elem_mask=None):
     """Attention forward over [B, H, Nq, d] queries and [B, Hkv, Nk, d] keys/values.
 
     Query head h reads kv head h // (H // Hkv). A block mask has
@@ -248,6 +260,8 @@ def forward(q, k, v, scale, causal=False, block_mask=None, heads=None, rows=None
     stacked in the order of ``heads`` (a list of (b, h)): o [nh, R, d], lse [nh, R].
     A positive ``dropout_rate`` applies dropout with the generator keyed by
     ``seed`` (``oracle.dropout``); query head (b, h) draws stream b * H + h.
+    ``elem_mask``: None or a boolean [Nq, Nk] visibility matrix shared by
+    every batch and head.
     """
     B, H, _, d = q.shape
     Hkv = k.shape[1]
@@ -259,7 +273,7 @@ def forward(q, k, v, scale, causal=False, block_mask=None, heads=None, rows=None
     for b, h in hl:
         dr = (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None
         o, l_ = head_forward(q[b, h], k[b, h // G], v[b, h // G], scale, causal, block_mask, rows, chunk, dr,
-                             window, None if alibi_slopes is None else alibi_slopes[h])
+                             window, None if alibi_slopes is None else alibi_slopes[h], elem_mask)
         outs.append(o)
         lses.append(l_)
     o = np.stack(outs)
@@ -271,7 +285,7 @@ def forward(q, k, v, scale, causal=False, block_mask=None, heads=None, rows=None
 
 
 def backward(q, k, v, do, scale, causal=False, block_mask=None, heads=None, chunk=256,
-             dropout_rate=0.0, seed=0, window=(-1, -1), alibi_slopes=None):
+             dropout_rate=0.0, seed=0, window=(-1, -1), alibi_slopes=None, elem_mask=None):
     """Gradients of sum(O * dO) with respect to q, k, v (dropout as in ``forward``).
 
     With ``heads=None`` returns full dq [B, H, Nq, d], dk, dv [B, Hkv, Nk, d]
@@ -293,14 +307,14 @@ def backward(q, k, v, do, scale, causal=False, block_mask=None, heads=None, chun
                 dr = (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None
                 a, bk, bv = head_backward(q[b, h], k[b, h // G], v[b, h // G], do[b, h],
                                           scale, causal, block_mask, chunk, dr, window,
-                                          None if alibi_slopes is None else alibi_slopes[h])
+                                          None if alibi_slopes is None else alibi_slopes[h], elem_mask)
                 dq[b, h] = a
                 dk[b, h // G] += bk
                 dv[b, h // G] += bv
         return dq, dk, dv
     res = [head_backward(q[b, h], k[b, h // G], v[b, h // G], do[b, h], scale, causal, block_mask, chunk,
                          (dropout_rate, seed, b * H + h) if dropout_rate > 0 else None, window,
-                         None if alibi_slopes is None else alibi_slopes[h])
+                         None if alibi_slopes is None else alibi_slopes[h], elem_mask)
            for b, h in _heads(B, H, heads)]
     return tuple(np.stack(x) for x in zip(*res))
 

@@ -972,6 +972,166 @@ def pin_alibi_finite_differences():
                 assert abs(num - grads[which][idx]) <= 1e-6 * max(1.0, abs(num)), ("qkv"[which], causal)
 
 
+
+# ----------------------------------------------------------------------------------------------
+# P-17: element masks (an arbitrary boolean predicate per (query, key) pair, shared by every
+# batch and head; the "FlashAttention" lesson, Researcher tier, "Beyond hand-written kernels")
+# ----------------------------------------------------------------------------------------------
+def _masked_brute_force(q, k, v, scale, causal, allow):
+    """Scalar loops over an explicit visibility matrix allow[i][j] (and causal
+    j <= i + len(k) - len(q))."""
+    n, d, dv = len(q), len(q[0]), len(v[0])
+    outs, lses = [], []
+    for i in range(n):
+        pos = i + len(k) - n
+        keys = [j for j in range(len(k)) if allow[i][j] and (not causal or j <= pos)]
+        if not keys:
+            outs.append([0.0] * dv)
+            lses.append(-math.inf)
+            continue
+        sc = [scale * sum(q[i][t] * k[j][t] for t in range(d)) for j in keys]
+        mx = max(sc)
+        w = [math.exp(x - mx) for x in sc]
+        z = sum(w)
+        outs.append([sum(w[a] * v[j][t] for a, j in enumerate(keys)) / z for t in range(dv)])
+        lses.append(mx + math.log(z))
+    return np.array(outs), np.array(lses)
+
+
+def pin_elem_mask_brute_force():
+    rng = np.random.default_rng(1701)
+    seed = 1700
+    for nq, nk in ((1, 1), (3, 3), (4, 6), (6, 4), (5, 5)):
+        for causal in (False, True):
+            for density in (0.3, 0.7):
+                seed += 1
+                allow = rng.random((nq, nk)) < density
+                allow[0] = False                      # a row that sees nothing
+                q, k, v = _rand((nq, 3), seed), _rand((nk, 3), seed + 50), _rand((nk, 2), seed + 90)
+                o, l_ = A.forward(q[None, None], k[None, None], v[None, None], 0.8, causal, elem_mask=allow)
+                ob, lb = _masked_brute_force(q.tolist(), k.tolist(), v.tolist(), 0.8, causal, allow.tolist())
+                where = (nq, nk, causal, density)
+                assert np.abs(o[0, 0] - ob).max() <= 1e-12, where
+                fin = np.isfinite(lb)
+                assert np.array_equal(np.isfinite(l_[0, 0]), fin), where
+                assert np.abs(l_[0, 0][fin] - lb[fin]).max(initial=0.0) <= 1e-12, where
+
+
+def pin_elem_mask_torch_sdpa():
+    """Against PyTorch's float64 CPU attention with the boolean mask as its
+    attn_mask, gradients through autograd (grouped-query and causal cases)."""
+    import torch
+    import torch.nn.functional as F
+    for (B, H, Hkv, nq, nk, d, causal, seed) in [(1, 2, 2, 150, 150, 8, False, 1711),
+                                                 (2, 4, 2, 90, 200, 8, True, 1712),
+                                                 (1, 3, 1, 260, 260, 4, True, 1713)]:
+        rng = np.random.default_rng(seed)
+        allow = rng.random((nq, nk)) < 0.4
+        allow[:, 0] = True                             # every row sees a key (torch gives NaN otherwise)
+        q, k, v = _rand((B, H, nq, d), seed), _rand((B, Hkv, nk, d), seed + 1), _rand((B, Hkv, nk, d), seed + 2)
+        g = _rand((B, H, nq, d), seed + 3)
+        full = allow.copy()
+        if causal:
+            full &= np.arange(nk)[None, :] <= np.arange(nq)[:, None] + (nk - nq)
+        G = H // Hkv
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        to = F.scaled_dot_product_attention(tq, tk.repeat_interleave(G, dim=1), tv.repeat_interleave(G, dim=1),
+                                            attn_mask=torch.tensor(full), scale=0.3)
+        to.backward(torch.tensor(g))
+        o, l_ = A.forward(q, k, v, 0.3, causal, elem_mask=allow)
+        dq, dk, dv = A.backward(q, k, v, g, 0.3, causal, elem_mask=allow)
+        assert np.abs(o - to.detach().numpy()).max() <= 1e-12
+        s = torch.tensor(q) @ torch.tensor(np.repeat(k, G, axis=1)).transpose(-1, -2) * 0.3
+        s = s.masked_fill(~torch.tensor(full), float("-inf"))
+        assert np.abs(l_ - torch.logsumexp(s, dim=-1).numpy()).max() <= 1e-12
+        for a, b in ((dq, tq), (dk, tk), (dv, tv)):
+            assert np.abs(a - b.grad.numpy()).max() <= 1e-12
+
+
+def pin_elem_mask_equivalences():
+    """Masks that other arguments already express give identical results: all
+    true = no mask; lower triangle = causal; constant on 128 x 128 blocks = the
+    block mask; a band = the window; a document mask (same document) = the
+    packed batch of those documents."""
+    n, d = 300, 4
+    q, k, v, g = (_rand((1, 2, n, d), s) for s in (1721, 1722, 1723, 1724))
+    ii, jj = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+
+    def same(kw_a, kw_b):
+        o1, l1 = A.forward(q, k, v, 0.5, **kw_a)
+        o2, l2 = A.forward(q, k, v, 0.5, **kw_b)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2), (kw_a.keys(), kw_b.keys())
+        g1 = A.backward(q, k, v, g, 0.5, **kw_a)
+        g2 = A.backward(q, k, v, g, 0.5, **kw_b)
+        for a, b in zip(g1, g2):
+            assert np.array_equal(a, b)
+
+    same(dict(causal=False), dict(causal=False, elem_mask=np.ones((n, n), dtype=bool)))
+    same(dict(causal=True), dict(causal=False, elem_mask=jj <= ii))
+    bm = np.array([[1, 0, 1], [1, 1, 0], [0, 1, 1]], dtype=np.uint8)
+    same(dict(causal=False, block_mask=bm), dict(causal=False, elem_mask=bm[ii // 128, jj // 128] != 0))
+    same(dict(causal=True, window=(37, 0)), dict(causal=False, elem_mask=(jj <= ii) & (jj >= ii - 37)))
+    # a document mask equals the packed batch of the documents (forward and backward)
+    lens = [70, 1, 129, 100]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    doc = np.repeat(np.arange(len(lens)), lens)
+    allow = doc[:, None] == doc[None, :]
+    for causal in (False, True):
+        o1, l1 = A.forward(q, k, v, 0.5, causal, elem_mask=allow)
+        o2, l2 = A.forward_varlen(q[0], k[0], v[0], cu, cu, 0.5, causal)
+        assert np.abs(o1[0] - o2).max() <= 1e-14 and np.abs(l1[0] - l2).max() <= 1e-13
+        d1 = A.backward(q, k, v, g, 0.5, causal, elem_mask=allow)
+        d2 = A.backward_varlen(q[0], k[0], v[0], g[0], cu, cu, 0.5, causal)
+        for a, b in zip(d1, d2):
+            assert np.abs(a[0] - b).max() <= 1e-13
+
+
+def pin_elem_mask_empty_rows():
+    """Rows that see no key under the element mask: O = 0, L = -inf, zero dQ,
+    and their upstream gradient reaches no dK or dV."""
+    n, d = 200, 4
+    q, k, v, g = (_rand((1, 1, n, d), s) for s in (1731, 1732, 1733, 1734))
+    allow = np.random.default_rng(1735).random((n, n)) < 0.5
+    empty = np.array([0, 5, 130, 199])
+    allow[empty] = False
+    o, l_ = A.forward(q, k, v, 0.5, False, elem_mask=allow)
+    assert np.all(o[0, 0, empty] == 0) and np.all(np.isneginf(l_[0, 0, empty]))
+    dq, dk, dv = A.backward(q, k, v, g, 0.5, False, elem_mask=allow)
+    assert np.all(dq[0, 0, empty] == 0)
+    g2 = g.copy()
+    g2[0, 0, empty] = 1e3
+    _, dk2, dv2 = A.backward(q, k, v, g2, 0.5, False, elem_mask=allow)
+    assert np.array_equal(dk, dk2) and np.array_equal(dv, dv2)
+
+
+def pin_elem_mask_finite_differences():
+    n, d, scale = 14, 3, 0.6
+    rng = np.random.default_rng(1741)
+    allow = rng.random((n, n)) < 0.5
+    allow[:, 3] = True
+    q, k, v, g = (_rand((1, 2, n, d), s) for s in (1742, 1743, 1744, 1745))
+    k, v = k[:, :1], v[:, :1]                        # grouped-query: two query heads, one kv head
+    grads = A.backward(q, k, v, g, scale, True, elem_mask=allow)
+
+    def f(q_, k_, v_):
+        o, _ = A.forward(q_, k_, v_, scale, True, elem_mask=allow)
+        return float((o * g).sum())
+
+    h = 1e-6
+    for which, x in enumerate((q, k, v)):
+        num, ana = [], []
+        for flat in rng.choice(x.size, size=min(20, x.size), replace=False):
+            idx = np.unravel_index(flat, x.shape)
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            a_p, a_m = [q, k, v], [q, k, v]
+            a_p[which], a_m[which] = xp, xm
+            num.append((f(*a_p) - f(*a_m)) / (2 * h))
+            ana.append(grads[which][idx])
+        num, ana = np.array(num), np.array(ana)
+        assert np.abs(num - ana).max() / max(np.abs(ana).max(), 1e-3) <= 1e-6, "qkv"[which]
+
 ALL_PINS = [pin_worked_example, pin_recurrence, pin_brute_force, pin_rows_sum_to_one, pin_zero_query,
             pin_dominant_score, pin_permutation, pin_causal_locality, pin_finite_differences,
             pin_gqa_repeat, pin_mask_semantics, pin_empty_rows, pin_scale_zero, pin_torch_sdpa,
@@ -980,4 +1140,6 @@ ALL_PINS = [pin_worked_example, pin_recurrence, pin_brute_force, pin_rows_sum_to
             pin_cross_lengths_finite_differences, pin_varlen_brute_force, pin_varlen_finite_differences,
             pin_varlen_dropout_streams, pin_window_brute_force, pin_window_torch_sdpa, pin_window_limits,
             pin_window_finite_differences, pin_e4m3_decode, pin_fp8_descales, pin_alibi_brute_force,
-            pin_alibi_torch_sdpa, pin_alibi_limits, pin_alibi_finite_differences]
+            pin_alibi_torch_sdpa, pin_alibi_limits, pin_alibi_finite_differences, pin_elem_mask_brute_force,
+            pin_elem_mask_torch_sdpa, pin_elem_mask_equivalences, pin_elem_mask_empty_rows,
+            pin_elem_mask_finite_differences]

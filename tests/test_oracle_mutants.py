@@ -37,10 +37,10 @@ MUTANTS = {
     "candidate_keys_short": ("keys = keys[keys <= rows.max() + offset]", "keys = keys[keys < rows.max() + offset]"),
     "candidate_keys_no_offset": ("keys = keys[keys <= rows.max() + offset]", "keys = keys[keys <= rows.max()]"),
     "offset_sign": ("off = n - q.shape[0]", "off = q.shape[0] - n"),
-    "offset_top_left_forward": ("        if keys.size:\n            vis = visible(ch, keys, causal, block_mask, offset=off, window=window)",
-                                "        if keys.size:\n            vis = visible(ch, keys, causal, block_mask, window=window)"),
-    "offset_top_left_backward": ("        vis = visible(ch, keys, causal, block_mask, offset=off, window=window)\n        _, p, _ =",
-                                 "        vis = visible(ch, keys, causal, block_mask, window=window)\n        _, p, _ ="),
+    "offset_top_left_forward": ("        if keys.size:\n            vis = visible(ch, keys, causal, block_mask, offset=off, window=window, elem_mask=elem_mask)",
+                                "        if keys.size:\n            vis = visible(ch, keys, causal, block_mask, window=window, elem_mask=elem_mask)"),
+    "offset_top_left_backward": ("        vis = visible(ch, keys, causal, block_mask, offset=off, window=window, elem_mask=elem_mask)\n        _, p, _ =",
+                                 "        vis = visible(ch, keys, causal, block_mask, window=window, elem_mask=elem_mask)\n        _, p, _ ="),
     "varlen_keys_from_query_spans": ("head_forward(q[h, q0:q1], k[h // G, k0:k1], v[h // G, k0:k1]",
                                      "head_forward(q[h, q0:q1], k[h // G, q0:q1], v[h // G, q0:q1]"),
     "window_left_strict": ("a &= keys[None, :] >= rows[:, None] + offset - left",
@@ -51,8 +51,16 @@ MUTANTS = {
                                     "a &= keys[None, :] <= rows[:, None] + right"),
     "window_candidates_short": ("keys = keys[keys >= rows.min() + offset - window[0]]",
                                 "keys = keys[keys > rows.min() + offset - window[0]]"),
-    "window_dropped_in_backward": ("        vis = visible(ch, keys, causal, block_mask, offset=off, window=window)\n        _, p, _ =",
-                                   "        vis = visible(ch, keys, causal, block_mask, offset=off)\n        _, p, _ ="),
+    "window_dropped_in_backward": ("        vis = visible(ch, keys, causal, block_mask, offset=off, window=window, elem_mask=elem_mask)\n        _, p, _ =",
+                                   "        vis = visible(ch, keys, causal, block_mask, offset=off, elem_mask=elem_mask)\n        _, p, _ ="),
+    "elem_mask_transposed": ("np.asarray(elem_mask, dtype=bool)[rows[:, None], keys[None, :]]",
+                             "np.asarray(elem_mask, dtype=bool).T[rows[:, None], keys[None, :]]"),
+    "elem_mask_inverted": ("a &= np.asarray(elem_mask, dtype=bool)[rows[:, None], keys[None, :]]",
+                           "a &= ~np.asarray(elem_mask, dtype=bool)[rows[:, None], keys[None, :]]"),
+    "elem_mask_dropped_in_backward": ("        vis = visible(ch, keys, causal, block_mask, offset=off, window=window, elem_mask=elem_mask)\n        _, p, _ =",
+                                      "        vis = visible(ch, keys, causal, block_mask, offset=off, window=window)\n        _, p, _ ="),
+    "elem_mask_candidates_first_row": ("keys = keys[np.asarray(elem_mask, dtype=bool)[rows].any(axis=0)[keys]]",
+                                       "keys = keys[np.asarray(elem_mask, dtype=bool)[rows[:1]].any(axis=0)[keys]]"),
     "alibi_sign": ("return -float(slope) * np.abs(", "return float(slope) * np.abs("),
     "alibi_no_abs": ("np.abs((rows[:, None] + offset) - keys[None, :]).astype(np.float64)",
                      "((rows[:, None] + offset) - keys[None, :]).astype(np.float64)"),
