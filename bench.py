@@ -19,6 +19,14 @@ visible pairs; not the headline configuration.
 --alibi times causal attention with ALiBi's geometric slopes (one per head) on
 the workload's shape, alone or with --window; not the headline configuration.
 
+--docmask times a causal document mask over one sequence of the workload's
+B * N tokens per head (the documents of --packed laid end to end) through the
+element-mask calls (fa_forward_bitmask, fa_backward_bitmask: full blocks
+unmasked, partial blocks from bit tiles), beside the same attention as a
+packed batch and the block mask alone (partial blocks computed whole: the
+tile work without the bits); FLOP counted from the visible pairs. It is not
+the headline configuration.
+
 --packed splits the workload's B * N tokens per head into a seeded
 document-like mix of sequence lengths and times the packed variable-length
 calls (fa_forward_varlen, fa_backward_varlen), with the same batch padded to
@@ -132,6 +140,9 @@ def parse():
                     help="sliding-window causal attention over the last W keys of each query (not the headline)")
     ap.add_argument("--alibi", action="store_true",
                     help="causal attention with ALiBi's geometric slopes, one per head (not the headline)")
+    ap.add_argument("--docmask", action="store_true",
+                    help="causal document mask over the workload's tokens as an element mask of partial "
+                         "blocks (not the headline)")
     ap.add_argument("--packed", action="store_true",
                     help="time packed variable-length batches of the workload's tokens (not the headline)")
     ap.add_argument("--flush-mb", type=int, default=0,
@@ -189,6 +200,8 @@ def main():
     w = I.WORKLOADS[args.workload]
     if args.packed:
         return packed_main(args, w)
+    if args.docmask:
+        return docmask_main(args, w)
     if args.window or args.alibi:
         return window_main(args, w)
     if args.fp8:
@@ -523,6 +536,91 @@ def window_main(args, w):
         "roofline": {"bound": "mfma", "kernel": "forward (one launch)", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "launch_ms": round(t_fwd, 4), "flop_per_launch": 2 * per},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def docmask_main(args, w):
+    """A causal document mask as an element mask, against the packed batch of
+    the same documents and against its block mask alone."""
+    import numpy as np
+    import torch
+    from exact_attention_110_amd import binding
+    from exact_attention_110_amd import inputs as I
+
+    if w.sparse or w.dtype == "fp32" or not w.causal:
+        print("--docmask needs a dense causal 16-bit workload", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda", 0)
+    lens = I.packed_lengths(w.B * w.N, w.N / 8, w.seed + 300)
+    n = sum(lens)
+    x = I.make_packed(lens, lens, w.H, w.Hkv, w.d, w.dtype, w.seed, with_grad=True)
+    qp, kp, vp, dop = (x[t].to(dev) for t in ("q", "k", "v", "do"))      # [H, n, d]
+    q, k, v, do = (t.unsqueeze(0) for t in (qp, kp, vp, dop))           # [1, H, n, d], the same memory
+    cu = torch.from_numpy(x["cu_q"]).to(dev)
+    doc = torch.repeat_interleave(torch.arange(len(lens), device=dev), torch.tensor(lens, device=dev))
+    allow = doc[:, None] == doc[None, :]
+    bm, bt, tb = binding.bit_block_mask(allow)
+    del allow
+    causal_blocks = torch.tril(torch.ones_like(bm))
+    n_kept = int((bm * causal_blocks).sum())
+    pairs = sum(m * (m + 1) // 2 for m in lens)
+    per = 2.0 * pairs * w.d * w.H
+    total_flop = 7 * per
+    o, lse = torch.empty_like(q), torch.empty((1, w.H, n), dtype=torch.float32, device=dev)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    ws = binding.workspace(q, k)
+    mx = max(lens)
+    wsp = torch.empty(binding.workspace_size(len(lens), w.H, w.Hkv, mx, w.d, q.dtype), dtype=torch.uint8,
+                      device=dev)
+
+    def step_bits():
+        binding.forward_bitmask(q, k, v, bm, bt, tb, w.scale, True, out=o, lse=lse)
+        binding.backward_bitmask(q, k, v, o, lse, do, bm, bt, tb, w.scale, True, ws=ws, grads=grads)
+
+    def step_blocks():
+        binding.forward(q, k, v, w.scale, True, bm, out=o, lse=lse)
+        binding.backward(q, k, v, o, lse, do, w.scale, True, bm, ws=ws, grads=grads)
+
+    def step_packed():
+        o2, l2 = binding.forward_varlen(qp, kp, vp, cu, cu, mx, mx, w.scale, True, out=o[0], lse=lse[0])
+        binding.backward_varlen(qp, kp, vp, o2, l2, dop, cu, cu, mx, mx, w.scale, True, ws=wsp,
+                                grads=tuple(g[0] for g in grads))
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps
+
+    ms = timed(step_bits)
+    ms_blocks = timed(step_blocks)
+    ms_packed = timed(step_packed)
+    value = total_flop / (ms * 1e-3) / 1e12
+    print(f"[bench] causal document mask ({len(lens)} documents, {n_kept} kept blocks on or below the diagonal, "
+          f"{tb.shape[0]} partial): element mask {ms:.3f} ms/step ({value:.1f} TFLOP/s); block mask alone "
+          f"{ms_blocks:.3f}; packed batch {ms_packed:.3f}", file=sys.stderr, flush=True)
+    line = {
+        "metric": "causal document-masked attention fwd+bwd TFLOP/s (visible-pair FLOP)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name + "_docmask", "documents": len(lens), "tokens": n, "H": w.H, "Hkv": w.Hkv,
+                   "d": w.d, "kept_blocks": n_kept, "partial_blocks": int(tb.shape[0]),
+                   "flop_per_step": total_flop, "block_mask_alone_ms_per_step": round(ms_blocks, 4),
+                   "packed_ms_per_step": round(ms_packed, 4)},
     }
     print(json.dumps(line), flush=True)
 

@@ -73,6 +73,11 @@ def load():
     lib.fa_forward_select.restype = I
     lib.fa_forward_kernel_rows.argtypes = [I] * 12
     lib.fa_forward_kernel_rows.restype = I
+    lib.fa_forward_bitmask.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, I, I, F, U64, P]
+    lib.fa_forward_bitmask.restype = I
+    lib.fa_backward_bitmask.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, I, I, F, U64,
+                                        P, S, P]
+    lib.fa_backward_bitmask.restype = I
     lib.fa_backward_launches.argtypes = [I, I, I, I, I, I, F, I, I, I]
     lib.fa_backward_launches.restype = I
     lib.fa_forward_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, F, F, F, F, I, I, P]
@@ -284,6 +289,79 @@ def backward_noalloc(q, k, v, o, lse, do, scale=None, causal=False, block_mask=N
                                     _stream(q.device))
     if st != 0:
         raise FAError(st, "fa_backward_noalloc")
+    return dq, dk, dv
+
+
+def bit_block_mask(allow):
+    """Block form of a boolean visibility matrix allow [Nq, Nk] (True = key j
+    visible to query i), for fa_forward_bitmask / fa_backward_bitmask:
+    (block_mask uint8 [nbq, nbk], block_tile int32 [nbq, nbk], tile_bits int32
+    [n_tiles, 128, 4]) on allow's device. A block with no visible element is
+    0 in block_mask; a block whose every element is visible has tile -1; the
+    others get consecutive tiles whose bit j % 32 of word (j % 128) / 32 of
+    row i % 128 is allow[i, j]. Rows and keys past Nq, Nk count as visible, so
+    that a ragged last block whose real elements are all visible stays full."""
+    allow = torch.as_tensor(allow, dtype=torch.bool)
+    nq, nk = allow.shape
+    nbq, nbk = -(-nq // MASK_BLOCK), -(-nk // MASK_BLOCK)
+    pad = torch.ones((nbq * MASK_BLOCK, nbk * MASK_BLOCK), dtype=torch.bool, device=allow.device)
+    pad[:nq, :nk] = allow
+    blocks = pad.view(nbq, MASK_BLOCK, nbk, MASK_BLOCK).permute(0, 2, 1, 3)  # [nbq, nbk, 128, 128]
+    real = torch.zeros_like(pad)
+    real[:nq, :nk] = True
+    any_real = (pad & real).view(nbq, MASK_BLOCK, nbk, MASK_BLOCK).permute(0, 2, 1, 3).flatten(2).any(dim=2)
+    full = blocks.flatten(2).all(dim=2)
+    block_mask = any_real.to(torch.uint8).contiguous()
+    partial = any_real & ~full
+    block_tile = torch.full((nbq, nbk), -1, dtype=torch.int32, device=allow.device)
+    n_tiles = int(partial.sum())
+    block_tile[partial] = torch.arange(n_tiles, dtype=torch.int32, device=allow.device)
+    tiles = blocks[partial].reshape(n_tiles, MASK_BLOCK, 4, 32).to(torch.int64)
+    weights = torch.tensor([1 << b for b in range(32)], dtype=torch.int64, device=allow.device)
+    words = (tiles * weights).sum(dim=3)                                   # [n_tiles, 128, 4], < 2^32
+    words = torch.where(words >= 1 << 31, words - (1 << 32), words).to(torch.int32)
+    return block_mask, block_tile.contiguous(), words.contiguous()
+
+
+def forward_bitmask(q, k, v, block_mask, block_tile, tile_bits, scale=None, causal=False, out=None, lse=None,
+                    dropout_rate=0.0, seed=0):
+    """O, LSE under a block mask with element masks of partial blocks
+    (fa_forward_bitmask); the mask arrays as returned by ``bit_block_mask``."""
+    B, H, Hkv, N, Nk, d = _shape4(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    m = _mask(block_mask, N, q.device, Nk)
+    bt = block_tile.to(q.device, torch.int32).contiguous()
+    tb = tile_bits.to(q.device, torch.int32).contiguous()
+    st = load().fa_forward_bitmask(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, Hkv, N, Nk, d, scale,
+                                   int(bool(causal)), _ptr(m), _ptr(bt), _ptr(tb) if tb.numel() else None,
+                                   tb.shape[0], _DTYPES[q.dtype], float(dropout_rate), _seed(seed),
+                                   _stream(q.device))
+    if st != 0:
+        raise FAError(st, "fa_forward_bitmask")
+    return o, lse_t
+
+
+def backward_bitmask(q, k, v, o, lse, do, block_mask, block_tile, tile_bits, scale=None, causal=False, ws=None,
+                     grads=None, dropout_rate=0.0, seed=0):
+    """dq, dk, dv under the mask of ``forward_bitmask`` (fa_backward_bitmask)."""
+    B, H, Hkv, N, Nk, d = _shape4(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    for name, t in (("o", o), ("do", do)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must match q")
+    m = _mask(block_mask, N, q.device, Nk)
+    bt = block_tile.to(q.device, torch.int32).contiguous()
+    tb = tile_bits.to(q.device, torch.int32).contiguous()
+    ws = workspace(q, k) if ws is None else ws
+    dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    st = load().fa_backward_bitmask(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), B, H, Hkv, N, Nk, d, scale, int(bool(causal)), _ptr(m), _ptr(bt),
+                                    _ptr(tb) if tb.numel() else None, tb.shape[0], _DTYPES[q.dtype],
+                                    float(dropout_rate), _seed(seed), _ptr(ws), ws.numel(), _stream(q.device))
+    if st != 0:
+        raise FAError(st, "fa_backward_bitmask")
     return dq, dk, dv
 
 

@@ -76,6 +76,30 @@ bool make_band(int causal, int window_left, int window_right, Band* b) {
   return true;
 }
 
+// Element masks of partial blocks (fa_forward_bitmask / fa_backward_bitmask).
+struct ElemMask {
+  const int32_t* btile;
+  const uint32_t* bits;
+  int ntiles;
+};
+constexpr int kMaxTiles = 1 << 21;  // tile offsets (2 KB per tile) stay inside 32 bits
+
+// NULL (no element mask) or a well-formed one: a block mask beside it, block_tile
+// 4-byte aligned, tile_bits 16-byte aligned and present when there are tiles.
+int check_elem(const ElemMask* em, const uint8_t* block_mask) {
+  if (!em) return FA_OK;
+  if (!block_mask || !em->btile || ((uintptr_t)em->btile & 3u)) return FA_ERR_INVALID_ARG;
+  if (em->ntiles < 0 || em->ntiles > kMaxTiles) return FA_ERR_INVALID_ARG;
+  if (em->ntiles > 0 && (!em->bits || !aligned16(em->bits))) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+void set_elem(fa::AttnShape& s, const ElemMask* em) {
+  s.btile = em ? em->btile : nullptr;
+  s.bits = em && em->ntiles > 0 ? em->bits : nullptr;
+  s.ntiles = em ? em->ntiles : 0;
+}
+
 fa::AttnShape make_shape(const Geo& g, float scale, const Band& band, const uint8_t* mask) {
   fa::AttnShape s;
   s.B = g.B;
@@ -100,6 +124,9 @@ fa::AttnShape make_shape(const Geo& g, float scale, const Band& band, const uint
   s.drop_scale = 1.f;
   s.seed0 = s.seed1 = 0;
   s.alibi = nullptr;
+  s.btile = nullptr;
+  s.bits = nullptr;
+  s.ntiles = 0;
   return s;
 }
 
@@ -151,7 +178,7 @@ int check_backward(const void* q, const void* k, const void* v, const void* o, c
 int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, const Geo& g,
                  float scale, int causal, int window_left, int window_right, const float* alibi,
                  const uint8_t* block_mask, int dtype, float rate, unsigned long long seed, void* stream,
-                 int rows = 0) {
+                 int rows = 0, const ElemMask* em = nullptr) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u) ||
       ((uintptr_t)alibi & 3u))
@@ -159,11 +186,13 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   int st = check_shape(g, scale, dtype);
   if (st != FA_OK) return st;
   if (mask_too_long(g, block_mask)) return FA_ERR_UNSUPPORTED;
+  if (check_elem(em, block_mask) != FA_OK) return FA_ERR_INVALID_ARG;
   Band band;
   if (!make_band(causal, window_left, window_right, &band)) return FA_ERR_INVALID_ARG;
   fa::FwdArgs a;
   a.s = make_shape(g, scale, band, block_mask);
   a.s.alibi = alibi;
+  set_elem(a.s, em);
   if (!set_dropout(a.s, rate, seed)) return FA_ERR_INVALID_ARG;
   if (a.s.drop_t > 0 && dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   a.q = q;
@@ -189,9 +218,11 @@ bool fused_ok(const Geo& g, float rate, const float* alibi, const uint8_t* block
 int stage_impl(int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dO, void* dq, void* dk, void* dv, const Geo& g, float scale, int causal,
                int window_left, int window_right, const float* alibi, const uint8_t* block_mask, int dtype,
-               float rate, unsigned long long seed, void* workspace, size_t workspace_bytes, void* stream) {
+               float rate, unsigned long long seed, void* workspace, size_t workspace_bytes, void* stream,
+               const ElemMask* em = nullptr) {
   if (stage < 0 || stage > 3) return FA_ERR_INVALID_ARG;
   if ((uintptr_t)alibi & 3u) return FA_ERR_INVALID_ARG;
+  if (check_elem(em, block_mask) != FA_OK) return FA_ERR_INVALID_ARG;
   int st = check_backward(q, k, v, o, lse, dO, dq, dk, dv, g, scale, block_mask, dtype, workspace,
                           workspace_bytes);
   if (st != FA_OK) return st;
@@ -200,6 +231,7 @@ int stage_impl(int stage, const void* q, const void* k, const void* v, const voi
   fa::BwdArgs a;
   a.s = make_shape(g, scale, band, block_mask);
   a.s.alibi = alibi;
+  set_elem(a.s, em);
   if (!set_dropout(a.s, rate, seed)) return FA_ERR_INVALID_ARG;
   if (stage == 3 && (!fused_ok(g, 0.f, alibi, block_mask) || a.s.drop_t > 0)) return FA_ERR_UNSUPPORTED;
   a.q = q;
@@ -222,7 +254,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
                   const void* dO, void* dq, void* dk, void* dv, const Geo& g, float scale, int causal,
                   int window_left, int window_right, const float* alibi, const uint8_t* block_mask,
                   int dtype, float rate, unsigned long long seed, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+                  void* stream, const ElemMask* em = nullptr) {
   // For d <= 64 without dropout, score bias or block mask, the dK/dV and dQ
   // kernels run two workgroups per CU each and go out as one launch (stage 3),
   // so the dQ workgroups fill the CUs the dK/dV kernel's causal tail leaves
@@ -234,7 +266,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   for (int i = 0; i < (fused ? 2 : 3); ++i) {
     const int stage = stages[i];
     int st = stage_impl(stage, q, k, v, o, lse, dO, dq, dk, dv, g, scale, causal, window_left, window_right,
-                        alibi, block_mask, dtype, rate, seed, workspace, workspace_bytes, stream);
+                        alibi, block_mask, dtype, rate, seed, workspace, workspace_bytes, stream, em);
     if (st != FA_OK) return st;
   }
   return FA_OK;
@@ -307,6 +339,27 @@ int fa_forward_select(int rows_per_wave, const void* q, const void* k, const voi
   if (rows_per_wave != 0 && rows_per_wave != 32 && rows_per_wave != 64) return FA_ERR_INVALID_ARG;
   return forward_impl(q, k, v, o, lse, fixed_geo(B, H, Hkv, Nq, Nk, d), scale, causal, window_left, window_right,
                       alibi_slopes, block_mask, dtype, dropout_rate, seed, stream, rows_per_wave);
+}
+
+int fa_forward_bitmask(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
+                       int Nq, int Nk, int d, float scale, int causal, const uint8_t* block_mask,
+                       const int32_t* block_tile, const uint32_t* tile_bits, int n_tiles, int dtype,
+                       float dropout_rate, unsigned long long seed, void* stream) {
+  if (!block_mask || !block_tile) return FA_ERR_INVALID_ARG;
+  const ElemMask em{block_tile, tile_bits, n_tiles};
+  return forward_impl(q, k, v, o, lse, fixed_geo(B, H, Hkv, Nq, Nk, d), scale, causal, -1, -1, nullptr, block_mask,
+                      dtype, dropout_rate, seed, stream, 0, &em);
+}
+
+int fa_backward_bitmask(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int Nq, int Nk, int d,
+                        float scale, int causal, const uint8_t* block_mask, const int32_t* block_tile,
+                        const uint32_t* tile_bits, int n_tiles, int dtype, float dropout_rate,
+                        unsigned long long seed, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!block_mask || !block_tile) return FA_ERR_INVALID_ARG;
+  const ElemMask em{block_tile, tile_bits, n_tiles};
+  return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, fixed_geo(B, H, Hkv, Nq, Nk, d), scale, causal, -1, -1,
+                       nullptr, block_mask, dtype, dropout_rate, seed, workspace, workspace_bytes, stream, &em);
 }
 
 int fa_forward_kernel_rows(int B, int H, int Hkv, int Nq, int Nk, int d, int causal, int window_left,

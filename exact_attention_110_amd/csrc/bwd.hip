@@ -267,9 +267,28 @@ __device__ __forceinline__ void bwd_kv_body(const BwdArgs& a, const int hk, cons
   // dS = P (z c dP - D), the gradient flowing to P through the dropped values.
   // ALiBi adds -slope log2(e) |query + off - kj| of the step's query head to
   // the log2-unit score (a constant bias: dS is unchanged in form).
+  // Element masks of partial blocks (block masks with bit tiles): such steps
+  // run the masked variant, whose bitrow bit i says whether element i is
+  // visible; the lane's key is bit kj % 32 = l32 of word (kj % 128) / 32 = w
+  // of each of its 16 rows.
+  const rsrc_t rbits = make_rsrc(s.bits, (unsigned)s.ntiles * 2048u);
   auto probs = [&](auto masked, const f32x16& sc, const f32x16& dp, int q0, int stb, int bh, unsigned int (&pk)[8],
                    unsigned int (&sk)[8]) {
     constexpr bool MASKED = decltype(masked)::value;
+    unsigned int bitrow = 0xffffu;
+    if constexpr (MASKED && MASK) {
+      if (s.btile) {
+        const int t = s.btile[(size_t)(q0 >> 7) * s.nbk + kblk];
+        if (t >= 0) {
+          bitrow = 0u;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const unsigned int word = bload_u32(rbits, bits_off(t, (q0 & 127) + 8 * (i >> 2) + 4 * hh + (i & 3), w));
+            bitrow |= ((word >> l32) & 1u) << i;
+          }
+        }
+      }
+    }
     const __attribute__((address_space(3))) float* lsel =
         (const __attribute__((address_space(3))) float*)(stat + stb * STB);
     const __attribute__((address_space(3))) float* ndl = lsel + BQ;  // -D
@@ -291,7 +310,8 @@ __device__ __forceinline__ void bwd_kv_body(const BwdArgs& a, const int hk, cons
         const int i = 4 * j4 + r;
         const float sh = ALIBI ? fmaf(nsl2, fabsf((float)(dbase + 8 * j4 + r)), -L4[r]) : -L4[r];
         float pv = fast_exp2(fmaf(sc[i], c, sh));
-        if constexpr (MASKED) pv = (8 * j4 + r < thr || (LOWER && 8 * j4 + r > thr2)) ? 0.f : pv;
+        if constexpr (MASKED)
+          pv = (8 * j4 + r < thr || (LOWER && 8 * j4 + r > thr2) || !((bitrow >> i) & 1u)) ? 0.f : pv;
         if constexpr (DROP) {
           const bool z = drop_keep(dwc[j4], r, s.drop_t);
           p[r] = z ? pv * s.drop_scale : 0.f;
@@ -405,7 +425,16 @@ __device__ __forceinline__ void bwd_kv_body(const BwdArgs& a, const int hk, cons
   const std::false_type plain;
   const RingAt<-1> rt;
   int e = 0;
-  for (int hg = 0; hg < s.G; ++hg) {
+  // with element masks of partial blocks any step may need masking: every step
+  // runs the masked variant (the plain schedule below serves all other calls)
+  const bool all_masked = MASK && s.btile != nullptr;
+  for (int hg = 0; all_masked && hg < s.G; ++hg) {
+    for (int t = 0; t < nq; ++t, ++e) {
+      iter(e, masked, rt, scA, dpA, pkA, skA, scB, dpB, pkB, skB);
+      b_to_a();
+    }
+  }
+  for (int hg = 0; !all_masked && hg < s.G; ++hg) {
     for (int t = 0; t < ndiag; ++t, ++e) {
       iter(e, masked, rt, scA, dpA, pkA, skA, scB, dpB, pkB, skB);
       b_to_a();
@@ -584,6 +613,8 @@ __device__ __forceinline__ void bwd_q_body(const BwdArgs& a, const int h, const 
   for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+  // element masks of partial blocks: bit tiles through a buffer resource
+  const rsrc_t rbits = make_rsrc(s.bits, (unsigned)s.ntiles * 2048u);
 
   // K and V tiles by LDS DMA into the buffer the previous step read (the
   // barrier that ended it has passed); rows past the sequence arrive as zeros
@@ -607,6 +638,15 @@ __device__ __forceinline__ void bwd_q_body(const BwdArgs& a, const int h, const 
     // wave-uniform: does any row of the wave see a key of the tile
     const bool active = !(BAND && ks > qw + 31 + offu) && !(LOWER && ks + Q_BN - 1 < qw + offl);
     if (active) {
+      // a partial block: this row's bits for the tile's 32-key halves
+      int tidx = -1;
+      if constexpr (MASK) {
+        if (s.btile) tidx = s.btile[(size_t)qb * s.nbk + (ks >> 7)];
+      }
+      unsigned int bwq[Q_T2];
+#pragma unroll
+      for (int t2 = 0; t2 < Q_T2; ++t2)
+        bwq[t2] = tidx >= 0 ? bload_u32(rbits, bits_off(tidx, qi & 127, ((ks & 127) >> 5) + t2)) : ~0u;
       const lds_t* kb = kbuf + buf * KBUF;
       const lds_t* vb = vbuf + buf * VBUF;
       // S^T = K Q^T and dP^T = V dO^T for the tile's keys (32-key halves)
@@ -631,7 +671,7 @@ __device__ __forceinline__ void bwd_q_body(const BwdArgs& a, const int h, const 
       // dS for query qi and key ks + 32 t2 + 8 (i / 4) + 4 hh + i % 4. Band: kept
       // only if qi + off - wl <= key <= qi + off + wr. Keys past the sequence read
       // as zeros, so their dS multiplies a zero row of K and needs no mask.
-      const bool diag = (BAND && ks + Q_BN - 1 > qw + offu) || (LOWER && ks < qw + 31 + offl);
+      const bool diag = (BAND && ks + Q_BN - 1 > qw + offu) || (LOWER && ks < qw + 31 + offl) || tidx >= 0;
       const int thr = qi + offu - ks - 4 * hh;   // last kept 32 t2 + 8 (i / 4) + i % 4
       const int thr2 = qi + offl - ks - 4 * hh;  // first kept (with a lower edge)
       unsigned int sk[Q_T2][8];
@@ -660,7 +700,8 @@ __device__ __forceinline__ void bwd_q_body(const BwdArgs& a, const int h, const 
               float pv = fast_exp2(fmaf(sc[t2][i], c, sh));
               if constexpr (MASKED) {
                 const int kidx = 32 * t2 + 8 * (i >> 2) + (i & 3);
-                pv = (kidx > thr || (LOWER && kidx < thr2)) ? 0.f : pv;
+                pv = (kidx > thr || (LOWER && kidx < thr2) || !((bwq[t2] >> (kidx - 32 * t2 + 4 * hh)) & 1u)) ? 0.f
+                                                                                                      : pv;
               }
               if constexpr (DROP)
                 v2[r] = pv * ((drop_keep(wd, i & 3, s.drop_t) ? dp[t2][i] * s.drop_scale : 0.f) + ndd);

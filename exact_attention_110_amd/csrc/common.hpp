@@ -146,6 +146,18 @@ __device__ __forceinline__ void bstore8(rsrc_t r, unsigned int off, u32x2 v) {
 __device__ __forceinline__ void bstore_f32(rsrc_t r, unsigned int off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, off, 0, 0);
 }
+__device__ __forceinline__ unsigned int bload_u32(rsrc_t r, unsigned int off) {
+  return (unsigned int)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x2 bload_u32x2(rsrc_t r, unsigned int off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+// Element-mask bit tiles of partial blocks: tile t holds 128 rows of four
+// 32-bit words; bit k of word c of row r is key 32 c + k of the block for
+// query r of the block. Byte offset of word c of row r of tile t:
+__device__ __forceinline__ unsigned int bits_off(int t, int r, int c) {
+  return (unsigned)t * 2048u + (unsigned)(r * 16 + c * 4);
+}
 __device__ __forceinline__ void batomic_add(rsrc_t r, unsigned int off, float v) {
   __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, off, 0, 0);
 }

@@ -179,6 +179,8 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
   lstore_tile(0);
   __syncthreads();
 
+  // element masks of partial blocks: bit tiles through a buffer resource
+  const rsrc_t rbits = make_rsrc(s.bits, (unsigned)s.ntiles * 2048u);
   for (int e = 0; e < ntiles; ++e) {
     const int buf = e & 1;
     const int ks = tile_at(e) * FWD_BN;
@@ -187,6 +189,13 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
     // wave-uniform: does any row of the wave see a key of the tile
     const bool active = !(BAND && ks > qw + 31 + offu) && !(LOWER && ks + FWD_BN - 1 < qw + offl);
     if (active) {
+      // a partial block: this row's bits for the tile's two 32-key halves
+      int tidx = -1;
+      if constexpr (MASK) {
+        if (s.btile) tidx = s.btile[(size_t)qb * s.nbk + (ks >> 7)];
+      }
+      u32x2 bw = {~0u, ~0u};
+      if (tidx >= 0) bw = bload_u32x2(rbits, bits_off(tidx, qi & 127, (ks & 127) >> 5));
       const lds_t* kb = kbuf + buf * KBUF;
       const lds_t* vb = vbuf + buf * VBUF;
       f32x16 sc[2];
@@ -204,15 +213,17 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
         }
       }
       // sc[t2][i] is S for query qi and key ks + 32 t2 + 8 (i / 4) + 4 hh + i % 4
-      const bool need_mask =
-          (BAND && ks + FWD_BN - 1 > qw + offu) || (LOWER && ks < qw + 31 + offl) || (ks + FWD_BN > nk);
+      const bool need_mask = (BAND && ks + FWD_BN - 1 > qw + offu) || (LOWER && ks < qw + 31 + offl) ||
+                             (ks + FWD_BN > nk) || tidx >= 0;
       if (need_mask) {
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int key = ks + 32 * t2 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            if ((BAND && key > qi + offu) || (LOWER && key < qi + offl) || key >= nk) sc[t2][i] = -INFINITY;
+            const int kofs = 8 * (i >> 2) + 4 * hh + (i & 3);  // key within the 32-key half
+            const int key = ks + 32 * t2 + kofs;
+            if ((BAND && key > qi + offu) || (LOWER && key < qi + offl) || key >= nk || !((bw[t2] >> kofs) & 1u))
+              sc[t2][i] = -INFINITY;
           }
       }
       // ALiBi: the scores move to log2 units with the bias added, -slope log2(e)
@@ -755,7 +766,11 @@ __global__ __launch_bounds__(F32_R * F32_S) void fwd_f32_kernel(FwdArgs a) {
 #pragma unroll
     for (int t = 0; t < F32_C; ++t) {
       const int j = j0 + t;
-      const bool vis = j >= kbeg_row && j < kend_row && (!s.mask || s.mask[(size_t)mrow * s.nbk + j / 128] != 0);
+      bool vis = j >= kbeg_row && j < kend_row && (!s.mask || s.mask[(size_t)mrow * s.nbk + j / 128] != 0);
+      if (vis && s.mask && s.btile) {  // a partial block: the element's bit (tiles past the last read as 0)
+        const int t = s.btile[(size_t)mrow * s.nbk + j / 128];
+        if (t >= 0) vis = t < s.ntiles && ((s.bits[(size_t)t * 512 + (qi & 127) * 4 + ((j & 127) >> 5)] >> (j & 31)) & 1u);
+      }
       float dot = 0.f;
       if (vis) {
         const float4* kr = (const float4*)(K + (size_t)j * D);

@@ -27,6 +27,15 @@ struct AttnShape {
   int band;
   int wl, wr;
   const uint8_t* mask;  // NULL or uint8 [nbq][nbk] (fixed lengths only)
+  // element masks of partial blocks (only with mask): btile NULL, or int32
+  // [nbq][nbk] with -1 for a kept block whose every element is visible and
+  // t >= 0 for one whose elements are tile t of bits: uint32 [ntiles][128][4],
+  // bit j % 32 of word j / 32 of row i set = key j of the block visible to
+  // query i of the block. Tiles are read through a buffer resource of ntiles
+  // tiles, so an index past the last tile reads zeros (no element visible).
+  const int* btile;
+  const unsigned int* bits;
+  int ntiles;
   // NULL or float [H]: ALiBi slopes, s_ij += -alibi[h] * |i + (nk - nq) - j|
   const float* alibi;
   int nbq, nbk;   // ceil(Nq / 128), ceil(Nk / 128)

@@ -263,6 +263,45 @@ int fa_backward_qk(const void* q, const void* k, const void* v, const void* o,
                    void* stream);
 
 /*
+ * Element masks for partial blocks (pranaymahendrakar.com lesson
+ * "FlashAttention", Researcher tier, "Beyond hand-written kernels": one tiled
+ * kernel serving user mask functions evaluated per query-key pair; the pages
+ * fix no encoding, this is the reading taken). A C ABI takes no device code,
+ * so the predicate arrives evaluated, in block form: the block mask says
+ * which 128 x 128 blocks hold any visible element (zero blocks are skipped
+ * without being read), and for each kept block block_tile says whether all of
+ * its elements are visible (-1) or only those set in one 128 x 128 bit tile
+ * (t >= 0). Key j is then visible to query i iff block_mask[I][J] != 0 and,
+ * for t = block_tile[I][J] >= 0, bit j % 32 of word (j % 128) / 32 of row
+ * i % 128 of tile t is set (I = i / 128, J = j / 128), intersected with causal
+ * masking as for fa_forward_qk (queries aligned to the last key). Full blocks
+ * run the unmasked tile code; only partial blocks read their bits.
+ *   block_mask   device uint8 [ceil(Nq/128)][ceil(Nk/128)] (both <= 2048)
+ *   block_tile   device int32 [ceil(Nq/128)][ceil(Nk/128)], 4-byte aligned
+ *   tile_bits    device uint32 [n_tiles][128][4], 16-byte aligned (may be
+ *                NULL when n_tiles is 0)
+ *   n_tiles      0 <= n_tiles <= 2^21; an index in block_tile at or past
+ *                n_tiles reads as an all-zero tile (no element visible) - the
+ *                kernels never read past the tiles
+ * The same mask serves every batch and head. block_tile and tile_bits live in
+ * device memory and are not checked by the host beyond alignment. Dropout as
+ * for fa_forward_dropout. Other arguments, layouts, limits and errors as for
+ * fa_forward_qk / fa_backward_qk (no window, no ALiBi); FA_ERR_INVALID_ARG for
+ * a NULL block_mask or block_tile, misalignment or n_tiles out of range. The
+ * backward call must get the mask arrays the forward call got.
+ */
+int fa_forward_bitmask(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                       const uint8_t* block_mask, const int32_t* block_tile, const uint32_t* tile_bits,
+                       int n_tiles, int dtype, float dropout_rate, unsigned long long seed, void* stream);
+int fa_backward_bitmask(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dO, void* dq, void* dk, void* dv,
+                        int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                        const uint8_t* block_mask, const int32_t* block_tile, const uint32_t* tile_bits,
+                        int n_tiles, int dtype, float dropout_rate, unsigned long long seed,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Forward kernel choice. The 16-bit forward pass has two kernels: one with 64
  * query rows per wave (one wave per SIMD; long dense or causal rows over few
  * heads) and one with 32 rows per wave (two waves per SIMD; everything else,

@@ -332,3 +332,26 @@ def test_backward_noalloc_rejects(lib):
     # 8 bytes of statistics per (b, h, padded row): 2^21 rows fit, one block more does not
     assert call(B=1, H=64, Hkv=1, N=65536, d=32) == EUNSUP
     assert call(B=1, H=32, Hkv=1, N=65536 + 128, d=32) == EUNSUP
+
+
+def test_bitmask_rejects(lib):
+    """Element-mask entry points: both mask arrays required, aligned, a tile
+    count in range, tiles present when counted; all before any HIP call."""
+    def fwdm(mask=GOOD, tile=GOOD, bits=GOOD, n=3, dtype=BF16):
+        return lib.fa_forward_bitmask(GOOD, GOOD, GOOD, GOOD, GOOD, 1, 2, 1, 256, 256, 64, 0.125, 1, mask, tile,
+                                      bits, n, dtype, 0.0, 0, None)
+
+    def bwdm(mask=GOOD, tile=GOOD, bits=GOOD, n=3):
+        return lib.fa_backward_bitmask(GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 1, 2, 1, 256, 256, 64,
+                                       0.125, 1, mask, tile, bits, n, BF16, 0.0, 0, None, 0, None)
+    for f in (fwdm, bwdm):
+        assert f(mask=None) == EINVAL
+        assert f(tile=None) == EINVAL
+        assert f(tile=P((1 << 20) + 2)) == EINVAL
+        assert f(bits=None) == EINVAL
+        assert f(bits=ODD) == EINVAL
+        assert f(n=-1) == EINVAL
+        assert f(n=(1 << 21) + 1) == EINVAL
+    assert fwdm(dtype=5) == EINVAL
+    # no workspace: the backward reaches the workspace check only after the mask checks pass
+    assert bwdm(n=0, bits=None) == EWS
