@@ -78,5 +78,49 @@ def build(verbose=False, extra=()):
     return LIB
 
 
+# Host-side sanitizer build of the C ABI's argument checking: api.hip with
+# AddressSanitizer and UndefinedBehaviorSanitizer on its host code only (the
+# device code is built as usual), linked with the kernel objects of the
+# regular build into _build/libfa_sanitized.so. Loading it needs the ASan
+# runtime preloaded (``asan_runtime()``); tests/test_abi_sanitized.py runs the
+# C-ABI tests against it on the CPU.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+SANITIZED_LIB = os.path.join(BUILD, "libfa_sanitized.so")
+
+
+def asan_runtime():
+    """Path of the AddressSanitizer runtime that belongs to hipcc's clang."""
+    r = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("AddressSanitizer runtime not found")
+    return path
+
+
+def build_sanitized():
+    """Compile api.hip with host sanitizers and link it with the regular
+    build's kernel objects (built first when missing); returns the path."""
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        if src == "api.hip":
+            obj = os.path.join(BUILD, "api_sanitized.o")
+            cmd = [_hipcc(), *FLAGS, *SANITIZE, "-c", os.path.join(CSRC, "api.hip"), "-o", obj]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed for the sanitized api.hip:\n{r.stderr}")
+        else:
+            obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+            if not os.path.exists(obj):
+                obj, _ = _compile(src, [])
+        objs.append(obj)
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *SANITIZE, "-o", SANITIZED_LIB, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    return SANITIZED_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
