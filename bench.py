@@ -34,6 +34,11 @@ its longest sequence and run through the fixed-length calls beside it; FLOP
 are counted per sequence (n^2 d per contraction under causal masking). It is
 not the headline configuration.
 
+Warm-up: --warmup W untimed steps, continued until the GPU has been busy for
+0.3 s (the clocks settle over the first few hundred milliseconds of load); the
+JSON line reports the steps run as "warmup_steps_run". The timed region is
+exactly --steps K steps.
+
 Prints one JSON line. Besides the headline it carries:
 * "roofline": the dominant kernel's algorithmic FLOP per launch over its mean
   duration inside the step loop, measured with HIP events between the step's
@@ -152,6 +157,28 @@ def parse():
     return ap.parse_args()
 
 
+WARMUP_SECONDS = 0.3
+
+
+def warm_up(step, n):
+    """Untimed warm-up: at least n steps, and more until the GPU has been busy
+    for WARMUP_SECONDS. The clocks rise over the first few hundred
+    milliseconds of load; a timed loop that starts earlier measures the ramp
+    (measured: the first 20 launches after 3 warm-up launches ran 3-10%
+    slower than every later loop of 20). Returns the number of steps run."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    done = 0
+    while done < n or time.perf_counter() - t0 < WARMUP_SECONDS:
+        step()
+        done += 1
+        if done >= n:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return done
+
+
 def cpu_baseline(w, x, n_heads=6):
     """Time the float64 oracle on the first few (b, h) heads of the workload,
     forward (+ backward), on the host cores: a bounded sample of the same work."""
@@ -227,9 +254,7 @@ def main():
         if w.backward:
             binding.backward(q, k, v, o, lse, do, w.scale, w.causal, mask, ws=ws, grads=(dq, dk, dv), **drop)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_steps = warm_up(step, args.warmup)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
@@ -237,7 +262,8 @@ def main():
     elapsed = time.perf_counter() - t0
     ms = elapsed * 1e3 / args.steps
     value = total_flop / (ms * 1e-3) / 1e12
-    print(f"[bench] {w.name}: {ms:.3f} ms/step, {value:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    print(f"[bench] {w.name}: {ms:.3f} ms/step, {value:.1f} TFLOP/s ({warm_steps} warm-up steps)", file=sys.stderr,
+          flush=True)
 
     # The same step again with HIP events between its kernels (on torch's
     # current stream, which the library launches on): the forward call, then
@@ -350,6 +376,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm_steps,
         "ms_per_step": round(ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
