@@ -308,8 +308,7 @@ def main():
     # per-kernel times with HIP events, each kernel back to back on its own
     def event_time(fn, n):
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        fn()
-        torch.cuda.synchronize()
+        warm_up(fn, args.warmup)
         s.record()
         for _ in range(n):
             fn()
@@ -442,9 +441,7 @@ def fp8_main(args, w):
 
     def timed(fn, n_it):
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for _ in range(args.warmup):
-            fn()
-        torch.cuda.synchronize()
+        warm_up(fn, args.warmup)
         s.record()
         for _ in range(n_it):
             fn()
@@ -517,8 +514,7 @@ def window_main(args, w):
 
     def timed(fn, n_it):
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        fn()
-        torch.cuda.synchronize()
+        warm_up(fn, args.warmup)
         s.record()
         for _ in range(n_it):
             fn()
@@ -526,14 +522,14 @@ def window_main(args, w):
         torch.cuda.synchronize()
         return s.elapsed_time(e) / n_it
 
-    for _ in range(args.warmup):
+    def step():
         fwd()
         bwd()
-    torch.cuda.synchronize()
+
+    warm_up(step, args.warmup)
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        fwd()
-        bwd()
+        step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     value = total_flop / (ms * 1e-3) / 1e12
@@ -615,9 +611,7 @@ def docmask_main(args, w):
                                 grads=tuple(g[0] for g in grads))
 
     def timed(fn):
-        for _ in range(args.warmup):
-            fn()
-        torch.cuda.synchronize()
+        warm_up(fn, args.warmup)
         t0 = time.perf_counter()
         for _ in range(args.steps):
             fn()
@@ -701,9 +695,7 @@ def packed_main(args, w):
 
     def timed(fn, n):
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for _ in range(args.warmup):
-            fn()
-        torch.cuda.synchronize()
+        warm_up(fn, args.warmup)
         s.record()
         for _ in range(n):
             fn()
@@ -715,9 +707,7 @@ def packed_main(args, w):
         fwd()
         bwd()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args.warmup)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
