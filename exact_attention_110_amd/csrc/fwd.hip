@@ -18,8 +18,8 @@
 //    gfx950 transposing read ds_read_b64_tr_b16, so V needs no transpose pass.
 //  * LDS row pitches are padded so that the 16-byte row reads of K and the
 //    transposing reads of V are free of bank conflicts.
-//  * Long dense or causal inputs over few heads run fwd64_kernel (64 query
-//    rows per wave, one wave per SIMD, 256 rows per workgroup); the others,
+//  * Long rows at head size 128 run fwd64_kernel (64 query rows per wave,
+//    one wave per SIMD, 256 rows per workgroup); the others,
 //    and all block-sparse inputs, run fwd_kernel (32 rows per wave, two waves
 //    per SIMD, 128 rows per workgroup = one mask block row).
 //  * Causal: a workgroup stops at its diagonal tile, waves skip tiles that lie
@@ -957,17 +957,17 @@ static hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st) {
 }
 
 // Which 16-bit kernel a forward call takes by default. The 64-row kernel pays
-// off for long sequences over few heads (measured: N = 16384 x 16 heads, 4%
-// faster). With many workgroups the 32-row kernel's two waves per SIMD balance
-// better (4 x 32 heads over 8 kv heads at N = 8192: 1% faster), and short rows
-// spend much of their time in the 64-row kernel's diagonal tail (N = 1024:
-// 1.8x faster with 32 rows). Block masks and score biases always take the
-// 32-row kernel. Float32 inputs take the float32 kernel (0).
+// off for long rows at head size 128 (measured, causal bf16: N = 16384 x 16
+// heads 8% faster, 4 x 32 heads over 8 kv heads at N = 8192 6% faster, N =
+// 32768 9%; N = 4096 even). At head size 64 the exponentials dominate and the
+// 32-row kernel's two waves per SIMD do better (N = 16384: 6% faster), as they
+// do for short rows, where the 64-row kernel spends much of its time in the
+// diagonal tail (N = 1024: 1.6x faster). Block masks and score biases always
+// take the 32-row kernel. Float32 inputs take the float32 kernel (0).
 int forward_rows(const AttnShape& s, int dtype) {
   if (dtype == 0) return 0;
   if (s.mask || s.alibi) return 32;
-  const long long wg64 = (long long)s.B * s.H * ((s.Nq + F64_BM - 1) / F64_BM);
-  return (min(s.Nq, s.Nk) >= 8192 && wg64 <= 2048) ? 64 : 32;
+  return (s.d == 128 && min(s.Nq, s.Nk) >= 8192) ? 64 : 32;
 }
 
 hipError_t launch_forward(const FwdArgs& a, int dtype, hipStream_t st, int rows) {

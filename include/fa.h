@@ -303,8 +303,8 @@ int fa_backward_bitmask(const void* q, const void* k, const void* v, const void*
 
 /*
  * Forward kernel choice. The 16-bit forward pass has two kernels: one with 64
- * query rows per wave (one wave per SIMD; long dense or causal rows over few
- * heads) and one with 32 rows per wave (two waves per SIMD; everything else,
+ * query rows per wave (one wave per SIMD; rows of at least 8192 keys at head
+ * size 128) and one with 32 rows per wave (two waves per SIMD; everything else,
  * and every call with a block mask or score bias). Both compute the same
  * attention (results agree within the tolerances, not bit for bit).
  *

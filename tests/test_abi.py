@@ -264,7 +264,7 @@ def test_fp8_head_sizes(lib):
 
 def test_forward_kernel_rows(lib):
     """The library's forward-kernel choice, as bench.py reads it: 64 rows per
-    wave for long dense or causal rows over few workgroups, 32 otherwise and
+    wave for long rows at head size 128, 32 otherwise and
     always with a block mask or score bias, 0 (the float32 kernel) for FA_F32;
     negative statuses for arguments the forward calls reject."""
     rows = lambda *a: lib.fa_forward_kernel_rows(*a)  # noqa: E731
@@ -272,10 +272,11 @@ def test_forward_kernel_rows(lib):
     assert rows(1, 16, 16, 16384, 16384, 128, 1, -1, -1, 0, 0, BF16) == 64
     assert rows(1, 16, 16, 16384, 16384, 128, 1, -1, -1, 1, 0, BF16) == 32
     assert rows(1, 16, 16, 16384, 16384, 128, 1, -1, -1, 0, 1, BF16) == 32
-    assert rows(4, 32, 8, 8192, 8192, 128, 1, -1, -1, 0, 0, BF16) == 32   # 4096 workgroups of 256 rows
+    assert rows(4, 32, 8, 8192, 8192, 128, 1, -1, -1, 0, 0, BF16) == 64
     assert rows(8, 12, 12, 1024, 1024, 64, 1, -1, -1, 0, 0, BF16) == 32
-    assert rows(1, 8, 8, 8192, 8191, 64, 0, -1, -1, 0, 0, F16) == 32      # the shorter side decides
-    assert rows(1, 8, 8, 8192, 8192, 64, 0, -1, -1, 0, 0, F16) == 64
+    assert rows(1, 8, 8, 8192, 8191, 128, 0, -1, -1, 0, 0, F16) == 32     # the shorter side decides
+    assert rows(1, 8, 8, 8192, 8192, 128, 0, -1, -1, 0, 0, F16) == 64
+    assert rows(1, 16, 16, 16384, 16384, 64, 1, -1, -1, 0, 0, BF16) == 32  # head size 64: 32 rows
     assert rows(1, 1, 1, 512, 512, 32, 0, -1, -1, 0, 0, F32) == 0
     assert rows(1, 2, 1, 256, 256, 96, 1, -1, -1, 0, 0, BF16) == EINVAL
     assert rows(1, 2, 1, 256, 256, 64, 1, -2, -1, 0, 0, BF16) == EINVAL
