@@ -215,8 +215,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
-              "heads and batches shard across GPUs without exchange, but this build "
-              "measures the single-GPU kernel only", file=sys.stderr)
+              "heads and batches shard across GPUs without exchange, and this "
+              "benchmark measures the kernels of one GPU only", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
