@@ -276,9 +276,16 @@ __device__ __forceinline__ void bwd_kv_body(const BwdArgs& a, const int hk, cons
                    unsigned int (&sk)[8]) {
     constexpr bool MASKED = decltype(masked)::value;
     unsigned int bitrow = 0xffffu;
+    // (masked variant) whether this step needs element masks at all: a
+    // partial block, or rows that cross a band edge (the upper while
+    // q0 + off + wr < k0 + 127, the lower while q0 + 31 + off - wl > k0);
+    // with element masks every step takes this variant, and full blocks inside
+    // the band skip the per-element selects
+    bool domask = true;
     if constexpr (MASKED && MASK) {
       if (s.btile) {
         const int t = s.btile[(size_t)(q0 >> 7) * s.nbk + kblk];
+        domask = t >= 0 || (BAND && q0 + offu < k0 + KV_BKV - 1) || (LOWER && q0 + BQ - 1 + offl > k0);
         if (t >= 0) {
           bitrow = 0u;
 #pragma unroll
@@ -299,19 +306,34 @@ __device__ __forceinline__ void bwd_kv_body(const BwdArgs& a, const int hk, cons
     if constexpr (DROP) drop_words_col4(s.seed0, s.seed1, bh, kj, q0 + 4 * hh, 8, dwc);
     const float nsl2 = ALIBI ? -s.alibi[bh - b * s.H] * kLog2e : 0.f;
     const int dbase = q0 + 4 * hh + off - kj;  // query + off - kj less 8 (i / 4) + i % 4
+    float pvv[16];
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       const f32x4 L4 = *(const __attribute__((address_space(3))) f32x4*)(lsel + 8 * j4 + 4 * hh);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float sh = ALIBI ? fmaf(nsl2, fabsf((float)(dbase + 8 * j4 + r)), -L4[r]) : -L4[r];
+        pvv[4 * j4 + r] = fast_exp2(fmaf(sc[4 * j4 + r], c, sh));
+      }
+    }
+    if constexpr (MASKED) {
+      if (domask) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int o = 8 * (i >> 2) + (i & 3);
+          pvv[i] = (o < thr || (LOWER && o > thr2) || !((bitrow >> i) & 1u)) ? 0.f : pvv[i];
+        }
+      }
+    }
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
       f32x4 nd4 = {0.f, 0.f, 0.f, 0.f};
       if constexpr (DROP) nd4 = *(const __attribute__((address_space(3))) f32x4*)(ndl + 8 * j4 + 4 * hh);
       float p[4], d2[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * j4 + r;
-        const float sh = ALIBI ? fmaf(nsl2, fabsf((float)(dbase + 8 * j4 + r)), -L4[r]) : -L4[r];
-        float pv = fast_exp2(fmaf(sc[i], c, sh));
-        if constexpr (MASKED)
-          pv = (8 * j4 + r < thr || (LOWER && 8 * j4 + r > thr2) || !((bitrow >> i) & 1u)) ? 0.f : pv;
+        const float pv = pvv[i];
         if constexpr (DROP) {
           const bool z = drop_keep(dwc[j4], r, s.drop_t);
           p[r] = z ? pv * s.drop_scale : 0.f;
