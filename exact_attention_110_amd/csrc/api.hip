@@ -279,7 +279,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
 // first call on a device looks up the array's device address with
 // hipGetSymbolAddress (with that device current) and keeps it per device.
 constexpr size_t kScratchBytes = (size_t)FA_NOALLOC_SCRATCH_BYTES;
-__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
 
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mutex;

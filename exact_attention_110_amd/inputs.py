@@ -141,6 +141,25 @@ def make_small(B, H, Hkv, N, d, dtype, seed, sigma=1.0, with_grad=True):
     return out
 
 
+def make_on_device(B, H, Hkv, N, d, dtype, seed, device, sigma=1.0, with_grad=True):
+    """Seeded inputs too large to draw on the host (sequences near the length
+    limit): q, k, v (and do) drawn in that order as float32 normals N(0, sigma)
+    by torch's generator on ``device`` seeded with ``seed``, then rounded to the
+    storage dtype (RNE). Tests hand slices of the same tensors to the oracle."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    dt = _torch_dtype(dtype)
+
+    def one(shape):
+        return (torch.randn(shape, generator=g, device=device, dtype=torch.float32) * sigma).to(dt)
+
+    out = {"q": one((B, H, N, d)), "k": one((B, Hkv, N, d)), "v": one((B, Hkv, N, d))}
+    if with_grad:
+        out["do"] = one((B, H, N, d))
+    return out
+
+
 def random_block_mask(n, density, seed, block=MASK_BLOCK, keep_diagonal=False, n_keys=None):
     """uint8 [ceil(n / block), ceil(n_keys / block)] mask with i.i.d.
     Bernoulli(density) blocks (for small tests); n_keys defaults to n."""
