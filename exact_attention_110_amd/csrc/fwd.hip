@@ -141,8 +141,10 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fwd_kernel(FwdArgs a) {
   // Running reference m (in log2 units) and this lane's share l of the running
   // sum (its half of the keys). m is raised only when a row of the wave
   // exceeds it by more than kSlack, so most tiles skip the rescale; any common
-  // reference gives the same O / l and m + log2(l), and P stays <= 2^kSlack.
-  constexpr float kSlack = 8.f;
+  // reference gives the same O / l and m + log2(l), and P stays <= 2^kSlack
+  // (2^7 for float16 with dropout, whose keep scale reaches 256: the scaled
+  // probability must stay below float16's largest value, 65504).
+  constexpr float kSlack = (std::is_same<T, F16>::value && DROP) ? 7.f : 8.f;
   float m = -INFINITY;
   float l = 0.f;
 
@@ -377,7 +379,7 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
   static_assert(TCH % NT == 0 || TCH < NT, "tile loader shape");
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
-  constexpr float kSlack = 8.f;
+  constexpr float kSlack = (std::is_same<T, F16>::value && DROP) ? 7.f : 8.f;  // as in fwd_kernel
 
   __shared__ __attribute__((aligned(16))) char smem_raw[F64_NB * (KBUF + VBUF)];
   lds_t* kbuf = (lds_t*)smem_raw;
@@ -588,7 +590,10 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
   // O / l, m + log2(l) does not depend on the reference chosen. Should a row's
   // sum end above 2^60 (some later score at least 60 above the first tile's
   // maximum), the whole workgroup starts over in the general loop below, which
-  // raises the reference as it goes.
+  // raises the reference as it goes. With float16 the 16-bit probabilities
+  // have the tighter bound: the restart comes once a row sum exceeds 65504
+  // divided by the dropout keep scale, which every probability (so scaled)
+  // beyond float16's range implies, since the sum holds each probability.
   int j = 0;
   if (nfull > 0) {
     auto probs = [&](const f32x16 (&st)[2], unsigned int (&pk)[2][8], int ks) {
@@ -709,7 +714,8 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
     }
     // workgroup-uniform decision (it also orders the reads above before any
     // slot is refilled)
-    if (__syncthreads_or(l[0] > 0x1p60f || l[1] > 0x1p60f)) {
+    const float lmax = std::is_same<T, F16>::value ? 65504.f / (DROP ? s.drop_scale : 1.f) : 0x1p60f;
+    if (__syncthreads_or(l[0] > lmax || l[1] > lmax)) {
       j = 0;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {

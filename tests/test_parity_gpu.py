@@ -103,6 +103,29 @@ def test_late_dominant_scores(dtype, causal, rows):
                  rows_per_wave=int(rows))
 
 
+@pytest.mark.parametrize("rows", ["64", "32"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("boost,rate", [(2.0, 0.0), (4.0, 0.0), (4.0, 0.5)])
+def test_moderately_late_dominant_scores(dtype, boost, rate, rows):
+    """One key far into the sequence whose score exceeds the first tile's
+    maximum by about 23 (boost 2) or 46 (boost 4) in log2 units: inside the
+    fixed-reference range of the 64-row kernel's main loop, so nothing forces
+    a restart through the row sums, but relative to that reference its
+    probability is above the largest finite float16 (2^16); the 16-bit
+    probabilities must not overflow, also once scaled for dropout. (The
+    causal 64-row kernel needs at least two full tiles before a workgroup's
+    diagonal: N = 600 gives the last workgroups up to 16.)"""
+    N, d = 600, 64
+    x = I.make_small(1, 2, 1, N, d, dtype, 23)
+    x["q"] = x["q"] + 1.0
+    x["k"][:, :, 350, :] += boost
+    q, k = (PT.np64(x[n]) for n in ("q", "k"))
+    big = float(np.abs(q @ np.swapaxes(k, -1, -2)).max()) / np.sqrt(d)
+    tol = PT.TOL_LSE + 4 * 2.0 ** -23 * big
+    PT.run_given(x, dtype, True, where=f"moderately late dominant score {dtype} boost={boost} dropout={rate}",
+                 lse_tol=tol, dropout_rate=rate, drop_seed=5, rows_per_wave=int(rows))
+
+
 DROP_SHAPES = [(1, 2, 1, 17, 32), (2, 2, 2, 64, 64), (1, 3, 1, 127, 128), (1, 4, 2, 300, 64),
                (1, 2, 2, 513, 128)]
 
