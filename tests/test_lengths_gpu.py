@@ -109,6 +109,18 @@ def test_varlen_dropout(causal):
     PT.run_varlen(lq, lk, H, Hkv, d, "bf16", causal, seed=31, dropout_rate=0.3, drop_seed=77)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_long_sequences(causal, dtype):
+    """Packed sequences long enough (the longest 9000 keys at d = 128) that the
+    library takes the 64-row forward kernel for the packed batch, with an empty
+    and a short sequence between them: every element against the oracle."""
+    lens = [9000, 0, 131, 8300]
+    assert binding.forward_kernel_rows(len(lens), 2, 1, max(lens), max(lens), 128, causal) == 64
+    PT.run_varlen(lens, lens, 2, 1, 128, dtype, causal, seed=_seed(7, causal, dtype == "fp16", 13))
+
+
 def test_varlen_grid_larger_than_sequences():
     """max_seqlen above every length: the extra workgroups exit without writing."""
     PT.run_varlen([70, 5], [9, 300], 2, 1, 64, "bf16", True, seed=41, max_q=1000, max_k=1200)
