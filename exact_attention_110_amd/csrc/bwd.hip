@@ -24,6 +24,10 @@
 //     iteration issues S and dP of the next query block, P and dS of this
 //     block and dV, dK of the previous block, which do not depend on each
 //     other, so the MFMAs overlap the softmax arithmetic within one wave.
+//     At d = 128 without block mask, dropout, score bias or a lower band edge
+//     the same grid runs eight waves per workgroup in two roles instead:
+//     producers form S, dP, P and dS; consumers accumulate dV and dK
+//     (bwd_kv_split_body).
 //  2. query-block kernel (dQ): one workgroup per 128 query rows, four waves of
 //     32 rows, laid out like the forward pass: S^T = K Q^T and dP^T = V dO^T
 //     with Q^T and dO^T in registers, so a lane owns one query row and its LSE
@@ -522,10 +526,333 @@ __device__ __forceinline__ void bwd_kv_body(const BwdArgs& a, const int hk, cons
     }
 }
 
+// ---------------------------------------------------------------------------
+// stage 1 with split roles (d = 128 without block mask, dropout, score bias or
+// a lower band edge): eight waves per key block, two per SIMD. Producer wave j
+// (0..3) holds K^T and V^T of keys k0 + 32 j .. + 31, forms S and dP of each
+// step and from them P and dS, and hands P and dS through LDS to consumer wave
+// j + 4, which holds dK^T and dV^T of the same keys and accumulates dV^T +=
+// dO^T P and dK^T += Q^T dS one step behind. Each role fits in half the
+// register file, so the two waves of a SIMD overlap one's softmax arithmetic
+// with the other's MFMAs, which the one-role kernel (all 512 registers, one
+// wave per SIMD) can only do within a single in-order instruction stream.
+//
+// Iteration e (one barrier at its end): producers load step e + 2 into the
+// ring buffer step e - 2 used, form S and dP of step e + 1 and P and dS of
+// step e (into hand-over buffer e % 2); consumers take dV, dK of step e - 1
+// from ring buffer (e - 1) % 4 and hand-over buffer (e - 1) % 2. A ring buffer
+// is read by producers in iterations e - 1 and e and by consumers in e + 1,
+// and rewritten in e + 2; a hand-over buffer is written in e, read in e + 1
+// and rewritten in e + 2.
+// ---------------------------------------------------------------------------
+constexpr int KS_NW = 8;  // waves per split-role workgroup: 4 producers, 4 consumers
+
+template <int D, int BAND, bool MASK, bool DROP, bool ALIBI>
+constexpr bool kv_split() {
+  return D == 128 && BAND <= 1 && !MASK && !DROP && !ALIBI;
+}
+
+template <class T, int D, int BAND>
+__device__ __forceinline__ void bwd_kv_split_body(const BwdArgs& a, const int hk, const int b, const int kblk) {
+  constexpr int BQ = KV_BQ;
+  constexpr int QBUF = BQ * 2 * D;  // one Q or dO block, swizzled rows
+  constexpr int STB = 2 * BQ * 4;   // one statistics block: BQ log2-scaled LSE, then BQ -D
+  constexpr int PSB = 64 * 64;      // one producer's P and dS of a step: 64 bytes per lane
+  constexpr int NS = D / 16;
+  constexpr int ND = D / 32;
+  constexpr int NB = 4;             // the unrolled step loops cover the ring once per pass
+  __shared__ __attribute__((aligned(16))) char smem_raw[NB * STB + 2 * NB * QBUF + 2 * 4 * PSB];
+  lds_t* stat = (lds_t*)smem_raw;   // [NB][2 BQ] float
+  lds_t* qbuf = stat + NB * STB;    // [NB][BQ rows, swizzled]
+  lds_t* obuf = qbuf + NB * QBUF;   // dO, [NB][BQ rows, swizzled]
+  lds_t* psbuf = obuf + NB * QBUF;  // [2][4 producers][4 chunks of 16 bytes][64 lanes]
+
+  const AttnShape& s = a.s;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);  // the wave index as a scalar
+  const bool producer = wu < 4;
+  const int jw = wu & 3;  // the wave's 32 keys within the block
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int g16 = lane >> 4;
+  const int roff = 4 * (g16 >> 1) + ((lane & 15) >> 2);  // transposing-read row offset
+  const int coff = 16 * (g16 & 1) + 4 * (lane & 3);      // transposing-read column offset
+  // the sequence as seen from the group's first query head
+  const SeqView sv = seq_view(s, b, hk * s.G, hk);
+  const int len_q = sv.nq, len_k = sv.nk, off = sv.off;
+  const int k0 = kblk * KV_BKV;
+  if (k0 >= len_k) return;  // a sequence shorter than the grid (packed batches)
+  const int kj = k0 + 32 * jw + l32;  // this lane's key (its column of S)
+  const unsigned int qbytes = (unsigned int)len_q * D * 2, kbytes = (unsigned int)len_k * D * 2;
+  const size_t krow0 = sv.krow0;
+  // query blocks from the first one that sees a key of the block (rows from
+  // k0 - off - wr) to the end, for each query head of the group
+  const int offu = off + s.wr;
+  const int nqb_all = (len_q + BQ - 1) / BQ;
+  const int qb_first = BAND ? max(0, k0 - offu) / BQ : 0;
+  const int nq = max(0, nqb_all - qb_first);
+  const int nsteps = nq * s.G;
+
+  if (producer) {
+    const float c = s.scale * kLog2e;
+    // K^T and V^T operands: lane holds key kj, d = 16 ss + 8 hh + 0..7 (keys
+    // past the sequence read as zeros)
+    const rsrc_t rk = make_rsrc((const unsigned short*)a.k + krow0 * D, kbytes);
+    const rsrc_t rv = make_rsrc((const unsigned short*)a.v + krow0 * D, kbytes);
+    s16x8 kf[NS], vf[NS];
+#pragma unroll
+    for (int ss = 0; ss < NS; ++ss) {
+      kf[ss] = bload16(rk, (unsigned)(kj * D + 16 * ss + 8 * hh) * 2u);
+      vf[ss] = bload16(rv, (unsigned)(kj * D + 16 * ss + 8 * hh) * 2u);
+    }
+    auto advance = [&](StepPos p) -> StepPos {
+      const bool next_head = p.qi + 1 >= nq;
+      return StepPos{next_head ? 0 : p.qi + 1, next_head ? p.hb + 1 : p.hb, next_head ? p.soff + 2 * a.npad : p.soff,
+                     next_head ? p.qoff + (unsigned long long)sv.qstride * D : p.qoff};
+    };
+    // a step's Q and dO rows and statistics into ring buffer buf by LDS DMA,
+    // shared by the four producers (the last also moves the statistics)
+    auto dma_q = [&](StepPos p, int buf) {
+      const int q0 = (qb_first + p.qi) * BQ;
+      const i32x4 rq = rsrc_words((const unsigned short*)a.q + p.qoff, qbytes);
+      const i32x4 rg = rsrc_words((const unsigned short*)a.dO + p.qoff, qbytes);
+      dma_tile<D, BQ, 4>(rq, q0, qbuf + buf * QBUF, wu, lane);
+      dma_tile<D, BQ, 4>(rg, q0, obuf + buf * QBUF, wu, lane);
+      if (wu == 3) {
+        const i32x4 rs = rsrc_words(a.stats + p.soff, (unsigned)a.npad * 8u);
+        dma4(rs, (unsigned)(((lane >> 5) * a.npad + q0 + (lane & 31)) * 4), lds_addr(stat + buf * STB));
+      }
+    };
+    // one plane of a ring buffer's statistics (0: LSE, 1: -D) for this lane's
+    // rows 8 j4 + 4 hh + 0..3
+    auto stats4 = [&](int sb, int plane, f32x4 (&v)[4]) {
+      const __attribute__((address_space(3))) float* pl =
+          (const __attribute__((address_space(3))) float*)(stat + sb * STB) + plane * BQ;
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) v[j4] = *(const __attribute__((address_space(3))) f32x4*)(pl + 8 * j4 + 4 * hh);
+    };
+    // S = Q K^T and dP - D = dO V^T - D of this wave's 32 keys from ring buffer
+    // sb (dP starts at -D)
+    auto sdp = [&](int sb, f32x16& sc, f32x16& dp, const f32x4 (&nd)[4]) {
+      const lds_t* qb = qbuf + sb * QBUF;
+      const lds_t* ob = obuf + sb * QBUF;
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sc[4 * j4 + r] = 0.f;
+          dp[4 * j4 + r] = nd[j4][r];
+        }
+#pragma unroll
+      for (int ss = 0; ss < NS; ++ss) {
+        const int o = swz_off<D>(l32, 2 * ss + hh);
+        const s16x8 qa = lds_read16(qb + o);
+        const s16x8 ga = lds_read16(ob + o);
+        sc = mfma32<T>(qa, kf[ss], sc);
+        dp = mfma32<T>(ga, vf[ss], dp);
+      }
+    };
+    // P and dS (unscaled) of a step into hand-over buffer pb, as the consumer's
+    // B operands: chunk 2 m + u holds slots of MFMA step u (m = 0 P, 1 dS), lane
+    // by lane. Element i is query q0 + 8 (i / 4) + 4 hh + i % 4 of key kj;
+    // under causal masking or a right window it is kept only while
+    // kj - off - wr <= query (the masked variant, for blocks crossing that edge).
+    auto probs = [&](auto masked, const f32x16& sc, const f32x16& dp, int q0, const f32x4 (&lv)[4], int pb) {
+      constexpr bool MASKED = decltype(masked)::value;
+      float pvv[16];
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pvv[4 * j4 + r] = fast_exp2(fmaf(sc[4 * j4 + r], c, -lv[j4][r]));
+      if constexpr (MASKED) {
+        const int thr = kj - offu - q0 - 4 * hh;  // first kept 8 (i / 4) + i % 4
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int o = 8 * (i >> 2) + (i & 3);
+          pvv[i] = o < thr ? 0.f : pvv[i];
+        }
+      }
+      unsigned int pk[8], sk[8];
+#pragma unroll
+      for (int j2 = 0; j2 < 8; ++j2) {
+        pk[j2] = pack2<T>(pvv[2 * j2], pvv[2 * j2 + 1]);
+        sk[j2] = pack2<T>(pvv[2 * j2] * dp[2 * j2], pvv[2 * j2 + 1] * dp[2 * j2 + 1]);
+      }
+      lds_t* pw = psbuf + (pb * 4 + jw) * PSB + lane * 16;
+      lds_write16(pw, __builtin_bit_cast(s16x8, (u32x4){pk[0], pk[1], pk[2], pk[3]}));
+      lds_write16(pw + 1024, __builtin_bit_cast(s16x8, (u32x4){pk[4], pk[5], pk[6], pk[7]}));
+      lds_write16(pw + 2048, __builtin_bit_cast(s16x8, (u32x4){sk[0], sk[1], sk[2], sk[3]}));
+      lds_write16(pw + 3072, __builtin_bit_cast(s16x8, (u32x4){sk[4], sk[5], sk[6], sk[7]}));
+    };
+    const int hb0 = b * s.H + hk * s.G;  // first query head of the group, batch included
+    StepPos cur{0, hb0, hb0 * 2 * a.npad, (unsigned long long)sv.qrow0 * D};
+    StepPos nxt = nsteps > 1 ? advance(cur) : cur;
+    dma_q(cur, 0);
+    dma_q(nxt, 1);
+    dma_wait();
+    __syncthreads();
+    // iteration e: P and dS of step e from (sc, dp), S and dP of step e + 1
+    // into (scn, dpn). phase is RingAt<e % NB> where the caller knows it at
+    // compile time, RingAt<-1> otherwise. Loads are issued on every path
+    // (indices clamped; a redundant block lands in a buffer nobody reads), and
+    // the last iteration's S and dP of a step past the list go unused.
+    auto iter = [&](int e, auto masked, auto phase, const f32x16& sc, const f32x16& dp, f32x16& scn, f32x16& dpn) {
+      constexpr int P = decltype(phase)::value;
+      const int er = P >= 0 ? P : e;  // congruent to e modulo NB
+      const StepPos nn = e + 2 < nsteps ? advance(nxt) : nxt;
+      f32x4 lv[4], nd[4];
+      stats4(er & (NB - 1), 0, lv);
+      stats4((er + 1) & (NB - 1), 1, nd);
+      dma_q(nn, (er + 2) & (NB - 1));
+      sdp((er + 1) & (NB - 1), scn, dpn, nd);
+      probs(masked, sc, dp, (qb_first + cur.qi) * BQ, lv, er & 1);
+      dma_wait();
+      __syncthreads();
+      cur = nxt;
+      nxt = nn;
+    };
+    f32x16 scA, dpA, scB, dpB;
+    {
+      f32x4 nd0[4];
+      stats4(0, 1, nd0);
+      sdp(0, scA, dpA, nd0);
+    }
+    auto b_to_a = [&]() {
+      scA = scB;
+      dpA = dpB;
+    };
+    // the first ndiag steps of each query head's list cross the band's upper
+    // edge (q0 + off + wr < k0 + 127) and take the masked variant
+    int ndiag = 0;
+    if constexpr (BAND) {
+      const int lim = k0 + KV_BKV - 1 - offu;
+      while (ndiag < nq && (qb_first + ndiag) * BQ < lim) ++ndiag;
+    }
+    const std::true_type masked;
+    const std::false_type plain;
+    const RingAt<-1> rt;
+    int e = 0;
+    for (int hg = 0; hg < s.G; ++hg) {
+      for (int t = 0; t < ndiag; ++t, ++e) {
+        iter(e, masked, rt, scA, dpA, scB, dpB);
+        b_to_a();
+      }
+      // unmasked steps: up to three to bring e to a multiple of NB, then four
+      // at a time with the ring position fixed at compile time, then the rest;
+      // pairs alternate the register sets, a single step copies them back
+      int t = ndiag;
+      if ((e & 1) && t < nq) {
+        iter(e, plain, rt, scA, dpA, scB, dpB);
+        b_to_a();
+        ++e;
+        ++t;
+      }
+      if ((e & 2) && t + 1 < nq) {
+        iter(e, plain, rt, scA, dpA, scB, dpB);
+        iter(e + 1, plain, rt, scB, dpB, scA, dpA);
+        e += 2;
+        t += 2;
+      }
+      if ((e & (NB - 1)) == 0) {
+        for (; t + 3 < nq; t += 4, e += 4) {
+          iter(e, plain, RingAt<0>{}, scA, dpA, scB, dpB);
+          iter(e + 1, plain, RingAt<1>{}, scB, dpB, scA, dpA);
+          iter(e + 2, plain, RingAt<2>{}, scA, dpA, scB, dpB);
+          iter(e + 3, plain, RingAt<3>{}, scB, dpB, scA, dpA);
+        }
+      }
+      for (; t + 1 < nq; t += 2, e += 2) {
+        iter(e, plain, rt, scA, dpA, scB, dpB);
+        iter(e + 1, plain, rt, scB, dpB, scA, dpA);
+      }
+      if (t < nq) {
+        iter(e, plain, rt, scA, dpA, scB, dpB);
+        b_to_a();
+        ++e;
+        ++t;
+      }
+    }
+  } else {
+    f32x16 dka[ND], dva[ND];
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        dka[dt][i] = 0.f;
+        dva[dt][i] = 0.f;
+      }
+    // dV^T(d x key) += dO^T(d x q) P(q x key); dK^T += Q^T dS of step e from
+    // its ring buffer and its producer's hand-over buffer. B operand k-slot j
+    // of MFMA step u is query 16 u + 8 (j / 4) + 4 hh + j % 4, matched by the
+    // transposing reads.
+    auto dvdk = [&](int e, auto phase) {
+      constexpr int P = decltype(phase)::value;
+      const int er = P >= 0 ? P : e;
+      const lds_t* qb = qbuf + (er & (NB - 1)) * QBUF;
+      const lds_t* ob = obuf + (er & (NB - 1)) * QBUF;
+      const lds_t* pr = psbuf + ((er & 1) * 4 + jw) * PSB + lane * 16;
+      const s16x8 pop[2] = {lds_read16(pr), lds_read16(pr + 1024)};
+      const s16x8 sop[2] = {lds_read16(pr + 2048), lds_read16(pr + 3072)};
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          // rows 16 u + roff and 8 below it, columns 32 dt + coff .. + 3
+          const int cc = 4 * dt + (coff >> 3), within = 2 * (coff & 7);
+          const int off0 = swz_off<D>(16 * u + roff, cc) + within;
+          const int off1 = swz_off<D>(16 * u + roff + 8, cc) + within;
+          const s16x8 ga = concat(lds_read_tr(ob + off0), lds_read_tr(ob + off1));
+          const s16x8 qa = concat(lds_read_tr(qb + off0), lds_read_tr(qb + off1));
+          dva[dt] = mfma32<T>(ga, pop[u], dva[dt]);
+          dka[dt] = mfma32<T>(qa, sop[u], dka[dt]);
+        }
+    };
+    // as many barriers as the producers: the prologue's, then one per step
+    __syncthreads();
+    if (nsteps > 0) __syncthreads();  // iteration 0: step 0's P and dS
+    // iteration e (1 <= e < nsteps) takes step e - 1 while the producers form step e
+    int e = 1;
+    for (; e + 3 < nsteps; e += 4) {
+      dvdk(e - 1, RingAt<0>{});
+      __syncthreads();
+      dvdk(e, RingAt<1>{});
+      __syncthreads();
+      dvdk(e + 1, RingAt<2>{});
+      __syncthreads();
+      dvdk(e + 2, RingAt<3>{});
+      __syncthreads();
+    }
+    for (; e < nsteps; ++e) {
+      dvdk(e - 1, RingAt<-1>{});
+      __syncthreads();
+    }
+    if (nsteps > 0) dvdk(nsteps - 1, RingAt<-1>{});  // after the producers' last barrier
+
+    // dK^T / dV^T: lane holds key kj, d = 32 dt + 8 j + 4 hh + 0..3; dK takes the scale
+    const float scale = s.scale;
+    const rsrc_t rdk = make_rsrc((unsigned short*)a.dk + krow0 * D, kbytes);
+    const rsrc_t rdv = make_rsrc((unsigned short*)a.dv + krow0 * D, kbytes);
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2 kv = {pack2<T>(dka[dt][4 * j] * scale, dka[dt][4 * j + 1] * scale),
+                    pack2<T>(dka[dt][4 * j + 2] * scale, dka[dt][4 * j + 3] * scale)};
+        u32x2 vv = {pack2<T>(dva[dt][4 * j], dva[dt][4 * j + 1]), pack2<T>(dva[dt][4 * j + 2], dva[dt][4 * j + 3])};
+        const unsigned int o = (unsigned)(kj * D + 32 * dt + 8 * j + 4 * hh) * 2u;
+        bstore8(rdk, o, kv);
+        bstore8(rdv, o, vv);
+      }
+  }
+}
+
 template <class T, int D, int BAND, bool MASK, bool DROP, bool ALIBI>
-__global__ __launch_bounds__(KV_NW * 64, D <= 64 ? 2 : 1) void bwd_kv_kernel(BwdArgs a) {
+__global__ __launch_bounds__((kv_split<D, BAND, MASK, DROP, ALIBI>() ? KS_NW * 64 : KV_NW * 64), D <= 64 ? 2 : 1)
+    void bwd_kv_kernel(BwdArgs a) {
   const GridPos gp = grid_pos(a.s);  // grid: tile_grid over kv heads and key blocks
-  bwd_kv_body<T, D, BAND, MASK, DROP, ALIBI>(a, blockIdx.x, gp.b, gp.blk);
+  if constexpr (kv_split<D, BAND, MASK, DROP, ALIBI>())
+    bwd_kv_split_body<T, D, BAND>(a, blockIdx.x, gp.b, gp.blk);
+  else
+    bwd_kv_body<T, D, BAND, MASK, DROP, ALIBI>(a, blockIdx.x, gp.b, gp.blk);
 }
 
 // ---------------------------------------------------------------------------
@@ -823,13 +1150,22 @@ template <class T, int D, int BAND, bool DROP>
 static hipError_t launch_kv_t3(const BwdArgs& a, hipStream_t st) {
   BwdArgs la = a;
   const dim3 grid = tile_grid(la.s, a.s.Hkv, (a.s.Nk + KV_BKV - 1) / KV_BKV);
-  const dim3 block(KV_NW * 64);
+  // workgroup size: eight waves for the split-role instantiations, else four
+  auto block = [](bool split) { return dim3(split ? KS_NW * 64 : KV_NW * 64); };
   if (a.s.alibi) {
-    if (a.s.mask) hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, true, DROP, true>), grid, block, 0, st, la);
-    else hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, false, DROP, true>), grid, block, 0, st, la);
+    if (a.s.mask)
+      hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, true, DROP, true>), grid,
+                         block(kv_split<D, BAND, true, DROP, true>()), 0, st, la);
+    else
+      hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, false, DROP, true>), grid,
+                         block(kv_split<D, BAND, false, DROP, true>()), 0, st, la);
   } else {
-    if (a.s.mask) hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, true, DROP, false>), grid, block, 0, st, la);
-    else hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, false, DROP, false>), grid, block, 0, st, la);
+    if (a.s.mask)
+      hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, true, DROP, false>), grid,
+                         block(kv_split<D, BAND, true, DROP, false>()), 0, st, la);
+    else
+      hipLaunchKernelGGL((bwd_kv_kernel<T, D, BAND, false, DROP, false>), grid,
+                         block(kv_split<D, BAND, false, DROP, false>()), 0, st, la);
   }
   return hipGetLastError();
 }
