@@ -18,8 +18,10 @@
 //    gfx950 transposing read ds_read_b64_tr_b16, so V needs no transpose pass.
 //  * LDS row pitches are padded so that the 16-byte row reads of K and the
 //    transposing reads of V are free of bank conflicts.
-//  * Long rows at head size 128 run fwd64_kernel (64 query rows per wave,
-//    one wave per SIMD, 256 rows per workgroup); the others,
+//  * Long rows at head size 128 run fwd64_kernel (64 query rows per wave
+//    pair, 256 rows per workgroup: without dropout and a lower band edge as
+//    a producer wave forming the probabilities and a consumer wave holding O
+//    on each SIMD, otherwise as one wave per SIMD); the others,
 //    and all block-sparse inputs, run fwd_kernel (32 rows per wave, two waves
 //    per SIMD, 128 rows per workgroup = one mask block row).
 //  * Causal: a workgroup stops at its diagonal tile, waves skip tiles that lie
@@ -360,39 +362,70 @@ __device__ __forceinline__ void scale_acc(f32x16& x, float s) {
 // last tile follow in a plain loop with element masks and lazy rescaling,
 // which also takes over the whole workgroup in the rare case that a later
 // score outgrows the fixed reference.
-constexpr int F64_NW = 4;                 // waves per workgroup
+constexpr int F64_NW = 4;                 // waves per workgroup (wave pairs in the split-role form)
 constexpr int F64_RW = 64;                // query rows per wave
 constexpr int F64_BM = F64_NW * F64_RW;   // query rows per workgroup
 constexpr int F64_BN = 32;                // keys per tile
 constexpr int F64_NB = 4;                 // LDS ring slots
 
-template <class T, int D, int BAND, bool DROP>
-__global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
+// The same rows and tiles with split roles (d = 128 without dropout; causal,
+// dense or an upper band edge): eight waves, two per SIMD. Producer wave j
+// (0..3) holds Q^T of rows q0 + 64 j .. + 63 and forms S^T and the
+// probabilities; it hands P^T, as the consumer's MFMA B operands, through one
+// of two LDS buffers to consumer wave j + 4 on the same SIMD, which holds the
+// O^T accumulators and adds V^T P^T one tile behind. Each role fits in half
+// the register file, so the producer's softmax arithmetic runs while the
+// consumer's products occupy the matrix unit. Main loop (the tiles every row
+// sees in full, fixed reference): iteration j forms S of tile j + 1 and P of
+// tile j on the producer side, in slots of one MFMA and two probability
+// elements each (fenced order: the compiler's own order put the products of
+// a tile ahead of all its exponentials, which left the producer waiting on
+// the matrix unit the consumer shares), and P V of tile j - 1 on the consumer
+// side; all eight waves stage tile j + 2 and meet at one barrier. The general
+// loop (diagonal and ragged tiles, or a restart) raises the reference lazily:
+// the producer then also hands over, per tile, whether its rows see the tile
+// and whether the reference rose, with the per-row factors exp(m_old - m_new)
+// by which the consumer scales O first. Finally the producer writes the
+// log-sum-exp and hands 1 / l to the consumer, which writes O.
+template <int D, int BAND, bool DROP>
+constexpr bool f64_split() {
+  return D == 128 && BAND <= 1 && !DROP;
+}
+
+template <class T, int D, int BAND>
+__device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
   constexpr int KP = D * 2 + 16;  // K row pitch (bytes): conflict-free 16-byte row reads
   constexpr int VP = D * 2 + 32;  // V row pitch (bytes): conflict-free transposing reads
   constexpr int KBUF = F64_BN * KP;
   constexpr int VBUF = F64_BN * VP;
-  constexpr int NT = F64_NW * 64;
+  constexpr int NT = 2 * F64_NW * 64;  // every wave stages tiles
   constexpr int CH = D / 8;
-  constexpr int TCH = F64_BN * CH;            // 16-byte chunks per tile per tensor
+  constexpr int TCH = F64_BN * CH;  // 16-byte chunks per tile per tensor
   constexpr int PER = (TCH + NT - 1) / NT;
   static_assert(TCH % NT == 0 || TCH < NT, "tile loader shape");
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
-  constexpr float kSlack = (std::is_same<T, F16>::value && DROP) ? 7.f : 8.f;  // as in fwd_kernel
-
-  __shared__ __attribute__((aligned(16))) char smem_raw[F64_NB * (KBUF + VBUF)];
+  constexpr float kSlack = 8.f;  // as in fwd_kernel
+  // one pair's hand-over buffer: P^T (four 16-byte chunks per lane, chunk
+  // 2 rb + u holding the B operand of MFMA step u of row block rb), then the
+  // 64 rows' rescale factors, then the flags (bit 0: the pair's rows see the
+  // tile, bit 1: the reference rose)
+  constexpr int HB = 4096 + 256 + 16;
+  __shared__ __attribute__((aligned(16))) char smem_raw[F64_NB * (KBUF + VBUF) + 2 * F64_NW * HB + F64_NW * 256];
   lds_t* kbuf = (lds_t*)smem_raw;
   lds_t* vbuf = kbuf + F64_NB * KBUF;
+  lds_t* hbuf = vbuf + F64_NB * VBUF;    // [2][pairs][HB]
+  lds_t* ibuf = hbuf + 2 * F64_NW * HB;  // [pairs][64 rows] final 1 / l
 
   const AttnShape& s = a.s;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);  // the wave index as a scalar
+  const bool producer = wu < F64_NW;
+  const int pw = wu & (F64_NW - 1);  // the pair: rows q0 + 64 pw .. + 63
   const int l32 = lane & 31, hh = lane >> 5;
   const int g16 = lane >> 4;
   const int roff = 4 * (g16 >> 1) + ((lane & 15) >> 2);
   const int coff = 16 * (g16 & 1) + 4 * (lane & 3);
-  // grid (tile_grid): heads fastest; under a band mask the later (under causal
-  // masking, longer) query blocks are dispatched first
   const GridPos gp = grid_pos(s);
   const int qb = BAND ? gp.nblk - 1 - gp.blk : gp.blk;
   const int h = query_head(s, blockIdx.x), b = gp.b;
@@ -403,68 +436,26 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
   if (q0 >= nq) return;  // a sequence shorter than the grid (packed batches)
   const size_t qrow0 = sv.qrow0, krow0 = sv.krow0;
   const unsigned int qbytes = (unsigned int)nq * D * 2, kbytes = (unsigned int)nk * D * 2;
-  const rsrc_t rq = make_rsrc((const unsigned short*)a.q + qrow0 * D, qbytes);
   const rsrc_t rk = make_rsrc((const unsigned short*)a.k + krow0 * D, kbytes);
   const rsrc_t rv = make_rsrc((const unsigned short*)a.v + krow0 * D, kbytes);
-  const int qw = q0 + F64_RW * w;  // first query row of this wave; block rb holds rows qw + 32 rb + 0..31
+  const int qw = q0 + F64_RW * pw;  // block rb of the pair holds rows qw + 32 rb + 0..31
   const float c = fmaxf(s.scale * kLog2e, 1e-30f);
-
-  // tiles [tbeg, tbeg + ntiles) hold every key some row of the workgroup sees
-  // (row q0's band starts lowest, the last row's ends highest); tiles
-  // [fbeg, fend) hold only keys that every row sees (the last row's band starts
-  // highest, row q0's ends lowest)
-  // (band: row i sees keys i + offl .. i + offu; offl binds only with a lower edge)
-  constexpr bool LOWER = BAND == 2;
-  const int offu = off + s.wr, offl = off - s.wl;
-  const int kbeg = LOWER ? max(0, q0 + offl) : 0;
+  // tiles [0, ntiles) hold every key some row of the workgroup sees, tiles
+  // [0, nfull) only keys that every row sees (row i sees keys up to i + off + wr)
+  const int offu = off + s.wr;
   const int kend = BAND ? min(nk, max(0, q0 + F64_BM + offu)) : nk;
-  const int tbeg = kbeg / F64_BN;
-  const int ntiles = max(0, (kend + F64_BN - 1) / F64_BN - tbeg);
-  // (clamped to the tile range: padding rows past the sequence can put the
-  // last row's band start beyond the last key)
-  const int fbeg =
-      LOWER ? min(tbeg + ntiles, max(tbeg, (max(0, q0 + F64_BM - 1 + offl) + F64_BN - 1) / F64_BN)) : 0;
-  const int fend = BAND ? max(fbeg, min(max(0, q0 + offu + 1) / F64_BN, nk / F64_BN)) : nk / F64_BN;
-  const int nfull = fend - fbeg;
-  // processing order e = 0, 1, ...: the full tiles, then the partial tiles
-  // above them (together the run fbeg, fbeg + 1, ...), then those below (the
-  // result does not depend on the order); without a lower edge the order is
-  // simply the tile index
-  const int nhead = tbeg + ntiles - fbeg;
-  auto tile_of = [&](int e) -> int {
-    if constexpr (LOWER) return e < nhead ? fbeg + e : tbeg + (e - nhead);
-    else return e;
-  };
-
-  // Q^T operands of both row blocks: lane holds query qw + 32 rb + l32, d = 16 ss + 8 hh + 0..7
-  s16x8 qf[2][NS];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int ss = 0; ss < NS; ++ss)
-      qf[rb][ss] = bload16(rq, (unsigned)((qw + 32 * rb + l32) * D + 16 * ss + 8 * hh) * 2u);
-
-  f32x16 acc[2][ND];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[rb][dt][i] = 0.f;
-  // running reference m (log2 units) and this lane's half of the running sum,
-  // per row block, raised lazily as in the 32-row kernel
-  float m[2] = {-INFINITY, -INFINITY};
-  float l[2] = {0.f, 0.f};
+  const int ntiles = max(0, (kend + F64_BN - 1) / F64_BN);
+  const int nfull = BAND ? max(0, min(max(0, q0 + offu + 1) / F64_BN, nk / F64_BN)) : nk / F64_BN;
 
   s16x8 kreg[PER], vreg[PER];
   auto gload = [&](int t) {
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
-      const int ci = min(tid + r * NT, TCH - 1);  // spare threads repeat the last chunk
+      const int ci = min(tid + r * NT, TCH - 1);
       const int row = ci / CH, col = (ci % CH) * 8;
-      const unsigned int off = (unsigned)((t * F64_BN + row) * D + col) * 2u;
-      kreg[r] = bload16(rk, off);
-      vreg[r] = bload16(rv, off);
+      const unsigned int o = (unsigned)((t * F64_BN + row) * D + col) * 2u;
+      kreg[r] = bload16(rk, o);
+      vreg[r] = bload16(rv, o);
     }
   };
   auto lstore = [&](int slot) {
@@ -476,308 +467,701 @@ __global__ __launch_bounds__(F64_NW * 64, 1) void fwd64_kernel(FwdArgs a) {
       lds_write16(vbuf + slot * VBUF + row * VP + col * 2, vreg[r]);
     }
   };
-  // S^T = K Q^T of the tile in a slot; st[rb][i] is S of query qw + 32 rb + l32
-  // and key 8 (i / 4) + 4 hh + i % 4 of the tile
-  auto s_tile = [&](int slot, f32x16 (&st)[2]) {
-    const lds_t* kb = kbuf + slot * KBUF + l32 * KP + 16 * hh;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      st[0][i] = 0.f;
-      st[1][i] = 0.f;
-    }
-#pragma unroll
-    for (int ss = 0; ss < NS; ++ss) {
-      const s16x8 ka = lds_read16(kb + 32 * ss);
-      st[0] = mfma32<T>(ka, qf[0][ss], st[0]);
-      st[1] = mfma32<T>(ka, qf[1][ss], st[1]);
-    }
-  };
-  // O^T += V^T P^T for the tile in a slot; B operand k-slot j of step u is key
-  // 16 u + 8 (j / 4) + 4 hh + j % 4, matched by the transposing reads of V
-  auto pv_tile = [&](int slot, const unsigned int (&pk)[2][8]) {
-    const lds_t* vb = vbuf + slot * VBUF;
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const lds_t* vp = vb + (16 * u + roff) * VP + (32 * dt + coff) * 2;
-        const s16x8 va = concat(lds_read_tr(vp), lds_read_tr(vp + 8 * VP));
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-          acc[rb][dt] = mfma32<T>(va, as_operand(pk[rb][4 * u], pk[rb][4 * u + 1], pk[rb][4 * u + 2],
-                                                 pk[rb][4 * u + 3]),
-                                  acc[rb][dt]);
-      }
-  };
-  // Softmax of one tile against the running reference: returns whether the
-  // reference rises (wave-uniform), with the new reference in mn, the 16-bit
-  // probabilities in pk and this lane's share of their row sums in ls.
-  // 16-bit probabilities of elements 2 jj, 2 jj + 1 of row block rb, with dropout
-  // when built for it (keys ks + 8 (jj / 2) + 4 hh + (2 jj & 3) + 0, 1)
-  // (dw: this row's dropout words for key groups ks + 8 g + 4 hh, g = 0..3,
-  // from drop_words_row4)
-  auto pack_p = [&](float p0, float p1, int jj, const unsigned int (&dw)[4]) -> unsigned int {
-    if constexpr (DROP) {
-      const unsigned int wd = dw[jj >> 1];
-      const int t0 = (2 * jj) & 3;
-      return pack2<T>(drop_keep(wd, t0, s.drop_t) ? p0 * s.drop_scale : 0.f,
-                      drop_keep(wd, t0 + 1, s.drop_t) ? p1 * s.drop_scale : 0.f);
-    } else {
-      return pack2<T>(p0, p1);
-    }
-  };
-  auto softmax = [&](const f32x16 (&st)[2], float (&mn)[2], unsigned int (&pk)[2][8], float (&ls)[2], int ks) {
-    float mx[2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      float x = st[rb][0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) x = fmaxf(x, st[rb][i]);
-      mx[rb] = fmaxf(x, swap_halves(x)) * c;
-    }
-    const bool resc = __any(mx[0] > m[0] + kSlack || mx[1] > m[1] + kSlack);
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      mn[rb] = resc ? fmaxf(m[rb], mx[rb]) : m[rb];
-      const float mu = mn[rb] == -INFINITY ? 0.f : mn[rb];  // a row with no visible key yet
-      float sum = 0.f;
-      unsigned int dw[4];
-      if constexpr (DROP) drop_words_row4(s.seed0, s.seed1, b * s.H + h, qw + 32 * rb + l32, ks + 4 * hh, 8, dw);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p0 = fast_exp2(fmaf(st[rb][2 * j], c, -mu));
-        const float p1 = fast_exp2(fmaf(st[rb][2 * j + 1], c, -mu));
-        sum += p0 + p1;
-        pk[rb][j] = pack_p(p0, p1, j, dw);
-      }
-      ls[rb] = sum;
-    }
-    return resc;
-  };
-  // fold a tile's statistics into the running ones; when the reference rose,
-  // scale the output and the sum by exp(m_old - m_new) first
-  auto update = [&](bool resc, const float (&mn)[2], const float (&ls)[2]) {
-    if (resc) {
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const float corr = fast_exp2(m[rb] - (mn[rb] == -INFINITY ? 0.f : mn[rb]));
-        l[rb] *= corr;
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt) scale_acc(acc[rb][dt], corr);
-      }
-    }
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      l[rb] += ls[rb];
-      m[rb] = mn[rb];
-    }
-  };
+  auto hand = [&](int buf) -> lds_t* { return hbuf + (buf * F64_NW + pw) * HB; };
 
-  // Prologue: tiles 0 and 1 in slots 0 and 1; the V half of slot 3 is zeroed
-  // because the first iteration multiplies it with zero probabilities.
-  for (int i = tid; i < VBUF / 16; i += NT)
-    lds_write16(vbuf + (F64_NB - 1) * VBUF + i * 16, (s16x8){0, 0, 0, 0, 0, 0, 0, 0});
-  gload(tile_of(0));
+  // Every wave takes the same sequence of barriers: the prologue's, one per
+  // main-loop tile, the restart vote, one per general-loop tile, the final one.
+  gload(0);
   lstore(0);
-  gload(tile_of(max(0, min(1, ntiles - 1))));
+  gload(max(0, min(1, ntiles - 1)));
   lstore(1);
   __syncthreads();
 
-  // Main loop over the tiles that every row sees in full. The reference m is
-  // fixed at the first tile's row maximum, so the loop never rescales and has
-  // no branch: probabilities relative to that reference stay finite while no
-  // later score exceeds it by more than about 120 in log2 units, and the result
-  // O / l, m + log2(l) does not depend on the reference chosen. Should a row's
-  // sum end above 2^60 (some later score at least 60 above the first tile's
-  // maximum), the whole workgroup starts over in the general loop below, which
-  // raises the reference as it goes. With float16 the 16-bit probabilities
-  // have the tighter bound: the restart comes once a row sum exceeds 65504
-  // divided by the dropout keep scale, which every probability (so scaled)
-  // beyond float16's range implies, since the sum holds each probability.
+  // restart bound of the fixed-reference loop, as in the one-role form below
+  const float lmax = std::is_same<T, F16>::value ? 65504.f : 0x1p60f;
   int j = 0;
-  if (nfull > 0) {
-    auto probs = [&](const f32x16 (&st)[2], unsigned int (&pk)[2][8], int ks) {
+  if (producer) {
+    const rsrc_t rq = make_rsrc((const unsigned short*)a.q + qrow0 * D, qbytes);
+    s16x8 qf[2][NS];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        float sum = 0.f;
-        unsigned int dw[4];
-        if constexpr (DROP) drop_words_row4(s.seed0, s.seed1, b * s.H + h, qw + 32 * rb + l32, ks + 4 * hh, 8, dw);
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const float p0 = fast_exp2(fmaf(st[rb][2 * jj], c, -m[rb]));
-          const float p1 = fast_exp2(fmaf(st[rb][2 * jj + 1], c, -m[rb]));
-          sum += p0 + p1;
-          pk[rb][jj] = pack_p(p0, p1, jj, dw);
-        }
-        l[rb] += sum;
+      for (int ss = 0; ss < NS; ++ss)
+        qf[rb][ss] = bload16(rq, (unsigned)((qw + 32 * rb + l32) * D + 16 * ss + 8 * hh) * 2u);
+    // running reference m (log2 units) and this lane's half of the running sum, per row block
+    float m[2] = {-INFINITY, -INFINITY};
+    float l[2] = {0.f, 0.f};
+    // S^T = K Q^T of the tile in a slot: st[rb][i] is S of query qw + 32 rb + l32
+    // and key 8 (i / 4) + 4 hh + i % 4 of the tile
+    auto s_tile = [&](int slot, f32x16 (&st)[2]) {
+      const lds_t* kb = kbuf + slot * KBUF + l32 * KP + 16 * hh;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        st[0][i] = 0.f;
+        st[1][i] = 0.f;
+      }
+#pragma unroll
+      for (int ss = 0; ss < NS; ++ss) {
+        const s16x8 ka = lds_read16(kb + 32 * ss);
+        st[0] = mfma32<T>(ka, qf[0][ss], st[0]);
+        st[1] = mfma32<T>(ka, qf[1][ss], st[1]);
       }
     };
-    // one iteration: S of tile jj + 1, probabilities of tile jj, P V of tile
-    // jj - 1 (mutually independent), then tile jj + 2 into the slot of tile
-    // jj - 2. Loads are issued on every path (tile index clamped; a redundant
-    // copy lands in a slot nobody reads). Without dropout the iteration is laid
-    // out in slots of one MFMA each, products of S and of P V alternating, with
-    // the probabilities of the current tile spread over the slots (one element,
-    // or a few at small head sizes, per slot) and the K and V^T fragments read
-    // two fragment groups ahead; scheduling fences keep that order, which the
-    // compiler's own schedule (MFMAs in runs, the exponentials and sums bunched
-    // between them) ran 4% slower at N = 16384, d = 128.
-    auto iter = [&](int jj, const f32x16 (&scur)[2], f32x16 (&snext)[2], const unsigned int (&pprev)[2][8],
-                    unsigned int (&pcur)[2][8]) {
-      gload(tile_of(min(jj + 2, ntiles - 1)));
-      if constexpr (DROP) {
-        s_tile((jj + 1) & (F64_NB - 1), snext);
-        probs(scur, pcur, (fbeg + jj) * F64_BN);
-        pv_tile((jj + F64_NB - 1) & (F64_NB - 1), pprev);
-      } else {
+    auto write_p = [&](lds_t* hb, const unsigned int (&pk)[2][8]) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          lds_write16(hb + (2 * rb + u) * 1024 + lane * 16,
+                      __builtin_bit_cast(s16x8, (u32x4){pk[rb][4 * u], pk[rb][4 * u + 1], pk[rb][4 * u + 2],
+                                                        pk[rb][4 * u + 3]}));
+    };
+    if (nfull > 0) {
+      // one iteration in slots: S product t of the next tile, then elements
+      // 2 t and 2 t + 1 of the current tile's probabilities (fenced order)
+      auto iter = [&](int jj, const f32x16 (&scur)[2], f32x16 (&snext)[2]) {
+        gload(min(jj + 2, ntiles - 1));
         const lds_t* kb = kbuf + ((jj + 1) & (F64_NB - 1)) * KBUF + l32 * KP + 16 * hh;
-        const lds_t* vb = vbuf + ((jj + F64_NB - 1) & (F64_NB - 1)) * VBUF;
-        auto vread = [&](int g) {
-          const lds_t* vp = vb + (16 * (g & 1) + roff) * VP + (32 * (g >> 1) + coff) * 2;
-          return concat(lds_read_tr(vp), lds_read_tr(vp + 8 * VP));
-        };
-        constexpr int NG = NS;          // fragment groups: K fragment g and V^T fragment g
-        constexpr int NSLOT = 4 * NG;   // MFMAs: 2 NS products of S, 4 ND = 2 NS of P V
-        constexpr int EPS = 32 / NSLOT; // softmax elements per slot
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           snext[0][i] = 0.f;
           snext[1][i] = 0.f;
         }
-        s16x8 ka[NG], va[NG];
-        ka[0] = lds_read16(kb);
-        va[0] = vread(0);
-        if constexpr (NG > 1) {
-          ka[1] = lds_read16(kb + 32);
-          va[1] = vread(1);
-        }
+        s16x8 ka[NS];
+#pragma unroll
+        for (int ss = 0; ss < NS; ++ss) ka[ss] = lds_read16(kb + 32 * ss);
+        unsigned int pk[2][8];
         float sum[2] = {0.f, 0.f};
-        float pe = 0.f;
 #pragma unroll
-        for (int t = 0; t < NSLOT; ++t) {
+        for (int t = 0; t < 2 * NS; ++t) {
           __builtin_amdgcn_sched_barrier(0);
-          const int g = t >> 2;
-          if ((t & 3) == 0 && g + 2 < NG) {
-            ka[g + 2] = lds_read16(kb + 32 * (g + 2));
-            va[g + 2] = vread(g + 2);
-          }
-          if ((t & 1) == 0) {
-            const int n = t >> 1, rb = n & 1;
-            snext[rb] = mfma32<T>(ka[n >> 1], qf[rb][n >> 1], snext[rb]);
-          } else {
-            const int n = t >> 1, rb = n & 1, pg = n >> 1, u = pg & 1;
-            acc[rb][pg >> 1] = mfma32<T>(va[pg], as_operand(pprev[rb][4 * u], pprev[rb][4 * u + 1],
-                                                            pprev[rb][4 * u + 2], pprev[rb][4 * u + 3]),
-                                         acc[rb][pg >> 1]);
-          }
-#pragma unroll
-          for (int x = 0; x < EPS; ++x) {
-            const int e = t * EPS + x, rb = e >> 4, i = e & 15;
-            const float p = fast_exp2(fmaf(scur[rb][i], c, -m[rb]));
-            if (i & 1) {
-              sum[rb] += pe + p;
-              pcur[rb][i >> 1] = pack2<T>(pe, p);
-            } else {
-              pe = p;
-            }
-          }
+          const int rb = t & 1, ss = t >> 1;
+          snext[rb] = mfma32<T>(ka[ss], qf[rb][ss], snext[rb]);
+          const int e = 2 * t, rbe = e >> 4, i = e & 15;
+          const float p0 = fast_exp2(fmaf(scur[rbe][i], c, -m[rbe]));
+          const float p1 = fast_exp2(fmaf(scur[rbe][i + 1], c, -m[rbe]));
+          sum[rbe] += p0 + p1;
+          pk[rbe][i >> 1] = pack2<T>(p0, p1);
         }
         __builtin_amdgcn_sched_barrier(0);
         l[0] += sum[0];
         l[1] += sum[1];
+        write_p(hand(jj & 1), pk);
+        lstore((jj + 2) & (F64_NB - 1));
+        __syncthreads();
+      };
+      // the reference: the first tile's row maximum
+      f32x16 sa[2], sb[2];
+      s_tile(0, sa);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float x = sa[rb][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) x = fmaxf(x, sa[rb][i]);
+        m[rb] = fmaxf(x, swap_halves(x)) * c;
       }
-      lstore((jj + 2) & (F64_NB - 1));
+      for (; j + 1 < nfull; j += 2) {
+        iter(j, sa, sb);
+        iter(j + 1, sb, sa);
+      }
+      if (j < nfull) {
+        iter(j, sa, sb);
+        ++j;
+      }
+      // workgroup-wide vote (the consumers vote no): start over in the general loop
+      if (__syncthreads_or(l[0] > lmax || l[1] > lmax)) {
+        j = 0;
+        m[0] = m[1] = -INFINITY;
+        l[0] = l[1] = 0.f;
+        gload(0);
+        lstore(0);
+        gload(max(0, min(1, ntiles - 1)));
+        lstore(1);
+        __syncthreads();
+      }
+    }
+    // general loop: element masks, lazy rescaling; a pair whose rows see no key of the tile skips it
+    for (; j < ntiles; ++j) {
+      gload(min(j + 2, ntiles - 1));
+      const int ks = j * F64_BN;
+      lds_t* hb = hand(j & 1);
+      const bool act = !BAND || ks <= qw + F64_RW - 1 + offu;
+      bool resc = false;
+      if (act) {
+        f32x16 st[2];
+        s_tile(j & (F64_NB - 1), st);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const int qi = qw + 32 * rb + l32;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = ks + 8 * (i >> 2) + 4 * hh + (i & 3);
+            if ((BAND && key > qi + offu) || key >= nk) st[rb][i] = -INFINITY;
+          }
+        }
+        float mx[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          float x = st[rb][0];
+#pragma unroll
+          for (int i = 1; i < 16; ++i) x = fmaxf(x, st[rb][i]);
+          mx[rb] = fmaxf(x, swap_halves(x)) * c;
+        }
+        resc = __any(mx[0] > m[0] + kSlack || mx[1] > m[1] + kSlack);
+        unsigned int pk[2][8];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const float mn = resc ? fmaxf(m[rb], mx[rb]) : m[rb];
+          const float mu = mn == -INFINITY ? 0.f : mn;
+          float sum = 0.f;
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            const float p0 = fast_exp2(fmaf(st[rb][2 * jj], c, -mu));
+            const float p1 = fast_exp2(fmaf(st[rb][2 * jj + 1], c, -mu));
+            sum += p0 + p1;
+            pk[rb][jj] = pack2<T>(p0, p1);
+          }
+          if (resc) {
+            const float corr = fast_exp2(m[rb] - mu);
+            l[rb] *= corr;
+            if (hh == 0) *(__attribute__((address_space(3))) float*)(hb + 4096 + (32 * rb + l32) * 4) = corr;
+          }
+          l[rb] += sum;
+          m[rb] = mn;
+        }
+        write_p(hb, pk);
+      }
+      if (lane == 0) *(__attribute__((address_space(3))) int*)(hb + 4096 + 256) = (act ? 1 : 0) | (resc ? 2 : 0);
+      lstore((j + 2) & (F64_NB - 1));
       __syncthreads();
-    };
-    f32x16 sa[2], sb[2];
-    unsigned int pa[2][8], pb[2][8];
-    s_tile(0, sa);
+    }
+    // 1 / l per row for the consumer; the log-sum-exp from here
+    const rsrc_t rl = make_rsrc(a.lse + qrow0, (unsigned)nq * 4u);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      float x = sa[rb][0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) x = fmaxf(x, sa[rb][i]);
-      m[rb] = fmaxf(x, swap_halves(x)) * c;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) pb[rb][jj] = 0u;
-    }
-    for (; j + 1 < nfull; j += 2) {
-      iter(j, sa, sb, pb, pa);
-      iter(j + 1, sb, sa, pa, pb);
-    }
-    if (j < nfull) {
-      iter(j, sa, sb, pb, pa);
-      pv_tile(j & (F64_NB - 1), pa);
-      ++j;
-    } else {
-      pv_tile((nfull - 1) & (F64_NB - 1), pb);
-    }
-    // workgroup-uniform decision (it also orders the reads above before any
-    // slot is refilled)
-    const float lmax = std::is_same<T, F16>::value ? 65504.f / (DROP ? s.drop_scale : 1.f) : 0x1p60f;
-    if (__syncthreads_or(l[0] > lmax || l[1] > lmax)) {
-      j = 0;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        m[rb] = -INFINITY;
-        l[rb] = 0.f;
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[rb][dt][i] = 0.f;
+      const int qi = qw + 32 * rb + l32;
+      const float lt = l[rb] + swap_halves(l[rb]);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float lse = lt > 0.f ? (m[rb] + fast_log2(lt)) * kLn2 : -INFINITY;
+      if (hh == 0) {
+        *(__attribute__((address_space(3))) float*)(ibuf + pw * 256 + (32 * rb + l32) * 4) = inv;
+        bstore_f32(rl, (unsigned)qi * 4u, lse);
       }
-      gload(tile_of(0));
-      lstore(0);
-      gload(tile_of(max(0, min(1, ntiles - 1))));
-      lstore(1);
+    }
+    __syncthreads();
+  } else {
+    f32x16 acc[2][ND];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[rb][dt][i] = 0.f;
+    // O^T += V^T P^T of the tile in a slot with P from a hand-over buffer
+    auto pv = [&](int slot, const lds_t* hb) {
+      s16x8 pop[2][2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) pop[rb][u] = lds_read16(hb + (2 * rb + u) * 1024 + lane * 16);
+      const lds_t* vb = vbuf + slot * VBUF;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const lds_t* vp = vb + (16 * u + roff) * VP + (32 * dt + coff) * 2;
+          const s16x8 va = concat(lds_read_tr(vp), lds_read_tr(vp + 8 * VP));
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) acc[rb][dt] = mfma32<T>(va, pop[rb][u], acc[rb][dt]);
+        }
+    };
+    // a general-loop tile: its flags, the rescale when the reference rose, then P V
+    auto consume = [&](int t) {
+      const lds_t* hb = hand(t & 1);
+      const int fl = __builtin_amdgcn_readfirstlane(*(const __attribute__((address_space(3))) int*)(hb + 4096 + 256));
+      if (fl & 1) {
+        if (fl & 2) {
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            const float corr = *(const __attribute__((address_space(3))) float*)(hb + 4096 + (32 * rb + l32) * 4);
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) acc[rb][dt][i] *= corr;
+          }
+        }
+        pv(t & (F64_NB - 1), hb);
+      }
+    };
+    if (nfull > 0) {
+      // main loop: iteration j takes P V of tile j - 1 (fixed reference: no rescale)
+      for (; j < nfull; ++j) {
+        gload(min(j + 2, ntiles - 1));
+        if (j > 0) pv((j - 1) & (F64_NB - 1), hand((j - 1) & 1));
+        lstore((j + 2) & (F64_NB - 1));
+        __syncthreads();
+      }
+      pv((nfull - 1) & (F64_NB - 1), hand((nfull - 1) & 1));
+      if (__syncthreads_or(0)) {
+        j = 0;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[rb][dt][i] = 0.f;
+        gload(0);
+        lstore(0);
+        gload(max(0, min(1, ntiles - 1)));
+        lstore(1);
+        __syncthreads();
+      }
+    }
+    // general loop: iteration j takes tile j - 1, the last tile follows the last barrier
+    const int j0 = j;
+    for (; j < ntiles; ++j) {
+      gload(min(j + 2, ntiles - 1));
+      if (j > j0) consume(j - 1);
+      lstore((j + 2) & (F64_NB - 1));
       __syncthreads();
     }
+    if (ntiles > j0) consume(ntiles - 1);
+    __syncthreads();
+    const rsrc_t ro = make_rsrc((unsigned short*)a.o + qrow0 * D, qbytes);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int qi = qw + 32 * rb + l32;
+      const float inv = *(const __attribute__((address_space(3))) float*)(ibuf + pw * 256 + (32 * rb + l32) * 4);
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          u32x2 v2 = {pack2<T>(acc[rb][dt][4 * jj] * inv, acc[rb][dt][4 * jj + 1] * inv),
+                      pack2<T>(acc[rb][dt][4 * jj + 2] * inv, acc[rb][dt][4 * jj + 3] * inv)};
+          bstore8(ro, (unsigned)(qi * D + 32 * dt + 8 * jj + 4 * hh) * 2u, v2);
+        }
+    }
   }
+}
 
-  // general loop (diagonal and ragged tiles, or a restart): element masks,
-  // lazy rescaling, waves without a visible key skip the tile
-  for (; j < ntiles; ++j) {
-    gload(tile_of(min(j + 2, ntiles - 1)));
-    const int ks = tile_of(j) * F64_BN;
-    if ((!BAND || ks <= qw + F64_RW - 1 + offu) && (!LOWER || ks + F64_BN - 1 >= qw + offl)) {
-      f32x16 st[2];
-      s_tile(j & (F64_NB - 1), st);
+template <class T, int D, int BAND, bool DROP>
+__global__ __launch_bounds__((f64_split<D, BAND, DROP>() ? 2 * F64_NW * 64 : F64_NW * 64), 1)
+    void fwd64_kernel(FwdArgs a) {
+  if constexpr (f64_split<D, BAND, DROP>()) {
+    fwd64_split_body<T, D, BAND>(a);
+    return;
+  } else {
+    constexpr int KP = D * 2 + 16;  // K row pitch (bytes): conflict-free 16-byte row reads
+    constexpr int VP = D * 2 + 32;  // V row pitch (bytes): conflict-free transposing reads
+    constexpr int KBUF = F64_BN * KP;
+    constexpr int VBUF = F64_BN * VP;
+    constexpr int NT = F64_NW * 64;
+    constexpr int CH = D / 8;
+    constexpr int TCH = F64_BN * CH;            // 16-byte chunks per tile per tensor
+    constexpr int PER = (TCH + NT - 1) / NT;
+    static_assert(TCH % NT == 0 || TCH < NT, "tile loader shape");
+    constexpr int NS = D / 16;
+    constexpr int ND = D / 32;
+    constexpr float kSlack = (std::is_same<T, F16>::value && DROP) ? 7.f : 8.f;  // as in fwd_kernel
+
+    __shared__ __attribute__((aligned(16))) char smem_raw[F64_NB * (KBUF + VBUF)];
+    lds_t* kbuf = (lds_t*)smem_raw;
+    lds_t* vbuf = kbuf + F64_NB * KBUF;
+
+    const AttnShape& s = a.s;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int g16 = lane >> 4;
+    const int roff = 4 * (g16 >> 1) + ((lane & 15) >> 2);
+    const int coff = 16 * (g16 & 1) + 4 * (lane & 3);
+    // grid (tile_grid): heads fastest; under a band mask the later (under causal
+    // masking, longer) query blocks are dispatched first
+    const GridPos gp = grid_pos(s);
+    const int qb = BAND ? gp.nblk - 1 - gp.blk : gp.blk;
+    const int h = query_head(s, blockIdx.x), b = gp.b;
+    const int hk = h / s.G;
+    const SeqView sv = seq_view(s, b, h, hk);
+    const int nq = sv.nq, nk = sv.nk, off = sv.off;
+    const int q0 = qb * F64_BM;
+    if (q0 >= nq) return;  // a sequence shorter than the grid (packed batches)
+    const size_t qrow0 = sv.qrow0, krow0 = sv.krow0;
+    const unsigned int qbytes = (unsigned int)nq * D * 2, kbytes = (unsigned int)nk * D * 2;
+    const rsrc_t rq = make_rsrc((const unsigned short*)a.q + qrow0 * D, qbytes);
+    const rsrc_t rk = make_rsrc((const unsigned short*)a.k + krow0 * D, kbytes);
+    const rsrc_t rv = make_rsrc((const unsigned short*)a.v + krow0 * D, kbytes);
+    const int qw = q0 + F64_RW * w;  // first query row of this wave; block rb holds rows qw + 32 rb + 0..31
+    const float c = fmaxf(s.scale * kLog2e, 1e-30f);
+
+    // tiles [tbeg, tbeg + ntiles) hold every key some row of the workgroup sees
+    // (row q0's band starts lowest, the last row's ends highest); tiles
+    // [fbeg, fend) hold only keys that every row sees (the last row's band starts
+    // highest, row q0's ends lowest)
+    // (band: row i sees keys i + offl .. i + offu; offl binds only with a lower edge)
+    constexpr bool LOWER = BAND == 2;
+    const int offu = off + s.wr, offl = off - s.wl;
+    const int kbeg = LOWER ? max(0, q0 + offl) : 0;
+    const int kend = BAND ? min(nk, max(0, q0 + F64_BM + offu)) : nk;
+    const int tbeg = kbeg / F64_BN;
+    const int ntiles = max(0, (kend + F64_BN - 1) / F64_BN - tbeg);
+    // (clamped to the tile range: padding rows past the sequence can put the
+    // last row's band start beyond the last key)
+    const int fbeg =
+        LOWER ? min(tbeg + ntiles, max(tbeg, (max(0, q0 + F64_BM - 1 + offl) + F64_BN - 1) / F64_BN)) : 0;
+    const int fend = BAND ? max(fbeg, min(max(0, q0 + offu + 1) / F64_BN, nk / F64_BN)) : nk / F64_BN;
+    const int nfull = fend - fbeg;
+    // processing order e = 0, 1, ...: the full tiles, then the partial tiles
+    // above them (together the run fbeg, fbeg + 1, ...), then those below (the
+    // result does not depend on the order); without a lower edge the order is
+    // simply the tile index
+    const int nhead = tbeg + ntiles - fbeg;
+    auto tile_of = [&](int e) -> int {
+      if constexpr (LOWER) return e < nhead ? fbeg + e : tbeg + (e - nhead);
+      else return e;
+    };
+
+    // Q^T operands of both row blocks: lane holds query qw + 32 rb + l32, d = 16 ss + 8 hh + 0..7
+    s16x8 qf[2][NS];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int ss = 0; ss < NS; ++ss)
+        qf[rb][ss] = bload16(rq, (unsigned)((qw + 32 * rb + l32) * D + 16 * ss + 8 * hh) * 2u);
+
+    f32x16 acc[2][ND];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[rb][dt][i] = 0.f;
+    // running reference m (log2 units) and this lane's half of the running sum,
+    // per row block, raised lazily as in the 32-row kernel
+    float m[2] = {-INFINITY, -INFINITY};
+    float l[2] = {0.f, 0.f};
+
+    s16x8 kreg[PER], vreg[PER];
+    auto gload = [&](int t) {
+#pragma unroll
+      for (int r = 0; r < PER; ++r) {
+        const int ci = min(tid + r * NT, TCH - 1);  // spare threads repeat the last chunk
+        const int row = ci / CH, col = (ci % CH) * 8;
+        const unsigned int off = (unsigned)((t * F64_BN + row) * D + col) * 2u;
+        kreg[r] = bload16(rk, off);
+        vreg[r] = bload16(rv, off);
+      }
+    };
+    auto lstore = [&](int slot) {
+#pragma unroll
+      for (int r = 0; r < PER; ++r) {
+        const int ci = min(tid + r * NT, TCH - 1);
+        const int row = ci / CH, col = (ci % CH) * 8;
+        lds_write16(kbuf + slot * KBUF + row * KP + col * 2, kreg[r]);
+        lds_write16(vbuf + slot * VBUF + row * VP + col * 2, vreg[r]);
+      }
+    };
+    // S^T = K Q^T of the tile in a slot; st[rb][i] is S of query qw + 32 rb + l32
+    // and key 8 (i / 4) + 4 hh + i % 4 of the tile
+    auto s_tile = [&](int slot, f32x16 (&st)[2]) {
+      const lds_t* kb = kbuf + slot * KBUF + l32 * KP + 16 * hh;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        st[0][i] = 0.f;
+        st[1][i] = 0.f;
+      }
+#pragma unroll
+      for (int ss = 0; ss < NS; ++ss) {
+        const s16x8 ka = lds_read16(kb + 32 * ss);
+        st[0] = mfma32<T>(ka, qf[0][ss], st[0]);
+        st[1] = mfma32<T>(ka, qf[1][ss], st[1]);
+      }
+    };
+    // O^T += V^T P^T for the tile in a slot; B operand k-slot j of step u is key
+    // 16 u + 8 (j / 4) + 4 hh + j % 4, matched by the transposing reads of V
+    auto pv_tile = [&](int slot, const unsigned int (&pk)[2][8]) {
+      const lds_t* vb = vbuf + slot * VBUF;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const lds_t* vp = vb + (16 * u + roff) * VP + (32 * dt + coff) * 2;
+          const s16x8 va = concat(lds_read_tr(vp), lds_read_tr(vp + 8 * VP));
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            acc[rb][dt] = mfma32<T>(va, as_operand(pk[rb][4 * u], pk[rb][4 * u + 1], pk[rb][4 * u + 2],
+                                                   pk[rb][4 * u + 3]),
+                                    acc[rb][dt]);
+        }
+    };
+    // Softmax of one tile against the running reference: returns whether the
+    // reference rises (wave-uniform), with the new reference in mn, the 16-bit
+    // probabilities in pk and this lane's share of their row sums in ls.
+    // 16-bit probabilities of elements 2 jj, 2 jj + 1 of row block rb, with dropout
+    // when built for it (keys ks + 8 (jj / 2) + 4 hh + (2 jj & 3) + 0, 1)
+    // (dw: this row's dropout words for key groups ks + 8 g + 4 hh, g = 0..3,
+    // from drop_words_row4)
+    auto pack_p = [&](float p0, float p1, int jj, const unsigned int (&dw)[4]) -> unsigned int {
+      if constexpr (DROP) {
+        const unsigned int wd = dw[jj >> 1];
+        const int t0 = (2 * jj) & 3;
+        return pack2<T>(drop_keep(wd, t0, s.drop_t) ? p0 * s.drop_scale : 0.f,
+                        drop_keep(wd, t0 + 1, s.drop_t) ? p1 * s.drop_scale : 0.f);
+      } else {
+        return pack2<T>(p0, p1);
+      }
+    };
+    auto softmax = [&](const f32x16 (&st)[2], float (&mn)[2], unsigned int (&pk)[2][8], float (&ls)[2], int ks) {
+      float mx[2];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        const int qi = qw + 32 * rb + l32;
+        float x = st[rb][0];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = ks + 8 * (i >> 2) + 4 * hh + (i & 3);
-          if ((BAND && key > qi + offu) || (LOWER && key < qi + offl) || key >= nk) st[rb][i] = -INFINITY;
+        for (int i = 1; i < 16; ++i) x = fmaxf(x, st[rb][i]);
+        mx[rb] = fmaxf(x, swap_halves(x)) * c;
+      }
+      const bool resc = __any(mx[0] > m[0] + kSlack || mx[1] > m[1] + kSlack);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        mn[rb] = resc ? fmaxf(m[rb], mx[rb]) : m[rb];
+        const float mu = mn[rb] == -INFINITY ? 0.f : mn[rb];  // a row with no visible key yet
+        float sum = 0.f;
+        unsigned int dw[4];
+        if constexpr (DROP) drop_words_row4(s.seed0, s.seed1, b * s.H + h, qw + 32 * rb + l32, ks + 4 * hh, 8, dw);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p0 = fast_exp2(fmaf(st[rb][2 * j], c, -mu));
+          const float p1 = fast_exp2(fmaf(st[rb][2 * j + 1], c, -mu));
+          sum += p0 + p1;
+          pk[rb][j] = pack_p(p0, p1, j, dw);
+        }
+        ls[rb] = sum;
+      }
+      return resc;
+    };
+    // fold a tile's statistics into the running ones; when the reference rose,
+    // scale the output and the sum by exp(m_old - m_new) first
+    auto update = [&](bool resc, const float (&mn)[2], const float (&ls)[2]) {
+      if (resc) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const float corr = fast_exp2(m[rb] - (mn[rb] == -INFINITY ? 0.f : mn[rb]));
+          l[rb] *= corr;
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt) scale_acc(acc[rb][dt], corr);
         }
       }
-      float mn[2], ls[2];
-      unsigned int pt[2][8];
-      const bool resc = softmax(st, mn, pt, ls, ks);
-      update(resc, mn, ls);
-      pv_tile(j & (F64_NB - 1), pt);
-    }
-    lstore((j + 2) & (F64_NB - 1));
-    __syncthreads();
-  }
-
-  const rsrc_t ro = make_rsrc((unsigned short*)a.o + qrow0 * D, qbytes);
-  const rsrc_t rl = make_rsrc(a.lse + qrow0, (unsigned)nq * 4u);
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int qi = qw + 32 * rb + l32;
-    const float lt = l[rb] + swap_halves(l[rb]);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float lse = lt > 0.f ? (m[rb] + fast_log2(lt)) * kLn2 : -INFINITY;
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x2 v2 = {pack2<T>(acc[rb][dt][4 * j] * inv, acc[rb][dt][4 * j + 1] * inv),
-                    pack2<T>(acc[rb][dt][4 * j + 2] * inv, acc[rb][dt][4 * j + 3] * inv)};
-        bstore8(ro, (unsigned)(qi * D + 32 * dt + 8 * j + 4 * hh) * 2u, v2);
+      for (int rb = 0; rb < 2; ++rb) {
+        l[rb] += ls[rb];
+        m[rb] = mn[rb];
       }
-    if (hh == 0) bstore_f32(rl, (unsigned)qi * 4u, lse);
+    };
+
+    // Prologue: tiles 0 and 1 in slots 0 and 1; the V half of slot 3 is zeroed
+    // because the first iteration multiplies it with zero probabilities.
+    for (int i = tid; i < VBUF / 16; i += NT)
+      lds_write16(vbuf + (F64_NB - 1) * VBUF + i * 16, (s16x8){0, 0, 0, 0, 0, 0, 0, 0});
+    gload(tile_of(0));
+    lstore(0);
+    gload(tile_of(max(0, min(1, ntiles - 1))));
+    lstore(1);
+    __syncthreads();
+
+    // Main loop over the tiles that every row sees in full. The reference m is
+    // fixed at the first tile's row maximum, so the loop never rescales and has
+    // no branch: probabilities relative to that reference stay finite while no
+    // later score exceeds it by more than about 120 in log2 units, and the result
+    // O / l, m + log2(l) does not depend on the reference chosen. Should a row's
+    // sum end above 2^60 (some later score at least 60 above the first tile's
+    // maximum), the whole workgroup starts over in the general loop below, which
+    // raises the reference as it goes. With float16 the 16-bit probabilities
+    // have the tighter bound: the restart comes once a row sum exceeds 65504
+    // divided by the dropout keep scale, which every probability (so scaled)
+    // beyond float16's range implies, since the sum holds each probability.
+    int j = 0;
+    if (nfull > 0) {
+      auto probs = [&](const f32x16 (&st)[2], unsigned int (&pk)[2][8], int ks) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          float sum = 0.f;
+          unsigned int dw[4];
+          if constexpr (DROP) drop_words_row4(s.seed0, s.seed1, b * s.H + h, qw + 32 * rb + l32, ks + 4 * hh, 8, dw);
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            const float p0 = fast_exp2(fmaf(st[rb][2 * jj], c, -m[rb]));
+            const float p1 = fast_exp2(fmaf(st[rb][2 * jj + 1], c, -m[rb]));
+            sum += p0 + p1;
+            pk[rb][jj] = pack_p(p0, p1, jj, dw);
+          }
+          l[rb] += sum;
+        }
+      };
+      // one iteration: S of tile jj + 1, probabilities of tile jj, P V of tile
+      // jj - 1 (mutually independent), then tile jj + 2 into the slot of tile
+      // jj - 2. Loads are issued on every path (tile index clamped; a redundant
+      // copy lands in a slot nobody reads). Without dropout the iteration is laid
+      // out in slots of one MFMA each, products of S and of P V alternating, with
+      // the probabilities of the current tile spread over the slots (one element,
+      // or a few at small head sizes, per slot) and the K and V^T fragments read
+      // two fragment groups ahead; scheduling fences keep that order, which the
+      // compiler's own schedule (MFMAs in runs, the exponentials and sums bunched
+      // between them) ran 4% slower at N = 16384, d = 128.
+      auto iter = [&](int jj, const f32x16 (&scur)[2], f32x16 (&snext)[2], const unsigned int (&pprev)[2][8],
+                      unsigned int (&pcur)[2][8]) {
+        gload(tile_of(min(jj + 2, ntiles - 1)));
+        if constexpr (DROP) {
+          s_tile((jj + 1) & (F64_NB - 1), snext);
+          probs(scur, pcur, (fbeg + jj) * F64_BN);
+          pv_tile((jj + F64_NB - 1) & (F64_NB - 1), pprev);
+        } else {
+          const lds_t* kb = kbuf + ((jj + 1) & (F64_NB - 1)) * KBUF + l32 * KP + 16 * hh;
+          const lds_t* vb = vbuf + ((jj + F64_NB - 1) & (F64_NB - 1)) * VBUF;
+          auto vread = [&](int g) {
+            const lds_t* vp = vb + (16 * (g & 1) + roff) * VP + (32 * (g >> 1) + coff) * 2;
+            return concat(lds_read_tr(vp), lds_read_tr(vp + 8 * VP));
+          };
+          constexpr int NG = NS;          // fragment groups: K fragment g and V^T fragment g
+          constexpr int NSLOT = 4 * NG;   // MFMAs: 2 NS products of S, 4 ND = 2 NS of P V
+          constexpr int EPS = 32 / NSLOT; // softmax elements per slot
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            snext[0][i] = 0.f;
+            snext[1][i] = 0.f;
+          }
+          s16x8 ka[NG], va[NG];
+          ka[0] = lds_read16(kb);
+          va[0] = vread(0);
+          if constexpr (NG > 1) {
+            ka[1] = lds_read16(kb + 32);
+            va[1] = vread(1);
+          }
+          float sum[2] = {0.f, 0.f};
+          float pe = 0.f;
+#pragma unroll
+          for (int t = 0; t < NSLOT; ++t) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int g = t >> 2;
+            if ((t & 3) == 0 && g + 2 < NG) {
+              ka[g + 2] = lds_read16(kb + 32 * (g + 2));
+              va[g + 2] = vread(g + 2);
+            }
+            if ((t & 1) == 0) {
+              const int n = t >> 1, rb = n & 1;
+              snext[rb] = mfma32<T>(ka[n >> 1], qf[rb][n >> 1], snext[rb]);
+            } else {
+              const int n = t >> 1, rb = n & 1, pg = n >> 1, u = pg & 1;
+              acc[rb][pg >> 1] = mfma32<T>(va[pg], as_operand(pprev[rb][4 * u], pprev[rb][4 * u + 1],
+                                                              pprev[rb][4 * u + 2], pprev[rb][4 * u + 3]),
+                                           acc[rb][pg >> 1]);
+            }
+#pragma unroll
+            for (int x = 0; x < EPS; ++x) {
+              const int e = t * EPS + x, rb = e >> 4, i = e & 15;
+              const float p = fast_exp2(fmaf(scur[rb][i], c, -m[rb]));
+              if (i & 1) {
+                sum[rb] += pe + p;
+                pcur[rb][i >> 1] = pack2<T>(pe, p);
+              } else {
+                pe = p;
+              }
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          l[0] += sum[0];
+          l[1] += sum[1];
+        }
+        lstore((jj + 2) & (F64_NB - 1));
+        __syncthreads();
+      };
+      f32x16 sa[2], sb[2];
+      unsigned int pa[2][8], pb[2][8];
+      s_tile(0, sa);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float x = sa[rb][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) x = fmaxf(x, sa[rb][i]);
+        m[rb] = fmaxf(x, swap_halves(x)) * c;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) pb[rb][jj] = 0u;
+      }
+      for (; j + 1 < nfull; j += 2) {
+        iter(j, sa, sb, pb, pa);
+        iter(j + 1, sb, sa, pa, pb);
+      }
+      if (j < nfull) {
+        iter(j, sa, sb, pb, pa);
+        pv_tile(j & (F64_NB - 1), pa);
+        ++j;
+      } else {
+        pv_tile((nfull - 1) & (F64_NB - 1), pb);
+      }
+      // workgroup-uniform decision (it also orders the reads above before any
+      // slot is refilled)
+      const float lmax = std::is_same<T, F16>::value ? 65504.f / (DROP ? s.drop_scale : 1.f) : 0x1p60f;
+      if (__syncthreads_or(l[0] > lmax || l[1] > lmax)) {
+        j = 0;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          m[rb] = -INFINITY;
+          l[rb] = 0.f;
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[rb][dt][i] = 0.f;
+        }
+        gload(tile_of(0));
+        lstore(0);
+        gload(tile_of(max(0, min(1, ntiles - 1))));
+        lstore(1);
+        __syncthreads();
+      }
+    }
+
+    // general loop (diagonal and ragged tiles, or a restart): element masks,
+    // lazy rescaling, waves without a visible key skip the tile
+    for (; j < ntiles; ++j) {
+      gload(tile_of(min(j + 2, ntiles - 1)));
+      const int ks = tile_of(j) * F64_BN;
+      if ((!BAND || ks <= qw + F64_RW - 1 + offu) && (!LOWER || ks + F64_BN - 1 >= qw + offl)) {
+        f32x16 st[2];
+        s_tile(j & (F64_NB - 1), st);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const int qi = qw + 32 * rb + l32;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = ks + 8 * (i >> 2) + 4 * hh + (i & 3);
+            if ((BAND && key > qi + offu) || (LOWER && key < qi + offl) || key >= nk) st[rb][i] = -INFINITY;
+          }
+        }
+        float mn[2], ls[2];
+        unsigned int pt[2][8];
+        const bool resc = softmax(st, mn, pt, ls, ks);
+        update(resc, mn, ls);
+        pv_tile(j & (F64_NB - 1), pt);
+      }
+      lstore((j + 2) & (F64_NB - 1));
+      __syncthreads();
+    }
+
+    const rsrc_t ro = make_rsrc((unsigned short*)a.o + qrow0 * D, qbytes);
+    const rsrc_t rl = make_rsrc(a.lse + qrow0, (unsigned)nq * 4u);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int qi = qw + 32 * rb + l32;
+      const float lt = l[rb] + swap_halves(l[rb]);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float lse = lt > 0.f ? (m[rb] + fast_log2(lt)) * kLn2 : -INFINITY;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          u32x2 v2 = {pack2<T>(acc[rb][dt][4 * j] * inv, acc[rb][dt][4 * j + 1] * inv),
+                      pack2<T>(acc[rb][dt][4 * j + 2] * inv, acc[rb][dt][4 * j + 3] * inv)};
+          bstore8(ro, (unsigned)(qi * D + 32 * dt + 8 * j + 4 * hh) * 2u, v2);
+        }
+      if (hh == 0) bstore_f32(rl, (unsigned)qi * 4u, lse);
+    }
   }
 }
 
@@ -922,7 +1306,8 @@ static hipError_t launch_fwd_t3(const FwdArgs& a, hipStream_t st, bool mask, boo
   if (use64) {  // the caller has checked: no block mask, no score bias
     FwdArgs la = a;
     const dim3 grid = tile_grid(la.s, a.s.H, (a.s.Nq + F64_BM - 1) / F64_BM);
-    hipLaunchKernelGGL((fwd64_kernel<T, D, BAND, DROP>), grid, dim3(F64_NW * 64), 0, st, la);
+    const dim3 block(f64_split<D, BAND, DROP>() ? 2 * F64_NW * 64 : F64_NW * 64);  // split roles: eight waves
+    hipLaunchKernelGGL((fwd64_kernel<T, D, BAND, DROP>), grid, block, 0, st, la);
     return hipGetLastError();
   }
   FwdArgs la = a;
