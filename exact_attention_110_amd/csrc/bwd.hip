@@ -24,8 +24,8 @@
 //     iteration issues S and dP of the next query block, P and dS of this
 //     block and dV, dK of the previous block, which do not depend on each
 //     other, so the MFMAs overlap the softmax arithmetic within one wave.
-//     At d = 128 without block mask, dropout, score bias or a lower band edge
-//     the same grid runs eight waves per workgroup in two roles instead:
+//     At d = 128 without block mask or a lower band edge the same grid runs
+//     eight waves per workgroup in two roles instead:
 //     producers form S, dP, P and dS; consumers accumulate dV and dK
 //     (bwd_kv_split_body).
 //  2. query-block kernel (dQ): one workgroup per 128 query rows, four waves of
@@ -527,8 +527,8 @@ __device__ __forceinline__ void bwd_kv_body(const BwdArgs& a, const int hk, cons
 }
 
 // ---------------------------------------------------------------------------
-// stage 1 with split roles (d = 128 without block mask, dropout, score bias or
-// a lower band edge): eight waves per key block, two per SIMD. Producer wave j
+// stage 1 with split roles (d = 128 without block mask or a lower band edge;
+// dropout and ALiBi included): eight waves per key block, two per SIMD. Producer wave j
 // (0..3) holds K^T and V^T of keys k0 + 32 j .. + 31, forms S and dP of each
 // step and from them P and dS, and hands P and dS through LDS to consumer wave
 // j + 4, which holds dK^T and dV^T of the same keys and accumulates dV^T +=
@@ -549,10 +549,10 @@ constexpr int KS_NW = 8;  // waves per split-role workgroup: 4 producers, 4 cons
 
 template <int D, int BAND, bool MASK, bool DROP, bool ALIBI>
 constexpr bool kv_split() {
-  return D == 128 && BAND <= 1 && !MASK && !DROP && !ALIBI;
+  return D == 128 && BAND <= 1 && !MASK;
 }
 
-template <class T, int D, int BAND>
+template <class T, int D, int BAND, bool DROP, bool ALIBI>
 __device__ __forceinline__ void bwd_kv_split_body(const BwdArgs& a, const int hk, const int b, const int kblk) {
   constexpr int BQ = KV_BQ;
   constexpr int QBUF = BQ * 2 * D;  // one Q or dO block, swizzled rows
@@ -631,7 +631,8 @@ __device__ __forceinline__ void bwd_kv_split_body(const BwdArgs& a, const int hk
       for (int j4 = 0; j4 < 4; ++j4) v[j4] = *(const __attribute__((address_space(3))) f32x4*)(pl + 8 * j4 + 4 * hh);
     };
     // S = Q K^T and dP - D = dO V^T - D of this wave's 32 keys from ring buffer
-    // sb (dP starts at -D)
+    // sb (dP starts at -D; with dropout at 0, the -D term added after the keep
+    // factor)
     auto sdp = [&](int sb, f32x16& sc, f32x16& dp, const f32x4 (&nd)[4]) {
       const lds_t* qb = qbuf + sb * QBUF;
       const lds_t* ob = obuf + sb * QBUF;
@@ -640,7 +641,7 @@ __device__ __forceinline__ void bwd_kv_split_body(const BwdArgs& a, const int hk
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           sc[4 * j4 + r] = 0.f;
-          dp[4 * j4 + r] = nd[j4][r];
+          dp[4 * j4 + r] = DROP ? 0.f : nd[j4][r];
         }
 #pragma unroll
       for (int ss = 0; ss < NS; ++ss) {
@@ -656,13 +657,25 @@ __device__ __forceinline__ void bwd_kv_split_body(const BwdArgs& a, const int hk
     // by lane. Element i is query q0 + 8 (i / 4) + 4 hh + i % 4 of key kj;
     // under causal masking or a right window it is kept only while
     // kj - off - wr <= query (the masked variant, for blocks crossing that edge).
-    auto probs = [&](auto masked, const f32x16& sc, const f32x16& dp, int q0, const f32x4 (&lv)[4], int pb) {
+    // With dropout (z the keep decision, cz its scale) P V uses z cz P and
+    // dS = P (z cz dP - D); ALiBi adds the query head's distance bias to the
+    // log2-unit score (bh: the step's query head, batch included; nd: -D of the
+    // step's rows, read only with dropout).
+    auto probs = [&](auto masked, const f32x16& sc, const f32x16& dp, int q0, const f32x4 (&lv)[4], int pb, int bh,
+                     const f32x4 (&nd)[4]) {
       constexpr bool MASKED = decltype(masked)::value;
+      unsigned int dwc[4];
+      if constexpr (DROP) drop_words_col4(s.seed0, s.seed1, bh, kj, q0 + 4 * hh, 8, dwc);
+      const float nsl2 = ALIBI ? -s.alibi[bh - b * s.H] * kLog2e : 0.f;
+      const int dbase = q0 + 4 * hh + off - kj;  // query + off - kj less 8 (i / 4) + i % 4
       float pvv[16];
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pvv[4 * j4 + r] = fast_exp2(fmaf(sc[4 * j4 + r], c, -lv[j4][r]));
+        for (int r = 0; r < 4; ++r) {
+          const float sh = ALIBI ? fmaf(nsl2, fabsf((float)(dbase + 8 * j4 + r)), -lv[j4][r]) : -lv[j4][r];
+          pvv[4 * j4 + r] = fast_exp2(fmaf(sc[4 * j4 + r], c, sh));
+        }
       if constexpr (MASKED) {
         const int thr = kj - offu - q0 - 4 * hh;  // first kept 8 (i / 4) + i % 4
 #pragma unroll
@@ -674,8 +687,21 @@ __device__ __forceinline__ void bwd_kv_split_body(const BwdArgs& a, const int hk
       unsigned int pk[8], sk[8];
 #pragma unroll
       for (int j2 = 0; j2 < 8; ++j2) {
-        pk[j2] = pack2<T>(pvv[2 * j2], pvv[2 * j2 + 1]);
-        sk[j2] = pack2<T>(pvv[2 * j2] * dp[2 * j2], pvv[2 * j2 + 1] * dp[2 * j2 + 1]);
+        float p2[2], d2[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int i = 2 * j2 + r;
+          if constexpr (DROP) {
+            const bool z = drop_keep(dwc[i >> 2], i & 3, s.drop_t);
+            p2[r] = z ? pvv[i] * s.drop_scale : 0.f;
+            d2[r] = pvv[i] * ((z ? dp[i] * s.drop_scale : 0.f) + nd[i >> 2][i & 3]);
+          } else {
+            p2[r] = pvv[i];
+            d2[r] = pvv[i] * dp[i];
+          }
+        }
+        pk[j2] = pack2<T>(p2[0], p2[1]);
+        sk[j2] = pack2<T>(d2[0], d2[1]);
       }
       lds_t* pw = psbuf + (pb * 4 + jw) * PSB + lane * 16;
       lds_write16(pw, __builtin_bit_cast(s16x8, (u32x4){pk[0], pk[1], pk[2], pk[3]}));
@@ -699,12 +725,13 @@ __device__ __forceinline__ void bwd_kv_split_body(const BwdArgs& a, const int hk
       constexpr int P = decltype(phase)::value;
       const int er = P >= 0 ? P : e;  // congruent to e modulo NB
       const StepPos nn = e + 2 < nsteps ? advance(nxt) : nxt;
-      f32x4 lv[4], nd[4];
+      f32x4 lv[4], nd[4], ndp[4];
       stats4(er & (NB - 1), 0, lv);
-      stats4((er + 1) & (NB - 1), 1, nd);
+      if constexpr (DROP) stats4(er & (NB - 1), 1, ndp);
+      else stats4((er + 1) & (NB - 1), 1, nd);
       dma_q(nn, (er + 2) & (NB - 1));
       sdp((er + 1) & (NB - 1), scn, dpn, nd);
-      probs(masked, sc, dp, (qb_first + cur.qi) * BQ, lv, er & 1);
+      probs(masked, sc, dp, (qb_first + cur.qi) * BQ, lv, er & 1, cur.hb, ndp);
       dma_wait();
       __syncthreads();
       cur = nxt;
@@ -714,7 +741,7 @@ __device__ __forceinline__ void bwd_kv_split_body(const BwdArgs& a, const int hk
     {
       f32x4 nd0[4];
       stats4(0, 1, nd0);
-      sdp(0, scA, dpA, nd0);
+      sdp(0, scA, dpA, nd0);  // (the first step's -D, unused with dropout)
     }
     auto b_to_a = [&]() {
       scA = scB;
@@ -850,7 +877,7 @@ __global__ __launch_bounds__((kv_split<D, BAND, MASK, DROP, ALIBI>() ? KS_NW * 6
     void bwd_kv_kernel(BwdArgs a) {
   const GridPos gp = grid_pos(a.s);  // grid: tile_grid over kv heads and key blocks
   if constexpr (kv_split<D, BAND, MASK, DROP, ALIBI>())
-    bwd_kv_split_body<T, D, BAND>(a, blockIdx.x, gp.b, gp.blk);
+    bwd_kv_split_body<T, D, BAND, DROP, ALIBI>(a, blockIdx.x, gp.b, gp.blk);
   else
     bwd_kv_body<T, D, BAND, MASK, DROP, ALIBI>(a, blockIdx.x, gp.b, gp.blk);
 }
