@@ -19,9 +19,9 @@
 //  * LDS row pitches are padded so that the 16-byte row reads of K and the
 //    transposing reads of V are free of bank conflicts.
 //  * Long rows at head size 128 run fwd64_kernel (64 query rows per wave
-//    pair, 256 rows per workgroup: without dropout and a lower band edge as
-//    a producer wave forming the probabilities and a consumer wave holding O
-//    on each SIMD, otherwise as one wave per SIMD); the others,
+//    pair, 256 rows per workgroup: without a lower band edge as a producer
+//    wave forming the probabilities and a consumer wave holding O on each
+//    SIMD, otherwise as one wave per SIMD); the others,
 //    and all block-sparse inputs, run fwd_kernel (32 rows per wave, two waves
 //    per SIMD, 128 rows per workgroup = one mask block row).
 //  * Causal: a workgroup stops at its diagonal tile, waves skip tiles that lie
@@ -368,8 +368,8 @@ constexpr int F64_BM = F64_NW * F64_RW;   // query rows per workgroup
 constexpr int F64_BN = 32;                // keys per tile
 constexpr int F64_NB = 4;                 // LDS ring slots
 
-// The same rows and tiles with split roles (d = 128 without dropout; causal,
-// dense or an upper band edge): eight waves, two per SIMD. Producer wave j
+// The same rows and tiles with split roles (d = 128; causal, dense or an
+// upper band edge; dropout included): eight waves, two per SIMD. Producer wave j
 // (0..3) holds Q^T of rows q0 + 64 j .. + 63 and forms S^T and the
 // probabilities; it hands P^T, as the consumer's MFMA B operands, through one
 // of two LDS buffers to consumer wave j + 4 on the same SIMD, which holds the
@@ -389,10 +389,10 @@ constexpr int F64_NB = 4;                 // LDS ring slots
 // log-sum-exp and hands 1 / l to the consumer, which writes O.
 template <int D, int BAND, bool DROP>
 constexpr bool f64_split() {
-  return D == 128 && BAND <= 1 && !DROP;
+  return D == 128 && BAND <= 1;
 }
 
-template <class T, int D, int BAND>
+template <class T, int D, int BAND, bool DROP>
 __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
   constexpr int KP = D * 2 + 16;  // K row pitch (bytes): conflict-free 16-byte row reads
   constexpr int VP = D * 2 + 32;  // V row pitch (bytes): conflict-free transposing reads
@@ -405,7 +405,7 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
   static_assert(TCH % NT == 0 || TCH < NT, "tile loader shape");
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
-  constexpr float kSlack = 8.f;  // as in fwd_kernel
+  constexpr float kSlack = (std::is_same<T, F16>::value && DROP) ? 7.f : 8.f;  // as in fwd_kernel
   // one pair's hand-over buffer: P^T (four 16-byte chunks per lane, chunk
   // 2 rb + u holding the B operand of MFMA step u of row block rb), then the
   // 64 rows' rescale factors, then the flags (bit 0: the pair's rows see the
@@ -478,7 +478,7 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
   __syncthreads();
 
   // restart bound of the fixed-reference loop, as in the one-role form below
-  const float lmax = std::is_same<T, F16>::value ? 65504.f : 0x1p60f;
+  const float lmax = std::is_same<T, F16>::value ? 65504.f / (DROP ? s.drop_scale : 1.f) : 0x1p60f;
   int j = 0;
   if (producer) {
     const rsrc_t rq = make_rsrc((const unsigned short*)a.q + qrow0 * D, qbytes);
@@ -507,6 +507,19 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
         st[1] = mfma32<T>(ka, qf[1][ss], st[1]);
       }
     };
+    // 16-bit probabilities of a pair of elements, with dropout when built for
+    // it (dw: the row's dropout words for key groups ks + 8 g + 4 hh, g = 0..3,
+    // from drop_words_row4; jj: the pair, keys ks + 8 (jj / 2) + 4 hh + (2 jj & 3) + 0, 1)
+    auto pack_p = [&](float p0, float p1, int jj, const unsigned int (&dw)[4]) -> unsigned int {
+      if constexpr (DROP) {
+        const unsigned int wd = dw[jj >> 1];
+        const int t0 = (2 * jj) & 3;
+        return pack2<T>(drop_keep(wd, t0, s.drop_t) ? p0 * s.drop_scale : 0.f,
+                        drop_keep(wd, t0 + 1, s.drop_t) ? p1 * s.drop_scale : 0.f);
+      } else {
+        return pack2<T>(p0, p1);
+      }
+    };
     auto write_p = [&](lds_t* hb, const unsigned int (&pk)[2][8]) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
@@ -530,6 +543,12 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
         s16x8 ka[NS];
 #pragma unroll
         for (int ss = 0; ss < NS; ++ss) ka[ss] = lds_read16(kb + 32 * ss);
+        unsigned int dw[2][4];
+        if constexpr (DROP) {
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            drop_words_row4(s.seed0, s.seed1, b * s.H + h, qw + 32 * rb + l32, jj * F64_BN + 4 * hh, 8, dw[rb]);
+        }
         unsigned int pk[2][8];
         float sum[2] = {0.f, 0.f};
 #pragma unroll
@@ -541,7 +560,7 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
           const float p0 = fast_exp2(fmaf(scur[rbe][i], c, -m[rbe]));
           const float p1 = fast_exp2(fmaf(scur[rbe][i + 1], c, -m[rbe]));
           sum[rbe] += p0 + p1;
-          pk[rbe][i >> 1] = pack2<T>(p0, p1);
+          pk[rbe][i >> 1] = pack_p(p0, p1, i >> 1, dw[rbe]);
         }
         __builtin_amdgcn_sched_barrier(0);
         l[0] += sum[0];
@@ -614,12 +633,14 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
           const float mn = resc ? fmaxf(m[rb], mx[rb]) : m[rb];
           const float mu = mn == -INFINITY ? 0.f : mn;
           float sum = 0.f;
+          unsigned int dw[4];
+          if constexpr (DROP) drop_words_row4(s.seed0, s.seed1, b * s.H + h, qw + 32 * rb + l32, ks + 4 * hh, 8, dw);
 #pragma unroll
           for (int jj = 0; jj < 8; ++jj) {
             const float p0 = fast_exp2(fmaf(st[rb][2 * jj], c, -mu));
             const float p1 = fast_exp2(fmaf(st[rb][2 * jj + 1], c, -mu));
             sum += p0 + p1;
-            pk[rb][jj] = pack2<T>(p0, p1);
+            pk[rb][jj] = pack_p(p0, p1, jj, dw);
           }
           if (resc) {
             const float corr = fast_exp2(m[rb] - mu);
@@ -748,7 +769,7 @@ template <class T, int D, int BAND, bool DROP>
 __global__ __launch_bounds__((f64_split<D, BAND, DROP>() ? 2 * F64_NW * 64 : F64_NW * 64), 1)
     void fwd64_kernel(FwdArgs a) {
   if constexpr (f64_split<D, BAND, DROP>()) {
-    fwd64_split_body<T, D, BAND>(a);
+    fwd64_split_body<T, D, BAND, DROP>(a);
     return;
   } else {
     constexpr int KP = D * 2 + 16;  // K row pitch (bytes): conflict-free 16-byte row reads
