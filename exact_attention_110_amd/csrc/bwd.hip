@@ -24,8 +24,8 @@
 //     iteration issues S and dP of the next query block, P and dS of this
 //     block and dV, dK of the previous block, which do not depend on each
 //     other, so the MFMAs overlap the softmax arithmetic within one wave.
-//     At d = 128 without block mask or a lower band edge the same grid runs
-//     eight waves per workgroup in two roles instead:
+//     At d = 128 without block mask the same grid runs eight waves per
+//     workgroup in two roles instead:
 //     producers form S, dP, P and dS; consumers accumulate dV and dK
 //     (bwd_kv_split_body).
 //  2. query-block kernel (dQ): one workgroup per 128 query rows, four waves of
@@ -527,8 +527,8 @@ __device__ __forceinline__ void bwd_kv_body(const BwdArgs& a, const int hk, cons
 }
 
 // ---------------------------------------------------------------------------
-// stage 1 with split roles (d = 128 without block mask or a lower band edge;
-// dropout and ALiBi included): eight waves per key block, two per SIMD. Producer wave j
+// stage 1 with split roles (d = 128 without block mask; band edges, dropout
+// and ALiBi included): eight waves per key block, two per SIMD. Producer wave j
 // (0..3) holds K^T and V^T of keys k0 + 32 j .. + 31, forms S and dP of each
 // step and from them P and dS, and hands P and dS through LDS to consumer wave
 // j + 4, which holds dK^T and dV^T of the same keys and accumulates dV^T +=
@@ -549,7 +549,7 @@ constexpr int KS_NW = 8;  // waves per split-role workgroup: 4 producers, 4 cons
 
 template <int D, int BAND, bool MASK, bool DROP, bool ALIBI>
 constexpr bool kv_split() {
-  return D == 128 && BAND <= 1 && !MASK;
+  return D == 128 && !MASK;
 }
 
 template <class T, int D, int BAND, bool DROP, bool ALIBI>
@@ -584,12 +584,15 @@ __device__ __forceinline__ void bwd_kv_split_body(const BwdArgs& a, const int hk
   const int kj = k0 + 32 * jw + l32;  // this lane's key (its column of S)
   const unsigned int qbytes = (unsigned int)len_q * D * 2, kbytes = (unsigned int)len_k * D * 2;
   const size_t krow0 = sv.krow0;
-  // query blocks from the first one that sees a key of the block (rows from
-  // k0 - off - wr) to the end, for each query head of the group
-  const int offu = off + s.wr;
+  // query blocks that see a key of the block: rows from k0 - off - wr to
+  // k0 + 127 - off + wl (offu = off + wr, offl = off - wl; offl binds only
+  // with a lower edge), for each query head of the group
+  constexpr bool LOWER = BAND == 2;
+  const int offu = off + s.wr, offl = off - s.wl;
   const int nqb_all = (len_q + BQ - 1) / BQ;
   const int qb_first = BAND ? max(0, k0 - offu) / BQ : 0;
-  const int nq = max(0, nqb_all - qb_first);
+  const int qb_end = LOWER ? min(nqb_all, (max(0, k0 + KV_BKV - offl) + BQ - 1) / BQ) : nqb_all;
+  const int nq = max(0, qb_end - qb_first);
   const int nsteps = nq * s.G;
 
   if (producer) {
@@ -656,7 +659,8 @@ __device__ __forceinline__ void bwd_kv_split_body(const BwdArgs& a, const int hk
     // B operands: chunk 2 m + u holds slots of MFMA step u (m = 0 P, 1 dS), lane
     // by lane. Element i is query q0 + 8 (i / 4) + 4 hh + i % 4 of key kj;
     // under causal masking or a right window it is kept only while
-    // kj - off - wr <= query (the masked variant, for blocks crossing that edge).
+    // kj - off - wr <= query, and with a lower edge while query <= kj - off + wl
+    // (the masked variant, for blocks crossing an edge).
     // With dropout (z the keep decision, cz its scale) P V uses z cz P and
     // dS = P (z cz dP - D); ALiBi adds the query head's distance bias to the
     // log2-unit score (bh: the step's query head, batch included; nd: -D of the
@@ -677,11 +681,12 @@ __device__ __forceinline__ void bwd_kv_split_body(const BwdArgs& a, const int hk
           pvv[4 * j4 + r] = fast_exp2(fmaf(sc[4 * j4 + r], c, sh));
         }
       if constexpr (MASKED) {
-        const int thr = kj - offu - q0 - 4 * hh;  // first kept 8 (i / 4) + i % 4
+        const int thr = kj - offu - q0 - 4 * hh;   // first kept 8 (i / 4) + i % 4
+        const int thr2 = kj - offl - q0 - 4 * hh;  // last kept (with a lower edge)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int o = 8 * (i >> 2) + (i & 3);
-          pvv[i] = o < thr ? 0.f : pvv[i];
+          pvv[i] = (o < thr || (LOWER && o > thr2)) ? 0.f : pvv[i];
         }
       }
       unsigned int pk[8], sk[8];
@@ -748,12 +753,18 @@ __device__ __forceinline__ void bwd_kv_split_body(const BwdArgs& a, const int hk
       dpA = dpB;
     };
     // the first ndiag steps of each query head's list cross the band's upper
-    // edge (q0 + off + wr < k0 + 127) and take the masked variant
-    int ndiag = 0;
+    // edge (q0 + off + wr < k0 + 127), the last nsuf its lower edge
+    // (q0 + 31 + off - wl > k0); they take the masked variant
+    int ndiag = 0, nsuf = 0;
     if constexpr (BAND) {
       const int lim = k0 + KV_BKV - 1 - offu;
       while (ndiag < nq && (qb_first + ndiag) * BQ < lim) ++ndiag;
     }
+    if constexpr (LOWER) {
+      const int lim2 = k0 - (BQ - 1) - offl;
+      while (nsuf < nq - ndiag && (qb_first + nq - 1 - nsuf) * BQ > lim2) ++nsuf;
+    }
+    const int nmid_end = nq - nsuf;
     const std::true_type masked;
     const std::false_type plain;
     const RingAt<-1> rt;
@@ -767,35 +778,41 @@ __device__ __forceinline__ void bwd_kv_split_body(const BwdArgs& a, const int hk
       // at a time with the ring position fixed at compile time, then the rest;
       // pairs alternate the register sets, a single step copies them back
       int t = ndiag;
-      if ((e & 1) && t < nq) {
+      if ((e & 1) && t < nmid_end) {
         iter(e, plain, rt, scA, dpA, scB, dpB);
         b_to_a();
         ++e;
         ++t;
       }
-      if ((e & 2) && t + 1 < nq) {
+      if ((e & 2) && t + 1 < nmid_end) {
         iter(e, plain, rt, scA, dpA, scB, dpB);
         iter(e + 1, plain, rt, scB, dpB, scA, dpA);
         e += 2;
         t += 2;
       }
       if ((e & (NB - 1)) == 0) {
-        for (; t + 3 < nq; t += 4, e += 4) {
+        for (; t + 3 < nmid_end; t += 4, e += 4) {
           iter(e, plain, RingAt<0>{}, scA, dpA, scB, dpB);
           iter(e + 1, plain, RingAt<1>{}, scB, dpB, scA, dpA);
           iter(e + 2, plain, RingAt<2>{}, scA, dpA, scB, dpB);
           iter(e + 3, plain, RingAt<3>{}, scB, dpB, scA, dpA);
         }
       }
-      for (; t + 1 < nq; t += 2, e += 2) {
+      for (; t + 1 < nmid_end; t += 2, e += 2) {
         iter(e, plain, rt, scA, dpA, scB, dpB);
         iter(e + 1, plain, rt, scB, dpB, scA, dpA);
       }
-      if (t < nq) {
+      if (t < nmid_end) {
         iter(e, plain, rt, scA, dpA, scB, dpB);
         b_to_a();
         ++e;
         ++t;
+      }
+      if constexpr (LOWER) {
+        for (; t < nq; ++t, ++e) {
+          iter(e, masked, rt, scA, dpA, scB, dpB);
+          b_to_a();
+        }
       }
     }
   } else {

@@ -19,9 +19,9 @@
 //  * LDS row pitches are padded so that the 16-byte row reads of K and the
 //    transposing reads of V are free of bank conflicts.
 //  * Long rows at head size 128 run fwd64_kernel (64 query rows per wave
-//    pair, 256 rows per workgroup: without a lower band edge as a producer
-//    wave forming the probabilities and a consumer wave holding O on each
-//    SIMD, otherwise as one wave per SIMD); the others,
+//    pair, 256 rows per workgroup; at d = 128 as a producer wave forming the
+//    probabilities and a consumer wave holding O on each SIMD, otherwise as
+//    one wave per SIMD); the others,
 //    and all block-sparse inputs, run fwd_kernel (32 rows per wave, two waves
 //    per SIMD, 128 rows per workgroup = one mask block row).
 //  * Causal: a workgroup stops at its diagonal tile, waves skip tiles that lie
@@ -368,8 +368,8 @@ constexpr int F64_BM = F64_NW * F64_RW;   // query rows per workgroup
 constexpr int F64_BN = 32;                // keys per tile
 constexpr int F64_NB = 4;                 // LDS ring slots
 
-// The same rows and tiles with split roles (d = 128; causal, dense or an
-// upper band edge; dropout included): eight waves, two per SIMD. Producer wave j
+// The same rows and tiles with split roles (d = 128; every band kind and
+// dropout): eight waves, two per SIMD. Producer wave j
 // (0..3) holds Q^T of rows q0 + 64 j .. + 63 and forms S^T and the
 // probabilities; it hands P^T, as the consumer's MFMA B operands, through one
 // of two LDS buffers to consumer wave j + 4 on the same SIMD, which holds the
@@ -389,7 +389,7 @@ constexpr int F64_NB = 4;                 // LDS ring slots
 // log-sum-exp and hands 1 / l to the consumer, which writes O.
 template <int D, int BAND, bool DROP>
 constexpr bool f64_split() {
-  return D == 128 && BAND <= 1;
+  return D == 128;
 }
 
 template <class T, int D, int BAND, bool DROP>
@@ -440,12 +440,25 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
   const rsrc_t rv = make_rsrc((const unsigned short*)a.v + krow0 * D, kbytes);
   const int qw = q0 + F64_RW * pw;  // block rb of the pair holds rows qw + 32 rb + 0..31
   const float c = fmaxf(s.scale * kLog2e, 1e-30f);
-  // tiles [0, ntiles) hold every key some row of the workgroup sees, tiles
-  // [0, nfull) only keys that every row sees (row i sees keys up to i + off + wr)
-  const int offu = off + s.wr;
+  // tiles [tbeg, tbeg + ntiles) hold every key some row of the workgroup sees,
+  // tiles [fbeg, fend) only keys that every row sees (row i sees keys i + off -
+  // wl .. i + off + wr; offl binds only with a lower edge); processing order:
+  // the full tiles, the partial ones above them, then those below (tile_of)
+  constexpr bool LOWER = BAND == 2;
+  const int offu = off + s.wr, offl = off - s.wl;
+  const int kbeg = LOWER ? max(0, q0 + offl) : 0;
   const int kend = BAND ? min(nk, max(0, q0 + F64_BM + offu)) : nk;
-  const int ntiles = max(0, (kend + F64_BN - 1) / F64_BN);
-  const int nfull = BAND ? max(0, min(max(0, q0 + offu + 1) / F64_BN, nk / F64_BN)) : nk / F64_BN;
+  const int tbeg = kbeg / F64_BN;
+  const int ntiles = max(0, (kend + F64_BN - 1) / F64_BN - tbeg);
+  const int fbeg =
+      LOWER ? min(tbeg + ntiles, max(tbeg, (max(0, q0 + F64_BM - 1 + offl) + F64_BN - 1) / F64_BN)) : 0;
+  const int fend = BAND ? max(fbeg, min(max(0, q0 + offu + 1) / F64_BN, nk / F64_BN)) : nk / F64_BN;
+  const int nfull = fend - fbeg;
+  const int nhead = tbeg + ntiles - fbeg;
+  auto tile_of = [&](int e) -> int {
+    if constexpr (LOWER) return e < nhead ? fbeg + e : tbeg + (e - nhead);
+    else return e;
+  };
 
   s16x8 kreg[PER], vreg[PER];
   auto gload = [&](int t) {
@@ -471,9 +484,9 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
 
   // Every wave takes the same sequence of barriers: the prologue's, one per
   // main-loop tile, the restart vote, one per general-loop tile, the final one.
-  gload(0);
+  gload(tile_of(0));
   lstore(0);
-  gload(max(0, min(1, ntiles - 1)));
+  gload(tile_of(max(0, min(1, ntiles - 1))));
   lstore(1);
   __syncthreads();
 
@@ -533,7 +546,7 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
       // one iteration in slots: S product t of the next tile, then elements
       // 2 t and 2 t + 1 of the current tile's probabilities (fenced order)
       auto iter = [&](int jj, const f32x16 (&scur)[2], f32x16 (&snext)[2]) {
-        gload(min(jj + 2, ntiles - 1));
+        gload(tile_of(min(jj + 2, ntiles - 1)));
         const lds_t* kb = kbuf + ((jj + 1) & (F64_NB - 1)) * KBUF + l32 * KP + 16 * hh;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -547,7 +560,8 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
         if constexpr (DROP) {
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb)
-            drop_words_row4(s.seed0, s.seed1, b * s.H + h, qw + 32 * rb + l32, jj * F64_BN + 4 * hh, 8, dw[rb]);
+            drop_words_row4(s.seed0, s.seed1, b * s.H + h, qw + 32 * rb + l32, tile_of(jj) * F64_BN + 4 * hh, 8,
+                            dw[rb]);
         }
         unsigned int pk[2][8];
         float sum[2] = {0.f, 0.f};
@@ -592,19 +606,19 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
         j = 0;
         m[0] = m[1] = -INFINITY;
         l[0] = l[1] = 0.f;
-        gload(0);
+        gload(tile_of(0));
         lstore(0);
-        gload(max(0, min(1, ntiles - 1)));
+        gload(tile_of(max(0, min(1, ntiles - 1))));
         lstore(1);
         __syncthreads();
       }
     }
     // general loop: element masks, lazy rescaling; a pair whose rows see no key of the tile skips it
     for (; j < ntiles; ++j) {
-      gload(min(j + 2, ntiles - 1));
-      const int ks = j * F64_BN;
+      gload(tile_of(min(j + 2, ntiles - 1)));
+      const int ks = tile_of(j) * F64_BN;
       lds_t* hb = hand(j & 1);
-      const bool act = !BAND || ks <= qw + F64_RW - 1 + offu;
+      const bool act = (!BAND || ks <= qw + F64_RW - 1 + offu) && (!LOWER || ks + F64_BN - 1 >= qw + offl);
       bool resc = false;
       if (act) {
         f32x16 st[2];
@@ -615,7 +629,7 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = ks + 8 * (i >> 2) + 4 * hh + (i & 3);
-            if ((BAND && key > qi + offu) || key >= nk) st[rb][i] = -INFINITY;
+            if ((BAND && key > qi + offu) || (LOWER && key < qi + offl) || key >= nk) st[rb][i] = -INFINITY;
           }
         }
         float mx[2];
@@ -717,7 +731,7 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
     if (nfull > 0) {
       // main loop: iteration j takes P V of tile j - 1 (fixed reference: no rescale)
       for (; j < nfull; ++j) {
-        gload(min(j + 2, ntiles - 1));
+        gload(tile_of(min(j + 2, ntiles - 1)));
         if (j > 0) pv((j - 1) & (F64_NB - 1), hand((j - 1) & 1));
         lstore((j + 2) & (F64_NB - 1));
         __syncthreads();
@@ -731,9 +745,9 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
           for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[rb][dt][i] = 0.f;
-        gload(0);
+        gload(tile_of(0));
         lstore(0);
-        gload(max(0, min(1, ntiles - 1)));
+        gload(tile_of(max(0, min(1, ntiles - 1))));
         lstore(1);
         __syncthreads();
       }
@@ -741,7 +755,7 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
     // general loop: iteration j takes tile j - 1, the last tile follows the last barrier
     const int j0 = j;
     for (; j < ntiles; ++j) {
-      gload(min(j + 2, ntiles - 1));
+      gload(tile_of(min(j + 2, ntiles - 1)));
       if (j > j0) consume(j - 1);
       lstore((j + 2) & (F64_NB - 1));
       __syncthreads();
