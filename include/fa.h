@@ -303,10 +303,13 @@ int fa_backward_bitmask(const void* q, const void* k, const void* v, const void*
 
 /*
  * Forward kernel choice. The 16-bit forward pass has two kernels: one with 64
- * query rows per wave (one wave per SIMD; rows of at least 8192 keys at head
- * size 128) and one with 32 rows per wave (two waves per SIMD; everything else,
- * and every call with a block mask or score bias). Both compute the same
- * attention (results agree within the tolerances, not bit for bit).
+ * query rows per wave (rows of at least 8192 keys at head size 128; at that
+ * head size a producer wave forming the probabilities and a consumer wave
+ * holding the output share each SIMD, at smaller head sizes, when forced, it
+ * runs one wave per SIMD) and one with 32 rows per wave (two waves per SIMD;
+ * everything else, and every call with a block mask or score bias). Both
+ * compute the same attention (results agree within the tolerances, not bit
+ * for bit).
  *
  * fa_forward_kernel_rows: the rows per wave of the kernel that fa_forward /
  * fa_forward_qk / fa_forward_dropout take for these arguments: 64 or 32, 0
