@@ -1382,18 +1382,20 @@ static hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Which 16-bit kernel a forward call takes by default. The 64-row kernel pays
-// off for long rows at head size 128 (measured, causal bf16: N = 16384 x 16
-// heads 8% faster, 4 x 32 heads over 8 kv heads at N = 8192 6% faster, N =
-// 32768 9%; N = 4096 even). At head size 64 the exponentials dominate and the
-// 32-row kernel's two waves per SIMD do better (N = 16384: 6% faster), as they
-// do for short rows, where the 64-row kernel spends much of its time in the
-// diagonal tail (N = 1024: 1.6x faster). Block masks and score biases always
-// take the 32-row kernel. Float32 inputs take the float32 kernel (0).
+// Which 16-bit kernel a forward call takes by default. At head size 128 the
+// 64-row kernel (in its split-role form) pays off from 4096 keys with a band
+// (causal or windowed) and from 1024 without (measured, bf16, one box: causal
+// N = 4096 x 64 heads 7% faster, N = 16384 x 16 heads 11%, N = 2048 even,
+// N = 1024 13% slower, the 256-row workgroups spending much of their time in
+// the diagonal tail; without a band N = 1024 8% faster, N = 4096 10%, N = 512
+// even). At head size 64 the exponentials dominate and the 32-row kernel's two
+// waves per SIMD do better (N = 16384: 6% faster). Block masks and score
+// biases always take the 32-row kernel. Float32 inputs take the float32
+// kernel (0).
 int forward_rows(const AttnShape& s, int dtype) {
   if (dtype == 0) return 0;
   if (s.mask || s.alibi) return 32;
-  return (s.d == 128 && min(s.Nq, s.Nk) >= 8192) ? 64 : 32;
+  return (s.d == 128 && min(s.Nq, s.Nk) >= (s.band ? 4096 : 1024)) ? 64 : 32;
 }
 
 hipError_t launch_forward(const FwdArgs& a, int dtype, hipStream_t st, int rows) {

@@ -303,7 +303,8 @@ int fa_backward_bitmask(const void* q, const void* k, const void* v, const void*
 
 /*
  * Forward kernel choice. The 16-bit forward pass has two kernels: one with 64
- * query rows per wave (rows of at least 8192 keys at head size 128; at that
+ * query rows per wave (head size 128 with at least 4096 keys per row under a
+ * causal or window band, 1024 without; at that
  * head size a producer wave forming the probabilities and a consumer wave
  * holding the output share each SIMD, at smaller head sizes, when forced, it
  * runs one wave per SIMD) and one with 32 rows per wave (two waves per SIMD;

@@ -274,8 +274,14 @@ def test_forward_kernel_rows(lib):
     assert rows(1, 16, 16, 16384, 16384, 128, 1, -1, -1, 0, 1, BF16) == 32
     assert rows(4, 32, 8, 8192, 8192, 128, 1, -1, -1, 0, 0, BF16) == 64
     assert rows(8, 12, 12, 1024, 1024, 64, 1, -1, -1, 0, 0, BF16) == 32
-    assert rows(1, 8, 8, 8192, 8191, 128, 0, -1, -1, 0, 0, F16) == 32     # the shorter side decides
-    assert rows(1, 8, 8, 8192, 8192, 128, 0, -1, -1, 0, 0, F16) == 64
+    # head size 128: from 4096 keys with a band (causal, windows), from 1024 without;
+    # the shorter side decides
+    assert rows(1, 8, 8, 8192, 4095, 128, 1, -1, -1, 0, 0, F16) == 32
+    assert rows(1, 8, 8, 8192, 4096, 128, 1, -1, -1, 0, 0, F16) == 64
+    assert rows(1, 8, 8, 4096, 4096, 128, 0, 256, -1, 0, 0, BF16) == 64    # a lower window edge is a band
+    assert rows(1, 8, 8, 2048, 2048, 128, 0, -1, 64, 0, 0, BF16) == 32     # so is an upper one
+    assert rows(1, 8, 8, 2048, 1023, 128, 0, -1, -1, 0, 0, F16) == 32
+    assert rows(1, 8, 8, 2048, 1024, 128, 0, -1, -1, 0, 0, F16) == 64
     assert rows(1, 16, 16, 16384, 16384, 64, 1, -1, -1, 0, 0, BF16) == 32  # head size 64: 32 rows
     assert rows(1, 1, 1, 512, 512, 32, 0, -1, -1, 0, 0, F32) == 0
     assert rows(1, 2, 1, 256, 256, 96, 1, -1, -1, 0, 0, BF16) == EINVAL
