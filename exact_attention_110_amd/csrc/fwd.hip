@@ -18,7 +18,8 @@
 //    gfx950 transposing read ds_read_b64_tr_b16, so V needs no transpose pass.
 //  * LDS row pitches are padded so that the 16-byte row reads of K and the
 //    transposing reads of V are free of bank conflicts.
-//  * Long rows at head size 128 run fwd64_kernel (64 query rows per wave
+//  * Rows of 4096 keys or more at head size 128 (1024 without a causal or
+//    window band) run fwd64_kernel (64 query rows per wave
 //    pair, 256 rows per workgroup; at d = 128 as a producer wave forming the
 //    probabilities and a consumer wave holding O on each SIMD, otherwise as
 //    one wave per SIMD); the others,

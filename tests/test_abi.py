@@ -264,7 +264,8 @@ def test_fp8_head_sizes(lib):
 
 def test_forward_kernel_rows(lib):
     """The library's forward-kernel choice, as bench.py reads it: 64 rows per
-    wave for long rows at head size 128, 32 otherwise and
+    wave at head size 128 for rows of 4096 keys under a band (1024 without),
+    32 otherwise and
     always with a block mask or score bias, 0 (the float32 kernel) for FA_F32;
     negative statuses for arguments the forward calls reject."""
     rows = lambda *a: lib.fa_forward_kernel_rows(*a)  # noqa: E731

@@ -43,9 +43,9 @@ def test_dense(shape, causal, dtype):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_dense_64_rows_per_wave(shape, causal, dtype):
-    """The 64-row forward kernel (chosen by the library for rows of 8192 keys
-    or more at head size 128) at every small shape, forced through
-    fa_forward_select."""
+    """The 64-row forward kernel (chosen by the library at head size 128 for
+    rows of 4096 keys or more under a band, 1024 without) at every small
+    shape, forced through fa_forward_select."""
     B, H, Hkv, N, d = shape
     PT.run_small(B, H, Hkv, N, d, dtype, causal, seed=5000 + N + d + int(causal) + (1 if dtype == "fp16" else 0),
                  backward=False, rows_per_wave=64)
