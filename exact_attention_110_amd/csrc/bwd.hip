@@ -540,8 +540,9 @@ __device__ __forceinline__ void bwd_kv_body(const BwdArgs& a, const int hk, cons
 // Iteration e (one barrier at its end): producers load step e + 2 into the
 // ring buffer step e - 2 used, form S and dP of step e + 1 and P and dS of
 // step e (into hand-over buffer e % 2); consumers take dV, dK of step e - 1
-// from ring buffer (e - 1) % 4 and hand-over buffer (e - 1) % 2. A ring buffer
-// is read by producers in iterations e - 1 and e and by consumers in e + 1,
+// with P and dS from hand-over buffer (e - 1) % 2 and the transposed Q, dO of
+// step e - 1 read in iteration e - 1, then read those of step e. Step e's ring
+// buffer is read by producers in iterations e - 1 and e and by consumers in e,
 // and rewritten in e + 2; a hand-over buffer is written in e, read in e + 1
 // and rewritten in e + 2.
 // ---------------------------------------------------------------------------
