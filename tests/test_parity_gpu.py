@@ -185,6 +185,28 @@ def test_forward_bitwise_deterministic(gpu_lib):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("causal,N,rate", [(False, 1100, 0.0), (True, 4200, 0.0), (False, 1100, 0.2)])
+def test_split_role_kernels_bitwise_repeatable(gpu_lib, causal, N, rate):
+    """At head size 128 the long-row forward and the key-block backward hand
+    probabilities from producer to consumer waves through LDS: two runs on the
+    same inputs agree bit for bit (a missed wait on that hand-over would show
+    here as run-to-run differences)."""
+    B, H, Hkv, d = 1, 2, 1, 128
+    assert gpu_lib.forward_kernel_rows(B, H, Hkv, N, N, d, causal) == 64
+    x = I.make_small(B, H, Hkv, N, d, "bf16", 13)
+    q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
+    PT.say(f"split-role repeatability causal={causal} N={N} rate={rate}")
+    runs = []
+    for _ in range(2):
+        o, lse = gpu_lib.forward(q, k, v, None, causal, dropout_rate=rate, seed=3)
+        g = gpu_lib.backward(q, k, v, o, lse, do, None, causal, dropout_rate=rate, seed=3)
+        runs.append((o, lse) + tuple(g))
+    torch.cuda.synchronize()
+    for a, b in zip(*runs):
+        assert torch.isfinite(a).all()
+        assert torch.equal(a, b)
+
+
 def test_forward_allocates_nothing(gpu_lib):
     """With caller-owned outputs the library takes no device memory (O(N) memory:
     only O and LSE are written)."""
