@@ -65,3 +65,13 @@ def test_traffic_lookup_checks_the_sources(monkeypatch):
     monkeypatch.setitem(bench.KERNEL_SOURCES, "bwd_kv_kernel", ["bwd.hip", "common.hpp"])
     assert bench.measured_traffic("bwd_kv_kernel", "long_seq_bf16") is None
     assert bench.measured_traffic("no_such_kernel", "long_seq_bf16") is None
+
+
+def test_committed_profiles_cover_the_current_sources():
+    """The counter summaries under profiles/ were taken from the kernels as they
+    are: every kernel of the long-sequence step has a traffic line whose source
+    hash matches, so bench.py reports its counter bytes (after a change to a
+    kernel source or the compiler flags, the profiles are taken again)."""
+    for k in ("fwd64_kernel", "bwd_pre_kernel", "bwd_kv_kernel", "bwd_q_kernel"):
+        t = bench.measured_traffic(k, "long_seq_bf16")
+        assert t is not None and t > 0, k
