@@ -79,18 +79,22 @@ def test_empty_rows(dtype):
     assert res["o"] <= (PT.TOL_F32 if dtype == "fp32" else PT.TOL_16)
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("rows", ["64", "32"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_late_dominant_scores(dtype, causal, rows):
+def test_late_dominant_scores(dtype, causal, rows, d):
     """Keys far into the sequence whose scores exceed every earlier one by far
     more than the forward's fixed-reference range (keys 400..410: about 90 in
     log2 units above the first tile's maximum, forcing a restart with lazy
     rescaling) or its rescale slack (key 350: about 46 above). The large keys
     keep their random part: with identical key rows the exact dQ of every row
     that attends to them would be zero (the dS of a row sums to zero), and any
-    rounding of dS would make the relative error meaningless."""
-    N, d = 600, 64
+    rounding of dS would make the relative error meaningless. At d = 128 (the
+    split-role forward with 64 rows) the same offsets lift the scores further,
+    past float32's range relative to the first tile's maximum: the restart
+    must also discard the infinite sums."""
+    N = 600
     x = I.make_small(1, 2, 1, N, d, dtype, 21)
     x["q"] = x["q"] + 1.0
     x["k"][:, :, 400:411, :] += 8.0
@@ -105,10 +109,11 @@ def test_late_dominant_scores(dtype, causal, rows):
                  rows_per_wave=int(rows))
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("rows", ["64", "32"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("boost,rate", [(2.0, 0.0), (4.0, 0.0), (4.0, 0.5)])
-def test_moderately_late_dominant_scores(dtype, boost, rate, rows):
+def test_moderately_late_dominant_scores(dtype, boost, rate, rows, d):
     """One key far into the sequence whose score exceeds the first tile's
     maximum by about 23 (boost 2) or 46 (boost 4) in log2 units: inside the
     fixed-reference range of the 64-row kernel's main loop, so nothing forces
@@ -116,8 +121,10 @@ def test_moderately_late_dominant_scores(dtype, boost, rate, rows):
     probability is above the largest finite float16 (2^16); the 16-bit
     probabilities must not overflow, also once scaled for dropout. (The
     causal 64-row kernel needs at least two full tiles before a workgroup's
-    diagonal: N = 600 gives the last workgroups up to 16.)"""
-    N, d = 600, 64
+    diagonal: N = 600 gives the last workgroups up to 16.) At d = 128 (the
+    split-role forward with 64 rows) the same boosts lift the score about 1.4
+    times as far, about 33 and 65, where the larger one leaves that range."""
+    N = 600
     x = I.make_small(1, 2, 1, N, d, dtype, 23)
     x["q"] = x["q"] + 1.0
     x["k"][:, :, 350, :] += boost
