@@ -382,7 +382,10 @@ constexpr int F64_NB = 4;                 // LDS ring slots
 // elements each (fenced order: the compiler's own order put the products of
 // a tile ahead of all its exponentials, which left the producer waiting on
 // the matrix unit the consumer shares), and P V of tile j - 1 on the consumer
-// side; all eight waves stage tile j + 2 and meet at one barrier. The general
+// side. The producers also start the LDS DMA of tile j + 3 (swizzled rows; K
+// in a ring of four slots, V, which the consumers read four iterations after
+// it is started, in a ring of eight) and wait only for the loads they started
+// an iteration earlier; all eight waves meet at one barrier. The general
 // loop (diagonal and ragged tiles, or a restart) raises the reference lazily:
 // the producer then also hands over, per tile, whether its rows see the tile
 // and whether the reference rose, with the per-row factors exp(m_old - m_new)
@@ -395,15 +398,8 @@ constexpr bool f64_split() {
 
 template <class T, int D, int BAND, bool DROP>
 __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
-  constexpr int KP = D * 2 + 16;  // K row pitch (bytes): conflict-free 16-byte row reads
-  constexpr int VP = D * 2 + 32;  // V row pitch (bytes): conflict-free transposing reads
-  constexpr int KBUF = F64_BN * KP;
-  constexpr int VBUF = F64_BN * VP;
-  constexpr int NT = 2 * F64_NW * 64;  // every wave stages tiles
-  constexpr int CH = D / 8;
-  constexpr int TCH = F64_BN * CH;  // 16-byte chunks per tile per tensor
-  constexpr int PER = (TCH + NT - 1) / NT;
-  static_assert(TCH % NT == 0 || TCH < NT, "tile loader shape");
+  constexpr int KBUF = F64_BN * 2 * D;  // K tile: swizzled rows (16-byte row reads)
+  constexpr int VBUF = F64_BN * 2 * D;  // V tile: swizzled rows (transposing reads)
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
   constexpr float kSlack = (std::is_same<T, F16>::value && DROP) ? 7.f : 8.f;  // as in fwd_kernel
@@ -412,10 +408,11 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
   // 64 rows' rescale factors, then the flags (bit 0: the pair's rows see the
   // tile, bit 1: the reference rose)
   constexpr int HB = 4096 + 256 + 16;
-  __shared__ __attribute__((aligned(16))) char smem_raw[F64_NB * (KBUF + VBUF) + 2 * F64_NW * HB + F64_NW * 256];
+  constexpr int VNB = 2 * F64_NB;  // V ring slots
+  __shared__ __attribute__((aligned(16))) char smem_raw[F64_NB * KBUF + VNB * VBUF + 2 * F64_NW * HB + F64_NW * 256];
   lds_t* kbuf = (lds_t*)smem_raw;
   lds_t* vbuf = kbuf + F64_NB * KBUF;
-  lds_t* hbuf = vbuf + F64_NB * VBUF;    // [2][pairs][HB]
+  lds_t* hbuf = vbuf + VNB * VBUF;    // [2][pairs][HB]
   lds_t* ibuf = hbuf + 2 * F64_NW * HB;  // [pairs][64 rows] final 1 / l
 
   const AttnShape& s = a.s;
@@ -437,8 +434,6 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
   if (q0 >= nq) return;  // a sequence shorter than the grid (packed batches)
   const size_t qrow0 = sv.qrow0, krow0 = sv.krow0;
   const unsigned int qbytes = (unsigned int)nq * D * 2, kbytes = (unsigned int)nk * D * 2;
-  const rsrc_t rk = make_rsrc((const unsigned short*)a.k + krow0 * D, kbytes);
-  const rsrc_t rv = make_rsrc((const unsigned short*)a.v + krow0 * D, kbytes);
   const int qw = q0 + F64_RW * pw;  // block rb of the pair holds rows qw + 32 rb + 0..31
   const float c = fmaxf(s.scale * kLog2e, 1e-30f);
   // tiles [tbeg, tbeg + ntiles) hold every key some row of the workgroup sees,
@@ -461,34 +456,27 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
     else return e;
   };
 
-  s16x8 kreg[PER], vreg[PER];
-  auto gload = [&](int t) {
-#pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const int ci = min(tid + r * NT, TCH - 1);
-      const int row = ci / CH, col = (ci % CH) * 8;
-      const unsigned int o = (unsigned)((t * F64_BN + row) * D + col) * 2u;
-      kreg[r] = bload16(rk, o);
-      vreg[r] = bload16(rv, o);
-    }
+  const i32x4 rkw = rsrc_words((const unsigned short*)a.k + krow0 * D, kbytes);
+  const i32x4 rvw = rsrc_words((const unsigned short*)a.v + krow0 * D, kbytes);
+  // the producer waves stage key tile t, the e-th of the processing order, by
+  // LDS DMA into K slot e % 4 and V slot e % 8 (keys past the sequence read as
+  // zeros); a stager's wait for all but its last stage's four loads lets each
+  // load run for a whole iteration
+  auto stage = [&](int t, int e) {
+    dma_tile<D, F64_BN, F64_NW>(rkw, t * F64_BN, kbuf + (e & (F64_NB - 1)) * KBUF, wu, lane);
+    dma_tile<D, F64_BN, F64_NW>(rvw, t * F64_BN, vbuf + (e & (VNB - 1)) * VBUF, wu, lane);
   };
-  auto lstore = [&](int slot) {
-#pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const int ci = min(tid + r * NT, TCH - 1);
-      const int row = ci / CH, col = (ci % CH) * 8;
-      lds_write16(kbuf + slot * KBUF + row * KP + col * 2, kreg[r]);
-      lds_write16(vbuf + slot * VBUF + row * VP + col * 2, vreg[r]);
-    }
-  };
+  auto dma_wait_prev = [&]() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); };
   auto hand = [&](int buf) -> lds_t* { return hbuf + (buf * F64_NW + pw) * HB; };
 
   // Every wave takes the same sequence of barriers: the prologue's, one per
   // main-loop tile, the restart vote, one per general-loop tile, the final one.
-  gload(tile_of(0));
-  lstore(0);
-  gload(tile_of(max(0, min(1, ntiles - 1))));
-  lstore(1);
+  if (producer) {
+    stage(tile_of(0), 0);
+    stage(tile_of(max(0, min(1, ntiles - 1))), 1);
+    stage(tile_of(max(0, min(2, ntiles - 1))), 2);
+    dma_wait();
+  }
   __syncthreads();
 
   // restart bound of the fixed-reference loop, as in the one-role form below
@@ -508,7 +496,7 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
     // S^T = K Q^T of the tile in a slot: st[rb][i] is S of query qw + 32 rb + l32
     // and key 8 (i / 4) + 4 hh + i % 4 of the tile
     auto s_tile = [&](int slot, f32x16 (&st)[2]) {
-      const lds_t* kb = kbuf + slot * KBUF + l32 * KP + 16 * hh;
+      const lds_t* kb = kbuf + slot * KBUF;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         st[0][i] = 0.f;
@@ -516,7 +504,7 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
       }
 #pragma unroll
       for (int ss = 0; ss < NS; ++ss) {
-        const s16x8 ka = lds_read16(kb + 32 * ss);
+        const s16x8 ka = lds_read16(kb + swz_off<D>(l32, 2 * ss + hh));
         st[0] = mfma32<T>(ka, qf[0][ss], st[0]);
         st[1] = mfma32<T>(ka, qf[1][ss], st[1]);
       }
@@ -547,8 +535,8 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
       // one iteration in slots: S product t of the next tile, then elements
       // 2 t and 2 t + 1 of the current tile's probabilities (fenced order)
       auto iter = [&](int jj, const f32x16 (&scur)[2], f32x16 (&snext)[2]) {
-        gload(tile_of(min(jj + 2, ntiles - 1)));
-        const lds_t* kb = kbuf + ((jj + 1) & (F64_NB - 1)) * KBUF + l32 * KP + 16 * hh;
+        stage(tile_of(min(jj + 3, ntiles - 1)), jj + 3);
+        const lds_t* kb = kbuf + ((jj + 1) & (F64_NB - 1)) * KBUF;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           snext[0][i] = 0.f;
@@ -556,7 +544,7 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
         }
         s16x8 ka[NS];
 #pragma unroll
-        for (int ss = 0; ss < NS; ++ss) ka[ss] = lds_read16(kb + 32 * ss);
+        for (int ss = 0; ss < NS; ++ss) ka[ss] = lds_read16(kb + swz_off<D>(l32, 2 * ss + hh));
         unsigned int dw[2][4];
         if constexpr (DROP) {
 #pragma unroll
@@ -581,7 +569,7 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
         l[0] += sum[0];
         l[1] += sum[1];
         write_p(hand(jj & 1), pk);
-        lstore((jj + 2) & (F64_NB - 1));
+        dma_wait_prev();
         __syncthreads();
       };
       // the reference: the first tile's row maximum
@@ -603,20 +591,21 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
         ++j;
       }
       // workgroup-wide vote (the consumers vote no): start over in the general loop
+      dma_wait();
       if (__syncthreads_or(l[0] > lmax || l[1] > lmax)) {
         j = 0;
         m[0] = m[1] = -INFINITY;
         l[0] = l[1] = 0.f;
-        gload(tile_of(0));
-        lstore(0);
-        gload(tile_of(max(0, min(1, ntiles - 1))));
-        lstore(1);
+        stage(tile_of(0), 0);
+        stage(tile_of(max(0, min(1, ntiles - 1))), 1);
+        stage(tile_of(max(0, min(2, ntiles - 1))), 2);
+        dma_wait();
         __syncthreads();
       }
     }
     // general loop: element masks, lazy rescaling; a pair whose rows see no key of the tile skips it
     for (; j < ntiles; ++j) {
-      gload(tile_of(min(j + 2, ntiles - 1)));
+      stage(tile_of(min(j + 3, ntiles - 1)), j + 3);
       const int ks = tile_of(j) * F64_BN;
       lds_t* hb = hand(j & 1);
       const bool act = (!BAND || ks <= qw + F64_RW - 1 + offu) && (!LOWER || ks + F64_BN - 1 >= qw + offl);
@@ -668,9 +657,10 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
         write_p(hb, pk);
       }
       if (lane == 0) *(__attribute__((address_space(3))) int*)(hb + 4096 + 256) = (act ? 1 : 0) | (resc ? 2 : 0);
-      lstore((j + 2) & (F64_NB - 1));
+      dma_wait_prev();
       __syncthreads();
     }
+    dma_wait();
     // 1 / l per row for the consumer; the log-sum-exp from here
     const rsrc_t rl = make_rsrc(a.lse + qrow0, (unsigned)nq * 4u);
 #pragma unroll
@@ -700,13 +690,14 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int u = 0; u < 2; ++u) pop[rb][u] = lds_read16(hb + (2 * rb + u) * 1024 + lane * 16);
-      const lds_t* vb = vbuf + slot * VBUF;
+      const lds_t* vb = vbuf + slot * VBUF;  // slot: tile index modulo 8
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const lds_t* vp = vb + (16 * u + roff) * VP + (32 * dt + coff) * 2;
-          const s16x8 va = concat(lds_read_tr(vp), lds_read_tr(vp + 8 * VP));
+          const int cc = 4 * dt + (coff >> 3), within = 2 * (coff & 7);
+          const s16x8 va = concat(lds_read_tr(vb + swz_off<D>(16 * u + roff, cc) + within),
+                                  lds_read_tr(vb + swz_off<D>(16 * u + roff + 8, cc) + within));
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb) acc[rb][dt] = mfma32<T>(va, pop[rb][u], acc[rb][dt]);
         }
@@ -726,18 +717,16 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
               for (int i = 0; i < 16; ++i) acc[rb][dt][i] *= corr;
           }
         }
-        pv(t & (F64_NB - 1), hb);
+        pv(t & (VNB - 1), hb);
       }
     };
     if (nfull > 0) {
       // main loop: iteration j takes P V of tile j - 1 (fixed reference: no rescale)
       for (; j < nfull; ++j) {
-        gload(tile_of(min(j + 2, ntiles - 1)));
-        if (j > 0) pv((j - 1) & (F64_NB - 1), hand((j - 1) & 1));
-        lstore((j + 2) & (F64_NB - 1));
+        if (j > 0) pv((j - 1) & (VNB - 1), hand((j - 1) & 1));
         __syncthreads();
       }
-      pv((nfull - 1) & (F64_NB - 1), hand((nfull - 1) & 1));
+      pv((nfull - 1) & (VNB - 1), hand((nfull - 1) & 1));
       if (__syncthreads_or(0)) {
         j = 0;
 #pragma unroll
@@ -746,19 +735,13 @@ __device__ __forceinline__ void fwd64_split_body(const FwdArgs& a) {
           for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[rb][dt][i] = 0.f;
-        gload(tile_of(0));
-        lstore(0);
-        gload(tile_of(max(0, min(1, ntiles - 1))));
-        lstore(1);
         __syncthreads();
       }
     }
     // general loop: iteration j takes tile j - 1, the last tile follows the last barrier
     const int j0 = j;
     for (; j < ntiles; ++j) {
-      gload(tile_of(min(j + 2, ntiles - 1)));
       if (j > j0) consume(j - 1);
-      lstore((j + 2) & (F64_NB - 1));
       __syncthreads();
     }
     if (ntiles > j0) consume(ntiles - 1);
