@@ -181,14 +181,16 @@ def run_varlen(lens_q, lens_k, H, Hkv, d, dtype, causal, seed=0, backward=True, 
 
 
 def run_window(B, H, Hkv, Nq, Nk, d, dtype, causal, window, mask=None, seed=0, backward=True, dropout_rate=0.0,
-               drop_seed=0, rows_per_wave=0):
-    """Full comparison with a sliding-window band (fa_forward_qk / fa_backward_qk)."""
+               drop_seed=0, rows_per_wave=0, x=None, lse_tol=TOL_LSE):
+    """Full comparison with a sliding-window band (fa_forward_qk / fa_backward_qk);
+    x: given CPU inputs of that shape instead of the seeded ones."""
     where = (f"B{B} H{H} Hkv{Hkv} Nq{Nq} Nk{Nk} d{d} {dtype} causal={causal} window={tuple(window)} "
              f"mask={mask is not None} seed={seed} rows_per_wave={rows_per_wave}")
     if dropout_rate:
         where += f" dropout={dropout_rate} drop_seed={drop_seed}"
     say("case", where)
-    x = I.make_cross(B, H, Hkv, Nq, Nk, d, dtype, seed, with_grad=backward)
+    if x is None:
+        x = I.make_cross(B, H, Hkv, Nq, Nk, d, dtype, seed, with_grad=backward)
     dev = torch.device("cuda", 0)
     q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
     scale = 1.0 / math.sqrt(d)
@@ -199,7 +201,7 @@ def run_window(B, H, Hkv, Nq, Nk, d, dtype, causal, window, mask=None, seed=0, b
     qd, kd, vd = (np64(x[n]) for n in ("q", "k", "v"))
     oref, lref = oracle.forward(qd, kd, vd, scale, causal, mask, dropout_rate=dropout_rate, seed=drop_seed,
                                 window=tuple(window))
-    res = {"o": check_out(np64(o), oref, dtype, where), "lse": check_lse(np64(lse), lref, where)}
+    res = {"o": check_out(np64(o), oref, dtype, where), "lse": check_lse(np64(lse), lref, where, lse_tol)}
     if backward and dtype != "fp32":
         do = x["do"].to(dev)
         dq, dk, dv = binding.backward(q, k, v, o, lse, do, scale, causal, mt, dropout_rate=dropout_rate,

@@ -53,6 +53,27 @@ def test_window_forward_kernels(window, rows):
                   backward=False, rows_per_wave=int(rows))
 
 
+@pytest.mark.parametrize("rows", ["64", "32"])
+@pytest.mark.parametrize("window", [(600, 0), (500, 100)], ids=str)
+def test_window_restart(window, rows):
+    """Keys 900..910 whose scores exceed every other by far more than the
+    64-row forward's fixed-reference range, under a two-edged band: in the
+    256-row workgroups the tiles every row sees in full start well before
+    those keys (from key 640 for rows 768..1023 with window (600, 0)), so the
+    main loop's row sums overflow and it restarts with lazy rescaling while
+    the band's tile order (full tiles, then the partial ones above and below)
+    drives its LDS ring (d = 128: the split-role form). The 32-row kernel
+    takes the same scores with its lazy reference."""
+    Nq, Nk, d = 1100, 1300, 128
+    x = I.make_cross(1, 2, 1, Nq, Nk, d, "bf16", _seed(*window, int(rows), 9), with_grad=True)
+    x["q"] = x["q"] + 1.0
+    x["k"][:, :, 900:911, :] += 8.0
+    q, k = (PT.np64(x[n]) for n in ("q", "k"))
+    big = float(np.abs(q @ np.swapaxes(k, -1, -2)).max()) / np.sqrt(d)
+    PT.run_window(1, 2, 1, Nq, Nk, d, "bf16", False, window, rows_per_wave=int(rows), x=x,
+                  lse_tol=PT.TOL_LSE + 4 * 2.0 ** -23 * big)
+
+
 @pytest.mark.parametrize("window", [(64, 0), (17, 5), (0, 0), (300, -1)], ids=str)
 def test_window_fp32(window):
     PT.run_window(1, 2, 1, 200, 260, 32, "fp32", False, window, seed=_seed(*window, 5), backward=False)
