@@ -91,8 +91,13 @@ def test_window_varlen(window):
                   window=window)
 
 
-def test_window_dropout():
-    PT.run_window(1, 2, 2, 300, 400, 128, "bf16", True, (100, 0), seed=71, dropout_rate=0.2, drop_seed=72)
+@pytest.mark.parametrize("rows", ["0", "64"])
+@pytest.mark.parametrize("window,causal", [((100, 0), True), ((150, 60), False)], ids=str)
+def test_window_dropout(window, causal, rows):
+    """Dropout under a band; rows 64 forces the split-role forward at d = 128,
+    whose keep decisions follow the band's tile order."""
+    PT.run_window(1, 2, 2, 300, 400, 128, "bf16", causal, window, seed=71, dropout_rate=0.2, drop_seed=72,
+                  rows_per_wave=int(rows))
 
 
 def test_window_large_sampled():
