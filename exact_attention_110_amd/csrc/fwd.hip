@@ -18,13 +18,14 @@
 //    gfx950 transposing read ds_read_b64_tr_b16, so V needs no transpose pass.
 //  * LDS row pitches are padded so that the 16-byte row reads of K and the
 //    transposing reads of V are free of bank conflicts.
-//  * Rows of 4096 keys or more at head size 128 (1024 without a causal or
-//    window band) run fwd64_kernel (64 query rows per wave
-//    pair, 256 rows per workgroup; at d = 128 as a producer wave forming the
-//    probabilities and a consumer wave holding O on each SIMD, otherwise as
-//    one wave per SIMD); the others,
-//    and all block-sparse inputs, run fwd_kernel (32 rows per wave, two waves
-//    per SIMD, 128 rows per workgroup = one mask block row).
+//  * fwd64_kernel (64 query rows per wave pair, 256 rows per workgroup; at
+//    d = 128 as a producer wave forming the probabilities and a consumer wave
+//    holding O on each SIMD, otherwise as one wave per SIMD) runs at head size
+//    128 when its grid holds at least 256 workgroups and the rows have 4096
+//    keys or more (1024 without a causal or window band), or when the grid
+//    holds at least 2048; the others, and all block-sparse inputs, run
+//    fwd_kernel (32 rows per wave, two waves per SIMD, 128 rows per workgroup
+//    = one mask block row).
 //  * Causal: a workgroup stops at its diagonal tile, waves skip tiles that lie
 //    wholly after their rows, and only diagonal and tail tiles are masked
 //    element by element. Heaviest query blocks are launched first.
@@ -1367,19 +1368,27 @@ static hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st) {
 }
 
 // Which 16-bit kernel a forward call takes by default. At head size 128 the
-// 64-row kernel (in its split-role form) pays off from 4096 keys with a band
-// (causal or windowed) and from 1024 without (measured, bf16, one box: causal
-// N = 4096 x 64 heads 7% faster, N = 16384 x 16 heads 11%, N = 2048 even,
-// N = 1024 13% slower, the 256-row workgroups spending much of their time in
-// the diagonal tail; without a band N = 1024 8% faster, N = 4096 10%, N = 512
-// even). At head size 64 the exponentials dominate and the 32-row kernel's two
-// waves per SIMD do better (N = 16384: 6% faster). Block masks and score
-// biases always take the 32-row kernel. Float32 inputs take the float32
-// kernel (0).
+// 64-row kernel (in its split-role form) needs a grid of at least one
+// 256-row workgroup per CU to pay off: with fewer, the 32-row kernel's twice
+// as many workgroups fill more of the chip (measured, bf16, one box, forward
+// time 64-row / 32-row: causal N = 16384 with 2 heads 1.08, 4 heads 0.97, 16
+// heads 0.87; N = 8192 with 4 heads 1.08, 8 heads 1.00, 16 heads 0.85;
+// without a band N = 2048 with 16 heads 1.17, N = 4096 with 8 heads 1.16, 16
+// heads 0.97). Given that grid, it pays off from 4096 keys per row with a
+// band (causal or windowed) and from 1024 without, and at shorter rows only
+// once the grid holds about eight workgroups per CU (without a band N = 768
+// with 1024 heads 0.82, N = 512 with 1024 heads 0.95 but with 256 heads 1.07;
+// causal N = 2048 with 1024 heads 0.84, N = 3072 with 256 heads 0.90 but with
+// 64 heads 1.04). At head size 64 the exponentials dominate and the 32-row
+// kernel's two waves per SIMD do better (N = 16384: 6% faster). Block masks
+// and score biases always take the 32-row kernel. Float32 inputs take the
+// float32 kernel (0).
 int forward_rows(const AttnShape& s, int dtype) {
   if (dtype == 0) return 0;
-  if (s.mask || s.alibi) return 32;
-  return (s.d == 128 && min(s.Nq, s.Nk) >= (s.band ? 4096 : 1024)) ? 64 : 32;
+  if (s.mask || s.alibi || s.d != 128) return 32;
+  const long long grid = (long long)s.B * s.H * ((s.Nq + F64_BM - 1) / F64_BM);  // 64-row workgroups
+  const int len = min(s.Nq, s.Nk);
+  return (grid >= 256 && (len >= (s.band ? 4096 : 1024) || grid >= 2048)) ? 64 : 32;
 }
 
 hipError_t launch_forward(const FwdArgs& a, int dtype, hipStream_t st, int rows) {

@@ -303,8 +303,10 @@ int fa_backward_bitmask(const void* q, const void* k, const void* v, const void*
 
 /*
  * Forward kernel choice. The 16-bit forward pass has two kernels: one with 64
- * query rows per wave (head size 128 with at least 4096 keys per row under a
- * causal or window band, 1024 without; at that
+ * query rows per wave (head size 128 when its grid, B * H * ceil(Nq / 256)
+ * workgroups, holds at least 256 of them and either the shorter of Nq, Nk is
+ * at least 4096 under a causal or window band, 1024 without, or the grid
+ * holds at least 2048; at that
  * head size a producer wave forming the probabilities and a consumer wave
  * holding the output share each SIMD, at smaller head sizes, when forced, it
  * runs one wave per SIMD) and one with 32 rows per wave (two waves per SIMD;

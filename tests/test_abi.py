@@ -264,8 +264,9 @@ def test_fp8_head_sizes(lib):
 
 def test_forward_kernel_rows(lib):
     """The library's forward-kernel choice, as bench.py reads it: 64 rows per
-    wave at head size 128 for rows of 4096 keys under a band (1024 without),
-    32 otherwise and
+    wave at head size 128 when the 64-row grid (B * H * ceil(Nq / 256)
+    workgroups) holds at least 256 and the rows have 4096 keys under a band
+    (1024 without) or the grid holds at least 2048; 32 otherwise and
     always with a block mask or score bias, 0 (the float32 kernel) for FA_F32;
     negative statuses for arguments the forward calls reject."""
     rows = lambda *a: lib.fa_forward_kernel_rows(*a)  # noqa: E731
@@ -275,14 +276,24 @@ def test_forward_kernel_rows(lib):
     assert rows(1, 16, 16, 16384, 16384, 128, 1, -1, -1, 0, 1, BF16) == 32
     assert rows(4, 32, 8, 8192, 8192, 128, 1, -1, -1, 0, 0, BF16) == 64
     assert rows(8, 12, 12, 1024, 1024, 64, 1, -1, -1, 0, 0, BF16) == 32
-    # head size 128: from 4096 keys with a band (causal, windows), from 1024 without;
-    # the shorter side decides
+    # head size 128, grids of at least 256 workgroups: from 4096 keys with a band
+    # (causal, windows), from 1024 without; the shorter side decides
     assert rows(1, 8, 8, 8192, 4095, 128, 1, -1, -1, 0, 0, F16) == 32
     assert rows(1, 8, 8, 8192, 4096, 128, 1, -1, -1, 0, 0, F16) == 64
-    assert rows(1, 8, 8, 4096, 4096, 128, 0, 256, -1, 0, 0, BF16) == 64    # a lower window edge is a band
-    assert rows(1, 8, 8, 2048, 2048, 128, 0, -1, 64, 0, 0, BF16) == 32     # so is an upper one
-    assert rows(1, 8, 8, 2048, 1023, 128, 0, -1, -1, 0, 0, F16) == 32
-    assert rows(1, 8, 8, 2048, 1024, 128, 0, -1, -1, 0, 0, F16) == 64
+    assert rows(1, 16, 16, 4096, 4096, 128, 0, 256, -1, 0, 0, BF16) == 64  # a lower window edge is a band
+    assert rows(4, 16, 16, 2048, 2048, 128, 0, -1, 64, 0, 0, BF16) == 32   # so is an upper one
+    assert rows(4, 8, 8, 2048, 1023, 128, 0, -1, -1, 0, 0, F16) == 32
+    assert rows(4, 8, 8, 2048, 1024, 128, 0, -1, -1, 0, 0, F16) == 64
+    # smaller grids take the 32-row kernel whatever the length
+    assert rows(1, 2, 2, 16384, 16384, 128, 1, -1, -1, 0, 0, BF16) == 32   # 128 workgroups
+    assert rows(1, 4, 4, 16384, 16384, 128, 1, -1, -1, 0, 0, BF16) == 64   # 256
+    assert rows(1, 16, 16, 2048, 2048, 128, 0, -1, -1, 0, 0, BF16) == 32   # 128
+    assert rows(1, 8, 8, 4096, 4096, 128, 0, 256, -1, 0, 0, BF16) == 32    # 128
+    # shorter rows in grids of 2048 workgroups or more
+    assert rows(64, 16, 16, 512, 512, 128, 0, -1, -1, 0, 0, BF16) == 64    # 2048
+    assert rows(32, 16, 16, 512, 512, 128, 0, -1, -1, 0, 0, BF16) == 32    # 1024
+    assert rows(64, 16, 16, 2048, 2048, 128, 1, -1, -1, 0, 0, BF16) == 64  # 8192, causal
+    assert rows(8, 16, 16, 2048, 2048, 128, 1, -1, -1, 0, 0, BF16) == 32   # 1024, causal
     assert rows(1, 16, 16, 16384, 16384, 64, 1, -1, -1, 0, 0, BF16) == 32  # head size 64: 32 rows
     assert rows(1, 1, 1, 512, 512, 32, 0, -1, -1, 0, 0, F32) == 0
     assert rows(1, 2, 1, 256, 256, 96, 1, -1, -1, 0, 0, BF16) == EINVAL

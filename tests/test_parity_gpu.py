@@ -44,8 +44,8 @@ def test_dense(shape, causal, dtype):
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_dense_64_rows_per_wave(shape, causal, dtype):
     """The 64-row forward kernel (chosen by the library at head size 128 for
-    rows of 4096 keys or more under a band, 1024 without) at every small
-    shape, forced through fa_forward_select."""
+    large enough grids and long enough rows) at every small shape, forced
+    through fa_forward_select."""
     B, H, Hkv, N, d = shape
     PT.run_small(B, H, Hkv, N, d, dtype, causal, seed=5000 + N + d + int(causal) + (1 if dtype == "fp16" else 0),
                  backward=False, rows_per_wave=64)
@@ -199,13 +199,12 @@ def test_split_role_kernels_bitwise_repeatable(gpu_lib, causal, N, rate):
     same inputs agree bit for bit (a missed wait on that hand-over would show
     here as run-to-run differences)."""
     B, H, Hkv, d = 1, 2, 1, 128
-    assert gpu_lib.forward_kernel_rows(B, H, Hkv, N, N, d, causal) == 64
     x = I.make_small(B, H, Hkv, N, d, "bf16", 13)
     q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
     PT.say(f"split-role repeatability causal={causal} N={N} rate={rate}")
     runs = []
     for _ in range(2):
-        o, lse = gpu_lib.forward(q, k, v, None, causal, dropout_rate=rate, seed=3)
+        o, lse = gpu_lib.forward(q, k, v, None, causal, dropout_rate=rate, seed=3, rows_per_wave=64)
         g = gpu_lib.backward(q, k, v, o, lse, do, None, causal, dropout_rate=rate, seed=3)
         runs.append((o, lse) + tuple(g))
     torch.cuda.synchronize()
