@@ -213,6 +213,26 @@ def test_split_role_kernels_bitwise_repeatable(gpu_lib, causal, N, rate):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("B,H,N,causal", [(1, 2, 1024, False), (64, 16, 512, False), (1, 4, 16384, True)])
+def test_default_kernel_is_the_reported_one(gpu_lib, B, H, N, causal):
+    """A forward call without a forced kernel runs the one
+    fa_forward_kernel_rows names (bench.py credits that kernel): its output is
+    bitwise that of the same call forced to it, and differs from the other
+    kernel's (the two round differently)."""
+    d = 128
+    rows = gpu_lib.forward_kernel_rows(B, H, H, N, N, d, causal)
+    assert rows in (32, 64)
+    g = torch.Generator().manual_seed(B * 1000 + N)
+    q, k, v = (torch.randn(B, H, N, d, generator=g).to(torch.bfloat16).cuda() for _ in range(3))
+    o0, l0 = gpu_lib.forward(q, k, v, None, causal)
+    o1, l1 = gpu_lib.forward(q, k, v, None, causal, rows_per_wave=rows)
+    o2, _ = gpu_lib.forward(q, k, v, None, causal, rows_per_wave=96 - rows)
+    torch.cuda.synchronize()
+    PT.say(f"default kernel B={B} H={H} N={N} causal={causal}: {rows} rows")
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    assert not torch.equal(o0, o2)
+
+
 def test_forward_allocates_nothing(gpu_lib):
     """With caller-owned outputs the library takes no device memory (O(N) memory:
     only O and LSE are written)."""
